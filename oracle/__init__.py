@@ -1,0 +1,146 @@
+"""ctypes loader for the CPU oracle (oracle.cpp).
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product package.  It shares no
+code with the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+SOURCES = [os.path.join(HERE, "oracle.cpp")]
+
+OK = 0
+EINVAL = -1
+REASONS = {0: "none", 1: "zero_size", 2: "misaligned", 3: "live_flag",
+           4: "out_of_arena", 5: "overlap"}
+U64_MAX = (1 << 64) - 1
+
+
+def build(verbose: bool = False) -> str:
+    """Compile liboracle.so with g++ (plain -O2, single-threaded)."""
+    cmd = ["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-Wall", "-Wextra",
+           "-o", LIB_PATH + ".tmp"] + SOURCES
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+class _Stats(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_uint64) for k in (
+        "arena_bytes", "live_bytes", "free_bytes", "largest_hole", "hole_count",
+        "live_blocks", "moved_blocks", "moved_bytes")] + [
+        ("frag_free_over_largest_minus_1", ctypes.c_double),
+        ("frag_one_minus_largest_over_free", ctypes.c_double)]
+
+
+@dataclasses.dataclass(frozen=True)
+class Stats:
+    arena_bytes: int
+    live_bytes: int
+    free_bytes: int
+    largest_hole: int
+    hole_count: int
+    live_blocks: int
+    moved_blocks: int
+    moved_bytes: int
+    frag_free_over_largest_minus_1: float
+    frag_one_minus_largest_over_free: float
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        U = ctypes.c_uint64
+        L.oracle_validate.argtypes = [P, P, P, U, U, P, P]
+        L.oracle_validate.restype = ctypes.c_int
+        L.oracle_new_offsets.argtypes = [P, P, P, U, P]
+        L.oracle_compact.argtypes = [P, U, P, P, P, U]
+        L.oracle_stats_walk.argtypes = [P, P, P, U, U, P]
+        L.oracle_remap.argtypes = [P, P, P, U, P, P, U, P]
+        L.oracle_source_map.argtypes = [P, P, P, U, U, U, U, P, P, P, U]
+        L.oracle_source_map.restype = ctypes.c_int64
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _table(off, size, live):
+    off = np.ascontiguousarray(off, dtype=np.uint64)
+    size = np.ascontiguousarray(size, dtype=np.uint64)
+    live = np.ascontiguousarray(live, dtype=np.uint8)
+    assert off.shape == size.shape == live.shape
+    return off, size, live
+
+
+def validate(off, size, live, arena_bytes):
+    off, size, live = _table(off, size, live)
+    bad = ctypes.c_uint64()
+    reason = ctypes.c_int32()
+    rc = lib().oracle_validate(_p(off), _p(size), _p(live), off.shape[0],
+                               arena_bytes, ctypes.byref(bad), ctypes.byref(reason))
+    return rc, bad.value, reason.value
+
+
+def new_offsets(off, size, live):
+    off, size, live = _table(off, size, live)
+    out = np.empty(off.shape[0], dtype=np.uint64)
+    lib().oracle_new_offsets(_p(off), _p(size), _p(live), off.shape[0], _p(out))
+    return out
+
+
+def compact(arena: np.ndarray, off, size, live):
+    """In place on a host uint8 arena."""
+    assert arena.dtype == np.uint8 and arena.flags["C_CONTIGUOUS"]
+    off, size, live = _table(off, size, live)
+    lib().oracle_compact(_p(arena), arena.shape[0], _p(off), _p(size), _p(live),
+                         off.shape[0])
+
+
+def stats(off, size, live, arena_bytes) -> Stats:
+    off, size, live = _table(off, size, live)
+    s = _Stats()
+    lib().oracle_stats_walk(_p(off), _p(size), _p(live), off.shape[0],
+                            arena_bytes, ctypes.byref(s))
+    return Stats(*[getattr(s, f[0]) for f in _Stats._fields_])
+
+
+def remap(off, size, live, handles):
+    off, size, live = _table(off, size, live)
+    h = np.ascontiguousarray(handles, dtype=np.uint64)
+    out = np.empty_like(h)
+    bad = ctypes.c_uint64()
+    lib().oracle_remap(_p(off), _p(size), _p(live), off.shape[0], _p(h), _p(out),
+                       h.shape[0], ctypes.byref(bad))
+    return out, bad.value
+
+
+def source_map(off, size, live, arena_bytes, p0, length, cap=1 << 16):
+    off, size, live = _table(off, size, live)
+    d = np.empty(cap, dtype=np.uint64)
+    s = np.empty(cap, dtype=np.uint64)
+    l = np.empty(cap, dtype=np.uint64)
+    k = lib().oracle_source_map(_p(off), _p(size), _p(live), off.shape[0],
+                                arena_bytes, p0, length, _p(d), _p(s), _p(l), cap)
+    if k < 0:
+        raise ValueError("source map needs more segments than cap")
+    return d[:k].copy(), s[:k].copy(), l[:k].copy()

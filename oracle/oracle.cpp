@@ -1,0 +1,186 @@
+// oracle.cpp -- plain single-threaded CPU oracle for in-place arena compaction.
+//
+// TEST INFRASTRUCTURE ONLY (tests, smoke check, benchmark CPU baseline).  It
+// shares nothing with the HIP library.  Each function states the passage of
+// the pages it writes out; see oracle.h for the page titles.
+//
+// Readings where the pages are silent (also listed in the design notes):
+//  * a hole is any maximal byte run not covered by a live entry -- free
+//    entries, untracked gaps and the tail alike; adjacent free pieces form one
+//    hole, as the CANN pool merges adjacent free blocks ([CANN] 2.2);
+//  * entries are 32-byte aligned and non-empty ([CANN] 2.2 rounds every
+//    request up to 32 bytes; 3.3 aligns allocations to 32 or 64 bytes);
+//  * compaction keeps block order and packs from arena offset 0 with no
+//    padding: every live block moves down by the total hole size below it
+//    ([910C] periodic compaction: holes scanned low to high, downward shift);
+//  * bytes at or above the live total keep whatever they held.
+#include "oracle.h"
+
+#include <algorithm>
+#include <cstring>
+
+extern "C" {
+
+// Entry checks, lowest entry first; within an entry the checks run in the
+// order of the reason codes in oracle.h.
+int oracle_validate(const uint64_t *offset, const uint64_t *size,
+                    const uint8_t *live, uint64_t n, uint64_t arena_bytes,
+                    uint64_t *bad_index, int32_t *reason) {
+    *bad_index = UINT64_MAX;
+    *reason = ORACLE_REASON_NONE;
+    for (uint64_t i = 0; i < n; ++i) {
+        int32_t r = ORACLE_REASON_NONE;
+        if (size[i] == 0)
+            r = ORACLE_REASON_ZERO_SIZE;
+        else if (offset[i] % 32 != 0 || size[i] % 32 != 0)
+            r = ORACLE_REASON_MISALIGNED;
+        else if (live[i] > 1)
+            r = ORACLE_REASON_LIVE_FLAG;
+        else if (offset[i] > arena_bytes || size[i] > arena_bytes - offset[i])
+            r = ORACLE_REASON_OUT_OF_ARENA;
+        else if (i > 0 && offset[i - 1] + size[i - 1] > offset[i])
+            r = ORACLE_REASON_OVERLAP;
+        if (r != ORACLE_REASON_NONE) {
+            *bad_index = i;
+            *reason = r;
+            return ORACLE_EINVAL;
+        }
+    }
+    return ORACLE_OK;
+}
+
+// [910C] periodic compaction: each live tensor moves toward low addresses by
+// the holes below it, so its new start is the bytes of live data below it.
+void oracle_new_offsets(const uint64_t *offset, const uint64_t *size,
+                        const uint8_t *live, uint64_t n, uint64_t *new_offset) {
+    (void)offset;
+    uint64_t running = 0;
+    for (uint64_t i = 0; i < n; ++i) {
+        new_offset[i] = running;
+        if (live[i]) running += size[i];
+    }
+}
+
+// [910C] periodic compaction, "move the data"; [CANN] 3.3 periodic
+// compaction gathers every allocated block into one contiguous region.
+// Lowest block first: block i's destination can only overlap its own source
+// (memmove copes) and sources of lower blocks, which have already moved.
+void oracle_compact(uint8_t *arena, uint64_t arena_bytes,
+                    const uint64_t *offset, const uint64_t *size,
+                    const uint8_t *live, uint64_t n) {
+    (void)arena_bytes;
+    uint64_t dst = 0;
+    for (uint64_t i = 0; i < n; ++i) {
+        if (!live[i]) continue;
+        if (dst != offset[i])
+            std::memmove(arena + dst, arena + offset[i], size[i]);
+        dst += size[i];
+    }
+}
+
+// [910C] monitoring: the free total and the largest contiguous free block,
+// and free/largest - 1.  [CANN] 3.2: 1 - largest/free, 0 when nothing is
+// free (the same rule is taken for the first ratio).  [CANN] 2.2: adjacent
+// free blocks merge, so a hole is the whole gap between two live blocks.
+void oracle_stats_walk(const uint64_t *offset, const uint64_t *size,
+                       const uint8_t *live, uint64_t n, uint64_t arena_bytes,
+                       oracle_stats *out) {
+    std::memset(out, 0, sizeof(*out));
+    out->arena_bytes = arena_bytes;
+    uint64_t cursor = 0;   // end of the last live block seen so far
+    uint64_t new_off = 0;  // where the current live block would land
+    for (uint64_t i = 0; i < n; ++i) {
+        if (!live[i]) continue;
+        const uint64_t gap = offset[i] - cursor;
+        if (gap > 0) {
+            out->hole_count += 1;
+            if (gap > out->largest_hole) out->largest_hole = gap;
+        }
+        out->live_blocks += 1;
+        out->live_bytes += size[i];
+        if (offset[i] != new_off) {
+            out->moved_blocks += 1;
+            out->moved_bytes += size[i];
+        }
+        new_off += size[i];
+        cursor = offset[i] + size[i];
+    }
+    const uint64_t tail = arena_bytes - cursor;
+    if (tail > 0) {
+        out->hole_count += 1;
+        if (tail > out->largest_hole) out->largest_hole = tail;
+    }
+    out->free_bytes = arena_bytes - out->live_bytes;
+    if (out->free_bytes == 0) {
+        out->frag_free_over_largest_minus_1 = 0.0;
+        out->frag_one_minus_largest_over_free = 0.0;
+    } else {
+        const double F = (double)out->free_bytes;
+        const double L = (double)out->largest_hole;
+        out->frag_free_over_largest_minus_1 = F / L - 1.0;
+        out->frag_one_minus_largest_over_free = 1.0 - L / F;
+    }
+}
+
+// [910C] periodic compaction, "update the references in one batch"; and
+// "Moving to other accelerators": without a framework call that rewrites
+// tensor addresses, references are kept at operator level -- here a handle is
+// a byte address in the arena; it keeps its offset inside its block.
+void oracle_remap(const uint64_t *offset, const uint64_t *size,
+                  const uint8_t *live, uint64_t n, const uint64_t *h_in,
+                  uint64_t *h_out, uint64_t n_handles, uint64_t *n_invalid) {
+    uint64_t *new_off = new uint64_t[n ? n : 1];
+    oracle_new_offsets(offset, size, live, n, new_off);
+    uint64_t bad = 0;
+    for (uint64_t k = 0; k < n_handles; ++k) {
+        const uint64_t h = h_in[k];
+        const uint64_t *it = std::upper_bound(offset, offset + n, h);
+        uint64_t result = UINT64_MAX;
+        if (it != offset) {
+            const uint64_t i = (uint64_t)(it - offset) - 1;
+            if (live[i] && h - offset[i] < size[i])
+                result = new_off[i] + (h - offset[i]);
+        }
+        if (result == UINT64_MAX) bad += 1;
+        h_out[k] = result;
+    }
+    delete[] new_off;
+    *n_invalid = bad;
+}
+
+// The compacted arena written as a function of the original one: a byte
+// below the live total holds the byte of the live block that lands there
+// (same offset inside the block); a byte at or above it is untouched.
+int64_t oracle_source_map(const uint64_t *offset, const uint64_t *size,
+                          const uint8_t *live, uint64_t n, uint64_t arena_bytes,
+                          uint64_t p0, uint64_t len, uint64_t *seg_dst,
+                          uint64_t *seg_src, uint64_t *seg_len, uint64_t cap) {
+    (void)arena_bytes;
+    const uint64_t p1 = p0 + len;
+    uint64_t count = 0;
+    uint64_t dst = 0;
+    for (uint64_t i = 0; i < n; ++i) {
+        if (!live[i]) continue;
+        const uint64_t a = std::max(dst, p0);
+        const uint64_t b = std::min(dst + size[i], p1);
+        if (a < b) {
+            if (count == cap) return -1;
+            seg_dst[count] = a;
+            seg_src[count] = offset[i] + (a - dst);
+            seg_len[count] = b - a;
+            ++count;
+        }
+        dst += size[i];
+    }
+    const uint64_t a = std::max(dst, p0);
+    if (a < p1) {
+        if (count == cap) return -1;
+        seg_dst[count] = a;
+        seg_src[count] = a;
+        seg_len[count] = p1 - a;
+        ++count;
+    }
+    return (int64_t)count;
+}
+
+}  // extern "C"

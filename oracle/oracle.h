@@ -1,0 +1,101 @@
+/*
+ * oracle.h -- plain, single-threaded CPU oracle for in-place arena compaction.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this code: only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or constant with
+ * the HIP library; the two agree only because both follow the same pages.
+ *
+ * Pages followed (cited by title and section):
+ *   [910C]  "Ascend 910C cluster tuning: memory-fragment compaction in
+ *           mixed-precision training" -- sections "Total-usage monitoring
+ *           misses fragmentation" (free total, largest contiguous free block,
+ *           ratio free/largest - 1) and "Periodic compaction with Ascend C"
+ *           (mark live tensors; scan holes from low to high addresses and give
+ *           every live tensor its downward shift; move, then update every
+ *           reference in one batch).
+ *   [CANN]  "CANN memory management and memory optimisation: the NPU storage
+ *           hierarchy" -- section 2.2 (memory pool: 32-byte rounding, adjacent
+ *           free blocks merge into one), section 3.2 (fragmentation rate
+ *           1 - largest/free, defined as 0 when nothing is free) and section
+ *           3.3 (periodic compaction moves every allocated block into one
+ *           contiguous region, leaving one large free region).
+ *
+ * All byte quantities are unsigned 64-bit.  The table is structure-of-arrays:
+ * offset[n], size[n], live[n] (0/1), host memory, owned by the caller.
+ */
+#ifndef ARENA_COMPACTION_ORACLE_H
+#define ARENA_COMPACTION_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define ORACLE_OK 0
+#define ORACLE_EINVAL (-1)
+
+/* Which check rejected a table entry (first failing entry, first failing
+ * check in this order). */
+#define ORACLE_REASON_NONE 0
+#define ORACLE_REASON_ZERO_SIZE 1      /* size == 0                          */
+#define ORACLE_REASON_MISALIGNED 2     /* offset or size not a multiple of 32 */
+#define ORACLE_REASON_LIVE_FLAG 3      /* live not 0 or 1                     */
+#define ORACLE_REASON_OUT_OF_ARENA 4   /* offset + size > arena bytes         */
+#define ORACLE_REASON_OVERLAP 5        /* starts before the previous one ends */
+
+typedef struct oracle_stats {
+    uint64_t arena_bytes;
+    uint64_t live_bytes;
+    uint64_t free_bytes;
+    uint64_t largest_hole;
+    uint64_t hole_count;
+    uint64_t live_blocks;
+    uint64_t moved_blocks;
+    uint64_t moved_bytes;
+    double frag_free_over_largest_minus_1;   /* [910C] monitoring section */
+    double frag_one_minus_largest_over_free; /* [CANN] section 3.2        */
+} oracle_stats;
+
+/* Validate a table; on failure set *bad_index and *reason. */
+int oracle_validate(const uint64_t *offset, const uint64_t *size,
+                    const uint8_t *live, uint64_t n, uint64_t arena_bytes,
+                    uint64_t *bad_index, int32_t *reason);
+
+/* new_offset[i] = total size of the live entries before i. */
+void oracle_new_offsets(const uint64_t *offset, const uint64_t *size,
+                        const uint8_t *live, uint64_t n, uint64_t *new_offset);
+
+/* Ordered in-place compaction of a host arena: live blocks, lowest first,
+ * memmove'd to their new offsets. */
+void oracle_compact(uint8_t *arena, uint64_t arena_bytes,
+                    const uint64_t *offset, const uint64_t *size,
+                    const uint8_t *live, uint64_t n);
+
+/* Free total, holes and ratios by one low-to-high walk. */
+void oracle_stats_walk(const uint64_t *offset, const uint64_t *size,
+                       const uint8_t *live, uint64_t n, uint64_t arena_bytes,
+                       oracle_stats *out);
+
+/* Address of every handle after compaction, UINT64_MAX if the handle is not
+ * inside a live block; *n_invalid counts the latter.  h_out may equal h_in. */
+void oracle_remap(const uint64_t *offset, const uint64_t *size,
+                  const uint8_t *live, uint64_t n, const uint64_t *h_in,
+                  uint64_t *h_out, uint64_t n_handles, uint64_t *n_invalid);
+
+/* Where each byte of the compacted arena window [p0, p0+len) came from in the
+ * original arena, as segments (dst, src, len), ascending.  Returns the number
+ * of segments, or -1 if more than cap are needed.  Bytes at or above the live
+ * total keep their original value, so their src equals their dst. */
+int64_t oracle_source_map(const uint64_t *offset, const uint64_t *size,
+                          const uint8_t *live, uint64_t n, uint64_t arena_bytes,
+                          uint64_t p0, uint64_t len, uint64_t *seg_dst,
+                          uint64_t *seg_src, uint64_t *seg_len, uint64_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif
