@@ -1,0 +1,219 @@
+"""Python binding for libarena_compaction.so (gfx950).
+
+Argument marshalling only: every step of the compaction runs in the HIP
+kernels behind the C-ABI declared in include/arena_compaction.h.  PyTorch is
+used for device memory and streams.  Importing this module fails loudly if
+the library has not been built -- there is no CPU fallback.
+
+Tables are torch tensors on the GPU: offset and size as int64 holding the
+unsigned 64-bit values, live as uint8 (or None: every entry live).  Handles
+and new offsets are int64 tensors holding unsigned values; an unmapped handle
+reads back as -1 (UINT64_MAX).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libarena_compaction.so")
+
+DEFRAG_OK = 0
+DEFRAG_EINVAL = -1
+DEFRAG_EWORKSPACE = -2
+DEFRAG_ENOPLAN = -3
+DEFRAG_EHIP = -4
+DEFRAG_ETIMEOUT = -5
+REASONS = {0: "none", 1: "zero_size", 2: "misaligned", 3: "live_flag",
+           4: "out_of_arena", 5: "overlap", 6: "argument"}
+U64_MAX = (1 << 64) - 1
+
+
+class defrag_table(ctypes.Structure):
+    _fields_ = [("offset_dev", ctypes.c_void_p), ("size_dev", ctypes.c_void_p),
+                ("live_dev", ctypes.c_void_p), ("n", ctypes.c_uint64)]
+
+
+class defrag_stats_t(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_uint64) for k in (
+        "arena_bytes", "live_bytes", "free_bytes", "largest_hole", "hole_count",
+        "live_blocks", "moved_blocks", "moved_bytes")] + [
+        ("frag_free_over_largest_minus_1", ctypes.c_double),
+        ("frag_one_minus_largest_over_free", ctypes.c_double),
+        ("invalid_index", ctypes.c_uint64), ("invalid_reason", ctypes.c_int32),
+        ("reserved", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {k: getattr(self, k) for k, _ in self._fields_ if k != "reserved"}
+
+
+class defrag_tuning(ctypes.Structure):
+    _fields_ = [("tile_bytes", ctypes.c_uint32), ("wg_per_cu", ctypes.c_uint32),
+                ("nontemporal", ctypes.c_uint32), ("spin_limit_log2", ctypes.c_uint32)]
+
+
+class defrag_plan_t(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint64), ("epoch", ctypes.c_uint64),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
+                ("n", ctypes.c_uint64), ("arena_bytes", ctypes.c_uint64),
+                ("live_blocks", ctypes.c_uint64), ("first_moved", ctypes.c_uint64),
+                ("move_begin", ctypes.c_uint64), ("live_bytes", ctypes.c_uint64),
+                ("n_tiles", ctypes.c_uint64), ("max_blocks_per_tile", ctypes.c_uint64),
+                ("state", ctypes.c_int32), ("device", ctypes.c_int32),
+                ("tuning", defrag_tuning), ("stats", defrag_stats_t)]
+
+
+class DefragError(RuntimeError):
+    def __init__(self, code: int, what: str, stats: Optional[defrag_stats_t] = None):
+        self.code = code
+        self.invalid_index = None
+        self.invalid_reason = None
+        msg = f"{what}: {strerror(code)} ({code})"
+        if stats is not None and stats.invalid_reason:
+            self.invalid_index = int(stats.invalid_index)
+            self.invalid_reason = int(stats.invalid_reason)
+            msg += f"; entry {self.invalid_index}: {REASONS.get(self.invalid_reason, '?')}"
+        super().__init__(msg)
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; "
+            "g.build()'); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    P, U, S = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_size_t
+    L.defrag_workspace_bytes.argtypes = [U, U, ctypes.c_uint32]
+    L.defrag_workspace_bytes.restype = S
+    L.defrag_stats.argtypes = [ctypes.POINTER(defrag_table), U, P, S, P,
+                               ctypes.POINTER(defrag_stats_t)]
+    L.defrag_plan.argtypes = [ctypes.POINTER(defrag_table), U, ctypes.POINTER(defrag_tuning),
+                              P, S, P, P, ctypes.POINTER(defrag_plan_t)]
+    L.defrag_move.argtypes = [P, U, ctypes.POINTER(defrag_plan_t), P, S, P]
+    L.defrag_move_status.argtypes = [ctypes.POINTER(defrag_plan_t), P, P]
+    L.defrag_remap.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, U, P, P]
+    L.defrag_commit.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, P, P]
+    L.defrag_strerror.argtypes = [ctypes.c_int]
+    L.defrag_strerror.restype = ctypes.c_char_p
+    for f in ("defrag_stats", "defrag_plan", "defrag_move", "defrag_move_status",
+              "defrag_remap", "defrag_commit"):
+        getattr(L, f).restype = ctypes.c_int
+    return L
+
+
+lib = _load()
+
+EXPORTS = ("defrag_workspace_bytes", "defrag_stats", "defrag_plan", "defrag_move",
+           "defrag_move_status", "defrag_remap", "defrag_commit", "defrag_strerror")
+
+
+def strerror(code: int) -> str:
+    return lib.defrag_strerror(int(code)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous CUDA/HIP tensors"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_table(offset: torch.Tensor, size: torch.Tensor,
+               live: Optional[torch.Tensor]) -> defrag_table:
+    n = offset.numel()
+    assert offset.dtype == torch.int64 and size.dtype == torch.int64 and size.numel() == n
+    if live is not None:
+        assert live.dtype == torch.uint8 and live.numel() == n
+    return defrag_table(_ptr(offset) if n else None, _ptr(size) if n else None,
+                        _ptr(live) if (live is not None and n) else None, n)
+
+
+def defrag_workspace_bytes(n: int, arena_bytes: int, tile_bytes: int = 0) -> int:
+    return int(lib.defrag_workspace_bytes(n, arena_bytes, tile_bytes))
+
+
+def workspace(n: int, arena_bytes: int, tile_bytes: int = 0, device=None) -> torch.Tensor:
+    """Allocate a workspace tensor (torch allocations are 256-byte aligned)."""
+    nb = defrag_workspace_bytes(n, arena_bytes, tile_bytes)
+    if nb == 0:
+        raise DefragError(DEFRAG_EINVAL, "defrag_workspace_bytes")
+    return torch.empty(nb, dtype=torch.uint8, device=device or "cuda")
+
+
+def defrag_stats(offset, size, live, arena_bytes: int, ws: torch.Tensor,
+                 stream=None) -> defrag_stats_t:
+    t = make_table(offset, size, live)
+    out = defrag_stats_t()
+    rc = lib.defrag_stats(ctypes.byref(t), arena_bytes, _ptr(ws), ws.numel(), _stream(stream),
+                          ctypes.byref(out))
+    if rc != DEFRAG_OK:
+        raise DefragError(rc, "defrag_stats", out)
+    return out
+
+
+def defrag_plan(offset, size, live, arena_bytes: int, ws: torch.Tensor,
+                new_offset: Optional[torch.Tensor] = None,
+                tuning: Optional[defrag_tuning] = None, stream=None) -> defrag_plan_t:
+    t = make_table(offset, size, live)
+    plan = defrag_plan_t()
+    if new_offset is not None:
+        assert new_offset.dtype == torch.int64 and new_offset.numel() >= offset.numel()
+    rc = lib.defrag_plan(ctypes.byref(t), arena_bytes,
+                         ctypes.byref(tuning) if tuning is not None else None,
+                         _ptr(ws), ws.numel(), _stream(stream),
+                         _ptr(new_offset) if new_offset is not None and new_offset.numel() else None,
+                         ctypes.byref(plan))
+    if rc != DEFRAG_OK:
+        raise DefragError(rc, "defrag_plan", plan.stats)
+    return plan
+
+
+def defrag_move(arena: torch.Tensor, plan: defrag_plan_t, ws: torch.Tensor, stream=None) -> None:
+    assert arena.dtype == torch.uint8
+    rc = lib.defrag_move(_ptr(arena) if arena.numel() else None, arena.numel(),
+                         ctypes.byref(plan), _ptr(ws), ws.numel(), _stream(stream))
+    if rc != DEFRAG_OK:
+        raise DefragError(rc, "defrag_move")
+
+
+def defrag_move_status(plan: defrag_plan_t, ws: torch.Tensor, stream=None) -> int:
+    return int(lib.defrag_move_status(ctypes.byref(plan), _ptr(ws), _stream(stream)))
+
+
+def defrag_remap(plan: defrag_plan_t, ws: torch.Tensor, h_in: torch.Tensor,
+                 h_out: Optional[torch.Tensor] = None,
+                 n_invalid: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    assert h_in.dtype == torch.int64
+    if h_out is None:
+        h_out = torch.empty_like(h_in)
+    if n_invalid is not None:
+        assert n_invalid.dtype == torch.int64 and n_invalid.numel() >= 1
+    H = h_in.numel()
+    rc = lib.defrag_remap(ctypes.byref(plan), _ptr(ws), ws.numel(),
+                          _ptr(h_in) if H else None, _ptr(h_out) if H else None, H,
+                          _ptr(n_invalid), _stream(stream))
+    if rc != DEFRAG_OK:
+        raise DefragError(rc, "defrag_remap")
+    return h_out
+
+
+def defrag_commit(plan: defrag_plan_t, ws: torch.Tensor, offset_out=None, size_out=None,
+                  live_out=None, stream=None) -> None:
+    rc = lib.defrag_commit(ctypes.byref(plan), _ptr(ws), ws.numel(), _ptr(offset_out),
+                           _ptr(size_out), _ptr(live_out), _stream(stream))
+    if rc != DEFRAG_OK:
+        raise DefragError(rc, "defrag_commit")
+
+
+def defrag_strerror(code: int) -> str:
+    return strerror(code)

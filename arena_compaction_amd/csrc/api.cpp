@@ -1,0 +1,305 @@
+// api.cpp -- the C-ABI entry points: argument checks, workspace layout,
+// kernel launches and error mapping.  All arithmetic on the table and the
+// arena runs in the kernels (plan.hip, move.hip, remap.hip); the host only
+// turns two integers into the two fragmentation ratios (IEEE binary64).
+#include <atomic>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/arena_compaction.h"
+#include "internal.h"
+
+using namespace ac;
+
+namespace {
+
+constexpr uint64_t kPlanMagic = 0x4e414c5047415244ull;  // "DRAGPLAN"
+
+std::atomic<uint64_t> g_epoch{0x9E3779B97F4A7C15ull};
+
+int num_cus_of(int dev) {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    if (dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lk(mu);
+    if (cache[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cache[dev] = v;
+    }
+    return cache[dev];
+}
+
+bool tile_ok(uint32_t t) { return t >= kMinTile && t <= kMaxTile && (t & (t - 1)) == 0; }
+
+int check_table(const defrag_table *t) {
+    if (!t) return DEFRAG_EINVAL;
+    if (t->n > DEFRAG_MAX_ENTRIES) return DEFRAG_EINVAL;
+    if (t->n && (!t->offset_dev || !t->size_dev)) return DEFRAG_EINVAL;
+    return DEFRAG_OK;
+}
+
+int check_ws(const void *ws, size_t ws_bytes, size_t need) {
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u)) return DEFRAG_EWORKSPACE;
+    if (ws_bytes < need) return DEFRAG_EWORKSPACE;
+    return DEFRAG_OK;
+}
+
+void arg_error(defrag_stats_t *o) {
+    if (!o) return;
+    std::memset(o, 0, sizeof(*o));
+    o->invalid_index = kNone;
+    o->invalid_reason = DEFRAG_REASON_ARGUMENT;
+}
+
+// Free total and largest hole -> the two ratios; 0 when nothing is free.
+void fill_stats(defrag_stats_t *o, const WsHeader &h, uint64_t arena_bytes) {
+    std::memset(o, 0, sizeof(*o));
+    o->arena_bytes = arena_bytes;
+    o->invalid_index = kNone;
+    o->invalid_reason = DEFRAG_REASON_NONE;
+    if (h.bad_key != kNone) {
+        o->invalid_index = h.bad_key >> 3;
+        o->invalid_reason = (int32_t)(h.bad_key & 7u);
+        return;
+    }
+    o->live_bytes = h.live_bytes;
+    o->free_bytes = arena_bytes - h.live_bytes;
+    o->largest_hole = h.largest_hole;
+    o->hole_count = h.hole_count;
+    o->live_blocks = h.live_blocks;
+    o->moved_blocks = h.moved_blocks;
+    o->moved_bytes = h.moved_bytes;
+    if (o->free_bytes == 0) {
+        o->frag_free_over_largest_minus_1 = 0.0;
+        o->frag_one_minus_largest_over_free = 0.0;
+    } else {
+        const double F = (double)o->free_bytes;
+        const double L = (double)o->largest_hole;
+        o->frag_free_over_largest_minus_1 = F / L - 1.0;
+        o->frag_one_minus_largest_over_free = 1.0 - L / F;
+    }
+}
+
+int read_header(WsHeader *out, const uint8_t *ws, const WsLayout &L, hipStream_t s) {
+    if (hipMemcpyAsync(out, ws + L.header, sizeof(WsHeader), hipMemcpyDeviceToHost, s) !=
+        hipSuccess)
+        return DEFRAG_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return DEFRAG_EHIP;
+    return DEFRAG_OK;
+}
+
+TableView view_of(const defrag_table *t) {
+    return TableView{t->offset_dev, t->size_dev, t->live_dev, t->n};
+}
+
+int current_device() {
+    int d = -1;
+    if (hipGetDevice(&d) != hipSuccess) return -1;
+    return d;
+}
+
+int check_plan(const defrag_plan_t *p, const void *ws, size_t ws_bytes) {
+    if (!p || p->magic != kPlanMagic || p->state < 1) return DEFRAG_ENOPLAN;
+    if (ws != p->workspace) return DEFRAG_ENOPLAN;
+    if (ws_bytes < p->workspace_bytes) return DEFRAG_EWORKSPACE;
+    if (current_device() != p->device) return DEFRAG_EINVAL;
+    return DEFRAG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t defrag_workspace_bytes(uint64_t n, uint64_t arena_bytes, uint32_t tile_bytes) {
+    const uint32_t T = tile_bytes ? tile_bytes : kDefaultTile;
+    if (!tile_ok(T) || n > DEFRAG_MAX_ENTRIES) return 0;
+    return ws_layout(n, arena_bytes, T).total;
+}
+
+int defrag_stats(const defrag_table *table, uint64_t arena_bytes, void *ws_dev, size_t ws_bytes,
+                 hipStream_t stream, defrag_stats_t *out_host) {
+    if (!out_host) return DEFRAG_EINVAL;
+    int rc = check_table(table);
+    if (rc) {
+        arg_error(out_host);
+        return rc;
+    }
+    const WsLayout L = ws_layout(table->n, arena_bytes, kDefaultTile);
+    rc = check_ws(ws_dev, ws_bytes, L.live_dst);  // the partial-result region only
+    if (rc) {
+        arg_error(out_host);
+        return rc;
+    }
+    uint8_t *ws = static_cast<uint8_t *>(ws_dev);
+    if (launch_scan(view_of(table), arena_bytes, ws, L, nullptr, false, 0, stream) != hipSuccess)
+        return DEFRAG_EHIP;
+    WsHeader h;
+    rc = read_header(&h, ws, L, stream);
+    if (rc) return rc;
+    fill_stats(out_host, h, arena_bytes);
+    return h.bad_key == kNone ? DEFRAG_OK : DEFRAG_EINVAL;
+}
+
+int defrag_plan(const defrag_table *table, uint64_t arena_bytes, const defrag_tuning *tuning,
+                void *ws_dev, size_t ws_bytes, hipStream_t stream, uint64_t *new_offset_dev,
+                defrag_plan_t *plan) {
+    if (!plan) return DEFRAG_EINVAL;
+    std::memset(plan, 0, sizeof(*plan));
+    defrag_tuning tu{};
+    if (tuning) tu = *tuning;
+    if (!tu.tile_bytes) tu.tile_bytes = kDefaultTile;
+    if (!tu.spin_limit_log2) tu.spin_limit_log2 = kDefaultSpinLog2;
+    if (!tile_ok(tu.tile_bytes) || tu.spin_limit_log2 > 40) {
+        arg_error(&plan->stats);
+        return DEFRAG_EINVAL;
+    }
+    int rc = check_table(table);
+    if (rc) {
+        arg_error(&plan->stats);
+        return rc;
+    }
+    const WsLayout L = ws_layout(table->n, arena_bytes, tu.tile_bytes);
+    rc = check_ws(ws_dev, ws_bytes, L.total);
+    if (rc) {
+        arg_error(&plan->stats);
+        return rc;
+    }
+    const int dev = current_device();
+    if (dev < 0) return DEFRAG_EHIP;
+    uint8_t *ws = static_cast<uint8_t *>(ws_dev);
+    const uint64_t epoch = g_epoch.fetch_add(0x9E3779B97F4A7C15ull) ^ reinterpret_cast<uintptr_t>(ws);
+    if (launch_scan(view_of(table), arena_bytes, ws, L, new_offset_dev, true, epoch, stream) !=
+        hipSuccess)
+        return DEFRAG_EHIP;
+    WsHeader h;
+    rc = read_header(&h, ws, L, stream);
+    if (rc) return rc;
+    fill_stats(&plan->stats, h, arena_bytes);
+    if (h.bad_key != kNone) return DEFRAG_EINVAL;
+
+    const uint64_t T = tu.tile_bytes;
+    plan->epoch = epoch;
+    plan->workspace = ws_dev;
+    plan->workspace_bytes = L.total;
+    plan->n = table->n;
+    plan->arena_bytes = arena_bytes;
+    plan->live_blocks = h.live_blocks;
+    plan->first_moved = h.first_moved;
+    plan->move_begin = h.move_begin;
+    plan->live_bytes = h.live_bytes;
+    plan->device = dev;
+    plan->tuning = tu;
+    uint64_t n_tiles = 0, base = 0;
+    if (h.move_begin < h.live_bytes) {
+        base = h.move_begin & ~(T - 1);
+        n_tiles = (h.live_bytes - base + T - 1) / T;
+    }
+    plan->n_tiles = n_tiles;
+    // blocks meeting one tile: at most T / (smallest live size) + 2
+    uint64_t mb = 1;
+    if (h.min_live_size != kNone && h.min_live_size) mb = T / h.min_live_size + 2;
+    if (mb > T / 32 + 2) mb = T / 32 + 2;
+    plan->max_blocks_per_tile = mb;
+    if (launch_tiles(ws, L, n_tiles, base, tu.tile_bytes, h.move_begin, h.live_bytes,
+                     h.first_moved, h.live_blocks, stream) != hipSuccess)
+        return DEFRAG_EHIP;
+    plan->magic = kPlanMagic;
+    plan->state = 1;
+    return DEFRAG_OK;
+}
+
+int defrag_move(void *arena_dev, uint64_t arena_bytes, defrag_plan_t *plan, void *ws_dev,
+                size_t ws_bytes, hipStream_t stream) {
+    int rc = check_plan(plan, ws_dev, ws_bytes);
+    if (rc) return rc;
+    if (plan->state != 1) return DEFRAG_ENOPLAN;
+    if (arena_bytes != plan->arena_bytes) return DEFRAG_EINVAL;
+    if (plan->n_tiles && (!arena_dev || (reinterpret_cast<uintptr_t>(arena_dev) & 15u)))
+        return DEFRAG_EINVAL;
+    plan->state = 2;
+    if (plan->n_tiles == 0) return DEFRAG_OK;
+    const int cus = num_cus_of(plan->device);
+    if (cus <= 0) return DEFRAG_EHIP;
+    const WsLayout L = ws_layout(plan->n, plan->arena_bytes, plan->tuning.tile_bytes);
+    uint8_t *ws = static_cast<uint8_t *>(ws_dev);
+    MoveArgs a{};
+    a.arena = static_cast<uint8_t *>(arena_dev);
+    a.live_dst = reinterpret_cast<const uint64_t *>(ws + L.live_dst);
+    a.live_src = reinterpret_cast<const uint64_t *>(ws + L.live_src);
+    a.tiles = reinterpret_cast<const TileRec *>(ws + L.tiles);
+    a.flags = reinterpret_cast<uint32_t *>(ws + L.flags);
+    a.hdr = reinterpret_cast<WsHeader *>(ws + L.header);
+    a.n_tiles = plan->n_tiles;
+    a.tile_base = plan->move_begin & ~((uint64_t)plan->tuning.tile_bytes - 1);
+    a.move_begin = plan->move_begin;
+    a.live_bytes = plan->live_bytes;
+    a.epoch = plan->epoch;
+    a.spin_limit = 1ull << plan->tuning.spin_limit_log2;
+    a.tile_bytes = plan->tuning.tile_bytes;
+    a.max_blocks = (uint32_t)plan->max_blocks_per_tile;
+    if (launch_move(a, plan->tuning.wg_per_cu, plan->tuning.nontemporal != 0, cus, stream) !=
+        hipSuccess)
+        return DEFRAG_EHIP;
+    return DEFRAG_OK;
+}
+
+int defrag_move_status(const defrag_plan_t *plan, const void *ws_dev, hipStream_t stream) {
+    int rc = check_plan(plan, ws_dev, plan ? plan->workspace_bytes : 0);
+    if (rc) return rc;
+    if (plan->state != 2) return DEFRAG_ENOPLAN;
+    if (plan->n_tiles == 0) {
+        return hipStreamSynchronize(stream) == hipSuccess ? DEFRAG_OK : DEFRAG_EHIP;
+    }
+    const WsLayout L = ws_layout(plan->n, plan->arena_bytes, plan->tuning.tile_bytes);
+    WsHeader h;
+    rc = read_header(&h, static_cast<const uint8_t *>(ws_dev), L, stream);
+    if (rc) return rc;
+    if (h.epoch != plan->epoch) return DEFRAG_ENOPLAN;
+    if (h.status & kStatusTimeout) return DEFRAG_ETIMEOUT;
+    return DEFRAG_OK;
+}
+
+int defrag_remap(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes,
+                 const uint64_t *h_in_dev, uint64_t *h_out_dev, uint64_t n_handles,
+                 uint64_t *n_invalid_dev, hipStream_t stream) {
+    int rc = check_plan(plan, ws_dev, ws_bytes);
+    if (rc) return rc;
+    if (n_handles && (!h_in_dev || !h_out_dev)) return DEFRAG_EINVAL;
+    const int cus = num_cus_of(plan->device);
+    if (cus <= 0) return DEFRAG_EHIP;
+    const WsLayout L = ws_layout(plan->n, plan->arena_bytes, plan->tuning.tile_bytes);
+    const uint8_t *ws = static_cast<const uint8_t *>(ws_dev);
+    if (launch_remap(reinterpret_cast<const uint64_t *>(ws + L.live_dst),
+                     reinterpret_cast<const uint64_t *>(ws + L.live_src), plan->live_blocks,
+                     h_in_dev, h_out_dev, n_handles, n_invalid_dev, cus, stream) != hipSuccess)
+        return DEFRAG_EHIP;
+    return DEFRAG_OK;
+}
+
+int defrag_commit(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes,
+                  uint64_t *offset_out_dev, uint64_t *size_out_dev, uint8_t *live_out_dev,
+                  hipStream_t stream) {
+    int rc = check_plan(plan, ws_dev, ws_bytes);
+    if (rc) return rc;
+    const WsLayout L = ws_layout(plan->n, plan->arena_bytes, plan->tuning.tile_bytes);
+    if (launch_commit(static_cast<const uint8_t *>(ws_dev), L, plan->live_blocks, offset_out_dev,
+                      size_out_dev, live_out_dev, stream) != hipSuccess)
+        return DEFRAG_EHIP;
+    return DEFRAG_OK;
+}
+
+const char *defrag_strerror(int code) {
+    switch (code) {
+        case DEFRAG_OK: return "ok";
+        case DEFRAG_EINVAL: return "invalid table or argument";
+        case DEFRAG_EWORKSPACE: return "workspace missing, misaligned or too small";
+        case DEFRAG_ENOPLAN: return "no matching plan for this workspace";
+        case DEFRAG_EHIP: return "HIP runtime error";
+        case DEFRAG_ETIMEOUT: return "mover wait timed out";
+        default: return "unknown error";
+    }
+}
+
+}  // extern "C"

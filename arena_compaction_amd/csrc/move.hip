@@ -1,0 +1,197 @@
+// move.hip -- the in-place block mover for gfx950.
+//
+// Page: "Ascend 910C cluster tuning: memory-fragment compaction in
+// mixed-precision training", section "Periodic compaction with Ascend C"
+// (move the live data toward low addresses); "CANN memory management and
+// memory optimisation", section 3.3 (periodic compaction gathers every
+// allocated block into one contiguous region) and section 1.2 (data movement
+// dominates and many small transfers cost far more than one large one -- so
+// this is one fused kernel over all blocks, not a copy per block).
+//
+// Result: for every destination byte p below the live total, arena[p] takes
+// the pre-move value of arena[p + shift(p)], where shift(p) is the downward
+// shift of the live block landing on p.  Destination positions are packed,
+// so the source position p + shift(p) rises strictly with p.
+//
+// Design.  The destination range [move_begin, LT) is cut into tiles of T
+// bytes aligned to T.  Workgroups claim tiles in ascending order from an
+// atomic ticket and, per tile:
+//   1. load every 16-byte source vector of the tile into VGPRs (reads never
+//      wait: a source byte can only be overwritten by the tile owning it as
+//      a destination, which is at or above this tile and waits for it);
+//   2. publish "sources read" for the tile;
+//   3. wait until every earlier tile whose source range overlaps this tile's
+//      destination has published (at most two tiles, found by the plan);
+//   4. store.
+// A wait only ever targets lower tickets, whose owners are running and whose
+// reads never wait, so the schedule cannot deadlock and does not depend on
+// how many workgroups are resident.  Self-overlap inside a tile is handled by
+// the workgroup barrier between steps 1 and 4, so a move whose shift is far
+// smaller than its size still runs in tile-sized waves spread over the whole
+// chip rather than shift-sized serial steps.  Blocks whose shift is zero lie
+// entirely below move_begin and are never touched; nothing at or above LT
+// is written.
+//
+// Vectors are 16 bytes: offsets and sizes are multiples of 32, so a vector
+// never straddles two blocks and both of its addresses are 16-byte aligned.
+// Per tile the kernel reads 16 B per live-block descriptor it needs (in LDS
+// only for tiles holding more than one block).
+#include "internal.h"
+
+namespace ac {
+namespace {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ v4u load16(const uint8_t *p) {
+    const v4u *q = reinterpret_cast<const v4u *>(p);
+    if constexpr (NT) return __builtin_nontemporal_load(q);
+    else return *q;
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(uint8_t *p, v4u v) {
+    v4u *q = reinterpret_cast<v4u *>(p);
+    if constexpr (NT) __builtin_nontemporal_store(v, q);
+    else *q = v;
+}
+
+template <int VPT, bool NT>
+__global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
+    extern __shared__ uint64_t lds_dyn[];
+    uint64_t *s_shift = lds_dyn;                                           // [max_blocks]
+    uint32_t *s_rel = reinterpret_cast<uint32_t *>(lds_dyn + a.max_blocks);  // [max_blocks]
+    __shared__ uint32_t s_ticket;
+    __shared__ uint32_t s_skip;
+    const uint32_t tid = threadIdx.x;
+
+    if (tid == 0) {
+        // a workspace re-planned since this plan: move nothing, write nothing
+        // (the status query sees the epoch mismatch)
+        uint32_t tk = 0xFFFFFFFFu;
+        if (__hip_atomic_load(&a.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch)
+            tk = atomicAdd(&a.hdr->ticket, 1u);
+        s_ticket = tk;
+    }
+    __syncthreads();
+    uint32_t t = s_ticket;
+
+    while (t < a.n_tiles) {
+        // claim the next tile now; its value is needed only at the loop end
+        uint32_t next = 0;
+        if (tid == 0) next = atomicAdd(&a.hdr->ticket, 1u);
+
+        const TileRec rec = a.tiles[t];
+        const uint64_t tb = a.tile_base + (uint64_t)t * a.tile_bytes;
+        const uint64_t t0 = tb > a.move_begin ? tb : a.move_begin;
+        const uint64_t te = tb + a.tile_bytes;
+        const uint64_t t1 = te < a.live_bytes ? te : a.live_bytes;
+        const uint32_t rel0 = (uint32_t)(t0 - tb);
+        const uint32_t rel1 = (uint32_t)(t1 - tb);
+        const uint32_t nblk = rec.last_block - rec.first_block + 1u;
+        bool ok = nblk <= a.max_blocks;
+
+        uint64_t shift0 = 0;
+        if (nblk == 1u) {
+            shift0 = a.live_src[rec.first_block] - a.live_dst[rec.first_block];
+        } else if (ok) {
+            for (uint32_t k = tid; k < nblk; k += kMoveThreads) {
+                const uint64_t d = a.live_dst[rec.first_block + k];
+                s_shift[k] = a.live_src[rec.first_block + k] - d;
+                s_rel[k] = d <= tb ? 0u : (uint32_t)(d - tb);
+            }
+            __syncthreads();
+        }
+
+        v4u v[VPT];
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const uint32_t r = ((uint32_t)j * kMoveThreads + tid) * 16u;
+            if (ok && r >= rel0 && r < rel1) {
+                uint64_t sh = shift0;
+                if (nblk > 1u) {
+                    uint32_t lo = 0, n = nblk;  // largest k with s_rel[k] <= r
+                    while (n > 1u) {
+                        const uint32_t half = n >> 1;
+                        lo = (s_rel[lo + half] <= r) ? lo + half : lo;
+                        n -= half;
+                    }
+                    sh = s_shift[lo];
+                }
+                v[j] = load16<NT>(a.arena + tb + r + sh);
+            }
+        }
+        // every load of this tile has returned before its flag is published
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t skip = ok ? 0u : 1u;
+            if (!ok) atomicOr(&a.hdr->status, kStatusTimeout);
+            __hip_atomic_store(&a.flags[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (uint32_t u = rec.dep_lo; u <= rec.dep_hi && !skip; ++u) {
+                uint64_t polls = 0;
+                while (__hip_atomic_load(&a.flags[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                    if (++polls > a.spin_limit) {
+                        skip = 1u;
+                        atomicOr(&a.hdr->status, kStatusTimeout);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            s_skip = skip;
+        }
+        __syncthreads();
+        if (!s_skip) {
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                const uint32_t r = ((uint32_t)j * kMoveThreads + tid) * 16u;
+                if (r >= rel0 && r < rel1) store16<NT>(a.arena + tb + r, v[j]);
+            }
+        }
+        if (tid == 0) s_ticket = next;
+        __syncthreads();
+        t = s_ticket;
+    }
+}
+
+template <int VPT, bool NT>
+hipError_t launch_t(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
+    const size_t lds = (size_t)a.max_blocks * 12u + 16u;
+    int occ = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_move<VPT, NT>,
+                                                                kMoveThreads, lds);
+    if (e != hipSuccess) return e;
+    if (occ < 1) occ = 1;
+    uint64_t per_cu = wg_per_cu ? wg_per_cu : (uint32_t)occ;
+    uint64_t grid = per_cu * (uint64_t)num_cus;
+    if (grid > a.n_tiles) grid = a.n_tiles;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((k_move<VPT, NT>), dim3((uint32_t)grid), dim3(kMoveThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+template <bool NT>
+hipError_t launch_nt(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
+    switch (a.tile_bytes <= kMoveRowBytes ? 1u : a.tile_bytes / kMoveRowBytes) {
+        case 1: return launch_t<1, NT>(a, wg_per_cu, num_cus, s);
+        case 2: return launch_t<2, NT>(a, wg_per_cu, num_cus, s);
+        case 4: return launch_t<4, NT>(a, wg_per_cu, num_cus, s);
+        case 8: return launch_t<8, NT>(a, wg_per_cu, num_cus, s);
+        case 16: return launch_t<16, NT>(a, wg_per_cu, num_cus, s);
+        case 32: return launch_t<32, NT>(a, wg_per_cu, num_cus, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, bool nontemporal, int num_cus,
+                       hipStream_t s) {
+    if (a.n_tiles == 0) return hipSuccess;
+    return nontemporal ? launch_nt<true>(a, wg_per_cu, num_cus, s)
+                       : launch_nt<false>(a, wg_per_cu, num_cus, s);
+}
+
+}  // namespace ac

@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark: in-place compaction of the 80 GiB config-3 arena on one MI355X.
+
+One step = the whole hot path on one fragmented arena:
+  plan   (validate, live-size scan, hole statistics, mover tile table)
+  move   (the in-place mover)
+  remap  (4,000,000 handles)
+  commit + statistics of the packed table (one top hole, ratios 0).
+Before every step the arena is refilled to its pristine fragmented content on
+the GPU; the refill sits outside the timed events (inputs resident in HBM when
+a step starts).  Each step is timed with HIP events on the stream the library
+launches on; the mover launch has its own event pair, which gives the
+roofline figure.
+
+Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak (8 TB/s)
+METRIC = "compaction GB/s moved (read+write) & % HBM peak; handles remapped/s"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "move_config3_traffic.json")
+
+
+def _mover_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("move.hip", "internal.h"):
+        with open(os.path.join(ROOT, "arena_compaction_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(moved_bytes: int):
+    """Measured HBM bytes per mover launch (rocprofv3 FETCH_SIZE + WRITE_SIZE,
+    scaled by a plain copy of known size), if taken on the current mover
+    source for this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("mover_source_hash") != _mover_source_hash() or t.get("moved_bytes") != moved_bytes:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(heap, budget_s: float = 12.0):
+    """The oracle, single-threaded, on a bounded slice of the same workload:
+    the entries of the config-3 table that lie in a 4 GiB window of its mixed
+    activation/small-block region, rebased to offset 0, with the handles that
+    fall inside it.  Times validate + new offsets + stats + ordered memmove +
+    remap, repeated (restoring the arena untimed) until the budget is spent."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads as W
+
+    lo_addr = 40 * W.GiB
+    hi_addr = 44 * W.GiB
+    off, size, live = heap.offset, heap.size, heap.live
+    i0 = int(np.searchsorted(off, lo_addr))
+    ends = off + size
+    i1 = int(np.searchsorted(ends, hi_addr, side="right"))
+    base = int(off[i0])
+    s_off = off[i0:i1] - np.uint64(base)
+    s_size = size[i0:i1].copy()
+    s_live = live[i0:i1].copy()
+    S = int(s_off[-1] + s_size[-1])
+    hs = heap.handles
+    hs = hs[(hs >= np.uint64(base)) & (hs < np.uint64(base + S))] - np.uint64(base)
+    pristine = torch.empty(S, dtype=torch.uint8)
+    W.fill_payload(pristine, base, heap.payload_mode, heap.payload_seed)
+    pristine = pristine.numpy()
+    arena = np.empty_like(pristine)
+    moved = oracle.stats(s_off, s_size, s_live, S).moved_bytes
+    reps, t_total = 0, 0.0
+    while t_total < budget_s and reps < 50:
+        np.copyto(arena, pristine)
+        t0 = time.perf_counter()
+        rc = oracle.validate(s_off, s_size, s_live, S)[0]
+        oracle.new_offsets(s_off, s_size, s_live)
+        oracle.stats(s_off, s_size, s_live, S)
+        oracle.compact(arena, s_off, s_size, s_live)
+        oracle.remap(s_off, s_size, s_live, hs)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        assert rc == oracle.OK
+    per = t_total / reps
+    return {
+        "value": round(2 * moved / per / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"config-3 entries {i0}..{i1 - 1} (the 4 GiB window at 40 GiB, "
+                   f"{i1 - i0} entries, {S} B arena, {moved} B moved, {hs.shape[0]} handles); "
+                   f"validate+plan+stats+memmove+remap, {reps} reps, {per * 1e3:.1f} ms each"),
+        "handles_per_s": round(hs.shape[0] / per, 1),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 is the headline)")
+    ap.add_argument("--tile", type=int, default=0)
+    ap.add_argument("--wg-per-cu", type=int, default=0)
+    ap.add_argument("--nontemporal", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; each GPU compacts "
+                                   "its own arena independently, so there is no multi-GPU step",
+                          "n_gpus": args.gpus}), flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+    import arena_compaction_amd as ac
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.time()
+    heap = W.config(args.config)
+    S = heap.arena_bytes
+    off = torch.from_numpy(heap.offset.view(np.int64)).to(dev)
+    size = torch.from_numpy(heap.size.view(np.int64)).to(dev)
+    live = torch.from_numpy(heap.live).to(dev)
+    h_in = torch.from_numpy(heap.handles.view(np.int64)).to(dev)
+    h_out = torch.empty_like(h_in)
+    n_bad = torch.zeros(1, dtype=torch.int64, device=dev)
+    arena = torch.empty(S, dtype=torch.uint8, device=dev)
+    tuning = ac.defrag_tuning(args.tile, args.wg_per_cu, args.nontemporal, 0)
+    ws = ac.workspace(heap.n, S, args.tile, device=dev)
+    new_off = torch.empty(heap.n, dtype=torch.int64, device=dev)
+    m = int(heap.live.sum())
+    c_off = torch.empty(m, dtype=torch.int64, device=dev)
+    c_size = torch.empty(m, dtype=torch.int64, device=dev)
+    c_live = torch.empty(m, dtype=torch.uint8, device=dev)
+    W.fill_payload(arena, 0, heap.payload_mode, heap.payload_seed)
+    torch.cuda.synchronize()
+    print(f"# {heap.describe()} generated+filled in {time.time() - t_gen:.1f}s", file=sys.stderr,
+          flush=True)
+    stream = torch.cuda.current_stream()
+    refill_from = 0
+
+    def refill():
+        # bytes below the first destination are never written: refill the rest
+        a0 = (refill_from // 8) * 8
+        W.fill_payload(arena[a0:], a0, heap.payload_mode, heap.payload_seed)
+
+    def one_step():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        ev[0].record(stream)
+        plan = ac.defrag_plan(off, size, live, S, ws, new_off, tuning=tuning, stream=stream)
+        ev[1].record(stream)
+        ac.defrag_move(arena, plan, ws, stream=stream)
+        ev[2].record(stream)
+        ac.defrag_remap(plan, ws, h_in, h_out, n_bad, stream=stream)
+        ev[3].record(stream)
+        ac.defrag_commit(plan, ws, c_off, c_size, c_live, stream=stream)
+        post = ac.defrag_stats(c_off, c_size, c_live, S, ws, stream=stream)
+        ev[4].record(stream)
+        return plan, post, ev
+
+    for w in range(args.warmup):
+        refill()
+        torch.cuda.synchronize()
+        plan, post, ev = one_step()
+        assert ac.defrag_move_status(plan, ws) == ac.DEFRAG_OK
+        refill_from = int(plan.move_begin)
+        print(f"# warmup {w} done", file=sys.stderr, flush=True)
+
+    times = {"step": [], "plan": [], "move": [], "remap": [], "post": []}
+    torch.cuda.synchronize()
+    t_wall0 = time.time()
+    moved = None
+    for k in range(args.steps):
+        refill()
+        torch.cuda.synchronize()
+        plan, post, ev = one_step()
+        torch.cuda.synchronize()
+        st = ac.defrag_move_status(plan, ws)
+        assert st == ac.DEFRAG_OK, st
+        assert post.hole_count == (1 if post.free_bytes else 0)
+        assert post.frag_free_over_largest_minus_1 == 0.0
+        assert int(n_bad.item()) == 0
+        moved = int(plan.stats.moved_bytes)
+        times["step"].append(ev[0].elapsed_time(ev[4]))
+        times["plan"].append(ev[0].elapsed_time(ev[1]))
+        times["move"].append(ev[1].elapsed_time(ev[2]))
+        times["remap"].append(ev[2].elapsed_time(ev[3]))
+        times["post"].append(ev[3].elapsed_time(ev[4]))
+        print(f"# step {k}: step {times['step'][-1]:.3f} ms, move {times['move'][-1]:.3f} ms",
+              file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    wall = time.time() - t_wall0
+
+    mean = {k: float(np.mean(v)) for k, v in times.items()}
+    ms_step = mean["step"]
+    value = 2 * moved / (ms_step * 1e-3) / 1e9
+    move_gbps = 2 * moved / (mean["move"] * 1e-3) / 1e9
+    handles_per_s = heap.handles.shape[0] / (mean["remap"] * 1e-3)
+    traffic = _traffic(moved)
+    s0 = plan.stats
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"config{args.config}" + (
+                ": 80 GiB arena shaped like the 910C failure (40 pinned, 200 activation, "
+                "200k small blocks; 14 GiB free, free/largest-1 = 4.7), 4M handles"
+                if args.config == 3 else ""),
+            "arena_bytes": S, "entries": heap.n, "live_blocks": m,
+            "handles": int(heap.handles.shape[0]), "moved_bytes": moved,
+            "tile_bytes": int(plan.tuning.tile_bytes), "seed": heap.seed,
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "move_only_GBps": round(move_gbps, 2),
+        "move_pct_hbm_peak": round(100 * move_gbps / HBM_PEAK_GBPS, 2),
+        "handles_per_s": round(handles_per_s, 1),
+        "ms": {k: round(v, 4) for k, v in mean.items()},
+        "min_move_ms": round(float(np.min(times["move"])), 4),
+        "wall_s_incl_refill": round(wall, 3),
+        "before": {"free_bytes": int(s0.free_bytes), "largest_hole": int(s0.largest_hole),
+                   "hole_count": int(s0.hole_count),
+                   "frag_free_over_largest_minus_1": s0.frag_free_over_largest_minus_1,
+                   "frag_one_minus_largest_over_free": s0.frag_one_minus_largest_over_free},
+        "after": {"largest_hole": int(post.largest_hole), "hole_count": int(post.hole_count),
+                  "frag_free_over_largest_minus_1": post.frag_free_over_largest_minus_1},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_move (defrag_move)",
+            "achieved": round(move_gbps, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(move_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": 2 * moved,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(heap, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

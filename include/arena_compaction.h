@@ -1,0 +1,202 @@
+/*
+ * arena_compaction.h -- in-place compaction of a device-memory arena on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is the periodic compaction operator of the page "Ascend 910C
+ * cluster tuning: memory-fragment compaction in mixed-precision training"
+ * (section "Periodic compaction with Ascend C"): live tensors are known (the
+ * caller marks them), holes are scanned from low to high addresses and every
+ * live block gets its downward shift, the data moves, then every reference is
+ * updated in one batch.  The free-space measures are that page's section
+ * "Total-usage monitoring misses fragmentation" and section 3.2 of "CANN
+ * memory management and memory optimisation" (fragmentation rate); the
+ * post-state -- all allocated blocks contiguous, one large free region -- is
+ * the periodic compaction of that page's section 3.3.
+ *
+ * Model
+ *   arena   : caller-owned device bytes [0, S).
+ *   table   : n entries (offset, size, live), structure of arrays in device
+ *             memory, ascending by offset and non-overlapping.  Entries are
+ *             32-byte aligned and non-empty (the CANN pool rounds every
+ *             request up to 32 bytes, section 2.2; section 3.3 aligns to 32 or
+ *             64 bytes).  Bytes not covered by a live entry -- free entries,
+ *             untracked gaps, the tail -- are free; adjacent free bytes form
+ *             one hole (the CANN pool merges adjacent free blocks, 2.2).
+ *   result  : live blocks keep their order and are packed from offset 0:
+ *             new_offset[i] = sum of sizes of live entries before i, for every
+ *             entry (a free entry gets the value of the next live one).  Bytes
+ *             at or above the live total are never written.
+ *   handles : byte addresses in the arena.  A handle inside live block i maps
+ *             to new_offset[i] + (h - offset[i]); any other handle (in a hole,
+ *             at or past the arena end) maps to UINT64_MAX and is counted.
+ *
+ * Call order per compaction: defrag_plan -> defrag_move -> defrag_remap (any
+ * number of handle batches) -> defrag_commit (optional: the packed table).
+ * defrag_stats measures any table without planning.
+ *
+ * Ownership: the caller owns every buffer (arena, table, outputs, handles and
+ * the workspace).  The library allocates no device memory and never writes
+ * the table.  Its only process-wide state is a counter for plan epochs and a
+ * per-device cache of the compute-unit count.
+ *
+ * Concurrency: between defrag_plan and the end of defrag_move nothing else
+ * may read or write the arena, the table or the workspace (the 910C page runs
+ * compaction while the affected tensors pause reads and writes -- a global
+ * sync point).  Ordering is the stream's order; calls on distinct workspaces
+ * are independent.  Every pointer argument named "_dev" is device memory on
+ * the stream's device; "_host" is host memory.
+ *
+ * Errors: negative return codes below.  Validation runs inside defrag_plan /
+ * defrag_stats on the device before any output is written, so an invalid
+ * table moves no byte and leaves new_offset untouched.
+ */
+#ifndef ARENA_COMPACTION_H
+#define ARENA_COMPACTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DEFRAG_OK 0
+#define DEFRAG_EINVAL (-1)     /* bad table or argument                        */
+#define DEFRAG_EWORKSPACE (-2) /* workspace missing, misaligned or too small   */
+#define DEFRAG_ENOPLAN (-3)    /* move/remap/commit without a matching plan     */
+#define DEFRAG_EHIP (-4)       /* a HIP runtime call failed                    */
+#define DEFRAG_ETIMEOUT (-5)   /* mover watchdog expired (a wait never ended)  */
+
+/* Why a table was rejected: the first failing entry, and within it the first
+ * failing check in this order. */
+#define DEFRAG_REASON_NONE 0
+#define DEFRAG_REASON_ZERO_SIZE 1     /* size == 0                              */
+#define DEFRAG_REASON_MISALIGNED 2    /* offset or size not a multiple of 32    */
+#define DEFRAG_REASON_LIVE_FLAG 3     /* live is neither 0 nor 1                */
+#define DEFRAG_REASON_OUT_OF_ARENA 4  /* offset + size > arena bytes            */
+#define DEFRAG_REASON_OVERLAP 5       /* starts before the previous entry ends  */
+#define DEFRAG_REASON_ARGUMENT 6      /* a pointer or size argument (host side) */
+
+/* Largest supported table: entry indices are 32-bit inside the kernels. */
+#define DEFRAG_MAX_ENTRIES 0xFFFFFFF0ull
+
+typedef struct defrag_table {
+    const uint64_t *offset_dev; /* n byte offsets from the arena base          */
+    const uint64_t *size_dev;   /* n sizes in bytes                            */
+    const uint8_t *live_dev;    /* n flags 0/1; NULL means every entry is live */
+    uint64_t n;
+} defrag_table;
+
+typedef struct defrag_stats_t {
+    uint64_t arena_bytes;
+    uint64_t live_bytes;   /* sum of live sizes                              */
+    uint64_t free_bytes;   /* arena_bytes - live_bytes                       */
+    uint64_t largest_hole; /* longest run of bytes outside live blocks       */
+    uint64_t hole_count;   /* number of such runs                            */
+    uint64_t live_blocks;
+    uint64_t moved_blocks; /* live blocks whose new offset differs           */
+    uint64_t moved_bytes;  /* their total size                               */
+    /* free/largest - 1 (910C page, monitoring section); 0 when nothing free */
+    double frag_free_over_largest_minus_1;
+    /* 1 - largest/free (CANN page 3.2); 0 when nothing is free              */
+    double frag_one_minus_largest_over_free;
+    uint64_t invalid_index; /* first rejected entry, UINT64_MAX if valid     */
+    int32_t invalid_reason; /* DEFRAG_REASON_*                               */
+    int32_t reserved;
+} defrag_stats_t;
+
+/* Optional knobs; zero fields take the defaults. */
+typedef struct defrag_tuning {
+    uint32_t tile_bytes;      /* mover tile: power of two in [256, 131072];
+                                 default 65536.  Fixed at plan time.        */
+    uint32_t wg_per_cu;       /* mover workgroups per compute unit; default:
+                                 as many as the kernel's resources allow     */
+    uint32_t nontemporal;     /* 1: streaming (non-temporal) loads/stores     */
+    uint32_t spin_limit_log2; /* mover watchdog: a wait gives up after
+                                 2^x polls (default 22, a few seconds)       */
+} defrag_tuning;
+
+/* Filled by defrag_plan (host memory, caller-owned).  Treat as opaque except
+ * for .stats and the tuning fields wg_per_cu / nontemporal, which may be
+ * changed before defrag_move. */
+typedef struct defrag_plan_t {
+    uint64_t magic;
+    uint64_t epoch;
+    const void *workspace;
+    uint64_t workspace_bytes;
+    uint64_t n;
+    uint64_t arena_bytes;
+    uint64_t live_blocks;
+    uint64_t first_moved;  /* index among live blocks of the first one to move */
+    uint64_t move_begin;   /* lowest destination byte written by the move       */
+    uint64_t live_bytes;
+    uint64_t n_tiles;
+    uint64_t max_blocks_per_tile;
+    int32_t state;         /* 0 none/invalid, 1 planned, 2 moved               */
+    int32_t device;
+    defrag_tuning tuning;
+    defrag_stats_t stats;    /* of the table as planned (before the move)        */
+} defrag_plan_t;
+
+/* Workspace bytes needed for a table of n entries over an arena of
+ * arena_bytes with the given tile size (0 = default).  The workspace is
+ * device memory, 256-byte aligned, owned by the caller; any content. */
+size_t defrag_workspace_bytes(uint64_t n, uint64_t arena_bytes, uint32_t tile_bytes);
+
+/* Measure a table (910C monitoring: free total, largest contiguous free
+ * block, both ratios; CANN 3.2).  Validates the table; on DEFRAG_EINVAL
+ * out_host->invalid_index / invalid_reason say why.  Synchronises the
+ * stream.  Ratios are IEEE binary64 computed on the host from the integers:
+ * free/largest - 1 and 1 - largest/free, both 0 when free is 0. */
+int defrag_stats(const defrag_table *table, uint64_t arena_bytes, void *ws_dev,
+                 size_t ws_bytes, hipStream_t stream, defrag_stats_t *out_host);
+
+/* Plan a compaction (910C: scan holes low to high, give every live block its
+ * downward shift).  Validates, writes new_offset_dev[n] (may be NULL), fills
+ * *plan_host (including the stats of the table), and builds the mover's tile
+ * table in the workspace.  Synchronises once on a small header; the tile
+ * table build is left queued on the stream.  tuning may be NULL. */
+int defrag_plan(const defrag_table *table, uint64_t arena_bytes,
+                const defrag_tuning *tuning, void *ws_dev, size_t ws_bytes,
+                hipStream_t stream, uint64_t *new_offset_dev,
+                defrag_plan_t *plan_host);
+
+/* Move the live blocks (910C: move the data).  arena_dev must be 16-byte
+ * aligned and arena_bytes must equal the planned size.  Asynchronous; a plan
+ * is consumed by one move (DEFRAG_ENOPLAN on reuse).  The table is not read:
+ * everything comes from the plan's workspace. */
+int defrag_move(void *arena_dev, uint64_t arena_bytes, defrag_plan_t *plan_host,
+                void *ws_dev, size_t ws_bytes, hipStream_t stream);
+
+/* After defrag_move: synchronise the stream and report whether the move
+ * finished (DEFRAG_OK), or a wait timed out (DEFRAG_ETIMEOUT; the arena is
+ * then undefined) or the workspace no longer held this plan
+ * (DEFRAG_ENOPLAN; nothing moved). */
+int defrag_move_status(const defrag_plan_t *plan_host, const void *ws_dev,
+                       hipStream_t stream);
+
+/* Remap handles (910C: update every reference in one batch).  h_out_dev may
+ * equal h_in_dev.  *n_invalid_dev (may be NULL) receives the number of
+ * handles mapped to UINT64_MAX.  Needs a valid plan of the table the handles
+ * refer to (before or after the move).  Asynchronous. */
+int defrag_remap(const defrag_plan_t *plan_host, const void *ws_dev,
+                 size_t ws_bytes, const uint64_t *h_in_dev, uint64_t *h_out_dev,
+                 uint64_t n_handles, uint64_t *n_invalid_dev, hipStream_t stream);
+
+/* Write the packed table: the live_blocks entries (new offset, size, 1) in
+ * order.  Any output pointer may be NULL.  Asynchronous. */
+int defrag_commit(const defrag_plan_t *plan_host, const void *ws_dev,
+                  size_t ws_bytes, uint64_t *offset_out_dev,
+                  uint64_t *size_out_dev, uint8_t *live_out_dev,
+                  hipStream_t stream);
+
+/* Short text for a return code. */
+const char *defrag_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARENA_COMPACTION_H */

@@ -1,0 +1,158 @@
+"""Shared test plumbing: run a heap through the HIP path (C-ABI) and through
+the oracle, and compare.  Inputs come from workloads only; expected values
+come from the oracle only."""
+from __future__ import annotations
+
+import dataclasses
+import sys
+from typing import Optional
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as W
+
+U64_MAX = (1 << 64) - 1
+STAT_KEYS = ("arena_bytes", "live_bytes", "free_bytes", "largest_hole", "hole_count",
+             "live_blocks", "moved_blocks", "moved_bytes",
+             "frag_free_over_largest_minus_1", "frag_one_minus_largest_over_free")
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def u64_to_t(a: np.ndarray, dev) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint64).view(np.int64)).to(dev)
+
+
+def t_to_u64(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint64)
+
+
+@dataclasses.dataclass
+class GpuRun:
+    plan: object
+    new_off: np.ndarray
+    remapped: np.ndarray
+    n_invalid: int
+    post_stats: object
+    status: int
+    arena: Optional[torch.Tensor]   # device arena after the move (kept on device)
+    ws: torch.Tensor
+
+
+def device_table(heap: W.Heap, dev):
+    return (u64_to_t(heap.offset, dev), u64_to_t(heap.size, dev),
+            torch.from_numpy(heap.live).to(dev))
+
+
+def pristine_host(heap: W.Heap) -> torch.Tensor:
+    t = torch.empty(heap.arena_bytes, dtype=torch.uint8)
+    W.fill_payload(t, 0, heap.payload_mode, heap.payload_seed)
+    return t
+
+
+def run_gpu(heap: W.Heap, dev="cuda", tuning=None, arena: Optional[torch.Tensor] = None,
+            handles: Optional[np.ndarray] = None) -> GpuRun:
+    import arena_compaction_amd as ac
+    off, size, live = device_table(heap, dev)
+    ws = ac.workspace(heap.n, heap.arena_bytes,
+                      tuning.tile_bytes if tuning is not None else 0, device=dev)
+    new_off = torch.full((heap.n,), -7, dtype=torch.int64, device=dev)
+    plan = ac.defrag_plan(off, size, live, heap.arena_bytes, ws, new_off, tuning=tuning)
+    if arena is None:
+        arena = torch.empty(heap.arena_bytes, dtype=torch.uint8, device=dev)
+        W.fill_payload(arena, 0, heap.payload_mode, heap.payload_seed)
+    ac.defrag_move(arena, plan, ws)
+    status = ac.defrag_move_status(plan, ws)
+    hs = heap.handles if handles is None else handles
+    h = u64_to_t(hs, dev)
+    n_bad = torch.full((1,), -3, dtype=torch.int64, device=dev)
+    h_out = ac.defrag_remap(plan, ws, h, n_invalid=n_bad)
+    m = int(plan.live_blocks)
+    c_off = torch.empty(m, dtype=torch.int64, device=dev)
+    c_size = torch.empty(m, dtype=torch.int64, device=dev)
+    c_live = torch.zeros(m, dtype=torch.uint8, device=dev)
+    ac.defrag_commit(plan, ws, c_off, c_size, c_live)
+    post = ac.defrag_stats(c_off, c_size, c_live, heap.arena_bytes, ws)
+    torch.cuda.synchronize()
+    assert bool((c_live == 1).all()), "commit must mark every packed entry live"
+    return GpuRun(plan, t_to_u64(new_off), t_to_u64(h_out), int(n_bad.item()), post, status,
+                  arena, ws)
+
+
+def check_stats(got, want, what=""):
+    for k in STAT_KEYS:
+        g, w = getattr(got, k), getattr(want, k)
+        assert g == w, f"{what} stats.{k}: gpu {g} != oracle {w}"
+
+
+def check_tables_and_handles(heap: W.Heap, r: GpuRun, handles: Optional[np.ndarray] = None):
+    """new offsets, plan stats, remap, post-move stats: all bit-exact."""
+    want_new = oracle.new_offsets(heap.offset, heap.size, heap.live)
+    assert np.array_equal(r.new_off, want_new), "new offsets differ"
+    check_stats(r.plan.stats, oracle.stats(heap.offset, heap.size, heap.live, heap.arena_bytes),
+                "plan")
+    hs = heap.handles if handles is None else handles
+    want_h, want_bad = oracle.remap(heap.offset, heap.size, heap.live, hs)
+    assert np.array_equal(r.remapped, want_h), "remapped handles differ"
+    assert r.n_invalid == want_bad, (r.n_invalid, want_bad)
+    li = np.flatnonzero(heap.live)
+    post_want = oracle.stats(want_new[li], heap.size[li], np.ones(li.shape[0], np.uint8),
+                             heap.arena_bytes)
+    check_stats(r.post_stats, post_want, "post")
+
+
+def check_arena_full(heap: W.Heap, r: GpuRun, pristine: torch.Tensor):
+    """Whole arena against the oracle's ordered memmove of the same bytes."""
+    ref = pristine.numpy().copy()
+    oracle.compact(ref, heap.offset, heap.size, heap.live)
+    got = r.arena.cpu().numpy()
+    if not np.array_equal(got, ref):
+        bad = np.flatnonzero(got != ref)
+        raise AssertionError(f"arena differs at {bad.shape[0]} bytes, first {bad[:8].tolist()}")
+
+
+def sample_windows(heap: W.Heap, rng: np.random.Generator, n_random: int = 2048,
+                   win: int = 4096, per_block_cap: int = 4096):
+    """Windows (start, length) of the compacted arena to check: the first and
+    last bytes of (a sample of) every live block at its new place, random
+    windows below and above the live total, and the window across it."""
+    new = oracle.new_offsets(heap.offset, heap.size, heap.live)
+    li = np.flatnonzero(heap.live)
+    if li.shape[0] > per_block_cap:
+        li = np.sort(rng.choice(li, per_block_cap, replace=False))
+    lt = int((heap.size * heap.live).sum())
+    S = heap.arena_bytes
+    wins = []
+    for i in li.tolist():
+        a, s = int(new[i]), int(heap.size[i])
+        wins.append((a, min(win, s)))
+        wins.append((a + s - min(win, s), min(win, s)))
+    for p in rng.integers(0, max(S - win, 1), n_random).tolist():
+        p = (p // 16) * 16
+        wins.append((p, min(win, S - p)))
+    if lt > 0 and S > 0:
+        p = max(0, lt - win // 2)
+        wins.append((p, min(win, S - p)))
+    return wins
+
+
+def check_arena_sampled(heap: W.Heap, r: GpuRun, windows):
+    """Sampled windows against the oracle's per-byte source map applied to
+    the generator's pristine payload."""
+    for (p0, ln) in windows:
+        if ln <= 0:
+            continue
+        got = r.arena[p0:p0 + ln].cpu().numpy()
+        d, s, l = oracle.source_map(heap.offset, heap.size, heap.live, heap.arena_bytes, p0, ln)
+        want = np.empty(ln, dtype=np.uint8)
+        for dd, ss, ll in zip(d.tolist(), s.tolist(), l.tolist()):
+            want[dd - p0:dd - p0 + ll] = W.payload_window(ss, ll, heap.payload_mode,
+                                                          heap.payload_seed)
+        if not np.array_equal(got, want):
+            bad = np.flatnonzero(got != want)
+            raise AssertionError(f"window [{p0}, {p0 + ln}) differs at {bad[:8].tolist()}")

@@ -1,0 +1,98 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and answers the calls that need no GPU (sizes, error text, and
+argument errors caught on the host before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "arena_compaction.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(defrag_[a-z_]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    fns = _declared_functions()
+    for f in ("defrag_stats", "defrag_plan", "defrag_move", "defrag_remap",
+              "defrag_workspace_bytes", "defrag_strerror", "defrag_commit",
+              "defrag_move_status"):
+        assert f in fns, f
+
+
+def test_library_exports_every_declared_symbol():
+    import arena_compaction_amd as ac
+    lib = ctypes.CDLL(ac.LIB_PATH)
+    for f in _declared_functions():
+        assert hasattr(lib, f), f"{f} declared in the header but not exported"
+    assert set(_declared_functions()) == set(ac.EXPORTS)
+
+
+def test_strerror_and_codes():
+    import arena_compaction_amd as ac
+    assert ac.defrag_strerror(0) == "ok"
+    for c in (-1, -2, -3, -4, -5):
+        assert ac.defrag_strerror(c) not in ("ok", "unknown error")
+    assert ac.defrag_strerror(-99) == "unknown error"
+
+
+def test_workspace_bytes():
+    import arena_compaction_amd as ac
+    a = ac.defrag_workspace_bytes(0, 0)
+    assert a > 0 and a % 256 == 0
+    b = ac.defrag_workspace_bytes(4096, 64 << 20)
+    c = ac.defrag_workspace_bytes(8192, 64 << 20)
+    d = ac.defrag_workspace_bytes(4096, 64 << 20, 256)
+    assert a < b < c and b < d
+    # 80 GiB arena, 200k entries, default tiles: tens of MB, not GBs
+    big = ac.defrag_workspace_bytes(200_247, 80 << 30)
+    assert big < 64 << 20
+    for bad_tile in (100, 128, 3000, 262144):
+        assert ac.defrag_workspace_bytes(16, 4096, bad_tile) == 0
+
+
+def test_host_side_argument_errors_need_no_gpu():
+    import arena_compaction_amd as ac
+    L = ac.lib
+    plan = ac.defrag_plan_t()
+    # a zeroed plan is refused before any HIP call
+    assert L.defrag_move(None, 0, ctypes.byref(plan), None, 0, None) == ac.DEFRAG_ENOPLAN
+    assert L.defrag_remap(ctypes.byref(plan), None, 0, None, None, 0, None, None) == ac.DEFRAG_ENOPLAN
+    assert L.defrag_commit(ctypes.byref(plan), None, 0, None, None, None, None) == ac.DEFRAG_ENOPLAN
+    assert L.defrag_move_status(ctypes.byref(plan), None, None) == ac.DEFRAG_ENOPLAN
+    # missing table / output pointers
+    st = ac.defrag_stats_t()
+    assert L.defrag_stats(None, 0, None, 0, None, ctypes.byref(st)) == ac.DEFRAG_EINVAL
+    assert st.invalid_reason == 6
+    assert L.defrag_stats(None, 0, None, 0, None, None) == ac.DEFRAG_EINVAL
+    assert L.defrag_plan(None, 0, None, None, 0, None, None, None) == ac.DEFRAG_EINVAL
+    t = ac.defrag_table(None, None, None, 5)   # n > 0 with NULL arrays
+    assert L.defrag_plan(ctypes.byref(t), 4096, None, None, 0, None, None,
+                         ctypes.byref(plan)) == ac.DEFRAG_EINVAL
+    t = ac.defrag_table(None, None, None, 0)
+    # no workspace
+    assert L.defrag_plan(ctypes.byref(t), 4096, None, None, 0, None, None,
+                         ctypes.byref(plan)) == ac.DEFRAG_EWORKSPACE
+    # misaligned workspace pointer (never dereferenced: refused on the host)
+    assert L.defrag_stats(ctypes.byref(t), 4096, ctypes.c_void_p(0x1008), 1 << 20, None,
+                          ctypes.byref(st)) == ac.DEFRAG_EWORKSPACE
+    # bad tile size
+    tu = ac.defrag_tuning(100, 0, 0, 0)
+    assert L.defrag_plan(ctypes.byref(t), 4096, ctypes.byref(tu), ctypes.c_void_p(0x1000),
+                         1 << 20, None, None, ctypes.byref(plan)) == ac.DEFRAG_EINVAL
+
+
+def test_oracle_is_not_linked_into_the_product():
+    """The product library and binding never reference the oracle."""
+    pkg = os.path.join(ROOT, "arena_compaction_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f"{f} mentions the oracle"

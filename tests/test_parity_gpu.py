@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle,
+bit-exact on arena bytes, new offsets, remapped handles and statistics.
+
+Small cases compare every byte; the full-size workloads compare every byte
+where the host can hold the arena (configs 1, 2, 4) and otherwise sampled
+windows through the oracle's per-byte source map (configs 3, 5), always with
+full new offsets, statistics and handles.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from harness import (check_arena_full, check_arena_sampled, check_stats,
+                     check_tables_and_handles, device_table, log, pristine_host, run_gpu,
+                     sample_windows, t_to_u64, u64_to_t)
+
+pytestmark = pytest.mark.gpu
+
+TILES = (256, 4096, 65536, 131072)
+
+
+@pytest.fixture(scope="module")
+def ac():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import arena_compaction_amd
+    return arena_compaction_amd
+
+
+def _tuning(ac, tile=0, wg=0, nt=0):
+    return ac.defrag_tuning(tile, wg, nt, 0)
+
+
+def _full_check(heap, tuning=None, handles=None):
+    import arena_compaction_amd as ac
+    log(f"case {heap.describe()} tuning={None if tuning is None else (tuning.tile_bytes, tuning.wg_per_cu, tuning.nontemporal)}")
+    host = pristine_host(heap)
+    r = run_gpu(heap, tuning=tuning, arena=host.cuda(), handles=handles)
+    assert r.status == ac.DEFRAG_OK, r.status
+    check_tables_and_handles(heap, r, handles)
+    check_arena_full(heap, r, host)
+    return r
+
+
+def test_payload_generator_same_on_gpu(ac):
+    for mode, seed in (("hash", 0xC0FFEE03), ("counter32", 0x5EED0005)):
+        for base in (0, 8 << 30, (1 << 36) + 4096):
+            g = torch.empty(3 << 20, dtype=torch.uint8, device="cuda")
+            W.fill_payload(g, base, mode, seed, chunk_bytes=1 << 20)
+            c = torch.empty(3 << 20, dtype=torch.uint8)
+            W.fill_payload(c, base, mode, seed)
+            assert torch.equal(g.cpu(), c), (mode, base)
+
+
+def test_golden_cases_gpu(ac):
+    import json, os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                        "hand_worked.json")))["cases"]
+    for case in cases:
+        t = np.array(case["table"], dtype=np.uint64).reshape(-1, 3)
+        heap = W.table_from_lists(case["arena_bytes"], [tuple(x) for x in t[:, :2].tolist()],
+                                  t[:, 2].tolist(), case["handles"], name=case["name"])
+        for tile in (256, 65536):
+            r = _full_check(heap, _tuning(ac, tile))
+            assert r.new_off.tolist() == case["new_offset"]
+            want = [W.U64_MAX if v < 0 else v for v in case["remapped"]]
+            assert r.remapped.tolist() == want
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_random_tiny_heaps_gpu(ac, tile):
+    rng = np.random.default_rng(1000 + tile)
+    for k in range(25):
+        n = int(rng.integers(0, 60))
+        heap = W.tiny_heap(rng, n, sizes=(32, 64, 96, 160, 4096, 8192),
+                           gap_p=float(rng.choice([0.0, 0.3, 0.8])),
+                           live_p=float(rng.choice([0.2, 0.5, 0.9, 1.0])))
+        _full_check(heap, _tuning(ac, tile))
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("tile,nt", [(256, 0), (4096, 1), (65536, 0), (65536, 1), (131072, 0)])
+def test_small_configs_gpu(ac, k, tile, nt):
+    _full_check(W.config(k, small=True), _tuning(ac, tile, 0, nt))
+
+
+@pytest.mark.parametrize("k", [1, 4, 5])
+def test_one_workgroup_per_cu_and_tiny_tiles(ac, k):
+    """Fewer resident workgroups and many more tiles per workgroup: the
+    ticket order alone must keep the schedule correct."""
+    _full_check(W.config(k, small=True), _tuning(ac, 512, 1, 0))
+
+
+def test_tiny_shift_under_large_blocks(ac):
+    """One 32-byte hole under a 64 MiB block and a 4 KiB hole under the next:
+    every tile's source overlaps its own destination and its successor's."""
+    blocks = [(0, 32), (32, 64 << 20), ((64 << 20) + 32, 4096), ((64 << 20) + 4128, 32 << 20)]
+    heap = W.table_from_lists((64 << 20) + 4128 + (32 << 20) + 96, blocks, [0, 1, 0, 1],
+                              [33, 32 + 12345, (64 << 20) + 4128 + 7])
+    for tile in (256, 4096, 65536):
+        _full_check(heap, _tuning(ac, tile))
+
+
+def test_edge_cases_gpu(ac):
+    cases = [
+        W.table_from_lists(4096, [], [], [0, 5, 4096]),                    # n = 0
+        W.table_from_lists(0, [], [], [0]),                                # empty arena
+        W.table_from_lists(4096, [(0, 1024), (2048, 512)], [0, 0], [0, 2048]),  # all free
+        W.table_from_lists(2048, [(0, 1024), (1024, 1024)], [1, 1], [0, 2047]),  # all live, full
+        W.table_from_lists(4096, [(0, 1024), (1024, 1024)], [1, 1], [0, 2047, 2048]),  # no hole below
+        W.table_from_lists(4104, [(32, 4064)], [1], [32, 4095, 4096]),     # ragged 8-byte tail
+        W.table_from_lists(8192, [(4096, 32)], [1], [4096, 4127]),         # one tiny block, big shift
+    ]
+    for heap in cases:
+        for tile in (256, 65536):
+            r = _full_check(heap, _tuning(ac, tile),
+                            handles=np.concatenate([heap.handles,
+                                                    W.edge_handles(heap, np.random.default_rng(0), 8)]))
+            if heap.live.sum() == 0 or np.all(heap.offset == oracle.new_offsets(
+                    heap.offset, heap.size, heap.live)):
+                assert r.plan.n_tiles == 0
+
+
+def test_remap_in_place_and_batches(ac):
+    heap = W.config(2, small=True)
+    off, size, live = device_table(heap, "cuda")
+    ws = ac.workspace(heap.n, heap.arena_bytes)
+    plan = ac.defrag_plan(off, size, live, heap.arena_bytes, ws)
+    h = u64_to_t(heap.handles, "cuda")
+    bad = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ac.defrag_remap(plan, ws, h, h, bad)          # in place, before the move
+    want, wb = oracle.remap(heap.offset, heap.size, heap.live, heap.handles)
+    assert np.array_equal(t_to_u64(h), want) and int(bad) == wb
+    empty = torch.empty(0, dtype=torch.int64, device="cuda")
+    ac.defrag_remap(plan, ws, empty, empty, bad)
+    assert int(bad) == 0
+
+
+def test_invalid_tables_gpu(ac):
+    """Every validation reason, first failing entry wins, and nothing is
+    written: new offsets keep their sentinel, the arena keeps its bytes."""
+    U = (1 << 64) - 1
+    cases = [
+        ([(0, 0, 1)], 64), ([(0, 32, 1), (32, 0, 0)], 64), ([(16, 32, 1)], 64),
+        ([(0, 48, 1)], 64), ([(0, 32, 2)], 64), ([(0, 32, 1), (32, 64, 1)], 64),
+        ([(96, 32, 1)], 64), ([(0, 64, 1), (32, 32, 0)], 128), ([(64, 32, 1), (0, 32, 1)], 128),
+        ([(0, 32, 1), (64, 32, 0), (64, 0, 1)], 128), ([(0, 32, 1), (1 << 63, 1 << 63, 1)], 1 << 63),
+        ([(2**64 - 48, 32, 1)], U), ([(2**64 - 32, 32, 1)], U),
+    ]
+    rng = np.random.default_rng(5)
+    # a long valid table with one bad entry deep inside (crosses scan workgroups)
+    n = 50_000
+    size = np.full(n, 64, np.uint64)
+    off = np.arange(n, dtype=np.uint64) * np.uint64(64)
+    for bad_at, kind in ((40_000, "overlap"), (2047, "zero"), (2048, "align"), (n - 1, "oob")):
+        o, s = off.copy(), size.copy()
+        if kind == "overlap":
+            o[bad_at] -= np.uint64(32)
+        elif kind == "zero":
+            s[bad_at] = 0
+        elif kind == "align":
+            o[bad_at] += np.uint64(16)
+        else:
+            s[bad_at] = np.uint64(1 << 20)
+        cases.append((list(zip(o.tolist(), s.tolist(), rng.integers(0, 2, n).tolist())), n * 64))
+    for table, S in cases:
+        t = np.array(table, dtype=np.uint64)
+        o, s, l = t[:, 0].copy(), t[:, 1].copy(), t[:, 2].astype(np.uint8)
+        rc, bad, reason = oracle.validate(o, s, l, S)
+        assert rc == oracle.EINVAL
+        dev_o, dev_s, dev_l = u64_to_t(o, "cuda"), u64_to_t(s, "cuda"), torch.from_numpy(l).cuda()
+        # statistics need partial results only: their workspace ignores the arena size
+        ws = ac.workspace(len(table), 1 << 20)
+        with pytest.raises(ac.DefragError) as ei:
+            ac.defrag_stats(dev_o, dev_s, dev_l, S, ws)
+        assert ei.value.code == ac.DEFRAG_EINVAL
+        assert (ei.value.invalid_index, ei.value.invalid_reason) == (bad, reason)
+        if ac.defrag_workspace_bytes(len(table), S) > (256 << 20):
+            continue   # planning an arena this size needs a tile table this large
+        ws = ac.workspace(len(table), S)
+        new = torch.full((len(table),), -7, dtype=torch.int64, device="cuda")
+        with pytest.raises(ac.DefragError) as ei:
+            ac.defrag_plan(dev_o, dev_s, dev_l, S, ws, new)
+        assert ei.value.code == ac.DEFRAG_EINVAL
+        assert (ei.value.invalid_index, ei.value.invalid_reason) == (bad, reason)
+        assert bool((new == -7).all()), "new offsets written for an invalid table"
+
+
+def test_plan_protocol_errors(ac):
+    heap = W.config(1, small=True)
+    off, size, live = device_table(heap, "cuda")
+    S = heap.arena_bytes
+    ws = ac.workspace(heap.n, S)
+    arena = torch.empty(S, dtype=torch.uint8, device="cuda")
+    W.fill_payload(arena, 0, heap.payload_mode, heap.payload_seed)
+    before = arena.clone()
+    # workspace too small
+    small = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ac.DefragError) as ei:
+        ac.defrag_plan(off, size, live, S, small)
+    assert ei.value.code == ac.DEFRAG_EWORKSPACE
+    # a stale plan: the workspace was re-planned since -> the mover refuses
+    p1 = ac.defrag_plan(off, size, live, S, ws)
+    p2 = ac.defrag_plan(off, size, live, S, ws)
+    ac.defrag_move(arena, p1, ws)
+    assert ac.defrag_move_status(p1, ws) == ac.DEFRAG_ENOPLAN
+    torch.cuda.synchronize()
+    assert torch.equal(arena, before), "a stale plan moved bytes"
+    # wrong arena size
+    with pytest.raises(ac.DefragError) as ei:
+        ac.defrag_move(arena[:-32], p2, ws)
+    assert ei.value.code == ac.DEFRAG_EINVAL
+    # misaligned arena pointer
+    with pytest.raises(ac.DefragError) as ei:
+        big = torch.empty(S + 16, dtype=torch.uint8, device="cuda")
+        ac.defrag_move(big[8:8 + S], p2, ws)
+    assert ei.value.code == ac.DEFRAG_EINVAL
+    # the current plan moves once, then is consumed
+    ac.defrag_move(arena, p2, ws)
+    assert ac.defrag_move_status(p2, ws) == ac.DEFRAG_OK
+    with pytest.raises(ac.DefragError) as ei:
+        ac.defrag_move(arena, p2, ws)
+    assert ei.value.code == ac.DEFRAG_ENOPLAN
+    ref = before.cpu().numpy().copy()
+    oracle.compact(ref, heap.offset, heap.size, heap.live)
+    assert np.array_equal(arena.cpu().numpy(), ref)
+    # another workspace than the plan's
+    ws2 = ac.workspace(heap.n, S)
+    with pytest.raises(ac.DefragError) as ei:
+        ac.defrag_remap(p2, ws2, u64_to_t(heap.handles, "cuda"))
+    assert ei.value.code == ac.DEFRAG_ENOPLAN
+
+
+@pytest.mark.parametrize("k", [1, 2, 4])
+def test_full_size_configs_every_byte(ac, k):
+    heap = W.config(k)
+    _full_check(heap)
+
+
+@pytest.mark.parametrize("k", [3, 5])
+def test_full_size_configs_sampled(ac, k):
+    heap = W.config(k)
+    log(f"case {heap.describe()} (sampled bytes)")
+    r = run_gpu(heap)
+    assert r.status == ac.DEFRAG_OK
+    check_tables_and_handles(heap, r)
+    wins = sample_windows(heap, np.random.default_rng(k), n_random=1024)
+    check_arena_sampled(heap, r, wins)
+    if k == 3:
+        s = r.plan.stats
+        assert abs(s.frag_free_over_largest_minus_1 - 4.7) < 1e-3
+        assert r.post_stats.frag_free_over_largest_minus_1 == 0.0
+    del r
+    torch.cuda.empty_cache()

@@ -30,8 +30,11 @@ side), so both sides start from identical bytes by construction.
 """
 from __future__ import annotations
 
+import ctypes
 import dataclasses
 import math
+import os
+import subprocess
 from typing import Optional
 
 import numpy as np
@@ -81,13 +84,45 @@ def _splitmix64_words_(z: torch.Tensor, seed: int) -> torch.Tensor:
     return z
 
 
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_CLIB_PATH = os.path.join(_HERE, "libworkloads.so")
+_clib = None
+
+
+def build_host_generator(verbose: bool = False) -> str:
+    """Compile the C payload generator used for CPU buffers."""
+    cmd = ["gcc", "-O3", "-fopenmp", "-shared", "-fPIC", "-Wall", "-o",
+           _CLIB_PATH + ".tmp", os.path.join(_HERE, "payload.c")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(_CLIB_PATH + ".tmp", _CLIB_PATH)
+    return _CLIB_PATH
+
+
+def _host_lib():
+    global _clib
+    if _clib is None:
+        if not os.path.exists(_CLIB_PATH):
+            build_host_generator()
+        L = ctypes.CDLL(_CLIB_PATH)
+        L.wl_fill_hash.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
+                                   ctypes.c_uint64]
+        L.wl_fill_counter32.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
+                                        ctypes.c_uint32]
+        _clib = L
+    return _clib
+
+
 def fill_payload(dst: torch.Tensor, base_addr: int, mode: str, seed: int,
-                 chunk_bytes: int = 256 * MiB) -> None:
+                 chunk_bytes: int = 256 * MiB, use_torch: bool = False) -> None:
     """Write the pristine payload of arena bytes [base_addr, base_addr+len)
     into the 1-D uint8 tensor ``dst`` (CPU or GPU).
 
     ``base_addr`` and ``len(dst)`` must be multiples of 8 (hash) or 4
-    (counter32).  Works in chunks so temporaries stay bounded.
+    (counter32).  GPU tensors are filled with torch ops in bounded chunks;
+    CPU tensors with the equivalent C loop (``use_torch`` forces the torch
+    code on the CPU too, to pin the two against each other).
     """
     assert dst.dtype == torch.uint8 and dst.dim() == 1 and dst.is_contiguous()
     n = dst.numel()
@@ -100,6 +135,13 @@ def fill_payload(dst: torch.Tensor, base_addr: int, mode: str, seed: int,
     if base_addr % wb or n % wb:
         raise ValueError("payload window must be word aligned")
     if n == 0:
+        return
+    if not dst.is_cuda and not use_torch:
+        L = _host_lib()
+        if mode == "hash":
+            L.wl_fill_hash(dst.data_ptr(), base_addr // 8, n // 8, seed & U64_MAX)
+        else:
+            L.wl_fill_counter32(dst.data_ptr(), base_addr // 4, n // 4, seed & 0xFFFFFFFF)
         return
     dev = dst.device
     step = max(wb, (chunk_bytes // wb) * wb)
