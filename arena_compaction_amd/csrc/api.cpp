@@ -147,11 +147,11 @@ int defrag_plan(const defrag_table *table, uint64_t arena_bytes, const defrag_tu
                 defrag_plan_t *plan) {
     if (!plan) return DEFRAG_EINVAL;
     std::memset(plan, 0, sizeof(*plan));
-    defrag_tuning tu{};
+    defrag_tuning tu{0, kDefaultWgPerCu, kDefaultNontemporal, 0};
     if (tuning) tu = *tuning;
     if (!tu.tile_bytes) tu.tile_bytes = kDefaultTile;
     if (!tu.spin_limit_log2) tu.spin_limit_log2 = kDefaultSpinLog2;
-    if (!tile_ok(tu.tile_bytes) || tu.spin_limit_log2 > 40) {
+    if (!tile_ok(tu.tile_bytes) || tu.spin_limit_log2 > 40 || tu.nontemporal > 3) {
         arg_error(&plan->stats);
         return DEFRAG_EINVAL;
     }
@@ -216,6 +216,7 @@ int defrag_move(void *arena_dev, uint64_t arena_bytes, defrag_plan_t *plan, void
     if (rc) return rc;
     if (plan->state != 1) return DEFRAG_ENOPLAN;
     if (arena_bytes != plan->arena_bytes) return DEFRAG_EINVAL;
+    if (plan->tuning.nontemporal > 3) return DEFRAG_EINVAL;
     if (plan->n_tiles && (!arena_dev || (reinterpret_cast<uintptr_t>(arena_dev) & 15u)))
         return DEFRAG_EINVAL;
     plan->state = 2;
@@ -239,7 +240,7 @@ int defrag_move(void *arena_dev, uint64_t arena_bytes, defrag_plan_t *plan, void
     a.spin_limit = 1ull << plan->tuning.spin_limit_log2;
     a.tile_bytes = plan->tuning.tile_bytes;
     a.max_blocks = (uint32_t)plan->max_blocks_per_tile;
-    if (launch_move(a, plan->tuning.wg_per_cu, plan->tuning.nontemporal != 0, cus, stream) !=
+    if (launch_move(a, plan->tuning.wg_per_cu, plan->tuning.nontemporal, cus, stream) !=
         hipSuccess)
         return DEFRAG_EHIP;
     return DEFRAG_OK;

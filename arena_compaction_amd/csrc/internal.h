@@ -16,6 +16,8 @@ constexpr uint32_t kSpineThreads = 1024;        // single-workgroup passes
 constexpr uint32_t kMoveThreads = 256;          // mover workgroup
 constexpr uint32_t kMoveRowBytes = kMoveThreads * 16;  // one 16-B vector per lane
 constexpr uint32_t kDefaultTile = 65536;
+constexpr uint32_t kDefaultWgPerCu = 2;     // measured best on the 80 GiB workload
+constexpr uint32_t kDefaultNontemporal = 1; // streaming loads and stores
 constexpr uint32_t kMinTile = 256;
 constexpr uint32_t kMaxTile = 131072;
 constexpr uint32_t kDefaultSpinLog2 = 22;
@@ -134,7 +136,7 @@ struct MoveArgs {
     uint32_t tile_bytes;
     uint32_t max_blocks;  // LDS capacity in block descriptors
 };
-hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, bool nontemporal,
+hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, uint32_t nontemporal,
                        int num_cus, hipStream_t s);
 
 // ---- remap.hip ----

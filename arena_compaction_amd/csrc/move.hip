@@ -43,21 +43,24 @@ namespace {
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-template <bool NT>
+// Streaming hints: NT bit 0 marks loads, bit 1 marks stores non-temporal
+// (the moved bytes are touched once; keeping them out of L2 leaves it to the
+// tile table, descriptors and flags).
+template <int NT>
 __device__ __forceinline__ v4u load16(const uint8_t *p) {
     const v4u *q = reinterpret_cast<const v4u *>(p);
-    if constexpr (NT) return __builtin_nontemporal_load(q);
+    if constexpr ((NT & 1) != 0) return __builtin_nontemporal_load(q);
     else return *q;
 }
 
-template <bool NT>
+template <int NT>
 __device__ __forceinline__ void store16(uint8_t *p, v4u v) {
     v4u *q = reinterpret_cast<v4u *>(p);
-    if constexpr (NT) __builtin_nontemporal_store(v, q);
+    if constexpr ((NT & 2) != 0) __builtin_nontemporal_store(v, q);
     else *q = v;
 }
 
-template <int VPT, bool NT>
+template <int VPT, int NT>
 __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
     extern __shared__ uint64_t lds_dyn[];
     uint64_t *s_shift = lds_dyn;                                           // [max_blocks]
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
     }
 }
 
-template <int VPT, bool NT>
+template <int VPT, int NT>
 hipError_t launch_t(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
     const size_t lds = (size_t)a.max_blocks * 12u + 16u;
     int occ = 0;
@@ -172,7 +175,7 @@ hipError_t launch_t(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStrea
     return hipGetLastError();
 }
 
-template <bool NT>
+template <int NT>
 hipError_t launch_nt(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
     switch (a.tile_bytes <= kMoveRowBytes ? 1u : a.tile_bytes / kMoveRowBytes) {
         case 1: return launch_t<1, NT>(a, wg_per_cu, num_cus, s);
@@ -187,11 +190,16 @@ hipError_t launch_nt(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStre
 
 }  // namespace
 
-hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, bool nontemporal, int num_cus,
+hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, uint32_t nontemporal, int num_cus,
                        hipStream_t s) {
     if (a.n_tiles == 0) return hipSuccess;
-    return nontemporal ? launch_nt<true>(a, wg_per_cu, num_cus, s)
-                       : launch_nt<false>(a, wg_per_cu, num_cus, s);
+    switch (nontemporal) {
+        case 0: return launch_nt<0>(a, wg_per_cu, num_cus, s);
+        case 1: return launch_nt<3>(a, wg_per_cu, num_cus, s);
+        case 2: return launch_nt<1>(a, wg_per_cu, num_cus, s);
+        case 3: return launch_nt<2>(a, wg_per_cu, num_cus, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace ac

@@ -113,11 +113,14 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 is the headline)")
-    ap.add_argument("--tile", type=int, default=0)
-    ap.add_argument("--wg-per-cu", type=int, default=0)
-    ap.add_argument("--nontemporal", type=int, default=0)
+    ap.add_argument("--tile", type=int, default=None, help="override the mover tile bytes")
+    ap.add_argument("--wg-per-cu", type=int, default=None, help="override (0 = max occupancy)")
+    ap.add_argument("--nontemporal", type=int, default=None, help="override (0..3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="GIB",
+                    help="only run a plain device-to-device copy of GIB GiB (twice): the "
+                         "reference kernel that scales the HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -134,6 +137,15 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        nb = args.calibrate_copy << 30
+        a = torch.empty(nb, dtype=torch.uint8, device=dev)
+        b = torch.empty(nb, dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": nb, "copies": 2}), flush=True)
+        return 0
     t_gen = time.time()
     heap = W.config(args.config)
     S = heap.arena_bytes
@@ -144,8 +156,11 @@ def main() -> int:
     h_out = torch.empty_like(h_in)
     n_bad = torch.zeros(1, dtype=torch.int64, device=dev)
     arena = torch.empty(S, dtype=torch.uint8, device=dev)
-    tuning = ac.defrag_tuning(args.tile, args.wg_per_cu, args.nontemporal, 0)
-    ws = ac.workspace(heap.n, S, args.tile, device=dev)
+    tuning = None   # library defaults unless a knob is overridden
+    if args.tile is not None or args.wg_per_cu is not None or args.nontemporal is not None:
+        tuning = ac.defrag_tuning(args.tile or 0, 2 if args.wg_per_cu is None else args.wg_per_cu,
+                                  1 if args.nontemporal is None else args.nontemporal, 0)
+    ws = ac.workspace(heap.n, S, args.tile or 0, device=dev)
     new_off = torch.empty(heap.n, dtype=torch.int64, device=dev)
     m = int(heap.live.sum())
     c_off = torch.empty(m, dtype=torch.int64, device=dev)

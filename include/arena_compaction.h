@@ -107,13 +107,17 @@ typedef struct defrag_stats_t {
     int32_t reserved;
 } defrag_stats_t;
 
-/* Optional knobs; zero fields take the defaults. */
+/* Optional knobs.  Passing NULL takes the defaults (65536-byte tiles, two
+ * mover workgroups per compute unit, streaming loads and stores); in a
+ * struct passed explicitly, a zero tile size or spin limit takes its default
+ * and the other fields are taken as given. */
 typedef struct defrag_tuning {
-    uint32_t tile_bytes;      /* mover tile: power of two in [256, 131072];
-                                 default 65536.  Fixed at plan time.        */
-    uint32_t wg_per_cu;       /* mover workgroups per compute unit; default:
-                                 as many as the kernel's resources allow     */
-    uint32_t nontemporal;     /* 1: streaming (non-temporal) loads/stores     */
+    uint32_t tile_bytes;      /* mover tile: power of two in [256, 131072].
+                                 Fixed at plan time.                          */
+    uint32_t wg_per_cu;       /* mover workgroups per compute unit; 0 means as
+                                 many as the kernel's resources allow         */
+    uint32_t nontemporal;     /* streaming hints: 0 none, 1 loads and stores,
+                                 2 loads only, 3 stores only                 */
     uint32_t spin_limit_log2; /* mover watchdog: a wait gives up after
                                  2^x polls (default 22, a few seconds)       */
 } defrag_tuning;
