@@ -11,38 +11,59 @@
 //
 // One lane per handle, grid-stride.  The search runs over the plan's packed
 // live-block arrays (old offsets ascending, and new offsets whose successive
-// differences are the block sizes), so free entries never cost a probe.  The
-// search is branchless with a trip count fixed by the table size, so the 64
-// lanes of a wave step together.  HBM traffic is 16 B per handle; the probes
-// hit the top of the table, which stays in L2 and the Infinity Cache.
+// differences are the block sizes), so free entries never cost a probe.  A
+// plain binary search is bound by L2 transactions (every probe of every lane
+// is its own cache line), so the top levels run in LDS over a sample of the
+// old offsets and only the last few probe global memory.  HBM traffic is
+// 16 B per handle.
 #include "internal.h"
 
 namespace ac {
 namespace {
 
-__global__ __launch_bounds__(256) void k_remap(const uint64_t *__restrict__ live_dst,
-                                               const uint64_t *__restrict__ live_src, uint64_t m,
-                                               const uint64_t *h_in, uint64_t *h_out, uint64_t H,
-                                               unsigned long long *n_invalid) {
+constexpr uint32_t kRemapThreads = 256;
+constexpr uint32_t kSplitters = 4096;  // 32 KB of LDS per workgroup
+
+// Largest j in [lo, lo + n) with a[j] <= h, given a[lo] <= h (or j = lo).
+template <typename T>
+__device__ __forceinline__ uint64_t search_le(const T *a, uint64_t lo, uint64_t n, uint64_t h) {
+    while (n > 1) {
+        const uint64_t half = n >> 1;
+        lo = ((uint64_t)a[lo + half] <= h) ? lo + half : lo;
+        n -= half;
+    }
+    return lo;
+}
+
+// The top of each search runs in LDS over a sample of every step-th old
+// offset; the rest runs over one bucket of at most `step` offsets in global
+// memory (L2-resident).  For m <= kSplitters the sample is the whole array.
+// Searches are branchless with trip counts set by the sizes alone, so the
+// 64 lanes of a wave step together.
+__global__ __launch_bounds__(kRemapThreads) void k_remap(const uint64_t *__restrict__ live_dst,
+                                                         const uint64_t *__restrict__ live_src,
+                                                         uint64_t m, const uint64_t *h_in,
+                                                         uint64_t *h_out, uint64_t H,
+                                                         unsigned long long *n_invalid) {
+    __shared__ uint64_t sp[kSplitters];
+    const uint64_t step = (m + kSplitters - 1) / kSplitters;
+    const uint64_t ns = m ? (m + step - 1) / step : 0;
+    for (uint64_t i = threadIdx.x; i < ns; i += kRemapThreads) sp[i] = live_src[i * step];
+    __syncthreads();
     uint64_t bad = 0;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < H; k += stride) {
         const uint64_t h = h_in[k];
         uint64_t out = kNone;
-        if (m) {
-            // largest j with live_src[j] <= h (j = 0 when none; checked below)
-            uint64_t lo = 0, n = m;
-            while (n > 1) {
-                const uint64_t half = n >> 1;
-                lo = (live_src[lo + half] <= h) ? lo + half : lo;
-                n -= half;
-            }
-            const uint64_t src = live_src[lo];
-            if (src <= h) {
-                const uint64_t d = live_dst[lo];
-                const uint64_t size = live_dst[lo + 1] - d;
-                if (h - src < size) out = d + (h - src);
-            }
+        if (ns && sp[0] <= h) {
+            const uint64_t b = search_le(sp, 0, ns, h);
+            const uint64_t lo = b * step;
+            const uint64_t hi = (lo + step < m) ? lo + step : m;
+            const uint64_t j = search_le(live_src, lo, hi - lo, h);
+            const uint64_t src = live_src[j];
+            const uint64_t d = live_dst[j];
+            const uint64_t size = live_dst[j + 1] - d;
+            if (h - src < size) out = d + (h - src);
         }
         bad += (out == kNone) ? 1u : 0u;
         h_out[k] = out;
@@ -65,10 +86,11 @@ hipError_t launch_remap(const uint64_t *live_dst, const uint64_t *live_src, uint
                         uint64_t *n_invalid, int num_cus, hipStream_t s) {
     if (n_invalid) hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, n_invalid);
     if (n_handles == 0) return hipGetLastError();
-    uint64_t grid = (n_handles + 255) / 256;
-    const uint64_t cap = (uint64_t)num_cus * 16;
+    // persistent grid: every workgroup pays for loading the LDS sample once
+    uint64_t grid = (n_handles + kRemapThreads - 1) / kRemapThreads;
+    const uint64_t cap = (uint64_t)num_cus * 4;  // measured best of 4, 5 and 8 per CU
     if (grid > cap) grid = cap;
-    hipLaunchKernelGGL(k_remap, dim3((uint32_t)grid), dim3(256), 0, s, live_dst, live_src,
+    hipLaunchKernelGGL(k_remap, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s, live_dst, live_src,
                        live_blocks, h_in, h_out, n_handles,
                        reinterpret_cast<unsigned long long *>(n_invalid));
     return hipGetLastError();
