@@ -60,23 +60,42 @@ class Stats:
 _lib = None
 
 
+def _bind(path: str):
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    U = ctypes.c_uint64
+    L.oracle_validate.argtypes = [P, P, P, U, U, P, P]
+    L.oracle_validate.restype = ctypes.c_int
+    L.oracle_new_offsets.argtypes = [P, P, P, U, P]
+    L.oracle_compact.argtypes = [P, U, P, P, P, U]
+    L.oracle_stats_walk.argtypes = [P, P, P, U, U, P]
+    L.oracle_remap.argtypes = [P, P, P, U, P, P, U, P]
+    L.oracle_source_map.argtypes = [P, P, P, U, U, U, U, P, P, P, U]
+    L.oracle_source_map.restype = ctypes.c_int64
+    return L
+
+
+def swap_library(path: str):
+    """Load the oracle from another build (tests use it to check that the
+    pins reject deliberately broken copies).  Returns the previous handle;
+    pass it to restore_library."""
+    global _lib
+    prev = lib()
+    _lib = _bind(path)
+    return prev
+
+
+def restore_library(handle) -> None:
+    global _lib
+    _lib = handle
+
+
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             build()
-        L = ctypes.CDLL(LIB_PATH)
-        P = ctypes.c_void_p
-        U = ctypes.c_uint64
-        L.oracle_validate.argtypes = [P, P, P, U, U, P, P]
-        L.oracle_validate.restype = ctypes.c_int
-        L.oracle_new_offsets.argtypes = [P, P, P, U, P]
-        L.oracle_compact.argtypes = [P, U, P, P, P, U]
-        L.oracle_stats_walk.argtypes = [P, P, P, U, U, P]
-        L.oracle_remap.argtypes = [P, P, P, U, P, P, U, P]
-        L.oracle_source_map.argtypes = [P, P, P, U, U, U, U, P, P, P, U]
-        L.oracle_source_map.restype = ctypes.c_int64
-        _lib = L
+        _lib = _bind(LIB_PATH)
     return _lib
 
 

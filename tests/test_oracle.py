@@ -245,3 +245,30 @@ def test_empty_and_degenerate(oracle_lib):
     assert bad == 2 and out.tolist() == [U64_MAX, U64_MAX]
     d, s_, l = oracle.source_map(e, e, el, 4096, 100, 50)
     assert (d.tolist(), s_.tolist(), l.tolist()) == ([100], [100], [50])
+
+
+def _check_source_map_windows(heap, rng, n_windows=12):
+    """Any window of the source map equals that slice of the compacted arena
+    (windows start and end inside blocks, holes and the tail)."""
+    S = heap.arena_bytes
+    A = rng.integers(0, 256, S, dtype=np.uint8)
+    got = A.copy()
+    oracle.compact(got, heap.offset, heap.size, heap.live)
+    for _ in range(n_windows):
+        if S == 0:
+            break
+        p0 = int(rng.integers(0, S))
+        ln = int(rng.integers(1, S - p0 + 1))
+        d, s, l = oracle.source_map(heap.offset, heap.size, heap.live, S, p0, ln)
+        rebuilt = np.full(ln, -1, dtype=np.int16)
+        for dd, ss, ll in zip(d.tolist(), s.tolist(), l.tolist()):
+            rebuilt[dd - p0:dd - p0 + ll] = A[ss:ss + ll]
+        assert np.array_equal(rebuilt, got[p0:p0 + ln].astype(np.int16)), (p0, ln)
+
+
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(seed=st.integers(0, 2**32 - 1), n=st.integers(1, 30))
+def test_source_map_any_window(seed, n):
+    rng = np.random.default_rng(seed)
+    heap = W.tiny_heap(rng, n, sizes=(32, 64, 96, 160), gap_p=0.4, live_p=0.6)
+    _check_source_map_windows(heap, rng)
