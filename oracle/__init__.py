@@ -20,7 +20,7 @@ SOURCES = [os.path.join(HERE, "oracle.cpp")]
 OK = 0
 EINVAL = -1
 REASONS = {0: "none", 1: "zero_size", 2: "misaligned", 3: "live_flag",
-           4: "out_of_arena", 5: "overlap"}
+           4: "out_of_arena", 5: "overlap", 7: "pinned_flag"}
 U64_MAX = (1 << 64) - 1
 
 
@@ -64,13 +64,13 @@ def _bind(path: str):
     L = ctypes.CDLL(path)
     P = ctypes.c_void_p
     U = ctypes.c_uint64
-    L.oracle_validate.argtypes = [P, P, P, U, U, P, P]
+    L.oracle_validate.argtypes = [P, P, P, P, U, U, P, P]
     L.oracle_validate.restype = ctypes.c_int
-    L.oracle_new_offsets.argtypes = [P, P, P, U, P]
-    L.oracle_compact.argtypes = [P, U, P, P, P, U]
-    L.oracle_stats_walk.argtypes = [P, P, P, U, U, P]
-    L.oracle_remap.argtypes = [P, P, P, U, P, P, U, P]
-    L.oracle_source_map.argtypes = [P, P, P, U, U, U, U, P, P, P, U]
+    L.oracle_new_offsets.argtypes = [P, P, P, P, U, P]
+    L.oracle_compact.argtypes = [P, U, P, P, P, P, U]
+    L.oracle_stats_walk.argtypes = [P, P, P, P, U, U, P]
+    L.oracle_remap.argtypes = [P, P, P, P, U, P, P, U, P]
+    L.oracle_source_map.argtypes = [P, P, P, P, U, U, U, U, P, P, P, U]
     L.oracle_source_map.restype = ctypes.c_int64
     return L
 
@@ -93,73 +93,79 @@ def restore_library(handle) -> None:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        stale = (not os.path.exists(LIB_PATH) or
+                 any(os.path.getmtime(f) > os.path.getmtime(LIB_PATH)
+                     for f in SOURCES + [os.path.join(HERE, "oracle.h")]))
+        if stale:
             build()
         _lib = _bind(LIB_PATH)
     return _lib
 
 
-def _p(a: np.ndarray):
-    return a.ctypes.data_as(ctypes.c_void_p)
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _table(off, size, live):
+def _table(off, size, live, pinned=None):
     off = np.ascontiguousarray(off, dtype=np.uint64)
     size = np.ascontiguousarray(size, dtype=np.uint64)
     live = np.ascontiguousarray(live, dtype=np.uint8)
     assert off.shape == size.shape == live.shape
-    return off, size, live
+    if pinned is not None:
+        pinned = np.ascontiguousarray(pinned, dtype=np.uint8)
+        assert pinned.shape == off.shape
+    return off, size, live, pinned
 
 
-def validate(off, size, live, arena_bytes):
-    off, size, live = _table(off, size, live)
+def validate(off, size, live, arena_bytes, pinned=None):
+    off, size, live, pinned = _table(off, size, live, pinned)
     bad = ctypes.c_uint64()
     reason = ctypes.c_int32()
-    rc = lib().oracle_validate(_p(off), _p(size), _p(live), off.shape[0],
+    rc = lib().oracle_validate(_p(off), _p(size), _p(live), _p(pinned), off.shape[0],
                                arena_bytes, ctypes.byref(bad), ctypes.byref(reason))
     return rc, bad.value, reason.value
 
 
-def new_offsets(off, size, live):
-    off, size, live = _table(off, size, live)
+def new_offsets(off, size, live, pinned=None):
+    off, size, live, pinned = _table(off, size, live, pinned)
     out = np.empty(off.shape[0], dtype=np.uint64)
-    lib().oracle_new_offsets(_p(off), _p(size), _p(live), off.shape[0], _p(out))
+    lib().oracle_new_offsets(_p(off), _p(size), _p(live), _p(pinned), off.shape[0], _p(out))
     return out
 
 
-def compact(arena: np.ndarray, off, size, live):
+def compact(arena: np.ndarray, off, size, live, pinned=None):
     """In place on a host uint8 arena."""
     assert arena.dtype == np.uint8 and arena.flags["C_CONTIGUOUS"]
-    off, size, live = _table(off, size, live)
-    lib().oracle_compact(_p(arena), arena.shape[0], _p(off), _p(size), _p(live),
+    off, size, live, pinned = _table(off, size, live, pinned)
+    lib().oracle_compact(_p(arena), arena.shape[0], _p(off), _p(size), _p(live), _p(pinned),
                          off.shape[0])
 
 
-def stats(off, size, live, arena_bytes) -> Stats:
-    off, size, live = _table(off, size, live)
+def stats(off, size, live, arena_bytes, pinned=None) -> Stats:
+    off, size, live, pinned = _table(off, size, live, pinned)
     s = _Stats()
-    lib().oracle_stats_walk(_p(off), _p(size), _p(live), off.shape[0],
+    lib().oracle_stats_walk(_p(off), _p(size), _p(live), _p(pinned), off.shape[0],
                             arena_bytes, ctypes.byref(s))
     return Stats(*[getattr(s, f[0]) for f in _Stats._fields_])
 
 
-def remap(off, size, live, handles):
-    off, size, live = _table(off, size, live)
+def remap(off, size, live, handles, pinned=None):
+    off, size, live, pinned = _table(off, size, live, pinned)
     h = np.ascontiguousarray(handles, dtype=np.uint64)
     out = np.empty_like(h)
     bad = ctypes.c_uint64()
-    lib().oracle_remap(_p(off), _p(size), _p(live), off.shape[0], _p(h), _p(out),
+    lib().oracle_remap(_p(off), _p(size), _p(live), _p(pinned), off.shape[0], _p(h), _p(out),
                        h.shape[0], ctypes.byref(bad))
     return out, bad.value
 
 
-def source_map(off, size, live, arena_bytes, p0, length, cap=1 << 16):
-    off, size, live = _table(off, size, live)
+def source_map(off, size, live, arena_bytes, p0, length, cap=1 << 16, pinned=None):
+    off, size, live, pinned = _table(off, size, live, pinned)
     d = np.empty(cap, dtype=np.uint64)
     s = np.empty(cap, dtype=np.uint64)
     l = np.empty(cap, dtype=np.uint64)
-    k = lib().oracle_source_map(_p(off), _p(size), _p(live), off.shape[0],
+    k = lib().oracle_source_map(_p(off), _p(size), _p(live), _p(pinned), off.shape[0],
                                 arena_bytes, p0, length, _p(d), _p(s), _p(l), cap)
     if k < 0:
-        raise ValueError("source map needs more segments than cap")
+        raise ValueError("source map needs more pieces than cap")
     return d[:k].copy(), s[:k].copy(), l[:k].copy()

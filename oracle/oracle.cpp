@@ -10,22 +10,31 @@
 //    hole, as the CANN pool merges adjacent free blocks ([CANN] 2.2);
 //  * entries are 32-byte aligned and non-empty ([CANN] 2.2 rounds every
 //    request up to 32 bytes; 3.3 aligns allocations to 32 or 64 bytes);
-//  * compaction keeps block order and packs from arena offset 0 with no
-//    padding: every live block moves down by the total hole size below it
-//    ([910C] periodic compaction: holes scanned low to high, downward shift);
-//  * bytes at or above the live total keep whatever they held.
+//  * compaction keeps block order and packs each segment from its start with
+//    no padding: every movable live block moves down by the total hole size
+//    below it in its segment ([910C] periodic compaction: holes scanned low to
+//    high, downward shift); with nothing pinned the one segment starts at 0;
+//  * a pinned block ([910C] fixed-address parameter region) is live and stays;
+//  * bytes that no movable block lands on keep whatever they held.
 #include "oracle.h"
 
 #include <algorithm>
 #include <cstring>
+#include <vector>
+
+namespace {
+
+inline bool is_pinned(const uint8_t *pinned, uint64_t i) { return pinned && pinned[i]; }
+
+}  // namespace
 
 extern "C" {
 
 // Entry checks, lowest entry first; within an entry the checks run in the
-// order of the reason codes in oracle.h.
+// order documented in oracle.h.
 int oracle_validate(const uint64_t *offset, const uint64_t *size,
-                    const uint8_t *live, uint64_t n, uint64_t arena_bytes,
-                    uint64_t *bad_index, int32_t *reason) {
+                    const uint8_t *live, const uint8_t *pinned, uint64_t n,
+                    uint64_t arena_bytes, uint64_t *bad_index, int32_t *reason) {
     *bad_index = UINT64_MAX;
     *reason = ORACLE_REASON_NONE;
     for (uint64_t i = 0; i < n; ++i) {
@@ -36,6 +45,8 @@ int oracle_validate(const uint64_t *offset, const uint64_t *size,
             r = ORACLE_REASON_MISALIGNED;
         else if (live[i] > 1)
             r = ORACLE_REASON_LIVE_FLAG;
+        else if (pinned && (pinned[i] > 1 || (pinned[i] == 1 && live[i] == 0)))
+            r = ORACLE_REASON_PINNED_FLAG;
         else if (offset[i] > arena_bytes || size[i] > arena_bytes - offset[i])
             r = ORACLE_REASON_OUT_OF_ARENA;
         else if (i > 0 && offset[i - 1] + size[i - 1] > offset[i])
@@ -50,12 +61,18 @@ int oracle_validate(const uint64_t *offset, const uint64_t *size,
 }
 
 // [910C] periodic compaction: each live tensor moves toward low addresses by
-// the holes below it, so its new start is the bytes of live data below it.
+// the holes below it, so its new start is its segment's start plus the live
+// data below it in the segment.  A pinned block stays and starts a segment.
 void oracle_new_offsets(const uint64_t *offset, const uint64_t *size,
-                        const uint8_t *live, uint64_t n, uint64_t *new_offset) {
-    (void)offset;
+                        const uint8_t *live, const uint8_t *pinned, uint64_t n,
+                        uint64_t *new_offset) {
     uint64_t running = 0;
     for (uint64_t i = 0; i < n; ++i) {
+        if (is_pinned(pinned, i)) {
+            new_offset[i] = offset[i];
+            running = offset[i] + size[i];
+            continue;
+        }
         new_offset[i] = running;
         if (live[i]) running += size[i];
     }
@@ -63,14 +80,19 @@ void oracle_new_offsets(const uint64_t *offset, const uint64_t *size,
 
 // [910C] periodic compaction, "move the data"; [CANN] 3.3 periodic
 // compaction gathers every allocated block into one contiguous region.
-// Lowest block first: block i's destination can only overlap its own source
-// (memmove copes) and sources of lower blocks, which have already moved.
+// Lowest block first: block i's destination lies in its own segment and can
+// only overlap its own source (memmove copes) and sources of lower blocks,
+// which have already moved.
 void oracle_compact(uint8_t *arena, uint64_t arena_bytes,
                     const uint64_t *offset, const uint64_t *size,
-                    const uint8_t *live, uint64_t n) {
+                    const uint8_t *live, const uint8_t *pinned, uint64_t n) {
     (void)arena_bytes;
     uint64_t dst = 0;
     for (uint64_t i = 0; i < n; ++i) {
+        if (is_pinned(pinned, i)) {
+            dst = offset[i] + size[i];
+            continue;
+        }
         if (!live[i]) continue;
         if (dst != offset[i])
             std::memmove(arena + dst, arena + offset[i], size[i]);
@@ -83,12 +105,12 @@ void oracle_compact(uint8_t *arena, uint64_t arena_bytes,
 // free (the same rule is taken for the first ratio).  [CANN] 2.2: adjacent
 // free blocks merge, so a hole is the whole gap between two live blocks.
 void oracle_stats_walk(const uint64_t *offset, const uint64_t *size,
-                       const uint8_t *live, uint64_t n, uint64_t arena_bytes,
-                       oracle_stats *out) {
+                       const uint8_t *live, const uint8_t *pinned, uint64_t n,
+                       uint64_t arena_bytes, oracle_stats *out) {
     std::memset(out, 0, sizeof(*out));
     out->arena_bytes = arena_bytes;
     uint64_t cursor = 0;   // end of the last live block seen so far
-    uint64_t new_off = 0;  // where the current live block would land
+    uint64_t new_off = 0;  // where the current movable block would land
     for (uint64_t i = 0; i < n; ++i) {
         if (!live[i]) continue;
         const uint64_t gap = offset[i] - cursor;
@@ -98,11 +120,15 @@ void oracle_stats_walk(const uint64_t *offset, const uint64_t *size,
         }
         out->live_blocks += 1;
         out->live_bytes += size[i];
-        if (offset[i] != new_off) {
-            out->moved_blocks += 1;
-            out->moved_bytes += size[i];
+        if (is_pinned(pinned, i)) {
+            new_off = offset[i] + size[i];
+        } else {
+            if (offset[i] != new_off) {
+                out->moved_blocks += 1;
+                out->moved_bytes += size[i];
+            }
+            new_off += size[i];
         }
-        new_off += size[i];
         cursor = offset[i] + size[i];
     }
     const uint64_t tail = arena_bytes - cursor;
@@ -127,10 +153,11 @@ void oracle_stats_walk(const uint64_t *offset, const uint64_t *size,
 // tensor addresses, references are kept at operator level -- here a handle is
 // a byte address in the arena; it keeps its offset inside its block.
 void oracle_remap(const uint64_t *offset, const uint64_t *size,
-                  const uint8_t *live, uint64_t n, const uint64_t *h_in,
-                  uint64_t *h_out, uint64_t n_handles, uint64_t *n_invalid) {
-    uint64_t *new_off = new uint64_t[n ? n : 1];
-    oracle_new_offsets(offset, size, live, n, new_off);
+                  const uint8_t *live, const uint8_t *pinned, uint64_t n,
+                  const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
+                  uint64_t *n_invalid) {
+    std::vector<uint64_t> new_off(n);
+    oracle_new_offsets(offset, size, live, pinned, n, new_off.data());
     uint64_t bad = 0;
     for (uint64_t k = 0; k < n_handles; ++k) {
         const uint64_t h = h_in[k];
@@ -144,42 +171,46 @@ void oracle_remap(const uint64_t *offset, const uint64_t *size,
         if (result == UINT64_MAX) bad += 1;
         h_out[k] = result;
     }
-    delete[] new_off;
     *n_invalid = bad;
 }
 
-// The compacted arena written as a function of the original one: a byte
-// below the live total holds the byte of the live block that lands there
-// (same offset inside the block); a byte at or above it is untouched.
+// The compacted arena written as a function of the original one: a byte a
+// movable live block lands on holds that block's byte at the same offset
+// inside the block; every other byte is untouched.
 int64_t oracle_source_map(const uint64_t *offset, const uint64_t *size,
-                          const uint8_t *live, uint64_t n, uint64_t arena_bytes,
-                          uint64_t p0, uint64_t len, uint64_t *seg_dst,
-                          uint64_t *seg_src, uint64_t *seg_len, uint64_t cap) {
+                          const uint8_t *live, const uint8_t *pinned, uint64_t n,
+                          uint64_t arena_bytes, uint64_t p0, uint64_t len,
+                          uint64_t *seg_dst, uint64_t *seg_src, uint64_t *seg_len,
+                          uint64_t cap) {
     (void)arena_bytes;
     const uint64_t p1 = p0 + len;
     uint64_t count = 0;
+    uint64_t covered = p0;  // window bytes below this are already emitted
+    auto emit = [&](uint64_t d, uint64_t s, uint64_t l) -> bool {
+        if (count == cap) return false;
+        seg_dst[count] = d;
+        seg_src[count] = s;
+        seg_len[count] = l;
+        ++count;
+        return true;
+    };
     uint64_t dst = 0;
     for (uint64_t i = 0; i < n; ++i) {
+        if (is_pinned(pinned, i)) {
+            dst = offset[i] + size[i];
+            continue;
+        }
         if (!live[i]) continue;
         const uint64_t a = std::max(dst, p0);
         const uint64_t b = std::min(dst + size[i], p1);
         if (a < b) {
-            if (count == cap) return -1;
-            seg_dst[count] = a;
-            seg_src[count] = offset[i] + (a - dst);
-            seg_len[count] = b - a;
-            ++count;
+            if (covered < a && !emit(covered, covered, a - covered)) return -1;
+            if (!emit(a, offset[i] + (a - dst), b - a)) return -1;
+            covered = b;
         }
         dst += size[i];
     }
-    const uint64_t a = std::max(dst, p0);
-    if (a < p1) {
-        if (count == cap) return -1;
-        seg_dst[count] = a;
-        seg_src[count] = a;
-        seg_len[count] = p1 - a;
-        ++count;
-    }
+    if (covered < p1 && !emit(covered, covered, p1 - covered)) return -1;
     return (int64_t)count;
 }
 

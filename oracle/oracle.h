@@ -20,9 +20,19 @@
  *           1 - largest/free, defined as 0 when nothing is free) and section
  *           3.3 (periodic compaction moves every allocated block into one
  *           contiguous region, leaving one large free region).
+ *   [910C] section "Cutting alloc and free at the source": the parameter
+ *           region keeps fixed addresses and is never freed.  A pinned entry
+ *           models such a block: it is live, never moves, and splits the
+ *           arena into segments that compact independently.
  *
  * All byte quantities are unsigned 64-bit.  The table is structure-of-arrays:
- * offset[n], size[n], live[n] (0/1), host memory, owned by the caller.
+ * offset[n], size[n], live[n] (0/1) and pinned[n] (0/1, or NULL: nothing
+ * pinned), host memory, owned by the caller.
+ *
+ * Segments: a segment is the span between two consecutive pinned blocks (or
+ * an arena end).  Within each segment the movable live blocks keep their
+ * order and pack down to the segment's start; pinned blocks stay put.  With
+ * nothing pinned there is one segment, [0, arena_bytes).
  */
 #ifndef ARENA_COMPACTION_ORACLE_H
 #define ARENA_COMPACTION_ORACLE_H
@@ -37,14 +47,16 @@ extern "C" {
 #define ORACLE_OK 0
 #define ORACLE_EINVAL (-1)
 
-/* Which check rejected a table entry (first failing entry, first failing
- * check in this order). */
+/* Which check rejected a table entry: the first failing entry, and within it
+ * the first failing check in the order zero size, misaligned, live flag,
+ * pinned flag, out of arena, overlap. */
 #define ORACLE_REASON_NONE 0
 #define ORACLE_REASON_ZERO_SIZE 1      /* size == 0                          */
 #define ORACLE_REASON_MISALIGNED 2     /* offset or size not a multiple of 32 */
 #define ORACLE_REASON_LIVE_FLAG 3      /* live not 0 or 1                     */
 #define ORACLE_REASON_OUT_OF_ARENA 4   /* offset + size > arena bytes         */
 #define ORACLE_REASON_OVERLAP 5        /* starts before the previous one ends */
+#define ORACLE_REASON_PINNED_FLAG 7    /* pinned not 0/1, or pinned but free  */
 
 typedef struct oracle_stats {
     uint64_t arena_bytes;
@@ -61,38 +73,44 @@ typedef struct oracle_stats {
 
 /* Validate a table; on failure set *bad_index and *reason. */
 int oracle_validate(const uint64_t *offset, const uint64_t *size,
-                    const uint8_t *live, uint64_t n, uint64_t arena_bytes,
-                    uint64_t *bad_index, int32_t *reason);
+                    const uint8_t *live, const uint8_t *pinned, uint64_t n,
+                    uint64_t arena_bytes, uint64_t *bad_index, int32_t *reason);
 
-/* new_offset[i] = total size of the live entries before i. */
+/* new_offset[i]: a pinned entry keeps its offset; any other entry gets its
+ * segment's start plus the sizes of the movable live entries before it in
+ * that segment (with nothing pinned: the live bytes before it). */
 void oracle_new_offsets(const uint64_t *offset, const uint64_t *size,
-                        const uint8_t *live, uint64_t n, uint64_t *new_offset);
+                        const uint8_t *live, const uint8_t *pinned, uint64_t n,
+                        uint64_t *new_offset);
 
-/* Ordered in-place compaction of a host arena: live blocks, lowest first,
- * memmove'd to their new offsets. */
+/* Ordered in-place compaction of a host arena: movable live blocks, lowest
+ * first, memmove'd to their new offsets. */
 void oracle_compact(uint8_t *arena, uint64_t arena_bytes,
                     const uint64_t *offset, const uint64_t *size,
-                    const uint8_t *live, uint64_t n);
+                    const uint8_t *live, const uint8_t *pinned, uint64_t n);
 
 /* Free total, holes and ratios by one low-to-high walk. */
 void oracle_stats_walk(const uint64_t *offset, const uint64_t *size,
-                       const uint8_t *live, uint64_t n, uint64_t arena_bytes,
-                       oracle_stats *out);
+                       const uint8_t *live, const uint8_t *pinned, uint64_t n,
+                       uint64_t arena_bytes, oracle_stats *out);
 
 /* Address of every handle after compaction, UINT64_MAX if the handle is not
  * inside a live block; *n_invalid counts the latter.  h_out may equal h_in. */
 void oracle_remap(const uint64_t *offset, const uint64_t *size,
-                  const uint8_t *live, uint64_t n, const uint64_t *h_in,
-                  uint64_t *h_out, uint64_t n_handles, uint64_t *n_invalid);
+                  const uint8_t *live, const uint8_t *pinned, uint64_t n,
+                  const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
+                  uint64_t *n_invalid);
 
 /* Where each byte of the compacted arena window [p0, p0+len) came from in the
- * original arena, as segments (dst, src, len), ascending.  Returns the number
- * of segments, or -1 if more than cap are needed.  Bytes at or above the live
- * total keep their original value, so their src equals their dst. */
+ * original arena, as pieces (dst, src, len), ascending.  Returns the number
+ * of pieces, or -1 if more than cap are needed.  A byte that no movable live
+ * block lands on (pinned bytes, each segment's top hole) keeps its original
+ * value, so its src equals its dst. */
 int64_t oracle_source_map(const uint64_t *offset, const uint64_t *size,
-                          const uint8_t *live, uint64_t n, uint64_t arena_bytes,
-                          uint64_t p0, uint64_t len, uint64_t *seg_dst,
-                          uint64_t *seg_src, uint64_t *seg_len, uint64_t cap);
+                          const uint8_t *live, const uint8_t *pinned, uint64_t n,
+                          uint64_t arena_bytes, uint64_t p0, uint64_t len,
+                          uint64_t *seg_dst, uint64_t *seg_src, uint64_t *seg_len,
+                          uint64_t cap);
 
 #ifdef __cplusplus
 }

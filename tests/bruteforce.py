@@ -1,14 +1,19 @@
 """Byte-level brute force for tiny heaps, written independently of the oracle.
 
-Compaction is stated here as a stable partition of bytes: mark every byte that
-lies in a live block, then the compacted arena is the marked bytes in address
-order followed by the original bytes from that point on.  New offsets, holes
-and remapped handles are all read off the byte bitmap by counting, with no
-per-block running sum.  Only for arenas of at most a few MiB.
+Compaction is stated here as a stable partition of bytes inside each segment:
+mark every byte of a movable live block; a segment is the span between two
+pinned blocks (or an arena end); in each segment the marked bytes, in address
+order, are written from the segment's start, and every other byte keeps its
+value.  New offsets, holes and remapped handles are read off the byte maps by
+counting, with no per-block running sum.  Only for arenas of a few MiB.
 """
 import numpy as np
 
 U64_MAX = (1 << 64) - 1
+
+
+def _pin(pinned, n):
+    return np.zeros(n, np.uint8) if pinned is None else pinned
 
 
 def live_bitmap(arena_bytes, off, size, live):
@@ -19,16 +24,57 @@ def live_bitmap(arena_bytes, off, size, live):
     return B
 
 
-def compacted(arena, B):
+def _maps(arena_bytes, off, size, live, pinned):
+    """(movable-live byte map, pinned byte map, segment start of every byte)"""
+    pinned = _pin(pinned, len(off))
+    M = np.zeros(arena_bytes, dtype=bool)
+    P = np.zeros(arena_bytes, dtype=bool)
+    for o, s, l, p in zip(off.tolist(), size.tolist(), live.tolist(), pinned.tolist()):
+        if p:
+            P[o:o + s] = True
+        elif l:
+            M[o:o + s] = True
+    seg = np.zeros(arena_bytes, dtype=np.int64)
+    start = 0
+    prev = False
+    for a in range(arena_bytes):
+        if prev and not P[a]:
+            start = a                 # first byte after a pinned run
+        seg[a] = start
+        prev = bool(P[a])
+    return M, P, seg
+
+
+def compacted(arena, off, size, live, pinned=None):
+    M, P, seg = _maps(arena.shape[0], off, size, live, pinned)
     out = arena.copy()
-    keep = arena[B]
-    out[:keep.shape[0]] = keep
+    S = arena.shape[0]
+    a = 0
+    while a < S:
+        if P[a]:
+            a += 1
+            continue
+        b = a
+        while b < S and not P[b]:
+            b += 1
+        keep = arena[a:b][M[a:b]]
+        out[a:a + keep.shape[0]] = keep
+        a = b
     return out
 
 
-def new_offsets(B, off):
-    below = np.concatenate([[0], np.cumsum(B, dtype=np.int64)])
-    return np.array([below[o] for o in off.tolist()], dtype=np.uint64)
+def new_offsets(arena_bytes, off, size, live, pinned=None):
+    M, P, seg = _maps(arena_bytes, off, size, live, pinned)
+    below = np.concatenate([[0], np.cumsum(M, dtype=np.int64)])
+    pinned = _pin(pinned, len(off))
+    out = []
+    for o, p in zip(off.tolist(), pinned.tolist()):
+        if p:
+            out.append(o)
+        else:
+            s0 = int(seg[o]) if o < arena_bytes else (int(seg[-1]) if arena_bytes else 0)
+            out.append(s0 + int(below[o] - below[s0]))
+    return np.array(out, dtype=np.uint64)
 
 
 def holes(B):
@@ -46,13 +92,13 @@ def holes(B):
     return runs
 
 
-def stats(arena_bytes, off, size, live):
+def stats(arena_bytes, off, size, live, pinned=None):
     B = live_bitmap(arena_bytes, off, size, live)
     hs = holes(B)
     lt = int(B.sum())
     F = arena_bytes - lt
     L = max((h[1] for h in hs), default=0)
-    newo = new_offsets(B, off)
+    newo = new_offsets(arena_bytes, off, size, live, pinned)
     moved = [(i, int(size[i])) for i in range(len(off))
              if live[i] and int(newo[i]) != int(off[i])]
     r1 = 0.0 if F == 0 else F / L - 1.0
@@ -65,13 +111,16 @@ def stats(arena_bytes, off, size, live):
                 frag_one_minus_largest_over_free=r2)
 
 
-def remap(arena_bytes, off, size, live, handles):
-    B = live_bitmap(arena_bytes, off, size, live)
-    rank = np.concatenate([[0], np.cumsum(B, dtype=np.int64)])
+def remap(arena_bytes, off, size, live, handles, pinned=None):
+    M, P, seg = _maps(arena_bytes, off, size, live, pinned)
+    rank = np.concatenate([[0], np.cumsum(M, dtype=np.int64)])
     out = []
     for h in handles.tolist():
-        if h < arena_bytes and B[h]:
-            out.append(int(rank[h]))
+        if h < arena_bytes and P[h]:
+            out.append(h)
+        elif h < arena_bytes and M[h]:
+            s0 = int(seg[h])
+            out.append(s0 + int(rank[h] - rank[s0]))
         else:
             out.append(U64_MAX)
     out = np.array(out, dtype=np.uint64)

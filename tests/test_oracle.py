@@ -32,7 +32,8 @@ def _golden():
 
 def _table(case):
     t = np.array(case["table"], dtype=np.uint64).reshape(-1, 3)
-    return t[:, 0].copy(), t[:, 1].copy(), t[:, 2].astype(np.uint8)
+    pin = np.array(case["pinned"], dtype=np.uint8) if "pinned" in case else None
+    return t[:, 0].copy(), t[:, 1].copy(), t[:, 2].astype(np.uint8), pin
 
 
 def _src_of_each_byte(segments, S):
@@ -46,11 +47,11 @@ def _src_of_each_byte(segments, S):
 
 @pytest.mark.parametrize("case", _golden(), ids=lambda c: c["name"])
 def test_golden_hand_worked(case, oracle_lib):
-    off, size, live = _table(case)
+    off, size, live, pin = _table(case)
     S = case["arena_bytes"]
-    assert oracle.validate(off, size, live, S)[0] == oracle.OK
-    assert oracle.new_offsets(off, size, live).tolist() == case["new_offset"]
-    st_ = oracle.stats(off, size, live, S)
+    assert oracle.validate(off, size, live, S, pinned=pin)[0] == oracle.OK
+    assert oracle.new_offsets(off, size, live, pin).tolist() == case["new_offset"]
+    st_ = oracle.stats(off, size, live, S, pinned=pin)
     exp = case["stats"]
     for k in ("arena_bytes", "live_bytes", "free_bytes", "largest_hole", "hole_count",
               "live_blocks", "moved_blocks", "moved_bytes"):
@@ -67,22 +68,23 @@ def test_golden_hand_worked(case, oracle_lib):
     rng = np.random.default_rng(0)
     A = rng.integers(0, 256, S, dtype=np.uint8)
     B = A.copy()
-    oracle.compact(B, off, size, live)
+    oracle.compact(B, off, size, live, pin)
     expect = np.empty_like(A)
     for d, s, l in case["after_move_sources"]:
         expect[d:d + l] = A[s:s + l]
     assert np.array_equal(B, expect)
-    d, s, l = oracle.source_map(off, size, live, S, 0, S)
+    d, s, l = oracle.source_map(off, size, live, S, 0, S, pinned=pin)
     assert _src_of_each_byte(zip(d.tolist(), s.tolist(), l.tolist()), S) == \
         _src_of_each_byte(case["after_move_sources"], S)
     h = np.array(case["handles"], dtype=np.uint64)
-    out, bad = oracle.remap(off, size, live, h)
+    out, bad = oracle.remap(off, size, live, h, pinned=pin)
     want = [U64_MAX if v < 0 else v for v in case["remapped"]]
     assert out.tolist() == want
     assert bad == sum(1 for v in case["remapped"] if v < 0)
     if "post_table" in case:
         t = np.array(case["post_table"], dtype=np.uint64)
-        ps = oracle.stats(t[:, 0], t[:, 1], t[:, 2].astype(np.uint8), S)
+        ppin = np.array(case["post_pinned"], dtype=np.uint8) if "post_pinned" in case else None
+        ps = oracle.stats(t[:, 0], t[:, 1], t[:, 2].astype(np.uint8), S, pinned=ppin)
         pe = case["post_stats"]
         assert (ps.free_bytes, ps.largest_hole, ps.hole_count) == \
             (pe["free_bytes"], pe["largest_hole"], pe["hole_count"])
@@ -91,28 +93,28 @@ def test_golden_hand_worked(case, oracle_lib):
 
 
 def _check_against_bruteforce(heap):
-    off, size, live, S = heap.offset, heap.size, heap.live, heap.arena_bytes
-    assert oracle.validate(off, size, live, S)[0] == oracle.OK
-    B = BF.live_bitmap(S, off, size, live)
-    # new offsets: live bytes below each entry's start
-    assert np.array_equal(oracle.new_offsets(off, size, live), BF.new_offsets(B, off))
-    # arena: stable partition of live bytes
+    off, size, live, S, pin = heap.offset, heap.size, heap.live, heap.arena_bytes, heap.pinned
+    assert oracle.validate(off, size, live, S, pinned=pin)[0] == oracle.OK
+    # new offsets: segment start + movable live bytes below each entry's start
+    assert np.array_equal(oracle.new_offsets(off, size, live, pin),
+                          BF.new_offsets(S, off, size, live, pin))
+    # arena: stable partition of movable live bytes inside each segment
     rng = np.random.default_rng(int(heap.payload_seed) & 0xFFFF)
     A = rng.integers(0, 256, S, dtype=np.uint8)
     got = A.copy()
-    oracle.compact(got, off, size, live)
-    assert np.array_equal(got, BF.compacted(A, B))
+    oracle.compact(got, off, size, live, pin)
+    assert np.array_equal(got, BF.compacted(A, off, size, live, pin))
     # stats
-    exp = BF.stats(S, off, size, live)
-    s = oracle.stats(off, size, live, S)
+    exp = BF.stats(S, off, size, live, pin)
+    s = oracle.stats(off, size, live, S, pinned=pin)
     for k, v in exp.items():
         assert getattr(s, k) == v, (k, getattr(s, k), v)
-    # remap: rank of the byte among live bytes
-    out, bad = oracle.remap(off, size, live, heap.handles)
-    eo, eb = BF.remap(S, off, size, live, heap.handles)
+    # remap: rank of the byte among movable live bytes of its segment
+    out, bad = oracle.remap(off, size, live, heap.handles, pinned=pin)
+    eo, eb = BF.remap(S, off, size, live, heap.handles, pin)
     assert np.array_equal(out, eo) and bad == eb
     # the source map rebuilds the same compacted arena
-    d, s_, l = oracle.source_map(off, size, live, S, 0, S)
+    d, s_, l = oracle.source_map(off, size, live, S, 0, S, pinned=pin)
     rebuilt = np.empty_like(A)
     for dd, ss, ll in zip(d.tolist(), s_.tolist(), l.tolist()):
         rebuilt[dd:dd + ll] = A[ss:ss + ll]
@@ -139,13 +141,28 @@ def test_exhaustive_live_masks(oracle_lib):
                     _check_against_bruteforce(h)
 
 
-@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@settings(max_examples=200, deadline=None, suppress_health_check=[HealthCheck.too_slow])
 @given(seed=st.integers(0, 2**32 - 1), n=st.integers(0, 40),
-       gap_p=st.sampled_from([0.0, 0.3, 0.8]), live_p=st.sampled_from([0.0, 0.5, 0.9, 1.0]))
-def test_random_tiny_heaps(seed, n, gap_p, live_p):
+       gap_p=st.sampled_from([0.0, 0.3, 0.8]), live_p=st.sampled_from([0.0, 0.5, 0.9, 1.0]),
+       pinned_p=st.sampled_from([0.0, 0.0, 0.2, 0.5]))
+def test_random_tiny_heaps(seed, n, gap_p, live_p, pinned_p):
     rng = np.random.default_rng(seed)
-    heap = W.tiny_heap(rng, n, sizes=(32, 64, 96, 160, 4096), gap_p=gap_p, live_p=live_p)
+    heap = W.tiny_heap(rng, n, sizes=(32, 64, 96, 160, 4096), gap_p=gap_p, live_p=live_p,
+                       pinned_p=pinned_p)
     _check_against_bruteforce(heap)
+
+
+def test_exhaustive_pinned_masks(oracle_lib):
+    """Every (free, live, pinned) assignment over a 5-entry table with gaps."""
+    blocks = [(32, 32), (64, 64), (160, 96), (256, 32), (320, 64)]
+    for tail in (0, 96):
+        S = 384 + tail
+        for states in itertools.product((0, 1, 2), repeat=len(blocks)):
+            live = [1 if x else 0 for x in states]
+            pin = [1 if x == 2 else 0 for x in states]
+            h = W.table_from_lists(S, blocks, live, pinned=pin)
+            h.handles = W.edge_handles(h, np.random.default_rng(sum(states)), 4)
+            _check_against_bruteforce(h)
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
@@ -253,13 +270,14 @@ def _check_source_map_windows(heap, rng, n_windows=12):
     S = heap.arena_bytes
     A = rng.integers(0, 256, S, dtype=np.uint8)
     got = A.copy()
-    oracle.compact(got, heap.offset, heap.size, heap.live)
+    oracle.compact(got, heap.offset, heap.size, heap.live, heap.pinned)
     for _ in range(n_windows):
         if S == 0:
             break
         p0 = int(rng.integers(0, S))
         ln = int(rng.integers(1, S - p0 + 1))
-        d, s, l = oracle.source_map(heap.offset, heap.size, heap.live, S, p0, ln)
+        d, s, l = oracle.source_map(heap.offset, heap.size, heap.live, S, p0, ln,
+                                    pinned=heap.pinned)
         rebuilt = np.full(ln, -1, dtype=np.int16)
         for dd, ss, ll in zip(d.tolist(), s.tolist(), l.tolist()):
             rebuilt[dd - p0:dd - p0 + ll] = A[ss:ss + ll]
@@ -270,5 +288,64 @@ def _check_source_map_windows(heap, rng, n_windows=12):
 @given(seed=st.integers(0, 2**32 - 1), n=st.integers(1, 30))
 def test_source_map_any_window(seed, n):
     rng = np.random.default_rng(seed)
-    heap = W.tiny_heap(rng, n, sizes=(32, 64, 96, 160), gap_p=0.4, live_p=0.6)
+    heap = W.tiny_heap(rng, n, sizes=(32, 64, 96, 160), gap_p=0.4, live_p=0.6,
+                       pinned_p=0.25 if seed % 2 else 0.0)
     _check_source_map_windows(heap, rng)
+
+
+@pytest.mark.parametrize("table,pinned,S,idx,reason", [
+    ([(0, 32, 1)], [2], 64, 0, 7),
+    ([(0, 32, 0)], [1], 64, 0, 7),
+    ([(0, 32, 1), (32, 32, 0)], [0, 1], 64, 1, 7),
+    ([(0, 32, 2)], [1], 64, 0, 3),            # live flag is checked before pinned
+    ([(0, 32, 0), (96, 32, 1)], [1, 0], 64, 0, 7),   # pinned before out of arena
+    ([(0, 32, 1), (96, 32, 1)], [1, 1], 64, 1, 4),
+    ([(0, 64, 1), (32, 32, 1)], [1, 1], 128, 1, 5),
+])
+def test_validation_reasons_pinned(table, pinned, S, idx, reason, oracle_lib):
+    t = np.array(table, dtype=np.uint64)
+    rc, bad, r = oracle.validate(t[:, 0], t[:, 1], t[:, 2].astype(np.uint8), S,
+                                 pinned=np.array(pinned, np.uint8))
+    assert (rc, bad, r) == (oracle.EINVAL, idx, reason)
+
+
+def test_pinned_segments_invariants(oracle_lib):
+    """Reduced config 3 with its 40 parameter/optimizer blocks pinned: pinned
+    bytes never change; every segment's movable blocks are packed from the
+    segment start in order, payload intact; afterwards every segment holds at
+    most one hole, at its top, and the free total is unchanged."""
+    import torch
+    heap = W.config("3p", small=True)
+    off, size, live, pin, S = heap.offset, heap.size, heap.live, heap.pinned, heap.arena_bytes
+    assert heap.n_pinned == 40
+    assert oracle.validate(off, size, live, S, pinned=pin)[0] == oracle.OK
+    new = oracle.new_offsets(off, size, live, pin)
+    A = torch.empty(S, dtype=torch.uint8)
+    W.fill_payload(A, 0, heap.payload_mode, heap.payload_seed)
+    A = A.numpy()
+    got = A.copy()
+    oracle.compact(got, off, size, live, pin)
+    seg_start = 0
+    cursor = 0
+    for i in range(heap.n):
+        o, s_ = int(off[i]), int(size[i])
+        if pin[i]:
+            assert int(new[i]) == o and np.array_equal(got[o:o + s_], A[o:o + s_])
+            seg_start = cursor = o + s_
+            continue
+        if live[i]:
+            assert int(new[i]) == cursor >= seg_start
+            if i % 97 == 0 or s_ > (1 << 20):
+                assert np.array_equal(got[cursor:cursor + s_], A[o:o + s_]), i
+            cursor += s_
+    li = np.flatnonzero(live)
+    before = oracle.stats(off, size, live, S, pinned=pin)
+    pt = oracle.stats(new[li], size[li], np.ones(li.shape[0], np.uint8), S, pinned=pin[li])
+    assert pt.free_bytes == before.free_bytes
+    assert pt.moved_blocks == 0
+    # at most one hole per segment: segments = pinned blocks + 1
+    assert pt.hole_count <= heap.n_pinned + 1
+    assert pt.largest_hole < before.free_bytes   # the pinned blocks keep free space apart
+    out, bad = oracle.remap(off, size, live, heap.handles, pinned=pin)
+    assert bad == 0
+    assert np.array_equal(got[out[:5000].astype(np.int64)], A[heap.handles[:5000].astype(np.int64)])

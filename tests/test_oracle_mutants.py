@@ -45,7 +45,15 @@ MUTANTS = [
     ("validate_exact_fit_rejected", "size[i] > arena_bytes - offset[i]", "size[i] >= arena_bytes - offset[i]"),
     ("validate_order_swapped", "        if (size[i] == 0)\n            r = ORACLE_REASON_ZERO_SIZE;\n        else if (offset[i] % 32 != 0 || size[i] % 32 != 0)\n            r = ORACLE_REASON_MISALIGNED;",
      "        if (offset[i] % 32 != 0 || size[i] % 32 != 0)\n            r = ORACLE_REASON_MISALIGNED;\n        else if (size[i] == 0)\n            r = ORACLE_REASON_ZERO_SIZE;"),
-    ("source_map_block_start", "seg_src[count] = offset[i] + (a - dst);", "seg_src[count] = offset[i];"),
+    ("source_map_block_start", "emit(a, offset[i] + (a - dst), b - a)", "emit(a, offset[i], b - a)"),
+    ("pinned_segment_base_drops_size",
+     "            new_offset[i] = offset[i];\n            running = offset[i] + size[i];",
+     "            new_offset[i] = offset[i];\n            running = offset[i];"),
+    ("pinned_blocks_move", "        if (is_pinned(pinned, i)) {\n            dst = offset[i] + size[i];\n            continue;\n        }\n        if (!live[i]) continue;\n        if (dst != offset[i])",
+     "        if (!live[i]) continue;\n        if (dst != offset[i])"),
+    ("pinned_free_accepted", "(pinned[i] == 1 && live[i] == 0)", "(pinned[i] == 3 && live[i] == 0)"),
+    ("pinned_moved_counted", "        if (is_pinned(pinned, i)) {\n            new_off = offset[i] + size[i];\n        } else {",
+     "        if (false) {\n        } else {"),
 ]
 
 
@@ -55,9 +63,10 @@ def _battery():
         for case in T._golden():
             T.test_golden_hand_worked(case, None)
         rng = np.random.default_rng(99)
-        for k in range(40):
+        for k in range(60):
             heap = W.tiny_heap(rng, int(rng.integers(0, 25)), sizes=(32, 64, 96, 160, 4096),
-                               gap_p=[0.0, 0.3, 0.8][k % 3], live_p=[0.3, 0.6, 1.0][k % 3])
+                               gap_p=[0.0, 0.3, 0.8][k % 3], live_p=[0.3, 0.6, 1.0][k % 3],
+                               pinned_p=[0.0, 0.3][k % 2])
             T._check_against_bruteforce(heap)
             T._check_source_map_windows(heap, rng, 4)
         for table, S, idx, reason in [
@@ -65,6 +74,7 @@ def _battery():
                 ([(0, 32, 2)], 64, 0, 3), ([(0, 32, 1), (32, 64, 1)], 64, 1, 4),
                 ([(0, 64, 1), (32, 32, 0)], 128, 1, 5), ([(16, 0, 1)], 64, 0, 1)]:
             T.test_validation_reasons(table, S, idx, reason, None)
+        T.test_validation_reasons_pinned([(0, 32, 0)], [1], 64, 0, 7, None)
         # a valid table that fills the arena exactly and touches neighbours
         t = np.array([(0, 32, 1), (32, 32, 1)], dtype=np.uint64)
         assert oracle.validate(t[:, 0], t[:, 1], t[:, 2].astype(np.uint8), 64)[0] == oracle.OK

@@ -103,7 +103,8 @@ def build_host_generator(verbose: bool = False) -> str:
 def _host_lib():
     global _clib
     if _clib is None:
-        if not os.path.exists(_CLIB_PATH):
+        src = os.path.join(_HERE, "payload.c")
+        if not os.path.exists(_CLIB_PATH) or os.path.getmtime(src) > os.path.getmtime(_CLIB_PATH):
             build_host_generator()
         L = ctypes.CDLL(_CLIB_PATH)
         L.wl_fill_hash.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
@@ -191,15 +192,20 @@ class Heap:
     payload_seed: int = 0
     seed: int = 0
     notes: dict = dataclasses.field(default_factory=dict)
+    pinned: Optional[np.ndarray] = None   # uint8 0/1 per entry, or None: nothing pinned
 
     @property
     def n(self) -> int:
         return int(self.offset.shape[0])
 
+    @property
+    def n_pinned(self) -> int:
+        return 0 if self.pinned is None else int(self.pinned.sum())
+
     def describe(self) -> str:
         return (f"{self.name}: S={self.arena_bytes} n={self.n} "
-                f"live={int(self.live.sum())} handles={self.handles.shape[0]} "
-                f"seed={self.seed}")
+                f"live={int(self.live.sum())} pinned={self.n_pinned} "
+                f"handles={self.handles.shape[0]} seed={self.seed}")
 
 
 # --------------------------------------------------------------------------
@@ -294,7 +300,7 @@ def config2(seed: int = 2, n_pairs: int = 32768, arena_bytes: int = 1 * GiB,
 
 def config3(seed: int = 3, arena_bytes: int = 80 * GiB, n_pinned: int = 40,
             n_act: int = 200, n_small: int = 200_000, gran: int = 4 * KiB,
-            n_handles: int = 4_000_000) -> Heap:
+            n_handles: int = 4_000_000, pin_params: bool = False) -> Heap:
     """An arena shaped like the 910C page's failure: 14/80 of the arena free,
     largest hole = floor_g(free / 5.7) so that free/largest - 1 = 4.7.
 
@@ -306,6 +312,10 @@ def config3(seed: int = 3, arena_bytes: int = 80 * GiB, n_pinned: int = 40,
     tiles the arena exactly; random non-adjacent activation/small blocks are
     then freed until the free total is exactly 14/80 of the arena.
     Sizes are multiples of ``gran``.
+
+    With ``pin_params`` the 40 parameter/optimizer blocks are pinned (fixed
+    addresses, as the 910C page's parameter region in "cutting alloc and free
+    at the source"): the same table, but those blocks may not move.
     """
     rng = np.random.default_rng(seed)
     S = arena_bytes
@@ -383,9 +393,12 @@ def config3(seed: int = 3, arena_bytes: int = 80 * GiB, n_pinned: int = 40,
     assert remaining == 0, "could not reach the free-total target exactly"
 
     h = draw_handles(off, size, live, n_handles, rng)
-    heap = Heap("config3", S, off, size, live, h, "hash", 0xC0FFEE00 + seed, seed)
+    heap = Heap("config3" + ("-pinned" if pin_params else ""), S, off, size, live, h, "hash",
+                0xC0FFEE00 + seed, seed)
     heap.notes.update(dict(free_target=F, largest_target=L, alpha=alpha,
                            named_free=named_free, gap=2 * half + g))
+    if pin_params:
+        heap.pinned = (kind == 0).astype(np.uint8)
     return heap
 
 
@@ -427,9 +440,15 @@ def config5(seed: int = 5, n_live: int = 64, block_bytes: int = 1 * GiB,
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
-def config(k: int, small: bool = False) -> Heap:
-    """Workload ``k`` (1..5) at its full size, or a reduced variant with the
+def config(k, small: bool = False) -> Heap:
+    """Workload ``k`` (1..5, or "3p": config 3 with its 40 parameter and
+    optimizer blocks pinned) at its full size, or a reduced variant with the
     same structure (for oracle runs that must finish in seconds)."""
+    if k == "3p":
+        if not small:
+            return config3(pin_params=True)
+        return config3(arena_bytes=80 * 16 * MiB, n_small=3000, n_act=60, n_pinned=40,
+                       n_handles=65536, pin_params=True)
     if not small:
         return CONFIGS[k]()
     if k == 1:
@@ -453,7 +472,7 @@ def config(k: int, small: bool = False) -> Heap:
 
 def tiny_heap(rng: np.random.Generator, n: int, sizes=(32, 64, 96),
               gap_p: float = 0.3, tail_max: int = 3, live_p: float = 0.5,
-              gran: int = 32) -> Heap:
+              gran: int = 32, pinned_p: float = 0.0) -> Heap:
     """A small random table: n blocks with sizes from ``sizes``, optional
     untracked gaps (multiples of ``gran``) between them and an optional
     untracked tail."""
@@ -469,15 +488,20 @@ def tiny_heap(rng: np.random.Generator, n: int, sizes=(32, 64, 96),
     live = (rng.random(n) < live_p).astype(np.uint8)
     h = draw_handles(off, size, live, 4 * max(n, 1), rng)
     heap = Heap(f"tiny{n}", S, off, size, live, h, "hash", int(rng.integers(1, 1 << 62)), 0)
+    if pinned_p > 0:
+        heap.pinned = ((rng.random(n) < pinned_p) & (live == 1)).astype(np.uint8)
     heap.handles = np.concatenate([h, edge_handles(heap, rng, 8)])
     return heap
 
 
 def table_from_lists(arena_bytes: int, blocks, live, handles=(), name="hand",
-                     payload_mode="hash", payload_seed=7) -> Heap:
-    """Build a Heap from explicit (offset, size) pairs and live flags."""
+                     payload_mode="hash", payload_seed=7, pinned=None) -> Heap:
+    """Build a Heap from explicit (offset, size) pairs, live and pinned flags."""
     off = np.array([b[0] for b in blocks], dtype=np.uint64)
     size = np.array([b[1] for b in blocks], dtype=np.uint64)
     lv = np.array(live, dtype=np.uint8)
     h = np.array(list(handles), dtype=np.uint64)
-    return Heap(name, arena_bytes, off, size, lv, h, payload_mode, payload_seed, 0)
+    heap = Heap(name, arena_bytes, off, size, lv, h, payload_mode, payload_seed, 0)
+    if pinned is not None:
+        heap.pinned = np.array(pinned, dtype=np.uint8)
+    return heap
