@@ -6,7 +6,8 @@ used for device memory and streams.  Importing this module fails loudly if
 the library has not been built -- there is no CPU fallback.
 
 Tables are torch tensors on the GPU: offset and size as int64 holding the
-unsigned 64-bit values, live as uint8 (or None: every entry live).  Handles
+unsigned 64-bit values, live as uint8 (or None: every entry live), pinned as
+uint8 (or None: nothing pinned).  Handles
 and new offsets are int64 tensors holding unsigned values; an unmapped handle
 reads back as -1 (UINT64_MAX).
 """
@@ -29,13 +30,14 @@ DEFRAG_ENOPLAN = -3
 DEFRAG_EHIP = -4
 DEFRAG_ETIMEOUT = -5
 REASONS = {0: "none", 1: "zero_size", 2: "misaligned", 3: "live_flag",
-           4: "out_of_arena", 5: "overlap", 6: "argument"}
+           4: "out_of_arena", 5: "overlap", 6: "argument", 7: "pinned_flag"}
 U64_MAX = (1 << 64) - 1
 
 
 class defrag_table(ctypes.Structure):
     _fields_ = [("offset_dev", ctypes.c_void_p), ("size_dev", ctypes.c_void_p),
-                ("live_dev", ctypes.c_void_p), ("n", ctypes.c_uint64)]
+                ("live_dev", ctypes.c_void_p), ("n", ctypes.c_uint64),
+                ("pinned_dev", ctypes.c_void_p)]
 
 
 class defrag_stats_t(ctypes.Structure):
@@ -60,9 +62,10 @@ class defrag_plan_t(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint64), ("epoch", ctypes.c_uint64),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
                 ("n", ctypes.c_uint64), ("arena_bytes", ctypes.c_uint64),
-                ("live_blocks", ctypes.c_uint64), ("first_moved", ctypes.c_uint64),
+                ("live_blocks", ctypes.c_uint64), ("pinned_blocks", ctypes.c_uint64),
                 ("move_begin", ctypes.c_uint64), ("live_bytes", ctypes.c_uint64),
-                ("n_tiles", ctypes.c_uint64), ("max_blocks_per_tile", ctypes.c_uint64),
+                ("n_tiles", ctypes.c_uint64), ("max_tiles", ctypes.c_uint64),
+                ("max_blocks_per_tile", ctypes.c_uint64),
                 ("state", ctypes.c_int32), ("device", ctypes.c_int32),
                 ("tuning", defrag_tuning), ("stats", defrag_stats_t)]
 
@@ -87,7 +90,7 @@ def _load() -> ctypes.CDLL:
             "g.build()'); there is no fallback path")
     L = ctypes.CDLL(LIB_PATH)
     P, U, S = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_size_t
-    L.defrag_workspace_bytes.argtypes = [U, U, ctypes.c_uint32]
+    L.defrag_workspace_bytes.argtypes = [U, U, U, ctypes.c_uint32]
     L.defrag_workspace_bytes.restype = S
     L.defrag_stats.argtypes = [ctypes.POINTER(defrag_table), U, P, S, P,
                                ctypes.POINTER(defrag_stats_t)]
@@ -96,7 +99,7 @@ def _load() -> ctypes.CDLL:
     L.defrag_move.argtypes = [P, U, ctypes.POINTER(defrag_plan_t), P, S, P]
     L.defrag_move_status.argtypes = [ctypes.POINTER(defrag_plan_t), P, P]
     L.defrag_remap.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, U, P, P]
-    L.defrag_commit.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, P, P]
+    L.defrag_commit.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, P, P, P]
     L.defrag_strerror.argtypes = [ctypes.c_int]
     L.defrag_strerror.restype = ctypes.c_char_p
     for f in ("defrag_stats", "defrag_plan", "defrag_move", "defrag_move_status",
@@ -128,31 +131,35 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def make_table(offset: torch.Tensor, size: torch.Tensor,
-               live: Optional[torch.Tensor]) -> defrag_table:
+def make_table(offset: torch.Tensor, size: torch.Tensor, live: Optional[torch.Tensor],
+               pinned: Optional[torch.Tensor] = None) -> defrag_table:
     n = offset.numel()
     assert offset.dtype == torch.int64 and size.dtype == torch.int64 and size.numel() == n
-    if live is not None:
-        assert live.dtype == torch.uint8 and live.numel() == n
+    for f in (live, pinned):
+        if f is not None:
+            assert f.dtype == torch.uint8 and f.numel() == n
     return defrag_table(_ptr(offset) if n else None, _ptr(size) if n else None,
-                        _ptr(live) if (live is not None and n) else None, n)
+                        _ptr(live) if (live is not None and n) else None, n,
+                        _ptr(pinned) if (pinned is not None and n) else None)
 
 
-def defrag_workspace_bytes(n: int, arena_bytes: int, tile_bytes: int = 0) -> int:
-    return int(lib.defrag_workspace_bytes(n, arena_bytes, tile_bytes))
+def defrag_workspace_bytes(n: int, arena_bytes: int, tile_bytes: int = 0,
+                           max_pinned: int = 0) -> int:
+    return int(lib.defrag_workspace_bytes(n, max_pinned, arena_bytes, tile_bytes))
 
 
-def workspace(n: int, arena_bytes: int, tile_bytes: int = 0, device=None) -> torch.Tensor:
+def workspace(n: int, arena_bytes: int, tile_bytes: int = 0, device=None,
+              max_pinned: int = 0) -> torch.Tensor:
     """Allocate a workspace tensor (torch allocations are 256-byte aligned)."""
-    nb = defrag_workspace_bytes(n, arena_bytes, tile_bytes)
+    nb = defrag_workspace_bytes(n, arena_bytes, tile_bytes, max_pinned)
     if nb == 0:
         raise DefragError(DEFRAG_EINVAL, "defrag_workspace_bytes")
     return torch.empty(nb, dtype=torch.uint8, device=device or "cuda")
 
 
 def defrag_stats(offset, size, live, arena_bytes: int, ws: torch.Tensor,
-                 stream=None) -> defrag_stats_t:
-    t = make_table(offset, size, live)
+                 stream=None, pinned=None) -> defrag_stats_t:
+    t = make_table(offset, size, live, pinned)
     out = defrag_stats_t()
     rc = lib.defrag_stats(ctypes.byref(t), arena_bytes, _ptr(ws), ws.numel(), _stream(stream),
                           ctypes.byref(out))
@@ -163,8 +170,9 @@ def defrag_stats(offset, size, live, arena_bytes: int, ws: torch.Tensor,
 
 def defrag_plan(offset, size, live, arena_bytes: int, ws: torch.Tensor,
                 new_offset: Optional[torch.Tensor] = None,
-                tuning: Optional[defrag_tuning] = None, stream=None) -> defrag_plan_t:
-    t = make_table(offset, size, live)
+                tuning: Optional[defrag_tuning] = None, stream=None,
+                pinned: Optional[torch.Tensor] = None) -> defrag_plan_t:
+    t = make_table(offset, size, live, pinned)
     plan = defrag_plan_t()
     if new_offset is not None:
         assert new_offset.dtype == torch.int64 and new_offset.numel() >= offset.numel()
@@ -208,9 +216,9 @@ def defrag_remap(plan: defrag_plan_t, ws: torch.Tensor, h_in: torch.Tensor,
 
 
 def defrag_commit(plan: defrag_plan_t, ws: torch.Tensor, offset_out=None, size_out=None,
-                  live_out=None, stream=None) -> None:
+                  live_out=None, stream=None, pinned_out=None) -> None:
     rc = lib.defrag_commit(ctypes.byref(plan), _ptr(ws), ws.numel(), _ptr(offset_out),
-                           _ptr(size_out), _ptr(live_out), _stream(stream))
+                           _ptr(size_out), _ptr(live_out), _ptr(pinned_out), _stream(stream))
     if rc != DEFRAG_OK:
         raise DefragError(rc, "defrag_commit")
 

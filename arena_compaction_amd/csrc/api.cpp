@@ -91,8 +91,10 @@ int read_header(WsHeader *out, const uint8_t *ws, const WsLayout &L, hipStream_t
 }
 
 TableView view_of(const defrag_table *t) {
-    return TableView{t->offset_dev, t->size_dev, t->live_dev, t->n};
+    return TableView{t->offset_dev, t->size_dev, t->live_dev, t->pinned_dev, t->n};
 }
+
+WsLayout plan_layout(const defrag_plan_t *p) { return ws_with_tiles(p->n, p->max_tiles); }
 
 int current_device() {
     int d = -1;
@@ -112,10 +114,13 @@ int check_plan(const defrag_plan_t *p, const void *ws, size_t ws_bytes) {
 
 extern "C" {
 
-size_t defrag_workspace_bytes(uint64_t n, uint64_t arena_bytes, uint32_t tile_bytes) {
+size_t defrag_workspace_bytes(uint64_t n, uint64_t max_pinned, uint64_t arena_bytes,
+                              uint32_t tile_bytes) {
     const uint32_t T = tile_bytes ? tile_bytes : kDefaultTile;
-    if (!tile_ok(T) || n > DEFRAG_MAX_ENTRIES) return 0;
-    return ws_layout(n, arena_bytes, T).total;
+    if (!tile_ok(T) || n > DEFRAG_MAX_ENTRIES || max_pinned > n) return 0;
+    const uint64_t tiles = tiles_bound(arena_bytes, max_pinned, T);
+    if (tiles > 0xFFFFFFF0ull) return 0;
+    return ws_with_tiles(n, tiles).total;
 }
 
 int defrag_stats(const defrag_table *table, uint64_t arena_bytes, void *ws_dev, size_t ws_bytes,
@@ -126,14 +131,15 @@ int defrag_stats(const defrag_table *table, uint64_t arena_bytes, void *ws_dev, 
         arg_error(out_host);
         return rc;
     }
-    const WsLayout L = ws_layout(table->n, arena_bytes, kDefaultTile);
-    rc = check_ws(ws_dev, ws_bytes, L.live_dst);  // the partial-result region only
+    const WsLayout L = ws_fixed(table->n);
+    rc = check_ws(ws_dev, ws_bytes, L.tpart);  // the partial-result region only
     if (rc) {
         arg_error(out_host);
         return rc;
     }
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
-    if (launch_scan(view_of(table), arena_bytes, ws, L, nullptr, false, 0, stream) != hipSuccess)
+    if (launch_scan(view_of(table), arena_bytes, ws, L, nullptr, false, kDefaultTile, 0, stream) !=
+        hipSuccess)
         return DEFRAG_EHIP;
     WsHeader h;
     rc = read_header(&h, ws, L, stream);
@@ -160,24 +166,26 @@ int defrag_plan(const defrag_table *table, uint64_t arena_bytes, const defrag_tu
         arg_error(&plan->stats);
         return rc;
     }
-    const WsLayout L = ws_layout(table->n, arena_bytes, tu.tile_bytes);
-    rc = check_ws(ws_dev, ws_bytes, L.total);
-    if (rc) {
+    const uint64_t max_tiles = tiles_fitting(table->n, ws_bytes);
+    rc = check_ws(ws_dev, ws_bytes, ws_fixed(table->n).fixed);
+    if (rc || max_tiles == 0) {
         arg_error(&plan->stats);
-        return rc;
+        return DEFRAG_EWORKSPACE;
     }
+    const WsLayout L = ws_with_tiles(table->n, max_tiles < 0xFFFFFFF0ull ? max_tiles : 0xFFFFFFF0ull);
     const int dev = current_device();
     if (dev < 0) return DEFRAG_EHIP;
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
     const uint64_t epoch = g_epoch.fetch_add(0x9E3779B97F4A7C15ull) ^ reinterpret_cast<uintptr_t>(ws);
-    if (launch_scan(view_of(table), arena_bytes, ws, L, new_offset_dev, true, epoch, stream) !=
-        hipSuccess)
+    if (launch_scan(view_of(table), arena_bytes, ws, L, new_offset_dev, true, tu.tile_bytes, epoch,
+                    stream) != hipSuccess)
         return DEFRAG_EHIP;
     WsHeader h;
     rc = read_header(&h, ws, L, stream);
     if (rc) return rc;
     fill_stats(&plan->stats, h, arena_bytes);
     if (h.bad_key != kNone) return DEFRAG_EINVAL;
+    if (h.n_tiles > L.max_tiles) return DEFRAG_EWORKSPACE;  // new offsets are written
 
     const uint64_t T = tu.tile_bytes;
     plan->epoch = epoch;
@@ -186,24 +194,19 @@ int defrag_plan(const defrag_table *table, uint64_t arena_bytes, const defrag_tu
     plan->n = table->n;
     plan->arena_bytes = arena_bytes;
     plan->live_blocks = h.live_blocks;
-    plan->first_moved = h.first_moved;
+    plan->pinned_blocks = h.pinned_blocks;
     plan->move_begin = h.move_begin;
     plan->live_bytes = h.live_bytes;
     plan->device = dev;
     plan->tuning = tu;
-    uint64_t n_tiles = 0, base = 0;
-    if (h.move_begin < h.live_bytes) {
-        base = h.move_begin & ~(T - 1);
-        n_tiles = (h.live_bytes - base + T - 1) / T;
-    }
-    plan->n_tiles = n_tiles;
+    plan->n_tiles = h.n_tiles;
+    plan->max_tiles = L.max_tiles;
     // blocks meeting one tile: at most T / (smallest live size) + 2
     uint64_t mb = 1;
     if (h.min_live_size != kNone && h.min_live_size) mb = T / h.min_live_size + 2;
     if (mb > T / 32 + 2) mb = T / 32 + 2;
     plan->max_blocks_per_tile = mb;
-    if (launch_tiles(ws, L, n_tiles, base, tu.tile_bytes, h.move_begin, h.live_bytes,
-                     h.first_moved, h.live_blocks, stream) != hipSuccess)
+    if (launch_tiles(ws, L, h.n_tiles, h.live_blocks, tu.tile_bytes, stream) != hipSuccess)
         return DEFRAG_EHIP;
     plan->magic = kPlanMagic;
     plan->state = 1;
@@ -223,7 +226,7 @@ int defrag_move(void *arena_dev, uint64_t arena_bytes, defrag_plan_t *plan, void
     if (plan->n_tiles == 0) return DEFRAG_OK;
     const int cus = num_cus_of(plan->device);
     if (cus <= 0) return DEFRAG_EHIP;
-    const WsLayout L = ws_layout(plan->n, plan->arena_bytes, plan->tuning.tile_bytes);
+    const WsLayout L = plan_layout(plan);
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
     MoveArgs a{};
     a.arena = static_cast<uint8_t *>(arena_dev);
@@ -233,9 +236,6 @@ int defrag_move(void *arena_dev, uint64_t arena_bytes, defrag_plan_t *plan, void
     a.flags = reinterpret_cast<uint32_t *>(ws + L.flags);
     a.hdr = reinterpret_cast<WsHeader *>(ws + L.header);
     a.n_tiles = plan->n_tiles;
-    a.tile_base = plan->move_begin & ~((uint64_t)plan->tuning.tile_bytes - 1);
-    a.move_begin = plan->move_begin;
-    a.live_bytes = plan->live_bytes;
     a.epoch = plan->epoch;
     a.spin_limit = 1ull << plan->tuning.spin_limit_log2;
     a.tile_bytes = plan->tuning.tile_bytes;
@@ -253,7 +253,7 @@ int defrag_move_status(const defrag_plan_t *plan, const void *ws_dev, hipStream_
     if (plan->n_tiles == 0) {
         return hipStreamSynchronize(stream) == hipSuccess ? DEFRAG_OK : DEFRAG_EHIP;
     }
-    const WsLayout L = ws_layout(plan->n, plan->arena_bytes, plan->tuning.tile_bytes);
+    const WsLayout L = plan_layout(plan);
     WsHeader h;
     rc = read_header(&h, static_cast<const uint8_t *>(ws_dev), L, stream);
     if (rc) return rc;
@@ -270,10 +270,8 @@ int defrag_remap(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes,
     if (n_handles && (!h_in_dev || !h_out_dev)) return DEFRAG_EINVAL;
     const int cus = num_cus_of(plan->device);
     if (cus <= 0) return DEFRAG_EHIP;
-    const WsLayout L = ws_layout(plan->n, plan->arena_bytes, plan->tuning.tile_bytes);
-    const uint8_t *ws = static_cast<const uint8_t *>(ws_dev);
-    if (launch_remap(reinterpret_cast<const uint64_t *>(ws + L.live_dst),
-                     reinterpret_cast<const uint64_t *>(ws + L.live_src), plan->live_blocks,
+    const WsLayout L = plan_layout(plan);
+    if (launch_remap(live_view(static_cast<const uint8_t *>(ws_dev), L), plan->live_blocks,
                      h_in_dev, h_out_dev, n_handles, n_invalid_dev, cus, stream) != hipSuccess)
         return DEFRAG_EHIP;
     return DEFRAG_OK;
@@ -281,12 +279,12 @@ int defrag_remap(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes,
 
 int defrag_commit(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes,
                   uint64_t *offset_out_dev, uint64_t *size_out_dev, uint8_t *live_out_dev,
-                  hipStream_t stream) {
+                  uint8_t *pinned_out_dev, hipStream_t stream) {
     int rc = check_plan(plan, ws_dev, ws_bytes);
     if (rc) return rc;
-    const WsLayout L = ws_layout(plan->n, plan->arena_bytes, plan->tuning.tile_bytes);
+    const WsLayout L = plan_layout(plan);
     if (launch_commit(static_cast<const uint8_t *>(ws_dev), L, plan->live_blocks, offset_out_dev,
-                      size_out_dev, live_out_dev, stream) != hipSuccess)
+                      size_out_dev, live_out_dev, pinned_out_dev, stream) != hipSuccess)
         return DEFRAG_EHIP;
     return DEFRAG_OK;
 }

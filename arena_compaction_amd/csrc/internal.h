@@ -25,32 +25,43 @@ constexpr uint64_t kNone = ~0ull;
 
 // Device-resident plan header (first 256 bytes of the workspace).
 struct alignas(256) WsHeader {
-    uint64_t live_bytes;     // LT: sum of live sizes
-    uint64_t live_blocks;    // m
+    uint64_t live_bytes;     // LT: sum of live sizes (pinned included)
+    uint64_t live_blocks;    // m (pinned included)
     uint64_t max_live_end;   // end of the highest live block (0 if none)
     uint64_t bad_key;        // (index << 3) | reason of the first bad entry, kNone if valid
     uint64_t largest_hole;   // longest run outside live blocks, tail included
     uint64_t hole_count;     // number of such runs
     uint64_t moved_blocks;
     uint64_t moved_bytes;
-    uint64_t first_moved;    // index (among live blocks) of the first moved block, m if none
+    uint64_t pinned_blocks;
     uint64_t min_live_size;  // kNone if no live block
-    uint64_t move_begin;     // new offset of the first moved block (LT if none)
+    uint64_t move_begin;     // lowest destination written by the move (kNone if none)
+    uint64_t n_tiles;        // mover tiles
     uint64_t epoch;          // plan epoch, checked by the mover
     uint32_t ticket;         // mover tile ticket counter
     uint32_t status;         // mover status bits (kStatus*)
-    uint64_t pad[19];
+    uint64_t pad[18];
 };
 static_assert(sizeof(WsHeader) == 256, "header size");
 
 constexpr uint32_t kStatusTimeout = 1u;  // a wait gave up, or a tile overflowed LDS
 
-// Per scan-workgroup aggregate of (live size sum, live end max, live count)
-// plus the smallest bad-entry key seen.
+// Element of the plan's scan over table entries.  v is a segmented sum: a
+// pinned entry resets it to its own end (the start of the next segment), a
+// movable live entry adds its size.  The other fields are plain sum / max.
+struct Agg {
+    uint64_t v;      // packed position inside the current segment
+    uint64_t mx;     // highest live end
+    uint64_t cnt;    // live entries
+    uint64_t lsum;   // live bytes
+    uint64_t pcnt;   // pinned entries
+    uint32_t r;      // a pinned entry (segment reset) is inside
+    uint32_t pad;
+};
+
+// Per scan-workgroup aggregate plus the smallest bad-entry key seen.
 struct ScanPart {
-    uint64_t sum;
-    uint64_t maxend;
-    uint64_t count;
+    Agg a;
     uint64_t bad_key;
 };
 
@@ -60,77 +71,135 @@ struct StatPart {
     uint64_t gaps;
     uint64_t moved_blocks;
     uint64_t moved_bytes;
-    uint64_t first_moved;
+    uint64_t min_moved_dst;
     uint64_t min_size;
     uint64_t pad[2];
 };
 
-// Per destination tile: live-block range touching it and the earlier tiles
-// whose sources overlap it (dep_lo > dep_hi means none).
-struct TileRec {
+// One mover tile: the destination bytes [t0, t1) -- a piece of one run of
+// moved blocks, inside one tile-size window -- the live blocks first..last it
+// covers, the shift of its first block, and the earlier tiles whose sources
+// overlap [t0, t1) (dep_lo > dep_hi means none).
+struct alignas(16) TileRec {
+    uint64_t t0;
+    uint64_t t1;
+    uint64_t shift0;
     uint32_t first_block;
     uint32_t last_block;
     uint32_t dep_lo;
     uint32_t dep_hi;
+    uint64_t pad;
 };
+static_assert(sizeof(TileRec) == 48, "tile record size");
+
+constexpr size_t kPerTileBytes = sizeof(uint64_t) + sizeof(TileRec) + sizeof(uint32_t);
 
 struct WsLayout {
-    size_t header, part, prefix, spart, live_dst, live_src, tiles, flags, total;
+    // fixed part (depends on n only)
+    size_t header, part, prefix, spart, tpart, tprefix, live_dst, live_src, live_size,
+        live_pin, tile_base, fixed;
+    // tile part (depends on the tile capacity)
+    size_t tile_start, tiles, flags, total;
     uint64_t n_scan_blocks, max_tiles;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline WsLayout ws_layout(uint64_t n, uint64_t arena_bytes, uint32_t tile_bytes) {
+inline WsLayout ws_fixed(uint64_t n) {
     WsLayout L{};
     L.n_scan_blocks = (n + kScanTile - 1) / kScanTile;
-    uint64_t nb = L.n_scan_blocks ? L.n_scan_blocks : 1;
-    L.max_tiles = arena_bytes / tile_bytes + 2;
+    const uint64_t nb = L.n_scan_blocks ? L.n_scan_blocks : 1;
     size_t at = 0;
-    L.header = at;   at += align256(sizeof(WsHeader));
-    L.part = at;     at += align256(nb * sizeof(ScanPart));
-    L.prefix = at;   at += align256(nb * sizeof(ScanPart));
-    L.spart = at;    at += align256(nb * sizeof(StatPart));
-    L.live_dst = at; at += align256((n + 1) * sizeof(uint64_t));
-    L.live_src = at; at += align256((n + 1) * sizeof(uint64_t));
-    L.tiles = at;    at += align256(L.max_tiles * sizeof(TileRec));
-    L.flags = at;    at += align256(L.max_tiles * sizeof(uint32_t));
+    L.header = at;    at += align256(sizeof(WsHeader));
+    L.part = at;      at += align256(nb * sizeof(ScanPart));
+    L.prefix = at;    at += align256(nb * sizeof(ScanPart));
+    L.spart = at;     at += align256(nb * sizeof(StatPart));
+    L.tpart = at;     at += align256(nb * sizeof(uint64_t));
+    L.tprefix = at;   at += align256(nb * sizeof(uint64_t));
+    L.live_dst = at;  at += align256((n + 1) * sizeof(uint64_t));
+    L.live_src = at;  at += align256((n + 1) * sizeof(uint64_t));
+    L.live_size = at; at += align256((n + 1) * sizeof(uint64_t));
+    L.live_pin = at;  at += align256((n + 1) * sizeof(uint8_t));
+    L.tile_base = at; at += align256((n + 1) * sizeof(uint32_t));
+    L.fixed = at;
+    return L;
+}
+
+inline WsLayout ws_with_tiles(uint64_t n, uint64_t max_tiles) {
+    WsLayout L = ws_fixed(n);
+    L.max_tiles = max_tiles;
+    size_t at = L.fixed;
+    L.tile_start = at; at += align256(max_tiles * sizeof(uint64_t));
+    L.tiles = at;      at += align256(max_tiles * sizeof(TileRec));
+    L.flags = at;      at += align256(max_tiles * sizeof(uint32_t));
     L.total = at;
     return L;
+}
+
+// Tiles a compaction may need: every window of the arena, plus the two
+// partial windows at each end of every run of moved blocks (one run per
+// segment at most, and there are max_pinned + 1 segments).
+inline uint64_t tiles_bound(uint64_t arena_bytes, uint64_t max_pinned, uint32_t tile_bytes) {
+    return arena_bytes / tile_bytes + 2 * (max_pinned + 1) + 2;
+}
+
+// The largest tile capacity whose layout fits in ws_bytes.
+inline uint64_t tiles_fitting(uint64_t n, size_t ws_bytes) {
+    const WsLayout F = ws_fixed(n);
+    if (ws_bytes <= F.fixed) return 0;
+    // upper estimate, then step down past the (at most 3 x 255 bytes of)
+    // alignment padding
+    uint64_t t = (ws_bytes - F.fixed) / kPerTileBytes;
+    while (t > 0 && ws_with_tiles(n, t).total > ws_bytes) --t;
+    return t;
 }
 
 // Table pointers as the kernels see them.
 struct TableView {
     const uint64_t *off;
     const uint64_t *size;
-    const uint8_t *live;  // may be null: all live
+    const uint8_t *live;    // may be null: all live
+    const uint8_t *pinned;  // may be null: none pinned
     uint64_t n;
 };
 
+// Packed live-block arrays (m + 1 entries each).
+struct LiveView {
+    const uint64_t *dst;   // new offset
+    const uint64_t *src;   // old offset
+    const uint64_t *size;
+    const uint8_t *pin;
+};
+
+inline LiveView live_view(const uint8_t *ws, const WsLayout &L) {
+    return LiveView{reinterpret_cast<const uint64_t *>(ws + L.live_dst),
+                    reinterpret_cast<const uint64_t *>(ws + L.live_src),
+                    reinterpret_cast<const uint64_t *>(ws + L.live_size),
+                    reinterpret_cast<const uint8_t *>(ws + L.live_pin)};
+}
+
 // ---- plan.hip ----
+// Scan passes (and, when write_outputs, the tile-count passes).  All
+// asynchronous; the header then holds totals, statistics and n_tiles.
 hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws,
                        const WsLayout &L, uint64_t *new_offset, bool write_outputs,
-                       uint64_t epoch, hipStream_t s);
-hipError_t launch_tiles(uint8_t *ws, const WsLayout &L, uint64_t n_tiles,
-                        uint64_t tile_base, uint32_t tile_bytes, uint64_t move_begin,
-                        uint64_t live_bytes, uint64_t first_moved, uint64_t live_blocks,
-                        hipStream_t s);
+                       uint32_t tile_bytes, uint64_t epoch, hipStream_t s);
+// Tile starts and records for n_tiles tiles (n_tiles <= L.max_tiles).
+hipError_t launch_tiles(uint8_t *ws, const WsLayout &L, uint64_t n_tiles, uint64_t live_blocks,
+                        uint32_t tile_bytes, hipStream_t s);
 hipError_t launch_commit(const uint8_t *ws, const WsLayout &L, uint64_t live_blocks,
                          uint64_t *off_out, uint64_t *size_out, uint8_t *live_out,
-                         hipStream_t s);
+                         uint8_t *pinned_out, hipStream_t s);
 
 // ---- move.hip ----
 struct MoveArgs {
     uint8_t *arena;
-    const uint64_t *live_dst;  // new offset of every live block, [m] = LT
+    const uint64_t *live_dst;  // new offset of every live block
     const uint64_t *live_src;  // old offset of every live block
     const TileRec *tiles;
     uint32_t *flags;
     WsHeader *hdr;
     uint64_t n_tiles;
-    uint64_t tile_base;
-    uint64_t move_begin;
-    uint64_t live_bytes;
     uint64_t epoch;
     uint64_t spin_limit;
     uint32_t tile_bytes;
@@ -140,9 +209,8 @@ hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, uint32_t nontempor
                        int num_cus, hipStream_t s);
 
 // ---- remap.hip ----
-hipError_t launch_remap(const uint64_t *live_dst, const uint64_t *live_src,
-                        uint64_t live_blocks, const uint64_t *h_in, uint64_t *h_out,
-                        uint64_t n_handles, uint64_t *n_invalid, int num_cus,
-                        hipStream_t s);
+hipError_t launch_remap(const LiveView &lv, uint64_t live_blocks, const uint64_t *h_in,
+                        uint64_t *h_out, uint64_t n_handles, uint64_t *n_invalid,
+                        int num_cus, hipStream_t s);
 
 }  // namespace ac

@@ -13,9 +13,11 @@
 // shift of the live block landing on p.  Destination positions are packed,
 // so the source position p + shift(p) rises strictly with p.
 //
-// Design.  The destination range [move_begin, LT) is cut into tiles of T
-// bytes aligned to T.  Workgroups claim tiles in ascending order from an
-// atomic ticket and, per tile:
+// Design.  The moved destinations form runs (one per segment between pinned
+// blocks); each run is cut at every multiple of T into tiles, so a tile is
+// at most one T-aligned window.  The plan records each tile's exact byte
+// range, its blocks, and the earlier tiles it depends on.  Workgroups claim
+// tiles in ascending order from an atomic ticket and, per tile:
 //   1. load every 16-byte source vector of the tile into VGPRs (reads never
 //      wait: a source byte can only be overwritten by the tile owning it as
 //      a destination, which is at or above this tile and waits for it);
@@ -28,9 +30,9 @@
 // how many workgroups are resident.  Self-overlap inside a tile is handled by
 // the workgroup barrier between steps 1 and 4, so a move whose shift is far
 // smaller than its size still runs in tile-sized waves spread over the whole
-// chip rather than shift-sized serial steps.  Blocks whose shift is zero lie
-// entirely below move_begin and are never touched; nothing at or above LT
-// is written.
+// chip rather than shift-sized serial steps.  Blocks whose shift is zero
+// (pinned blocks, and the packed prefix of each segment) are in no tile and
+// are never touched; nor is any byte no block lands on.
 //
 // Vectors are 16 bytes: offsets and sizes are multiples of 32, so a vector
 // never straddles two blocks and both of its addresses are 16-byte aligned.
@@ -60,6 +62,12 @@ __device__ __forceinline__ void store16(uint8_t *p, v4u v) {
     else *q = v;
 }
 
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
 template <int VPT, int NT>
 __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
     extern __shared__ uint64_t lds_dyn[];
@@ -82,23 +90,27 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
 
     while (t < a.n_tiles) {
 
-        const TileRec rec = a.tiles[t];
-        const uint64_t tb = a.tile_base + (uint64_t)t * a.tile_bytes;
-        const uint64_t t0 = tb > a.move_begin ? tb : a.move_begin;
-        const uint64_t te = tb + a.tile_bytes;
-        const uint64_t t1 = te < a.live_bytes ? te : a.live_bytes;
+        // The record is the same for every lane: make each field wave-uniform
+        // (one wait for the record, scalar registers after) -- otherwise the
+        // compiler waits for the record again before every data load below.
+        const TileRec &rp = a.tiles[t];
+        const uint64_t t0 = uniform64(rp.t0);
+        const uint64_t t1 = uniform64(rp.t1);
+        const uint64_t shift0 = uniform64(rp.shift0);
+        const uint32_t first = __builtin_amdgcn_readfirstlane(rp.first_block);
+        const uint32_t last = __builtin_amdgcn_readfirstlane(rp.last_block);
+        const uint32_t dep_lo = __builtin_amdgcn_readfirstlane(rp.dep_lo);
+        const uint32_t dep_hi = __builtin_amdgcn_readfirstlane(rp.dep_hi);
+        const uint64_t tb = t0 & ~((uint64_t)a.tile_bytes - 1);  // the tile's window
         const uint32_t rel0 = (uint32_t)(t0 - tb);
         const uint32_t rel1 = (uint32_t)(t1 - tb);
-        const uint32_t nblk = rec.last_block - rec.first_block + 1u;
+        const uint32_t nblk = last - first + 1u;
         bool ok = nblk <= a.max_blocks;
 
-        uint64_t shift0 = 0;
-        if (nblk == 1u) {
-            shift0 = a.live_src[rec.first_block] - a.live_dst[rec.first_block];
-        } else if (ok) {
+        if (nblk > 1u && ok) {
             for (uint32_t k = tid; k < nblk; k += kMoveThreads) {
-                const uint64_t d = a.live_dst[rec.first_block + k];
-                s_shift[k] = a.live_src[rec.first_block + k] - d;
+                const uint64_t d = a.live_dst[first + k];
+                s_shift[k] = a.live_src[first + k] - d;
                 s_rel[k] = d <= tb ? 0u : (uint32_t)(d - tb);
             }
             __syncthreads();
@@ -129,7 +141,7 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
             uint32_t skip = ok ? 0u : 1u;
             if (!ok) atomicOr(&a.hdr->status, kStatusTimeout);
             __hip_atomic_store(&a.flags[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (uint32_t u = rec.dep_lo; u <= rec.dep_hi && !skip; ++u) {
+            for (uint32_t u = dep_lo; u <= dep_hi && !skip; ++u) {
                 uint64_t polls = 0;
                 while (__hip_atomic_load(&a.flags[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
                     if (++polls > a.spin_limit) {

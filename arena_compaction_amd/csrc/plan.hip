@@ -4,12 +4,17 @@
 // Page: "Ascend 910C cluster tuning: memory-fragment compaction in
 // mixed-precision training", section "Periodic compaction with Ascend C":
 // holes are scanned from low to high addresses and each live tensor gets the
-// downward shift it needs.  Here that is an exclusive scan over the table of
-// the triple (live size, live end, live count):
-//   new offset of entry i   = sum of live sizes before i
-//   hole just below live i  = offset_i - (end of the previous live block)
-//                           = offset_i - max of live ends before i
-//   index of i among live   = count of live entries before i
+// downward shift it needs.  Section "Cutting alloc and free at the source" of
+// the same page keeps the parameter region at fixed addresses: a pinned entry
+// stays put and splits the arena into segments that pack independently.
+// Here all of it is one exclusive scan over the table of
+//   v    : packed position, reset to a pinned entry's end (segmented sum)
+//   mx   : max end of the live entries so far
+//   cnt  : live entries so far (index into the packed live arrays)
+//   lsum : live bytes so far;   pcnt: pinned entries so far
+// so that
+//   new offset of entry i   = offset_i if pinned, else v before i
+//   hole just below live i  = offset_i - (mx before i)
 // Section "Total-usage monitoring misses fragmentation" of the same page asks
 // for the free total and the largest contiguous free block; section 3.2 of
 // "CANN memory management and memory optimisation" defines the ratio
@@ -17,12 +22,14 @@
 // merges adjacent free blocks, section 2.2), so one pass over live entries in
 // order sees every hole once, plus the tail above the highest live block.
 //
-// Three passes (n up to 2^32 entries): per-workgroup aggregates, a
-// single-workgroup spine scan of the aggregates, then a downsweep that writes
-// new offsets, the packed live-block arrays and per-workgroup hole/move
-// statistics, reduced by a final single-workgroup pass.  Table traffic is
-// 17 B per entry read twice plus 8 B per entry of new offsets and 16 B per
-// live block written.
+// Passes (n up to 2^32 entries): per-workgroup aggregates, a single-workgroup
+// spine scan, a downsweep that writes new offsets, the packed live-block
+// arrays (new and old offset, size, pinned flag) and per-workgroup
+// statistics, and a single-workgroup finish.  Then the mover's tiles: every
+// moved block counts the tiles that start inside it (a run of moved blocks
+// starts one, and so does every tile-size boundary inside a run); a scan of
+// those counts gives each block its first tile, and one lane per tile writes
+// the tile's start, its range, its blocks and its dependencies.
 #include "internal.h"
 
 namespace ac {
@@ -31,76 +38,104 @@ namespace {
 __device__ inline uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ inline uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
-// Reason code of entry i (0 when it passes); checks in the documented order.
-__device__ inline uint32_t entry_reason(uint64_t i, uint64_t o, uint64_t s, uint32_t l,
-                                        uint64_t arena_bytes, uint64_t prev_end) {
-    if (s == 0) return 1;
-    if ((o | s) & 31u) return 2;
-    if (l > 1u) return 3;
-    if (o > arena_bytes || s > arena_bytes - o) return 4;
-    if (i > 0 && prev_end > o) return 5;
-    return 0;
+__device__ inline Agg agg_zero() { return Agg{0, 0, 0, 0, 0, 0, 0}; }
+
+// Associative, not commutative: a before b.
+__device__ inline Agg combine(const Agg &a, const Agg &b) {
+    Agg c;
+    c.r = a.r | b.r;
+    c.v = b.r ? b.v : a.v + b.v;
+    c.mx = umax64(a.mx, b.mx);
+    c.cnt = a.cnt + b.cnt;
+    c.lsum = a.lsum + b.lsum;
+    c.pcnt = a.pcnt + b.pcnt;
+    c.pad = 0;
+    return c;
 }
 
-// Inclusive wave64 scan of (a: sum, b: max, c: sum).
-__device__ inline void wave_incl_scan3(uint64_t &a, uint64_t &b, uint64_t &c) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint64_t ya = __shfl_up(a, d, 64);
-        const uint64_t yb = __shfl_up(b, d, 64);
-        const uint64_t yc = __shfl_up(c, d, 64);
-        if (lane >= d) {
-            a += ya;
-            b = umax64(b, yb);
-            c += yc;
-        }
+__device__ inline Agg element(uint64_t o, uint64_t s, uint32_t l, uint32_t p) {
+    Agg e = agg_zero();
+    if (p) {
+        e.r = 1;
+        e.v = o + s;
+    } else if (l) {
+        e.v = s;
     }
+    if (l) {
+        e.mx = o + s;
+        e.cnt = 1;
+        e.lsum = s;
+    }
+    e.pcnt = p;
+    return e;
 }
 
-// Exclusive workgroup scan of (a, b, c) with identity (0, 0, 0); also returns
-// the workgroup totals.  sh needs 3 * NT/64 entries.
+__device__ inline Agg shfl_up_agg(const Agg &a, int d) {
+    Agg b;
+    b.v = __shfl_up(a.v, d, 64);
+    b.mx = __shfl_up(a.mx, d, 64);
+    b.cnt = __shfl_up(a.cnt, d, 64);
+    b.lsum = __shfl_up(a.lsum, d, 64);
+    b.pcnt = __shfl_up(a.pcnt, d, 64);
+    b.r = __shfl_up(a.r, d, 64);
+    b.pad = 0;
+    return b;
+}
+
+// Exclusive workgroup scan in thread order; also returns the total.
+// sh needs NT/64 entries.
 template <int NT>
-__device__ inline void block_excl_scan3(uint64_t &a, uint64_t &b, uint64_t &c,
-                                        uint64_t &ta, uint64_t &tb, uint64_t &tc,
-                                        uint64_t *sh) {
+__device__ inline Agg block_excl(const Agg &x, Agg &total, Agg *sh) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    uint64_t ia = a, ib = b, ic = c;
-    wave_incl_scan3(ia, ib, ic);
-    if (lane == 63) {
-        sh[w] = ia;
-        sh[NW + w] = ib;
-        sh[2 * NW + w] = ic;
+    Agg inc = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const Agg y = shfl_up_agg(inc, d);
+        if (lane >= d) inc = combine(y, inc);
     }
+    if (lane == 63) sh[w] = inc;
     __syncthreads();
-    uint64_t pa = 0, pb = 0, pc = 0;
-    ta = 0;
-    tb = 0;
-    tc = 0;
+    Agg pre = agg_zero(), tot = agg_zero();
 #pragma unroll
     for (int k = 0; k < NW; ++k) {
-        const uint64_t xa = sh[k], xb = sh[NW + k], xc = sh[2 * NW + k];
-        if (k < w) {
-            pa += xa;
-            pb = umax64(pb, xb);
-            pc += xc;
-        }
-        ta += xa;
-        tb = umax64(tb, xb);
-        tc += xc;
+        const Agg z = sh[k];
+        if (k < w) pre = combine(pre, z);
+        tot = combine(tot, z);
     }
-    uint64_t ea = __shfl_up(ia, 1, 64), eb = __shfl_up(ib, 1, 64), ec = __shfl_up(ic, 1, 64);
-    if (lane == 0) {
-        ea = 0;
-        eb = 0;
-        ec = 0;
-    }
-    a = pa + ea;
-    b = umax64(pb, eb);
-    c = pc + ec;
+    Agg ex = shfl_up_agg(inc, 1);
+    if (lane == 0) ex = agg_zero();
     __syncthreads();
+    total = tot;
+    return combine(pre, ex);
+}
+
+// Exclusive workgroup sum of u64; also returns the total.  sh: NT/64 slots.
+template <int NT>
+__device__ inline uint64_t block_excl_sum(uint64_t x, uint64_t &total, uint64_t *sh) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    uint64_t inc = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint64_t y = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += y;
+    }
+    if (lane == 63) sh[w] = inc;
+    __syncthreads();
+    uint64_t pre = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        if (k < w) pre += sh[k];
+        tot += sh[k];
+    }
+    uint64_t ex = __shfl_up(inc, 1, 64);
+    if (lane == 0) ex = 0;
+    __syncthreads();
+    total = tot;
+    return pre + ex;
 }
 
 // Workgroup reductions through LDS (NT threads, sh has NT/64 slots).
@@ -122,12 +157,29 @@ struct OpAdd { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { re
 struct OpMax { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return umax64(a, b); } };
 struct OpMin { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return umin64(a, b); } };
 
-// Pass 1: per-workgroup (live size sum, live end max, live count, first bad key).
+// Reason code of entry i (0 when it passes); checks in the documented order.
+__device__ inline uint32_t entry_reason(uint64_t i, uint64_t o, uint64_t s, uint32_t l,
+                                        uint32_t p, uint64_t arena_bytes, uint64_t prev_end) {
+    if (s == 0) return 1;
+    if ((o | s) & 31u) return 2;
+    if (l > 1u) return 3;
+    if (p > 1u || (p == 1u && l == 0u)) return 7;
+    if (o > arena_bytes || s > arena_bytes - o) return 4;
+    if (i > 0 && prev_end > o) return 5;
+    return 0;
+}
+
+__device__ inline uint32_t live_of(const TableView &t, uint64_t i) { return t.live ? t.live[i] : 1u; }
+__device__ inline uint32_t pin_of(const TableView &t, uint64_t i) { return t.pinned ? t.pinned[i] : 0u; }
+
+// Pass 1: per-workgroup aggregate and first bad key.
 __global__ __launch_bounds__(kScanThreads) void k_scan_partials(TableView t, uint64_t arena_bytes,
                                                                 ScanPart *part) {
-    __shared__ uint64_t sh[kScanThreads / 64];
+    __shared__ Agg sh[kScanThreads / 64];
+    __shared__ uint64_t shr[kScanThreads / 64];
     const uint64_t i0 = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanItems;
-    uint64_t sum = 0, mx = 0, cnt = 0, bad = kNone;
+    Agg a = agg_zero();
+    uint64_t bad = kNone;
     uint64_t prev_end = 0;
     if (i0 > 0 && i0 < t.n) prev_end = t.off[i0 - 1] + t.size[i0 - 1];
 #pragma unroll
@@ -135,169 +187,154 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_partials(TableView t, uin
         const uint64_t i = i0 + k;
         if (i < t.n) {
             const uint64_t o = t.off[i], s = t.size[i];
-            const uint32_t l = t.live ? t.live[i] : 1u;
-            const uint32_t r = entry_reason(i, o, s, l, arena_bytes, prev_end);
+            const uint32_t l = live_of(t, i), p = pin_of(t, i);
+            const uint32_t r = entry_reason(i, o, s, l, p, arena_bytes, prev_end);
             if (r) bad = umin64(bad, (i << 3) | r);
-            if (l) {
-                sum += s;
-                mx = umax64(mx, o + s);
-                cnt += 1;
-            }
+            a = combine(a, element(o, s, l ? 1u : 0u, p ? 1u : 0u));
             prev_end = o + s;
         }
     }
-    sum = block_reduce<kScanThreads>(sum, sh, OpAdd());
-    mx = block_reduce<kScanThreads>(mx, sh, OpMax());
-    cnt = block_reduce<kScanThreads>(cnt, sh, OpAdd());
-    bad = block_reduce<kScanThreads>(bad, sh, OpMin());
-    if (threadIdx.x == 0) part[blockIdx.x] = ScanPart{sum, mx, cnt, bad};
+    Agg total;
+    block_excl<kScanThreads>(a, total, sh);
+    bad = block_reduce<kScanThreads>(bad, shr, OpMin());
+    if (threadIdx.x == 0) part[blockIdx.x] = ScanPart{total, bad};
 }
 
 // Pass 2 (one workgroup): exclusive scan of the aggregates; table totals.
 __global__ __launch_bounds__(kSpineThreads) void k_scan_spine(const ScanPart *part, ScanPart *prefix,
                                                               uint64_t nb, WsHeader *hdr) {
-    __shared__ uint64_t sh[3 * kSpineThreads / 64];
+    __shared__ Agg sh[kSpineThreads / 64];
     __shared__ uint64_t shr[kSpineThreads / 64];
-    uint64_t ca = 0, cb = 0, cc = 0, bad = kNone;
+    Agg carry = agg_zero();
+    uint64_t bad = kNone;
     for (uint64_t base = 0; base < nb; base += kSpineThreads) {
         const uint64_t j = base + threadIdx.x;
-        uint64_t a = 0, b = 0, c = 0;
+        Agg x = agg_zero();
         if (j < nb) {
-            const ScanPart p = part[j];
-            a = p.sum;
-            b = p.maxend;
-            c = p.count;
-            bad = umin64(bad, p.bad_key);
+            x = part[j].a;
+            bad = umin64(bad, part[j].bad_key);
         }
-        uint64_t ta, tb, tc;
-        block_excl_scan3<kSpineThreads>(a, b, c, ta, tb, tc, sh);
-        if (j < nb) prefix[j] = ScanPart{ca + a, umax64(cb, b), cc + c, 0};
-        ca += ta;
-        cb = umax64(cb, tb);
-        cc += tc;
+        Agg total;
+        const Agg ex = block_excl<kSpineThreads>(x, total, sh);
+        if (j < nb) prefix[j] = ScanPart{combine(carry, ex), 0};
+        carry = combine(carry, total);
     }
     bad = block_reduce<kSpineThreads>(bad, shr, OpMin());
     if (threadIdx.x == 0) {
-        hdr->live_bytes = ca;
-        hdr->max_live_end = cb;
-        hdr->live_blocks = cc;
+        hdr->live_bytes = carry.lsum;
+        hdr->max_live_end = carry.mx;
+        hdr->live_blocks = carry.cnt;
+        hdr->pinned_blocks = carry.pcnt;
         hdr->bad_key = bad;
     }
 }
 
+struct LiveOut {
+    uint64_t *dst, *src, *size;
+    uint8_t *pin;
+};
+
 // Pass 3: new offsets, packed live arrays, per-workgroup hole/move stats.
 __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const ScanPart *prefix,
                                                             const WsHeader *hdr, uint64_t *new_offset,
-                                                            uint64_t *live_dst, uint64_t *live_src,
-                                                            StatPart *spart, int write_outputs) {
-    __shared__ uint64_t sh[3 * kScanThreads / 64];
+                                                            LiveOut lo, StatPart *spart,
+                                                            int write_outputs) {
+    __shared__ Agg sh[kScanThreads / 64];
+    __shared__ uint64_t shr[kScanThreads / 64];
     if (hdr->bad_key != kNone) return;  // invalid table: write nothing
     const uint64_t i0 = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanItems;
     uint64_t o[kScanItems], s[kScanItems];
-    uint32_t l[kScanItems];
-    uint64_t a = 0, b = 0, c = 0;
+    uint32_t l[kScanItems], p[kScanItems];
+    Agg a = agg_zero();
 #pragma unroll
     for (uint32_t k = 0; k < kScanItems; ++k) {
         const uint64_t i = i0 + k;
         o[k] = 0;
         s[k] = 0;
         l[k] = 0;
+        p[k] = 0;
         if (i < t.n) {
             o[k] = t.off[i];
             s[k] = t.size[i];
-            l[k] = t.live ? t.live[i] : 1u;
-            if (l[k]) {
-                a += s[k];
-                b = umax64(b, o[k] + s[k]);
-                c += 1;
-            }
+            l[k] = live_of(t, i) ? 1u : 0u;
+            p[k] = pin_of(t, i) ? 1u : 0u;
+            a = combine(a, element(o[k], s[k], l[k], p[k]));
         }
     }
-    uint64_t ta, tb, tc;
-    block_excl_scan3<kScanThreads>(a, b, c, ta, tb, tc, sh);
-    const ScanPart P = prefix[blockIdx.x];
-    uint64_t run_sum = P.sum + a;
-    uint64_t run_end = umax64(P.maxend, b);
-    uint64_t run_cnt = P.count + c;
-    uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, first_moved = kNone,
-             min_size = kNone;
+    Agg total;
+    const Agg ex = block_excl<kScanThreads>(a, total, sh);
+    Agg run = combine(prefix[blockIdx.x].a, ex);
+    uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, min_dst = kNone, min_size = kNone;
 #pragma unroll
     for (uint32_t k = 0; k < kScanItems; ++k) {
         const uint64_t i = i0 + k;
         if (i < t.n) {
-            if (write_outputs && new_offset) new_offset[i] = run_sum;
+            const uint64_t nw = p[k] ? o[k] : run.v;
+            if (write_outputs && new_offset) new_offset[i] = nw;
             if (l[k]) {
                 if (write_outputs) {
-                    live_dst[run_cnt] = run_sum;
-                    live_src[run_cnt] = o[k];
+                    lo.dst[run.cnt] = nw;
+                    lo.src[run.cnt] = o[k];
+                    lo.size[run.cnt] = s[k];
+                    lo.pin[run.cnt] = (uint8_t)p[k];
                 }
-                const uint64_t gap = o[k] - run_end;
+                const uint64_t gap = o[k] - run.mx;
                 if (gap) {
                     gaps += 1;
                     max_gap = umax64(max_gap, gap);
                 }
-                if (o[k] != run_sum) {
+                if (o[k] != nw) {
                     moved += 1;
                     moved_bytes += s[k];
-                    first_moved = umin64(first_moved, run_cnt);
+                    min_dst = umin64(min_dst, nw);
                 }
                 min_size = umin64(min_size, s[k]);
-                run_sum += s[k];
-                run_end = o[k] + s[k];
-                run_cnt += 1;
             }
+            run = combine(run, element(o[k], s[k], l[k], p[k]));
         }
     }
-    max_gap = block_reduce<kScanThreads>(max_gap, sh, OpMax());
-    gaps = block_reduce<kScanThreads>(gaps, sh, OpAdd());
-    moved = block_reduce<kScanThreads>(moved, sh, OpAdd());
-    moved_bytes = block_reduce<kScanThreads>(moved_bytes, sh, OpAdd());
-    first_moved = block_reduce<kScanThreads>(first_moved, sh, OpMin());
-    min_size = block_reduce<kScanThreads>(min_size, sh, OpMin());
+    max_gap = block_reduce<kScanThreads>(max_gap, shr, OpMax());
+    gaps = block_reduce<kScanThreads>(gaps, shr, OpAdd());
+    moved = block_reduce<kScanThreads>(moved, shr, OpAdd());
+    moved_bytes = block_reduce<kScanThreads>(moved_bytes, shr, OpAdd());
+    min_dst = block_reduce<kScanThreads>(min_dst, shr, OpMin());
+    min_size = block_reduce<kScanThreads>(min_size, shr, OpMin());
     if (threadIdx.x == 0)
-        spart[blockIdx.x] = StatPart{max_gap, gaps, moved, moved_bytes, first_moved, min_size, {0, 0}};
+        spart[blockIdx.x] = StatPart{max_gap, gaps, moved, moved_bytes, min_dst, min_size, {0, 0}};
 }
 
-// Pass 4 (one workgroup): reduce the statistics, add the tail hole, and set
-// the move range.
+// Pass 4 (one workgroup): reduce the statistics, add the tail hole.
 __global__ __launch_bounds__(kSpineThreads) void k_scan_finish(const StatPart *spart, uint64_t nb,
                                                                uint64_t arena_bytes, WsHeader *hdr,
-                                                               uint64_t *live_dst, uint64_t *live_src,
                                                                int write_outputs, uint64_t epoch) {
     __shared__ uint64_t sh[kSpineThreads / 64];
     if (hdr->bad_key != kNone) return;
-    uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, first_moved = kNone,
-             min_size = kNone;
+    uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, min_dst = kNone, min_size = kNone;
     for (uint64_t j = threadIdx.x; j < nb; j += kSpineThreads) {
-        const StatPart p = spart[j];
-        max_gap = umax64(max_gap, p.max_gap);
-        gaps += p.gaps;
-        moved += p.moved_blocks;
-        moved_bytes += p.moved_bytes;
-        first_moved = umin64(first_moved, p.first_moved);
-        min_size = umin64(min_size, p.min_size);
+        const StatPart q = spart[j];
+        max_gap = umax64(max_gap, q.max_gap);
+        gaps += q.gaps;
+        moved += q.moved_blocks;
+        moved_bytes += q.moved_bytes;
+        min_dst = umin64(min_dst, q.min_moved_dst);
+        min_size = umin64(min_size, q.min_size);
     }
     max_gap = block_reduce<kSpineThreads>(max_gap, sh, OpMax());
     gaps = block_reduce<kSpineThreads>(gaps, sh, OpAdd());
     moved = block_reduce<kSpineThreads>(moved, sh, OpAdd());
     moved_bytes = block_reduce<kSpineThreads>(moved_bytes, sh, OpAdd());
-    first_moved = block_reduce<kSpineThreads>(first_moved, sh, OpMin());
+    min_dst = block_reduce<kSpineThreads>(min_dst, sh, OpMin());
     min_size = block_reduce<kSpineThreads>(min_size, sh, OpMin());
     if (threadIdx.x == 0) {
-        const uint64_t m = hdr->live_blocks;
-        const uint64_t lt = hdr->live_bytes;
         const uint64_t tail = arena_bytes - hdr->max_live_end;
         hdr->largest_hole = umax64(max_gap, tail);
         hdr->hole_count = gaps + (tail ? 1 : 0);
         hdr->moved_blocks = moved;
         hdr->moved_bytes = moved_bytes;
-        hdr->first_moved = first_moved == kNone ? m : first_moved;
         hdr->min_live_size = min_size;
+        hdr->move_begin = min_dst;
         // plan fields: a statistics-only pass leaves an existing plan intact
         if (write_outputs) {
-            live_dst[m] = lt;
-            live_src[m] = arena_bytes;
-            hdr->move_begin = first_moved != kNone ? live_dst[first_moved] : lt;
             hdr->epoch = epoch;
             hdr->ticket = 0;
             hdr->status = 0;
@@ -305,82 +342,186 @@ __global__ __launch_bounds__(kSpineThreads) void k_scan_finish(const StatPart *s
     }
 }
 
-// Largest k in [lo, hi) with a[k] <= x, or lo - 1 if none (as int64).
-__device__ inline int64_t last_le(const uint64_t *a, int64_t lo, int64_t hi, uint64_t x) {
-    int64_t l = lo, h = hi;  // find first index with a[k] > x in [lo, hi)
+// ---------------------------------------------------------------------------
+// Tiles.  A run is a maximal sequence of moved live blocks; its destinations
+// are contiguous (packed inside one segment).  Its tiles are the pieces of it
+// inside each tile-size window: one starts at the run's first byte, and one at
+// every multiple of T inside the run.
+
+__device__ inline bool moved_at(const LiveView &lv, uint64_t k) { return lv.src[k] != lv.dst[k]; }
+
+// Tiles starting inside live block k (0 if k did not move).
+__device__ inline uint64_t tiles_in_block(const LiveView &lv, uint64_t k, uint64_t T) {
+    if (!moved_at(lv, k)) return 0;
+    const bool start = (k == 0) || !moved_at(lv, k - 1);
+    const uint64_t a = lv.dst[k], b = a + lv.size[k];
+    const uint64_t mult = (b + T - 1) / T - (a + T - 1) / T;  // multiples of T in [a, b)
+    return mult + ((start && (a & (T - 1))) ? 1 : 0);
+}
+
+// Pass 5: per-workgroup tile counts over the live blocks.
+__global__ __launch_bounds__(kScanThreads) void k_tcount_partials(LiveView lv, const WsHeader *hdr,
+                                                                  uint64_t T, uint64_t *tpart) {
+    __shared__ uint64_t sh[kScanThreads / 64];
+    if (hdr->bad_key != kNone) return;
+    const uint64_t m = hdr->live_blocks;
+    const uint64_t k0 = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanItems;
+    uint64_t c = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kScanItems; ++j)
+        if (k0 + j < m) c += tiles_in_block(lv, k0 + j, T);
+    c = block_reduce<kScanThreads>(c, sh, OpAdd());
+    if (threadIdx.x == 0) tpart[blockIdx.x] = c;
+}
+
+// Pass 6 (one workgroup): exclusive scan of the counts; n_tiles.
+__global__ __launch_bounds__(kSpineThreads) void k_tcount_spine(const uint64_t *tpart, uint64_t *tprefix,
+                                                                uint64_t nb, WsHeader *hdr) {
+    __shared__ uint64_t sh[kSpineThreads / 64];
+    if (hdr->bad_key != kNone) return;
+    uint64_t carry = 0;
+    for (uint64_t base = 0; base < nb; base += kSpineThreads) {
+        const uint64_t j = base + threadIdx.x;
+        const uint64_t x = j < nb ? tpart[j] : 0;
+        uint64_t total;
+        const uint64_t ex = block_excl_sum<kSpineThreads>(x, total, sh);
+        if (j < nb) tprefix[j] = carry + ex;
+        carry += total;
+    }
+    if (threadIdx.x == 0) hdr->n_tiles = carry;
+}
+
+// Pass 7: each live block's first tile index (a block with no tile gets the
+// same index as the next block that has one, so tile t belongs to the last
+// block whose first tile index is <= t).
+__global__ __launch_bounds__(kScanThreads) void k_tcount_down(LiveView lv, const WsHeader *hdr,
+                                                              uint64_t T, const uint64_t *tprefix,
+                                                              uint32_t *tile_base) {
+    __shared__ uint64_t sh[kScanThreads / 64];
+    if (hdr->bad_key != kNone) return;
+    const uint64_t m = hdr->live_blocks;
+    const uint64_t k0 = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanItems;
+    uint64_t c[kScanItems];
+    uint64_t sum = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kScanItems; ++j) {
+        c[j] = (k0 + j < m) ? tiles_in_block(lv, k0 + j, T) : 0;
+        sum += c[j];
+    }
+    uint64_t total;
+    uint64_t run = tprefix[blockIdx.x] + block_excl_sum<kScanThreads>(sum, total, sh);
+#pragma unroll
+    for (uint32_t j = 0; j < kScanItems; ++j) {
+        if (k0 + j < m) tile_base[k0 + j] = (uint32_t)run;
+        run += c[j];
+    }
+}
+
+// Largest k in [lo, hi) with a[k] <= x, or lo - 1 if none.
+template <typename T>
+__device__ inline int64_t last_le(const T *a, int64_t lo, int64_t hi, uint64_t x) {
+    int64_t l = lo, h = hi;  // first index with a[k] > x in [lo, hi)
     while (l < h) {
         const int64_t mid = l + ((h - l) >> 1);
-        if (a[mid] <= x) l = mid + 1;
+        if ((uint64_t)a[mid] <= x) l = mid + 1;
         else h = mid;
     }
     return l - 1;
 }
 
-// Tile table: one thread per destination tile.  Tile t covers destination
-// bytes [max(base + tT, begin), min(base + (t+1)T, LT)).  The move writes
-// p from p + shift(p); a tile may only write once every tile whose source
-// range overlaps its destination has read.  Sources move strictly upward
-// with destinations, so those sources come from one destination interval no
-// longer than T: at most two tiles, both at or below t.
-__global__ __launch_bounds__(256) void k_tiles(const uint64_t *live_dst, const uint64_t *live_src,
-                                               TileRec *tiles, uint32_t *flags, uint64_t n_tiles,
-                                               uint64_t base, uint64_t T, uint64_t begin, uint64_t lt,
-                                               uint64_t k0, uint64_t m) {
+// Pass 8: one lane per tile writes its start.
+__global__ __launch_bounds__(256) void k_tile_starts(LiveView lv, const uint32_t *tile_base,
+                                                     uint64_t m, uint64_t n_tiles, uint64_t T,
+                                                     uint64_t *tile_start) {
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= n_tiles) return;
-    const uint64_t tb = base + t * T;
-    const uint64_t t0 = umax64(tb, begin);
-    const uint64_t t1 = umin64(tb + T, lt);
-    const int64_t first = last_le(live_dst, (int64_t)k0, (int64_t)m, t0);
-    const int64_t last = last_le(live_dst, (int64_t)k0, (int64_t)m, t1 - 1);
-    // first moved block whose source ends above t0
-    int64_t l = (int64_t)k0, h = (int64_t)m;
+    const int64_t k = last_le(tile_base, 0, (int64_t)m, t);
+    const uint64_t j = t - tile_base[k];
+    const uint64_t a = lv.dst[k];
+    const bool start = (k == 0) || !moved_at(lv, (uint64_t)k - 1);
+    const uint64_t lead = (start && (a & (T - 1))) ? 1 : 0;
+    const uint64_t first_mult = (a + T - 1) & ~(T - 1);
+    tile_start[t] = (j < lead) ? a : first_mult + (j - lead) * T;
+}
+
+// Pass 9: one lane per tile.  [t0, t1) = the run's bytes from the tile start
+// up to the next tile start, the window end or the run end.  A tile may write
+// only once every tile whose sources overlap [t0, t1) has read them.  Sources
+// rise strictly with destinations (src = dst + shift, shifts never negative,
+// order kept), so the destinations whose sources lie in [t0, t1) are at most
+// t1 - t0 consecutive live bytes, all at or below [t0, t1): their tiles are a
+// short range ending at or before this one.
+__global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile_start, uint64_t m,
+                                               uint64_t n_tiles, uint64_t T, TileRec *tiles,
+                                               uint32_t *flags) {
+    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n_tiles) return;
+    const uint64_t t0 = tile_start[t];
+    uint64_t bound = (t0 & ~(T - 1)) + T;
+    if (t + 1 < n_tiles) bound = umin64(bound, tile_start[t + 1]);
+    const int64_t first = last_le(lv.dst, 0, (int64_t)m, t0);
+    const int64_t last_any = last_le(lv.dst, first, (int64_t)m, bound - 1);
+    // blocks first..last_any: the run's moved blocks, then only unmoved ones
+    int64_t l = first + 1, h = last_any + 1;  // first unmoved block in (first, last_any]
     while (l < h) {
         const int64_t mid = l + ((h - l) >> 1);
-        const uint64_t src_end = live_src[mid] + (live_dst[mid + 1] - live_dst[mid]);
-        if (src_end <= t0) l = mid + 1;
+        if (moved_at(lv, (uint64_t)mid)) l = mid + 1;
         else h = mid;
     }
+    const int64_t last = l - 1;
+    const uint64_t t1 = umin64(bound, lv.dst[last] + lv.size[last]);
+    // sources overlapping [t0, t1): first block whose source ends above t0 ...
+    int64_t lo = 0, hi = (int64_t)m;
+    while (lo < hi) {
+        const int64_t mid = lo + ((hi - lo) >> 1);
+        if (lv.src[mid] + lv.size[mid] <= t0) lo = mid + 1;
+        else hi = mid;
+    }
     uint32_t dep_lo = 1, dep_hi = 0;  // empty
-    if (l < (int64_t)m && live_src[l] < t1 && t > 0) {
-        const uint64_t j = (uint64_t)l;
-        const uint64_t q_lo = live_dst[j] + (t0 > live_src[j] ? t0 - live_src[j] : 0);
-        const int64_t c = last_le(live_src, (int64_t)j, (int64_t)m, t1 - 1);
-        const uint64_t cs = live_dst[c + 1] - live_dst[c];
-        const uint64_t q_hi = live_dst[c] + umin64(cs, t1 - live_src[c]) - 1;
-        const uint64_t lo_t = (q_lo - base) / T;
-        uint64_t hi_t = (q_hi - base) / T;
-        if (hi_t > t - 1) hi_t = t - 1;
-        if (lo_t <= hi_t) {
-            dep_lo = (uint32_t)lo_t;
-            dep_hi = (uint32_t)hi_t;
+    if (lo < (int64_t)m && lv.src[lo] < t1 && t > 0) {
+        const uint64_t j = (uint64_t)lo;
+        const uint64_t q_lo = lv.dst[j] + (t0 > lv.src[j] ? t0 - lv.src[j] : 0);
+        // ... and the last block whose source starts below t1
+        const int64_t c = last_le(lv.src, (int64_t)j, (int64_t)m, t1 - 1);
+        const uint64_t q_hi = lv.dst[c] + umin64(lv.size[c], t1 - lv.src[c]) - 1;
+        const int64_t u_lo = last_le(tile_start, 0, (int64_t)n_tiles, q_lo);
+        int64_t u_hi = last_le(tile_start, 0, (int64_t)n_tiles, q_hi);
+        if (u_hi > (int64_t)t - 1) u_hi = (int64_t)t - 1;
+        const int64_t d_lo = u_lo < 0 ? 0 : u_lo;
+        if (u_hi >= d_lo) {
+            dep_lo = (uint32_t)d_lo;
+            dep_hi = (uint32_t)u_hi;
         }
     }
-    tiles[t] = TileRec{(uint32_t)first, (uint32_t)last, dep_lo, dep_hi};
+    tiles[t] = TileRec{t0, t1, lv.src[first] - lv.dst[first], (uint32_t)first, (uint32_t)last,
+                       dep_lo, dep_hi, 0};
     flags[t] = 0u;
 }
 
-__global__ void k_commit(const uint64_t *live_dst, uint64_t m, uint64_t *off_out,
-                         uint64_t *size_out, uint8_t *live_out) {
+__global__ void k_commit(LiveView lv, uint64_t m, uint64_t *off_out, uint64_t *size_out,
+                         uint8_t *live_out, uint8_t *pinned_out) {
     for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < m;
          k += (uint64_t)gridDim.x * blockDim.x) {
-        const uint64_t d = live_dst[k];
-        if (off_out) off_out[k] = d;
-        if (size_out) size_out[k] = live_dst[k + 1] - d;
+        if (off_out) off_out[k] = lv.dst[k];
+        if (size_out) size_out[k] = lv.size[k];
         if (live_out) live_out[k] = 1;
+        if (pinned_out) pinned_out[k] = lv.pin[k];
     }
 }
 
 }  // namespace
 
 hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsLayout &L,
-                       uint64_t *new_offset, bool write_outputs, uint64_t epoch, hipStream_t s) {
+                       uint64_t *new_offset, bool write_outputs, uint32_t tile_bytes,
+                       uint64_t epoch, hipStream_t s) {
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.header);
     ScanPart *part = reinterpret_cast<ScanPart *>(ws + L.part);
     ScanPart *prefix = reinterpret_cast<ScanPart *>(ws + L.prefix);
     StatPart *spart = reinterpret_cast<StatPart *>(ws + L.spart);
-    uint64_t *live_dst = reinterpret_cast<uint64_t *>(ws + L.live_dst);
-    uint64_t *live_src = reinterpret_cast<uint64_t *>(ws + L.live_src);
+    LiveOut lo{reinterpret_cast<uint64_t *>(ws + L.live_dst),
+               reinterpret_cast<uint64_t *>(ws + L.live_src),
+               reinterpret_cast<uint64_t *>(ws + L.live_size),
+               reinterpret_cast<uint8_t *>(ws + L.live_pin)};
     const uint64_t nb = L.n_scan_blocks;
     if (nb) {
         hipLaunchKernelGGL(k_scan_partials, dim3((uint32_t)nb), dim3(kScanThreads), 0, s, t,
@@ -389,36 +530,50 @@ hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, co
     hipLaunchKernelGGL(k_scan_spine, dim3(1), dim3(kSpineThreads), 0, s, part, prefix, nb, hdr);
     if (nb) {
         hipLaunchKernelGGL(k_scan_down, dim3((uint32_t)nb), dim3(kScanThreads), 0, s, t, prefix,
-                           hdr, new_offset, live_dst, live_src, spart, write_outputs ? 1 : 0);
+                           hdr, new_offset, lo, spart, write_outputs ? 1 : 0);
     }
     hipLaunchKernelGGL(k_scan_finish, dim3(1), dim3(kSpineThreads), 0, s, spart, nb, arena_bytes,
-                       hdr, live_dst, live_src, write_outputs ? 1 : 0, epoch);
+                       hdr, write_outputs ? 1 : 0, epoch);
+    if (write_outputs) {
+        const LiveView lv = live_view(ws, L);
+        uint64_t *tpart = reinterpret_cast<uint64_t *>(ws + L.tpart);
+        uint64_t *tprefix = reinterpret_cast<uint64_t *>(ws + L.tprefix);
+        uint32_t *tile_base = reinterpret_cast<uint32_t *>(ws + L.tile_base);
+        const uint64_t gnb = nb ? nb : 1;  // live blocks <= entries
+        hipLaunchKernelGGL(k_tcount_partials, dim3((uint32_t)gnb), dim3(kScanThreads), 0, s, lv,
+                           hdr, (uint64_t)tile_bytes, tpart);
+        hipLaunchKernelGGL(k_tcount_spine, dim3(1), dim3(kSpineThreads), 0, s, tpart, tprefix, gnb,
+                           hdr);
+        hipLaunchKernelGGL(k_tcount_down, dim3((uint32_t)gnb), dim3(kScanThreads), 0, s, lv, hdr,
+                           (uint64_t)tile_bytes, tprefix, tile_base);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_tiles(uint8_t *ws, const WsLayout &L, uint64_t n_tiles, uint64_t tile_base,
-                        uint32_t tile_bytes, uint64_t move_begin, uint64_t live_bytes,
-                        uint64_t first_moved, uint64_t live_blocks, hipStream_t s) {
+hipError_t launch_tiles(uint8_t *ws, const WsLayout &L, uint64_t n_tiles, uint64_t live_blocks,
+                        uint32_t tile_bytes, hipStream_t s) {
     if (n_tiles == 0) return hipSuccess;
-    const uint64_t *live_dst = reinterpret_cast<const uint64_t *>(ws + L.live_dst);
-    const uint64_t *live_src = reinterpret_cast<const uint64_t *>(ws + L.live_src);
+    const LiveView lv = live_view(ws, L);
+    const uint32_t *tile_base = reinterpret_cast<const uint32_t *>(ws + L.tile_base);
+    uint64_t *tile_start = reinterpret_cast<uint64_t *>(ws + L.tile_start);
     TileRec *tiles = reinterpret_cast<TileRec *>(ws + L.tiles);
     uint32_t *flags = reinterpret_cast<uint32_t *>(ws + L.flags);
     const uint64_t grid = (n_tiles + 255) / 256;
-    hipLaunchKernelGGL(k_tiles, dim3((uint32_t)grid), dim3(256), 0, s, live_dst, live_src, tiles,
-                       flags, n_tiles, tile_base, (uint64_t)tile_bytes, move_begin, live_bytes,
-                       first_moved, live_blocks);
+    hipLaunchKernelGGL(k_tile_starts, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_base,
+                       live_blocks, n_tiles, (uint64_t)tile_bytes, tile_start);
+    hipLaunchKernelGGL(k_tiles, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_start, live_blocks,
+                       n_tiles, (uint64_t)tile_bytes, tiles, flags);
     return hipGetLastError();
 }
 
 hipError_t launch_commit(const uint8_t *ws, const WsLayout &L, uint64_t live_blocks,
-                         uint64_t *off_out, uint64_t *size_out, uint8_t *live_out, hipStream_t s) {
+                         uint64_t *off_out, uint64_t *size_out, uint8_t *live_out,
+                         uint8_t *pinned_out, hipStream_t s) {
     if (live_blocks == 0) return hipSuccess;
-    const uint64_t *live_dst = reinterpret_cast<const uint64_t *>(ws + L.live_dst);
     uint64_t grid = (live_blocks + 255) / 256;
     if (grid > 4096) grid = 4096;
-    hipLaunchKernelGGL(k_commit, dim3((uint32_t)grid), dim3(256), 0, s, live_dst, live_blocks,
-                       off_out, size_out, live_out);
+    hipLaunchKernelGGL(k_commit, dim3((uint32_t)grid), dim3(256), 0, s, live_view(ws, L),
+                       live_blocks, off_out, size_out, live_out, pinned_out);
     return hipGetLastError();
 }
 

@@ -10,8 +10,8 @@
 //   anything else          ->  UINT64_MAX (counted)
 //
 // One lane per handle, grid-stride.  The search runs over the plan's packed
-// live-block arrays (old offsets ascending, and new offsets whose successive
-// differences are the block sizes), so free entries never cost a probe.  A
+// live-block arrays (old offsets ascending, new offsets, sizes), so free
+// entries never cost a probe; a pinned block maps to itself.  A
 // plain binary search is bound by L2 transactions (every probe of every lane
 // is its own cache line), so the top levels run in LDS over a sample of the
 // old offsets and only the last few probe global memory.  HBM traffic is
@@ -42,6 +42,7 @@ __device__ __forceinline__ uint64_t search_le(const T *a, uint64_t lo, uint64_t 
 // 64 lanes of a wave step together.
 __global__ __launch_bounds__(kRemapThreads) void k_remap(const uint64_t *__restrict__ live_dst,
                                                          const uint64_t *__restrict__ live_src,
+                                                         const uint64_t *__restrict__ live_size,
                                                          uint64_t m, const uint64_t *h_in,
                                                          uint64_t *h_out, uint64_t H,
                                                          unsigned long long *n_invalid) {
@@ -61,9 +62,7 @@ __global__ __launch_bounds__(kRemapThreads) void k_remap(const uint64_t *__restr
             const uint64_t hi = (lo + step < m) ? lo + step : m;
             const uint64_t j = search_le(live_src, lo, hi - lo, h);
             const uint64_t src = live_src[j];
-            const uint64_t d = live_dst[j];
-            const uint64_t size = live_dst[j + 1] - d;
-            if (h - src < size) out = d + (h - src);
+            if (h - src < live_size[j]) out = live_dst[j] + (h - src);
         }
         bad += (out == kNone) ? 1u : 0u;
         h_out[k] = out;
@@ -81,17 +80,17 @@ __global__ void k_zero_u64(uint64_t *p) {
 
 }  // namespace
 
-hipError_t launch_remap(const uint64_t *live_dst, const uint64_t *live_src, uint64_t live_blocks,
-                        const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
-                        uint64_t *n_invalid, int num_cus, hipStream_t s) {
+hipError_t launch_remap(const LiveView &lv, uint64_t live_blocks, const uint64_t *h_in,
+                        uint64_t *h_out, uint64_t n_handles, uint64_t *n_invalid, int num_cus,
+                        hipStream_t s) {
     if (n_invalid) hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, n_invalid);
     if (n_handles == 0) return hipGetLastError();
     // persistent grid: every workgroup pays for loading the LDS sample once
     uint64_t grid = (n_handles + kRemapThreads - 1) / kRemapThreads;
     const uint64_t cap = (uint64_t)num_cus * 4;  // measured best of 4, 5 and 8 per CU
     if (grid > cap) grid = cap;
-    hipLaunchKernelGGL(k_remap, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s, live_dst, live_src,
-                       live_blocks, h_in, h_out, n_handles,
+    hipLaunchKernelGGL(k_remap, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s, lv.dst, lv.src,
+                       lv.size, live_blocks, h_in, h_out, n_handles,
                        reinterpret_cast<unsigned long long *>(n_invalid));
     return hipGetLastError();
 }

@@ -24,8 +24,10 @@
  *             one hole (the CANN pool merges adjacent free blocks, 2.2).
  *   result  : live blocks keep their order and are packed from offset 0:
  *             new_offset[i] = sum of sizes of live entries before i, for every
- *             entry (a free entry gets the value of the next live one).  Bytes
- *             at or above the live total are never written.
+ *             entry (a free entry gets the value of the next live one).  With
+ *             pinned entries (see defrag_table) the same holds inside every
+ *             segment, from the segment's start, and a pinned entry keeps its
+ *             offset.  A byte no moved block lands on is never written.
  *   handles : byte addresses in the arena.  A handle inside live block i maps
  *             to new_offset[i] + (h - offset[i]); any other handle (in a hole,
  *             at or past the arena end) maps to UINT64_MAX and is counted.
@@ -70,7 +72,8 @@ extern "C" {
 #define DEFRAG_ETIMEOUT (-5)   /* mover watchdog expired (a wait never ended)  */
 
 /* Why a table was rejected: the first failing entry, and within it the first
- * failing check in this order. */
+ * failing check in the order zero size, misaligned, live flag, pinned flag,
+ * out of arena, overlap. */
 #define DEFRAG_REASON_NONE 0
 #define DEFRAG_REASON_ZERO_SIZE 1     /* size == 0                              */
 #define DEFRAG_REASON_MISALIGNED 2    /* offset or size not a multiple of 32    */
@@ -78,6 +81,7 @@ extern "C" {
 #define DEFRAG_REASON_OUT_OF_ARENA 4  /* offset + size > arena bytes            */
 #define DEFRAG_REASON_OVERLAP 5       /* starts before the previous entry ends  */
 #define DEFRAG_REASON_ARGUMENT 6      /* a pointer or size argument (host side) */
+#define DEFRAG_REASON_PINNED_FLAG 7   /* pinned not 0/1, or pinned but not live */
 
 /* Largest supported table: entry indices are 32-bit inside the kernels. */
 #define DEFRAG_MAX_ENTRIES 0xFFFFFFF0ull
@@ -87,6 +91,13 @@ typedef struct defrag_table {
     const uint64_t *size_dev;   /* n sizes in bytes                            */
     const uint8_t *live_dev;    /* n flags 0/1; NULL means every entry is live */
     uint64_t n;
+    /* n flags 0/1; NULL means nothing is pinned.  A pinned entry must be
+     * live; it never moves (910C page, "Cutting alloc and free at the
+     * source": the parameter region keeps fixed addresses).  Pinned entries
+     * split the arena into segments -- from one pinned block's end to the
+     * next one's start, or to an arena end -- and each segment packs its
+     * movable live blocks down to its own start. */
+    const uint8_t *pinned_dev;
 } defrag_table;
 
 typedef struct defrag_stats_t {
@@ -133,10 +144,12 @@ typedef struct defrag_plan_t {
     uint64_t n;
     uint64_t arena_bytes;
     uint64_t live_blocks;
-    uint64_t first_moved;  /* index among live blocks of the first one to move */
-    uint64_t move_begin;   /* lowest destination byte written by the move       */
+    uint64_t pinned_blocks;
+    uint64_t move_begin;   /* lowest destination byte written by the move
+                              (UINT64_MAX when nothing moves)                  */
     uint64_t live_bytes;
     uint64_t n_tiles;
+    uint64_t max_tiles;    /* tile capacity of the workspace                   */
     uint64_t max_blocks_per_tile;
     int32_t state;         /* 0 none/invalid, 1 planned, 2 moved               */
     int32_t device;
@@ -144,10 +157,14 @@ typedef struct defrag_plan_t {
     defrag_stats_t stats;    /* of the table as planned (before the move)        */
 } defrag_plan_t;
 
-/* Workspace bytes needed for a table of n entries over an arena of
- * arena_bytes with the given tile size (0 = default).  The workspace is
- * device memory, 256-byte aligned, owned by the caller; any content. */
-size_t defrag_workspace_bytes(uint64_t n, uint64_t arena_bytes, uint32_t tile_bytes);
+/* Workspace bytes for a table of n entries, at most max_pinned of them
+ * pinned, over an arena of arena_bytes, with the given tile size (0 =
+ * default).  Returns 0 for impossible arguments.  The workspace is device
+ * memory, 256-byte aligned, owned by the caller; any content.  defrag_plan
+ * uses whatever size it is given and returns DEFRAG_EWORKSPACE if the
+ * table needs more mover tiles than fit. */
+size_t defrag_workspace_bytes(uint64_t n, uint64_t max_pinned, uint64_t arena_bytes,
+                              uint32_t tile_bytes);
 
 /* Measure a table (910C monitoring: free total, largest contiguous free
  * block, both ratios; CANN 3.2).  Validates the table; on DEFRAG_EINVAL
@@ -189,12 +206,13 @@ int defrag_remap(const defrag_plan_t *plan_host, const void *ws_dev,
                  size_t ws_bytes, const uint64_t *h_in_dev, uint64_t *h_out_dev,
                  uint64_t n_handles, uint64_t *n_invalid_dev, hipStream_t stream);
 
-/* Write the packed table: the live_blocks entries (new offset, size, 1) in
- * order.  Any output pointer may be NULL.  Asynchronous. */
+/* Write the packed table: the live_blocks entries (new offset, size, live
+ * = 1, pinned flag) in order.  Any output pointer may be NULL.
+ * Asynchronous. */
 int defrag_commit(const defrag_plan_t *plan_host, const void *ws_dev,
                   size_t ws_bytes, uint64_t *offset_out_dev,
                   uint64_t *size_out_dev, uint8_t *live_out_dev,
-                  hipStream_t stream);
+                  uint8_t *pinned_out_dev, hipStream_t stream);
 
 /* Short text for a return code. */
 const char *defrag_strerror(int code);

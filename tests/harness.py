@@ -49,6 +49,10 @@ def device_table(heap: W.Heap, dev):
             torch.from_numpy(heap.live).to(dev))
 
 
+def device_pinned(heap: W.Heap, dev):
+    return None if heap.pinned is None else torch.from_numpy(heap.pinned).to(dev)
+
+
 def pristine_host(heap: W.Heap) -> torch.Tensor:
     t = torch.empty(heap.arena_bytes, dtype=torch.uint8)
     W.fill_payload(t, 0, heap.payload_mode, heap.payload_seed)
@@ -59,10 +63,13 @@ def run_gpu(heap: W.Heap, dev="cuda", tuning=None, arena: Optional[torch.Tensor]
             handles: Optional[np.ndarray] = None) -> GpuRun:
     import arena_compaction_amd as ac
     off, size, live = device_table(heap, dev)
+    pin = device_pinned(heap, dev)
     ws = ac.workspace(heap.n, heap.arena_bytes,
-                      tuning.tile_bytes if tuning is not None else 0, device=dev)
+                      tuning.tile_bytes if tuning is not None else 0, device=dev,
+                      max_pinned=heap.n_pinned)
     new_off = torch.full((heap.n,), -7, dtype=torch.int64, device=dev)
-    plan = ac.defrag_plan(off, size, live, heap.arena_bytes, ws, new_off, tuning=tuning)
+    plan = ac.defrag_plan(off, size, live, heap.arena_bytes, ws, new_off, tuning=tuning,
+                          pinned=pin)
     if arena is None:
         arena = torch.empty(heap.arena_bytes, dtype=torch.uint8, device=dev)
         W.fill_payload(arena, 0, heap.payload_mode, heap.payload_seed)
@@ -76,10 +83,14 @@ def run_gpu(heap: W.Heap, dev="cuda", tuning=None, arena: Optional[torch.Tensor]
     c_off = torch.empty(m, dtype=torch.int64, device=dev)
     c_size = torch.empty(m, dtype=torch.int64, device=dev)
     c_live = torch.zeros(m, dtype=torch.uint8, device=dev)
-    ac.defrag_commit(plan, ws, c_off, c_size, c_live)
-    post = ac.defrag_stats(c_off, c_size, c_live, heap.arena_bytes, ws)
+    c_pin = torch.full((m,), 9, dtype=torch.uint8, device=dev)
+    ac.defrag_commit(plan, ws, c_off, c_size, c_live, pinned_out=c_pin)
+    post = ac.defrag_stats(c_off, c_size, c_live, heap.arena_bytes, ws, pinned=c_pin)
     torch.cuda.synchronize()
     assert bool((c_live == 1).all()), "commit must mark every packed entry live"
+    want_pin = (np.zeros(m, np.uint8) if heap.pinned is None
+                else heap.pinned[np.flatnonzero(heap.live)])
+    assert np.array_equal(c_pin.cpu().numpy(), want_pin), "commit's pinned flags differ"
     return GpuRun(plan, t_to_u64(new_off), t_to_u64(h_out), int(n_bad.item()), post, status,
                   arena, ws)
 
@@ -92,24 +103,25 @@ def check_stats(got, want, what=""):
 
 def check_tables_and_handles(heap: W.Heap, r: GpuRun, handles: Optional[np.ndarray] = None):
     """new offsets, plan stats, remap, post-move stats: all bit-exact."""
-    want_new = oracle.new_offsets(heap.offset, heap.size, heap.live)
+    pin = heap.pinned
+    want_new = oracle.new_offsets(heap.offset, heap.size, heap.live, pin)
     assert np.array_equal(r.new_off, want_new), "new offsets differ"
-    check_stats(r.plan.stats, oracle.stats(heap.offset, heap.size, heap.live, heap.arena_bytes),
-                "plan")
+    check_stats(r.plan.stats, oracle.stats(heap.offset, heap.size, heap.live, heap.arena_bytes,
+                                           pinned=pin), "plan")
     hs = heap.handles if handles is None else handles
-    want_h, want_bad = oracle.remap(heap.offset, heap.size, heap.live, hs)
+    want_h, want_bad = oracle.remap(heap.offset, heap.size, heap.live, hs, pinned=pin)
     assert np.array_equal(r.remapped, want_h), "remapped handles differ"
     assert r.n_invalid == want_bad, (r.n_invalid, want_bad)
     li = np.flatnonzero(heap.live)
     post_want = oracle.stats(want_new[li], heap.size[li], np.ones(li.shape[0], np.uint8),
-                             heap.arena_bytes)
+                             heap.arena_bytes, pinned=None if pin is None else pin[li])
     check_stats(r.post_stats, post_want, "post")
 
 
 def check_arena_full(heap: W.Heap, r: GpuRun, pristine: torch.Tensor):
     """Whole arena against the oracle's ordered memmove of the same bytes."""
     ref = pristine.numpy().copy()
-    oracle.compact(ref, heap.offset, heap.size, heap.live)
+    oracle.compact(ref, heap.offset, heap.size, heap.live, heap.pinned)
     got = r.arena.cpu().numpy()
     if not np.array_equal(got, ref):
         bad = np.flatnonzero(got != ref)
@@ -121,7 +133,7 @@ def sample_windows(heap: W.Heap, rng: np.random.Generator, n_random: int = 2048,
     """Windows (start, length) of the compacted arena to check: the first and
     last bytes of (a sample of) every live block at its new place, random
     windows below and above the live total, and the window across it."""
-    new = oracle.new_offsets(heap.offset, heap.size, heap.live)
+    new = oracle.new_offsets(heap.offset, heap.size, heap.live, heap.pinned)
     li = np.flatnonzero(heap.live)
     if li.shape[0] > per_block_cap:
         li = np.sort(rng.choice(li, per_block_cap, replace=False))
@@ -148,7 +160,8 @@ def check_arena_sampled(heap: W.Heap, r: GpuRun, windows):
         if ln <= 0:
             continue
         got = r.arena[p0:p0 + ln].cpu().numpy()
-        d, s, l = oracle.source_map(heap.offset, heap.size, heap.live, heap.arena_bytes, p0, ln)
+        d, s, l = oracle.source_map(heap.offset, heap.size, heap.live, heap.arena_bytes, p0, ln,
+                                    pinned=heap.pinned)
         want = np.empty(ln, dtype=np.uint8)
         for dd, ss, ll in zip(d.tolist(), s.tolist(), l.tolist()):
             want[dd - p0:dd - p0 + ll] = W.payload_window(ss, ll, heap.payload_mode,

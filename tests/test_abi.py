@@ -50,9 +50,13 @@ def test_workspace_bytes():
     c = ac.defrag_workspace_bytes(8192, 64 << 20)
     d = ac.defrag_workspace_bytes(4096, 64 << 20, 256)
     assert a < b < c and b < d
-    # 80 GiB arena, 200k entries, default tiles: tens of MB, not GBs
+    # 80 GiB arena, 200k entries, default tiles: about 0.1% of the arena
     big = ac.defrag_workspace_bytes(200_247, 80 << 30)
-    assert big < 64 << 20
+    assert big < 128 << 20
+    # room for pinned entries grows it only by the tiles they may add
+    pinned = ac.defrag_workspace_bytes(200_247, 80 << 30, 0, 40)
+    assert big < pinned < big + 40 * 2 * 64
+    assert ac.defrag_workspace_bytes(10, 4096, 0, 11) == 0   # more pinned than entries
     for bad_tile in (100, 128, 3000, 262144):
         assert ac.defrag_workspace_bytes(16, 4096, bad_tile) == 0
 
@@ -64,7 +68,7 @@ def test_host_side_argument_errors_need_no_gpu():
     # a zeroed plan is refused before any HIP call
     assert L.defrag_move(None, 0, ctypes.byref(plan), None, 0, None) == ac.DEFRAG_ENOPLAN
     assert L.defrag_remap(ctypes.byref(plan), None, 0, None, None, 0, None, None) == ac.DEFRAG_ENOPLAN
-    assert L.defrag_commit(ctypes.byref(plan), None, 0, None, None, None, None) == ac.DEFRAG_ENOPLAN
+    assert L.defrag_commit(ctypes.byref(plan), None, 0, None, None, None, None, None) == ac.DEFRAG_ENOPLAN
     assert L.defrag_move_status(ctypes.byref(plan), None, None) == ac.DEFRAG_ENOPLAN
     # missing table / output pointers
     st = ac.defrag_stats_t()

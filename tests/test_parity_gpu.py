@@ -61,7 +61,8 @@ def test_golden_cases_gpu(ac):
     for case in cases:
         t = np.array(case["table"], dtype=np.uint64).reshape(-1, 3)
         heap = W.table_from_lists(case["arena_bytes"], [tuple(x) for x in t[:, :2].tolist()],
-                                  t[:, 2].tolist(), case["handles"], name=case["name"])
+                                  t[:, 2].tolist(), case["handles"], name=case["name"],
+                                  pinned=case.get("pinned"))
         for tile in (256, 65536):
             r = _full_check(heap, _tuning(ac, tile))
             assert r.new_off.tolist() == case["new_offset"]
@@ -76,17 +77,18 @@ def test_random_tiny_heaps_gpu(ac, tile):
         n = int(rng.integers(0, 60))
         heap = W.tiny_heap(rng, n, sizes=(32, 64, 96, 160, 4096, 8192),
                            gap_p=float(rng.choice([0.0, 0.3, 0.8])),
-                           live_p=float(rng.choice([0.2, 0.5, 0.9, 1.0])))
+                           live_p=float(rng.choice([0.2, 0.5, 0.9, 1.0])),
+                           pinned_p=float(rng.choice([0.0, 0.0, 0.15, 0.4])))
         _full_check(heap, _tuning(ac, tile))
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("k", [1, 2, 3, "3p", 4, 5])
 @pytest.mark.parametrize("tile,nt", [(256, 0), (4096, 1), (65536, 0), (65536, 1), (131072, 0)])
 def test_small_configs_gpu(ac, k, tile, nt):
     _full_check(W.config(k, small=True), _tuning(ac, tile, 0, nt))
 
 
-@pytest.mark.parametrize("k", [1, 4, 5])
+@pytest.mark.parametrize("k", [1, "3p", 4, 5])
 def test_one_workgroup_per_cu_and_tiny_tiles(ac, k):
     """Fewer resident workgroups and many more tiles per workgroup: the
     ticket order alone must keep the schedule correct."""
@@ -177,7 +179,8 @@ def test_invalid_tables_gpu(ac):
             ac.defrag_stats(dev_o, dev_s, dev_l, S, ws)
         assert ei.value.code == ac.DEFRAG_EINVAL
         assert (ei.value.invalid_index, ei.value.invalid_reason) == (bad, reason)
-        if ac.defrag_workspace_bytes(len(table), S) > (256 << 20):
+        need = ac.defrag_workspace_bytes(len(table), S)
+        if need == 0 or need > (256 << 20):
             continue   # planning an arena this size needs a tile table this large
         ws = ac.workspace(len(table), S)
         new = torch.full((len(table),), -7, dtype=torch.int64, device="cuda")
@@ -239,18 +242,77 @@ def test_full_size_configs_every_byte(ac, k):
     _full_check(heap)
 
 
-@pytest.mark.parametrize("k", [3, 5])
+@pytest.mark.parametrize("k", [3, "3p", 5])
 def test_full_size_configs_sampled(ac, k):
     heap = W.config(k)
     log(f"case {heap.describe()} (sampled bytes)")
     r = run_gpu(heap)
     assert r.status == ac.DEFRAG_OK
     check_tables_and_handles(heap, r)
-    wins = sample_windows(heap, np.random.default_rng(k), n_random=1024)
+    wins = sample_windows(heap, np.random.default_rng(5 if k == "3p" else k), n_random=1024)
     check_arena_sampled(heap, r, wins)
-    if k == 3:
+    if k in (3, "3p"):
         s = r.plan.stats
         assert abs(s.frag_free_over_largest_minus_1 - 4.7) < 1e-3
-        assert r.post_stats.frag_free_over_largest_minus_1 == 0.0
+        if k == 3:   # one top hole afterwards
+            assert r.post_stats.frag_free_over_largest_minus_1 == 0.0
+        else:        # the pinned blocks keep free space in separate holes
+            assert r.post_stats.hole_count > 1
+            assert 0.0 < r.post_stats.frag_free_over_largest_minus_1 < 4.7
     del r
     torch.cuda.empty_cache()
+
+
+def test_pinned_edge_cases_gpu(ac):
+    """Pinned blocks at the arena ends, adjacent pinned blocks, everything
+    pinned, and runs on both sides of a pinned block inside one tile window
+    (so one window holds the end of one run and the start of the next)."""
+    cases = [
+        W.table_from_lists(4096, [(0, 1024), (1024, 512), (2048, 1024)], [1, 0, 1], [0, 2048, 3071],
+                           pinned=[1, 0, 0]),
+        W.table_from_lists(4096, [(0, 512), (1024, 512), (3072, 1024)], [1, 1, 1], [600, 1030, 4095],
+                           pinned=[0, 0, 1]),
+        W.table_from_lists(4096, [(64, 64), (128, 64), (512, 64), (576, 64)], [1, 1, 1, 1],
+                           [64, 200, 512, 639], pinned=[1, 1, 1, 1]),
+        W.table_from_lists(8192, [(128, 96), (320, 64), (384, 32), (512, 160), (800, 96), (1024, 64)],
+                           [1, 1, 1, 1, 1, 1], [130, 330, 390, 600, 801, 1030],
+                           pinned=[0, 0, 1, 0, 0, 0]),
+        W.table_from_lists(1 << 20, [(4096, 65536), (69632 + 32, 32), (69632 + 4096, 65536),
+                                     (200000 // 32 * 32, 64), (262144, 131072)],
+                           [1, 1, 1, 1, 1], [5000, 69664, 80000, 262144 + 77],
+                           pinned=[0, 1, 0, 1, 0]),
+    ]
+    for heap in cases:
+        for tile in (256, 512, 4096, 65536):
+            _full_check(heap, _tuning(ac, tile),
+                        handles=np.concatenate([heap.handles,
+                                                W.edge_handles(heap, np.random.default_rng(1), 8)]))
+
+
+def test_pinned_invalid_and_workspace(ac):
+    heap = W.table_from_lists(4096, [(0, 1024), (1024, 512)], [0, 1], pinned=[1, 0])
+    off, size, live = device_table(heap, "cuda")
+    pin = torch.from_numpy(heap.pinned).cuda()
+    ws = ac.workspace(2, 4096, max_pinned=2)
+    with pytest.raises(ac.DefragError) as ei:
+        ac.defrag_plan(off, size, live, 4096, ws, pinned=pin)
+    assert (ei.value.code, ei.value.invalid_index, ei.value.invalid_reason) == (ac.DEFRAG_EINVAL, 0, 7)
+    # a workspace sized for no pinned entries is too small for many small segments
+    rng = np.random.default_rng(3)
+    n = 4000
+    size_np = np.full(n, 64, np.uint64)
+    off_np = np.arange(n, dtype=np.uint64) * np.uint64(128)
+    live_np = np.ones(n, np.uint8)
+    pin_np = (np.arange(n) % 2 == 0).astype(np.uint8)
+    big = W.Heap("many_segments", n * 128, off_np, size_np, live_np,
+                 np.array([130, 64 * 128 + 70], np.uint64), "hash", 11, 0)
+    big.pinned = pin_np
+    o, s_, l = device_table(big, "cuda")
+    p_ = torch.from_numpy(pin_np).cuda()
+    # 64 KiB tiles: room for 11 tiles when nothing is pinned, but 2,000 runs
+    small = ac.workspace(n, big.arena_bytes, 65536, max_pinned=0)
+    with pytest.raises(ac.DefragError) as ei:
+        ac.defrag_plan(o, s_, l, big.arena_bytes, small, tuning=_tuning(ac, 65536), pinned=p_)
+    assert ei.value.code == ac.DEFRAG_EWORKSPACE
+    for tile in (256, 65536):
+        _full_check(big, _tuning(ac, tile))
