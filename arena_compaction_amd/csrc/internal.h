@@ -12,7 +12,7 @@ namespace ac {
 constexpr uint32_t kScanThreads = 256;          // threads per scan workgroup
 constexpr uint32_t kScanItems = 8;              // table entries per thread
 constexpr uint32_t kScanTile = kScanThreads * kScanItems;  // entries per workgroup
-constexpr uint32_t kSpineThreads = 1024;        // single-workgroup passes
+constexpr uint32_t kSpineThreads = 256;         // single-workgroup passes (no spills)
 constexpr uint32_t kMoveThreads = 256;          // mover workgroup
 constexpr uint32_t kMoveRowBytes = kMoveThreads * 16;  // one 16-B vector per lane
 constexpr uint32_t kDefaultTile = 65536;
@@ -92,14 +92,15 @@ struct alignas(16) TileRec {
 };
 static_assert(sizeof(TileRec) == 48, "tile record size");
 
-constexpr size_t kPerTileBytes = sizeof(uint64_t) + sizeof(TileRec) + sizeof(uint32_t);
+constexpr size_t kPerTileBytes =
+    sizeof(uint64_t) + sizeof(uint32_t) + sizeof(TileRec) + sizeof(uint32_t);
 
 struct WsLayout {
     // fixed part (depends on n only)
     size_t header, part, prefix, spart, tpart, tprefix, live_dst, live_src, live_size,
         live_pin, tile_base, fixed;
     // tile part (depends on the tile capacity)
-    size_t tile_start, tiles, flags, total;
+    size_t tile_start, tile_first, tiles, flags, total;
     uint64_t n_scan_blocks, max_tiles;
 };
 
@@ -130,6 +131,7 @@ inline WsLayout ws_with_tiles(uint64_t n, uint64_t max_tiles) {
     L.max_tiles = max_tiles;
     size_t at = L.fixed;
     L.tile_start = at; at += align256(max_tiles * sizeof(uint64_t));
+    L.tile_first = at; at += align256(max_tiles * sizeof(uint32_t));
     L.tiles = at;      at += align256(max_tiles * sizeof(TileRec));
     L.flags = at;      at += align256(max_tiles * sizeof(uint32_t));
     L.total = at;
@@ -147,7 +149,7 @@ inline uint64_t tiles_bound(uint64_t arena_bytes, uint64_t max_pinned, uint32_t 
 inline uint64_t tiles_fitting(uint64_t n, size_t ws_bytes) {
     const WsLayout F = ws_fixed(n);
     if (ws_bytes <= F.fixed) return 0;
-    // upper estimate, then step down past the (at most 3 x 255 bytes of)
+    // upper estimate, then step down past the (at most 4 x 255 bytes of)
     // alignment padding
     uint64_t t = (ws_bytes - F.fixed) / kPerTileBytes;
     while (t > 0 && ws_with_tiles(n, t).total > ws_bytes) --t;

@@ -429,10 +429,10 @@ __device__ inline int64_t last_le(const T *a, int64_t lo, int64_t hi, uint64_t x
     return l - 1;
 }
 
-// Pass 8: one lane per tile writes its start.
+// Pass 8: one lane per tile writes its start and its first block.
 __global__ __launch_bounds__(256) void k_tile_starts(LiveView lv, const uint32_t *tile_base,
                                                      uint64_t m, uint64_t n_tiles, uint64_t T,
-                                                     uint64_t *tile_start) {
+                                                     uint64_t *tile_start, uint32_t *tile_first) {
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= n_tiles) return;
     const int64_t k = last_le(tile_base, 0, (int64_t)m, t);
@@ -442,6 +442,21 @@ __global__ __launch_bounds__(256) void k_tile_starts(LiveView lv, const uint32_t
     const uint64_t lead = (start && (a & (T - 1))) ? 1 : 0;
     const uint64_t first_mult = (a + T - 1) & ~(T - 1);
     tile_start[t] = (j < lead) ? a : first_mult + (j - lead) * T;
+    tile_first[t] = (uint32_t)k;
+}
+
+// The tile holding destination byte q of moved block b (tiles cut each run
+// at its start and at every multiple of T).
+__device__ inline uint64_t tile_of(const LiveView &lv, const uint32_t *tile_base, uint64_t b,
+                                   uint64_t q, uint64_t T) {
+    const uint64_t a = lv.dst[b];
+    const uint64_t A = (a + T - 1) & ~(T - 1);
+    const bool start = (b == 0) || !moved_at(lv, b - 1);
+    const uint64_t lead = (start && (a & (T - 1))) ? 1 : 0;
+    if (q >= A) return tile_base[b] + lead + (q - A) / T;
+    // q lies in the window block b starts in: block b's own first tile if it
+    // starts a run there, else the tile that began earlier in the run
+    return lead ? tile_base[b] : tile_base[b] - 1;
 }
 
 // Pass 9: one lane per tile.  [t0, t1) = the run's bytes from the tile start
@@ -451,7 +466,9 @@ __global__ __launch_bounds__(256) void k_tile_starts(LiveView lv, const uint32_t
 // order kept), so the destinations whose sources lie in [t0, t1) are at most
 // t1 - t0 consecutive live bytes, all at or below [t0, t1): their tiles are a
 // short range ending at or before this one.
-__global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile_start, uint64_t m,
+__global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile_start,
+                                               const uint32_t *tile_first,
+                                               const uint32_t *tile_base, uint64_t m,
                                                uint64_t n_tiles, uint64_t T, TileRec *tiles,
                                                uint32_t *flags) {
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -459,16 +476,17 @@ __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile
     const uint64_t t0 = tile_start[t];
     uint64_t bound = (t0 & ~(T - 1)) + T;
     if (t + 1 < n_tiles) bound = umin64(bound, tile_start[t + 1]);
-    const int64_t first = last_le(lv.dst, 0, (int64_t)m, t0);
-    const int64_t last_any = last_le(lv.dst, first, (int64_t)m, bound - 1);
-    // blocks first..last_any: the run's moved blocks, then only unmoved ones
-    int64_t l = first + 1, h = last_any + 1;  // first unmoved block in (first, last_any]
-    while (l < h) {
-        const int64_t mid = l + ((h - l) >> 1);
-        if (moved_at(lv, (uint64_t)mid)) l = mid + 1;
-        else h = mid;
+    const uint64_t first = tile_first[t];
+    // last block of the run inside [t0, bound): blocks after first that start
+    // below bound and moved form a prefix -- gallop, then bisect
+    uint64_t last = first, stride = 1;
+    while (last + stride < m && lv.dst[last + stride] < bound && moved_at(lv, last + stride)) {
+        last += stride;
+        stride <<= 1;
     }
-    const int64_t last = l - 1;
+    for (; stride > 0; stride >>= 1)
+        if (last + stride < m && lv.dst[last + stride] < bound && moved_at(lv, last + stride))
+            last += stride;
     const uint64_t t1 = umin64(bound, lv.dst[last] + lv.size[last]);
     // sources overlapping [t0, t1): first block whose source ends above t0 ...
     int64_t lo = 0, hi = (int64_t)m;
@@ -481,15 +499,21 @@ __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile
     if (lo < (int64_t)m && lv.src[lo] < t1 && t > 0) {
         const uint64_t j = (uint64_t)lo;
         const uint64_t q_lo = lv.dst[j] + (t0 > lv.src[j] ? t0 - lv.src[j] : 0);
-        // ... and the last block whose source starts below t1
-        const int64_t c = last_le(lv.src, (int64_t)j, (int64_t)m, t1 - 1);
+        // ... and the last block whose source starts below t1 (gallop from j)
+        uint64_t c = j;
+        stride = 1;
+        while (c + stride < m && lv.src[c + stride] < t1) {
+            c += stride;
+            stride <<= 1;
+        }
+        for (; stride > 0; stride >>= 1)
+            if (c + stride < m && lv.src[c + stride] < t1) c += stride;
         const uint64_t q_hi = lv.dst[c] + umin64(lv.size[c], t1 - lv.src[c]) - 1;
-        const int64_t u_lo = last_le(tile_start, 0, (int64_t)n_tiles, q_lo);
-        int64_t u_hi = last_le(tile_start, 0, (int64_t)n_tiles, q_hi);
-        if (u_hi > (int64_t)t - 1) u_hi = (int64_t)t - 1;
-        const int64_t d_lo = u_lo < 0 ? 0 : u_lo;
-        if (u_hi >= d_lo) {
-            dep_lo = (uint32_t)d_lo;
+        const uint64_t u_lo = tile_of(lv, tile_base, j, q_lo, T);
+        uint64_t u_hi = tile_of(lv, tile_base, c, q_hi, T);
+        if (u_hi > t - 1) u_hi = t - 1;
+        if (u_lo <= u_hi) {
+            dep_lo = (uint32_t)u_lo;
             dep_hi = (uint32_t)u_hi;
         }
     }
@@ -556,13 +580,14 @@ hipError_t launch_tiles(uint8_t *ws, const WsLayout &L, uint64_t n_tiles, uint64
     const LiveView lv = live_view(ws, L);
     const uint32_t *tile_base = reinterpret_cast<const uint32_t *>(ws + L.tile_base);
     uint64_t *tile_start = reinterpret_cast<uint64_t *>(ws + L.tile_start);
+    uint32_t *tile_first = reinterpret_cast<uint32_t *>(ws + L.tile_first);
     TileRec *tiles = reinterpret_cast<TileRec *>(ws + L.tiles);
     uint32_t *flags = reinterpret_cast<uint32_t *>(ws + L.flags);
     const uint64_t grid = (n_tiles + 255) / 256;
     hipLaunchKernelGGL(k_tile_starts, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_base,
-                       live_blocks, n_tiles, (uint64_t)tile_bytes, tile_start);
-    hipLaunchKernelGGL(k_tiles, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_start, live_blocks,
-                       n_tiles, (uint64_t)tile_bytes, tiles, flags);
+                       live_blocks, n_tiles, (uint64_t)tile_bytes, tile_start, tile_first);
+    hipLaunchKernelGGL(k_tiles, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_start, tile_first,
+                       tile_base, live_blocks, n_tiles, (uint64_t)tile_bytes, tiles, flags);
     return hipGetLastError();
 }
 
