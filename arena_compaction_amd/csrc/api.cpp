@@ -185,7 +185,7 @@ int defrag_plan(const defrag_table *table, uint64_t arena_bytes, const defrag_tu
     if (rc) return rc;
     fill_stats(&plan->stats, h, arena_bytes);
     if (h.bad_key != kNone) return DEFRAG_EINVAL;
-    if (h.n_tiles > L.max_tiles) return DEFRAG_EWORKSPACE;  // new offsets are written
+    if (h.n_tiles > L.max_tiles) return DEFRAG_EWORKSPACE;  // new offsets were written
 
     const uint64_t T = tu.tile_bytes;
     plan->epoch = epoch;
@@ -206,8 +206,6 @@ int defrag_plan(const defrag_table *table, uint64_t arena_bytes, const defrag_tu
     if (h.min_live_size != kNone && h.min_live_size) mb = T / h.min_live_size + 2;
     if (mb > T / 32 + 2) mb = T / 32 + 2;
     plan->max_blocks_per_tile = mb;
-    if (launch_tiles(ws, L, h.n_tiles, h.live_blocks, tu.tile_bytes, stream) != hipSuccess)
-        return DEFRAG_EHIP;
     plan->magic = kPlanMagic;
     plan->state = 1;
     return DEFRAG_OK;

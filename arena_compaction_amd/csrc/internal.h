@@ -181,14 +181,12 @@ inline LiveView live_view(const uint8_t *ws, const WsLayout &L) {
 }
 
 // ---- plan.hip ----
-// Scan passes (and, when write_outputs, the tile-count passes).  All
-// asynchronous; the header then holds totals, statistics and n_tiles.
+// Scan passes and, when write_outputs, the mover's tiles (for at most
+// L.max_tiles tiles).  All asynchronous; the header then holds totals,
+// statistics and n_tiles (tiles are built only if n_tiles <= L.max_tiles).
 hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws,
                        const WsLayout &L, uint64_t *new_offset, bool write_outputs,
                        uint32_t tile_bytes, uint64_t epoch, hipStream_t s);
-// Tile starts and records for n_tiles tiles (n_tiles <= L.max_tiles).
-hipError_t launch_tiles(uint8_t *ws, const WsLayout &L, uint64_t n_tiles, uint64_t live_blocks,
-                        uint32_t tile_bytes, hipStream_t s);
 hipError_t launch_commit(const uint8_t *ws, const WsLayout &L, uint64_t live_blocks,
                          uint64_t *off_out, uint64_t *size_out, uint8_t *live_out,
                          uint8_t *pinned_out, hipStream_t s);

@@ -29,7 +29,9 @@
 // moved block counts the tiles that start inside it (a run of moved blocks
 // starts one, and so does every tile-size boundary inside a run); a scan of
 // those counts gives each block its first tile, and one lane per tile writes
-// the tile's start, its range, its blocks and its dependencies.
+// the tile's start, its range, its blocks and its dependencies.  The whole
+// sequence is queued at once; the host reads the header back only at the
+// end.
 #include "internal.h"
 
 namespace ac {
@@ -431,9 +433,12 @@ __device__ inline int64_t last_le(const T *a, int64_t lo, int64_t hi, uint64_t x
 
 // Pass 8: one lane per tile writes its start and its first block.
 __global__ __launch_bounds__(256) void k_tile_starts(LiveView lv, const uint32_t *tile_base,
-                                                     uint64_t m, uint64_t n_tiles, uint64_t T,
-                                                     uint64_t *tile_start, uint32_t *tile_first) {
+                                                     const WsHeader *hdr, uint64_t max_tiles,
+                                                     uint64_t T, uint64_t *tile_start,
+                                                     uint32_t *tile_first) {
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (hdr->bad_key != kNone || hdr->n_tiles > max_tiles) return;  // plan fails
+    const uint64_t n_tiles = hdr->n_tiles, m = hdr->live_blocks;
     if (t >= n_tiles) return;
     const int64_t k = last_le(tile_base, 0, (int64_t)m, t);
     const uint64_t j = t - tile_base[k];
@@ -468,10 +473,12 @@ __device__ inline uint64_t tile_of(const LiveView &lv, const uint32_t *tile_base
 // short range ending at or before this one.
 __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile_start,
                                                const uint32_t *tile_first,
-                                               const uint32_t *tile_base, uint64_t m,
-                                               uint64_t n_tiles, uint64_t T, TileRec *tiles,
+                                               const uint32_t *tile_base, const WsHeader *hdr,
+                                               uint64_t max_tiles, uint64_t T, TileRec *tiles,
                                                uint32_t *flags) {
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (hdr->bad_key != kNone || hdr->n_tiles > max_tiles) return;  // plan fails
+    const uint64_t n_tiles = hdr->n_tiles, m = hdr->live_blocks;
     if (t >= n_tiles) return;
     const uint64_t t0 = tile_start[t];
     uint64_t bound = (t0 & ~(T - 1)) + T;
@@ -570,24 +577,21 @@ hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, co
                            hdr);
         hipLaunchKernelGGL(k_tcount_down, dim3((uint32_t)gnb), dim3(kScanThreads), 0, s, lv, hdr,
                            (uint64_t)tile_bytes, tprefix, tile_base);
+        // tile starts and records: a grid for the whole capacity, each lane
+        // checks the device-side tile count (no host round trip)
+        uint64_t *tile_start = reinterpret_cast<uint64_t *>(ws + L.tile_start);
+        uint32_t *tile_first = reinterpret_cast<uint32_t *>(ws + L.tile_first);
+        TileRec *tiles = reinterpret_cast<TileRec *>(ws + L.tiles);
+        uint32_t *flags = reinterpret_cast<uint32_t *>(ws + L.flags);
+        const uint64_t grid = (L.max_tiles + 255) / 256;
+        if (grid) {
+            hipLaunchKernelGGL(k_tile_starts, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_base,
+                               hdr, L.max_tiles, (uint64_t)tile_bytes, tile_start, tile_first);
+            hipLaunchKernelGGL(k_tiles, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_start,
+                               tile_first, tile_base, hdr, L.max_tiles, (uint64_t)tile_bytes, tiles,
+                               flags);
+        }
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_tiles(uint8_t *ws, const WsLayout &L, uint64_t n_tiles, uint64_t live_blocks,
-                        uint32_t tile_bytes, hipStream_t s) {
-    if (n_tiles == 0) return hipSuccess;
-    const LiveView lv = live_view(ws, L);
-    const uint32_t *tile_base = reinterpret_cast<const uint32_t *>(ws + L.tile_base);
-    uint64_t *tile_start = reinterpret_cast<uint64_t *>(ws + L.tile_start);
-    uint32_t *tile_first = reinterpret_cast<uint32_t *>(ws + L.tile_first);
-    TileRec *tiles = reinterpret_cast<TileRec *>(ws + L.tiles);
-    uint32_t *flags = reinterpret_cast<uint32_t *>(ws + L.flags);
-    const uint64_t grid = (n_tiles + 255) / 256;
-    hipLaunchKernelGGL(k_tile_starts, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_base,
-                       live_blocks, n_tiles, (uint64_t)tile_bytes, tile_start, tile_first);
-    hipLaunchKernelGGL(k_tiles, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_start, tile_first,
-                       tile_base, live_blocks, n_tiles, (uint64_t)tile_bytes, tiles, flags);
     return hipGetLastError();
 }
 

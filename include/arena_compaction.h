@@ -177,8 +177,8 @@ int defrag_stats(const defrag_table *table, uint64_t arena_bytes, void *ws_dev,
 /* Plan a compaction (910C: scan holes low to high, give every live block its
  * downward shift).  Validates, writes new_offset_dev[n] (may be NULL), fills
  * *plan_host (including the stats of the table), and builds the mover's tile
- * table in the workspace.  Synchronises once on a small header; the tile
- * table build is left queued on the stream.  tuning may be NULL. */
+ * table in the workspace.  Queues every pass, then synchronises once to
+ * read a 256-byte header back.  tuning may be NULL. */
 int defrag_plan(const defrag_table *table, uint64_t arena_bytes,
                 const defrag_tuning *tuning, void *ws_dev, size_t ws_bytes,
                 hipStream_t stream, uint64_t *new_offset_dev,
