@@ -6,6 +6,7 @@ code with the HIP library.
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import dataclasses
 import os
@@ -72,6 +73,8 @@ def _bind(path: str):
     L.oracle_remap.argtypes = [P, P, P, P, U, P, P, U, P]
     L.oracle_source_map.argtypes = [P, P, P, P, U, U, U, U, P, P, P, U]
     L.oracle_source_map.restype = ctypes.c_int64
+    L.oracle_target_window.argtypes = [P, P, P, P, U, U, U, P]
+    L.oracle_target_window.restype = ctypes.c_int
     return L
 
 
@@ -169,3 +172,34 @@ def source_map(off, size, live, arena_bytes, p0, length, cap=1 << 16, pinned=Non
     if k < 0:
         raise ValueError("source map needs more pieces than cap")
     return d[:k].copy(), s[:k].copy(), l[:k].copy()
+
+
+class _Window(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_uint64) for k in ("found", "begin", "end", "hole", "moved_bytes")]
+
+
+Window = collections.namedtuple("Window", [f[0] for f in _Window._fields_])
+
+
+def target_window(off, size, live, arena_bytes, request, pinned=None) -> Window:
+    """The window targeted compaction packs (oracle.h); raises ValueError for
+    request == 0."""
+    off, size, live, pinned = _table(off, size, live, pinned)
+    w = _Window()
+    rc = lib().oracle_target_window(_p(off), _p(size), _p(live), _p(pinned), off.shape[0],
+                                    arena_bytes, request, ctypes.byref(w))
+    if rc != 0:
+        raise ValueError("request must be at least one byte")
+    return Window(*[getattr(w, f[0]) for f in _Window._fields_])
+
+
+def window_pins(off, live, pinned, window: Window) -> np.ndarray:
+    """Targeted compaction is segmented compaction in which every live block
+    outside the window is held in place: the pinned flags that say so."""
+    off = np.asarray(off, dtype=np.uint64)
+    live = np.asarray(live, dtype=np.uint8)
+    outside = (off < np.uint64(window.begin)) | (off >= np.uint64(window.end))
+    fixed = (live == 1) & outside
+    if pinned is not None:
+        fixed |= np.asarray(pinned, dtype=np.uint8) == 1
+    return fixed.astype(np.uint8)

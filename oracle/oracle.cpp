@@ -214,4 +214,66 @@ int64_t oracle_source_map(const uint64_t *offset, const uint64_t *size,
     return (int64_t)count;
 }
 
+// [910C] "Periodic compaction with Ascend C": compaction pauses every tensor
+// it touches, so it is a stop-loss step, and the failure it answers is one
+// request (the 4.2 GB communication buffer) larger than any free block.
+// Holes are listed low to high; between two neighbouring holes lie some live
+// bytes, and possibly a pinned block, which no window may contain.  A sweep
+// over the last hole of the window keeps, for each, the shortest window
+// ending there that still frees `request` bytes (its first hole only moves
+// up as the last one does), and the cheapest of those wins.
+int oracle_target_window(const uint64_t *offset, const uint64_t *size,
+                         const uint8_t *live, const uint8_t *pinned, uint64_t n,
+                         uint64_t arena_bytes, uint64_t request, oracle_window *out) {
+    std::memset(out, 0, sizeof(*out));
+    if (request == 0) return ORACLE_EINVAL;
+    struct Hole {
+        uint64_t start, len;
+        uint64_t live_after;  // live bytes between this hole and the next
+        bool pinned_after;    // a pinned block lies between them
+    };
+    std::vector<Hole> holes;
+    uint64_t cursor = 0;
+    for (uint64_t i = 0; i < n; ++i) {
+        if (!live[i]) continue;
+        if (offset[i] > cursor) holes.push_back(Hole{cursor, offset[i] - cursor, 0, false});
+        if (!holes.empty()) {
+            holes.back().live_after += size[i];
+            if (is_pinned(pinned, i)) holes.back().pinned_after = true;
+        }
+        cursor = offset[i] + size[i];
+    }
+    if (arena_bytes > cursor) holes.push_back(Hole{cursor, arena_bytes - cursor, 0, false});
+
+    uint64_t first = 0, free_sum = 0, live_sum = 0;
+    for (uint64_t last = 0; last < holes.size(); ++last) {
+        if (last > 0) {
+            if (holes[last - 1].pinned_after) {  // start again past the barrier
+                first = last;
+                free_sum = 0;
+                live_sum = 0;
+            } else {
+                live_sum += holes[last - 1].live_after;
+            }
+        }
+        free_sum += holes[last].len;
+        while (first < last && free_sum - holes[first].len >= request) {
+            free_sum -= holes[first].len;
+            live_sum -= holes[first].live_after;
+            ++first;
+        }
+        if (free_sum < request) continue;
+        const uint64_t begin = holes[first].start;
+        if (!out->found || live_sum < out->moved_bytes ||
+            (live_sum == out->moved_bytes && begin < out->begin)) {
+            out->found = 1;
+            out->begin = begin;
+            out->end = holes[last].start + holes[last].len;
+            out->hole = free_sum;
+            out->moved_bytes = live_sum;
+        }
+    }
+    return ORACLE_OK;
+}
+
 }  // extern "C"

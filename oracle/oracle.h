@@ -112,6 +112,29 @@ int64_t oracle_source_map(const uint64_t *offset, const uint64_t *size,
                           uint64_t *seg_dst, uint64_t *seg_src, uint64_t *seg_len,
                           uint64_t cap);
 
+/* Targeted compaction ([910C] periodic compaction is a costly global pause,
+ * kept for stopping the damage; the failure it answers is one request -- the
+ * 4.2 GB communication buffer -- that no contiguous free block can hold).
+ * A window is a run of consecutive holes together with the live blocks
+ * between them, none of them pinned.  Packing the window's blocks down to
+ * the window's start (the other blocks stay) merges its holes into one at
+ * the window's top.  The chosen window is the one whose merged hole holds at
+ * least `request` bytes with the fewest live bytes inside (the bytes that
+ * move); among those, the one starting lowest. */
+typedef struct oracle_window {
+    uint64_t found;        /* 0: no window can hold the request              */
+    uint64_t begin;        /* window = [begin, end): from its first hole's   */
+    uint64_t end;          /*   start to its last hole's end                 */
+    uint64_t hole;         /* free bytes inside = the merged hole's size     */
+    uint64_t moved_bytes;  /* live bytes inside                              */
+} oracle_window;
+
+/* Returns ORACLE_EINVAL for request == 0, else ORACLE_OK.  The table must
+ * be valid (oracle_validate). */
+int oracle_target_window(const uint64_t *offset, const uint64_t *size,
+                         const uint8_t *live, const uint8_t *pinned, uint64_t n,
+                         uint64_t arena_bytes, uint64_t request, oracle_window *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -125,3 +125,35 @@ def remap(arena_bytes, off, size, live, handles, pinned=None):
             out.append(U64_MAX)
     out = np.array(out, dtype=np.uint64)
     return out, int(np.count_nonzero(out == np.uint64(U64_MAX)))
+
+
+def target_window(arena_bytes, off, size, live, request, pinned=None):
+    """Targeted compaction by simulation.  Every window from the start of one
+    hole to the end of the same or a later hole, holding no pinned byte, is
+    tried on the byte map: its live bytes are packed to its start, the bytes
+    whose address changed are counted, and the free run ending at the
+    window's end is measured.  Among windows whose run holds `request` bytes,
+    the fewest moved bytes wins, then the lowest start.
+    Returns (found, begin, end, hole, moved)."""
+    B = live_bitmap(arena_bytes, off, size, live)
+    _, P, _ = _maps(arena_bytes, off, size, live, pinned)
+    hs = holes(B)
+    best = None
+    for i in range(len(hs)):
+        for j in range(i, len(hs)):
+            a, b = hs[i][0], hs[j][0] + hs[j][1]
+            if P[a:b].any():
+                continue
+            inside = B[a:b]
+            k = int(inside.sum())
+            packed = np.zeros(b - a, dtype=bool)
+            packed[:k] = True
+            last_live = int(np.flatnonzero(packed)[-1]) if k else -1
+            run = (b - a) - (last_live + 1)
+            if run < request:
+                continue
+            moved = int(np.count_nonzero(np.flatnonzero(inside) != np.arange(k)))
+            key = (moved, a)
+            if best is None or key < best[0]:
+                best = (key, (1, a, b, run, moved))
+    return best[1] if best else (0, 0, 0, 0, 0)

@@ -13,6 +13,7 @@ import pytest
 import oracle
 import workloads as W
 import test_oracle as T
+import test_oracle_targeted as TT
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.cpp")
 
@@ -29,7 +30,10 @@ MUTANTS = [
      "out->frag_one_minus_largest_over_free = 1.0 - F / L;"),
     ("stats_no_tail", "    if (tail > 0) {\n        out->hole_count += 1;",
      "    if (tail > arena_bytes) {\n        out->hole_count += 1;"),
-    ("stats_cursor_start", "        cursor = offset[i] + size[i];", "        cursor = offset[i];"),
+    ("stats_cursor_start", "        cursor = offset[i] + size[i];\n    }\n    const uint64_t tail",
+     "        cursor = offset[i];\n    }\n    const uint64_t tail"),
+    ("window_hole_cursor_start", "        cursor = offset[i] + size[i];\n    }\n    if (arena_bytes > cursor)",
+     "        cursor = offset[i];\n    }\n    if (arena_bytes > cursor)"),
     ("stats_counts_every_gap", "        if (gap > 0) {\n            out->hole_count += 1;",
      "        if (gap >= 0) {\n            out->hole_count += 1;"),
     ("stats_min_not_max", "            if (gap > out->largest_hole) out->largest_hole = gap;",
@@ -54,6 +58,16 @@ MUTANTS = [
     ("pinned_free_accepted", "(pinned[i] == 1 && live[i] == 0)", "(pinned[i] == 3 && live[i] == 0)"),
     ("pinned_moved_counted", "        if (is_pinned(pinned, i)) {\n            new_off = offset[i] + size[i];\n        } else {",
      "        if (false) {\n        } else {"),
+    ("window_not_shortest", "while (first < last && free_sum - holes[first].len >= request)",
+     "while (first < last && free_sum - holes[first].len > request)"),
+    ("window_exact_fit_rejected", "        if (free_sum < request) continue;", "        if (free_sum <= request) continue;"),
+    ("window_highest_on_tie", "(live_sum == out->moved_bytes && begin < out->begin)",
+     "(live_sum == out->moved_bytes && begin > out->begin)"),
+    ("window_crosses_pinned", "            if (holes[last - 1].pinned_after) {  // start again past the barrier",
+     "            if (false) {"),
+    ("window_cost_not_dropped", "            live_sum -= holes[first].live_after;\n", ""),
+    ("window_tail_ignored", "    if (arena_bytes > cursor) holes.push_back(Hole{cursor, arena_bytes - cursor, 0, false});",
+     ""),
 ]
 
 
@@ -79,6 +93,13 @@ def _battery():
         t = np.array([(0, 32, 1), (32, 32, 1)], dtype=np.uint64)
         assert oracle.validate(t[:, 0], t[:, 1], t[:, 2].astype(np.uint8), 64)[0] == oracle.OK
         T.test_empty_and_degenerate(None)
+        for case in TT.golden_cases():
+            TT.check_golden(case)
+        for k in range(40):
+            heap = W.tiny_heap(rng, int(rng.integers(0, 16)), sizes=(32, 64, 96, 160, 1024),
+                               gap_p=[0.0, 0.3, 0.8][k % 3], live_p=[0.3, 0.6, 1.0][k % 3],
+                               pinned_p=[0.0, 0.3][k % 2])
+            TT.check_against_bruteforce(heap, rng)
     except AssertionError:
         return False
     return True
