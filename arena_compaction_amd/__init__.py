@@ -29,6 +29,7 @@ DEFRAG_EWORKSPACE = -2
 DEFRAG_ENOPLAN = -3
 DEFRAG_EHIP = -4
 DEFRAG_ETIMEOUT = -5
+DEFRAG_ENOFIT = -6
 REASONS = {0: "none", 1: "zero_size", 2: "misaligned", 3: "live_flag",
            4: "out_of_arena", 5: "overlap", 6: "argument", 7: "pinned_flag"}
 U64_MAX = (1 << 64) - 1
@@ -66,6 +67,8 @@ class defrag_plan_t(ctypes.Structure):
                 ("move_begin", ctypes.c_uint64), ("live_bytes", ctypes.c_uint64),
                 ("n_tiles", ctypes.c_uint64), ("max_tiles", ctypes.c_uint64),
                 ("max_blocks_per_tile", ctypes.c_uint64),
+                ("request_bytes", ctypes.c_uint64), ("window_begin", ctypes.c_uint64),
+                ("window_end", ctypes.c_uint64), ("window_hole", ctypes.c_uint64),
                 ("state", ctypes.c_int32), ("device", ctypes.c_int32),
                 ("tuning", defrag_tuning), ("stats", defrag_stats_t)]
 
@@ -96,13 +99,17 @@ def _load() -> ctypes.CDLL:
                                ctypes.POINTER(defrag_stats_t)]
     L.defrag_plan.argtypes = [ctypes.POINTER(defrag_table), U, ctypes.POINTER(defrag_tuning),
                               P, S, P, P, ctypes.POINTER(defrag_plan_t)]
+    L.defrag_plan_targeted.argtypes = [ctypes.POINTER(defrag_table), U, U,
+                                       ctypes.POINTER(defrag_tuning), P, S, P, P,
+                                       ctypes.POINTER(defrag_plan_t)]
     L.defrag_move.argtypes = [P, U, ctypes.POINTER(defrag_plan_t), P, S, P]
     L.defrag_move_status.argtypes = [ctypes.POINTER(defrag_plan_t), P, P]
     L.defrag_remap.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, U, P, P]
     L.defrag_commit.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, P, P, P]
     L.defrag_strerror.argtypes = [ctypes.c_int]
     L.defrag_strerror.restype = ctypes.c_char_p
-    for f in ("defrag_stats", "defrag_plan", "defrag_move", "defrag_move_status",
+    for f in ("defrag_stats", "defrag_plan", "defrag_plan_targeted", "defrag_move",
+              "defrag_move_status",
               "defrag_remap", "defrag_commit"):
         getattr(L, f).restype = ctypes.c_int
     return L
@@ -110,7 +117,8 @@ def _load() -> ctypes.CDLL:
 
 lib = _load()
 
-EXPORTS = ("defrag_workspace_bytes", "defrag_stats", "defrag_plan", "defrag_move",
+EXPORTS = ("defrag_workspace_bytes", "defrag_stats", "defrag_plan", "defrag_plan_targeted",
+           "defrag_move",
            "defrag_move_status", "defrag_remap", "defrag_commit", "defrag_strerror")
 
 
@@ -183,6 +191,25 @@ def defrag_plan(offset, size, live, arena_bytes: int, ws: torch.Tensor,
                          ctypes.byref(plan))
     if rc != DEFRAG_OK:
         raise DefragError(rc, "defrag_plan", plan.stats)
+    return plan
+
+
+def defrag_plan_targeted(offset, size, live, arena_bytes: int, request_bytes: int,
+                         ws: torch.Tensor, new_offset: Optional[torch.Tensor] = None,
+                         tuning: Optional[defrag_tuning] = None, stream=None,
+                         pinned: Optional[torch.Tensor] = None) -> defrag_plan_t:
+    """Raises DefragError with code DEFRAG_ENOFIT when no window fits."""
+    t = make_table(offset, size, live, pinned)
+    plan = defrag_plan_t()
+    if new_offset is not None:
+        assert new_offset.dtype == torch.int64 and new_offset.numel() >= offset.numel()
+    rc = lib.defrag_plan_targeted(ctypes.byref(t), arena_bytes, request_bytes,
+                                  ctypes.byref(tuning) if tuning is not None else None,
+                                  _ptr(ws), ws.numel(), _stream(stream),
+                                  _ptr(new_offset) if new_offset is not None and new_offset.numel()
+                                  else None, ctypes.byref(plan))
+    if rc != DEFRAG_OK:
+        raise DefragError(rc, "defrag_plan_targeted", plan.stats)
     return plan
 
 

@@ -138,7 +138,7 @@ int defrag_stats(const defrag_table *table, uint64_t arena_bytes, void *ws_dev, 
         return rc;
     }
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
-    if (launch_scan(view_of(table), arena_bytes, ws, L, nullptr, false, kDefaultTile, 0, stream) !=
+    if (launch_scan(view_of(table), arena_bytes, ws, L, nullptr, 0, kDefaultTile, 0, stream) !=
         hipSuccess)
         return DEFRAG_EHIP;
     WsHeader h;
@@ -148,9 +148,14 @@ int defrag_stats(const defrag_table *table, uint64_t arena_bytes, void *ws_dev, 
     return h.bad_key == kNone ? DEFRAG_OK : DEFRAG_EINVAL;
 }
 
-int defrag_plan(const defrag_table *table, uint64_t arena_bytes, const defrag_tuning *tuning,
-                void *ws_dev, size_t ws_bytes, hipStream_t stream, uint64_t *new_offset_dev,
-                defrag_plan_t *plan) {
+}  // extern "C"
+
+namespace {
+
+// Full plan (request == 0) or targeted plan (request > 0).
+int plan_common(const defrag_table *table, uint64_t arena_bytes, uint64_t request,
+                const defrag_tuning *tuning, void *ws_dev, size_t ws_bytes, hipStream_t stream,
+                uint64_t *new_offset_dev, defrag_plan_t *plan) {
     if (!plan) return DEFRAG_EINVAL;
     std::memset(plan, 0, sizeof(*plan));
     defrag_tuning tu{0, kDefaultWgPerCu, kDefaultNontemporal, 0};
@@ -177,14 +182,18 @@ int defrag_plan(const defrag_table *table, uint64_t arena_bytes, const defrag_tu
     if (dev < 0) return DEFRAG_EHIP;
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
     const uint64_t epoch = g_epoch.fetch_add(0x9E3779B97F4A7C15ull) ^ reinterpret_cast<uintptr_t>(ws);
-    if (launch_scan(view_of(table), arena_bytes, ws, L, new_offset_dev, true, tu.tile_bytes, epoch,
-                    stream) != hipSuccess)
-        return DEFRAG_EHIP;
+    const hipError_t e =
+        request ? launch_targeted(view_of(table), arena_bytes, request, ws, L, new_offset_dev,
+                                  tu.tile_bytes, epoch, stream)
+                : launch_scan(view_of(table), arena_bytes, ws, L, new_offset_dev, kOutNew,
+                              tu.tile_bytes, epoch, stream);
+    if (e != hipSuccess) return DEFRAG_EHIP;
     WsHeader h;
     rc = read_header(&h, ws, L, stream);
     if (rc) return rc;
     fill_stats(&plan->stats, h, arena_bytes);
     if (h.bad_key != kNone) return DEFRAG_EINVAL;
+    if (request && h.win_state != kWinFound) return DEFRAG_ENOFIT;  // nothing written
     if (h.n_tiles > L.max_tiles) return DEFRAG_EWORKSPACE;  // new offsets were written
 
     const uint64_t T = tu.tile_bytes;
@@ -206,9 +215,39 @@ int defrag_plan(const defrag_table *table, uint64_t arena_bytes, const defrag_tu
     if (h.min_live_size != kNone && h.min_live_size) mb = T / h.min_live_size + 2;
     if (mb > T / 32 + 2) mb = T / 32 + 2;
     plan->max_blocks_per_tile = mb;
+    if (request) {
+        plan->request_bytes = request;
+        plan->window_begin = h.win_begin;
+        plan->window_end = h.win_end;
+        plan->window_hole = h.win_hole;
+    }
     plan->magic = kPlanMagic;
     plan->state = 1;
     return DEFRAG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int defrag_plan(const defrag_table *table, uint64_t arena_bytes, const defrag_tuning *tuning,
+                void *ws_dev, size_t ws_bytes, hipStream_t stream, uint64_t *new_offset_dev,
+                defrag_plan_t *plan) {
+    return plan_common(table, arena_bytes, 0, tuning, ws_dev, ws_bytes, stream, new_offset_dev,
+                       plan);
+}
+
+int defrag_plan_targeted(const defrag_table *table, uint64_t arena_bytes, uint64_t request_bytes,
+                         const defrag_tuning *tuning, void *ws_dev, size_t ws_bytes,
+                         hipStream_t stream, uint64_t *new_offset_dev, defrag_plan_t *plan) {
+    if (plan && request_bytes == 0) {
+        std::memset(plan, 0, sizeof(*plan));
+        arg_error(&plan->stats);
+        return DEFRAG_EINVAL;
+    }
+    if (!plan) return DEFRAG_EINVAL;
+    return plan_common(table, arena_bytes, request_bytes, tuning, ws_dev, ws_bytes, stream,
+                       new_offset_dev, plan);
 }
 
 int defrag_move(void *arena_dev, uint64_t arena_bytes, defrag_plan_t *plan, void *ws_dev,
@@ -295,6 +334,7 @@ const char *defrag_strerror(int code) {
         case DEFRAG_ENOPLAN: return "no matching plan for this workspace";
         case DEFRAG_EHIP: return "HIP runtime error";
         case DEFRAG_ETIMEOUT: return "mover wait timed out";
+        case DEFRAG_ENOFIT: return "no window of the arena can free the requested bytes";
         default: return "unknown error";
     }
 }

@@ -40,11 +40,27 @@ struct alignas(256) WsHeader {
     uint64_t epoch;          // plan epoch, checked by the mover
     uint32_t ticket;         // mover tile ticket counter
     uint32_t status;         // mover status bits (kStatus*)
-    uint64_t pad[18];
+    // targeted plans: the window chosen for the request (kWin*)
+    uint64_t win_state;
+    uint64_t win_begin;      // [win_begin, win_end): the window's bytes
+    uint64_t win_end;
+    uint64_t win_hole;       // free bytes inside it (the hole it frees)
+    uint64_t win_moved;      // live bytes inside it (the bytes that move)
+    uint64_t pad[13];
 };
 static_assert(sizeof(WsHeader) == 256, "header size");
 
 constexpr uint32_t kStatusTimeout = 1u;  // a wait gave up, or a tile overflowed LDS
+
+constexpr uint64_t kWinNone = 0;   // not a targeted plan
+constexpr uint64_t kWinFound = 1;
+constexpr uint64_t kWinNoFit = 2;  // no window frees the request: plan nothing
+
+// Scan outputs (bit flags).
+constexpr int kOutNew = 1;     // new offsets, packed live arrays, plan epoch
+constexpr int kOutSelect = 2;  // packed old offset and size, live-byte and
+                               // pinned-count prefixes; plan epoch (bumped so
+                               // an older plan in the workspace goes stale)
 
 // Element of the plan's scan over table entries.  v is a segmented sum: a
 // pinned entry resets it to its own end (the start of the next segment), a
@@ -64,6 +80,17 @@ struct ScanPart {
     Agg a;
     uint64_t bad_key;
 };
+
+// Per selection-workgroup best window: fewest moved bytes, then lowest
+// first hole; k and l are the first and last hole (hole q lies just below
+// live block q, hole m is the tail).
+struct SelPart {
+    uint64_t cost;
+    uint64_t k;
+    uint64_t l;
+    uint64_t pad;
+};
+constexpr uint32_t kSelThreads = 256;  // one candidate last hole per thread
 
 // Per scan-workgroup hole / move statistics.
 struct StatPart {
@@ -98,10 +125,10 @@ constexpr size_t kPerTileBytes =
 struct WsLayout {
     // fixed part (depends on n only)
     size_t header, part, prefix, spart, tpart, tprefix, live_dst, live_src, live_size,
-        live_pin, tile_base, fixed;
+        live_pin, tile_base, live_z, live_pc, selpart, fixed;
     // tile part (depends on the tile capacity)
     size_t tile_start, tile_first, tiles, flags, total;
-    uint64_t n_scan_blocks, max_tiles;
+    uint64_t n_scan_blocks, n_sel_blocks, max_tiles;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -122,6 +149,10 @@ inline WsLayout ws_fixed(uint64_t n) {
     L.live_size = at; at += align256((n + 1) * sizeof(uint64_t));
     L.live_pin = at;  at += align256((n + 1) * sizeof(uint8_t));
     L.tile_base = at; at += align256((n + 1) * sizeof(uint32_t));
+    L.n_sel_blocks = (n + 1 + kSelThreads - 1) / kSelThreads;
+    L.live_z = at;    at += align256((n + 1) * sizeof(uint64_t));
+    L.live_pc = at;   at += align256((n + 1) * sizeof(uint32_t));
+    L.selpart = at;   at += align256(L.n_sel_blocks * sizeof(SelPart));
     L.fixed = at;
     return L;
 }
@@ -181,12 +212,18 @@ inline LiveView live_view(const uint8_t *ws, const WsLayout &L) {
 }
 
 // ---- plan.hip ----
-// Scan passes and, when write_outputs, the mover's tiles (for at most
+// Scan passes and, with kOutNew, the mover's tiles (for at most
 // L.max_tiles tiles).  All asynchronous; the header then holds totals,
 // statistics and n_tiles (tiles are built only if n_tiles <= L.max_tiles).
 hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws,
-                       const WsLayout &L, uint64_t *new_offset, bool write_outputs,
+                       const WsLayout &L, uint64_t *new_offset, int outputs,
                        uint32_t tile_bytes, uint64_t epoch, hipStream_t s);
+// Targeted plan: a selection scan, the window search (header win_*), then
+// the plan scan with every live block outside the window held in place.
+// Nothing is planned (and new_offset is not written) when no window fits.
+hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t request,
+                           uint8_t *ws, const WsLayout &L, uint64_t *new_offset,
+                           uint32_t tile_bytes, uint64_t epoch, hipStream_t s);
 hipError_t launch_commit(const uint8_t *ws, const WsLayout &L, uint64_t live_blocks,
                          uint64_t *off_out, uint64_t *size_out, uint8_t *live_out,
                          uint8_t *pinned_out, hipStream_t s);

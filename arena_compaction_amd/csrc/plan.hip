@@ -55,9 +55,11 @@ __device__ inline Agg combine(const Agg &a, const Agg &b) {
     return c;
 }
 
-__device__ inline Agg element(uint64_t o, uint64_t s, uint32_t l, uint32_t p) {
+// p: the entry is pinned; f: it stays in place (pinned, or a live block
+// outside a targeted plan's window).  A block that stays starts a segment.
+__device__ inline Agg element(uint64_t o, uint64_t s, uint32_t l, uint32_t p, uint32_t f) {
     Agg e = agg_zero();
-    if (p) {
+    if (f) {
         e.r = 1;
         e.v = o + s;
     } else if (l) {
@@ -174,11 +176,30 @@ __device__ inline uint32_t entry_reason(uint64_t i, uint64_t o, uint64_t s, uint
 __device__ inline uint32_t live_of(const TableView &t, uint64_t i) { return t.live ? t.live[i] : 1u; }
 __device__ inline uint32_t pin_of(const TableView &t, uint64_t i) { return t.pinned ? t.pinned[i] : 0u; }
 
+// A targeted plan moves only the live blocks inside its window [begin, end);
+// win is null for a full plan.
+struct Window {
+    uint64_t begin, end;
+};
+__device__ inline Window window_of(const uint64_t *win) {
+    return win ? Window{win[0], win[1]} : Window{0, kNone};
+}
+__device__ inline uint32_t stays(uint64_t o, uint32_t l, uint32_t p, const Window &w) {
+    return (p || (l && (o < w.begin || o >= w.end))) ? 1u : 0u;
+}
+
+// Nothing more to plan: the table is invalid, or no window fits the request.
+__device__ inline bool plan_dead(const WsHeader *hdr) {
+    return hdr->bad_key != kNone || hdr->win_state == kWinNoFit;
+}
+
 // Pass 1: per-workgroup aggregate and first bad key.
 __global__ __launch_bounds__(kScanThreads) void k_scan_partials(TableView t, uint64_t arena_bytes,
+                                                                const uint64_t *win,
                                                                 ScanPart *part) {
     __shared__ Agg sh[kScanThreads / 64];
     __shared__ uint64_t shr[kScanThreads / 64];
+    const Window w = window_of(win);
     const uint64_t i0 = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanItems;
     Agg a = agg_zero();
     uint64_t bad = kNone;
@@ -192,7 +213,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_partials(TableView t, uin
             const uint32_t l = live_of(t, i), p = pin_of(t, i);
             const uint32_t r = entry_reason(i, o, s, l, p, arena_bytes, prev_end);
             if (r) bad = umin64(bad, (i << 3) | r);
-            a = combine(a, element(o, s, l ? 1u : 0u, p ? 1u : 0u));
+            const uint32_t lb = l ? 1u : 0u, pb = p ? 1u : 0u;
+            a = combine(a, element(o, s, lb, pb, stays(o, lb, pb, w)));
             prev_end = o + s;
         }
     }
@@ -204,7 +226,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_partials(TableView t, uin
 
 // Pass 2 (one workgroup): exclusive scan of the aggregates; table totals.
 __global__ __launch_bounds__(kSpineThreads) void k_scan_spine(const ScanPart *part, ScanPart *prefix,
-                                                              uint64_t nb, WsHeader *hdr) {
+                                                              uint64_t nb, WsHeader *hdr,
+                                                              int reset_window) {
     __shared__ Agg sh[kSpineThreads / 64];
     __shared__ uint64_t shr[kSpineThreads / 64];
     Agg carry = agg_zero();
@@ -228,25 +251,30 @@ __global__ __launch_bounds__(kSpineThreads) void k_scan_spine(const ScanPart *pa
         hdr->live_blocks = carry.cnt;
         hdr->pinned_blocks = carry.pcnt;
         hdr->bad_key = bad;
+        if (reset_window) hdr->win_state = kWinNone;
     }
 }
 
 struct LiveOut {
     uint64_t *dst, *src, *size;
     uint8_t *pin;
+    uint64_t *z;   // live bytes below each live block (selection only)
+    uint32_t *pc;  // pinned blocks below each live block (selection only)
 };
 
 // Pass 3: new offsets, packed live arrays, per-workgroup hole/move stats.
-__global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const ScanPart *prefix,
+__global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const uint64_t *win,
+                                                            const ScanPart *prefix,
                                                             const WsHeader *hdr, uint64_t *new_offset,
                                                             LiveOut lo, StatPart *spart,
-                                                            int write_outputs) {
+                                                            int outputs) {
     __shared__ Agg sh[kScanThreads / 64];
     __shared__ uint64_t shr[kScanThreads / 64];
-    if (hdr->bad_key != kNone) return;  // invalid table: write nothing
+    if (plan_dead(hdr)) return;  // invalid table or nothing to plan: write nothing
+    const Window w = window_of(win);
     const uint64_t i0 = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanItems;
     uint64_t o[kScanItems], s[kScanItems];
-    uint32_t l[kScanItems], p[kScanItems];
+    uint32_t l[kScanItems], p[kScanItems], f[kScanItems];
     Agg a = agg_zero();
 #pragma unroll
     for (uint32_t k = 0; k < kScanItems; ++k) {
@@ -255,12 +283,14 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const S
         s[k] = 0;
         l[k] = 0;
         p[k] = 0;
+        f[k] = 0;
         if (i < t.n) {
             o[k] = t.off[i];
             s[k] = t.size[i];
             l[k] = live_of(t, i) ? 1u : 0u;
             p[k] = pin_of(t, i) ? 1u : 0u;
-            a = combine(a, element(o[k], s[k], l[k], p[k]));
+            f[k] = stays(o[k], l[k], p[k], w);
+            a = combine(a, element(o[k], s[k], l[k], p[k], f[k]));
         }
     }
     Agg total;
@@ -271,14 +301,20 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const S
     for (uint32_t k = 0; k < kScanItems; ++k) {
         const uint64_t i = i0 + k;
         if (i < t.n) {
-            const uint64_t nw = p[k] ? o[k] : run.v;
-            if (write_outputs && new_offset) new_offset[i] = nw;
+            const uint64_t nw = f[k] ? o[k] : run.v;
+            if ((outputs & kOutNew) && new_offset) new_offset[i] = nw;
             if (l[k]) {
-                if (write_outputs) {
+                if (outputs & kOutNew) {
                     lo.dst[run.cnt] = nw;
+                    lo.pin[run.cnt] = (uint8_t)p[k];
+                }
+                if (outputs & (kOutNew | kOutSelect)) {
                     lo.src[run.cnt] = o[k];
                     lo.size[run.cnt] = s[k];
-                    lo.pin[run.cnt] = (uint8_t)p[k];
+                }
+                if (outputs & kOutSelect) {
+                    lo.z[run.cnt] = run.lsum;
+                    lo.pc[run.cnt] = (uint32_t)run.pcnt;
                 }
                 const uint64_t gap = o[k] - run.mx;
                 if (gap) {
@@ -292,7 +328,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const S
                 }
                 min_size = umin64(min_size, s[k]);
             }
-            run = combine(run, element(o[k], s[k], l[k], p[k]));
+            run = combine(run, element(o[k], s[k], l[k], p[k], f[k]));
         }
     }
     max_gap = block_reduce<kScanThreads>(max_gap, shr, OpMax());
@@ -308,9 +344,9 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const S
 // Pass 4 (one workgroup): reduce the statistics, add the tail hole.
 __global__ __launch_bounds__(kSpineThreads) void k_scan_finish(const StatPart *spart, uint64_t nb,
                                                                uint64_t arena_bytes, WsHeader *hdr,
-                                                               int write_outputs, uint64_t epoch) {
+                                                               int outputs, uint64_t epoch) {
     __shared__ uint64_t sh[kSpineThreads / 64];
-    if (hdr->bad_key != kNone) return;
+    if (plan_dead(hdr)) return;
     uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, min_dst = kNone, min_size = kNone;
     for (uint64_t j = threadIdx.x; j < nb; j += kSpineThreads) {
         const StatPart q = spart[j];
@@ -336,7 +372,7 @@ __global__ __launch_bounds__(kSpineThreads) void k_scan_finish(const StatPart *s
         hdr->min_live_size = min_size;
         hdr->move_begin = min_dst;
         // plan fields: a statistics-only pass leaves an existing plan intact
-        if (write_outputs) {
+        if (outputs) {
             hdr->epoch = epoch;
             hdr->ticket = 0;
             hdr->status = 0;
@@ -365,7 +401,7 @@ __device__ inline uint64_t tiles_in_block(const LiveView &lv, uint64_t k, uint64
 __global__ __launch_bounds__(kScanThreads) void k_tcount_partials(LiveView lv, const WsHeader *hdr,
                                                                   uint64_t T, uint64_t *tpart) {
     __shared__ uint64_t sh[kScanThreads / 64];
-    if (hdr->bad_key != kNone) return;
+    if (plan_dead(hdr)) return;
     const uint64_t m = hdr->live_blocks;
     const uint64_t k0 = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanItems;
     uint64_t c = 0;
@@ -380,7 +416,7 @@ __global__ __launch_bounds__(kScanThreads) void k_tcount_partials(LiveView lv, c
 __global__ __launch_bounds__(kSpineThreads) void k_tcount_spine(const uint64_t *tpart, uint64_t *tprefix,
                                                                 uint64_t nb, WsHeader *hdr) {
     __shared__ uint64_t sh[kSpineThreads / 64];
-    if (hdr->bad_key != kNone) return;
+    if (plan_dead(hdr)) return;
     uint64_t carry = 0;
     for (uint64_t base = 0; base < nb; base += kSpineThreads) {
         const uint64_t j = base + threadIdx.x;
@@ -400,7 +436,7 @@ __global__ __launch_bounds__(kScanThreads) void k_tcount_down(LiveView lv, const
                                                               uint64_t T, const uint64_t *tprefix,
                                                               uint32_t *tile_base) {
     __shared__ uint64_t sh[kScanThreads / 64];
-    if (hdr->bad_key != kNone) return;
+    if (plan_dead(hdr)) return;
     const uint64_t m = hdr->live_blocks;
     const uint64_t k0 = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanItems;
     uint64_t c[kScanItems];
@@ -437,7 +473,7 @@ __global__ __launch_bounds__(256) void k_tile_starts(LiveView lv, const uint32_t
                                                      uint64_t T, uint64_t *tile_start,
                                                      uint32_t *tile_first) {
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (hdr->bad_key != kNone || hdr->n_tiles > max_tiles) return;  // plan fails
+    if (plan_dead(hdr) || hdr->n_tiles > max_tiles) return;  // plan fails
     const uint64_t n_tiles = hdr->n_tiles, m = hdr->live_blocks;
     if (t >= n_tiles) return;
     const int64_t k = last_le(tile_base, 0, (int64_t)m, t);
@@ -477,7 +513,7 @@ __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile
                                                uint64_t max_tiles, uint64_t T, TileRec *tiles,
                                                uint32_t *flags) {
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (hdr->bad_key != kNone || hdr->n_tiles > max_tiles) return;  // plan fails
+    if (plan_dead(hdr) || hdr->n_tiles > max_tiles) return;  // plan fails
     const uint64_t n_tiles = hdr->n_tiles, m = hdr->live_blocks;
     if (t >= n_tiles) return;
     const uint64_t t0 = tile_start[t];
@@ -540,11 +576,148 @@ __global__ void k_commit(LiveView lv, uint64_t m, uint64_t *off_out, uint64_t *s
     }
 }
 
+// ---------------------------------------------------------------------------
+// Targeted compaction.  Page: "Ascend 910C cluster tuning", section "Periodic
+// compaction with Ascend C": compaction pauses what it touches and is kept for
+// stopping the damage, and the failure it answers is one request larger than
+// any free block.  Number the holes by the live block just above them (hole q
+// lies below live block q; hole m is the tail), and let
+//   B_q = hole bytes below live block q's start  (B_m = free total)
+//   Z_q = live bytes below live block q          (Z_m = live total)
+// both non-decreasing.  The window of holes k..l (k <= l) holds live blocks
+// k..l-1; packed down to its start they free B_l - B_{k-1} bytes in one piece
+// (B_{-1} = 0) and move Z_l - Z_k bytes.  It may hold no pinned block.  For a
+// last hole l the cheapest window is the one with the largest k that still
+// frees the request, found by binary search over B; the best over all l --
+// fewest moved bytes, then lowest k -- is the window.
+
+__device__ inline uint64_t holes_below(const uint64_t *src, const uint64_t *z, uint64_t q,
+                                       uint64_t m, uint64_t free_total) {
+    return q < m ? src[q] - z[q] : free_total;
+}
+
+__device__ inline bool sel_better(uint64_t c1, uint64_t k1, uint64_t c2, uint64_t k2) {
+    return c1 < c2 || (c1 == c2 && k1 < k2);
+}
+
+// Workgroup arg-min of (cost, k) carrying l, through LDS (NT threads).
+template <int NT>
+__device__ inline void sel_reduce(uint64_t &c, uint64_t &k, uint64_t &l, uint64_t *sh) {
+    constexpr int NW = NT / 64;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const uint64_t c2 = __shfl_xor(c, d, 64), k2 = __shfl_xor(k, d, 64),
+                       l2 = __shfl_xor(l, d, 64);
+        if (sel_better(c2, k2, c, k)) {
+            c = c2;
+            k = k2;
+            l = l2;
+        }
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        sh[3 * w] = c;
+        sh[3 * w + 1] = k;
+        sh[3 * w + 2] = l;
+    }
+    __syncthreads();
+    c = sh[0];
+    k = sh[1];
+    l = sh[2];
+#pragma unroll
+    for (int j = 1; j < NW; ++j) {
+        if (sel_better(sh[3 * j], sh[3 * j + 1], c, k)) {
+            c = sh[3 * j];
+            k = sh[3 * j + 1];
+            l = sh[3 * j + 2];
+        }
+    }
+    __syncthreads();
+}
+
+// One lane per candidate last hole l in [0, m].
+__global__ __launch_bounds__(kSelThreads) void k_select(const uint64_t *src, const uint64_t *z,
+                                                        const uint32_t *pc, const WsHeader *hdr,
+                                                        uint64_t arena_bytes, uint64_t request,
+                                                        SelPart *sp) {
+    __shared__ uint64_t sh[3 * (kSelThreads / 64)];
+    if (hdr->bad_key != kNone) return;
+    const uint64_t m = hdr->live_blocks, lt = hdr->live_bytes, np = hdr->pinned_blocks;
+    const uint64_t free_total = arena_bytes - lt;
+    const uint64_t l = (uint64_t)blockIdx.x * kSelThreads + threadIdx.x;
+    uint64_t cost = kNone, kk = kNone, ll = kNone;
+    if (l <= m) {
+        const uint64_t bl = holes_below(src, z, l, m, free_total);
+        if (bl >= request) {
+            const uint64_t x = bl - request;
+            // first q in [0, l) with B_q > x; then k = q
+            uint64_t lo = 0, len = l;
+            while (len > 0) {
+                const uint64_t half = len >> 1, q = lo + half;
+                if (src[q] - z[q] <= x) {
+                    lo = q + 1;
+                    len -= half + 1;
+                } else {
+                    len = half;
+                }
+            }
+            const uint64_t k = lo;
+            const uint64_t pl = l < m ? pc[l] : np, pk = k < m ? pc[k] : np;
+            if (pl == pk) {  // no pinned block among k..l-1
+                cost = (l < m ? z[l] : lt) - (k < m ? z[k] : lt);
+                kk = k;
+                ll = l;
+            }
+        }
+    }
+    sel_reduce<kSelThreads>(cost, kk, ll, sh);
+    if (threadIdx.x == 0) sp[blockIdx.x] = SelPart{cost, kk, ll, 0};
+}
+
+// One workgroup: the best window over all candidates, as bytes.
+__global__ __launch_bounds__(kSpineThreads) void k_select_finish(const SelPart *sp, uint64_t nb,
+                                                                 const uint64_t *src,
+                                                                 const uint64_t *size,
+                                                                 const uint64_t *z,
+                                                                 uint64_t arena_bytes,
+                                                                 WsHeader *hdr) {
+    __shared__ uint64_t sh[3 * (kSpineThreads / 64)];
+    if (hdr->bad_key != kNone) return;
+    uint64_t c = kNone, k = kNone, l = kNone;
+    for (uint64_t j = threadIdx.x; j < nb; j += kSpineThreads) {
+        const SelPart q = sp[j];
+        if (sel_better(q.cost, q.k, c, k)) {
+            c = q.cost;
+            k = q.k;
+            l = q.l;
+        }
+    }
+    sel_reduce<kSpineThreads>(c, k, l, sh);
+    if (threadIdx.x != 0) return;
+    if (c == kNone) {
+        hdr->win_state = kWinNoFit;
+        hdr->win_begin = hdr->win_end = hdr->win_hole = hdr->win_moved = 0;
+        return;
+    }
+    const uint64_t m = hdr->live_blocks;
+    const uint64_t free_total = arena_bytes - hdr->live_bytes;
+    const uint64_t below = k ? holes_below(src, z, k - 1, m, free_total) : 0;
+    hdr->win_begin = k ? src[k - 1] + size[k - 1] : 0;
+    hdr->win_end = l < m ? src[l] : arena_bytes;
+    hdr->win_hole = holes_below(src, z, l, m, free_total) - below;
+    hdr->win_moved = c;
+    hdr->win_state = kWinFound;
+}
+
 }  // namespace
 
-hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsLayout &L,
-                       uint64_t *new_offset, bool write_outputs, uint32_t tile_bytes,
-                       uint64_t epoch, hipStream_t s) {
+namespace {
+
+// Scan passes, then (kOutNew) the tile passes.  win: the targeted plan's
+// window in the header, or null.
+void queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsLayout &L,
+                uint64_t *new_offset, int outputs, const uint64_t *win, uint32_t tile_bytes,
+                uint64_t epoch, hipStream_t s) {
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.header);
     ScanPart *part = reinterpret_cast<ScanPart *>(ws + L.part);
     ScanPart *prefix = reinterpret_cast<ScanPart *>(ws + L.prefix);
@@ -552,20 +725,23 @@ hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, co
     LiveOut lo{reinterpret_cast<uint64_t *>(ws + L.live_dst),
                reinterpret_cast<uint64_t *>(ws + L.live_src),
                reinterpret_cast<uint64_t *>(ws + L.live_size),
-               reinterpret_cast<uint8_t *>(ws + L.live_pin)};
+               reinterpret_cast<uint8_t *>(ws + L.live_pin),
+               reinterpret_cast<uint64_t *>(ws + L.live_z),
+               reinterpret_cast<uint32_t *>(ws + L.live_pc)};
     const uint64_t nb = L.n_scan_blocks;
     if (nb) {
         hipLaunchKernelGGL(k_scan_partials, dim3((uint32_t)nb), dim3(kScanThreads), 0, s, t,
-                           arena_bytes, part);
+                           arena_bytes, win, part);
     }
-    hipLaunchKernelGGL(k_scan_spine, dim3(1), dim3(kSpineThreads), 0, s, part, prefix, nb, hdr);
+    hipLaunchKernelGGL(k_scan_spine, dim3(1), dim3(kSpineThreads), 0, s, part, prefix, nb, hdr,
+                       win ? 0 : 1);
     if (nb) {
-        hipLaunchKernelGGL(k_scan_down, dim3((uint32_t)nb), dim3(kScanThreads), 0, s, t, prefix,
-                           hdr, new_offset, lo, spart, write_outputs ? 1 : 0);
+        hipLaunchKernelGGL(k_scan_down, dim3((uint32_t)nb), dim3(kScanThreads), 0, s, t, win,
+                           prefix, hdr, new_offset, lo, spart, outputs);
     }
     hipLaunchKernelGGL(k_scan_finish, dim3(1), dim3(kSpineThreads), 0, s, spart, nb, arena_bytes,
-                       hdr, write_outputs ? 1 : 0, epoch);
-    if (write_outputs) {
+                       hdr, outputs, epoch);
+    if (outputs & kOutNew) {
         const LiveView lv = live_view(ws, L);
         uint64_t *tpart = reinterpret_cast<uint64_t *>(ws + L.tpart);
         uint64_t *tprefix = reinterpret_cast<uint64_t *>(ws + L.tprefix);
@@ -592,6 +768,33 @@ hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, co
                                flags);
         }
     }
+}
+
+}  // namespace
+
+hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsLayout &L,
+                       uint64_t *new_offset, int outputs, uint32_t tile_bytes, uint64_t epoch,
+                       hipStream_t s) {
+    queue_scan(t, arena_bytes, ws, L, new_offset, outputs, nullptr, tile_bytes, epoch, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t request,
+                           uint8_t *ws, const WsLayout &L, uint64_t *new_offset,
+                           uint32_t tile_bytes, uint64_t epoch, hipStream_t s) {
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.header);
+    const uint64_t *src = reinterpret_cast<const uint64_t *>(ws + L.live_src);
+    const uint64_t *size = reinterpret_cast<const uint64_t *>(ws + L.live_size);
+    const uint64_t *z = reinterpret_cast<const uint64_t *>(ws + L.live_z);
+    const uint32_t *pc = reinterpret_cast<const uint32_t *>(ws + L.live_pc);
+    SelPart *sp = reinterpret_cast<SelPart *>(ws + L.selpart);
+    queue_scan(t, arena_bytes, ws, L, nullptr, kOutSelect, nullptr, tile_bytes, epoch, s);
+    // candidates: every last hole l in [0, m], m <= n
+    hipLaunchKernelGGL(k_select, dim3((uint32_t)L.n_sel_blocks), dim3(kSelThreads), 0, s, src, z,
+                       pc, hdr, arena_bytes, request, sp);
+    hipLaunchKernelGGL(k_select_finish, dim3(1), dim3(kSpineThreads), 0, s, sp, L.n_sel_blocks,
+                       src, size, z, arena_bytes, hdr);
+    queue_scan(t, arena_bytes, ws, L, new_offset, kOutNew, &hdr->win_begin, tile_bytes, epoch, s);
     return hipGetLastError();
 }
 

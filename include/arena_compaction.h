@@ -32,9 +32,10 @@
  *             to new_offset[i] + (h - offset[i]); any other handle (in a hole,
  *             at or past the arena end) maps to UINT64_MAX and is counted.
  *
- * Call order per compaction: defrag_plan -> defrag_move -> defrag_remap (any
- * number of handle batches) -> defrag_commit (optional: the packed table).
- * defrag_stats measures any table without planning.
+ * Call order per compaction: defrag_plan (or defrag_plan_targeted) ->
+ * defrag_move -> defrag_remap (any number of handle batches) ->
+ * defrag_commit (optional: the packed table).  defrag_stats measures any
+ * table without planning.
  *
  * Ownership: the caller owns every buffer (arena, table, outputs, handles and
  * the workspace).  The library allocates no device memory and never writes
@@ -70,6 +71,7 @@ extern "C" {
 #define DEFRAG_ENOPLAN (-3)    /* move/remap/commit without a matching plan     */
 #define DEFRAG_EHIP (-4)       /* a HIP runtime call failed                    */
 #define DEFRAG_ETIMEOUT (-5)   /* mover watchdog expired (a wait never ended)  */
+#define DEFRAG_ENOFIT (-6)     /* targeted plan: no window frees the request   */
 
 /* Why a table was rejected: the first failing entry, and within it the first
  * failing check in the order zero size, misaligned, live flag, pinned flag,
@@ -151,6 +153,13 @@ typedef struct defrag_plan_t {
     uint64_t n_tiles;
     uint64_t max_tiles;    /* tile capacity of the workspace                   */
     uint64_t max_blocks_per_tile;
+    /* targeted plans (all 0 for a full plan): the request and the window
+     * [window_begin, window_end) whose live blocks move; window_hole is the
+     * hole it frees, at [window_end - window_hole, window_end) */
+    uint64_t request_bytes;
+    uint64_t window_begin;
+    uint64_t window_end;
+    uint64_t window_hole;
     int32_t state;         /* 0 none/invalid, 1 planned, 2 moved               */
     int32_t device;
     defrag_tuning tuning;
@@ -183,6 +192,28 @@ int defrag_plan(const defrag_table *table, uint64_t arena_bytes,
                 const defrag_tuning *tuning, void *ws_dev, size_t ws_bytes,
                 hipStream_t stream, uint64_t *new_offset_dev,
                 defrag_plan_t *plan_host);
+
+/* Plan a targeted compaction: move the fewest bytes that free one hole of at
+ * least request_bytes (910C page, "Periodic compaction with Ascend C":
+ * compaction pauses what it touches and is a stop-loss step; the failure it
+ * answers is one request -- a 4.2 GB communication buffer -- that no free
+ * block can hold).  A window is a run of consecutive holes with the live
+ * blocks between them, none pinned; packing those blocks down to the
+ * window's start merges its holes into one at its top.  The plan takes the
+ * window whose hole holds the request with the fewest live bytes inside,
+ * and among those the lowest; every live block outside it keeps its place,
+ * so new_offset_dev is the segmented result with those blocks held (a
+ * window already holding the request moves nothing).  Otherwise as
+ * defrag_plan, and the plan feeds defrag_move / defrag_remap /
+ * defrag_commit unchanged.  request_bytes == 0 is DEFRAG_EINVAL.  When no
+ * window can free the request (it exceeds the largest hole a full
+ * compaction would leave) returns DEFRAG_ENOFIT, writes nothing, and fills
+ * plan_host->stats with the table's statistics, whose moved counts are
+ * those of a full compaction.  Queues every pass, then synchronises once. */
+int defrag_plan_targeted(const defrag_table *table, uint64_t arena_bytes,
+                         uint64_t request_bytes, const defrag_tuning *tuning,
+                         void *ws_dev, size_t ws_bytes, hipStream_t stream,
+                         uint64_t *new_offset_dev, defrag_plan_t *plan_host);
 
 /* Move the live blocks (910C: move the data).  arena_dev must be 16-byte
  * aligned and arena_bytes must equal the planned size.  Asynchronous; a plan

@@ -60,7 +60,9 @@ def pristine_host(heap: W.Heap) -> torch.Tensor:
 
 
 def run_gpu(heap: W.Heap, dev="cuda", tuning=None, arena: Optional[torch.Tensor] = None,
-            handles: Optional[np.ndarray] = None) -> GpuRun:
+            handles: Optional[np.ndarray] = None, request: Optional[int] = None) -> GpuRun:
+    """Plan (targeted when request is given), move, remap, commit and the
+    post-move statistics through the C-ABI."""
     import arena_compaction_amd as ac
     off, size, live = device_table(heap, dev)
     pin = device_pinned(heap, dev)
@@ -68,8 +70,12 @@ def run_gpu(heap: W.Heap, dev="cuda", tuning=None, arena: Optional[torch.Tensor]
                       tuning.tile_bytes if tuning is not None else 0, device=dev,
                       max_pinned=heap.n_pinned)
     new_off = torch.full((heap.n,), -7, dtype=torch.int64, device=dev)
-    plan = ac.defrag_plan(off, size, live, heap.arena_bytes, ws, new_off, tuning=tuning,
-                          pinned=pin)
+    if request is None:
+        plan = ac.defrag_plan(off, size, live, heap.arena_bytes, ws, new_off, tuning=tuning,
+                              pinned=pin)
+    else:
+        plan = ac.defrag_plan_targeted(off, size, live, heap.arena_bytes, request, ws, new_off,
+                                       tuning=tuning, pinned=pin)
     if arena is None:
         arena = torch.empty(heap.arena_bytes, dtype=torch.uint8, device=dev)
         W.fill_payload(arena, 0, heap.payload_mode, heap.payload_seed)
@@ -101,9 +107,12 @@ def check_stats(got, want, what=""):
         assert g == w, f"{what} stats.{k}: gpu {g} != oracle {w}"
 
 
-def check_tables_and_handles(heap: W.Heap, r: GpuRun, handles: Optional[np.ndarray] = None):
-    """new offsets, plan stats, remap, post-move stats: all bit-exact."""
-    pin = heap.pinned
+def check_tables_and_handles(heap: W.Heap, r: GpuRun, handles: Optional[np.ndarray] = None,
+                             hold: Optional[np.ndarray] = None):
+    """new offsets, plan stats, remap, post-move stats: all bit-exact.
+    hold: the blocks that stay in place, if not just the pinned ones (a
+    targeted plan holds every live block outside its window)."""
+    pin = heap.pinned if hold is None else hold
     want_new = oracle.new_offsets(heap.offset, heap.size, heap.live, pin)
     assert np.array_equal(r.new_off, want_new), "new offsets differ"
     check_stats(r.plan.stats, oracle.stats(heap.offset, heap.size, heap.live, heap.arena_bytes,
@@ -113,15 +122,18 @@ def check_tables_and_handles(heap: W.Heap, r: GpuRun, handles: Optional[np.ndarr
     assert np.array_equal(r.remapped, want_h), "remapped handles differ"
     assert r.n_invalid == want_bad, (r.n_invalid, want_bad)
     li = np.flatnonzero(heap.live)
+    user_pin = heap.pinned
     post_want = oracle.stats(want_new[li], heap.size[li], np.ones(li.shape[0], np.uint8),
-                             heap.arena_bytes, pinned=None if pin is None else pin[li])
+                             heap.arena_bytes, pinned=None if user_pin is None else user_pin[li])
     check_stats(r.post_stats, post_want, "post")
 
 
-def check_arena_full(heap: W.Heap, r: GpuRun, pristine: torch.Tensor):
+def check_arena_full(heap: W.Heap, r: GpuRun, pristine: torch.Tensor,
+                     hold: Optional[np.ndarray] = None):
     """Whole arena against the oracle's ordered memmove of the same bytes."""
     ref = pristine.numpy().copy()
-    oracle.compact(ref, heap.offset, heap.size, heap.live, heap.pinned)
+    oracle.compact(ref, heap.offset, heap.size, heap.live,
+                   heap.pinned if hold is None else hold)
     got = r.arena.cpu().numpy()
     if not np.array_equal(got, ref):
         bad = np.flatnonzero(got != ref)
@@ -129,11 +141,13 @@ def check_arena_full(heap: W.Heap, r: GpuRun, pristine: torch.Tensor):
 
 
 def sample_windows(heap: W.Heap, rng: np.random.Generator, n_random: int = 2048,
-                   win: int = 4096, per_block_cap: int = 4096):
+                   win: int = 4096, per_block_cap: int = 4096,
+                   hold: Optional[np.ndarray] = None):
     """Windows (start, length) of the compacted arena to check: the first and
     last bytes of (a sample of) every live block at its new place, random
     windows below and above the live total, and the window across it."""
-    new = oracle.new_offsets(heap.offset, heap.size, heap.live, heap.pinned)
+    new = oracle.new_offsets(heap.offset, heap.size, heap.live,
+                             heap.pinned if hold is None else hold)
     li = np.flatnonzero(heap.live)
     if li.shape[0] > per_block_cap:
         li = np.sort(rng.choice(li, per_block_cap, replace=False))
@@ -153,7 +167,7 @@ def sample_windows(heap: W.Heap, rng: np.random.Generator, n_random: int = 2048,
     return wins
 
 
-def check_arena_sampled(heap: W.Heap, r: GpuRun, windows):
+def check_arena_sampled(heap: W.Heap, r: GpuRun, windows, hold: Optional[np.ndarray] = None):
     """Sampled windows against the oracle's per-byte source map applied to
     the generator's pristine payload."""
     for (p0, ln) in windows:
@@ -161,7 +175,7 @@ def check_arena_sampled(heap: W.Heap, r: GpuRun, windows):
             continue
         got = r.arena[p0:p0 + ln].cpu().numpy()
         d, s, l = oracle.source_map(heap.offset, heap.size, heap.live, heap.arena_bytes, p0, ln,
-                                    pinned=heap.pinned)
+                                    pinned=heap.pinned if hold is None else hold)
         want = np.empty(ln, dtype=np.uint8)
         for dd, ss, ll in zip(d.tolist(), s.tolist(), l.tolist()):
             want[dd - p0:dd - p0 + ll] = W.payload_window(ss, ll, heap.payload_mode,

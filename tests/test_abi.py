@@ -20,7 +20,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     fns = _declared_functions()
-    for f in ("defrag_stats", "defrag_plan", "defrag_move", "defrag_remap",
+    for f in ("defrag_stats", "defrag_plan", "defrag_plan_targeted", "defrag_move", "defrag_remap",
               "defrag_workspace_bytes", "defrag_strerror", "defrag_commit",
               "defrag_move_status"):
         assert f in fns, f
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 def test_strerror_and_codes():
     import arena_compaction_amd as ac
     assert ac.defrag_strerror(0) == "ok"
-    for c in (-1, -2, -3, -4, -5):
+    for c in (-1, -2, -3, -4, -5, -6):
         assert ac.defrag_strerror(c) not in ("ok", "unknown error")
     assert ac.defrag_strerror(-99) == "unknown error"
 
@@ -86,6 +86,13 @@ def test_host_side_argument_errors_need_no_gpu():
     # misaligned workspace pointer (never dereferenced: refused on the host)
     assert L.defrag_stats(ctypes.byref(t), 4096, ctypes.c_void_p(0x1008), 1 << 20, None,
                           ctypes.byref(st)) == ac.DEFRAG_EWORKSPACE
+    # targeted plan: a zero request and a missing plan are refused on the host
+    assert L.defrag_plan_targeted(ctypes.byref(t), 4096, 0, None, ctypes.c_void_p(0x1000),
+                                  1 << 20, None, None, ctypes.byref(plan)) == ac.DEFRAG_EINVAL
+    assert plan.stats.invalid_reason == 6
+    assert L.defrag_plan_targeted(ctypes.byref(t), 4096, 64, None, ctypes.c_void_p(0x1000),
+                                  1 << 20, None, None, None) == ac.DEFRAG_EINVAL
+    assert ac.defrag_strerror(ac.DEFRAG_ENOFIT) not in ("ok", "unknown error")
     # bad tile size
     tu = ac.defrag_tuning(100, 0, 0, 0)
     assert L.defrag_plan(ctypes.byref(t), 4096, ctypes.byref(tu), ctypes.c_void_p(0x1000),
