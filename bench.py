@@ -118,6 +118,10 @@ def main() -> int:
     ap.add_argument("--tile", type=int, default=None, help="override the mover tile bytes")
     ap.add_argument("--wg-per-cu", type=int, default=None, help="override (0 = max occupancy)")
     ap.add_argument("--nontemporal", type=int, default=None, help="override (0..3)")
+    ap.add_argument("--request", type=int, default=None,
+                    help="bytes for the targeted-compaction leg (default: 4.2/80 of the arena "
+                         "for workloads 3 and 3p -- the 910C page's 4.2 GB buffer -- else off; "
+                         "0 turns it off)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="GIB",
@@ -231,6 +235,52 @@ def main() -> int:
               file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     wall = time.time() - t_wall0
+    full_plan = plan
+
+    # Targeted leg: the smallest move that frees one hole of the request.
+    request = args.request
+    if request is None:
+        request = S * 42 // 800 if args.config in ("3", "3p") else 0
+    targeted = None
+    if request:
+        tt = {"step": [], "plan": [], "move": [], "remap": [], "post": []}
+        for k in range(args.warmup + args.steps):
+            refill()
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            ev[0].record(stream)
+            tp = ac.defrag_plan_targeted(off, size, live, S, request, ws, new_off,
+                                         tuning=tuning, stream=stream, pinned=pinned)
+            ev[1].record(stream)
+            ac.defrag_move(arena, tp, ws, stream=stream)
+            ev[2].record(stream)
+            ac.defrag_remap(tp, ws, h_in, h_out, n_bad, stream=stream)
+            ev[3].record(stream)
+            ac.defrag_commit(tp, ws, c_off, c_size, c_live, stream=stream, pinned_out=c_pin)
+            tpost = ac.defrag_stats(c_off, c_size, c_live, S, ws, stream=stream, pinned=c_pin)
+            ev[4].record(stream)
+            torch.cuda.synchronize()
+            assert ac.defrag_move_status(tp, ws) == ac.DEFRAG_OK
+            assert tpost.largest_hole >= request and int(n_bad.item()) == 0
+            if k >= args.warmup:
+                for key, (a, b) in (("step", (0, 4)), ("plan", (0, 1)), ("move", (1, 2)),
+                                    ("remap", (2, 3)), ("post", (3, 4))):
+                    tt[key].append(ev[a].elapsed_time(ev[b]))
+        tmean = {k: float(np.mean(v)) for k, v in tt.items()}
+        tmoved = int(tp.stats.moved_bytes)
+        targeted = {
+            "request_bytes": request,
+            "window": [int(tp.window_begin), int(tp.window_end)],
+            "hole_bytes": int(tp.window_hole),
+            "moved_bytes": tmoved,
+            "moved_vs_full": round(tmoved / moved, 4) if moved else None,
+            "ms": {k: round(v, 4) for k, v in tmean.items()},
+            "step_vs_full": round(tmean["step"] / float(np.mean(times["step"])), 4),
+            "move_GBps": round(2 * tmoved / (tmean["move"] * 1e-3) / 1e9, 2) if tmoved else None,
+            "after_largest_hole": int(tpost.largest_hole),
+        }
+        print(f"# targeted: request {request} moved {tmoved} step {tmean['step']:.3f} ms",
+              file=sys.stderr, flush=True)
 
     mean = {k: float(np.mean(v)) for k, v in times.items()}
     ms_step = mean["step"]
@@ -238,7 +288,8 @@ def main() -> int:
     move_gbps = 2 * moved / (mean["move"] * 1e-3) / 1e9
     handles_per_s = heap.handles.shape[0] / (mean["remap"] * 1e-3)
     traffic = _traffic(moved)
-    s0 = plan.stats
+    s0 = full_plan.stats
+    plan = full_plan
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -277,6 +328,7 @@ def main() -> int:
                    "frag_one_minus_largest_over_free": s0.frag_one_minus_largest_over_free},
         "after": {"largest_hole": int(post.largest_hole), "hole_count": int(post.hole_count),
                   "frag_free_over_largest_minus_1": post.frag_free_over_largest_minus_1},
+        "targeted": targeted,
         "roofline": {
             "bound": "hbm",
             "kernel": "k_move (defrag_move)",
