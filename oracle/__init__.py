@@ -75,6 +75,8 @@ def _bind(path: str):
     L.oracle_source_map.restype = ctypes.c_int64
     L.oracle_target_window.argtypes = [P, P, P, P, U, U, U, P]
     L.oracle_target_window.restype = ctypes.c_int
+    L.oracle_first_fit.argtypes = [P, P, P, U, U, U, P]
+    L.oracle_first_fit.restype = ctypes.c_int
     return L
 
 
@@ -203,3 +205,15 @@ def window_pins(off, live, pinned, window: Window) -> np.ndarray:
     if pinned is not None:
         fixed |= np.asarray(pinned, dtype=np.uint8) == 1
     return fixed.astype(np.uint8)
+
+
+def first_fit(off, size, live, arena_bytes, request) -> int:
+    """Offset the CANN pool's first fit gives the request (oracle.h), or
+    U64_MAX when no hole holds it; ValueError for request == 0."""
+    off, size, live, _ = _table(off, size, live)
+    out = ctypes.c_uint64()
+    rc = lib().oracle_first_fit(_p(off), _p(size), _p(live), off.shape[0], arena_bytes, request,
+                                ctypes.byref(out))
+    if rc != 0:
+        raise ValueError("request must be at least one byte")
+    return out.value

@@ -276,4 +276,26 @@ int oracle_target_window(const uint64_t *offset, const uint64_t *size,
     return ORACLE_OK;
 }
 
+// [CANN] 2.2: the pool rounds a request up to 32 bytes and takes the first
+// free block that holds it; adjacent free blocks are merged, so a free block
+// is a whole hole.  Walk the holes from low to high addresses.
+int oracle_first_fit(const uint64_t *offset, const uint64_t *size,
+                     const uint8_t *live, uint64_t n, uint64_t arena_bytes,
+                     uint64_t request, uint64_t *offset_out) {
+    *offset_out = UINT64_MAX;
+    if (request == 0 || request > UINT64_MAX - 31) return ORACLE_EINVAL;
+    const uint64_t need = (request + 31) / 32 * 32;
+    uint64_t cursor = 0;  // end of the last live block
+    for (uint64_t i = 0; i < n; ++i) {
+        if (!live[i]) continue;
+        if (offset[i] - cursor >= need) {
+            *offset_out = cursor;
+            return ORACLE_OK;
+        }
+        cursor = offset[i] + size[i];
+    }
+    if (arena_bytes - cursor >= need) *offset_out = cursor;
+    return ORACLE_OK;
+}
+
 }  // extern "C"

@@ -135,6 +135,17 @@ int oracle_target_window(const uint64_t *offset, const uint64_t *size,
                          const uint8_t *live, const uint8_t *pinned, uint64_t n,
                          uint64_t arena_bytes, uint64_t request, oracle_window *out);
 
+/* First fit ([CANN] 2.2 memory pool): a request is rounded up to a multiple
+ * of 32 bytes and placed at the start of the first free block, in the
+ * pool's merged free list, that can hold it.  Here the merged free list is
+ * the table's holes in address order, so the result is the start of the
+ * lowest hole of at least the rounded size.  Returns ORACLE_EINVAL for
+ * request == 0 (or one that rounds past 2^64), else ORACLE_OK with
+ * *offset_out = that start, or UINT64_MAX if no hole holds it. */
+int oracle_first_fit(const uint64_t *offset, const uint64_t *size,
+                     const uint8_t *live, uint64_t n, uint64_t arena_bytes,
+                     uint64_t request, uint64_t *offset_out);
+
 #ifdef __cplusplus
 }
 #endif

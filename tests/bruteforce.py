@@ -157,3 +157,14 @@ def target_window(arena_bytes, off, size, live, request, pinned=None):
             if best is None or key < best[0]:
                 best = (key, (1, a, b, run, moved))
     return best[1] if best else (0, 0, 0, 0, 0)
+
+
+def first_fit(arena_bytes, off, size, live, request):
+    """The pool of the CANN page (section 2.2) run on the byte map: round the
+    request up to 32 bytes, list the free runs (merged neighbours) by
+    address, take the first long enough.  U64_MAX if none."""
+    need = -(-request // 32) * 32
+    for start, length in holes(live_bitmap(arena_bytes, off, size, live)):
+        if length >= need:
+            return start
+    return U64_MAX

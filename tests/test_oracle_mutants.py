@@ -14,6 +14,7 @@ import oracle
 import workloads as W
 import test_oracle as T
 import test_oracle_targeted as TT
+import test_oracle_first_fit as FF
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.cpp")
 
@@ -66,6 +67,13 @@ MUTANTS = [
     ("window_crosses_pinned", "            if (holes[last - 1].pinned_after) {  // start again past the barrier",
      "            if (false) {"),
     ("window_cost_not_dropped", "            live_sum -= holes[first].live_after;\n", ""),
+    ("first_fit_exact_rejected", "        if (offset[i] - cursor >= need) {", "        if (offset[i] - cursor > need) {"),
+    ("first_fit_no_rounding", "    const uint64_t need = (request + 31) / 32 * 32;", "    const uint64_t need = request;"),
+    ("first_fit_round_16", "    const uint64_t need = (request + 31) / 32 * 32;",
+     "    const uint64_t need = (request + 15) / 16 * 16;"),
+    ("first_fit_hole_end", "            *offset_out = cursor;\n            return ORACLE_OK;",
+     "            *offset_out = offset[i] - need;\n            return ORACLE_OK;"),
+    ("first_fit_tail_ignored", "    if (arena_bytes - cursor >= need) *offset_out = cursor;", ""),
     ("window_tail_ignored", "    if (arena_bytes > cursor) holes.push_back(Hole{cursor, arena_bytes - cursor, 0, false});",
      ""),
 ]
@@ -100,6 +108,9 @@ def _battery():
                                gap_p=[0.0, 0.3, 0.8][k % 3], live_p=[0.3, 0.6, 1.0][k % 3],
                                pinned_p=[0.0, 0.3][k % 2])
             TT.check_against_bruteforce(heap, rng)
+            FF.check_against_bruteforce(heap, rng)
+            FF.check_proof(heap, rng)
+        FF.check_golden()
     except AssertionError:
         return False
     return True
