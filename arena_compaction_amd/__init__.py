@@ -102,13 +102,17 @@ def _load() -> ctypes.CDLL:
     L.defrag_plan_targeted.argtypes = [ctypes.POINTER(defrag_table), U, U,
                                        ctypes.POINTER(defrag_tuning), P, S, P, P,
                                        ctypes.POINTER(defrag_plan_t)]
+    L.defrag_first_fit.argtypes = [ctypes.POINTER(defrag_table), U, U, P, S, P,
+                                   ctypes.POINTER(ctypes.c_uint64),
+                                   ctypes.POINTER(defrag_stats_t)]
     L.defrag_move.argtypes = [P, U, ctypes.POINTER(defrag_plan_t), P, S, P]
     L.defrag_move_status.argtypes = [ctypes.POINTER(defrag_plan_t), P, P]
     L.defrag_remap.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, U, P, P]
     L.defrag_commit.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, P, P, P]
     L.defrag_strerror.argtypes = [ctypes.c_int]
     L.defrag_strerror.restype = ctypes.c_char_p
-    for f in ("defrag_stats", "defrag_plan", "defrag_plan_targeted", "defrag_move",
+    for f in ("defrag_stats", "defrag_first_fit", "defrag_plan", "defrag_plan_targeted",
+              "defrag_move",
               "defrag_move_status",
               "defrag_remap", "defrag_commit"):
         getattr(L, f).restype = ctypes.c_int
@@ -117,7 +121,8 @@ def _load() -> ctypes.CDLL:
 
 lib = _load()
 
-EXPORTS = ("defrag_workspace_bytes", "defrag_stats", "defrag_plan", "defrag_plan_targeted",
+EXPORTS = ("defrag_workspace_bytes", "defrag_stats", "defrag_first_fit", "defrag_plan",
+           "defrag_plan_targeted",
            "defrag_move",
            "defrag_move_status", "defrag_remap", "defrag_commit", "defrag_strerror")
 
@@ -174,6 +179,22 @@ def defrag_stats(offset, size, live, arena_bytes: int, ws: torch.Tensor,
     if rc != DEFRAG_OK:
         raise DefragError(rc, "defrag_stats", out)
     return out
+
+
+def defrag_first_fit(offset, size, live, arena_bytes: int, request_bytes: int,
+                     ws: torch.Tensor, stream=None, pinned=None):
+    """(offset, stats): the offset first fit gives the request, or None when
+    no hole holds it (DEFRAG_ENOFIT)."""
+    t = make_table(offset, size, live, pinned)
+    out = ctypes.c_uint64()
+    st = defrag_stats_t()
+    rc = lib.defrag_first_fit(ctypes.byref(t), arena_bytes, request_bytes, _ptr(ws), ws.numel(),
+                              _stream(stream), ctypes.byref(out), ctypes.byref(st))
+    if rc == DEFRAG_ENOFIT:
+        return None, st
+    if rc != DEFRAG_OK:
+        raise DefragError(rc, "defrag_first_fit", st)
+    return int(out.value), st
 
 
 def defrag_plan(offset, size, live, arena_bytes: int, ws: torch.Tensor,

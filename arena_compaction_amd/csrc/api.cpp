@@ -123,9 +123,13 @@ size_t defrag_workspace_bytes(uint64_t n, uint64_t max_pinned, uint64_t arena_by
     return ws_with_tiles(n, tiles).total;
 }
 
-int defrag_stats(const defrag_table *table, uint64_t arena_bytes, void *ws_dev, size_t ws_bytes,
-                 hipStream_t stream, defrag_stats_t *out_host) {
-    if (!out_host) return DEFRAG_EINVAL;
+}  // extern "C"
+
+namespace {
+
+// The statistics pass (and, if fit_need != kNone, the first fit).
+int stats_pass(const defrag_table *table, uint64_t arena_bytes, uint64_t fit_need, void *ws_dev,
+               size_t ws_bytes, hipStream_t stream, defrag_stats_t *out_host, WsHeader *h) {
     int rc = check_table(table);
     if (rc) {
         arg_error(out_host);
@@ -138,14 +142,41 @@ int defrag_stats(const defrag_table *table, uint64_t arena_bytes, void *ws_dev, 
         return rc;
     }
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
-    if (launch_scan(view_of(table), arena_bytes, ws, L, nullptr, 0, kDefaultTile, 0, stream) !=
-        hipSuccess)
+    if (launch_scan(view_of(table), arena_bytes, ws, L, nullptr, 0, kDefaultTile, 0, fit_need,
+                    stream) != hipSuccess)
         return DEFRAG_EHIP;
-    WsHeader h;
-    rc = read_header(&h, ws, L, stream);
+    rc = read_header(h, ws, L, stream);
     if (rc) return rc;
-    fill_stats(out_host, h, arena_bytes);
-    return h.bad_key == kNone ? DEFRAG_OK : DEFRAG_EINVAL;
+    if (out_host) fill_stats(out_host, *h, arena_bytes);
+    return h->bad_key == kNone ? DEFRAG_OK : DEFRAG_EINVAL;
+}
+
+}  // namespace
+
+extern "C" {
+
+int defrag_stats(const defrag_table *table, uint64_t arena_bytes, void *ws_dev, size_t ws_bytes,
+                 hipStream_t stream, defrag_stats_t *out_host) {
+    if (!out_host) return DEFRAG_EINVAL;
+    WsHeader h;
+    return stats_pass(table, arena_bytes, kNone, ws_dev, ws_bytes, stream, out_host, &h);
+}
+
+int defrag_first_fit(const defrag_table *table, uint64_t arena_bytes, uint64_t request_bytes,
+                     void *ws_dev, size_t ws_bytes, hipStream_t stream, uint64_t *offset_host,
+                     defrag_stats_t *stats_host) {
+    if (!offset_host) return DEFRAG_EINVAL;
+    *offset_host = kNone;
+    if (request_bytes == 0 || request_bytes > kNone - 31) {
+        arg_error(stats_host);
+        return DEFRAG_EINVAL;
+    }
+    const uint64_t need = (request_bytes + 31) / 32 * 32;
+    WsHeader h;
+    const int rc = stats_pass(table, arena_bytes, need, ws_dev, ws_bytes, stream, stats_host, &h);
+    if (rc) return rc;
+    *offset_host = h.fit_offset;
+    return h.fit_offset == kNone ? DEFRAG_ENOFIT : DEFRAG_OK;
 }
 
 }  // extern "C"
@@ -186,7 +217,7 @@ int plan_common(const defrag_table *table, uint64_t arena_bytes, uint64_t reques
         request ? launch_targeted(view_of(table), arena_bytes, request, ws, L, new_offset_dev,
                                   tu.tile_bytes, epoch, stream)
                 : launch_scan(view_of(table), arena_bytes, ws, L, new_offset_dev, kOutNew,
-                              tu.tile_bytes, epoch, stream);
+                              tu.tile_bytes, epoch, kNone, stream);
     if (e != hipSuccess) return DEFRAG_EHIP;
     WsHeader h;
     rc = read_header(&h, ws, L, stream);
@@ -334,7 +365,7 @@ const char *defrag_strerror(int code) {
         case DEFRAG_ENOPLAN: return "no matching plan for this workspace";
         case DEFRAG_EHIP: return "HIP runtime error";
         case DEFRAG_ETIMEOUT: return "mover wait timed out";
-        case DEFRAG_ENOFIT: return "no window of the arena can free the requested bytes";
+        case DEFRAG_ENOFIT: return "no hole holds the request (and, for a targeted plan, no window can free it)";
         default: return "unknown error";
     }
 }

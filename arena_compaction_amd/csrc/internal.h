@@ -46,7 +46,8 @@ struct alignas(256) WsHeader {
     uint64_t win_end;
     uint64_t win_hole;       // free bytes inside it (the hole it frees)
     uint64_t win_moved;      // live bytes inside it (the bytes that move)
-    uint64_t pad[13];
+    uint64_t fit_offset;     // first fit: lowest hole start holding the request
+    uint64_t pad[12];
 };
 static_assert(sizeof(WsHeader) == 256, "header size");
 
@@ -100,7 +101,8 @@ struct StatPart {
     uint64_t moved_bytes;
     uint64_t min_moved_dst;
     uint64_t min_size;
-    uint64_t pad[2];
+    uint64_t min_fit;   // lowest start of a hole below a live block holding fit_need
+    uint64_t pad;
 };
 
 // One mover tile: the destination bytes [t0, t1) -- a piece of one run of
@@ -215,9 +217,10 @@ inline LiveView live_view(const uint8_t *ws, const WsLayout &L) {
 // Scan passes and, with kOutNew, the mover's tiles (for at most
 // L.max_tiles tiles).  All asynchronous; the header then holds totals,
 // statistics and n_tiles (tiles are built only if n_tiles <= L.max_tiles).
+// fit_need: a hole size to first-fit (header fit_offset), kNone for none.
 hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws,
                        const WsLayout &L, uint64_t *new_offset, int outputs,
-                       uint32_t tile_bytes, uint64_t epoch, hipStream_t s);
+                       uint32_t tile_bytes, uint64_t epoch, uint64_t fit_need, hipStream_t s);
 // Targeted plan: a selection scan, the window search (header win_*), then
 // the plan scan with every live block outside the window held in place.
 // Nothing is planned (and new_offset is not written) when no window fits.

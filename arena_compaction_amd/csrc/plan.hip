@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
                                                             const ScanPart *prefix,
                                                             const WsHeader *hdr, uint64_t *new_offset,
                                                             LiveOut lo, StatPart *spart,
-                                                            int outputs) {
+                                                            int outputs, uint64_t fit_need) {
     __shared__ Agg sh[kScanThreads / 64];
     __shared__ uint64_t shr[kScanThreads / 64];
     if (plan_dead(hdr)) return;  // invalid table or nothing to plan: write nothing
@@ -297,6 +297,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
     const Agg ex = block_excl<kScanThreads>(a, total, sh);
     Agg run = combine(prefix[blockIdx.x].a, ex);
     uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, min_dst = kNone, min_size = kNone;
+    uint64_t min_fit = kNone;
 #pragma unroll
     for (uint32_t k = 0; k < kScanItems; ++k) {
         const uint64_t i = i0 + k;
@@ -320,6 +321,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
                 if (gap) {
                     gaps += 1;
                     max_gap = umax64(max_gap, gap);
+                    if (gap >= fit_need) min_fit = umin64(min_fit, run.mx);
                 }
                 if (o[k] != nw) {
                     moved += 1;
@@ -337,19 +339,24 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
     moved_bytes = block_reduce<kScanThreads>(moved_bytes, shr, OpAdd());
     min_dst = block_reduce<kScanThreads>(min_dst, shr, OpMin());
     min_size = block_reduce<kScanThreads>(min_size, shr, OpMin());
+    min_fit = block_reduce<kScanThreads>(min_fit, shr, OpMin());
     if (threadIdx.x == 0)
-        spart[blockIdx.x] = StatPart{max_gap, gaps, moved, moved_bytes, min_dst, min_size, {0, 0}};
+        spart[blockIdx.x] =
+            StatPart{max_gap, gaps, moved, moved_bytes, min_dst, min_size, min_fit, 0};
 }
 
 // Pass 4 (one workgroup): reduce the statistics, add the tail hole.
 __global__ __launch_bounds__(kSpineThreads) void k_scan_finish(const StatPart *spart, uint64_t nb,
                                                                uint64_t arena_bytes, WsHeader *hdr,
-                                                               int outputs, uint64_t epoch) {
+                                                               int outputs, uint64_t epoch,
+                                                               uint64_t fit_need) {
     __shared__ uint64_t sh[kSpineThreads / 64];
     if (plan_dead(hdr)) return;
     uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, min_dst = kNone, min_size = kNone;
+    uint64_t min_fit = kNone;
     for (uint64_t j = threadIdx.x; j < nb; j += kSpineThreads) {
         const StatPart q = spart[j];
+        min_fit = umin64(min_fit, q.min_fit);
         max_gap = umax64(max_gap, q.max_gap);
         gaps += q.gaps;
         moved += q.moved_blocks;
@@ -363,8 +370,12 @@ __global__ __launch_bounds__(kSpineThreads) void k_scan_finish(const StatPart *s
     moved_bytes = block_reduce<kSpineThreads>(moved_bytes, sh, OpAdd());
     min_dst = block_reduce<kSpineThreads>(min_dst, sh, OpMin());
     min_size = block_reduce<kSpineThreads>(min_size, sh, OpMin());
+    min_fit = block_reduce<kSpineThreads>(min_fit, sh, OpMin());
     if (threadIdx.x == 0) {
         const uint64_t tail = arena_bytes - hdr->max_live_end;
+        // holes below live blocks come first in address order; the tail last
+        if (min_fit == kNone && tail && tail >= fit_need) min_fit = hdr->max_live_end;
+        hdr->fit_offset = min_fit;
         hdr->largest_hole = umax64(max_gap, tail);
         hdr->hole_count = gaps + (tail ? 1 : 0);
         hdr->moved_blocks = moved;
@@ -717,7 +728,7 @@ namespace {
 // window in the header, or null.
 void queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsLayout &L,
                 uint64_t *new_offset, int outputs, const uint64_t *win, uint32_t tile_bytes,
-                uint64_t epoch, hipStream_t s) {
+                uint64_t epoch, uint64_t fit_need, hipStream_t s) {
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.header);
     ScanPart *part = reinterpret_cast<ScanPart *>(ws + L.part);
     ScanPart *prefix = reinterpret_cast<ScanPart *>(ws + L.prefix);
@@ -737,10 +748,10 @@ void queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsL
                        win ? 0 : 1);
     if (nb) {
         hipLaunchKernelGGL(k_scan_down, dim3((uint32_t)nb), dim3(kScanThreads), 0, s, t, win,
-                           prefix, hdr, new_offset, lo, spart, outputs);
+                           prefix, hdr, new_offset, lo, spart, outputs, fit_need);
     }
     hipLaunchKernelGGL(k_scan_finish, dim3(1), dim3(kSpineThreads), 0, s, spart, nb, arena_bytes,
-                       hdr, outputs, epoch);
+                       hdr, outputs, epoch, fit_need);
     if (outputs & kOutNew) {
         const LiveView lv = live_view(ws, L);
         uint64_t *tpart = reinterpret_cast<uint64_t *>(ws + L.tpart);
@@ -774,8 +785,9 @@ void queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsL
 
 hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsLayout &L,
                        uint64_t *new_offset, int outputs, uint32_t tile_bytes, uint64_t epoch,
-                       hipStream_t s) {
-    queue_scan(t, arena_bytes, ws, L, new_offset, outputs, nullptr, tile_bytes, epoch, s);
+                       uint64_t fit_need, hipStream_t s) {
+    queue_scan(t, arena_bytes, ws, L, new_offset, outputs, nullptr, tile_bytes, epoch, fit_need,
+               s);
     return hipGetLastError();
 }
 
@@ -788,13 +800,14 @@ hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t re
     const uint64_t *z = reinterpret_cast<const uint64_t *>(ws + L.live_z);
     const uint32_t *pc = reinterpret_cast<const uint32_t *>(ws + L.live_pc);
     SelPart *sp = reinterpret_cast<SelPart *>(ws + L.selpart);
-    queue_scan(t, arena_bytes, ws, L, nullptr, kOutSelect, nullptr, tile_bytes, epoch, s);
+    queue_scan(t, arena_bytes, ws, L, nullptr, kOutSelect, nullptr, tile_bytes, epoch, kNone, s);
     // candidates: every last hole l in [0, m], m <= n
     hipLaunchKernelGGL(k_select, dim3((uint32_t)L.n_sel_blocks), dim3(kSelThreads), 0, s, src, z,
                        pc, hdr, arena_bytes, request, sp);
     hipLaunchKernelGGL(k_select_finish, dim3(1), dim3(kSpineThreads), 0, s, sp, L.n_sel_blocks,
                        src, size, z, arena_bytes, hdr);
-    queue_scan(t, arena_bytes, ws, L, new_offset, kOutNew, &hdr->win_begin, tile_bytes, epoch, s);
+    queue_scan(t, arena_bytes, ws, L, new_offset, kOutNew, &hdr->win_begin, tile_bytes, epoch,
+               kNone, s);
     return hipGetLastError();
 }
 

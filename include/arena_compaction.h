@@ -71,7 +71,7 @@ extern "C" {
 #define DEFRAG_ENOPLAN (-3)    /* move/remap/commit without a matching plan     */
 #define DEFRAG_EHIP (-4)       /* a HIP runtime call failed                    */
 #define DEFRAG_ETIMEOUT (-5)   /* mover watchdog expired (a wait never ended)  */
-#define DEFRAG_ENOFIT (-6)     /* targeted plan: no window frees the request   */
+#define DEFRAG_ENOFIT (-6)     /* no hole holds / no window frees the request  */
 
 /* Why a table was rejected: the first failing entry, and within it the first
  * failing check in the order zero size, misaligned, live flag, pinned flag,
@@ -182,6 +182,23 @@ size_t defrag_workspace_bytes(uint64_t n, uint64_t max_pinned, uint64_t arena_by
  * free/largest - 1 and 1 - largest/free, both 0 when free is 0. */
 int defrag_stats(const defrag_table *table, uint64_t arena_bytes, void *ws_dev,
                  size_t ws_bytes, hipStream_t stream, defrag_stats_t *out_host);
+
+/* First fit (CANN page, section 2.2 memory pool: a request is rounded up to
+ * a multiple of 32 bytes and placed at the first free block that holds it;
+ * adjacent free blocks are merged).  On a table the merged free blocks are
+ * its holes in address order, so *offset_host receives the start of the
+ * lowest hole of at least the rounded size.  This is the allocation the
+ * 910C page's 4.2 GB buffer failed to get: ask before a compaction, and
+ * again on the table defrag_commit writes after it.  Returns DEFRAG_OK, or
+ * DEFRAG_ENOFIT with *offset_host = UINT64_MAX when no hole holds it;
+ * DEFRAG_EINVAL for an invalid table (stats_host says why), a zero request
+ * or one that rounds past 2^64.  stats_host (may be NULL) receives the
+ * table's statistics, as defrag_stats.  The table is not changed: the
+ * caller records the allocation.  Synchronises the stream. */
+int defrag_first_fit(const defrag_table *table, uint64_t arena_bytes,
+                     uint64_t request_bytes, void *ws_dev, size_t ws_bytes,
+                     hipStream_t stream, uint64_t *offset_host,
+                     defrag_stats_t *stats_host);
 
 /* Plan a compaction (910C: scan holes low to high, give every live block its
  * downward shift).  Validates, writes new_offset_dev[n] (may be NULL), fills

@@ -20,7 +20,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     fns = _declared_functions()
-    for f in ("defrag_stats", "defrag_plan", "defrag_plan_targeted", "defrag_move", "defrag_remap",
+    for f in ("defrag_stats", "defrag_first_fit", "defrag_plan", "defrag_plan_targeted",
+              "defrag_move", "defrag_remap",
               "defrag_workspace_bytes", "defrag_strerror", "defrag_commit",
               "defrag_move_status"):
         assert f in fns, f
@@ -93,6 +94,15 @@ def test_host_side_argument_errors_need_no_gpu():
     assert L.defrag_plan_targeted(ctypes.byref(t), 4096, 64, None, ctypes.c_void_p(0x1000),
                                   1 << 20, None, None, None) == ac.DEFRAG_EINVAL
     assert ac.defrag_strerror(ac.DEFRAG_ENOFIT) not in ("ok", "unknown error")
+    # first fit: missing output, zero request and a request that rounds past 2^64
+    off_out = ctypes.c_uint64(7)
+    assert L.defrag_first_fit(ctypes.byref(t), 4096, 64, ctypes.c_void_p(0x1000), 1 << 20, None,
+                              None, None) == ac.DEFRAG_EINVAL
+    for bad_request in (0, (1 << 64) - 31):
+        assert L.defrag_first_fit(ctypes.byref(t), 4096, bad_request, ctypes.c_void_p(0x1000),
+                                  1 << 20, None, ctypes.byref(off_out),
+                                  ctypes.byref(st)) == ac.DEFRAG_EINVAL
+        assert off_out.value == (1 << 64) - 1 and st.invalid_reason == 6
     # bad tile size
     tu = ac.defrag_tuning(100, 0, 0, 0)
     assert L.defrag_plan(ctypes.byref(t), 4096, ctypes.byref(tu), ctypes.c_void_p(0x1000),
