@@ -77,6 +77,8 @@ def _bind(path: str):
     L.oracle_target_window.restype = ctypes.c_int
     L.oracle_first_fit.argtypes = [P, P, P, U, U, U, P]
     L.oracle_first_fit.restype = ctypes.c_int
+    D = ctypes.c_double
+    L.oracle_monitor.argtypes = [U, U, U, D, D, D, U, D, P]
     return L
 
 
@@ -217,3 +219,23 @@ def first_fit(off, size, live, arena_bytes, request) -> int:
     if rc != 0:
         raise ValueError("request must be at least one byte")
     return out.value
+
+
+class _MonitorOut(ctypes.Structure):
+    _fields_ = [("level", ctypes.c_int32), ("action", ctypes.c_int32),
+                ("usage_ratio", ctypes.c_double),
+                ("frag_free_over_largest_minus_1", ctypes.c_double),
+                ("seconds_to_full", ctypes.c_double)]
+
+
+Monitor = collections.namedtuple("Monitor", [f[0] for f in _MonitorOut._fields_])
+LEVELS = {0: "OK", 1: "WARNING", 2: "CRITICAL"}
+ACTIONS = {0: "none", 1: "targeted", 2: "full", 3: "no_room"}
+
+
+def monitor(arena_bytes, live_bytes, largest_hole, warning_ratio=0.85, critical_ratio=0.95,
+            frag_threshold=0.0, next_request=0, growth_bytes_per_s=0.0) -> Monitor:
+    o = _MonitorOut()
+    lib().oracle_monitor(arena_bytes, live_bytes, largest_hole, warning_ratio, critical_ratio,
+                         frag_threshold, next_request, growth_bytes_per_s, ctypes.byref(o))
+    return Monitor(*[getattr(o, f[0]) for f in _MonitorOut._fields_])

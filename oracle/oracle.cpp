@@ -298,4 +298,40 @@ int oracle_first_fit(const uint64_t *offset, const uint64_t *size,
     return ORACLE_OK;
 }
 
+// [CANN] 5.3 MemoryMonitor.check / predict_oom_time, and the 910C page's
+// rule of reading the largest free block next to the free total.
+void oracle_monitor(uint64_t arena_bytes, uint64_t live_bytes, uint64_t largest_hole,
+                    double warning_ratio, double critical_ratio, double frag_threshold,
+                    uint64_t next_request, double growth_bytes_per_s,
+                    oracle_monitor_out *out) {
+    std::memset(out, 0, sizeof(*out));
+    const uint64_t free_bytes = arena_bytes - live_bytes;
+    const double usage = arena_bytes ? (double)live_bytes / (double)arena_bytes : 0.0;
+    out->usage_ratio = usage;
+    if (usage > critical_ratio)
+        out->level = ORACLE_LEVEL_CRITICAL;
+    else if (usage > warning_ratio)
+        out->level = ORACLE_LEVEL_WARNING;
+    else
+        out->level = ORACLE_LEVEL_OK;
+    out->frag_free_over_largest_minus_1 =
+        free_bytes ? (double)free_bytes / (double)largest_hole - 1.0 : 0.0;
+    out->seconds_to_full = growth_bytes_per_s > 0.0
+                               ? (double)free_bytes / growth_bytes_per_s
+                               : __builtin_inf();
+    out->action = ORACLE_ACTION_NONE;
+    if (next_request > 0) {
+        // a request past 2^64 - 32 rounds to something no arena holds
+        const bool huge = next_request > UINT64_MAX - 31;
+        const uint64_t need = huge ? UINT64_MAX : (next_request + 31) / 32 * 32;
+        if (huge || need > largest_hole) {
+            out->action = (!huge && need <= free_bytes) ? ORACLE_ACTION_TARGETED
+                                                        : ORACLE_ACTION_NO_ROOM;
+            return;
+        }
+    }
+    if (frag_threshold > 0.0 && out->frag_free_over_largest_minus_1 > frag_threshold)
+        out->action = ORACLE_ACTION_FULL;
+}
+
 }  // extern "C"

@@ -146,6 +146,38 @@ int oracle_first_fit(const uint64_t *offset, const uint64_t *size,
                      const uint8_t *live, uint64_t n, uint64_t arena_bytes,
                      uint64_t request, uint64_t *offset_out);
 
+/* Layout monitor.  [CANN] 5.3 MemoryMonitor: usage = used / total; above
+ * the critical ratio the level is CRITICAL, else above the warning ratio
+ * WARNING, else OK; the time to exhaustion is the remaining bytes over the
+ * growth rate, infinite when the rate is not positive.  [910C] monitoring
+ * and the closing advice: when an allocation fails while enough is free,
+ * look at the largest contiguous free block -- the layout, not the
+ * capacity, is at fault; compaction is a costly stop-loss step.  Action:
+ * with a pending request (rounded up to 32 bytes, [CANN] 2.2) that the
+ * largest hole cannot hold, compact (targeted) if the free total could
+ * hold it, else report that no compaction can help; otherwise compact
+ * (full) when free/largest - 1 exceeds a threshold (> 0), else nothing. */
+#define ORACLE_LEVEL_OK 0
+#define ORACLE_LEVEL_WARNING 1
+#define ORACLE_LEVEL_CRITICAL 2
+#define ORACLE_ACTION_NONE 0
+#define ORACLE_ACTION_TARGETED 1
+#define ORACLE_ACTION_FULL 2
+#define ORACLE_ACTION_NO_ROOM 3
+
+typedef struct oracle_monitor_out {
+    int32_t level;
+    int32_t action;
+    double usage_ratio;
+    double frag_free_over_largest_minus_1;
+    double seconds_to_full;
+} oracle_monitor_out;
+
+void oracle_monitor(uint64_t arena_bytes, uint64_t live_bytes, uint64_t largest_hole,
+                    double warning_ratio, double critical_ratio, double frag_threshold,
+                    uint64_t next_request, double growth_bytes_per_s,
+                    oracle_monitor_out *out);
+
 #ifdef __cplusplus
 }
 #endif

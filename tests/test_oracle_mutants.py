@@ -15,6 +15,7 @@ import workloads as W
 import test_oracle as T
 import test_oracle_targeted as TT
 import test_oracle_first_fit as FF
+import test_oracle_monitor as MO
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.cpp")
 
@@ -74,6 +75,19 @@ MUTANTS = [
     ("first_fit_hole_end", "            *offset_out = cursor;\n            return ORACLE_OK;",
      "            *offset_out = offset[i] - need;\n            return ORACLE_OK;"),
     ("first_fit_tail_ignored", "    if (arena_bytes - cursor >= need) *offset_out = cursor;", ""),
+    ("monitor_critical_inclusive", "    if (usage > critical_ratio)", "    if (usage >= critical_ratio)"),
+    ("monitor_warning_inclusive", "    else if (usage > warning_ratio)", "    else if (usage >= warning_ratio)"),
+    ("monitor_levels_swapped", "        out->level = ORACLE_LEVEL_CRITICAL;\n    else if (usage > warning_ratio)\n        out->level = ORACLE_LEVEL_WARNING;",
+     "        out->level = ORACLE_LEVEL_WARNING;\n    else if (usage > warning_ratio)\n        out->level = ORACLE_LEVEL_CRITICAL;"),
+    ("monitor_no_rounding", "        const uint64_t need = huge ? UINT64_MAX : (next_request + 31) / 32 * 32;",
+     "        const uint64_t need = huge ? UINT64_MAX : next_request;"),
+    ("monitor_capacity_inverted", "            out->action = (!huge && need <= free_bytes) ? ORACLE_ACTION_TARGETED",
+     "            out->action = (!huge && need > free_bytes) ? ORACLE_ACTION_TARGETED"),
+    ("monitor_time_from_used", "                               ? (double)free_bytes / growth_bytes_per_s",
+     "                               ? (double)live_bytes / growth_bytes_per_s"),
+    ("monitor_threshold_inclusive", "out->frag_free_over_largest_minus_1 > frag_threshold)",
+     "out->frag_free_over_largest_minus_1 >= frag_threshold)"),
+    ("monitor_request_ignored", "    if (next_request > 0) {", "    if (next_request > UINT64_MAX) {"),
     ("window_tail_ignored", "    if (arena_bytes > cursor) holes.push_back(Hole{cursor, arena_bytes - cursor, 0, false});",
      ""),
 ]
@@ -111,6 +125,8 @@ def _battery():
             FF.check_against_bruteforce(heap, rng)
             FF.check_proof(heap, rng)
         FF.check_golden()
+        for case in MO.golden_cases():
+            MO.check_case(case, oracle.monitor)
     except AssertionError:
         return False
     return True
