@@ -73,6 +73,24 @@ class defrag_plan_t(ctypes.Structure):
                 ("tuning", defrag_tuning), ("stats", defrag_stats_t)]
 
 
+class defrag_monitor_cfg(ctypes.Structure):
+    _fields_ = [("warning_ratio", ctypes.c_double), ("critical_ratio", ctypes.c_double),
+                ("frag_threshold", ctypes.c_double), ("next_request", ctypes.c_uint64),
+                ("growth_bytes_per_s", ctypes.c_double)]
+
+
+class defrag_monitor_report(ctypes.Structure):
+    _fields_ = [("level", ctypes.c_int32), ("action", ctypes.c_int32),
+                ("usage_ratio", ctypes.c_double),
+                ("frag_free_over_largest_minus_1", ctypes.c_double),
+                ("frag_one_minus_largest_over_free", ctypes.c_double),
+                ("seconds_to_full", ctypes.c_double)]
+
+
+LEVELS = {0: "OK", 1: "WARNING", 2: "CRITICAL"}
+ACTIONS = {0: "none", 1: "targeted", 2: "full", 3: "no_room"}
+
+
 class DefragError(RuntimeError):
     def __init__(self, code: int, what: str, stats: Optional[defrag_stats_t] = None):
         self.code = code
@@ -109,10 +127,12 @@ def _load() -> ctypes.CDLL:
     L.defrag_move_status.argtypes = [ctypes.POINTER(defrag_plan_t), P, P]
     L.defrag_remap.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, U, P, P]
     L.defrag_commit.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, P, P, P]
+    L.defrag_monitor.argtypes = [ctypes.POINTER(defrag_stats_t), ctypes.POINTER(defrag_monitor_cfg),
+                                 ctypes.POINTER(defrag_monitor_report)]
     L.defrag_strerror.argtypes = [ctypes.c_int]
     L.defrag_strerror.restype = ctypes.c_char_p
     for f in ("defrag_stats", "defrag_first_fit", "defrag_plan", "defrag_plan_targeted",
-              "defrag_move",
+              "defrag_move", "defrag_monitor",
               "defrag_move_status",
               "defrag_remap", "defrag_commit"):
         getattr(L, f).restype = ctypes.c_int
@@ -124,7 +144,8 @@ lib = _load()
 EXPORTS = ("defrag_workspace_bytes", "defrag_stats", "defrag_first_fit", "defrag_plan",
            "defrag_plan_targeted",
            "defrag_move",
-           "defrag_move_status", "defrag_remap", "defrag_commit", "defrag_strerror")
+           "defrag_move_status", "defrag_remap", "defrag_commit", "defrag_monitor",
+           "defrag_strerror")
 
 
 def strerror(code: int) -> str:
@@ -269,6 +290,18 @@ def defrag_commit(plan: defrag_plan_t, ws: torch.Tensor, offset_out=None, size_o
                            _ptr(size_out), _ptr(live_out), _ptr(pinned_out), _stream(stream))
     if rc != DEFRAG_OK:
         raise DefragError(rc, "defrag_commit")
+
+
+def defrag_monitor(stats: defrag_stats_t, warning_ratio: float = 0.85,
+                   critical_ratio: float = 0.95, frag_threshold: float = 0.0,
+                   next_request: int = 0, growth_bytes_per_s: float = 0.0) -> defrag_monitor_report:
+    cfg = defrag_monitor_cfg(warning_ratio, critical_ratio, frag_threshold, next_request,
+                             growth_bytes_per_s)
+    out = defrag_monitor_report()
+    rc = lib.defrag_monitor(ctypes.byref(stats), ctypes.byref(cfg), ctypes.byref(out))
+    if rc != DEFRAG_OK:
+        raise DefragError(rc, "defrag_monitor")
+    return out
 
 
 def defrag_strerror(code: int) -> str:

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libarena_compaction.so")
-SOURCES = ["api.cpp", "plan.hip", "move.hip", "remap.hip"]
+SOURCES = ["api.cpp", "monitor.cpp", "plan.hip", "move.hip", "remap.hip"]
 ARCH = os.environ.get("ARENA_COMPACTION_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

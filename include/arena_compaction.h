@@ -262,6 +262,53 @@ int defrag_commit(const defrag_plan_t *plan_host, const void *ws_dev,
                   uint64_t *size_out_dev, uint8_t *live_out_dev,
                   uint8_t *pinned_out_dev, hipStream_t stream);
 
+/* Layout monitor: host arithmetic on a defrag_stats result, no HIP call.
+ * CANN page, section 5.3 (MemoryMonitor): usage = live / arena is rated OK,
+ * WARNING above warning_ratio, CRITICAL above critical_ratio (defaults 0.85
+ * and 0.95); seconds_to_full = free bytes / growth rate, +infinity for a
+ * rate that is not positive.  910C page (monitoring section and closing
+ * advice: read the largest free block next to the free total; compaction is
+ * a stop-loss step): the action is
+ *   TARGETED  a pending request, rounded up to 32 bytes as the CANN pool
+ *             does (section 2.2), exceeds the largest hole but not the free
+ *             total -- the layout is at fault (see defrag_plan_targeted,
+ *             which may still find no window when pinned blocks split the
+ *             free space);
+ *   NO_ROOM   it exceeds the free total: compaction cannot help;
+ *   FULL      otherwise, free/largest - 1 exceeds frag_threshold (> 0);
+ *   NONE      otherwise.
+ * Call it on a schedule (the 910C page scanned the layout every 100 steps).
+ * cfg may be NULL (defaults, no request, no threshold).  Returns
+ * DEFRAG_EINVAL for NULL stats/out, statistics of an invalid table or
+ * inconsistent figures, or a NaN in cfg. */
+#define DEFRAG_LEVEL_OK 0
+#define DEFRAG_LEVEL_WARNING 1
+#define DEFRAG_LEVEL_CRITICAL 2
+#define DEFRAG_ACTION_NONE 0
+#define DEFRAG_ACTION_TARGETED 1
+#define DEFRAG_ACTION_FULL 2
+#define DEFRAG_ACTION_NO_ROOM 3
+
+typedef struct defrag_monitor_cfg {
+    double warning_ratio;      /* usage above it: WARNING                     */
+    double critical_ratio;     /* usage above it: CRITICAL                    */
+    double frag_threshold;     /* free/largest - 1 above it: FULL; <= 0 off   */
+    uint64_t next_request;     /* bytes the next allocation needs; 0: none    */
+    double growth_bytes_per_s; /* live-byte growth rate                       */
+} defrag_monitor_cfg;
+
+typedef struct defrag_monitor_report {
+    int32_t level;   /* DEFRAG_LEVEL_*  */
+    int32_t action;  /* DEFRAG_ACTION_* */
+    double usage_ratio;
+    double frag_free_over_largest_minus_1;
+    double frag_one_minus_largest_over_free;
+    double seconds_to_full;
+} defrag_monitor_report;
+
+int defrag_monitor(const defrag_stats_t *stats, const defrag_monitor_cfg *cfg,
+                   defrag_monitor_report *out);
+
 /* Short text for a return code. */
 const char *defrag_strerror(int code);
 
