@@ -268,6 +268,12 @@ def main() -> int:
                     tt[key].append(ev[a].elapsed_time(ev[b]))
         tmean = {k: float(np.mean(v)) for k, v in tt.items()}
         tmoved = int(tp.stats.moved_bytes)
+        # the allocation the page's request failed to get, before and after,
+        # and what the layout monitor says about each state
+        ff_before, st_before = ac.defrag_first_fit(off, size, live, S, request, ws, pinned=pinned)
+        ff_after, _ = ac.defrag_first_fit(c_off, c_size, c_live, S, request, ws, pinned=c_pin)
+        mon_before = ac.defrag_monitor(st_before, next_request=request)
+        mon_after = ac.defrag_monitor(tpost, next_request=request)
         targeted = {
             "request_bytes": request,
             "window": [int(tp.window_begin), int(tp.window_end)],
@@ -278,6 +284,12 @@ def main() -> int:
             "step_vs_full": round(tmean["step"] / float(np.mean(times["step"])), 4),
             "move_GBps": round(2 * tmoved / (tmean["move"] * 1e-3) / 1e9, 2) if tmoved else None,
             "after_largest_hole": int(tpost.largest_hole),
+            "first_fit_before": ff_before,
+            "first_fit_after": ff_after,
+            "monitor_before": {"level": ac.LEVELS[mon_before.level],
+                               "action": ac.ACTIONS[mon_before.action]},
+            "monitor_after": {"level": ac.LEVELS[mon_after.level],
+                              "action": ac.ACTIONS[mon_after.action]},
         }
         print(f"# targeted: request {request} moved {tmoved} step {tmean['step']:.3f} ms",
               file=sys.stderr, flush=True)
