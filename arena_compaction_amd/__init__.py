@@ -66,7 +66,7 @@ class defrag_plan_t(ctypes.Structure):
                 ("live_blocks", ctypes.c_uint64), ("pinned_blocks", ctypes.c_uint64),
                 ("move_begin", ctypes.c_uint64), ("live_bytes", ctypes.c_uint64),
                 ("n_tiles", ctypes.c_uint64), ("max_tiles", ctypes.c_uint64),
-                ("max_blocks_per_tile", ctypes.c_uint64),
+                ("max_blocks_per_tile", ctypes.c_uint64), ("whole_tiles", ctypes.c_uint64),
                 ("request_bytes", ctypes.c_uint64), ("window_begin", ctypes.c_uint64),
                 ("window_end", ctypes.c_uint64), ("window_hole", ctypes.c_uint64),
                 ("state", ctypes.c_int32), ("device", ctypes.c_int32),

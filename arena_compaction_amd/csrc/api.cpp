@@ -238,7 +238,6 @@ int plan_common(const defrag_table *table, uint64_t arena_bytes, uint64_t reques
     plan->move_begin = h.move_begin;
     plan->live_bytes = h.live_bytes;
     plan->device = dev;
-    plan->tuning = tu;
     plan->n_tiles = h.n_tiles;
     plan->max_tiles = L.max_tiles;
     // blocks meeting one tile: at most T / (smallest live size) + 2
@@ -246,6 +245,9 @@ int plan_common(const defrag_table *table, uint64_t arena_bytes, uint64_t reques
     if (h.min_live_size != kNone && h.min_live_size) mb = T / h.min_live_size + 2;
     if (mb > T / 32 + 2) mb = T / 32 + 2;
     plan->max_blocks_per_tile = mb;
+    plan->whole_tiles = h.whole_tiles;
+    if (!tuning) tu.wg_per_cu = 2 * h.whole_tiles >= h.n_tiles ? kWgPerCuWhole : kDefaultWgPerCu;
+    plan->tuning = tu;
     if (request) {
         plan->request_bytes = request;
         plan->window_begin = h.win_begin;

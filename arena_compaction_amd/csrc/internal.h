@@ -16,7 +16,13 @@ constexpr uint32_t kSpineThreads = 256;         // single-workgroup passes (no s
 constexpr uint32_t kMoveThreads = 256;          // mover workgroup
 constexpr uint32_t kMoveRowBytes = kMoveThreads * 16;  // one 16-B vector per lane
 constexpr uint32_t kDefaultTile = 65536;
-constexpr uint32_t kDefaultWgPerCu = 2;     // measured best on the 80 GiB workload
+// Mover workgroups per compute unit when the caller gives no tuning: one
+// when at least half the tiles are whole single-block windows (they run the
+// straight-line path, and one narrow window of tiles in flight suits HBM
+// best), two otherwise (the general path needs a second workgroup to cover
+// its latencies).  Measured on the 80 GiB and the small-block workloads.
+constexpr uint32_t kWgPerCuWhole = 1;
+constexpr uint32_t kDefaultWgPerCu = 2;
 constexpr uint32_t kDefaultNontemporal = 1; // streaming loads and stores
 constexpr uint32_t kMinTile = 256;
 constexpr uint32_t kMaxTile = 131072;
@@ -47,7 +53,8 @@ struct alignas(256) WsHeader {
     uint64_t win_hole;       // free bytes inside it (the hole it frees)
     uint64_t win_moved;      // live bytes inside it (the bytes that move)
     uint64_t fit_offset;     // first fit: lowest hole start holding the request
-    uint64_t pad[12];
+    uint64_t whole_tiles;    // tiles that are one whole window of one block
+    uint64_t pad[11];
 };
 static_assert(sizeof(WsHeader) == 256, "header size");
 

@@ -34,6 +34,15 @@
 // (pinned blocks, and the packed prefix of each segment) are in no tile and
 // are never touched; nor is any byte no block lands on.
 //
+// Most tiles are one whole T-byte window of a single block.  Those take a
+// straight-line path: every lane loads and stores at fixed offsets from two
+// uniform bases, with no per-vector predicate, so all sixteen loads and all
+// sixteen stores of a lane stay in flight together (behind a per-vector
+// branch the compiler waits for each store before the next).  Partial and
+// multi-block tiles take the general path.  The dependency flags are read
+// once speculatively, right behind the tile's data loads: a dependency far
+// below is long done, and the tile then stores without another round trip.
+//
 // Vectors are 16 bytes: offsets and sizes are multiples of 32, so a vector
 // never straddles two blocks and both of its addresses are 16-byte aligned.
 // Per tile the kernel reads 16 B per live-block descriptor it needs (in LDS
@@ -106,6 +115,8 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
         const uint32_t rel1 = (uint32_t)(t1 - tb);
         const uint32_t nblk = last - first + 1u;
         bool ok = nblk <= a.max_blocks;
+        const bool whole = (uint64_t)VPT * kMoveRowBytes == a.tile_bytes && nblk == 1u &&
+                           rel0 == 0u && rel1 == a.tile_bytes;
 
         if (nblk > 1u && ok) {
             for (uint32_t k = tid; k < nblk; k += kMoveThreads) {
@@ -117,22 +128,34 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
         }
 
         v4u v[VPT];
+        if (whole) {
+            const uint8_t *src = a.arena + tb + shift0 + tid * 16u;
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const uint32_t r = ((uint32_t)j * kMoveThreads + tid) * 16u;
-            if (ok && r >= rel0 && r < rel1) {
-                uint64_t sh = shift0;
-                if (nblk > 1u) {
-                    uint32_t lo = 0, n = nblk;  // largest k with s_rel[k] <= r
-                    while (n > 1u) {
-                        const uint32_t half = n >> 1;
-                        lo = (s_rel[lo + half] <= r) ? lo + half : lo;
-                        n -= half;
+            for (int j = 0; j < VPT; ++j) v[j] = load16<NT>(src + (size_t)j * kMoveRowBytes);
+        } else {
+#pragma unroll
+            for (int j = 0; j < VPT; ++j) {
+                const uint32_t r = ((uint32_t)j * kMoveThreads + tid) * 16u;
+                if (ok && r >= rel0 && r < rel1) {
+                    uint64_t sh = shift0;
+                    if (nblk > 1u) {
+                        uint32_t lo = 0, n = nblk;  // largest k with s_rel[k] <= r
+                        while (n > 1u) {
+                            const uint32_t half = n >> 1;
+                            lo = (s_rel[lo + half] <= r) ? lo + half : lo;
+                            n -= half;
+                        }
+                        sh = s_shift[lo];
                     }
-                    sh = s_shift[lo];
+                    v[j] = load16<NT>(a.arena + tb + r + sh);
                 }
-                v[j] = load16<NT>(a.arena + tb + r + sh);
             }
+        }
+        // first look at the dependency flags, returned with the data loads
+        uint32_t f_lo = 0u, f_hi = 0u;
+        if (tid == 0 && dep_lo <= dep_hi) {
+            f_lo = __hip_atomic_load(&a.flags[dep_lo], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            f_hi = __hip_atomic_load(&a.flags[dep_hi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         // every load of this tile has returned before its flag is published
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -142,6 +165,7 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
             if (!ok) atomicOr(&a.hdr->status, kStatusTimeout);
             __hip_atomic_store(&a.flags[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             for (uint32_t u = dep_lo; u <= dep_hi && !skip; ++u) {
+                if ((u == dep_lo && f_lo) || (u == dep_hi && f_hi)) continue;  // seen done
                 uint64_t polls = 0;
                 while (__hip_atomic_load(&a.flags[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
                     if (++polls > a.spin_limit) {
@@ -156,10 +180,16 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
         }
         __syncthreads();
         if (!s_skip) {
+            if (whole) {
+                uint8_t *dst = a.arena + tb + tid * 16u;
 #pragma unroll
-            for (int j = 0; j < VPT; ++j) {
-                const uint32_t r = ((uint32_t)j * kMoveThreads + tid) * 16u;
-                if (r >= rel0 && r < rel1) store16<NT>(a.arena + tb + r, v[j]);
+                for (int j = 0; j < VPT; ++j) store16<NT>(dst + (size_t)j * kMoveRowBytes, v[j]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < VPT; ++j) {
+                    const uint32_t r = ((uint32_t)j * kMoveThreads + tid) * 16u;
+                    if (r >= rel0 && r < rel1) store16<NT>(a.arena + tb + r, v[j]);
+                }
             }
         }
         // Claim the next tile only now: each workgroup holds one ticket at a

@@ -387,6 +387,7 @@ __global__ __launch_bounds__(kSpineThreads) void k_scan_finish(const StatPart *s
             hdr->epoch = epoch;
             hdr->ticket = 0;
             hdr->status = 0;
+            hdr->whole_tiles = 0;
         }
     }
 }
@@ -520,7 +521,7 @@ __device__ inline uint64_t tile_of(const LiveView &lv, const uint32_t *tile_base
 // short range ending at or before this one.
 __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile_start,
                                                const uint32_t *tile_first,
-                                               const uint32_t *tile_base, const WsHeader *hdr,
+                                               const uint32_t *tile_base, WsHeader *hdr,
                                                uint64_t max_tiles, uint64_t T, TileRec *tiles,
                                                uint32_t *flags) {
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -574,6 +575,13 @@ __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile
     tiles[t] = TileRec{t0, t1, lv.src[first] - lv.dst[first], (uint32_t)first, (uint32_t)last,
                        dep_lo, dep_hi, 0};
     flags[t] = 0u;
+    // count the whole single-block windows (one atomic per wave)
+    const bool whole = first == last && (t0 & (T - 1)) == 0 && t1 - t0 == T;
+    const uint64_t active = __ballot(1);
+    const uint64_t wmask = __ballot(whole);
+    if (wmask && __lane_id() == (uint32_t)__builtin_ctzll(active))
+        atomicAdd(reinterpret_cast<unsigned long long *>(&hdr->whole_tiles),
+                  (unsigned long long)__popcll(wmask));
 }
 
 __global__ void k_commit(LiveView lv, uint64_t m, uint64_t *off_out, uint64_t *size_out,

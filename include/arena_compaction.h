@@ -120,10 +120,12 @@ typedef struct defrag_stats_t {
     int32_t reserved;
 } defrag_stats_t;
 
-/* Optional knobs.  Passing NULL takes the defaults (65536-byte tiles, two
- * mover workgroups per compute unit, streaming loads and stores); in a
- * struct passed explicitly, a zero tile size or spin limit takes its default
- * and the other fields are taken as given. */
+/* Optional knobs.  Passing NULL takes the defaults: 65536-byte tiles,
+ * streaming loads and stores, and one mover workgroup per compute unit when
+ * at least half the tiles are whole single-block windows, else two (the
+ * plan decides, and records its choice in plan_host->tuning).  In a struct
+ * passed explicitly, a zero tile size or spin limit takes its default and
+ * the other fields are taken as given. */
 typedef struct defrag_tuning {
     uint32_t tile_bytes;      /* mover tile: power of two in [256, 131072].
                                  Fixed at plan time.                          */
@@ -153,6 +155,7 @@ typedef struct defrag_plan_t {
     uint64_t n_tiles;
     uint64_t max_tiles;    /* tile capacity of the workspace                   */
     uint64_t max_blocks_per_tile;
+    uint64_t whole_tiles;  /* tiles that are one whole window of one block     */
     /* targeted plans (all 0 for a full plan): the request and the window
      * [window_begin, window_end) whose live blocks move; window_hole is the
      * hole it frees, at [window_end - window_hole, window_end) */
