@@ -133,7 +133,7 @@ constexpr size_t kPerTileBytes =
 
 struct WsLayout {
     // fixed part (depends on n only)
-    size_t header, part, prefix, spart, tpart, tprefix, live_dst, live_src, live_size,
+    size_t header, part, prefix, spart, tpart, twhole, tprefix, live_dst, live_src, live_size,
         live_pin, tile_base, live_z, live_pc, selpart, fixed;
     // tile part (depends on the tile capacity)
     size_t tile_start, tile_first, tiles, flags, total;
@@ -152,6 +152,7 @@ inline WsLayout ws_fixed(uint64_t n) {
     L.prefix = at;    at += align256(nb * sizeof(ScanPart));
     L.spart = at;     at += align256(nb * sizeof(StatPart));
     L.tpart = at;     at += align256(nb * sizeof(uint64_t));
+    L.twhole = at;    at += align256(nb * sizeof(uint64_t));
     L.tprefix = at;   at += align256(nb * sizeof(uint64_t));
     L.live_dst = at;  at += align256((n + 1) * sizeof(uint64_t));
     L.live_src = at;  at += align256((n + 1) * sizeof(uint64_t));

@@ -387,7 +387,6 @@ __global__ __launch_bounds__(kSpineThreads) void k_scan_finish(const StatPart *s
             hdr->epoch = epoch;
             hdr->ticket = 0;
             hdr->status = 0;
-            hdr->whole_tiles = 0;
         }
     }
 }
@@ -409,27 +408,50 @@ __device__ inline uint64_t tiles_in_block(const LiveView &lv, uint64_t k, uint64
     return mult + ((start && (a & (T - 1))) ? 1 : 0);
 }
 
-// Pass 5: per-workgroup tile counts over the live blocks.
+// Whole windows [cT, cT + T) inside moved block k: each is one tile holding
+// that block alone (the mover's straight-line case).
+__device__ inline uint64_t whole_in_block(const LiveView &lv, uint64_t k, uint64_t T) {
+    if (!moved_at(lv, k)) return 0;
+    const uint64_t a = lv.dst[k], b = a + lv.size[k];
+    const uint64_t lo = (a + T - 1) / T, hi = b / T;
+    return hi > lo ? hi - lo : 0;
+}
+
+// Pass 5: per-workgroup tile counts (and whole-window counts) over the live
+// blocks.
 __global__ __launch_bounds__(kScanThreads) void k_tcount_partials(LiveView lv, const WsHeader *hdr,
-                                                                  uint64_t T, uint64_t *tpart) {
+                                                                  uint64_t T, uint64_t *tpart,
+                                                                  uint64_t *twhole) {
     __shared__ uint64_t sh[kScanThreads / 64];
     if (plan_dead(hdr)) return;
     const uint64_t m = hdr->live_blocks;
     const uint64_t k0 = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanItems;
-    uint64_t c = 0;
+    uint64_t c = 0, w = 0;
 #pragma unroll
-    for (uint32_t j = 0; j < kScanItems; ++j)
-        if (k0 + j < m) c += tiles_in_block(lv, k0 + j, T);
+    for (uint32_t j = 0; j < kScanItems; ++j) {
+        if (k0 + j < m) {
+            c += tiles_in_block(lv, k0 + j, T);
+            w += whole_in_block(lv, k0 + j, T);
+        }
+    }
     c = block_reduce<kScanThreads>(c, sh, OpAdd());
-    if (threadIdx.x == 0) tpart[blockIdx.x] = c;
+    w = block_reduce<kScanThreads>(w, sh, OpAdd());
+    if (threadIdx.x == 0) {
+        tpart[blockIdx.x] = c;
+        twhole[blockIdx.x] = w;
+    }
 }
 
 // Pass 6 (one workgroup): exclusive scan of the counts; n_tiles.
-__global__ __launch_bounds__(kSpineThreads) void k_tcount_spine(const uint64_t *tpart, uint64_t *tprefix,
-                                                                uint64_t nb, WsHeader *hdr) {
+__global__ __launch_bounds__(kSpineThreads) void k_tcount_spine(const uint64_t *tpart,
+                                                                const uint64_t *twhole,
+                                                                uint64_t *tprefix, uint64_t nb,
+                                                                WsHeader *hdr) {
     __shared__ uint64_t sh[kSpineThreads / 64];
     if (plan_dead(hdr)) return;
-    uint64_t carry = 0;
+    uint64_t carry = 0, whole = 0;
+    for (uint64_t j = threadIdx.x; j < nb; j += kSpineThreads) whole += twhole[j];
+    whole = block_reduce<kSpineThreads>(whole, sh, OpAdd());
     for (uint64_t base = 0; base < nb; base += kSpineThreads) {
         const uint64_t j = base + threadIdx.x;
         const uint64_t x = j < nb ? tpart[j] : 0;
@@ -438,7 +460,10 @@ __global__ __launch_bounds__(kSpineThreads) void k_tcount_spine(const uint64_t *
         if (j < nb) tprefix[j] = carry + ex;
         carry += total;
     }
-    if (threadIdx.x == 0) hdr->n_tiles = carry;
+    if (threadIdx.x == 0) {
+        hdr->n_tiles = carry;
+        hdr->whole_tiles = whole;
+    }
 }
 
 // Pass 7: each live block's first tile index (a block with no tile gets the
@@ -521,7 +546,7 @@ __device__ inline uint64_t tile_of(const LiveView &lv, const uint32_t *tile_base
 // short range ending at or before this one.
 __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile_start,
                                                const uint32_t *tile_first,
-                                               const uint32_t *tile_base, WsHeader *hdr,
+                                               const uint32_t *tile_base, const WsHeader *hdr,
                                                uint64_t max_tiles, uint64_t T, TileRec *tiles,
                                                uint32_t *flags) {
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -575,13 +600,6 @@ __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile
     tiles[t] = TileRec{t0, t1, lv.src[first] - lv.dst[first], (uint32_t)first, (uint32_t)last,
                        dep_lo, dep_hi, 0};
     flags[t] = 0u;
-    // count the whole single-block windows (one atomic per wave)
-    const bool whole = first == last && (t0 & (T - 1)) == 0 && t1 - t0 == T;
-    const uint64_t active = __ballot(1);
-    const uint64_t wmask = __ballot(whole);
-    if (wmask && __lane_id() == (uint32_t)__builtin_ctzll(active))
-        atomicAdd(reinterpret_cast<unsigned long long *>(&hdr->whole_tiles),
-                  (unsigned long long)__popcll(wmask));
 }
 
 __global__ void k_commit(LiveView lv, uint64_t m, uint64_t *off_out, uint64_t *size_out,
@@ -764,11 +782,12 @@ void queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsL
         const LiveView lv = live_view(ws, L);
         uint64_t *tpart = reinterpret_cast<uint64_t *>(ws + L.tpart);
         uint64_t *tprefix = reinterpret_cast<uint64_t *>(ws + L.tprefix);
+        uint64_t *twhole = reinterpret_cast<uint64_t *>(ws + L.twhole);
         uint32_t *tile_base = reinterpret_cast<uint32_t *>(ws + L.tile_base);
         const uint64_t gnb = nb ? nb : 1;  // live blocks <= entries
         hipLaunchKernelGGL(k_tcount_partials, dim3((uint32_t)gnb), dim3(kScanThreads), 0, s, lv,
-                           hdr, (uint64_t)tile_bytes, tpart);
-        hipLaunchKernelGGL(k_tcount_spine, dim3(1), dim3(kSpineThreads), 0, s, tpart, tprefix, gnb,
+                           hdr, (uint64_t)tile_bytes, tpart, twhole);
+        hipLaunchKernelGGL(k_tcount_spine, dim3(1), dim3(kSpineThreads), 0, s, tpart, twhole, tprefix, gnb,
                            hdr);
         hipLaunchKernelGGL(k_tcount_down, dim3((uint32_t)gnb), dim3(kScanThreads), 0, s, lv, hdr,
                            (uint64_t)tile_bytes, tprefix, tile_base);
