@@ -39,7 +39,11 @@
 // uniform bases, with no per-vector predicate, so all sixteen loads and all
 // sixteen stores of a lane stay in flight together (behind a per-vector
 // branch the compiler waits for each store before the next).  Partial and
-// multi-block tiles take the general path.  The dependency flags are read
+// multi-block tiles take the general path, also without a branch around any
+// memory access: a lane outside the tile's range reloads the tile's first
+// source vector, and stores go through a buffer descriptor over the tile's
+// window, a disabled lane getting an offset the hardware drops as out of
+// range.  The dependency flags are read
 // once speculatively, right behind the tile's data loads: a dependency far
 // below is long done, and the tile then stores without another round trip.
 //
@@ -70,6 +74,13 @@ __device__ __forceinline__ void store16(uint8_t *p, v4u v) {
     if constexpr ((NT & 2) != 0) __builtin_nontemporal_store(v, q);
     else *q = v;
 }
+
+// Raw buffer resource (gfx9 family): word 3 of the descriptor, the
+// non-temporal cache-policy bit of a buffer access, and an offset beyond any
+// window (a buffer store out of range is dropped by the hardware).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kBufferNt = 2;
+constexpr uint32_t kOutOfWindow = 0x80000000u;
 
 __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -133,22 +144,24 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
 #pragma unroll
             for (int j = 0; j < VPT; ++j) v[j] = load16<NT>(src + (size_t)j * kMoveRowBytes);
         } else {
+            // no branch around a memory access: a lane outside [rel0, rel1)
+            // reloads the tile's first source vector and discards it
+            const uint8_t *first_src = a.arena + tb + rel0 + shift0;
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
                 const uint32_t r = ((uint32_t)j * kMoveThreads + tid) * 16u;
-                if (ok && r >= rel0 && r < rel1) {
-                    uint64_t sh = shift0;
-                    if (nblk > 1u) {
-                        uint32_t lo = 0, n = nblk;  // largest k with s_rel[k] <= r
-                        while (n > 1u) {
-                            const uint32_t half = n >> 1;
-                            lo = (s_rel[lo + half] <= r) ? lo + half : lo;
-                            n -= half;
-                        }
-                        sh = s_shift[lo];
+                uint64_t sh = shift0;
+                if (nblk > 1u && ok) {
+                    uint32_t lo = 0, n = nblk;  // largest k with s_rel[k] <= r
+                    while (n > 1u) {
+                        const uint32_t half = n >> 1;
+                        lo = (s_rel[lo + half] <= r) ? lo + half : lo;
+                        n -= half;
                     }
-                    v[j] = load16<NT>(a.arena + tb + r + sh);
+                    sh = s_shift[lo];
                 }
+                const bool in = ok && r >= rel0 && r < rel1;
+                v[j] = load16<NT>(in ? a.arena + tb + r + sh : first_src);
             }
         }
         // first look at the dependency flags, returned with the data loads
@@ -185,10 +198,17 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
 #pragma unroll
                 for (int j = 0; j < VPT; ++j) store16<NT>(dst + (size_t)j * kMoveRowBytes, v[j]);
             } else {
+                // buffer stores over the tile's window: a lane outside
+                // [rel0, rel1) gets an offset past the window's end, which
+                // the hardware drops -- no branch around any store
+                const __amdgpu_buffer_rsrc_t win = __builtin_amdgcn_make_buffer_rsrc(
+                    a.arena + tb, 0, (int)a.tile_bytes, kBufferRsrcWord3);
 #pragma unroll
                 for (int j = 0; j < VPT; ++j) {
                     const uint32_t r = ((uint32_t)j * kMoveThreads + tid) * 16u;
-                    if (r >= rel0 && r < rel1) store16<NT>(a.arena + tb + r, v[j]);
+                    const uint32_t off = (r >= rel0 && r < rel1) ? r : kOutOfWindow;
+                    __builtin_amdgcn_raw_buffer_store_b128(v[j], win, (int)off, 0,
+                                                           (NT & 2) ? kBufferNt : 0);
                 }
             }
         }
@@ -204,12 +224,14 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
 template <int VPT, int NT>
 hipError_t launch_t(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
     const size_t lds = (size_t)a.max_blocks * 12u + 16u;
-    int occ = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_move<VPT, NT>,
-                                                                kMoveThreads, lds);
-    if (e != hipSuccess) return e;
-    if (occ < 1) occ = 1;
-    uint64_t per_cu = wg_per_cu ? wg_per_cu : (uint32_t)occ;
+    uint64_t per_cu = wg_per_cu;
+    if (per_cu == 0) {  // as many as the kernel's resources allow (the query costs a few us)
+        int occ = 0;
+        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &occ, k_move<VPT, NT>, kMoveThreads, lds);
+        if (e != hipSuccess) return e;
+        per_cu = occ < 1 ? 1u : (uint32_t)occ;
+    }
     uint64_t grid = per_cu * (uint64_t)num_cus;
     if (grid > a.n_tiles) grid = a.n_tiles;
     if (grid < 1) grid = 1;
