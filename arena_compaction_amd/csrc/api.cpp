@@ -119,7 +119,7 @@ size_t defrag_workspace_bytes(uint64_t n, uint64_t max_pinned, uint64_t arena_by
     const uint32_t T = tile_bytes ? tile_bytes : kDefaultTile;
     if (!tile_ok(T) || n > DEFRAG_MAX_ENTRIES || max_pinned > n) return 0;
     const uint64_t tiles = tiles_bound(arena_bytes, max_pinned, T);
-    if (tiles > 0xFFFFFFF0ull) return 0;
+    if (tiles > kMaxTiles) return 0;
     return ws_with_tiles(n, tiles).total;
 }
 
@@ -208,7 +208,7 @@ int plan_common(const defrag_table *table, uint64_t arena_bytes, uint64_t reques
         arg_error(&plan->stats);
         return DEFRAG_EWORKSPACE;
     }
-    const WsLayout L = ws_with_tiles(table->n, max_tiles < 0xFFFFFFF0ull ? max_tiles : 0xFFFFFFF0ull);
+    const WsLayout L = ws_with_tiles(table->n, max_tiles < kMaxTiles ? max_tiles : kMaxTiles);
     const int dev = current_device();
     if (dev < 0) return DEFRAG_EHIP;
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);

@@ -28,6 +28,11 @@ constexpr uint32_t kMinTile = 256;
 constexpr uint32_t kMaxTile = 131072;
 constexpr uint32_t kDefaultSpinLog2 = 22;
 constexpr uint64_t kNone = ~0ull;
+// Tile indices and the mover's ticket are 32-bit.  Every mover workgroup
+// makes one last claim past the end, so tiles plus the grid must stay below
+// 2^32: tiles are capped here and the grid at kMaxMoveGrid.
+constexpr uint64_t kMaxTiles = 0xFFFF0000ull;
+constexpr uint64_t kMaxMoveGrid = 0xFFFFull;
 
 // Device-resident plan header (first 256 bytes of the workspace).
 struct alignas(256) WsHeader {

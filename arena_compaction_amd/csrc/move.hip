@@ -234,6 +234,7 @@ hipError_t launch_t(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStrea
     }
     uint64_t grid = per_cu * (uint64_t)num_cus;
     if (grid > a.n_tiles) grid = a.n_tiles;
+    if (grid > kMaxMoveGrid) grid = kMaxMoveGrid;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL((k_move<VPT, NT>), dim3((uint32_t)grid), dim3(kMoveThreads), lds, s, a);
     return hipGetLastError();

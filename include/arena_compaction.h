@@ -171,7 +171,8 @@ typedef struct defrag_plan_t {
 
 /* Workspace bytes for a table of n entries, at most max_pinned of them
  * pinned, over an arena of arena_bytes, with the given tile size (0 =
- * default).  Returns 0 for impossible arguments.  The workspace is device
+ * default).  Returns 0 for impossible arguments, including an arena that
+ * would need more than 0xFFFF0000 mover tiles (tile indices are 32-bit).  The workspace is device
  * memory, 256-byte aligned, owned by the caller; any content.  defrag_plan
  * uses whatever size it is given and returns DEFRAG_EWORKSPACE if the
  * table needs more mover tiles than fit. */

@@ -60,6 +60,9 @@ def test_workspace_bytes():
     assert ac.defrag_workspace_bytes(10, 4096, 0, 11) == 0   # more pinned than entries
     for bad_tile in (100, 128, 3000, 262144):
         assert ac.defrag_workspace_bytes(16, 4096, bad_tile) == 0
+    # more mover tiles than 32-bit tile indices (with room for the grid) allow
+    assert ac.defrag_workspace_bytes(16, 1 << 44, 256) == 0
+    assert ac.defrag_workspace_bytes(16, 0xFFFEFFF0 * 256, 256) > 0
 
 
 def test_host_side_argument_errors_need_no_gpu():
