@@ -53,6 +53,29 @@ def _traffic(moved_bytes: int):
     return t.get("hbm_bytes_per_launch")
 
 
+def _host_description() -> str:
+    """CPU model, logical CPUs and RAM of the host the oracle runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    mem = 0
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal:"):
+                    mem = int(line.split()[1]) * 1024
+                    break
+    except OSError:
+        pass
+    return f"{model}; {os.cpu_count()} logical CPUs; {mem / 2**30:.0f} GiB RAM"
+
+
 def cpu_baseline(heap, budget_s: float = 12.0):
     """The oracle, single-threaded, on a bounded slice of the same workload:
     the entries of the config-3 table that lie in a 4 GiB window of its mixed
@@ -100,6 +123,7 @@ def cpu_baseline(heap, budget_s: float = 12.0):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
+        "host": _host_description(),
         "sample": (f"config-3 entries {i0}..{i1 - 1} (the 4 GiB window at 40 GiB, "
                    f"{i1 - i0} entries, {S} B arena, {moved} B moved, {hs.shape[0]} handles); "
                    f"validate+plan+stats+memmove+remap, {reps} reps, {per * 1e3:.1f} ms each"),
@@ -395,6 +419,8 @@ def main() -> int:
         "handles_per_s": round(handles_per_s, 1),
         "ms": {k: round(v, 4) for k, v in mean.items()},
         "min_move_ms": round(float(np.min(times["move"])), 4),
+        "median_move_ms": round(float(np.median(times["move"])), 4),
+        "max_move_GBps": round(2 * moved / (float(np.min(times["move"])) * 1e-3) / 1e9, 2),
         "wall_s_incl_refill": round(wall, 3),
         "before": {"free_bytes": int(s0.free_bytes), "largest_hole": int(s0.largest_hole),
                    "hole_count": int(s0.hole_count),
