@@ -133,13 +133,41 @@ struct alignas(16) TileRec {
 };
 static_assert(sizeof(TileRec) == 48, "tile record size");
 
+// One live block as the handle remap reads it: one aligned 32-byte record,
+// so the block holding a handle costs one cache-line request.
+struct alignas(32) LiveRec {
+    uint64_t src;   // old offset
+    uint64_t size;
+    uint64_t dst;   // new offset
+    uint64_t pad;
+};
+static_assert(sizeof(LiveRec) == 32, "live record size");
+
+// Remap index: the arena is cut into buckets of 2^w bytes, at most
+// remap_bucket_cap(n) of them, and ridx[b] counts the live blocks starting
+// below bucket b (entries 0 .. buckets).
+inline uint64_t remap_bucket_cap(uint64_t n) {
+    uint64_t c = 16;
+    while (c < 2 * n + 2 && c < (1ull << 18)) c <<= 1;
+    return c;
+}
+inline uint32_t remap_shift(uint64_t arena_bytes, uint64_t n) {
+    const uint64_t cap = remap_bucket_cap(n);
+    uint32_t w = 5;
+    while ((arena_bytes >> w) >= cap) ++w;
+    return w;
+}
+inline uint64_t remap_buckets(uint64_t arena_bytes, uint64_t n) {
+    return (arena_bytes >> remap_shift(arena_bytes, n)) + 1;
+}
+
 constexpr size_t kPerTileBytes =
     sizeof(uint64_t) + sizeof(uint32_t) + sizeof(TileRec) + sizeof(uint32_t);
 
 struct WsLayout {
     // fixed part (depends on n only)
     size_t header, part, prefix, spart, tpart, twhole, tprefix, live_dst, live_src, live_size,
-        live_pin, tile_base, live_z, live_pc, selpart, fixed;
+        live_pin, tile_base, live_z, live_pc, selpart, live_rec, ridx, fixed;
     // tile part (depends on the tile capacity)
     size_t tile_start, tile_first, tiles, flags, total;
     uint64_t n_scan_blocks, n_sel_blocks, max_tiles;
@@ -168,6 +196,8 @@ inline WsLayout ws_fixed(uint64_t n) {
     L.live_z = at;    at += align256((n + 1) * sizeof(uint64_t));
     L.live_pc = at;   at += align256((n + 1) * sizeof(uint32_t));
     L.selpart = at;   at += align256(L.n_sel_blocks * sizeof(SelPart));
+    L.live_rec = at;  at += align256((n + 1) * sizeof(LiveRec));
+    L.ridx = at;      at += align256((remap_bucket_cap(n) + 2) * sizeof(uint32_t));
     L.fixed = at;
     return L;
 }
@@ -262,8 +292,13 @@ hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, uint32_t nontempor
                        int num_cus, hipStream_t s);
 
 // ---- remap.hip ----
-hipError_t launch_remap(const LiveView &lv, uint64_t live_blocks, const uint64_t *h_in,
-                        uint64_t *h_out, uint64_t n_handles, uint64_t *n_invalid,
-                        int num_cus, hipStream_t s);
+// The remap index of a plan (queued behind its scan; live-block count from
+// the header, nothing written if the plan failed).
+hipError_t launch_remap_index(const uint64_t *live_src, const WsHeader *hdr, uint64_t arena_bytes,
+                              uint64_t n, uint32_t *ridx, hipStream_t s);
+hipError_t launch_remap(const LiveRec *rec, const uint64_t *live_src, const uint32_t *ridx,
+                        uint64_t arena_bytes, uint64_t n, uint64_t live_blocks,
+                        const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
+                        uint64_t *n_invalid, int num_cus, hipStream_t s);
 
 }  // namespace ac

@@ -260,6 +260,7 @@ struct LiveOut {
     uint8_t *pin;
     uint64_t *z;   // live bytes below each live block (selection only)
     uint32_t *pc;  // pinned blocks below each live block (selection only)
+    LiveRec *rec;  // the remap's copy of (old offset, size, new offset)
 };
 
 // Pass 3: new offsets, packed live arrays, per-workgroup hole/move stats.
@@ -308,6 +309,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
                 if (outputs & kOutNew) {
                     lo.dst[run.cnt] = nw;
                     lo.pin[run.cnt] = (uint8_t)p[k];
+                    lo.rec[run.cnt] = LiveRec{o[k], s[k], nw, 0};
                 }
                 if (outputs & (kOutNew | kOutSelect)) {
                     lo.src[run.cnt] = o[k];
@@ -764,7 +766,8 @@ void queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsL
                reinterpret_cast<uint64_t *>(ws + L.live_size),
                reinterpret_cast<uint8_t *>(ws + L.live_pin),
                reinterpret_cast<uint64_t *>(ws + L.live_z),
-               reinterpret_cast<uint32_t *>(ws + L.live_pc)};
+               reinterpret_cast<uint32_t *>(ws + L.live_pc),
+               reinterpret_cast<LiveRec *>(ws + L.live_rec)};
     const uint64_t nb = L.n_scan_blocks;
     if (nb) {
         hipLaunchKernelGGL(k_scan_partials, dim3((uint32_t)nb), dim3(kScanThreads), 0, s, t,
@@ -805,6 +808,8 @@ void queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsL
                                tile_first, tile_base, hdr, L.max_tiles, (uint64_t)tile_bytes, tiles,
                                flags);
         }
+        launch_remap_index(lv.src, hdr, arena_bytes, t.n, reinterpret_cast<uint32_t *>(ws + L.ridx),
+                           s);
     }
 }
 

@@ -9,60 +9,77 @@
 //   h inside live block j  ->  new_offset_j + (h - offset_j)
 //   anything else          ->  UINT64_MAX (counted)
 //
-// One lane per handle, grid-stride.  The search runs over the plan's packed
-// live-block arrays (old offsets ascending, new offsets, sizes), so free
-// entries never cost a probe; a pinned block maps to itself.  A
-// plain binary search is bound by L2 transactions (every probe of every lane
-// is its own cache line), so the top levels run in LDS over a sample of the
-// old offsets and only the last few probe global memory.  HBM traffic is
-// 16 B per handle.
+// One lane per handle, grid-stride, over the plan's packed live blocks (old
+// offsets ascending), so free entries never cost a probe; a pinned block
+// maps to itself.  Random handles make the search bound by L2 requests (each
+// probe of each lane is its own cache line), so the plan builds an index --
+// the arena cut into at most 2^18 power-of-two buckets, each pointing at the
+// first live block starting in it -- and each live block also has one
+// 32-byte record (old offset, size, new offset).  HBM traffic is 16 B per
+// handle; the index, offsets and records stay in L2 / the last-level cache.
 #include "internal.h"
 
 namespace ac {
 namespace {
 
 constexpr uint32_t kRemapThreads = 256;
-constexpr uint32_t kSplitters = 4096;  // 32 KB of LDS per workgroup
 
-// Largest j in [lo, lo + n) with a[j] <= h, given a[lo] <= h (or j = lo).
-template <typename T>
-__device__ __forceinline__ uint64_t search_le(const T *a, uint64_t lo, uint64_t n, uint64_t h) {
-    while (n > 1) {
-        const uint64_t half = n >> 1;
-        lo = ((uint64_t)a[lo + half] <= h) ? lo + half : lo;
-        n -= half;
+// Index: ridx[b] = number of live blocks whose old offset is below b << w,
+// for b in [0, nb]; one lane per entry, a binary search over the packed old
+// offsets.  A failed plan leaves it alone (its blocks are not written).
+__global__ __launch_bounds__(256) void k_remap_index(const uint64_t *__restrict__ live_src,
+                                                     const WsHeader *hdr, uint32_t w, uint64_t nb,
+                                                     uint32_t *ridx) {
+    const uint64_t b = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b > nb || hdr->bad_key != kNone || hdr->win_state == kWinNoFit) return;
+    const uint64_t m = hdr->live_blocks;
+    const uint64_t x = b << w;
+    uint64_t lo = 0, len = m;  // first k with src[k] >= x
+    while (len > 0) {
+        const uint64_t half = len >> 1;
+        if (live_src[lo + half] < x) {
+            lo += half + 1;
+            len -= half + 1;
+        } else {
+            len = half;
+        }
     }
-    return lo;
+    ridx[b] = (uint32_t)lo;
 }
 
-// The top of each search runs in LDS over a sample of every step-th old
-// offset; the rest runs over one bucket of at most `step` offsets in global
-// memory (L2-resident).  For m <= kSplitters the sample is the whole array.
-// Searches are branchless with trip counts set by the sizes alone, so the
-// 64 lanes of a wave step together.
-__global__ __launch_bounds__(kRemapThreads) void k_remap(const uint64_t *__restrict__ live_dst,
+// One lane per handle, grid-stride.  The bucket of h gives the live blocks
+// starting in it, [ridx[b], ridx[b+1]); the block holding h, if any, is the
+// last one starting at or below h, so it is found by a short search inside
+// the bucket (or is the block before it), and its record is one 32-byte
+// read.  A random handle costs about three dependent cache-line requests:
+// the index pair, a probe or two, the record.
+__global__ __launch_bounds__(kRemapThreads) void k_remap(const LiveRec *__restrict__ rec,
                                                          const uint64_t *__restrict__ live_src,
-                                                         const uint64_t *__restrict__ live_size,
-                                                         uint64_t m, const uint64_t *h_in,
-                                                         uint64_t *h_out, uint64_t H,
-                                                         unsigned long long *n_invalid) {
-    __shared__ uint64_t sp[kSplitters];
-    const uint64_t step = (m + kSplitters - 1) / kSplitters;
-    const uint64_t ns = m ? (m + step - 1) / step : 0;
-    for (uint64_t i = threadIdx.x; i < ns; i += kRemapThreads) sp[i] = live_src[i * step];
-    __syncthreads();
+                                                         const uint32_t *__restrict__ ridx,
+                                                         uint32_t w, uint64_t nb, uint64_t m,
+                                                         const uint64_t *h_in, uint64_t *h_out,
+                                                         uint64_t H, unsigned long long *n_invalid) {
     uint64_t bad = 0;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < H; k += stride) {
         const uint64_t h = h_in[k];
         uint64_t out = kNone;
-        if (ns && sp[0] <= h) {
-            const uint64_t b = search_le(sp, 0, ns, h);
-            const uint64_t lo = b * step;
-            const uint64_t hi = (lo + step < m) ? lo + step : m;
-            const uint64_t j = search_le(live_src, lo, hi - lo, h);
-            const uint64_t src = live_src[j];
-            if (h - src < live_size[j]) out = live_dst[j] + (h - src);
+        const uint64_t b = h >> w;
+        if (m && b < nb) {
+            uint64_t first = ridx[b], len = ridx[b + 1] - first;  // first with src > h
+            while (len > 0) {
+                const uint64_t half = len >> 1;
+                if (live_src[first + half] <= h) {
+                    first += half + 1;
+                    len -= half + 1;
+                } else {
+                    len = half;
+                }
+            }
+            if (first > 0) {
+                const LiveRec r = rec[first - 1];
+                if (h - r.src < r.size) out = r.dst + (h - r.src);
+            }
         }
         bad += (out == kNone) ? 1u : 0u;
         h_out[k] = out;
@@ -80,17 +97,27 @@ __global__ void k_zero_u64(uint64_t *p) {
 
 }  // namespace
 
-hipError_t launch_remap(const LiveView &lv, uint64_t live_blocks, const uint64_t *h_in,
-                        uint64_t *h_out, uint64_t n_handles, uint64_t *n_invalid, int num_cus,
-                        hipStream_t s) {
+hipError_t launch_remap_index(const uint64_t *live_src, const WsHeader *hdr, uint64_t arena_bytes,
+                              uint64_t n, uint32_t *ridx, hipStream_t s) {
+    const uint32_t w = remap_shift(arena_bytes, n);
+    const uint64_t nb = remap_buckets(arena_bytes, n);
+    hipLaunchKernelGGL(k_remap_index, dim3((uint32_t)((nb + 1 + 255) / 256)), dim3(256), 0, s,
+                       live_src, hdr, w, nb, ridx);
+    return hipGetLastError();
+}
+
+hipError_t launch_remap(const LiveRec *rec, const uint64_t *live_src, const uint32_t *ridx,
+                        uint64_t arena_bytes, uint64_t n, uint64_t live_blocks,
+                        const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
+                        uint64_t *n_invalid, int num_cus, hipStream_t s) {
     if (n_invalid) hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, n_invalid);
     if (n_handles == 0) return hipGetLastError();
-    // persistent grid: every workgroup pays for loading the LDS sample once
     uint64_t grid = (n_handles + kRemapThreads - 1) / kRemapThreads;
-    const uint64_t cap = (uint64_t)num_cus * 4;  // measured best of 4, 5 and 8 per CU
+    const uint64_t cap = (uint64_t)num_cus * 2;  // measured best of 1, 2, 3, 4, 8, 16 per CU
     if (grid > cap) grid = cap;
-    hipLaunchKernelGGL(k_remap, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s, lv.dst, lv.src,
-                       lv.size, live_blocks, h_in, h_out, n_handles,
+    hipLaunchKernelGGL(k_remap, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s, rec, live_src,
+                       ridx, remap_shift(arena_bytes, n), remap_buckets(arena_bytes, n),
+                       live_blocks, h_in, h_out, n_handles,
                        reinterpret_cast<unsigned long long *>(n_invalid));
     return hipGetLastError();
 }
