@@ -316,3 +316,31 @@ def test_pinned_invalid_and_workspace(ac):
     assert ei.value.code == ac.DEFRAG_EWORKSPACE
     for tile in (256, 65536):
         _full_check(big, _tuning(ac, tile))
+
+
+def test_watchdog_turns_a_stalled_wait_into_an_error(ac):
+    """Failure handling forced from the host: with a spin limit of two polls,
+    tiles that wait on the tile just below them (one 64 MiB block above a
+    32-byte hole, 256-byte tiles) give up, and the move reports
+    DEFRAG_ETIMEOUT instead of hanging; every wave still exits.  The library
+    stays usable: a compaction with the default limit is bit-exact after."""
+    MiB = 1 << 20
+    heap = W.table_from_lists(32 + 64 * MiB, [(0, 32), (32, 64 * MiB)], [0, 1], [40, 4096])
+    off, size, live = device_table(heap, "cuda")
+    arena = torch.zeros(heap.arena_bytes, dtype=torch.uint8, device="cuda")
+    tripped = False
+    for attempt in range(3):
+        log(f"case watchdog attempt {attempt}: {heap.describe()} tile 256, spin limit 2 polls")
+        ws = ac.workspace(heap.n, heap.arena_bytes, 256)
+        plan = ac.defrag_plan(off, size, live, heap.arena_bytes, ws,
+                              tuning=ac.defrag_tuning(256, 0, 1, 1))
+        assert plan.n_tiles == (64 * MiB) // 256   # tile t + 1 waits on tile t
+        ac.defrag_move(arena, plan, ws)
+        st = ac.defrag_move_status(plan, ws)
+        assert st in (ac.DEFRAG_OK, ac.DEFRAG_ETIMEOUT), st
+        if st == ac.DEFRAG_ETIMEOUT:
+            tripped = True
+            break
+    assert tripped, "no wait gave up in three moves of 262,145 chained tiles"
+    del arena
+    _full_check(heap)
