@@ -91,6 +91,17 @@ LEVELS = {0: "OK", 1: "WARNING", 2: "CRITICAL"}
 ACTIONS = {0: "none", 1: "targeted", 2: "full", 3: "no_room"}
 
 
+class defrag_compact_args(ctypes.Structure):
+    _fields_ = [("table", ctypes.POINTER(defrag_table)), ("arena_bytes", ctypes.c_uint64),
+                ("arena_dev", ctypes.c_void_p), ("request_bytes", ctypes.c_uint64),
+                ("tuning", ctypes.POINTER(defrag_tuning)), ("ws_dev", ctypes.c_void_p),
+                ("ws_bytes", ctypes.c_size_t), ("new_offset_dev", ctypes.c_void_p),
+                ("h_in_dev", ctypes.c_void_p), ("h_out_dev", ctypes.c_void_p),
+                ("n_handles", ctypes.c_uint64), ("n_invalid_dev", ctypes.c_void_p),
+                ("offset_out_dev", ctypes.c_void_p), ("size_out_dev", ctypes.c_void_p),
+                ("live_out_dev", ctypes.c_void_p), ("pinned_out_dev", ctypes.c_void_p)]
+
+
 class DefragError(RuntimeError):
     def __init__(self, code: int, what: str, stats: Optional[defrag_stats_t] = None):
         self.code = code
@@ -127,12 +138,14 @@ def _load() -> ctypes.CDLL:
     L.defrag_move_status.argtypes = [ctypes.POINTER(defrag_plan_t), P, P]
     L.defrag_remap.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, U, P, P]
     L.defrag_commit.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, P, P, P]
+    L.defrag_compact.argtypes = [ctypes.POINTER(defrag_compact_args), P,
+                                 ctypes.POINTER(defrag_plan_t), ctypes.POINTER(defrag_stats_t)]
     L.defrag_monitor.argtypes = [ctypes.POINTER(defrag_stats_t), ctypes.POINTER(defrag_monitor_cfg),
                                  ctypes.POINTER(defrag_monitor_report)]
     L.defrag_strerror.argtypes = [ctypes.c_int]
     L.defrag_strerror.restype = ctypes.c_char_p
     for f in ("defrag_stats", "defrag_first_fit", "defrag_plan", "defrag_plan_targeted",
-              "defrag_move", "defrag_monitor",
+              "defrag_move", "defrag_monitor", "defrag_compact",
               "defrag_move_status",
               "defrag_remap", "defrag_commit"):
         getattr(L, f).restype = ctypes.c_int
@@ -144,7 +157,7 @@ lib = _load()
 EXPORTS = ("defrag_workspace_bytes", "defrag_stats", "defrag_first_fit", "defrag_plan",
            "defrag_plan_targeted",
            "defrag_move",
-           "defrag_move_status", "defrag_remap", "defrag_commit", "defrag_monitor",
+           "defrag_move_status", "defrag_remap", "defrag_commit", "defrag_compact", "defrag_monitor",
            "defrag_strerror")
 
 
@@ -290,6 +303,42 @@ def defrag_commit(plan: defrag_plan_t, ws: torch.Tensor, offset_out=None, size_o
                            _ptr(size_out), _ptr(live_out), _ptr(pinned_out), _stream(stream))
     if rc != DEFRAG_OK:
         raise DefragError(rc, "defrag_commit")
+
+
+def defrag_compact(offset, size, live, arena_bytes: int, arena: torch.Tensor, ws: torch.Tensor,
+                   request_bytes: int = 0, new_offset: Optional[torch.Tensor] = None,
+                   handles: Optional[torch.Tensor] = None, h_out: Optional[torch.Tensor] = None,
+                   n_invalid: Optional[torch.Tensor] = None, offset_out=None, size_out=None,
+                   live_out=None, pinned_out=None, tuning: Optional[defrag_tuning] = None,
+                   stream=None, pinned=None, after: Optional[bool] = None):
+    """Plan, move, remap, commit and the post-check in one C-ABI call.
+    after (default: whenever offset_out and size_out are given) asks for the
+    post-move statistics.  Returns (plan, post-move stats or None)."""
+    assert arena.dtype == torch.uint8
+    if after is None:
+        after = offset_out is not None and size_out is not None
+    t = make_table(offset, size, live, pinned)
+    H = 0 if handles is None else handles.numel()
+    if handles is not None:
+        assert handles.dtype == torch.int64
+        if h_out is None:
+            h_out = torch.empty_like(handles)
+    a = defrag_compact_args(
+        ctypes.pointer(t), arena_bytes, _ptr(arena) if arena.numel() else None, request_bytes,
+        ctypes.pointer(tuning) if tuning is not None else None, _ptr(ws), ws.numel(),
+        _ptr(new_offset) if new_offset is not None and new_offset.numel() else None,
+        _ptr(handles) if H else None, _ptr(h_out) if H else None, H, _ptr(n_invalid),
+        _ptr(offset_out) if offset_out is not None and offset_out.numel() else None,
+        _ptr(size_out) if size_out is not None and size_out.numel() else None,
+        _ptr(live_out) if live_out is not None and live_out.numel() else None,
+        _ptr(pinned_out) if pinned_out is not None and pinned_out.numel() else None)
+    plan = defrag_plan_t()
+    post = defrag_stats_t() if after else None
+    rc = lib.defrag_compact(ctypes.byref(a), _stream(stream), ctypes.byref(plan),
+                            ctypes.byref(post) if after else None)
+    if rc != DEFRAG_OK:
+        raise DefragError(rc, "defrag_compact", plan.stats if rc == DEFRAG_EINVAL else None)
+    return plan, post
 
 
 def defrag_monitor(stats: defrag_stats_t, warning_ratio: float = 0.85,

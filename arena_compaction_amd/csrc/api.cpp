@@ -363,6 +363,55 @@ int defrag_commit(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes
     return DEFRAG_OK;
 }
 
+int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan_t *plan,
+                   defrag_stats_t *after_host) {
+    if (!plan) return DEFRAG_EINVAL;
+    if (!a || (a->n_handles && (!a->h_in_dev || !a->h_out_dev))) {
+        std::memset(plan, 0, sizeof(*plan));
+        arg_error(&plan->stats);
+        return DEFRAG_EINVAL;
+    }
+    int rc = a->request_bytes
+                 ? defrag_plan_targeted(a->table, a->arena_bytes, a->request_bytes, a->tuning,
+                                        a->ws_dev, a->ws_bytes, stream, a->new_offset_dev, plan)
+                 : defrag_plan(a->table, a->arena_bytes, a->tuning, a->ws_dev, a->ws_bytes, stream,
+                               a->new_offset_dev, plan);
+    if (rc) return rc;
+    // the post-check reads the packed table (empty if nothing is live)
+    if (after_host && plan->live_blocks && (!a->offset_out_dev || !a->size_out_dev)) {
+        arg_error(after_host);
+        return DEFRAG_EINVAL;  // checked before anything moves
+    }
+    rc = defrag_move(a->arena_dev, a->arena_bytes, plan, a->ws_dev, a->ws_bytes, stream);
+    if (rc) return rc;
+    if (a->n_handles || a->n_invalid_dev) {
+        rc = defrag_remap(plan, a->ws_dev, a->ws_bytes, a->h_in_dev, a->h_out_dev, a->n_handles,
+                          a->n_invalid_dev, stream);
+        if (rc) return rc;
+    }
+    if (a->offset_out_dev || a->size_out_dev || a->live_out_dev || a->pinned_out_dev) {
+        rc = defrag_commit(plan, a->ws_dev, a->ws_bytes, a->offset_out_dev, a->size_out_dev,
+                           a->live_out_dev, a->pinned_out_dev, stream);
+        if (rc) return rc;
+    }
+    // one synchronisation: the post-move statistics (if asked for) and the
+    // mover's status come back in the same header read
+    WsHeader h;
+    if (after_host) {
+        const defrag_table packed{a->offset_out_dev, a->size_out_dev, a->live_out_dev,
+                                  plan->live_blocks, a->pinned_out_dev};
+        rc = stats_pass(&packed, a->arena_bytes, kNone, a->ws_dev, a->ws_bytes, stream,
+                        after_host, &h);
+        if (rc) return rc;
+    } else {
+        rc = read_header(&h, static_cast<const uint8_t *>(a->ws_dev), plan_layout(plan), stream);
+        if (rc) return rc;
+    }
+    if (plan->n_tiles && h.epoch != plan->epoch) return DEFRAG_ENOPLAN;
+    if (plan->n_tiles && (h.status & kStatusTimeout)) return DEFRAG_ETIMEOUT;
+    return DEFRAG_OK;
+}
+
 const char *defrag_strerror(int code) {
     switch (code) {
         case DEFRAG_OK: return "ok";

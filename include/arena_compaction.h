@@ -266,6 +266,43 @@ int defrag_commit(const defrag_plan_t *plan_host, const void *ws_dev,
                   uint64_t *size_out_dev, uint8_t *live_out_dev,
                   uint8_t *pinned_out_dev, hipStream_t stream);
 
+/* One whole compaction in one call -- the pages' operator: mark (the caller's
+ * live flags), scan holes and plan, move, update every reference in one
+ * batch (910C page, "Periodic compaction with Ascend C") -- then the
+ * post-check (CANN page 3.3: one contiguous free region).  Runs
+ * defrag_plan (or defrag_plan_targeted when request_bytes > 0),
+ * defrag_move, defrag_remap (when n_handles or n_invalid_dev is given),
+ * defrag_commit (when any packed-table output is given) and, when
+ * after_host is given, defrag_stats of the packed table, with two host
+ * synchronisations in all: the plan's header read-back and one at the end.
+ * Returns the first failing step's code (nothing moves if the plan fails;
+ * DEFRAG_ETIMEOUT leaves the arena undefined).  plan_host is filled as by
+ * the planning call and is consumed (state 2).  after_host needs
+ * offset_out_dev and size_out_dev unless nothing is live (DEFRAG_EINVAL,
+ * checked after the plan and before anything moves); pass pinned_out_dev
+ * too so pinned blocks stay pinned in the post-check. */
+typedef struct defrag_compact_args {
+    const defrag_table *table;
+    uint64_t arena_bytes;
+    void *arena_dev;
+    uint64_t request_bytes;        /* 0: full compaction; > 0: targeted       */
+    const defrag_tuning *tuning;   /* may be NULL                             */
+    void *ws_dev;
+    size_t ws_bytes;
+    uint64_t *new_offset_dev;      /* n entries, may be NULL                  */
+    const uint64_t *h_in_dev;      /* handles (n_handles), may be NULL if 0   */
+    uint64_t *h_out_dev;           /* may equal h_in_dev                      */
+    uint64_t n_handles;
+    uint64_t *n_invalid_dev;       /* may be NULL                             */
+    uint64_t *offset_out_dev;      /* packed table, live_blocks entries each; */
+    uint64_t *size_out_dev;        /* any may be NULL                         */
+    uint8_t *live_out_dev;
+    uint8_t *pinned_out_dev;
+} defrag_compact_args;
+
+int defrag_compact(const defrag_compact_args *args, hipStream_t stream,
+                   defrag_plan_t *plan_host, defrag_stats_t *after_host);
+
 /* Layout monitor: host arithmetic on a defrag_stats result, no HIP call.
  * CANN page, section 5.3 (MemoryMonitor): usage = live / arena is rated OK,
  * WARNING above warning_ratio, CRITICAL above critical_ratio (defaults 0.85

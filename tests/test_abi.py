@@ -21,7 +21,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     fns = _declared_functions()
     for f in ("defrag_stats", "defrag_first_fit", "defrag_plan", "defrag_plan_targeted",
-              "defrag_move", "defrag_remap",
+              "defrag_compact", "defrag_move", "defrag_remap",
               "defrag_workspace_bytes", "defrag_strerror", "defrag_commit",
               "defrag_move_status"):
         assert f in fns, f
@@ -106,6 +106,16 @@ def test_host_side_argument_errors_need_no_gpu():
                                   1 << 20, None, ctypes.byref(off_out),
                                   ctypes.byref(st)) == ac.DEFRAG_EINVAL
         assert off_out.value == (1 << 64) - 1 and st.invalid_reason == 6
+    # one-call compaction: missing arguments are refused on the host
+    assert L.defrag_compact(None, None, ctypes.byref(plan), None) == ac.DEFRAG_EINVAL
+    assert plan.stats.invalid_reason == 6
+    args = ac.defrag_compact_args()
+    args.n_handles = 5   # handles announced, no pointers
+    assert L.defrag_compact(ctypes.byref(args), None, ctypes.byref(plan), None) == ac.DEFRAG_EINVAL
+    args = ac.defrag_compact_args()   # no table: refused by the plan, on the host
+    assert L.defrag_compact(ctypes.byref(args), None, ctypes.byref(plan),
+                            ctypes.byref(st)) == ac.DEFRAG_EINVAL
+    assert L.defrag_compact(ctypes.byref(args), None, None, None) == ac.DEFRAG_EINVAL
     # bad tile size
     tu = ac.defrag_tuning(100, 0, 0, 0)
     assert L.defrag_plan(ctypes.byref(t), 4096, ctypes.byref(tu), ctypes.c_void_p(0x1000),

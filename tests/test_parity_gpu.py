@@ -344,3 +344,29 @@ def test_watchdog_turns_a_stalled_wait_into_an_error(ac):
     assert tripped, "no wait gave up in three moves of 262,145 chained tiles"
     del arena
     _full_check(heap)
+
+
+def test_remap_at_bucket_boundaries(ac):
+    """Blocks that start and end exactly on power-of-two boundaries, holes
+    that span many of them, and handles on every 4 KiB boundary and 16/32
+    bytes either side, in arenas whose size is and is not a power of two:
+    whatever bucket width the remap index picks, every handle matches the
+    oracle."""
+    KiB = 1 << 10
+    for S, blocks, live in (
+            (1 << 20, [(0, 32 * KiB), (64 * KiB, 64 * KiB), (256 * KiB, 4 * KiB),
+                       (260 * KiB, 128 * KiB), (512 * KiB, 32), (768 * KiB, 256 * KiB)],
+             [1, 0, 1, 1, 1, 1]),
+            ((1 << 20) + 96, [(32, 128 * KiB - 32), (128 * KiB, 128 * KiB), (640 * KiB, 32)],
+             [1, 1, 1]),
+            (3 << 20, [(1 << 20, 1 << 20)], [1])):
+        hs = []
+        for p in range(0, S + 8 * KiB, 4 * KiB):
+            for dlt in (-32, -16, 0, 16, 32):
+                if p + dlt >= 0:
+                    hs.append(p + dlt)
+        hs += [S - 1, S, (1 << 64) - 1]
+        heap = W.table_from_lists(S, blocks, live, hs, name=f"buckets S={S}")
+        r = _full_check(heap)
+        want, bad = oracle.remap(heap.offset, heap.size, heap.live, heap.handles)
+        assert np.array_equal(r.remapped, want) and r.n_invalid == bad
