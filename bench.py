@@ -273,7 +273,18 @@ def main() -> int:
         a0 = (refill_from // 8) * 8
         W.fill_payload(arena[a0:], a0, heap.payload_mode, heap.payload_seed)
 
+    def one_call(request=0):
+        # the whole step through one C-ABI call (defrag_compact)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        plan, post = ac.defrag_compact(off, size, live, S, arena, ws, request, new_off, h_in,
+                                       h_out, n_bad, c_off, c_size, c_live, c_pin, tuning=tuning,
+                                       stream=stream, pinned=pinned)
+        ev[1].record(stream)
+        return plan, post, ev
+
     def one_step():
+        # the same step through the separate calls, one event between each
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
         ev[0].record(stream)
         plan = ac.defrag_plan(off, size, live, S, ws, new_off, tuning=tuning, stream=stream,
@@ -296,11 +307,15 @@ def main() -> int:
         refill_from = int(plan.move_begin)
         print(f"# warmup {w} done", file=sys.stderr, flush=True)
 
-    times = {"step": [], "plan": [], "move": [], "remap": [], "post": []}
+    for w in range(args.warmup):
+        refill()
+        torch.cuda.synchronize()
+        one_call()
+    times = {"step": [], "one_call": [], "plan": [], "move": [], "remap": [], "post": []}
     torch.cuda.synchronize()
     t_wall0 = time.time()
     moved = None
-    for k in range(args.steps):
+    for k in range(args.steps):   # the timed steps, one event between each phase
         refill()
         torch.cuda.synchronize()
         plan, post, ev = one_step()
@@ -321,6 +336,14 @@ def main() -> int:
               file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     wall = time.time() - t_wall0
+    for k in range(args.steps):   # the same steps through defrag_compact, for comparison
+        refill()
+        torch.cuda.synchronize()
+        plan, post, ev = one_call()
+        torch.cuda.synchronize()
+        assert int(n_bad.item()) == 0 and int(plan.stats.moved_bytes) == moved
+        times["one_call"].append(ev[0].elapsed_time(ev[1]))
+    torch.cuda.synchronize()
     full_plan = plan
 
     # Targeted leg: the smallest move that frees one hole of the request.
@@ -329,7 +352,15 @@ def main() -> int:
         request = S * 42 // 800 if args.config in ("3", "3p") else 0
     targeted = None
     if request:
-        tt = {"step": [], "plan": [], "move": [], "remap": [], "post": []}
+        tt = {"step": [], "one_call": [], "plan": [], "move": [], "remap": [], "post": []}
+        for k in range(args.warmup + args.steps):
+            refill()
+            torch.cuda.synchronize()
+            tp, tpost, ev = one_call(request)
+            torch.cuda.synchronize()
+            assert tpost.largest_hole >= request and int(n_bad.item()) == 0
+            if k >= args.warmup:
+                tt["one_call"].append(ev[0].elapsed_time(ev[1]))
         for k in range(args.warmup + args.steps):
             refill()
             torch.cuda.synchronize()
