@@ -549,7 +549,8 @@ __device__ inline uint64_t tile_of(const LiveView &lv, const uint32_t *tile_base
 __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile_start,
                                                const uint32_t *tile_first,
                                                const uint32_t *tile_base, const WsHeader *hdr,
-                                               uint64_t max_tiles, uint64_t T, TileRec *tiles,
+                                               uint64_t max_tiles, uint64_t T,
+                                               const uint32_t *ridx, uint32_t w, TileRec *tiles,
                                                uint32_t *flags) {
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (plan_dead(hdr) || hdr->n_tiles > max_tiles) return;  // plan fails
@@ -570,8 +571,12 @@ __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile
         if (last + stride < m && lv.dst[last + stride] < bound && moved_at(lv, last + stride))
             last += stride;
     const uint64_t t1 = umin64(bound, lv.dst[last] + lv.size[last]);
-    // sources overlapping [t0, t1): first block whose source ends above t0 ...
-    int64_t lo = 0, hi = (int64_t)m;
+    // sources overlapping [t0, t1): first block whose source ends above t0.
+    // The remap index narrows it to the blocks starting in t0's bucket and
+    // the one before them: an earlier block ends before the bucket starts,
+    // and the first block of the next bucket already ends above t0.
+    const uint64_t bk = t0 >> w;
+    int64_t lo = ridx[bk] ? (int64_t)ridx[bk] - 1 : 0, hi = (int64_t)ridx[bk + 1];
     while (lo < hi) {
         const int64_t mid = lo + ((hi - lo) >> 1);
         if (lv.src[mid] + lv.size[mid] <= t0) lo = mid + 1;
@@ -794,6 +799,9 @@ void queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsL
                            hdr);
         hipLaunchKernelGGL(k_tcount_down, dim3((uint32_t)gnb), dim3(kScanThreads), 0, s, lv, hdr,
                            (uint64_t)tile_bytes, tprefix, tile_base);
+        // the remap's bucket index over old offsets; the tile records use it too
+        uint32_t *ridx = reinterpret_cast<uint32_t *>(ws + L.ridx);
+        launch_remap_index(lv.src, hdr, arena_bytes, t.n, ridx, s);
         // tile starts and records: a grid for the whole capacity, each lane
         // checks the device-side tile count (no host round trip)
         uint64_t *tile_start = reinterpret_cast<uint64_t *>(ws + L.tile_start);
@@ -805,11 +813,9 @@ void queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsL
             hipLaunchKernelGGL(k_tile_starts, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_base,
                                hdr, L.max_tiles, (uint64_t)tile_bytes, tile_start, tile_first);
             hipLaunchKernelGGL(k_tiles, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_start,
-                               tile_first, tile_base, hdr, L.max_tiles, (uint64_t)tile_bytes, tiles,
-                               flags);
+                               tile_first, tile_base, hdr, L.max_tiles, (uint64_t)tile_bytes,
+                               ridx, remap_shift(arena_bytes, t.n), tiles, flags);
         }
-        launch_remap_index(lv.src, hdr, arena_bytes, t.n, reinterpret_cast<uint32_t *>(ws + L.ridx),
-                           s);
     }
 }
 
