@@ -28,10 +28,11 @@
 // statistics, and a single-workgroup finish.  Then the mover's tiles: every
 // moved block counts the tiles that start inside it (a run of moved blocks
 // starts one, and so does every tile-size boundary inside a run); a scan of
-// those counts gives each block its first tile, and one lane per tile writes
-// the tile's start, its range, its blocks and its dependencies.  The whole
-// sequence is queued at once; the host reads the header back only at the
-// end.
+// those counts gives each block its first tile, the remap's bucket index
+// over old offsets is built (it also narrows the tiles' source searches),
+// and one lane per tile writes the tile's start, its range, its blocks and
+// its dependencies.  The whole sequence is queued at once; the host reads
+// the header back only at the end.
 #include "internal.h"
 
 namespace ac {
