@@ -8,7 +8,10 @@ One step = the whole hot path on one fragmented arena:
   commit + statistics of the packed table (one top hole, ratios 0).
 Before every step the arena is refilled to its pristine fragmented content on
 the GPU; the refill sits outside the timed events (inputs resident in HBM when
-a step starts).  Each step is timed with HIP events on the stream the library
+a step starts).  It is one device copy from a pristine snapshot kept in HBM:
+regenerating the payload with torch ops takes ~1,500 launches, after which
+the runtime's next calls ran 0.3-0.5 ms late on the host, a cost that
+belongs to the refill and not to the step (--regen-refill keeps that way).  Each step is timed with HIP events on the stream the library
 launches on; the mover launch has its own event pair, which gives the
 roofline figure.
 
@@ -206,6 +209,9 @@ def main() -> int:
                          "replaces -- every moved block copied in ascending order in waves of at "
                          "most its shift (one copy per wave, so no wave overlaps its own "
                          "source) -- against defrag_move on the same arena, and compare bytes")
+    ap.add_argument("--regen-refill", action="store_true",
+                    help="refill the arena before each step by regenerating the payload with "
+                         "torch ops instead of copying a pristine snapshot")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="GIB",
@@ -267,11 +273,24 @@ def main() -> int:
         return ablation_waves(args, heap, arena, off, size, live, pinned, ws, tuning)
     stream = torch.cuda.current_stream()
     refill_from = 0
+    snap = {"from": None, "bytes": None}   # pristine bytes [from, S), when they fit
 
     def refill():
         # bytes below the first destination are never written: refill the rest
         a0 = (refill_from // 8) * 8
-        W.fill_payload(arena[a0:], a0, heap.payload_mode, heap.payload_seed)
+        if not args.regen_refill and snap["from"] != a0:
+            snap["bytes"] = None
+            snap["from"] = a0
+            try:
+                t = torch.empty(S - a0, dtype=torch.uint8, device=dev)
+                W.fill_payload(t, a0, heap.payload_mode, heap.payload_seed)
+                snap["bytes"] = t
+            except torch.cuda.OutOfMemoryError:
+                torch.cuda.empty_cache()
+        if snap["bytes"] is not None:
+            arena[a0:].copy_(snap["bytes"])
+        else:
+            W.fill_payload(arena[a0:], a0, heap.payload_mode, heap.payload_seed)
 
     def one_call(request=0):
         # the whole step through one C-ABI call (defrag_compact)
@@ -453,6 +472,8 @@ def main() -> int:
         "median_move_ms": round(float(np.median(times["move"])), 4),
         "max_move_GBps": round(2 * moved / (float(np.min(times["move"])) * 1e-3) / 1e9, 2),
         "wall_s_incl_refill": round(wall, 3),
+        "refill": ("device copy of a pristine snapshot" if snap["bytes"] is not None
+                   else "payload regenerated with torch ops"),
         "before": {"free_bytes": int(s0.free_bytes), "largest_hole": int(s0.largest_hole),
                    "hole_count": int(s0.hole_count),
                    "frag_free_over_largest_minus_1": s0.frag_free_over_largest_minus_1,
