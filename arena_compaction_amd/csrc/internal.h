@@ -256,6 +256,15 @@ inline LiveView live_view(const uint8_t *ws, const WsLayout &L) {
                     reinterpret_cast<const uint8_t *>(ws + L.live_pin)};
 }
 
+// Return the first failing step: a kernel launch reports through the
+// thread's last-error state, so it is read after every launch, before a
+// later launch can replace it.
+#define AC_TRY(expr)                                    \
+    do {                                                \
+        const hipError_t ac_err_ = (expr);              \
+        if (ac_err_ != hipSuccess) return ac_err_;      \
+    } while (0)
+
 // ---- plan.hip ----
 // Scan passes and, with kOutNew, the mover's tiles (for at most
 // L.max_tiles tiles).  All asynchronous; the header then holds totals,

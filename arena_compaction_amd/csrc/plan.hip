@@ -760,7 +760,7 @@ namespace {
 
 // Scan passes, then (kOutNew) the tile passes.  win: the targeted plan's
 // window in the header, or null.
-void queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsLayout &L,
+hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsLayout &L,
                 uint64_t *new_offset, int outputs, const uint64_t *win, uint32_t tile_bytes,
                 uint64_t epoch, uint64_t fit_need, hipStream_t s) {
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.header);
@@ -778,15 +778,19 @@ void queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsL
     if (nb) {
         hipLaunchKernelGGL(k_scan_partials, dim3((uint32_t)nb), dim3(kScanThreads), 0, s, t,
                            arena_bytes, win, part);
+        AC_TRY(hipGetLastError());
     }
     hipLaunchKernelGGL(k_scan_spine, dim3(1), dim3(kSpineThreads), 0, s, part, prefix, nb, hdr,
                        win ? 0 : 1);
+    AC_TRY(hipGetLastError());
     if (nb) {
         hipLaunchKernelGGL(k_scan_down, dim3((uint32_t)nb), dim3(kScanThreads), 0, s, t, win,
                            prefix, hdr, new_offset, lo, spart, outputs, fit_need);
+        AC_TRY(hipGetLastError());
     }
     hipLaunchKernelGGL(k_scan_finish, dim3(1), dim3(kSpineThreads), 0, s, spart, nb, arena_bytes,
                        hdr, outputs, epoch, fit_need);
+    AC_TRY(hipGetLastError());
     if (outputs & kOutNew) {
         const LiveView lv = live_view(ws, L);
         uint64_t *tpart = reinterpret_cast<uint64_t *>(ws + L.tpart);
@@ -796,13 +800,16 @@ void queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsL
         const uint64_t gnb = nb ? nb : 1;  // live blocks <= entries
         hipLaunchKernelGGL(k_tcount_partials, dim3((uint32_t)gnb), dim3(kScanThreads), 0, s, lv,
                            hdr, (uint64_t)tile_bytes, tpart, twhole);
+        AC_TRY(hipGetLastError());
         hipLaunchKernelGGL(k_tcount_spine, dim3(1), dim3(kSpineThreads), 0, s, tpart, twhole, tprefix, gnb,
                            hdr);
+        AC_TRY(hipGetLastError());
         hipLaunchKernelGGL(k_tcount_down, dim3((uint32_t)gnb), dim3(kScanThreads), 0, s, lv, hdr,
                            (uint64_t)tile_bytes, tprefix, tile_base);
+        AC_TRY(hipGetLastError());
         // the remap's bucket index over old offsets; the tile records use it too
         uint32_t *ridx = reinterpret_cast<uint32_t *>(ws + L.ridx);
-        launch_remap_index(lv.src, hdr, arena_bytes, t.n, ridx, s);
+        AC_TRY(launch_remap_index(lv.src, hdr, arena_bytes, t.n, ridx, s));
         // tile starts and records: a grid for the whole capacity, each lane
         // checks the device-side tile count (no host round trip)
         uint64_t *tile_start = reinterpret_cast<uint64_t *>(ws + L.tile_start);
@@ -813,11 +820,14 @@ void queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsL
         if (grid) {
             hipLaunchKernelGGL(k_tile_starts, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_base,
                                hdr, L.max_tiles, (uint64_t)tile_bytes, tile_start, tile_first);
+            AC_TRY(hipGetLastError());
             hipLaunchKernelGGL(k_tiles, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_start,
                                tile_first, tile_base, hdr, L.max_tiles, (uint64_t)tile_bytes,
                                ridx, remap_shift(arena_bytes, t.n), tiles, flags);
+            AC_TRY(hipGetLastError());
         }
     }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -825,9 +835,8 @@ void queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsL
 hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsLayout &L,
                        uint64_t *new_offset, int outputs, uint32_t tile_bytes, uint64_t epoch,
                        uint64_t fit_need, hipStream_t s) {
-    queue_scan(t, arena_bytes, ws, L, new_offset, outputs, nullptr, tile_bytes, epoch, fit_need,
-               s);
-    return hipGetLastError();
+    return queue_scan(t, arena_bytes, ws, L, new_offset, outputs, nullptr, tile_bytes, epoch,
+                      fit_need, s);
 }
 
 hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t request,
@@ -839,15 +848,17 @@ hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t re
     const uint64_t *z = reinterpret_cast<const uint64_t *>(ws + L.live_z);
     const uint32_t *pc = reinterpret_cast<const uint32_t *>(ws + L.live_pc);
     SelPart *sp = reinterpret_cast<SelPart *>(ws + L.selpart);
-    queue_scan(t, arena_bytes, ws, L, nullptr, kOutSelect, nullptr, tile_bytes, epoch, kNone, s);
+    AC_TRY(queue_scan(t, arena_bytes, ws, L, nullptr, kOutSelect, nullptr, tile_bytes, epoch,
+                      kNone, s));
     // candidates: every last hole l in [0, m], m <= n
     hipLaunchKernelGGL(k_select, dim3((uint32_t)L.n_sel_blocks), dim3(kSelThreads), 0, s, src, z,
                        pc, hdr, arena_bytes, request, sp);
+    AC_TRY(hipGetLastError());
     hipLaunchKernelGGL(k_select_finish, dim3(1), dim3(kSpineThreads), 0, s, sp, L.n_sel_blocks,
                        src, size, z, arena_bytes, hdr);
-    queue_scan(t, arena_bytes, ws, L, new_offset, kOutNew, &hdr->win_begin, tile_bytes, epoch,
-               kNone, s);
-    return hipGetLastError();
+    AC_TRY(hipGetLastError());
+    return queue_scan(t, arena_bytes, ws, L, new_offset, kOutNew, &hdr->win_begin, tile_bytes,
+                      epoch, kNone, s);
 }
 
 hipError_t launch_commit(const uint8_t *ws, const WsLayout &L, uint64_t live_blocks,

@@ -110,8 +110,11 @@ hipError_t launch_remap(const LiveRec *rec, const uint64_t *live_src, const uint
                         uint64_t arena_bytes, uint64_t n, uint64_t live_blocks,
                         const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
                         uint64_t *n_invalid, int num_cus, hipStream_t s) {
-    if (n_invalid) hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, n_invalid);
-    if (n_handles == 0) return hipGetLastError();
+    if (n_invalid) {
+        hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, n_invalid);
+        AC_TRY(hipGetLastError());
+    }
+    if (n_handles == 0) return hipSuccess;
     uint64_t grid = (n_handles + kRemapThreads - 1) / kRemapThreads;
     const uint64_t cap = (uint64_t)num_cus * 2;  // measured best of 1, 2, 3, 4, 8, 16 per CU
     if (grid > cap) grid = cap;

@@ -105,6 +105,62 @@ def test_tiny_shift_under_large_blocks(ac):
         _full_check(heap, _tuning(ac, tile))
 
 
+def _chained_heap(tile, lead=0):
+    """Live blocks above holes of one tile, one tile + 32 B, two tiles - 32 B
+    and three tiles + 32 B (after an optional unmoved live block of `lead`
+    bytes): every moved block's source starts at least one tile above its
+    destination, and each tile's destination overlaps the source of a tile
+    one to three below it."""
+    MiB = 1 << 20
+    blocks, live, at = [], [], 0
+    if lead:
+        blocks.append((0, lead)); live.append(1); at = lead
+    for hole, n in ((tile, 8 * MiB), (tile + 32, 4 * MiB), (2 * tile - 32, 6 * MiB),
+                    (3 * tile + 32, 5 * MiB)):
+        blocks.append((at, hole)); live.append(0); at += hole
+        blocks.append((at, n)); live.append(1); at += n
+    handles = [b[0] + d for b, lv in zip(blocks, live) if lv for d in (0, 4096, b[1] - 1)]
+    return W.table_from_lists(at + 4096, blocks, live, handles,
+                              name=f"chained tile {tile} lead {lead}")
+
+
+def test_chained_whole_tiles_without_self_overlap(ac):
+    """Whole single-block tiles (the straight-line path) whose source lies at
+    least one tile above their destination, each waiting on a tile just below
+    it.  With an unmoved 96-byte block first, each block's first and last
+    tiles are partial (the general path) and the whole tiles next to them
+    wait on them, and the other way round."""
+    for tile in (4096, 65536):
+        for lead in (0, 96):
+            heap = _chained_heap(tile, lead)
+            r = _full_check(heap, _tuning(ac, tile))
+            if lead == 0:
+                assert r.plan.whole_tiles == r.plan.n_tiles, (r.plan.whole_tiles, r.plan.n_tiles)
+            else:
+                assert 0 < r.plan.whole_tiles < r.plan.n_tiles
+            _full_check(heap, _tuning(ac, tile, 1, 1))
+    _full_check(_chained_heap(65536, 96))   # library defaults
+
+
+def test_watchdog_on_chained_whole_tiles_ends_every_wave(ac):
+    """A spin limit of two polls on chained whole tiles: whether or not a
+    wait gives up, the move returns a status, and the library is bit-exact
+    afterwards with the default limit."""
+    heap = _chained_heap(4096)
+    off, size, live = device_table(heap, "cuda")
+    arena = torch.zeros(heap.arena_bytes, dtype=torch.uint8, device="cuda")
+    for attempt in range(3):
+        log(f"case whole-tile watchdog attempt {attempt}: {heap.describe()} tile 4096, spin limit 2")
+        ws = ac.workspace(heap.n, heap.arena_bytes, 4096)
+        plan = ac.defrag_plan(off, size, live, heap.arena_bytes, ws,
+                              tuning=ac.defrag_tuning(4096, 1, 1, 1))
+        assert plan.whole_tiles == plan.n_tiles
+        ac.defrag_move(arena, plan, ws)
+        assert ac.defrag_move_status(plan, ws) in (ac.DEFRAG_OK, ac.DEFRAG_ETIMEOUT)
+    del arena
+    _full_check(heap, _tuning(ac, 4096, 1, 1))
+
+
 def test_edge_cases_gpu(ac):
     cases = [
         W.table_from_lists(4096, [], [], [0, 5, 4096]),                    # n = 0
