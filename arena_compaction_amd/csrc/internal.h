@@ -133,15 +133,15 @@ struct alignas(16) TileRec {
 };
 static_assert(sizeof(TileRec) == 48, "tile record size");
 
-// One live block as the handle remap reads it: one aligned 32-byte record,
-// so the block holding a handle costs one cache-line request.
-struct alignas(32) LiveRec {
-    uint64_t src;   // old offset
-    uint64_t size;
-    uint64_t dst;   // new offset
-    uint64_t pad;
+// One live block as the handle remap reads it, once its search has found
+// the last block starting at or below a handle h: h lies in it iff h < end,
+// and then maps to h - shift.  16 bytes, so the records of the 80 GiB
+// workload (183k blocks) take 2.9 MB of L2 / last-level cache.
+struct alignas(16) LiveRec {
+    uint64_t end;    // old offset + size
+    uint64_t shift;  // old offset - new offset (0 for a block that stays)
 };
-static_assert(sizeof(LiveRec) == 32, "live record size");
+static_assert(sizeof(LiveRec) == 16, "live record size");
 
 // Remap index: the arena is cut into buckets of 2^w bytes, at most
 // remap_bucket_cap(n) of them, and ridx[b] counts the live blocks starting

@@ -261,7 +261,7 @@ struct LiveOut {
     uint8_t *pin;
     uint64_t *z;   // live bytes below each live block (selection only)
     uint32_t *pc;  // pinned blocks below each live block (selection only)
-    LiveRec *rec;  // the remap's copy of (old offset, size, new offset)
+    LiveRec *rec;  // the remap's (old end, shift) per live block
 };
 
 // Pass 3: new offsets, packed live arrays, per-workgroup hole/move stats.
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
                 if (outputs & kOutNew) {
                     lo.dst[run.cnt] = nw;
                     lo.pin[run.cnt] = (uint8_t)p[k];
-                    lo.rec[run.cnt] = LiveRec{o[k], s[k], nw, 0};
+                    lo.rec[run.cnt] = LiveRec{o[k] + s[k], o[k] - nw};
                 }
                 if (outputs & (kOutNew | kOutSelect)) {
                     lo.src[run.cnt] = o[k];

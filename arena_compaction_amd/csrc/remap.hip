@@ -15,8 +15,8 @@
 // probe of each lane is its own cache line), so the plan builds an index --
 // the arena cut into at most 2^18 power-of-two buckets, each pointing at the
 // first live block starting in it -- and each live block also has one
-// 32-byte record (old offset, size, new offset).  HBM traffic is 16 B per
-// handle; the index, offsets and records stay in L2 / the last-level cache.
+// 16-byte record (old end, shift).  HBM traffic is 16 B per handle; the
+// index, old offsets and records stay in L2 / the last-level cache.
 #include "internal.h"
 
 namespace ac {
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void k_remap_index(const uint64_t *__restrict_
 // One lane per handle, grid-stride.  The bucket of h gives the live blocks
 // starting in it, [ridx[b], ridx[b+1]); the block holding h, if any, is the
 // last one starting at or below h, so it is found by a short search inside
-// the bucket (or is the block before it), and its record is one 32-byte
+// the bucket (or is the block before it), and its record is one 16-byte
 // read.  A random handle costs about three dependent cache-line requests:
 // the index pair, a probe or two, the record.
 __global__ __launch_bounds__(kRemapThreads) void k_remap(const LiveRec *__restrict__ rec,
@@ -77,8 +77,8 @@ __global__ __launch_bounds__(kRemapThreads) void k_remap(const LiveRec *__restri
                 }
             }
             if (first > 0) {
-                const LiveRec r = rec[first - 1];
-                if (h - r.src < r.size) out = r.dst + (h - r.src);
+                const LiveRec r = rec[first - 1];  // starts at or below h
+                if (h < r.end) out = h - r.shift;
             }
         }
         bad += (out == kNone) ? 1u : 0u;
