@@ -160,6 +160,13 @@ inline uint32_t remap_shift(uint64_t arena_bytes, uint64_t n) {
 inline uint64_t remap_buckets(uint64_t arena_bytes, uint64_t n) {
     return (arena_bytes >> remap_shift(arena_bytes, n)) + 1;
 }
+// With buckets of at most 2^32 bytes the search inside a bucket compares
+// 32-bit keys, each live block's old offset inside its bucket, instead of
+// the 64-bit offsets: half the bytes per probe.  Wider buckets (a tiny
+// table in an arena above 2^35 bytes) search the 64-bit offsets.
+inline bool remap_keys32(uint64_t arena_bytes, uint64_t n) {
+    return remap_shift(arena_bytes, n) <= 32;
+}
 
 constexpr size_t kPerTileBytes =
     sizeof(uint64_t) + sizeof(uint32_t) + sizeof(TileRec) + sizeof(uint32_t);
@@ -167,7 +174,7 @@ constexpr size_t kPerTileBytes =
 struct WsLayout {
     // fixed part (depends on n only)
     size_t header, part, prefix, spart, tpart, twhole, tprefix, live_dst, live_src, live_size,
-        live_pin, tile_base, live_z, live_pc, selpart, live_rec, ridx, fixed;
+        live_pin, tile_base, live_z, live_pc, selpart, live_rec, live_key, ridx, fixed;
     // tile part (depends on the tile capacity)
     size_t tile_start, tile_first, tiles, flags, total;
     uint64_t n_scan_blocks, n_sel_blocks, max_tiles;
@@ -197,6 +204,7 @@ inline WsLayout ws_fixed(uint64_t n) {
     L.live_pc = at;   at += align256((n + 1) * sizeof(uint32_t));
     L.selpart = at;   at += align256(L.n_sel_blocks * sizeof(SelPart));
     L.live_rec = at;  at += align256((n + 1) * sizeof(LiveRec));
+    L.live_key = at;  at += align256((n + 1) * sizeof(uint32_t));
     L.ridx = at;      at += align256((remap_bucket_cap(n) + 2) * sizeof(uint32_t));
     L.fixed = at;
     return L;
@@ -305,7 +313,8 @@ hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, uint32_t nontempor
 // the header, nothing written if the plan failed).
 hipError_t launch_remap_index(const uint64_t *live_src, const WsHeader *hdr, uint64_t arena_bytes,
                               uint64_t n, uint32_t *ridx, hipStream_t s);
-hipError_t launch_remap(const LiveRec *rec, const uint64_t *live_src, const uint32_t *ridx,
+hipError_t launch_remap(const LiveRec *rec, const uint64_t *live_src, const uint32_t *key,
+                        const uint32_t *ridx,
                         uint64_t arena_bytes, uint64_t n, uint64_t live_blocks,
                         const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
                         uint64_t *n_invalid, int num_cus, hipStream_t s);

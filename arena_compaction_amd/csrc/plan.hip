@@ -262,6 +262,8 @@ struct LiveOut {
     uint64_t *z;   // live bytes below each live block (selection only)
     uint32_t *pc;  // pinned blocks below each live block (selection only)
     LiveRec *rec;  // the remap's (old end, shift) per live block
+    uint32_t *key;      // the remap's 32-bit search keys (null: 64-bit offsets)
+    uint64_t key_mask;  // old offset -> offset inside its remap bucket
 };
 
 // Pass 3: new offsets, packed live arrays, per-workgroup hole/move stats.
@@ -311,6 +313,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
                     lo.dst[run.cnt] = nw;
                     lo.pin[run.cnt] = (uint8_t)p[k];
                     lo.rec[run.cnt] = LiveRec{o[k] + s[k], o[k] - nw};
+                    if (lo.key) lo.key[run.cnt] = (uint32_t)(o[k] & lo.key_mask);
                 }
                 if (outputs & (kOutNew | kOutSelect)) {
                     lo.src[run.cnt] = o[k];
@@ -773,7 +776,11 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
                reinterpret_cast<uint8_t *>(ws + L.live_pin),
                reinterpret_cast<uint64_t *>(ws + L.live_z),
                reinterpret_cast<uint32_t *>(ws + L.live_pc),
-               reinterpret_cast<LiveRec *>(ws + L.live_rec)};
+               reinterpret_cast<LiveRec *>(ws + L.live_rec), nullptr, 0};
+    if (remap_keys32(arena_bytes, t.n)) {
+        lo.key = reinterpret_cast<uint32_t *>(ws + L.live_key);
+        lo.key_mask = (1ull << remap_shift(arena_bytes, t.n)) - 1;
+    }
     const uint64_t nb = L.n_scan_blocks;
     if (nb) {
         hipLaunchKernelGGL(k_scan_partials, dim3((uint32_t)nb), dim3(kScanThreads), 0, s, t,

@@ -15,8 +15,9 @@
 // probe of each lane is its own cache line), so the plan builds an index --
 // the arena cut into at most 2^18 power-of-two buckets, each pointing at the
 // first live block starting in it -- and each live block also has one
-// 16-byte record (old end, shift).  HBM traffic is 16 B per handle; the
-// index, old offsets and records stay in L2 / the last-level cache.
+// 16-byte record (old end, shift) and a 32-bit search key (its old offset
+// inside its bucket).  HBM traffic is 16 B per handle; the index, keys and
+// records stay in L2 / the last-level cache.
 #include "internal.h"
 
 namespace ac {
@@ -52,9 +53,10 @@ __global__ __launch_bounds__(256) void k_remap_index(const uint64_t *__restrict_
 // last one starting at or below h, so it is found by a short search inside
 // the bucket (or is the block before it), and its record is one 16-byte
 // read.  A random handle costs about three dependent cache-line requests:
-// the index pair, a probe or two, the record.
+// the index pair, a probe or two over the bucket's keys, the record.
 __global__ __launch_bounds__(kRemapThreads) void k_remap(const LiveRec *__restrict__ rec,
                                                          const uint64_t *__restrict__ live_src,
+                                                         const uint32_t *__restrict__ key,
                                                          const uint32_t *__restrict__ ridx,
                                                          uint32_t w, uint64_t nb, uint64_t m,
                                                          const uint64_t *h_in, uint64_t *h_out,
@@ -67,13 +69,26 @@ __global__ __launch_bounds__(kRemapThreads) void k_remap(const LiveRec *__restri
         const uint64_t b = h >> w;
         if (m && b < nb) {
             uint64_t first = ridx[b], len = ridx[b + 1] - first;  // first with src > h
-            while (len > 0) {
-                const uint64_t half = len >> 1;
-                if (live_src[first + half] <= h) {
-                    first += half + 1;
-                    len -= half + 1;
-                } else {
-                    len = half;
+            if (key) {  // offsets inside the bucket, as 32-bit keys
+                const uint32_t hk = (uint32_t)(h & ((1ull << w) - 1));
+                while (len > 0) {
+                    const uint64_t half = len >> 1;
+                    if (key[first + half] <= hk) {
+                        first += half + 1;
+                        len -= half + 1;
+                    } else {
+                        len = half;
+                    }
+                }
+            } else {
+                while (len > 0) {
+                    const uint64_t half = len >> 1;
+                    if (live_src[first + half] <= h) {
+                        first += half + 1;
+                        len -= half + 1;
+                    } else {
+                        len = half;
+                    }
                 }
             }
             if (first > 0) {
@@ -106,7 +121,8 @@ hipError_t launch_remap_index(const uint64_t *live_src, const WsHeader *hdr, uin
     return hipGetLastError();
 }
 
-hipError_t launch_remap(const LiveRec *rec, const uint64_t *live_src, const uint32_t *ridx,
+hipError_t launch_remap(const LiveRec *rec, const uint64_t *live_src, const uint32_t *key,
+                        const uint32_t *ridx,
                         uint64_t arena_bytes, uint64_t n, uint64_t live_blocks,
                         const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
                         uint64_t *n_invalid, int num_cus, hipStream_t s) {
@@ -119,7 +135,7 @@ hipError_t launch_remap(const LiveRec *rec, const uint64_t *live_src, const uint
     const uint64_t cap = (uint64_t)num_cus * 2;  // measured best of 1, 2, 3, 4, 8, 16 per CU
     if (grid > cap) grid = cap;
     hipLaunchKernelGGL(k_remap, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s, rec, live_src,
-                       ridx, remap_shift(arena_bytes, n), remap_buckets(arena_bytes, n),
+                       remap_keys32(arena_bytes, n) ? key : nullptr, ridx, remap_shift(arena_bytes, n), remap_buckets(arena_bytes, n),
                        live_blocks, h_in, h_out, n_handles,
                        reinterpret_cast<unsigned long long *>(n_invalid));
     return hipGetLastError();

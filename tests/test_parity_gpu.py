@@ -402,6 +402,38 @@ def test_watchdog_turns_a_stalled_wait_into_an_error(ac):
     _full_check(heap)
 
 
+def test_remap_in_huge_arenas_with_tiny_tables(ac):
+    """A table of a few blocks in an arena of 2^35, 2^36 + 4 KiB and 2^40
+    bytes: the remap's buckets are 2^32, 2^33 and 2^37 bytes wide, so its
+    in-bucket search runs on 32-bit keys at the widest bucket they allow,
+    and on 64-bit offsets above it.  Plan and remap only (neither reads the
+    arena); every handle matches the oracle."""
+    GiB = 1 << 30
+    for S in (1 << 35, (1 << 36) + 4096, 1 << 40):
+        blocks = [(0, 4096), (GiB, 1 << 20), ((1 << 32) - 4096, 8192), ((1 << 32) + 4096, 4096),
+                  (S // 2, 64 * GiB if S >= (1 << 40) else 32), (S - 4096, 4096)]
+        live = [0, 1, 1, 1, 1, 1]
+        hs = []
+        for o_, sz in blocks:
+            for p in (o_, o_ + sz - 1, o_ + sz, o_ + sz // 2):
+                for dlt in (-32, -1, 0, 1, 32):
+                    if 0 <= p + dlt:
+                        hs.append(p + dlt)
+        hs += [S - 1, S, (1 << 32) - 1, 1 << 32, (1 << 64) - 1]
+        heap = W.table_from_lists(S, blocks, live, hs, name=f"huge S={S}")
+        log(f"case {heap.describe()} remap only")
+        off, size, lv = device_table(heap, "cuda")
+        ws = ac.workspace(heap.n, S, 131072)
+        plan = ac.defrag_plan(off, size, lv, S, ws, tuning=ac.defrag_tuning(131072, 0, 1, 0))
+        h = torch.from_numpy(heap.handles.view(np.int64)).cuda()
+        nb = torch.zeros(1, dtype=torch.int64, device="cuda")
+        out = ac.defrag_remap(plan, ws, h, n_invalid=nb)
+        torch.cuda.synchronize()
+        want, bad = oracle.remap(heap.offset, heap.size, heap.live, heap.handles)
+        assert np.array_equal(out.cpu().numpy().view(np.uint64), want) and int(nb) == bad
+        del ws
+
+
 def test_remap_at_bucket_boundaries(ac):
     """Blocks that start and end exactly on power-of-two boundaries, holes
     that span many of them, and handles on every 4 KiB boundary and 16/32
