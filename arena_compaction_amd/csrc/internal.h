@@ -309,10 +309,6 @@ hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, uint32_t nontempor
                        int num_cus, hipStream_t s);
 
 // ---- remap.hip ----
-// The remap index of a plan (queued behind its scan; live-block count from
-// the header, nothing written if the plan failed).
-hipError_t launch_remap_index(const uint64_t *live_src, const WsHeader *hdr, uint64_t arena_bytes,
-                              uint64_t n, uint32_t *ridx, hipStream_t s);
 hipError_t launch_remap(const LiveRec *rec, const uint64_t *live_src, const uint32_t *key,
                         const uint32_t *ridx,
                         uint64_t arena_bytes, uint64_t n, uint64_t live_blocks,

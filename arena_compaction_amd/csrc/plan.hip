@@ -27,12 +27,13 @@
 // arrays (new and old offset, size, pinned flag) and per-workgroup
 // statistics, and a single-workgroup finish.  Then the mover's tiles: every
 // moved block counts the tiles that start inside it (a run of moved blocks
-// starts one, and so does every tile-size boundary inside a run); a scan of
-// those counts gives each block its first tile, the remap's bucket index
-// over old offsets is built (it also narrows the tiles' source searches),
-// and one lane per tile writes the tile's start, its range, its blocks and
-// its dependencies.  The whole sequence is queued at once; the host reads
-// the header back only at the end.
+// starts one, and so does every tile-size boundary inside a run), and the
+// remap's bucket index over old offsets is built (it also narrows the tiles'
+// source searches) -- in a plan the finish, these counts and the index share
+// one launch, as each reads only what the scan wrote; a scan of the counts
+// gives each block its first tile, and one lane per tile writes the tile's
+// start, its range, its blocks and its dependencies.  The whole sequence is
+// queued at once; the host reads the header back only at the end.
 #include "internal.h"
 
 namespace ac {
@@ -351,11 +352,11 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
             StatPart{max_gap, gaps, moved, moved_bytes, min_dst, min_size, min_fit, 0};
 }
 
-// Pass 4 (one workgroup): reduce the statistics, add the tail hole.
-__global__ __launch_bounds__(kSpineThreads) void k_scan_finish(const StatPart *spart, uint64_t nb,
-                                                               uint64_t arena_bytes, WsHeader *hdr,
-                                                               int outputs, uint64_t epoch,
-                                                               uint64_t fit_need) {
+// Pass 4 (one workgroup): reduce the statistics, add the tail hole.  A plan
+// runs it inside the launch after the scan (k_after_scan); a statistics pass
+// alone launches it by itself.
+__device__ void scan_finish(const StatPart *spart, uint64_t nb, uint64_t arena_bytes,
+                            WsHeader *hdr, int outputs, uint64_t epoch, uint64_t fit_need) {
     __shared__ uint64_t sh[kSpineThreads / 64];
     if (plan_dead(hdr)) return;
     uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, min_dst = kNone, min_size = kNone;
@@ -397,6 +398,13 @@ __global__ __launch_bounds__(kSpineThreads) void k_scan_finish(const StatPart *s
     }
 }
 
+__global__ __launch_bounds__(kSpineThreads) void k_scan_finish(const StatPart *spart, uint64_t nb,
+                                                               uint64_t arena_bytes, WsHeader *hdr,
+                                                               int outputs, uint64_t epoch,
+                                                               uint64_t fit_need) {
+    scan_finish(spart, nb, arena_bytes, hdr, outputs, epoch, fit_need);
+}
+
 // ---------------------------------------------------------------------------
 // Tiles.  A run is a maximal sequence of moved live blocks; its destinations
 // are contiguous (packed inside one segment).  Its tiles are the pieces of it
@@ -424,14 +432,13 @@ __device__ inline uint64_t whole_in_block(const LiveView &lv, uint64_t k, uint64
 }
 
 // Pass 5: per-workgroup tile counts (and whole-window counts) over the live
-// blocks.
-__global__ __launch_bounds__(kScanThreads) void k_tcount_partials(LiveView lv, const WsHeader *hdr,
-                                                                  uint64_t T, uint64_t *tpart,
-                                                                  uint64_t *twhole) {
+// blocks; workgroup blk covers live blocks [blk * kScanTile, ...).
+__device__ void tcount_partial(LiveView lv, const WsHeader *hdr, uint64_t T, uint64_t *tpart,
+                               uint64_t *twhole, uint64_t blk) {
     __shared__ uint64_t sh[kScanThreads / 64];
     if (plan_dead(hdr)) return;
     const uint64_t m = hdr->live_blocks;
-    const uint64_t k0 = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanItems;
+    const uint64_t k0 = blk * kScanTile + (uint64_t)threadIdx.x * kScanItems;
     uint64_t c = 0, w = 0;
 #pragma unroll
     for (uint32_t j = 0; j < kScanItems; ++j) {
@@ -443,8 +450,63 @@ __global__ __launch_bounds__(kScanThreads) void k_tcount_partials(LiveView lv, c
     c = block_reduce<kScanThreads>(c, sh, OpAdd());
     w = block_reduce<kScanThreads>(w, sh, OpAdd());
     if (threadIdx.x == 0) {
-        tpart[blockIdx.x] = c;
-        twhole[blockIdx.x] = w;
+        tpart[blk] = c;
+        twhole[blk] = w;
+    }
+}
+
+// The remap's bucket index: ridx[b] = number of live blocks whose old offset
+// is below b << w, for b in [0, nb]; one lane per entry, a binary search over
+// the packed old offsets (workgroup blk covers entries [256 blk, ...)).  A
+// failed plan leaves it alone.
+__device__ void remap_index_part(const uint64_t *__restrict__ live_src, const WsHeader *hdr,
+                                 uint32_t w, uint64_t nb, uint32_t *ridx, uint64_t blk) {
+    const uint64_t b = blk * kScanThreads + threadIdx.x;
+    if (b > nb || plan_dead(hdr)) return;
+    const uint64_t m = hdr->live_blocks;
+    const uint64_t x = b << w;
+    uint64_t lo = 0, len = m;  // first k with src[k] >= x
+    while (len > 0) {
+        const uint64_t half = len >> 1;
+        if (live_src[lo + half] < x) {
+            lo += half + 1;
+            len -= half + 1;
+        } else {
+            len = half;
+        }
+    }
+    ridx[b] = (uint32_t)lo;
+}
+
+// After a plan's scan, three jobs that read only what the scan wrote and
+// write disjoint outputs, in one launch (two dependent launches fewer):
+// workgroups [0, gnb) count tiles (pass 5), the next rblocks build the
+// remap index, and the last one reduces the statistics (pass 4).
+struct AfterScan {
+    LiveView lv;
+    uint64_t tile_bytes;
+    uint64_t *tpart, *twhole;
+    uint64_t gnb;
+    uint32_t *ridx;
+    uint32_t rw;        // remap bucket width (log2 bytes)
+    uint64_t rnb;       // remap buckets
+    uint64_t rblocks;   // workgroups building the index
+    const StatPart *spart;
+    uint64_t nb;        // scan workgroups
+    uint64_t arena_bytes;
+    int outputs;
+    uint64_t epoch;
+    uint64_t fit_need;
+};
+static_assert(kSpineThreads == kScanThreads, "the finish runs as one workgroup of the fused launch");
+__global__ __launch_bounds__(kScanThreads) void k_after_scan(AfterScan a, WsHeader *hdr) {
+    const uint64_t blk = blockIdx.x;
+    if (blk < a.gnb) {
+        tcount_partial(a.lv, hdr, a.tile_bytes, a.tpart, a.twhole, blk);
+    } else if (blk < a.gnb + a.rblocks) {
+        remap_index_part(a.lv.src, hdr, a.rw, a.rnb, a.ridx, blk - a.gnb);
+    } else {
+        scan_finish(a.spart, a.nb, a.arena_bytes, hdr, a.outputs, a.epoch, a.fit_need);
     }
 }
 
@@ -795,9 +857,11 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
                            prefix, hdr, new_offset, lo, spart, outputs, fit_need);
         AC_TRY(hipGetLastError());
     }
-    hipLaunchKernelGGL(k_scan_finish, dim3(1), dim3(kSpineThreads), 0, s, spart, nb, arena_bytes,
-                       hdr, outputs, epoch, fit_need);
-    AC_TRY(hipGetLastError());
+    if (!(outputs & kOutNew)) {
+        hipLaunchKernelGGL(k_scan_finish, dim3(1), dim3(kSpineThreads), 0, s, spart, nb,
+                           arena_bytes, hdr, outputs, epoch, fit_need);
+        AC_TRY(hipGetLastError());
+    }
     if (outputs & kOutNew) {
         const LiveView lv = live_view(ws, L);
         uint64_t *tpart = reinterpret_cast<uint64_t *>(ws + L.tpart);
@@ -805,8 +869,27 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
         uint64_t *twhole = reinterpret_cast<uint64_t *>(ws + L.twhole);
         uint32_t *tile_base = reinterpret_cast<uint32_t *>(ws + L.tile_base);
         const uint64_t gnb = nb ? nb : 1;  // live blocks <= entries
-        hipLaunchKernelGGL(k_tcount_partials, dim3((uint32_t)gnb), dim3(kScanThreads), 0, s, lv,
-                           hdr, (uint64_t)tile_bytes, tpart, twhole);
+        // tile counts, the remap's bucket index (the tile records use it
+        // too) and the statistics finish, in one launch
+        uint32_t *ridx = reinterpret_cast<uint32_t *>(ws + L.ridx);
+        AfterScan as{};
+        as.lv = lv;
+        as.tile_bytes = tile_bytes;
+        as.tpart = tpart;
+        as.twhole = twhole;
+        as.gnb = gnb;
+        as.ridx = ridx;
+        as.rw = remap_shift(arena_bytes, t.n);
+        as.rnb = remap_buckets(arena_bytes, t.n);
+        as.rblocks = (as.rnb + 1 + kScanThreads - 1) / kScanThreads;
+        as.spart = spart;
+        as.nb = nb;
+        as.arena_bytes = arena_bytes;
+        as.outputs = outputs;
+        as.epoch = epoch;
+        as.fit_need = fit_need;
+        hipLaunchKernelGGL(k_after_scan, dim3((uint32_t)(gnb + as.rblocks + 1)),
+                           dim3(kScanThreads), 0, s, as, hdr);
         AC_TRY(hipGetLastError());
         hipLaunchKernelGGL(k_tcount_spine, dim3(1), dim3(kSpineThreads), 0, s, tpart, twhole, tprefix, gnb,
                            hdr);
@@ -814,9 +897,6 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
         hipLaunchKernelGGL(k_tcount_down, dim3((uint32_t)gnb), dim3(kScanThreads), 0, s, lv, hdr,
                            (uint64_t)tile_bytes, tprefix, tile_base);
         AC_TRY(hipGetLastError());
-        // the remap's bucket index over old offsets; the tile records use it too
-        uint32_t *ridx = reinterpret_cast<uint32_t *>(ws + L.ridx);
-        AC_TRY(launch_remap_index(lv.src, hdr, arena_bytes, t.n, ridx, s));
         // tile starts and records: a grid for the whole capacity, each lane
         // checks the device-side tile count (no host round trip)
         uint64_t *tile_start = reinterpret_cast<uint64_t *>(ws + L.tile_start);

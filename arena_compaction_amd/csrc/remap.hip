@@ -25,29 +25,6 @@ namespace {
 
 constexpr uint32_t kRemapThreads = 256;
 
-// Index: ridx[b] = number of live blocks whose old offset is below b << w,
-// for b in [0, nb]; one lane per entry, a binary search over the packed old
-// offsets.  A failed plan leaves it alone (its blocks are not written).
-__global__ __launch_bounds__(256) void k_remap_index(const uint64_t *__restrict__ live_src,
-                                                     const WsHeader *hdr, uint32_t w, uint64_t nb,
-                                                     uint32_t *ridx) {
-    const uint64_t b = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (b > nb || hdr->bad_key != kNone || hdr->win_state == kWinNoFit) return;
-    const uint64_t m = hdr->live_blocks;
-    const uint64_t x = b << w;
-    uint64_t lo = 0, len = m;  // first k with src[k] >= x
-    while (len > 0) {
-        const uint64_t half = len >> 1;
-        if (live_src[lo + half] < x) {
-            lo += half + 1;
-            len -= half + 1;
-        } else {
-            len = half;
-        }
-    }
-    ridx[b] = (uint32_t)lo;
-}
-
 // One lane per handle, grid-stride.  The bucket of h gives the live blocks
 // starting in it, [ridx[b], ridx[b+1]); the block holding h, if any, is the
 // last one starting at or below h, so it is found by a short search inside
@@ -111,15 +88,6 @@ __global__ void k_zero_u64(uint64_t *p) {
 }
 
 }  // namespace
-
-hipError_t launch_remap_index(const uint64_t *live_src, const WsHeader *hdr, uint64_t arena_bytes,
-                              uint64_t n, uint32_t *ridx, hipStream_t s) {
-    const uint32_t w = remap_shift(arena_bytes, n);
-    const uint64_t nb = remap_buckets(arena_bytes, n);
-    hipLaunchKernelGGL(k_remap_index, dim3((uint32_t)((nb + 1 + 255) / 256)), dim3(256), 0, s,
-                       live_src, hdr, w, nb, ridx);
-    return hipGetLastError();
-}
 
 hipError_t launch_remap(const LiveRec *rec, const uint64_t *live_src, const uint32_t *key,
                         const uint32_t *ridx,
