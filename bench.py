@@ -408,6 +408,15 @@ def main() -> int:
         # and what the layout monitor says about each state
         ff_before, st_before = ac.defrag_first_fit(off, size, live, S, request, ws, pinned=pinned)
         ff_after, _ = ac.defrag_first_fit(c_off, c_size, c_live, S, request, ws, pinned=c_pin)
+        ff_ms = []   # first fit on the fragmented table: one statistics pass, one read-back
+        for k in range(args.warmup + args.steps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            ac.defrag_first_fit(off, size, live, S, request, ws, stream=stream, pinned=pinned)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            if k >= args.warmup:
+                ff_ms.append(ev[0].elapsed_time(ev[1]))
         mon_before = ac.defrag_monitor(st_before, next_request=request)
         mon_after = ac.defrag_monitor(tpost, next_request=request)
         targeted = {
@@ -422,6 +431,7 @@ def main() -> int:
             "after_largest_hole": int(tpost.largest_hole),
             "first_fit_before": ff_before,
             "first_fit_after": ff_after,
+            "first_fit_ms": round(float(np.mean(ff_ms)), 4),
             "monitor_before": {"level": ac.LEVELS[mon_before.level],
                                "action": ac.ACTIONS[mon_before.action]},
             "monitor_after": {"level": ac.LEVELS[mon_after.level],
