@@ -82,6 +82,26 @@ def test_random_tiny_heaps_gpu(ac, tile):
         _full_check(heap, _tuning(ac, tile))
 
 
+def test_random_medium_heaps_default_tuning(ac):
+    """Eight seeded heaps of 500-4,000 blocks with sizes log-uniform from 32 B
+    to 1 MiB (so shifts range from 32 bytes to many tiles, and tiles mix
+    whole single-block windows with many-block ones), varied live, gap and
+    pinned fractions, compacted with the library's default tuning (the
+    workgroup count the plan picks): every byte, offset and handle against
+    the oracle."""
+    rng = np.random.default_rng(4242)
+    sizes = np.unique((np.exp(rng.uniform(np.log(32), np.log(1 << 20), 96)) // 32 * 32)
+                      .astype(np.int64).clip(32))
+    for k in range(8):
+        n = int(rng.integers(500, 4001))
+        heap = W.tiny_heap(rng, n, sizes=tuple(int(x) for x in sizes),
+                           gap_p=float(rng.choice([0.0, 0.2, 0.6])),
+                           live_p=float(rng.choice([0.3, 0.6, 0.9])),
+                           pinned_p=float(rng.choice([0.0, 0.0, 0.02, 0.2])))
+        r = _full_check(heap)
+        log(f"  tiles {r.plan.n_tiles}, whole {r.plan.whole_tiles}, wg/cu {r.plan.tuning.wg_per_cu}")
+
+
 @pytest.mark.parametrize("k", [1, 2, 3, "3p", 4, 5])
 @pytest.mark.parametrize("tile,nt", [(256, 0), (4096, 1), (65536, 0), (65536, 1), (131072, 0)])
 def test_small_configs_gpu(ac, k, tile, nt):
