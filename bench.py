@@ -15,7 +15,8 @@ belongs to the refill and not to the step (--regen-refill keeps that way).  Each
 launches on; the mover launch has its own event pair, which gives the
 roofline figure.
 
-Prints one JSON line.  --gpus N > 1 is refused: this build runs on one GPU.
+Prints one JSON line.  --gpus N > 1 is refused: each GPU compacts its own arena, so
+the benchmark runs on one.
 """
 from __future__ import annotations
 
