@@ -183,10 +183,20 @@ int defrag_first_fit(const defrag_table *table, uint64_t arena_bytes, uint64_t r
 
 namespace {
 
-// Full plan (request == 0) or targeted plan (request > 0).
-int plan_common(const defrag_table *table, uint64_t arena_bytes, uint64_t request,
-                const defrag_tuning *tuning, void *ws_dev, size_t ws_bytes, hipStream_t stream,
-                uint64_t *new_offset_dev, defrag_plan_t *plan) {
+// A plan in flight: what its queued passes were given, for reading it back.
+struct PlanCtx {
+    WsLayout L;
+    defrag_tuning tu;
+    bool tuned;  // the caller gave a tuning (else the plan picks workgroups)
+    uint64_t epoch;
+    int dev;
+};
+
+// Full plan (request == 0) or targeted plan (request > 0): check the
+// arguments and queue every pass.  Nothing is read back.
+int plan_queue(const defrag_table *table, uint64_t arena_bytes, uint64_t request,
+               const defrag_tuning *tuning, void *ws_dev, size_t ws_bytes, hipStream_t stream,
+               uint64_t *new_offset_dev, defrag_plan_t *plan, PlanCtx *c) {
     if (!plan) return DEFRAG_EINVAL;
     std::memset(plan, 0, sizeof(*plan));
     defrag_tuning tu{0, kDefaultWgPerCu, kDefaultNontemporal, 0};
@@ -208,45 +218,50 @@ int plan_common(const defrag_table *table, uint64_t arena_bytes, uint64_t reques
         arg_error(&plan->stats);
         return DEFRAG_EWORKSPACE;
     }
-    const WsLayout L = ws_with_tiles(table->n, max_tiles < kMaxTiles ? max_tiles : kMaxTiles);
-    const int dev = current_device();
-    if (dev < 0) return DEFRAG_EHIP;
+    c->L = ws_with_tiles(table->n, max_tiles < kMaxTiles ? max_tiles : kMaxTiles);
+    c->dev = current_device();
+    if (c->dev < 0) return DEFRAG_EHIP;
+    c->tu = tu;
+    c->tuned = tuning != nullptr;
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
-    const uint64_t epoch = g_epoch.fetch_add(0x9E3779B97F4A7C15ull) ^ reinterpret_cast<uintptr_t>(ws);
+    c->epoch = g_epoch.fetch_add(0x9E3779B97F4A7C15ull) ^ reinterpret_cast<uintptr_t>(ws);
     const hipError_t e =
-        request ? launch_targeted(view_of(table), arena_bytes, request, ws, L, new_offset_dev,
-                                  tu.tile_bytes, epoch, stream)
-                : launch_scan(view_of(table), arena_bytes, ws, L, new_offset_dev, kOutNew,
-                              tu.tile_bytes, epoch, kNone, stream);
-    if (e != hipSuccess) return DEFRAG_EHIP;
-    WsHeader h;
-    rc = read_header(&h, ws, L, stream);
-    if (rc) return rc;
+        request ? launch_targeted(view_of(table), arena_bytes, request, ws, c->L, new_offset_dev,
+                                  tu.tile_bytes, c->epoch, stream)
+                : launch_scan(view_of(table), arena_bytes, ws, c->L, new_offset_dev, kOutNew,
+                              tu.tile_bytes, c->epoch, kNone, stream);
+    return e == hipSuccess ? DEFRAG_OK : DEFRAG_EHIP;
+}
+
+// Fill the host plan from the header its passes wrote.
+int plan_fill(const defrag_table *table, uint64_t arena_bytes, uint64_t request, void *ws_dev,
+              const PlanCtx &c, const WsHeader &h, defrag_plan_t *plan) {
     fill_stats(&plan->stats, h, arena_bytes);
     if (h.bad_key != kNone) return DEFRAG_EINVAL;
     if (request && h.win_state != kWinFound) return DEFRAG_ENOFIT;  // nothing written
-    if (h.n_tiles > L.max_tiles) return DEFRAG_EWORKSPACE;  // new offsets were written
+    if (h.n_tiles > c.L.max_tiles) return DEFRAG_EWORKSPACE;  // new offsets were written
 
+    defrag_tuning tu = c.tu;
     const uint64_t T = tu.tile_bytes;
-    plan->epoch = epoch;
+    plan->epoch = c.epoch;
     plan->workspace = ws_dev;
-    plan->workspace_bytes = L.total;
+    plan->workspace_bytes = c.L.total;
     plan->n = table->n;
     plan->arena_bytes = arena_bytes;
     plan->live_blocks = h.live_blocks;
     plan->pinned_blocks = h.pinned_blocks;
     plan->move_begin = h.move_begin;
     plan->live_bytes = h.live_bytes;
-    plan->device = dev;
+    plan->device = c.dev;
     plan->n_tiles = h.n_tiles;
-    plan->max_tiles = L.max_tiles;
+    plan->max_tiles = c.L.max_tiles;
     // blocks meeting one tile: at most T / (smallest live size) + 2
     uint64_t mb = 1;
     if (h.min_live_size != kNone && h.min_live_size) mb = T / h.min_live_size + 2;
     if (mb > T / 32 + 2) mb = T / 32 + 2;
     plan->max_blocks_per_tile = mb;
     plan->whole_tiles = h.whole_tiles;
-    if (!tuning) tu.wg_per_cu = 2 * h.whole_tiles >= h.n_tiles ? kWgPerCuWhole : kDefaultWgPerCu;
+    if (!c.tuned) tu.wg_per_cu = auto_wg_per_cu(h.whole_tiles, h.n_tiles);
     plan->tuning = tu;
     if (request) {
         plan->request_bytes = request;
@@ -257,6 +272,34 @@ int plan_common(const defrag_table *table, uint64_t arena_bytes, uint64_t reques
     plan->magic = kPlanMagic;
     plan->state = 1;
     return DEFRAG_OK;
+}
+
+int plan_common(const defrag_table *table, uint64_t arena_bytes, uint64_t request,
+                const defrag_tuning *tuning, void *ws_dev, size_t ws_bytes, hipStream_t stream,
+                uint64_t *new_offset_dev, defrag_plan_t *plan) {
+    PlanCtx c;
+    int rc = plan_queue(table, arena_bytes, request, tuning, ws_dev, ws_bytes, stream,
+                        new_offset_dev, plan, &c);
+    if (rc) return rc;
+    WsHeader h;
+    rc = read_header(&h, static_cast<uint8_t *>(ws_dev), c.L, stream);
+    if (rc) return rc;
+    return plan_fill(table, arena_bytes, request, ws_dev, c, h, plan);
+}
+
+// One stream per device, created on first use, on which the one-call path
+// reads a plan back while its move runs.
+hipStream_t side_stream_of(int dev) {
+    static std::mutex mu;
+    static hipStream_t streams[64] = {};
+    if (dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!streams[dev]) {
+        hipStream_t s = nullptr;
+        if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        streams[dev] = s;
+    }
+    return streams[dev];
 }
 
 }  // namespace
@@ -372,19 +415,72 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
         arg_error(&plan->stats);
         return DEFRAG_EINVAL;
     }
-    int rc = a->request_bytes
+    // The move is queued right behind the plan's passes, sized from the
+    // header on the device, and the plan is read back on a second stream
+    // while it runs: the host never stands between plan and move.  That
+    // needs the arena and the post-check's outputs known good before
+    // anything is queued, and a workgroup count the device can pick;
+    // otherwise the calls run in the plain order (plan, read back, check,
+    // move), which rejects a bad argument before any byte moves.
+    const bool arena_ok = a->arena_dev && !(reinterpret_cast<uintptr_t>(a->arena_dev) & 15u);
+    const bool post_ok = !after_host || (a->offset_out_dev && a->size_out_dev);
+    const bool wg_ok = !a->tuning || a->tuning->wg_per_cu != 0;
+    int rc;
+    if (arena_ok && post_ok && wg_ok) {
+        PlanCtx c;
+        rc = plan_queue(a->table, a->arena_bytes, a->request_bytes, a->tuning, a->ws_dev,
+                        a->ws_bytes, stream, a->new_offset_dev, plan, &c);
+        if (rc) return rc;
+        const int cus = num_cus_of(c.dev);
+        hipStream_t side = side_stream_of(c.dev);
+        if (cus <= 0 || !side) return DEFRAG_EHIP;
+        hipEvent_t planned = nullptr;
+        if (hipEventCreateWithFlags(&planned, hipEventDisableTiming) != hipSuccess)
+            return DEFRAG_EHIP;
+        uint8_t *ws = static_cast<uint8_t *>(a->ws_dev);
+        MoveArgs m{};
+        m.arena = static_cast<uint8_t *>(a->arena_dev);
+        m.live_dst = reinterpret_cast<const uint64_t *>(ws + c.L.live_dst);
+        m.live_src = reinterpret_cast<const uint64_t *>(ws + c.L.live_src);
+        m.tiles = reinterpret_cast<const TileRec *>(ws + c.L.tiles);
+        m.flags = reinterpret_cast<uint32_t *>(ws + c.L.flags);
+        m.hdr = reinterpret_cast<WsHeader *>(ws + c.L.header);
+        m.epoch = c.epoch;
+        m.spin_limit = 1ull << c.tu.spin_limit_log2;
+        m.tile_bytes = c.tu.tile_bytes;
+        m.max_blocks = c.tu.tile_bytes / 32 + 2;  // the most blocks a tile can meet
+        m.device_sized = 1;
+        m.wg_per_cu = c.tuned ? c.tu.wg_per_cu : 0;
+        m.num_cus = (uint32_t)cus;
+        m.max_tiles = c.L.max_tiles;
+        WsHeader hp;
+        const bool queued =
+            hipEventRecord(planned, stream) == hipSuccess &&
+            launch_move_device_sized(m, c.tu.nontemporal, stream) == hipSuccess &&
+            hipStreamWaitEvent(side, planned, 0) == hipSuccess;
+        rc = queued ? read_header(&hp, ws, c.L, side) : DEFRAG_EHIP;
+        const hipError_t destroyed = hipEventDestroy(planned);
+        if (rc) return rc;
+        if (destroyed != hipSuccess) return DEFRAG_EHIP;
+        // a failed plan: the queued move saw it in the header and moved nothing
+        rc = plan_fill(a->table, a->arena_bytes, a->request_bytes, a->ws_dev, c, hp, plan);
+        if (rc) return rc;
+        plan->state = 2;
+    } else {
+        rc = a->request_bytes
                  ? defrag_plan_targeted(a->table, a->arena_bytes, a->request_bytes, a->tuning,
                                         a->ws_dev, a->ws_bytes, stream, a->new_offset_dev, plan)
-                 : defrag_plan(a->table, a->arena_bytes, a->tuning, a->ws_dev, a->ws_bytes, stream,
-                               a->new_offset_dev, plan);
-    if (rc) return rc;
-    // the post-check reads the packed table (empty if nothing is live)
-    if (after_host && plan->live_blocks && (!a->offset_out_dev || !a->size_out_dev)) {
-        arg_error(after_host);
-        return DEFRAG_EINVAL;  // checked before anything moves
+                 : defrag_plan(a->table, a->arena_bytes, a->tuning, a->ws_dev, a->ws_bytes,
+                               stream, a->new_offset_dev, plan);
+        if (rc) return rc;
+        // the post-check reads the packed table (empty if nothing is live)
+        if (after_host && plan->live_blocks && (!a->offset_out_dev || !a->size_out_dev)) {
+            arg_error(after_host);
+            return DEFRAG_EINVAL;  // checked before anything moves
+        }
+        rc = defrag_move(a->arena_dev, a->arena_bytes, plan, a->ws_dev, a->ws_bytes, stream);
+        if (rc) return rc;
     }
-    rc = defrag_move(a->arena_dev, a->arena_bytes, plan, a->ws_dev, a->ws_bytes, stream);
-    if (rc) return rc;
     if (a->n_handles || a->n_invalid_dev) {
         rc = defrag_remap(plan, a->ws_dev, a->ws_bytes, a->h_in_dev, a->h_out_dev, a->n_handles,
                           a->n_invalid_dev, stream);

@@ -23,6 +23,9 @@ constexpr uint32_t kDefaultTile = 65536;
 // its latencies).  Measured on the 80 GiB and the small-block workloads.
 constexpr uint32_t kWgPerCuWhole = 1;
 constexpr uint32_t kDefaultWgPerCu = 2;
+__host__ __device__ inline uint32_t auto_wg_per_cu(uint64_t whole_tiles, uint64_t n_tiles) {
+    return 2 * whole_tiles >= n_tiles ? kWgPerCuWhole : kDefaultWgPerCu;
+}
 constexpr uint32_t kDefaultNontemporal = 1; // streaming loads and stores
 constexpr uint32_t kMinTile = 256;
 constexpr uint32_t kMaxTile = 131072;
@@ -304,9 +307,19 @@ struct MoveArgs {
     uint64_t spin_limit;
     uint32_t tile_bytes;
     uint32_t max_blocks;  // LDS capacity in block descriptors
+    // Sized on the device: the mover is queued right behind its plan, before
+    // the host has read the plan back, so the tile count and the workgroups
+    // that take part come from the header, and a failed plan moves nothing.
+    uint32_t device_sized;
+    uint32_t wg_per_cu;   // device-sized: 0 = the plan's rule (auto_wg_per_cu)
+    uint32_t num_cus;
+    uint64_t max_tiles;   // device-sized: the workspace's tile capacity
 };
 hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, uint32_t nontemporal,
                        int num_cus, hipStream_t s);
+// The device-sized mover: a grid for the largest workgroup count the rule
+// can pick, and LDS for the most blocks a tile can meet.
+hipError_t launch_move_device_sized(const MoveArgs &a, uint32_t nontemporal, hipStream_t s);
 
 // ---- remap.hip ----
 hipError_t launch_remap(const LiveRec *rec, const uint64_t *live_src, const uint32_t *key,

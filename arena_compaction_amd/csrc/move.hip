@@ -95,20 +95,37 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
     uint32_t *s_rel = reinterpret_cast<uint32_t *>(lds_dyn + a.max_blocks);  // [max_blocks]
     __shared__ uint32_t s_ticket;
     __shared__ uint32_t s_skip;
+    __shared__ uint64_t s_ntiles;
     const uint32_t tid = threadIdx.x;
 
     if (tid == 0) {
         // a workspace re-planned since this plan: move nothing, write nothing
         // (the status query sees the epoch mismatch)
         uint32_t tk = 0xFFFFFFFFu;
-        if (__hip_atomic_load(&a.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch)
-            tk = atomicAdd(&a.hdr->ticket, 1u);
+        uint64_t nt = a.n_tiles;
+        if (__hip_atomic_load(&a.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch) {
+            bool go = true;
+            if (a.device_sized) {
+                // the plan's results, read here instead of on the host: a
+                // failed plan (invalid table, no window, too many tiles)
+                // moves nothing; workgroups past the chosen count leave
+                const WsHeader *h = a.hdr;
+                nt = h->n_tiles;
+                const uint32_t per_cu = a.wg_per_cu ? a.wg_per_cu
+                                                    : auto_wg_per_cu(h->whole_tiles, nt);
+                go = h->bad_key == kNone && h->win_state != kWinNoFit && nt <= a.max_tiles &&
+                     blockIdx.x < (uint64_t)per_cu * a.num_cus;
+            }
+            if (go) tk = atomicAdd(&a.hdr->ticket, 1u);
+        }
         s_ticket = tk;
+        s_ntiles = nt;
     }
     __syncthreads();
+    const uint64_t n_tiles = s_ntiles;
     uint32_t t = s_ticket;
 
-    while (t < a.n_tiles) {
+    while (t < n_tiles) {
 
         // The record is the same for every lane: make each field wave-uniform
         // (one wait for the record, scalar registers after) -- otherwise the
@@ -240,6 +257,23 @@ hipError_t launch_t(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStrea
     return hipGetLastError();
 }
 
+// The device-sized mover: a grid for the largest workgroup count the rule
+// can pick (the workgroups past the plan's choice leave at once), LDS for
+// the most blocks a tile can meet.
+constexpr uint32_t kMaxAutoWgPerCu = kWgPerCuWhole > kDefaultWgPerCu ? kWgPerCuWhole
+                                                                      : kDefaultWgPerCu;
+
+template <int VPT, int NT>
+hipError_t launch_device_sized_t(const MoveArgs &a, hipStream_t s) {
+    const size_t lds = (size_t)a.max_blocks * 12u + 16u;
+    const uint64_t per_cu = a.wg_per_cu ? a.wg_per_cu : kMaxAutoWgPerCu;
+    uint64_t grid = per_cu * (uint64_t)a.num_cus;
+    if (grid > kMaxMoveGrid) grid = kMaxMoveGrid;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((k_move<VPT, NT>), dim3((uint32_t)grid), dim3(kMoveThreads), lds, s, a);
+    return hipGetLastError();
+}
+
 template <int NT>
 hipError_t launch_nt(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
     switch (a.tile_bytes <= kMoveRowBytes ? 1u : a.tile_bytes / kMoveRowBytes) {
@@ -249,6 +283,19 @@ hipError_t launch_nt(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStre
         case 8: return launch_t<8, NT>(a, wg_per_cu, num_cus, s);
         case 16: return launch_t<16, NT>(a, wg_per_cu, num_cus, s);
         case 32: return launch_t<32, NT>(a, wg_per_cu, num_cus, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int NT>
+hipError_t launch_device_sized_nt(const MoveArgs &a, hipStream_t s) {
+    switch (a.tile_bytes <= kMoveRowBytes ? 1u : a.tile_bytes / kMoveRowBytes) {
+        case 1: return launch_device_sized_t<1, NT>(a, s);
+        case 2: return launch_device_sized_t<2, NT>(a, s);
+        case 4: return launch_device_sized_t<4, NT>(a, s);
+        case 8: return launch_device_sized_t<8, NT>(a, s);
+        case 16: return launch_device_sized_t<16, NT>(a, s);
+        case 32: return launch_device_sized_t<32, NT>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -263,6 +310,16 @@ hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, uint32_t nontempor
         case 1: return launch_nt<3>(a, wg_per_cu, num_cus, s);
         case 2: return launch_nt<1>(a, wg_per_cu, num_cus, s);
         case 3: return launch_nt<2>(a, wg_per_cu, num_cus, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_move_device_sized(const MoveArgs &a, uint32_t nontemporal, hipStream_t s) {
+    switch (nontemporal) {
+        case 0: return launch_device_sized_nt<0>(a, s);
+        case 1: return launch_device_sized_nt<3>(a, s);
+        case 2: return launch_device_sized_nt<1>(a, s);
+        case 3: return launch_device_sized_nt<2>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -39,8 +39,9 @@
  *
  * Ownership: the caller owns every buffer (arena, table, outputs, handles and
  * the workspace).  The library allocates no device memory and never writes
- * the table.  Its only process-wide state is a counter for plan epochs and a
- * per-device cache of the compute-unit count.
+ * the table.  Its only process-wide state is a counter for plan epochs, a
+ * per-device cache of the compute-unit count, and one HIP stream per device
+ * that defrag_compact creates on first use.
  *
  * Concurrency: between defrag_plan and the end of defrag_move nothing else
  * may read or write the arena, the table or the workspace (the 910C page runs
@@ -273,9 +274,16 @@ int defrag_commit(const defrag_plan_t *plan_host, const void *ws_dev,
  * defrag_plan (or defrag_plan_targeted when request_bytes > 0),
  * defrag_move, defrag_remap (when n_handles or n_invalid_dev is given),
  * defrag_commit (when any packed-table output is given) and, when
- * after_host is given, defrag_stats of the packed table, with two host
- * synchronisations in all: the plan's header read-back and one at the end.
- * Returns the first failing step's code (nothing moves if the plan fails;
+ * after_host is given, defrag_stats of the packed table.  The move is
+ * queued right behind the plan's passes, before the plan is read back: it
+ * takes its tile count and workgroup count from the plan in the workspace,
+ * and moves nothing if the plan failed; the plan is read back on a second
+ * stream (one per device, created on first use and kept) while the move
+ * runs, and one read at the end brings the post-check and the mover's
+ * status.  With a NULL or misaligned arena, a tuning of wg_per_cu 0, or
+ * after_host without offset_out_dev and size_out_dev, the steps run in the
+ * plain order instead (plan, read back, argument checks, move).  Returns
+ * the first failing step's code (nothing moves if the plan fails;
  * DEFRAG_ETIMEOUT leaves the arena undefined).  plan_host is filled as by
  * the planning call and is consumed (state 2).  after_host needs
  * offset_out_dev and size_out_dev unless nothing is live (DEFRAG_EINVAL,

@@ -125,5 +125,38 @@ def test_compact_errors_leave_the_arena(ac):
         ac.defrag_compact(off, size, live, heap.arena_bytes, arena, ws, offset_out=c_off,
                           after=True)
     assert e.value.code == ac.DEFRAG_EINVAL
+    # room for fewer tiles than the plan needs (a workspace sized for
+    # 128 KiB tiles, planned with 256-byte ones): the plan says so only from
+    # the device, and the move queued behind it moves nothing
+    ws_few = ac.workspace(heap.n, heap.arena_bytes, 131072)
+    with pytest.raises(ac.DefragError) as e:
+        ac.defrag_compact(off, size, live, heap.arena_bytes, arena, ws_few,
+                          tuning=ac.defrag_tuning(256, 1, 1, 0))
+    assert e.value.code == ac.DEFRAG_EWORKSPACE
+    torch.cuda.synchronize()
+    assert torch.equal(arena.cpu(), host)
+
+
+def test_compact_failed_plan_after_a_good_one_moves_nothing(ac):
+    """The one-call path queues the move before the plan is read back; a
+    workspace whose header still holds an earlier plan's tile count must not
+    let an invalid table's move run."""
+    heap = W.config(1, small=True)
+    off, size, live = device_table(heap, "cuda")
+    host = pristine_host(heap)
+    ws = ac.workspace(heap.n, heap.arena_bytes)
+    done = host.cuda()
+    plan, _ = ac.defrag_compact(off, size, live, heap.arena_bytes, done, ws)
+    assert plan.n_tiles > 0
+    arena = host.cuda()
+    bad = size.clone()
+    bad[3] = 0
+    with pytest.raises(ac.DefragError) as e:
+        ac.defrag_compact(off, bad, live, heap.arena_bytes, arena, ws)
+    assert e.value.code == ac.DEFRAG_EINVAL and e.value.invalid_index == 3
+    with pytest.raises(ac.DefragError) as e:
+        ac.defrag_compact(off, size, live, heap.arena_bytes, arena, ws,
+                          request_bytes=heap.arena_bytes + 32)
+    assert e.value.code == ac.DEFRAG_ENOFIT
     torch.cuda.synchronize()
     assert torch.equal(arena.cpu(), host)
