@@ -56,17 +56,37 @@ def test_compact_small_configs(ac, k):
 
 
 def test_compact_tiny_heaps_and_tiles(ac):
+    """Workgroups per CU 0 (as many as fit: the plain order, plan read back
+    before the move) and 1-3 (the move queued behind the plan, sized on the
+    device), over tile sizes and nontemporal modes."""
     rng = np.random.default_rng(77)
-    for k in range(20):
+    for k in range(32):
         heap = W.tiny_heap(rng, int(rng.integers(0, 50)), sizes=(32, 64, 96, 160, 4096),
                            gap_p=float(rng.choice([0.0, 0.3, 0.8])),
                            live_p=float(rng.choice([0.2, 0.6, 1.0])),
                            pinned_p=float(rng.choice([0.0, 0.2])))
         tile = int(rng.choice([256, 4096, 65536]))
+        wg = k % 4
+        nt = int(rng.integers(0, 4))
         host = pristine_host(heap)
-        r = compact_gpu(heap, host.cuda(), tuning=ac.defrag_tuning(tile, 0, 1, 0))
+        r = compact_gpu(heap, host.cuda(), tuning=ac.defrag_tuning(tile, wg, nt, 0))
         check_tables_and_handles(heap, r)
         check_arena_full(heap, r, host)
+
+
+@pytest.mark.parametrize("k", [5, "3p"])
+def test_compact_full_size_sampled(ac, k):
+    """The one-call path at full size on the self-overlapping and the pinned
+    workload (the move sized on the device)."""
+    heap = W.config(k)
+    log(f"case compact {heap.describe()} (sampled bytes)")
+    arena = torch.empty(heap.arena_bytes, dtype=torch.uint8, device="cuda")
+    W.fill_payload(arena, 0, heap.payload_mode, heap.payload_seed)
+    r = compact_gpu(heap, arena)
+    check_tables_and_handles(heap, r)
+    check_arena_sampled(heap, r, sample_windows(heap, np.random.default_rng(9), n_random=512))
+    del r, arena
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("k", [3, "3p"])
