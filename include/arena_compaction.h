@@ -129,7 +129,10 @@ typedef struct defrag_stats_t {
  * the other fields are taken as given. */
 typedef struct defrag_tuning {
     uint32_t tile_bytes;      /* mover tile: power of two in [256, 131072].
-                                 Fixed at plan time.                          */
+                                 Fixed at plan time.  Compactions made mostly
+                                 of small shifts (under ~16 MiB, so a tile
+                                 often waits on one still being read) run
+                                 faster with 131072 and wg_per_cu 2.          */
     uint32_t wg_per_cu;       /* mover workgroups per compute unit; 0 means as
                                  many as the kernel's resources allow         */
     uint32_t nontemporal;     /* streaming hints: 0 none, 1 loads and stores,
