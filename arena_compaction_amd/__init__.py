@@ -168,8 +168,20 @@ def strerror(code: int) -> str:
 def _ptr(t: Optional[torch.Tensor]):
     if t is None:
         return None
-    assert t.is_cuda and t.is_contiguous(), "device tensors must be contiguous CUDA/HIP tensors"
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("device arguments must be contiguous GPU tensors")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: Optional[torch.Tensor], dtype: torch.dtype, n: int, what: str) -> None:
+    """Raise unless t is None or a tensor of dtype with at least n elements
+    (the kernels write or read that many; a shorter buffer would be overrun)."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype:
+        raise ValueError(f"{what}: expected a {dtype} tensor")
+    if t.numel() < n:
+        raise ValueError(f"{what}: {t.numel()} elements, {n} needed")
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -181,10 +193,10 @@ def _stream(stream) -> ctypes.c_void_p:
 def make_table(offset: torch.Tensor, size: torch.Tensor, live: Optional[torch.Tensor],
                pinned: Optional[torch.Tensor] = None) -> defrag_table:
     n = offset.numel()
-    assert offset.dtype == torch.int64 and size.dtype == torch.int64 and size.numel() == n
-    for f in (live, pinned):
-        if f is not None:
-            assert f.dtype == torch.uint8 and f.numel() == n
+    _need(offset, torch.int64, 0, "offset")
+    _need(size, torch.int64, n, "size")
+    _need(live, torch.uint8, n, "live")
+    _need(pinned, torch.uint8, n, "pinned")
     return defrag_table(_ptr(offset) if n else None, _ptr(size) if n else None,
                         _ptr(live) if (live is not None and n) else None, n,
                         _ptr(pinned) if (pinned is not None and n) else None)
@@ -235,10 +247,9 @@ def defrag_plan(offset, size, live, arena_bytes: int, ws: torch.Tensor,
                 new_offset: Optional[torch.Tensor] = None,
                 tuning: Optional[defrag_tuning] = None, stream=None,
                 pinned: Optional[torch.Tensor] = None) -> defrag_plan_t:
+    _need(new_offset, torch.int64, offset.numel(), "new_offset")
     t = make_table(offset, size, live, pinned)
     plan = defrag_plan_t()
-    if new_offset is not None:
-        assert new_offset.dtype == torch.int64 and new_offset.numel() >= offset.numel()
     rc = lib.defrag_plan(ctypes.byref(t), arena_bytes,
                          ctypes.byref(tuning) if tuning is not None else None,
                          _ptr(ws), ws.numel(), _stream(stream),
@@ -254,10 +265,9 @@ def defrag_plan_targeted(offset, size, live, arena_bytes: int, request_bytes: in
                          tuning: Optional[defrag_tuning] = None, stream=None,
                          pinned: Optional[torch.Tensor] = None) -> defrag_plan_t:
     """Raises DefragError with code DEFRAG_ENOFIT when no window fits."""
+    _need(new_offset, torch.int64, offset.numel(), "new_offset")
     t = make_table(offset, size, live, pinned)
     plan = defrag_plan_t()
-    if new_offset is not None:
-        assert new_offset.dtype == torch.int64 and new_offset.numel() >= offset.numel()
     rc = lib.defrag_plan_targeted(ctypes.byref(t), arena_bytes, request_bytes,
                                   ctypes.byref(tuning) if tuning is not None else None,
                                   _ptr(ws), ws.numel(), _stream(stream),
@@ -269,7 +279,7 @@ def defrag_plan_targeted(offset, size, live, arena_bytes: int, request_bytes: in
 
 
 def defrag_move(arena: torch.Tensor, plan: defrag_plan_t, ws: torch.Tensor, stream=None) -> None:
-    assert arena.dtype == torch.uint8
+    _need(arena, torch.uint8, 0, "arena")
     rc = lib.defrag_move(_ptr(arena) if arena.numel() else None, arena.numel(),
                          ctypes.byref(plan), _ptr(ws), ws.numel(), _stream(stream))
     if rc != DEFRAG_OK:
@@ -283,12 +293,12 @@ def defrag_move_status(plan: defrag_plan_t, ws: torch.Tensor, stream=None) -> in
 def defrag_remap(plan: defrag_plan_t, ws: torch.Tensor, h_in: torch.Tensor,
                  h_out: Optional[torch.Tensor] = None,
                  n_invalid: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    assert h_in.dtype == torch.int64
+    _need(h_in, torch.int64, 0, "h_in")
     if h_out is None:
         h_out = torch.empty_like(h_in)
-    if n_invalid is not None:
-        assert n_invalid.dtype == torch.int64 and n_invalid.numel() >= 1
     H = h_in.numel()
+    _need(h_out, torch.int64, H, "h_out")
+    _need(n_invalid, torch.int64, 1, "n_invalid")
     rc = lib.defrag_remap(ctypes.byref(plan), _ptr(ws), ws.numel(),
                           _ptr(h_in) if H else None, _ptr(h_out) if H else None, H,
                           _ptr(n_invalid), _stream(stream))
@@ -299,6 +309,11 @@ def defrag_remap(plan: defrag_plan_t, ws: torch.Tensor, h_in: torch.Tensor,
 
 def defrag_commit(plan: defrag_plan_t, ws: torch.Tensor, offset_out=None, size_out=None,
                   live_out=None, stream=None, pinned_out=None) -> None:
+    m = int(plan.live_blocks)
+    _need(offset_out, torch.int64, m, "offset_out")
+    _need(size_out, torch.int64, m, "size_out")
+    _need(live_out, torch.uint8, m, "live_out")
+    _need(pinned_out, torch.uint8, m, "pinned_out")
     rc = lib.defrag_commit(ctypes.byref(plan), _ptr(ws), ws.numel(), _ptr(offset_out),
                            _ptr(size_out), _ptr(live_out), _ptr(pinned_out), _stream(stream))
     if rc != DEFRAG_OK:
@@ -313,16 +328,25 @@ def defrag_compact(offset, size, live, arena_bytes: int, arena: torch.Tensor, ws
                    stream=None, pinned=None, after: Optional[bool] = None):
     """Plan, move, remap, commit and the post-check in one C-ABI call.
     after (default: whenever offset_out and size_out are given) asks for the
-    post-move statistics.  Returns (plan, post-move stats or None)."""
-    assert arena.dtype == torch.uint8
+    post-move statistics.  Returns (plan, post-move stats or None).
+    offset_out, size_out, live_out and pinned_out need one element per live
+    block, which is known only once the plan has run: neither this function
+    nor the library can check their length."""
+    _need(arena, torch.uint8, 0, "arena")
     if after is None:
         after = offset_out is not None and size_out is not None
-    t = make_table(offset, size, live, pinned)
+    _need(new_offset, torch.int64, offset.numel(), "new_offset")
     H = 0 if handles is None else handles.numel()
     if handles is not None:
-        assert handles.dtype == torch.int64
+        _need(handles, torch.int64, 0, "handles")
         if h_out is None:
             h_out = torch.empty_like(handles)
+        _need(h_out, torch.int64, H, "h_out")
+    _need(n_invalid, torch.int64, 1, "n_invalid")
+    for o, dt, name in ((offset_out, torch.int64, "offset_out"), (size_out, torch.int64, "size_out"),
+                        (live_out, torch.uint8, "live_out"), (pinned_out, torch.uint8, "pinned_out")):
+        _need(o, dt, 0, name)
+    t = make_table(offset, size, live, pinned)
     a = defrag_compact_args(
         ctypes.pointer(t), arena_bytes, _ptr(arena) if arena.numel() else None, request_bytes,
         ctypes.pointer(tuning) if tuning is not None else None, _ptr(ws), ws.numel(),

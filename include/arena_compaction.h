@@ -46,8 +46,14 @@
  * Concurrency: between defrag_plan and the end of defrag_move nothing else
  * may read or write the arena, the table or the workspace (the 910C page runs
  * compaction while the affected tensors pause reads and writes -- a global
- * sync point).  Ordering is the stream's order; calls on distinct workspaces
- * are independent.  Every pointer argument named "_dev" is device memory on
+ * sync point).  defrag_remap and defrag_commit read the plan from the
+ * workspace too, so until the last of them the workspace serves no other
+ * call, except defrag_stats and defrag_first_fit of a table with no more
+ * entries than the planned one: those write only the workspace's scratch
+ * region and the statistics fields of its header, below and beside the
+ * plan's data (defrag_compact's post-check is such a call).  A larger table
+ * would overwrite the plan without any call noticing.  Ordering is the
+ * stream's order; calls on distinct workspaces are independent.  Every pointer argument named "_dev" is device memory on
  * the stream's device; "_host" is host memory.
  *
  * Errors: negative return codes below.  Validation runs inside defrag_plan /

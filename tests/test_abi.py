@@ -122,6 +122,43 @@ def test_host_side_argument_errors_need_no_gpu():
                          1 << 20, None, None, ctypes.byref(plan)) == ac.DEFRAG_EINVAL
 
 
+def test_binding_refuses_bad_buffers_before_any_call():
+    """The binding checks what it can know -- device, layout, dtype and the
+    lengths the kernels will touch -- and raises before the library is
+    called (a CPU tensor or a short buffer would be read or written out of
+    bounds on the GPU)."""
+    import torch
+    import arena_compaction_amd as ac
+    with pytest.raises(ValueError):
+        ac._ptr(torch.zeros(4, dtype=torch.int64))          # host memory
+    with pytest.raises(ValueError):
+        ac._need(torch.zeros(4, dtype=torch.int32), torch.int64, 0, "x")
+    with pytest.raises(ValueError):
+        ac._need(torch.zeros(3, dtype=torch.int64), torch.int64, 4, "x")
+    ac._need(None, torch.int64, 4, "x")
+    ac._need(torch.zeros(4, dtype=torch.int64), torch.int64, 4, "x")
+    plan = ac.defrag_plan_t()
+    plan.live_blocks = 10
+    ws = torch.zeros(256, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="offset_out"):
+        ac.defrag_commit(plan, ws, torch.zeros(9, dtype=torch.int64))
+    with pytest.raises(ValueError, match="pinned_out"):
+        ac.defrag_commit(plan, ws, None, None, None, pinned_out=torch.zeros(10, dtype=torch.int64))
+    h = torch.zeros(8, dtype=torch.int64)
+    with pytest.raises(ValueError, match="h_out"):
+        ac.defrag_remap(plan, ws, h, torch.zeros(7, dtype=torch.int64))
+    with pytest.raises(ValueError, match="h_in"):
+        ac.defrag_remap(plan, ws, h.int())
+    with pytest.raises(ValueError, match="n_invalid"):
+        ac.defrag_remap(plan, ws, h, None, torch.zeros(0, dtype=torch.int64))
+    with pytest.raises(ValueError, match="new_offset"):
+        ac.defrag_plan(h, h, None, 4096, ws, torch.zeros(7, dtype=torch.int64))
+    with pytest.raises(ValueError, match="live"):
+        ac.defrag_stats(h, h, torch.zeros(7, dtype=torch.uint8), 4096, ws)
+    with pytest.raises(ValueError, match="arena"):
+        ac.defrag_move(torch.zeros(4, dtype=torch.int64), plan, ws)
+
+
 def test_oracle_is_not_linked_into_the_product():
     """The product library and binding never reference the oracle."""
     pkg = os.path.join(ROOT, "arena_compaction_amd")

@@ -7,7 +7,8 @@ import torch
 
 import oracle
 import workloads as W
-from harness import (GpuRun, check_arena_full, check_arena_sampled, check_tables_and_handles,
+from harness import (GpuRun, check_arena_full, check_arena_sampled, check_stats,
+                     check_tables_and_handles,
                      device_pinned, device_table, log, pristine_host, sample_windows, t_to_u64,
                      u64_to_t)
 
@@ -180,3 +181,41 @@ def test_compact_failed_plan_after_a_good_one_moves_nothing(ac):
     assert e.value.code == ac.DEFRAG_ENOFIT
     torch.cuda.synchronize()
     assert torch.equal(arena.cpu(), host)
+
+
+def test_plan_stays_usable_after_compact(ac):
+    """The one-call path's post-check reuses the workspace's scratch region;
+    the plan it returns still reports the move, remaps more handles and
+    commits again, also after a statistics pass of a table of the planned
+    size on the same workspace."""
+    heap = W.config("3p", small=True)
+    log(f"case plan after compact {heap.describe()}")
+    host = pristine_host(heap)
+    r = compact_gpu(heap, host.cuda())
+    check_tables_and_handles(heap, r)
+    ws = r.ws
+    extra = W.edge_handles(heap, np.random.default_rng(11), 512)
+    want_h, want_bad = oracle.remap(heap.offset, heap.size, heap.live, extra, pinned=heap.pinned)
+    li = np.flatnonzero(heap.live)
+    want_new = oracle.new_offsets(heap.offset, heap.size, heap.live, heap.pinned)[li]
+    off, size, live = device_table(heap, "cuda")
+    pin = device_pinned(heap, "cuda")
+    for rnd in range(2):
+        assert ac.defrag_move_status(r.plan, ws) == ac.DEFRAG_OK
+        nb = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+        got = ac.defrag_remap(r.plan, ws, u64_to_t(extra, "cuda"), None, nb)
+        torch.cuda.synchronize()
+        assert np.array_equal(t_to_u64(got), want_h), f"remap differs (pass {rnd})"
+        assert int(nb.item()) == want_bad
+        c_off = torch.empty(li.shape[0], dtype=torch.int64, device="cuda")
+        c_size = torch.empty_like(c_off)
+        c_pin = torch.full((li.shape[0],), 9, dtype=torch.uint8, device="cuda")
+        ac.defrag_commit(r.plan, ws, c_off, c_size, None, pinned_out=c_pin)
+        torch.cuda.synchronize()
+        assert np.array_equal(t_to_u64(c_off), want_new)
+        assert np.array_equal(t_to_u64(c_size), heap.size[li])
+        assert np.array_equal(c_pin.cpu().numpy(), heap.pinned[li])
+        # a statistics pass of the original table (as many entries as planned)
+        st = ac.defrag_stats(off, size, live, heap.arena_bytes, ws, pinned=pin)
+        check_stats(st, oracle.stats(heap.offset, heap.size, heap.live, heap.arena_bytes,
+                                     pinned=heap.pinned), "statistics pass")
