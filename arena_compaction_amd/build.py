@@ -9,11 +9,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libarena_compaction.so")
 SOURCES = ["api.cpp", "monitor.cpp", "plan.hip", "move.hip", "remap.hip"]
-ARCH = os.environ.get("ARENA_COMPACTION_ARCH", "gfx950")
+ARCH = "gfx950"  # MI355X (CDNA4) only
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-    "-Wall", "-Wno-unused-result",
+    "-Wall", "-Wextra",
     # no packed-FP32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
