@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Benchmark: in-place compaction of the 80 GiB config-3 arena on one MI355X.
+"""Benchmark: in-place compaction of the 80 GiB training arena on one MI355X.
 
 One step = the whole hot path on one fragmented arena:
   plan   (validate, live-size scan, hole statistics, mover tile table)
@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak (8 TB/s)
 METRIC = "compaction GB/s moved (read+write) & % HBM peak; handles remapped/s"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "move_config3_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "move_training80g_traffic.json")
 
 
 def _mover_source_hash() -> str:
@@ -87,7 +87,7 @@ def _host_description() -> str:
 
 def cpu_baseline(heap, budget_s: float = 12.0):
     """The oracle, single-threaded, on a bounded slice of the same workload:
-    the entries of the config-3 table that lie in a 4 GiB window of its mixed
+    the entries of the training-80g table that lie in a 4 GiB window of its mixed
     activation/small-block region, rebased to offset 0, with the handles that
     fall inside it.  Times validate + new offsets + stats + ordered memmove +
     remap, repeated (restoring the arena untimed) until the budget is spent."""
@@ -133,7 +133,7 @@ def cpu_baseline(heap, budget_s: float = 12.0):
         "cores": 1,
         "kind": "oracle",
         "host": _host_description(),
-        "sample": (f"config-3 entries {i0}..{i1 - 1} (the 4 GiB window at 40 GiB, "
+        "sample": (f"training-80g entries {i0}..{i1 - 1} (the 4 GiB window at 40 GiB, "
                    f"{i1 - i0} entries, {S} B arena, {moved} B moved, {hs.shape[0]} handles); "
                    f"validate+plan+stats+memmove+remap, {reps} reps, {per * 1e3:.1f} ms each"),
         "handles_per_s": round(hs.shape[0] / per, 1),
@@ -200,15 +200,16 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="3",
-                    help="workload 1..5 (3 is the headline), or 3p: config 3 with its 40 "
-                         "parameter/optimizer blocks pinned")
+    ap.add_argument("--workload", default="training-80g",
+                    help="one of mixed-64m, pairs-1g, training-80g (the headline), "
+                         "training-80g-pinned, small-blocks-4g, overlap-64g")
     ap.add_argument("--tile", type=int, default=None, help="override the mover tile bytes")
     ap.add_argument("--wg-per-cu", type=int, default=None, help="override (0 = max occupancy)")
     ap.add_argument("--nontemporal", type=int, default=None, help="override (0..3)")
     ap.add_argument("--request", type=int, default=None,
                     help="bytes for the targeted-compaction leg (default: 4.2/80 of the arena "
-                         "for workloads 3 and 3p -- the 910C page's 4.2 GB buffer -- else off; "
+                         "for the training-80g workloads -- the 910C page's 4.2 GB buffer -- "
+                         "else off; "
                          "0 turns it off)")
     ap.add_argument("--ablation-waves", action="store_true",
                     help="instead of the benchmark: time the alternative the tiled mover "
@@ -249,8 +250,7 @@ def main() -> int:
         print(json.dumps({"calibrate_copy_bytes": nb, "copies": 2}), flush=True)
         return 0
     t_gen = time.time()
-    cfg = args.config if args.config == "3p" else int(args.config)
-    heap = W.config(cfg)
+    heap = W.workload(args.workload)
     S = heap.arena_bytes
     off = torch.from_numpy(heap.offset.view(np.int64)).to(dev)
     size = torch.from_numpy(heap.size.view(np.int64)).to(dev)
@@ -374,7 +374,7 @@ def main() -> int:
     # Targeted leg: the smallest move that frees one hole of the request.
     request = args.request
     if request is None:
-        request = S * 42 // 800 if args.config in ("3", "3p") else 0
+        request = S * 42 // 800 if args.workload.startswith("training-80g") else 0
     targeted = None
     if request:
         tt = {"step": [], "one_call": [], "plan": [], "move": [], "remap": [], "post": []}
@@ -469,12 +469,7 @@ def main() -> int:
         "dtype": "u8",
         "data": "synthetic",
         "config": {
-            "workload": f"config{args.config}" + (
-                ": 80 GiB arena shaped like the 910C failure (40 pinned, 200 activation, "
-                "200k small blocks; 14 GiB free, free/largest-1 = 4.7), 4M handles"
-                if args.config == "3" else (
-                    ": config 3 with its 40 parameter/optimizer blocks pinned (immovable)"
-                    if args.config == "3p" else "")),
+            "workload": f"{args.workload}: {W.SUMMARY[args.workload]}",
             "arena_bytes": S, "entries": heap.n, "live_blocks": m,
             "handles": int(heap.handles.shape[0]), "moved_bytes": moved,
             "pinned_blocks": heap.n_pinned,
@@ -517,7 +512,7 @@ def main() -> int:
             "algorithmic_bytes_per_launch": 2 * moved,
         },
     }
-    if not args.no_cpu_baseline and args.config == "3":
+    if not args.no_cpu_baseline and args.workload == "training-80g":
         print("# cpu baseline ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(heap, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -4,7 +4,7 @@
 // shares nothing with the HIP library.  Each function states the passage of
 // the pages it writes out; see oracle.h for the page titles.
 //
-// Readings where the pages are silent (also listed in the design notes):
+// Readings where the pages are silent:
 //  * a hole is any maximal byte run not covered by a live entry -- free
 //    entries, untracked gaps and the tail alike; adjacent free pieces form one
 //    hole, as the CANN pool merges adjacent free blocks ([CANN] 2.2);

@@ -46,9 +46,9 @@ def compact_gpu(heap, arena, request=0, tuning=None):
     return GpuRun(plan, t_to_u64(new_off), t_to_u64(h), int(n_bad.item()), post, 0, arena, ws)
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, "3p", 4, 5])
-def test_compact_small_configs(ac, k):
-    heap = W.config(k, small=True)
+@pytest.mark.parametrize("k", W.NAMES)
+def test_compact_small_workloads(ac, k):
+    heap = W.workload(k, small=True)
     log(f"case compact {heap.describe()}")
     host = pristine_host(heap)
     r = compact_gpu(heap, host.cuda())
@@ -75,11 +75,11 @@ def test_compact_tiny_heaps_and_tiles(ac):
         check_arena_full(heap, r, host)
 
 
-@pytest.mark.parametrize("k", [5, "3p"])
+@pytest.mark.parametrize("k", ["overlap-64g", "training-80g-pinned"])
 def test_compact_full_size_sampled(ac, k):
     """The one-call path at full size on the self-overlapping and the pinned
     workload (the move sized on the device)."""
-    heap = W.config(k)
+    heap = W.workload(k)
     log(f"case compact {heap.describe()} (sampled bytes)")
     arena = torch.empty(heap.arena_bytes, dtype=torch.uint8, device="cuda")
     W.fill_payload(arena, 0, heap.payload_mode, heap.payload_seed)
@@ -90,9 +90,9 @@ def test_compact_full_size_sampled(ac, k):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("k", [3, "3p"])
+@pytest.mark.parametrize("k", ["training-80g", "training-80g-pinned"])
 def test_compact_targeted_small(ac, k):
-    heap = W.config(k, small=True)
+    heap = W.workload(k, small=True)
     st = oracle.stats(heap.offset, heap.size, heap.live, heap.arena_bytes, pinned=heap.pinned)
     for R in (st.largest_hole + 32, st.free_bytes // 2):
         w = oracle.target_window(heap.offset, heap.size, heap.live, heap.arena_bytes, R,
@@ -108,8 +108,8 @@ def test_compact_targeted_small(ac, k):
         assert r.post_stats.largest_hole >= R
 
 
-def test_compact_full_size_config3(ac):
-    heap = W.config(3)
+def test_compact_full_size_training_80g(ac):
+    heap = W.workload("training-80g")
     log(f"case compact {heap.describe()} (sampled bytes)")
     arena = torch.empty(heap.arena_bytes, dtype=torch.uint8, device="cuda")
     W.fill_payload(arena, 0, heap.payload_mode, heap.payload_seed)
@@ -122,7 +122,7 @@ def test_compact_full_size_config3(ac):
 
 
 def test_compact_errors_leave_the_arena(ac):
-    heap = W.config(1, small=True)
+    heap = W.workload("mixed-64m", small=True)
     off, size, live = device_table(heap, "cuda")
     host = pristine_host(heap)
     arena = host.cuda()
@@ -162,7 +162,7 @@ def test_compact_failed_plan_after_a_good_one_moves_nothing(ac):
     """The one-call path queues the move before the plan is read back; a
     workspace whose header still holds an earlier plan's tile count must not
     let an invalid table's move run."""
-    heap = W.config(1, small=True)
+    heap = W.workload("mixed-64m", small=True)
     off, size, live = device_table(heap, "cuda")
     host = pristine_host(heap)
     ws = ac.workspace(heap.n, heap.arena_bytes)
@@ -188,7 +188,7 @@ def test_plan_stays_usable_after_compact(ac):
     the plan it returns still reports the move, remaps more handles and
     commits again, also after a statistics pass of a table of the planned
     size on the same workspace."""
-    heap = W.config("3p", small=True)
+    heap = W.workload("training-80g-pinned", small=True)
     log(f"case plan after compact {heap.describe()}")
     host = pristine_host(heap)
     r = compact_gpu(heap, host.cuda())

@@ -84,19 +84,19 @@ def test_random_tiny_heaps_first_fit_gpu(ac):
         _check_heap(ac, heap, reqs)
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, "3p", 4, 5])
-def test_small_configs_first_fit_gpu(ac, k):
-    heap = W.config(k, small=True)
+@pytest.mark.parametrize("k", W.NAMES)
+def test_small_workloads_first_fit_gpu(ac, k):
+    heap = W.workload(k, small=True)
     st_ = oracle.stats(heap.offset, heap.size, heap.live, heap.arena_bytes, pinned=heap.pinned)
     L, F = st_.largest_hole, st_.free_bytes
     _check_heap(ac, heap, sorted({1, 32, L - 31 if L > 31 else 1, L, L + 1, F, F + 1}))
 
 
-@pytest.mark.parametrize("k", [3, "3p"])
+@pytest.mark.parametrize("k", ["training-80g", "training-80g-pinned"])
 def test_allocation_proof_full_size(ac, k):
     """The 910C page's 4.2 GB buffer on the 80 GiB workload: refused before,
     placed after the targeted compaction, where the oracle places it."""
-    heap = W.config(k)
+    heap = W.workload(k)
     S = heap.arena_bytes
     R = S * 42 // 800
     log(f"case {heap.describe()} first fit of {R} before and after targeted compaction")
@@ -114,7 +114,7 @@ def test_allocation_proof_full_size(ac, k):
 
 
 def test_first_fit_invalid_table(ac):
-    heap = W.config(1, small=True)
+    heap = W.workload("mixed-64m", small=True)
     off, size, live = device_table(heap, "cuda")
     ws = ac.workspace(heap.n, heap.arena_bytes)
     bad = off.clone()

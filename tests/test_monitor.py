@@ -78,7 +78,7 @@ def test_library_argument_errors():
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("k", [3, "3p"])
+@pytest.mark.parametrize("k", ["training-80g", "training-80g-pinned"])
 def test_monitor_on_measured_stats_gpu(k):
     """The 910C story on the GPU: the monitor asks for a targeted compaction
     for the 4.2 GB request, and for nothing once it has run."""
@@ -88,7 +88,7 @@ def test_monitor_on_measured_stats_gpu(k):
     import arena_compaction_amd as ac
     import workloads as W
     from harness import device_pinned, device_table, log, run_gpu
-    heap = W.config(k)
+    heap = W.workload(k)
     S = heap.arena_bytes
     R = S * 42 // 800
     log(f"case {heap.describe()} monitor before/after targeted compaction for {R}")

@@ -165,11 +165,11 @@ def test_exhaustive_pinned_masks(oracle_lib):
             _check_against_bruteforce(h)
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
-def test_invariants_small_configs(k, oracle_lib):
+@pytest.mark.parametrize("k", ["mixed-64m", "pairs-1g", "training-80g", "small-blocks-4g", "overlap-64g"])
+def test_invariants_small_workloads(k, oracle_lib):
     """I1-I6 on the reduced workloads, with the real payload generator."""
     import torch
-    heap = W.config(k, small=True)
+    heap = W.workload(k, small=True)
     off, size, live, S = heap.offset, heap.size, heap.live, heap.arena_bytes
     assert oracle.validate(off, size, live, S)[0] == oracle.OK
     new = oracle.new_offsets(off, size, live)
@@ -206,11 +206,11 @@ def test_invariants_small_configs(k, oracle_lib):
     assert np.array_equal(got[out[:5000].astype(np.int64)], A[hs.astype(np.int64)])
 
 
-def test_config3_page_proportions(oracle_lib):
+def test_training_80g_page_proportions(oracle_lib):
     """910C page, monitoring section: the ratio free/largest - 1 reached 4.7
     with 14 GB free; the workload built with those proportions must read 4.7
     (and 1 - largest/free = 1 - 1/5.7 = 0.8246) through the oracle."""
-    heap = W.config(3)
+    heap = W.workload("training-80g")
     s = oracle.stats(heap.offset, heap.size, heap.live, heap.arena_bytes)
     assert s.free_bytes == 14 * W.GiB
     assert s.largest_hole == heap.notes["largest_target"] == 2_637_258_752
@@ -310,12 +310,12 @@ def test_validation_reasons_pinned(table, pinned, S, idx, reason, oracle_lib):
 
 
 def test_pinned_segments_invariants(oracle_lib):
-    """Reduced config 3 with its 40 parameter/optimizer blocks pinned: pinned
+    """Reduced training-80g with its 40 parameter/optimizer blocks pinned: pinned
     bytes never change; every segment's movable blocks are packed from the
     segment start in order, payload intact; afterwards every segment holds at
     most one hole, at its top, and the free total is unchanged."""
     import torch
-    heap = W.config("3p", small=True)
+    heap = W.workload("training-80g-pinned", small=True)
     off, size, live, pin, S = heap.offset, heap.size, heap.live, heap.pinned, heap.arena_bytes
     assert heap.n_pinned == 40
     assert oracle.validate(off, size, live, S, pinned=pin)[0] == oracle.OK

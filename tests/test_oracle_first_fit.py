@@ -122,11 +122,11 @@ def test_request_validation(oracle_lib):
     assert oracle.first_fit(off, size, live, 64, U64_MAX - 31) == U64_MAX
 
 
-def test_page_failure_and_proof_on_workload3(oracle_lib):
+def test_page_failure_and_proof_on_training_80g(oracle_lib):
     """910C page: with 14 GB free and the largest block under 3 GB, the
     4.2 GB buffer cannot be allocated; after the targeted compaction it is
     placed at the hole that compaction freed."""
-    heap = W.config(3)
+    heap = W.workload("training-80g")
     S = heap.arena_bytes
     R = S * 42 // 800
     assert oracle.first_fit(heap.offset, heap.size, heap.live, S, R) == U64_MAX

@@ -146,9 +146,9 @@ def check_properties(heap, requests):
         assert not np.any((new[li] < w.end) & (ends > top))
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, "3p"])
-def test_properties_small_configs(k, oracle_lib):
-    heap = W.config(k, small=True)
+@pytest.mark.parametrize("k", ["mixed-64m", "pairs-1g", "training-80g", "small-blocks-4g", "overlap-64g", "training-80g-pinned"])
+def test_properties_small_workloads(k, oracle_lib):
+    heap = W.workload(k, small=True)
     st_ = oracle.stats(heap.offset, heap.size, heap.live, heap.arena_bytes, pinned=heap.pinned)
     F, L = st_.free_bytes, st_.largest_hole
     reqs = {1, L, L + 1, F // 2, F, F + 1}
@@ -156,12 +156,12 @@ def test_properties_small_configs(k, oracle_lib):
     check_properties(heap, reqs)
 
 
-def test_page_request_on_workload3(oracle_lib):
+def test_page_request_on_training_80g(oracle_lib):
     """910C page: 14 GB free, largest block under 3 GB, a 4.2 GB buffer
     request fails.  On the workload with those proportions a window that
     frees 4.2/80 of the arena exists and moves a small fraction of what a
     full compaction moves."""
-    heap = W.config(3)
+    heap = W.workload("training-80g")
     S = heap.arena_bytes
     R = S * 42 // 800
     before = oracle.stats(heap.offset, heap.size, heap.live, S)

@@ -2,8 +2,8 @@
 bit-exact on arena bytes, new offsets, remapped handles and statistics.
 
 Small cases compare every byte; the full-size workloads compare every byte
-where the host can hold the arena (configs 1, 2, 4) and otherwise sampled
-windows through the oracle's per-byte source map (configs 3, 5), always with
+where the host can hold the arena (mixed-64m, pairs-1g, small-blocks-4g) and otherwise sampled
+windows through the oracle's per-byte source map (training-80g, overlap-64g), always with
 full new offsets, statistics and handles.
 """
 import numpy as np
@@ -102,17 +102,17 @@ def test_random_medium_heaps_default_tuning(ac):
         log(f"  tiles {r.plan.n_tiles}, whole {r.plan.whole_tiles}, wg/cu {r.plan.tuning.wg_per_cu}")
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, "3p", 4, 5])
+@pytest.mark.parametrize("k", W.NAMES)
 @pytest.mark.parametrize("tile,nt", [(256, 0), (4096, 1), (65536, 0), (65536, 1), (131072, 0)])
-def test_small_configs_gpu(ac, k, tile, nt):
-    _full_check(W.config(k, small=True), _tuning(ac, tile, 0, nt))
+def test_small_workloads_gpu(ac, k, tile, nt):
+    _full_check(W.workload(k, small=True), _tuning(ac, tile, 0, nt))
 
 
-@pytest.mark.parametrize("k", [1, "3p", 4, 5])
+@pytest.mark.parametrize("k", ["mixed-64m", "training-80g-pinned", "small-blocks-4g", "overlap-64g"])
 def test_one_workgroup_per_cu_and_tiny_tiles(ac, k):
     """Fewer resident workgroups and many more tiles per workgroup: the
     ticket order alone must keep the schedule correct."""
-    _full_check(W.config(k, small=True), _tuning(ac, 512, 1, 0))
+    _full_check(W.workload(k, small=True), _tuning(ac, 512, 1, 0))
 
 
 def test_tiny_shift_under_large_blocks(ac):
@@ -202,7 +202,7 @@ def test_edge_cases_gpu(ac):
 
 
 def test_remap_in_place_and_batches(ac):
-    heap = W.config(2, small=True)
+    heap = W.workload("pairs-1g", small=True)
     off, size, live = device_table(heap, "cuda")
     ws = ac.workspace(heap.n, heap.arena_bytes)
     plan = ac.defrag_plan(off, size, live, heap.arena_bytes, ws)
@@ -268,7 +268,7 @@ def test_invalid_tables_gpu(ac):
 
 
 def test_plan_protocol_errors(ac):
-    heap = W.config(1, small=True)
+    heap = W.workload("mixed-64m", small=True)
     off, size, live = device_table(heap, "cuda")
     S = heap.arena_bytes
     ws = ac.workspace(heap.n, S)
@@ -312,25 +312,26 @@ def test_plan_protocol_errors(ac):
     assert ei.value.code == ac.DEFRAG_ENOPLAN
 
 
-@pytest.mark.parametrize("k", [1, 2, 4])
-def test_full_size_configs_every_byte(ac, k):
-    heap = W.config(k)
+@pytest.mark.parametrize("k", ["mixed-64m", "pairs-1g", "small-blocks-4g"])
+def test_full_size_workloads_every_byte(ac, k):
+    heap = W.workload(k)
     _full_check(heap)
 
 
-@pytest.mark.parametrize("k", [3, "3p", 5])
-def test_full_size_configs_sampled(ac, k):
-    heap = W.config(k)
+@pytest.mark.parametrize("k", ["training-80g", "training-80g-pinned", "overlap-64g"])
+def test_full_size_workloads_sampled(ac, k):
+    heap = W.workload(k)
     log(f"case {heap.describe()} (sampled bytes)")
     r = run_gpu(heap)
     assert r.status == ac.DEFRAG_OK
     check_tables_and_handles(heap, r)
-    wins = sample_windows(heap, np.random.default_rng(5 if k == "3p" else k), n_random=1024)
+    seed = {"training-80g": 3, "training-80g-pinned": 5, "overlap-64g": 5}[k]
+    wins = sample_windows(heap, np.random.default_rng(seed), n_random=1024)
     check_arena_sampled(heap, r, wins)
-    if k in (3, "3p"):
+    if k.startswith("training-80g"):
         s = r.plan.stats
         assert abs(s.frag_free_over_largest_minus_1 - 4.7) < 1e-3
-        if k == 3:   # one top hole afterwards
+        if k == "training-80g":   # one top hole afterwards
             assert r.post_stats.frag_free_over_largest_minus_1 == 0.0
         else:        # the pinned blocks keep free space in separate holes
             assert r.post_stats.hole_count > 1

@@ -106,9 +106,9 @@ def test_random_tiny_heaps_targeted_gpu(ac, tile):
             _check(heap, int(R), tile)
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, "3p", 4, 5])
-def test_small_configs_targeted_gpu(ac, k):
-    heap = W.config(k, small=True)
+@pytest.mark.parametrize("k", W.NAMES)
+def test_small_workloads_targeted_gpu(ac, k):
+    heap = W.workload(k, small=True)
     st_ = oracle.stats(heap.offset, heap.size, heap.live, heap.arena_bytes, pinned=heap.pinned)
     F, L = st_.free_bytes, st_.largest_hole
     for R in sorted({L, L + 1, F // 3, F // 2, F, F + 1}):
@@ -116,12 +116,12 @@ def test_small_configs_targeted_gpu(ac, k):
             _check(heap, R)
 
 
-@pytest.mark.parametrize("k", [3, "3p"])
+@pytest.mark.parametrize("k", ["training-80g", "training-80g-pinned"])
 def test_page_request_full_size(ac, k):
     """The 910C page's 4.2 GB request (4.2/80 of the arena) on the 80 GiB
     workload, and a 4 GiB one that the re-cut gap holds after moving one
     4 KiB block."""
-    heap = W.config(k)
+    heap = W.workload(k)
     rng = np.random.default_rng(11)
     for R in (heap.arena_bytes * 42 // 800, 4 * W.GiB):
         w = _check(heap, R, full=False, rng=rng)
@@ -152,7 +152,7 @@ def test_targeted_edge_cases(ac):
 
 
 def test_targeted_protocol(ac):
-    heap = W.config(1, small=True)
+    heap = W.workload("mixed-64m", small=True)
     off, size, live = device_table(heap, "cuda")
     ws = ac.workspace(heap.n, heap.arena_bytes)
     with pytest.raises(ac.DefragError) as e:

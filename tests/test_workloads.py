@@ -65,8 +65,8 @@ def _handles_inside_live(heap):
     assert np.all(h - heap.offset[i] < heap.size[i])
 
 
-def test_config1_shape():
-    h = W.config(1)
+def test_mixed_64m_shape():
+    h = W.workload("mixed-64m")
     _valid(h)
     assert h.n == 4096 and h.arena_bytes == 64 * W.MiB
     assert np.all(h.size % 32 == 0) and h.size.min() >= 256 and h.size.max() <= 64 * W.KiB
@@ -76,8 +76,8 @@ def test_config1_shape():
     _handles_inside_live(h)
 
 
-def test_config2_shape():
-    h = W.config(2)
+def test_pairs_1g_shape():
+    h = W.workload("pairs-1g")
     _valid(h)
     assert h.n == 65536 and h.arena_bytes == W.GiB
     assert np.all(h.size % 512 == 0)
@@ -87,8 +87,8 @@ def test_config2_shape():
     _handles_inside_live(h)
 
 
-def test_config3_shape():
-    h = W.config(3)
+def test_training_80g_shape():
+    h = W.workload("training-80g")
     _valid(h)
     assert h.arena_bytes == 80 * W.GiB
     assert np.all(h.size % 4096 == 0)
@@ -101,8 +101,8 @@ def test_config3_shape():
     _handles_inside_live(h)
 
 
-def test_config4_shape():
-    h = W.config(4)
+def test_small_blocks_4g_shape():
+    h = W.workload("small-blocks-4g")
     _valid(h)
     assert h.n == 2_000_000 and h.arena_bytes == 4 * W.GiB
     assert np.all(h.size % 32 == 0) and h.size.min() >= 32 and h.size.max() <= 4096
@@ -111,8 +111,8 @@ def test_config4_shape():
     _handles_inside_live(h)
 
 
-def test_config5_shape():
-    h = W.config(5)
+def test_overlap_64g_shape():
+    h = W.workload("overlap-64g")
     _valid(h)
     assert h.n == 128
     assert np.all(h.size[1::2] == W.GiB) and np.all(h.live[1::2] == 1)
@@ -123,10 +123,10 @@ def test_config5_shape():
     _handles_inside_live(h)
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("k", ["mixed-64m", "pairs-1g", "training-80g", "small-blocks-4g", "overlap-64g"])
 def test_small_variants_valid_and_seeded(k):
-    a = W.config(k, small=True)
-    b = W.config(k, small=True)
+    a = W.workload(k, small=True)
+    b = W.workload(k, small=True)
     _valid(a)
     assert np.array_equal(a.offset, b.offset) and np.array_equal(a.live, b.live)
     assert np.array_equal(a.handles, b.handles)

@@ -265,7 +265,7 @@ def edge_handles(heap: Heap, rng: np.random.Generator, extra_random: int = 64) -
 # the five workloads
 # --------------------------------------------------------------------------
 
-def config1(seed: int = 1, n_blocks: int = 4096, arena_bytes: int = 64 * MiB,
+def mixed_64mib(seed: int = 1, n_blocks: int = 4096, arena_bytes: int = 64 * MiB,
             n_handles: int = 16384) -> Heap:
     """64 MiB arena, 4,096 blocks of log-uniform 256 B..64 KiB (ceil to 32 B),
     packed from 0, untracked free tail; each block live with p = 0.5."""
@@ -275,16 +275,18 @@ def config1(seed: int = 1, n_blocks: int = 4096, arena_bytes: int = 64 * MiB,
     assert int(off[-1] + size[-1]) <= arena_bytes
     live = (rng.random(n_blocks) < 0.5).astype(np.uint8)
     h = draw_handles(off, size, live, n_handles, rng)
-    return Heap("config1", arena_bytes, off, size, live, h, "hash",
+    return Heap("mixed-64m", arena_bytes, off, size, live, h, "hash",
                 0xC0FFEE00 + seed, seed)
 
 
-def config2(seed: int = 2, n_pairs: int = 32768, arena_bytes: int = 1 * GiB,
+def pairs_1gib(seed: int = 2, n_pairs: int = 32768, arena_bytes: int = 1 * GiB,
             n_handles: int = 1_000_000) -> Heap:
     """1 GiB arena, 65,536 blocks as 32,768 interleaved pairs (b, 2b) -- a
     BF16-like tensor followed by an FP32-like one -- with b a multiple of
-    512 B.  b is log-uniform 4 KiB..1 MiB divided by 32 (so the pairs fit the
-    1 GiB arena; see the design notes), ceil to 512 B.  Live p = 0.6."""
+    512 B.  b is log-uniform 4 KiB..1 MiB divided by 32, ceil to 512 B: at
+    the undivided sizes a pair averages about 0.54 MiB and 32,768 pairs
+    would need some 17 GiB, so the law is scaled to fill about half of the
+    1 GiB arena.  Live p = 0.6."""
     rng = np.random.default_rng(seed)
     b = _ceil_to(_loguniform(rng, 4 * KiB, 1 * MiB, n_pairs) / 32.0, 512)
     size = np.empty(2 * n_pairs, dtype=np.uint64)
@@ -294,11 +296,11 @@ def config2(seed: int = 2, n_pairs: int = 32768, arena_bytes: int = 1 * GiB,
     assert int(off[-1] + size[-1]) <= arena_bytes
     live = (rng.random(2 * n_pairs) < 0.6).astype(np.uint8)
     h = draw_handles(off, size, live, n_handles, rng)
-    return Heap("config2", arena_bytes, off, size, live, h, "hash",
+    return Heap("pairs-1g", arena_bytes, off, size, live, h, "hash",
                 0xC0FFEE00 + seed, seed)
 
 
-def config3(seed: int = 3, arena_bytes: int = 80 * GiB, n_pinned: int = 40,
+def training_80gib(seed: int = 3, arena_bytes: int = 80 * GiB, n_pinned: int = 40,
             n_act: int = 200, n_small: int = 200_000, gran: int = 4 * KiB,
             n_handles: int = 4_000_000, pin_params: bool = False) -> Heap:
     """An arena shaped like the 910C page's failure: 14/80 of the arena free,
@@ -393,7 +395,7 @@ def config3(seed: int = 3, arena_bytes: int = 80 * GiB, n_pinned: int = 40,
     assert remaining == 0, "could not reach the free-total target exactly"
 
     h = draw_handles(off, size, live, n_handles, rng)
-    heap = Heap("config3" + ("-pinned" if pin_params else ""), S, off, size, live, h, "hash",
+    heap = Heap("training-80g" + ("-pinned" if pin_params else ""), S, off, size, live, h, "hash",
                 0xC0FFEE00 + seed, seed)
     heap.notes.update(dict(free_target=F, largest_target=L, alpha=alpha,
                            named_free=named_free, gap=2 * half + g))
@@ -402,7 +404,7 @@ def config3(seed: int = 3, arena_bytes: int = 80 * GiB, n_pinned: int = 40,
     return heap
 
 
-def config4(seed: int = 4, n_blocks: int = 2_000_000, arena_bytes: int = 4 * GiB,
+def small_blocks_4gib(seed: int = 4, n_blocks: int = 2_000_000, arena_bytes: int = 4 * GiB,
             n_handles: int = 8_000_000) -> Heap:
     """Adversarial small-block heap: 2,000,000 blocks of 32 * U{1..128} bytes,
     packed; block 0 free, then strictly alternating live/free so every live
@@ -413,11 +415,11 @@ def config4(seed: int = 4, n_blocks: int = 2_000_000, arena_bytes: int = 4 * GiB
     assert int(off[-1] + size[-1]) <= arena_bytes
     live = (np.arange(n_blocks) % 2 == 1).astype(np.uint8)
     h = draw_handles(off, size, live, n_handles, rng)
-    return Heap("config4", arena_bytes, off, size, live, h, "hash",
+    return Heap("small-blocks-4g", arena_bytes, off, size, live, h, "hash",
                 0xC0FFEE00 + seed, seed)
 
 
-def config5(seed: int = 5, n_live: int = 64, block_bytes: int = 1 * GiB,
+def self_overlap_64gib(seed: int = 5, n_live: int = 64, block_bytes: int = 1 * GiB,
             hole_lo: int = 4 * KiB, hole_hi: int = 64 * MiB,
             n_handles: int = 1_000_000) -> Heap:
     """Self-overlap stress: n_live live blocks of block_bytes, each preceded by
@@ -433,37 +435,58 @@ def config5(seed: int = 5, n_live: int = 64, block_bytes: int = 1 * GiB,
     off = _packed_offsets(size)
     S = int(off[-1] + size[-1])
     h = draw_handles(off, size, live, n_handles, rng)
-    return Heap("config5", S, off, size, live, h, "counter32",
+    return Heap("overlap-64g", S, off, size, live, h, "counter32",
                 0x5EED0000 + seed, seed)
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+# name -> (full size, reduced size with the same structure: small enough for
+# the oracle to finish in seconds, large enough for several mover tiles)
+_WORKLOADS = {
+    "mixed-64m": (mixed_64mib,
+                  lambda: mixed_64mib(n_blocks=1024, arena_bytes=16 * MiB, n_handles=4096)),
+    "pairs-1g": (pairs_1gib,
+                 lambda: pairs_1gib(n_pairs=2048, arena_bytes=64 * MiB, n_handles=65536)),
+    "training-80g": (training_80gib,
+                     lambda: training_80gib(arena_bytes=80 * 16 * MiB, n_small=3000, n_act=60,
+                                            n_pinned=40, n_handles=65536)),
+    "training-80g-pinned": (lambda: training_80gib(pin_params=True),
+                            lambda: training_80gib(arena_bytes=80 * 16 * MiB, n_small=3000,
+                                                   n_act=60, n_pinned=40, n_handles=65536,
+                                                   pin_params=True)),
+    "small-blocks-4g": (small_blocks_4gib,
+                        lambda: small_blocks_4gib(n_blocks=60_000, arena_bytes=128 * MiB,
+                                                  n_handles=65536)),
+    "overlap-64g": (self_overlap_64gib,
+                    lambda: self_overlap_64gib(n_live=8, block_bytes=8 * MiB, hole_lo=4 * KiB,
+                                               hole_hi=1 * MiB, n_handles=65536)),
+}
+NAMES = tuple(_WORKLOADS)
+
+# one line per workload, at its full size
+SUMMARY = {
+    "mixed-64m": "64 MiB arena, 4,096 blocks of 256 B-64 KiB, each live with p = 0.5; "
+                 "16,384 handles",
+    "pairs-1g": "1 GiB arena, 65,536 blocks as BF16/FP32-like pairs (b, 2b), live p = 0.6; "
+                "1M handles",
+    "training-80g": "80 GiB arena shaped like the 910C failure: 40 never-freed 1-2 GiB "
+                    "parameter/optimizer blocks, 200 activation and 200k small blocks, "
+                    "14 GiB free with free/largest - 1 = 4.7; 4M handles",
+    "training-80g-pinned": "the 80 GiB training arena with its 40 parameter/optimizer "
+                           "blocks pinned (immovable); 4M handles",
+    "small-blocks-4g": "4 GiB arena, 2,000,000 blocks of 32-4,096 B alternating free/live "
+                       "(every live block moves); 8M handles",
+    "overlap-64g": "64 GiB arena of 64 live 1 GiB blocks, each above a freed 4 KiB-64 MiB "
+                   "hole (every move self-overlapping); 1M handles",
+}
 
 
-def config(k, small: bool = False) -> Heap:
-    """Workload ``k`` (1..5, or "3p": config 3 with its 40 parameter and
-    optimizer blocks pinned) at its full size, or a reduced variant with the
-    same structure (for oracle runs that must finish in seconds)."""
-    if k == "3p":
-        if not small:
-            return config3(pin_params=True)
-        return config3(arena_bytes=80 * 16 * MiB, n_small=3000, n_act=60, n_pinned=40,
-                       n_handles=65536, pin_params=True)
-    if not small:
-        return CONFIGS[k]()
-    if k == 1:
-        return config1(n_blocks=1024, arena_bytes=16 * MiB, n_handles=4096)
-    if k == 2:
-        return config2(n_pairs=2048, arena_bytes=64 * MiB, n_handles=65536)
-    if k == 3:
-        return config3(arena_bytes=80 * 16 * MiB, n_small=3000,
-                       n_act=60, n_pinned=40, n_handles=65536)
-    if k == 4:
-        return config4(n_blocks=60_000, arena_bytes=128 * MiB, n_handles=65536)
-    if k == 5:
-        return config5(n_live=8, block_bytes=8 * MiB, hole_lo=4 * KiB,
-                       hole_hi=1 * MiB, n_handles=65536)
-    raise KeyError(k)
+def workload(name: str, small: bool = False) -> Heap:
+    """The named workload (a key of SUMMARY) at its full size, or its reduced
+    variant with the same structure."""
+    if name not in _WORKLOADS:
+        raise KeyError(f"unknown workload {name!r}; one of {', '.join(NAMES)}")
+    full, reduced = _WORKLOADS[name]
+    return reduced() if small else full()
 
 
 # --------------------------------------------------------------------------
