@@ -385,7 +385,7 @@ int defrag_remap(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes,
     if (cus <= 0) return DEFRAG_EHIP;
     const WsLayout L = plan_layout(plan);
     const uint8_t *ws = static_cast<const uint8_t *>(ws_dev);
-    if (launch_remap(reinterpret_cast<const LiveRec *>(ws + L.live_rec),
+    if (launch_remap(ws + L.live_rec,
                      reinterpret_cast<const uint64_t *>(ws + L.live_src),
                      reinterpret_cast<const uint32_t *>(ws + L.live_key),
                      reinterpret_cast<const uint32_t *>(ws + L.ridx), plan->arena_bytes, plan->n,

@@ -15,9 +15,10 @@
 // probe of each lane is its own cache line), so the plan builds an index --
 // the arena cut into at most 2^18 power-of-two buckets, each pointing at the
 // first live block starting in it -- and each live block also has one
-// 16-byte record (old end, shift) and a 32-bit search key (its old offset
-// inside its bucket).  HBM traffic is 16 B per handle; the index, keys and
-// records stay in L2 / the last-level cache.
+// record (old end, shift: 8 bytes in 32-byte units below 2^37 arena bytes,
+// else 16) and a 32-bit search key (its old offset inside its bucket).  HBM
+// traffic is 16 B per handle; the index, keys and records stay in L2 / the
+// last-level cache.
 #include "internal.h"
 
 namespace ac {
@@ -28,10 +29,12 @@ constexpr uint32_t kRemapThreads = 256;
 // One lane per handle, grid-stride.  The bucket of h gives the live blocks
 // starting in it, [ridx[b], ridx[b+1]); the block holding h, if any, is the
 // last one starting at or below h, so it is found by a short search inside
-// the bucket (or is the block before it), and its record is one 16-byte
-// read.  A random handle costs about three dependent cache-line requests:
+// the bucket (or is the block before it), and its record is one 8- or
+// 16-byte read.  A random handle costs about three dependent cache-line requests:
 // the index pair, a probe or two over the bucket's keys, the record.
-__global__ __launch_bounds__(kRemapThreads) void k_remap(const LiveRec *__restrict__ rec,
+// REC32: the records are LiveRec32 (arenas below 2^37 bytes), else LiveRec.
+template <bool REC32>
+__global__ __launch_bounds__(kRemapThreads) void k_remap(const void *__restrict__ rec,
                                                          const uint64_t *__restrict__ live_src,
                                                          const uint32_t *__restrict__ key,
                                                          const uint32_t *__restrict__ ridx,
@@ -68,9 +71,14 @@ __global__ __launch_bounds__(kRemapThreads) void k_remap(const LiveRec *__restri
                     }
                 }
             }
-            if (first > 0) {
-                const LiveRec r = rec[first - 1];  // starts at or below h
-                if (h < r.end) out = h - r.shift;
+            if (first > 0) {  // the record of the last block starting at or below h
+                if constexpr (REC32) {
+                    const LiveRec32 r = static_cast<const LiveRec32 *>(rec)[first - 1];
+                    if (h < ((uint64_t)r.end32 << 5)) out = h - ((uint64_t)r.shift32 << 5);
+                } else {
+                    const LiveRec r = static_cast<const LiveRec *>(rec)[first - 1];
+                    if (h < r.end) out = h - r.shift;
+                }
             }
         }
         bad += (out == kNone) ? 1u : 0u;
@@ -89,7 +97,7 @@ __global__ void k_zero_u64(uint64_t *p) {
 
 }  // namespace
 
-hipError_t launch_remap(const LiveRec *rec, const uint64_t *live_src, const uint32_t *key,
+hipError_t launch_remap(const void *rec, const uint64_t *live_src, const uint32_t *key,
                         const uint32_t *ridx,
                         uint64_t arena_bytes, uint64_t n, uint64_t live_blocks,
                         const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
@@ -102,10 +110,16 @@ hipError_t launch_remap(const LiveRec *rec, const uint64_t *live_src, const uint
     uint64_t grid = (n_handles + kRemapThreads - 1) / kRemapThreads;
     const uint64_t cap = (uint64_t)num_cus * 2;  // measured best of 1, 2, 3, 4, 8, 16 per CU
     if (grid > cap) grid = cap;
-    hipLaunchKernelGGL(k_remap, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s, rec, live_src,
-                       remap_keys32(arena_bytes, n) ? key : nullptr, ridx, remap_shift(arena_bytes, n), remap_buckets(arena_bytes, n),
-                       live_blocks, h_in, h_out, n_handles,
-                       reinterpret_cast<unsigned long long *>(n_invalid));
+    const uint32_t *k32 = remap_keys32(arena_bytes, n) ? key : nullptr;
+    const uint32_t w = remap_shift(arena_bytes, n);
+    const uint64_t nb = remap_buckets(arena_bytes, n);
+    unsigned long long *bad = reinterpret_cast<unsigned long long *>(n_invalid);
+    if (remap_rec32(arena_bytes))
+        hipLaunchKernelGGL(k_remap<true>, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s, rec,
+                           live_src, k32, ridx, w, nb, live_blocks, h_in, h_out, n_handles, bad);
+    else
+        hipLaunchKernelGGL(k_remap<false>, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s, rec,
+                           live_src, k32, ridx, w, nb, live_blocks, h_in, h_out, n_handles, bad);
     return hipGetLastError();
 }
 

@@ -424,15 +424,17 @@ def test_watchdog_turns_a_stalled_wait_into_an_error(ac):
 
 
 def test_remap_in_huge_arenas_with_tiny_tables(ac):
-    """A table of a few blocks in an arena of 2^35, 2^36 + 4 KiB and 2^40
-    bytes: the remap's buckets are 2^32, 2^33 and 2^37 bytes wide, so its
-    in-bucket search runs on 32-bit keys at the widest bucket they allow,
-    and on 64-bit offsets above it.  Plan and remap only (neither reads the
-    arena); every handle matches the oracle."""
+    """A table of a few blocks in an arena of 2^35, 2^36 + 4 KiB, 2^37 - 32,
+    2^37 and 2^40 bytes: the remap's buckets are 2^32 to 2^37 bytes wide, so
+    its in-bucket search runs on 32-bit keys at the widest bucket they allow
+    and on 64-bit offsets above it, and its records are the 8-byte form up
+    to the largest arena it holds (old ends up to 2^37 - 32) and the 16-byte
+    form from 2^37 on.  Plan and remap only (neither reads the arena); every
+    handle matches the oracle."""
     GiB = 1 << 30
-    for S in (1 << 35, (1 << 36) + 4096, 1 << 40):
+    for S in (1 << 35, (1 << 36) + 4096, (1 << 37) - 32, 1 << 37, 1 << 40):
         blocks = [(0, 4096), (GiB, 1 << 20), ((1 << 32) - 4096, 8192), ((1 << 32) + 4096, 4096),
-                  (S // 2, 64 * GiB if S >= (1 << 40) else 32), (S - 4096, 4096)]
+                  (S // 64 * 32, 64 * GiB if S >= (1 << 40) else 32), (S - 4096, 4096)]
         live = [0, 1, 1, 1, 1, 1]
         hs = []
         for o_, sz in blocks:
