@@ -18,6 +18,7 @@ import dataclasses
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -102,6 +103,13 @@ class defrag_compact_args(ctypes.Structure):
                 ("live_out_dev", ctypes.c_void_p), ("pinned_out_dev", ctypes.c_void_p)]
 
 
+# defrag_tile_t: one mover tile of a plan (defrag_plan_tiles)
+TILE_DTYPE = np.dtype([("dst_begin", "<u8"), ("dst_end", "<u8"), ("shift_first", "<u8"),
+                       ("first_block", "<u4"), ("last_block", "<u4"),
+                       ("dep_lo", "<u4"), ("dep_hi", "<u4")])
+assert TILE_DTYPE.itemsize == 40
+
+
 class DefragError(RuntimeError):
     def __init__(self, code: int, what: str, stats: Optional[defrag_stats_t] = None):
         self.code = code
@@ -136,6 +144,7 @@ def _load() -> ctypes.CDLL:
                                    ctypes.POINTER(defrag_stats_t)]
     L.defrag_move.argtypes = [P, U, ctypes.POINTER(defrag_plan_t), P, S, P]
     L.defrag_move_status.argtypes = [ctypes.POINTER(defrag_plan_t), P, P]
+    L.defrag_plan_tiles.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, U, P]
     L.defrag_remap.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, U, P, P]
     L.defrag_commit.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, P, P, P]
     L.defrag_compact.argtypes = [ctypes.POINTER(defrag_compact_args), P,
@@ -146,7 +155,7 @@ def _load() -> ctypes.CDLL:
     L.defrag_strerror.restype = ctypes.c_char_p
     for f in ("defrag_stats", "defrag_first_fit", "defrag_plan", "defrag_plan_targeted",
               "defrag_move", "defrag_monitor", "defrag_compact",
-              "defrag_move_status",
+              "defrag_move_status", "defrag_plan_tiles",
               "defrag_remap", "defrag_commit"):
         getattr(L, f).restype = ctypes.c_int
     return L
@@ -157,7 +166,8 @@ lib = _load()
 EXPORTS = ("defrag_workspace_bytes", "defrag_stats", "defrag_first_fit", "defrag_plan",
            "defrag_plan_targeted",
            "defrag_move",
-           "defrag_move_status", "defrag_remap", "defrag_commit", "defrag_compact", "defrag_monitor",
+           "defrag_move_status", "defrag_plan_tiles", "defrag_remap", "defrag_commit",
+           "defrag_compact", "defrag_monitor",
            "defrag_strerror")
 
 
@@ -288,6 +298,18 @@ def defrag_move(arena: torch.Tensor, plan: defrag_plan_t, ws: torch.Tensor, stre
 
 def defrag_move_status(plan: defrag_plan_t, ws: torch.Tensor, stream=None) -> int:
     return int(lib.defrag_move_status(ctypes.byref(plan), _ptr(ws), _stream(stream)))
+
+
+def defrag_plan_tiles(plan: defrag_plan_t, ws: torch.Tensor, stream=None) -> np.ndarray:
+    """The plan's mover tiles as a structured array of TILE_DTYPE."""
+    n = int(plan.n_tiles)
+    out = np.zeros(n, dtype=TILE_DTYPE)
+    rc = lib.defrag_plan_tiles(ctypes.byref(plan), _ptr(ws), ws.numel(),
+                               ctypes.c_void_p(out.ctypes.data) if n else None, n,
+                               _stream(stream))
+    if rc != DEFRAG_OK:
+        raise DefragError(rc, "defrag_plan_tiles")
+    return out
 
 
 def defrag_remap(plan: defrag_plan_t, ws: torch.Tensor, h_in: torch.Tensor,

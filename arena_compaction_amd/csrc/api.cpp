@@ -3,6 +3,7 @@
 // arena runs in the kernels (plan.hip, move.hip, remap.hip); the host only
 // turns two integers into the two fragmentation ratios (IEEE binary64).
 #include <atomic>
+#include <cstddef>
 #include <cstring>
 #include <mutex>
 
@@ -373,6 +374,35 @@ int defrag_move_status(const defrag_plan_t *plan, const void *ws_dev, hipStream_
     if (h.epoch != plan->epoch) return DEFRAG_ENOPLAN;
     if (h.status & kStatusTimeout) return DEFRAG_ETIMEOUT;
     return DEFRAG_OK;
+}
+
+int defrag_plan_tiles(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes,
+                      defrag_tile_t *out_host, uint64_t cap, hipStream_t stream) {
+    int rc = check_plan(plan, ws_dev, ws_bytes);
+    if (rc) return rc;
+    const uint64_t k = cap < plan->n_tiles ? cap : plan->n_tiles;
+    if (k && !out_host) return DEFRAG_EINVAL;
+    const WsLayout L = plan_layout(plan);
+    const uint8_t *ws = static_cast<const uint8_t *>(ws_dev);
+    WsHeader h;
+    rc = read_header(&h, ws, L, stream);
+    if (rc) return rc;
+    if (h.epoch != plan->epoch) return DEFRAG_ENOPLAN;  // planned again since
+    if (k == 0) return DEFRAG_OK;
+    // the device records are the public ones plus 8 bytes of padding
+    static_assert(sizeof(defrag_tile_t) == 40 && sizeof(TileRec) == 48 &&
+                      offsetof(TileRec, t0) == offsetof(defrag_tile_t, dst_begin) &&
+                      offsetof(TileRec, t1) == offsetof(defrag_tile_t, dst_end) &&
+                      offsetof(TileRec, shift0) == offsetof(defrag_tile_t, shift_first) &&
+                      offsetof(TileRec, first_block) == offsetof(defrag_tile_t, first_block) &&
+                      offsetof(TileRec, last_block) == offsetof(defrag_tile_t, last_block) &&
+                      offsetof(TileRec, dep_lo) == offsetof(defrag_tile_t, dep_lo) &&
+                      offsetof(TileRec, dep_hi) == offsetof(defrag_tile_t, dep_hi),
+                  "tile record layouts");
+    if (hipMemcpy2DAsync(out_host, sizeof(defrag_tile_t), ws + L.tiles, sizeof(TileRec),
+                         sizeof(defrag_tile_t), k, hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return DEFRAG_EHIP;
+    return hipStreamSynchronize(stream) == hipSuccess ? DEFRAG_OK : DEFRAG_EHIP;
 }
 
 int defrag_remap(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes,

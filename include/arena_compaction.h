@@ -260,6 +260,30 @@ int defrag_move(void *arena_dev, uint64_t arena_bytes, defrag_plan_t *plan_host,
 int defrag_move_status(const defrag_plan_t *plan_host, const void *ws_dev,
                        hipStream_t stream);
 
+/* Inspection of a plan's mover schedule, for tests and tools (the mover
+ * itself needs no call).  The moved destination bytes are cut into tiles --
+ * each the part of one run of consecutive moved blocks inside one
+ * tile_bytes-aligned window -- in ascending order; a tile loads all its
+ * sources, then stores once every earlier tile whose sources overlap its
+ * destination has loaded (the plan's answer to the in-place hazards of the
+ * 910C page's "Periodic compaction with Ascend C" move step).  Copies the
+ * first min(cap, plan_host->n_tiles) tiles to out_host and synchronises the
+ * stream.  Valid after defrag_plan and after defrag_move, until the
+ * workspace is planned again (DEFRAG_ENOPLAN then). */
+typedef struct defrag_tile_t {
+    uint64_t dst_begin;    /* destination bytes [dst_begin, dst_end)          */
+    uint64_t dst_end;
+    uint64_t shift_first;  /* shift of the tile's first block                 */
+    uint32_t first_block;  /* packed live-block indices (order of the table's */
+    uint32_t last_block;   /* live entries) of the blocks the tile covers     */
+    uint32_t dep_lo;       /* the earlier tiles it waits for, dep_lo..dep_hi; */
+    uint32_t dep_hi;       /* none when dep_lo > dep_hi                       */
+} defrag_tile_t;
+
+int defrag_plan_tiles(const defrag_plan_t *plan_host, const void *ws_dev,
+                      size_t ws_bytes, defrag_tile_t *out_host, uint64_t cap,
+                      hipStream_t stream);
+
 /* Remap handles (910C: update every reference in one batch).  h_out_dev may
  * equal h_in_dev.  *n_invalid_dev (may be NULL) receives the number of
  * handles mapped to UINT64_MAX.  Needs a valid plan of the table the handles

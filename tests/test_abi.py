@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
     for f in ("defrag_stats", "defrag_first_fit", "defrag_plan", "defrag_plan_targeted",
               "defrag_compact", "defrag_move", "defrag_remap",
               "defrag_workspace_bytes", "defrag_strerror", "defrag_commit",
-              "defrag_move_status"):
+              "defrag_move_status", "defrag_plan_tiles"):
         assert f in fns, f
 
 
@@ -74,6 +74,7 @@ def test_host_side_argument_errors_need_no_gpu():
     assert L.defrag_remap(ctypes.byref(plan), None, 0, None, None, 0, None, None) == ac.DEFRAG_ENOPLAN
     assert L.defrag_commit(ctypes.byref(plan), None, 0, None, None, None, None, None) == ac.DEFRAG_ENOPLAN
     assert L.defrag_move_status(ctypes.byref(plan), None, None) == ac.DEFRAG_ENOPLAN
+    assert L.defrag_plan_tiles(ctypes.byref(plan), None, 0, None, 0, None) == ac.DEFRAG_ENOPLAN
     # missing table / output pointers
     st = ac.defrag_stats_t()
     assert L.defrag_stats(None, 0, None, 0, None, ctypes.byref(st)) == ac.DEFRAG_EINVAL
