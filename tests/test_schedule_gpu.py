@@ -150,3 +150,31 @@ def test_schedule_full_size(ac, k):
     plan = check_schedule(ac, heap)
     log(f"  {plan.n_tiles} tiles, {plan.whole_tiles} whole")
     torch.cuda.empty_cache()
+
+
+def test_plan_tiles_protocol(ac):
+    """A partial copy returns the first tiles; a plan whose workspace was
+    planned again is refused (DEFRAG_ENOPLAN), as is a plan from nowhere."""
+    import ctypes
+    heap = W.workload("mixed-64m", small=True)
+    off, size, live = device_table(heap, "cuda")
+    ws = ac.workspace(heap.n, heap.arena_bytes, 4096)
+    tu = ac.defrag_tuning(4096, 0, 1, 0)
+    p1 = ac.defrag_plan(off, size, live, heap.arena_bytes, ws, tuning=tu)
+    full = ac.defrag_plan_tiles(p1, ws)
+    assert full.shape[0] == p1.n_tiles > 8
+    part = np.zeros(5, dtype=ac.TILE_DTYPE)
+    rc = ac.lib.defrag_plan_tiles(ctypes.byref(p1), ac._ptr(ws), ws.numel(),
+                                  ctypes.c_void_p(part.ctypes.data), 5, None)
+    assert rc == ac.DEFRAG_OK and np.array_equal(part, full[:5])
+    # cap 0 needs no output buffer
+    assert ac.lib.defrag_plan_tiles(ctypes.byref(p1), ac._ptr(ws), ws.numel(), None, 0,
+                                    None) == ac.DEFRAG_OK
+    # a missing output with a non-zero cap
+    assert ac.lib.defrag_plan_tiles(ctypes.byref(p1), ac._ptr(ws), ws.numel(), None, 5,
+                                    None) == ac.DEFRAG_EINVAL
+    p2 = ac.defrag_plan(off, size, live, heap.arena_bytes, ws, tuning=tu)
+    with pytest.raises(ac.DefragError) as e:
+        ac.defrag_plan_tiles(p1, ws)
+    assert e.value.code == ac.DEFRAG_ENOPLAN
+    assert np.array_equal(ac.defrag_plan_tiles(p2, ws), full)
