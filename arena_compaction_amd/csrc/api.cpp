@@ -16,6 +16,11 @@ namespace {
 
 constexpr uint64_t kPlanMagic = 0x4e414c5047415244ull;  // "DRAGPLAN"
 
+// defrag_compact runs the remap beside the move when the move has more than
+// this many moved bytes per handle (the remap's probes slow a short move by
+// more than they save).
+constexpr uint64_t kRemapOverlapBytesPerHandle = 1024;
+
 std::atomic<uint64_t> g_epoch{0x9E3779B97F4A7C15ull};
 
 int num_cus_of(int dev) {
@@ -455,6 +460,7 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     const bool arena_ok = a->arena_dev && !(reinterpret_cast<uintptr_t>(a->arena_dev) & 15u);
     const bool post_ok = !after_host || (a->offset_out_dev && a->size_out_dev);
     const bool wg_ok = !a->tuning || a->tuning->wg_per_cu != 0;
+    bool remap_done = false;
     int rc;
     if (arena_ok && post_ok && wg_ok) {
         PlanCtx c;
@@ -496,6 +502,22 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
         rc = plan_fill(a->table, a->arena_bytes, a->request_bytes, a->ws_dev, c, hp, plan);
         if (rc) return rc;
         plan->state = 2;
+        // The remap reads the plan and the handles, never the arena.  When
+        // the move is long beside it, it runs on the side stream while the
+        // move does, and the stream waits for it before the post-check.
+        if ((a->n_handles || a->n_invalid_dev) &&
+            plan->stats.moved_bytes / kRemapOverlapBytesPerHandle > a->n_handles) {
+            rc = defrag_remap(plan, a->ws_dev, a->ws_bytes, a->h_in_dev, a->h_out_dev,
+                              a->n_handles, a->n_invalid_dev, side);
+            if (rc) return rc;
+            hipEvent_t remapped = nullptr;
+            if (hipEventCreateWithFlags(&remapped, hipEventDisableTiming) != hipSuccess)
+                return DEFRAG_EHIP;
+            const bool joined = hipEventRecord(remapped, side) == hipSuccess &&
+                                hipStreamWaitEvent(stream, remapped, 0) == hipSuccess;
+            if (hipEventDestroy(remapped) != hipSuccess || !joined) return DEFRAG_EHIP;
+            remap_done = true;
+        }
     } else {
         rc = a->request_bytes
                  ? defrag_plan_targeted(a->table, a->arena_bytes, a->request_bytes, a->tuning,
@@ -511,7 +533,7 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
         rc = defrag_move(a->arena_dev, a->arena_bytes, plan, a->ws_dev, a->ws_bytes, stream);
         if (rc) return rc;
     }
-    if (a->n_handles || a->n_invalid_dev) {
+    if (!remap_done && (a->n_handles || a->n_invalid_dev)) {
         rc = defrag_remap(plan, a->ws_dev, a->ws_bytes, a->h_in_dev, a->h_out_dev, a->n_handles,
                           a->n_invalid_dev, stream);
         if (rc) return rc;

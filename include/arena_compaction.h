@@ -312,8 +312,10 @@ int defrag_commit(const defrag_plan_t *plan_host, const void *ws_dev,
  * takes its tile count and workgroup count from the plan in the workspace,
  * and moves nothing if the plan failed; the plan is read back on a second
  * stream (one per device, created on first use and kept) while the move
- * runs, and one read at the end brings the post-check and the mover's
- * status.  With a NULL or misaligned arena, a tuning of wg_per_cu 0, or
+ * runs; when the move has more than 1024 moved bytes per handle the remap
+ * (which never reads the arena) then runs on that stream beside the move,
+ * and the stream waits for it; one read at the end brings the post-check
+ * and the mover's status.  With a NULL or misaligned arena, a tuning of wg_per_cu 0, or
  * after_host without offset_out_dev and size_out_dev, the steps run in the
  * plain order instead (plan, read back, argument checks, move).  Returns
  * the first failing step's code (nothing moves if the plan fails;
