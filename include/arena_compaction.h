@@ -136,7 +136,7 @@ typedef struct defrag_stats_t {
 typedef struct defrag_tuning {
     uint32_t tile_bytes;      /* mover tile: power of two in [256, 131072].
                                  Fixed at plan time.  Compactions made mostly
-                                 of small shifts (under ~16 MiB, so a tile
+                                 of small shifts (under ~5 MiB, so a tile
                                  often waits on one still being read) run
                                  faster with 131072 and wg_per_cu 2.          */
     uint32_t wg_per_cu;       /* mover workgroups per compute unit; 0 means as
