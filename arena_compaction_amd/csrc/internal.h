@@ -139,7 +139,7 @@ static_assert(sizeof(TileRec) == 48, "tile record size");
 // One live block as the handle remap reads it, once its search has found
 // the last block starting at or below a handle h: h lies in it iff h < end,
 // and then maps to h - shift.  16 bytes; arenas below 2^37 bytes use the
-// 8-byte LiveRec32 below instead.
+// 8-byte LiveRec32 below, or the 16-byte key-and-record RemapEnt.
 struct alignas(16) LiveRec {
     uint64_t end;    // old offset + size
     uint64_t shift;  // old offset - new offset (0 for a block that stays)
@@ -148,8 +148,9 @@ static_assert(sizeof(LiveRec) == 16, "live record size");
 
 // The same record in 32-byte units, 8 bytes, for arenas below 2^37 bytes
 // (every offset and size is a multiple of 32, so nothing is lost and the
-// old end fits in 32 bits): half the cache footprint of LiveRec -- the 80 GiB
-// training arena's 183k live blocks take 1.5 MB instead of 2.9 MB.
+// old end fits in 32 bits): half the cache footprint of LiveRec.  Used when
+// the remap's buckets are wider than 2^32 bytes (a few blocks in an arena of
+// 2^35 bytes or more); narrower buckets put it beside the key in RemapEnt.
 struct alignas(8) LiveRec32 {
     uint32_t end32;    // (old offset + size) / 32
     uint32_t shift32;  // (old offset - new offset) / 32
@@ -180,6 +181,21 @@ inline uint64_t remap_buckets(uint64_t arena_bytes, uint64_t n) {
 // table in an arena above 2^35 bytes) search the 64-bit offsets.
 inline bool remap_keys32(uint64_t arena_bytes, uint64_t n) {
     return remap_shift(arena_bytes, n) <= 32;
+}
+
+// Both 32-bit forms at once (arenas below 2^37 bytes, buckets of at most
+// 2^32): a live block's search key and its record side by side in 16 bytes,
+// so the probe that finds the block has read its record too.
+struct alignas(16) RemapEnt {
+    uint32_t key;      // old offset inside its bucket
+    uint32_t end32;    // (old offset + size) / 32
+    uint32_t shift32;  // (old offset - new offset) / 32
+    uint32_t pad;
+};
+static_assert(sizeof(RemapEnt) == 16 && sizeof(RemapEnt) <= sizeof(LiveRec),
+              "remap entries share the record region");
+inline bool remap_ent(uint64_t arena_bytes, uint64_t n) {
+    return remap_rec32(arena_bytes) && remap_keys32(arena_bytes, n);
 }
 
 constexpr size_t kPerTileBytes =

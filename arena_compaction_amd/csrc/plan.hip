@@ -264,6 +264,7 @@ struct LiveOut {
     uint32_t *pc;  // pinned blocks below each live block (selection only)
     LiveRec *rec;      // the remap's (old end, shift) per live block, or
     LiveRec32 *rec32;  // the same in 32-byte units (arenas below 2^37 bytes)
+    RemapEnt *ent;     // or key and 32-bit record together (then rec, rec32, key null)
     uint32_t *key;      // the remap's 32-bit search keys (null: 64-bit offsets)
     uint64_t key_mask;  // old offset -> offset inside its remap bucket
 };
@@ -314,7 +315,11 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
                 if (outputs & kOutNew) {
                     lo.dst[run.cnt] = nw;
                     lo.pin[run.cnt] = (uint8_t)p[k];
-                    if (lo.rec32)
+                    if (lo.ent)
+                        lo.ent[run.cnt] = RemapEnt{(uint32_t)(o[k] & lo.key_mask),
+                                                   (uint32_t)((o[k] + s[k]) >> 5),
+                                                   (uint32_t)((o[k] - nw) >> 5), 0u};
+                    else if (lo.rec32)
                         lo.rec32[run.cnt] = LiveRec32{(uint32_t)((o[k] + s[k]) >> 5),
                                                       (uint32_t)((o[k] - nw) >> 5)};
                     else
@@ -843,12 +848,16 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
                reinterpret_cast<uint8_t *>(ws + L.live_pin),
                reinterpret_cast<uint64_t *>(ws + L.live_z),
                reinterpret_cast<uint32_t *>(ws + L.live_pc),
-               nullptr, nullptr, nullptr, 0};
-    if (remap_rec32(arena_bytes))
+               nullptr, nullptr, nullptr, nullptr, 0};
+    if (remap_ent(arena_bytes, t.n)) {
+        lo.ent = reinterpret_cast<RemapEnt *>(ws + L.live_rec);
+        lo.key_mask = (1ull << remap_shift(arena_bytes, t.n)) - 1;
+    } else if (remap_rec32(arena_bytes)) {
         lo.rec32 = reinterpret_cast<LiveRec32 *>(ws + L.live_rec);
-    else
+    } else {
         lo.rec = reinterpret_cast<LiveRec *>(ws + L.live_rec);
-    if (remap_keys32(arena_bytes, t.n)) {
+    }
+    if (!lo.ent && remap_keys32(arena_bytes, t.n)) {
         lo.key = reinterpret_cast<uint32_t *>(ws + L.live_key);
         lo.key_mask = (1ull << remap_shift(arena_bytes, t.n)) - 1;
     }

@@ -14,11 +14,14 @@
 // maps to itself.  Random handles make the search bound by L2 requests (each
 // probe of each lane is its own cache line), so the plan builds an index --
 // the arena cut into at most 2^18 power-of-two buckets, each pointing at the
-// first live block starting in it -- and each live block also has one
-// record (old end, shift: 8 bytes in 32-byte units below 2^37 arena bytes,
-// else 16) and a 32-bit search key (its old offset inside its bucket).  HBM
-// traffic is 16 B per handle; the index, keys and records stay in L2 / the
-// last-level cache.
+// first live block starting in it -- and each live block also has a search
+// key (its old offset inside its bucket) and a record (old end, shift).  In
+// arenas below 2^37 bytes with buckets of at most 2^32 bytes (the usual
+// case) both fit in 32 bits and sit side by side in one 16-byte entry, so
+// the probe that finds a block has its record too (k_remap_ent); otherwise
+// keys and records are separate arrays, the keys 32- or 64-bit and the
+// records 8 or 16 bytes (k_remap).  HBM traffic is 16 B per handle; the
+// index and the entries stay in L2 / the last-level cache.
 #include "internal.h"
 
 namespace ac {
@@ -91,6 +94,59 @@ __global__ __launch_bounds__(kRemapThreads) void k_remap(const void *__restrict_
     }
 }
 
+// The same with key and record side by side (RemapEnt): each probe that
+// finds a block at or below h has read that block's record with its key, so
+// the last such probe leaves the answer in registers; only a handle below
+// the bucket's first block start reads a record afterwards, that of the
+// block before the bucket.
+__global__ __launch_bounds__(kRemapThreads) void k_remap_ent(const RemapEnt *__restrict__ ent,
+                                                             const uint32_t *__restrict__ ridx,
+                                                             uint32_t w, uint64_t nb, uint64_t m,
+                                                             const uint64_t *h_in, uint64_t *h_out,
+                                                             uint64_t H,
+                                                             unsigned long long *n_invalid) {
+    uint64_t bad = 0;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < H; k += stride) {
+        const uint64_t h = h_in[k];
+        uint64_t out = kNone;
+        const uint64_t b = h >> w;
+        if (m && b < nb) {
+            const uint64_t r0 = ridx[b];
+            uint64_t first = r0, len = ridx[b + 1] - r0;
+            const uint32_t hk = (uint32_t)(h & ((1ull << w) - 1));
+            uint32_t end32 = 0, shift32 = 0;
+            bool hit = false;
+            while (len > 0) {
+                const uint64_t half = len >> 1;
+                const RemapEnt e = ent[first + half];
+                if (e.key <= hk) {
+                    end32 = e.end32;
+                    shift32 = e.shift32;
+                    hit = true;
+                    first += half + 1;
+                    len -= half + 1;
+                } else {
+                    len = half;
+                }
+            }
+            if (!hit && r0 > 0) {  // the block before the bucket
+                const RemapEnt e = ent[r0 - 1];
+                end32 = e.end32;
+                shift32 = e.shift32;
+            }
+            if (h < ((uint64_t)end32 << 5)) out = h - ((uint64_t)shift32 << 5);
+        }
+        bad += (out == kNone) ? 1u : 0u;
+        h_out[k] = out;
+    }
+    if (n_invalid) {
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) bad += __shfl_xor(bad, d, 64);
+        if ((threadIdx.x & 63) == 0 && bad) atomicAdd(n_invalid, (unsigned long long)bad);
+    }
+}
+
 __global__ void k_zero_u64(uint64_t *p) {
     if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0;
 }
@@ -114,7 +170,11 @@ hipError_t launch_remap(const void *rec, const uint64_t *live_src, const uint32_
     const uint32_t w = remap_shift(arena_bytes, n);
     const uint64_t nb = remap_buckets(arena_bytes, n);
     unsigned long long *bad = reinterpret_cast<unsigned long long *>(n_invalid);
-    if (remap_rec32(arena_bytes))
+    if (remap_ent(arena_bytes, n))
+        hipLaunchKernelGGL(k_remap_ent, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s,
+                           static_cast<const RemapEnt *>(rec), ridx, w, nb, live_blocks, h_in,
+                           h_out, n_handles, bad);
+    else if (remap_rec32(arena_bytes))
         hipLaunchKernelGGL(k_remap<true>, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s, rec,
                            live_src, k32, ridx, w, nb, live_blocks, h_in, h_out, n_handles, bad);
     else

@@ -457,6 +457,35 @@ def test_remap_in_huge_arenas_with_tiny_tables(ac):
         del ws
 
 
+def test_remap_in_a_huge_arena_with_narrow_buckets(ac):
+    """64 blocks spread over a 2^38-byte arena: the remap's buckets are 2^31
+    bytes wide (32-bit keys) while the arena needs 16-byte records, the one
+    combination the tiny tables above do not reach.  Plan and remap only."""
+    S = 1 << 38
+    step = S // 64
+    blocks = [(i * step + (i % 7) * 4096, 4096 * (1 + i % 5)) for i in range(64)]
+    live = [i % 3 != 1 for i in range(64)]
+    hs = []
+    for o_, sz in blocks:
+        for p in (o_, o_ + sz - 1, o_ + sz, o_ + sz // 2):
+            for dlt in (-32, -1, 0, 1, 32):
+                if 0 <= p + dlt:
+                    hs.append(p + dlt)
+    hs += [S - 1, S, (1 << 37) - 1, 1 << 37, (1 << 64) - 1]
+    heap = W.table_from_lists(S, blocks, [int(v) for v in live], hs, name="huge narrow")
+    log(f"case {heap.describe()} remap only")
+    off, size, lv = device_table(heap, "cuda")
+    ws = ac.workspace(heap.n, S, 131072)
+    plan = ac.defrag_plan(off, size, lv, S, ws, tuning=ac.defrag_tuning(131072, 0, 1, 0))
+    h = torch.from_numpy(heap.handles.view(np.int64)).cuda()
+    nb = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out = ac.defrag_remap(plan, ws, h, n_invalid=nb)
+    torch.cuda.synchronize()
+    want, bad = oracle.remap(heap.offset, heap.size, heap.live, heap.handles)
+    assert np.array_equal(out.cpu().numpy().view(np.uint64), want) and int(nb) == bad
+    del ws
+
+
 def test_remap_at_bucket_boundaries(ac):
     """Blocks that start and end exactly on power-of-two boundaries, holes
     that span many of them, and handles on every 4 KiB boundary and 16/32
