@@ -34,18 +34,18 @@
 // (pinned blocks, and the packed prefix of each segment) are in no tile and
 // are never touched; nor is any byte no block lands on.
 //
-// Most tiles are one whole T-byte window of a single block.  Those take a
-// straight-line path: every lane loads and stores at fixed offsets from two
-// uniform bases, with no per-vector predicate, so all sixteen loads and all
-// sixteen stores of a lane stay in flight together (behind a per-vector
-// branch the compiler waits for each store before the next).  Partial and
-// multi-block tiles take the general path, also without a branch around any
-// memory access: a lane outside the tile's range reloads the tile's first
-// source vector, and stores go through a buffer descriptor over the tile's
-// window, a disabled lane getting an offset the hardware drops as out of
-// range.  The dependency flags are read
-// once speculatively, right behind the tile's data loads: a dependency far
-// below is long done, and the tile then stores without another round trip.
+// Every tile, whole window of one block or not, takes one path with no
+// branch around a memory access, so all of a lane's loads, and then all of
+// its stores, stay in flight together (behind a per-vector branch the
+// compiler waits for each store before the next): a lane outside the tile's
+// range reloads the tile's first source vector, and stores go through a
+// buffer descriptor over the tile's window, a disabled lane getting an
+// offset the hardware drops as out of range.  (A separate straight-line
+// path for whole single-block tiles, with global stores from uniform bases,
+// was 0.8-1.0 points slower on the large workloads.)  The dependency flags
+// are read once speculatively, right behind the tile's data loads: a
+// dependency far below is long done, and the tile then stores without
+// another round trip.
 //
 // Vectors are 16 bytes: offsets and sizes are multiples of 32, so a vector
 // never straddles two blocks and both of its addresses are 16-byte aligned.
@@ -66,13 +66,6 @@ __device__ __forceinline__ v4u load16(const uint8_t *p) {
     const v4u *q = reinterpret_cast<const v4u *>(p);
     if constexpr ((NT & 1) != 0) return __builtin_nontemporal_load(q);
     else return *q;
-}
-
-template <int NT>
-__device__ __forceinline__ void store16(uint8_t *p, v4u v) {
-    v4u *q = reinterpret_cast<v4u *>(p);
-    if constexpr ((NT & 2) != 0) __builtin_nontemporal_store(v, q);
-    else *q = v;
 }
 
 // Raw buffer resource (gfx9 family): word 3 of the descriptor, the
@@ -143,8 +136,6 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
         const uint32_t rel1 = (uint32_t)(t1 - tb);
         const uint32_t nblk = last - first + 1u;
         bool ok = nblk <= a.max_blocks;
-        const bool whole = (uint64_t)VPT * kMoveRowBytes == a.tile_bytes && nblk == 1u &&
-                           rel0 == 0u && rel1 == a.tile_bytes;
 
         if (nblk > 1u && ok) {
             for (uint32_t k = tid; k < nblk; k += kMoveThreads) {
@@ -155,31 +146,25 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
             __syncthreads();
         }
 
+        // no branch around a memory access: a lane outside [rel0, rel1)
+        // reloads the tile's first source vector and discards it
         v4u v[VPT];
-        if (whole) {
-            const uint8_t *src = a.arena + tb + shift0 + tid * 16u;
+        const uint8_t *first_src = a.arena + tb + rel0 + shift0;
 #pragma unroll
-            for (int j = 0; j < VPT; ++j) v[j] = load16<NT>(src + (size_t)j * kMoveRowBytes);
-        } else {
-            // no branch around a memory access: a lane outside [rel0, rel1)
-            // reloads the tile's first source vector and discards it
-            const uint8_t *first_src = a.arena + tb + rel0 + shift0;
-#pragma unroll
-            for (int j = 0; j < VPT; ++j) {
-                const uint32_t r = ((uint32_t)j * kMoveThreads + tid) * 16u;
-                uint64_t sh = shift0;
-                if (nblk > 1u && ok) {
-                    uint32_t lo = 0, n = nblk;  // largest k with s_rel[k] <= r
-                    while (n > 1u) {
-                        const uint32_t half = n >> 1;
-                        lo = (s_rel[lo + half] <= r) ? lo + half : lo;
-                        n -= half;
-                    }
-                    sh = s_shift[lo];
+        for (int j = 0; j < VPT; ++j) {
+            const uint32_t r = ((uint32_t)j * kMoveThreads + tid) * 16u;
+            uint64_t sh = shift0;
+            if (nblk > 1u && ok) {
+                uint32_t lo = 0, n = nblk;  // largest k with s_rel[k] <= r
+                while (n > 1u) {
+                    const uint32_t half = n >> 1;
+                    lo = (s_rel[lo + half] <= r) ? lo + half : lo;
+                    n -= half;
                 }
-                const bool in = ok && r >= rel0 && r < rel1;
-                v[j] = load16<NT>(in ? a.arena + tb + r + sh : first_src);
+                sh = s_shift[lo];
             }
+            const bool in = ok && r >= rel0 && r < rel1;
+            v[j] = load16<NT>(in ? a.arena + tb + r + sh : first_src);
         }
         // first look at the dependency flags, returned with the data loads
         uint32_t f_lo = 0u, f_hi = 0u;
@@ -217,23 +202,17 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
         }
         __syncthreads();
         if (!s_skip) {
-            if (whole) {
-                uint8_t *dst = a.arena + tb + tid * 16u;
+            // buffer stores over the tile's window: a lane outside [rel0,
+            // rel1) gets an offset past the window's end, which the hardware
+            // drops -- no branch around any store
+            const __amdgpu_buffer_rsrc_t win = __builtin_amdgcn_make_buffer_rsrc(
+                a.arena + tb, 0, (int)a.tile_bytes, kBufferRsrcWord3);
 #pragma unroll
-                for (int j = 0; j < VPT; ++j) store16<NT>(dst + (size_t)j * kMoveRowBytes, v[j]);
-            } else {
-                // buffer stores over the tile's window: a lane outside
-                // [rel0, rel1) gets an offset past the window's end, which
-                // the hardware drops -- no branch around any store
-                const __amdgpu_buffer_rsrc_t win = __builtin_amdgcn_make_buffer_rsrc(
-                    a.arena + tb, 0, (int)a.tile_bytes, kBufferRsrcWord3);
-#pragma unroll
-                for (int j = 0; j < VPT; ++j) {
-                    const uint32_t r = ((uint32_t)j * kMoveThreads + tid) * 16u;
-                    const uint32_t off = (r >= rel0 && r < rel1) ? r : kOutOfWindow;
-                    __builtin_amdgcn_raw_buffer_store_b128(v[j], win, (int)off, 0,
-                                                           (NT & 2) ? kBufferNt : 0);
-                }
+            for (int j = 0; j < VPT; ++j) {
+                const uint32_t r = ((uint32_t)j * kMoveThreads + tid) * 16u;
+                const uint32_t off = (r >= rel0 && r < rel1) ? r : kOutOfWindow;
+                __builtin_amdgcn_raw_buffer_store_b128(v[j], win, (int)off, 0,
+                                                       (NT & 2) ? kBufferNt : 0);
             }
         }
         // Claim the next tile only now: each workgroup holds one ticket at a
