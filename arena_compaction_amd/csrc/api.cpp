@@ -267,7 +267,6 @@ int plan_fill(const defrag_table *table, uint64_t arena_bytes, uint64_t request,
     if (mb > T / 32 + 2) mb = T / 32 + 2;
     plan->max_blocks_per_tile = mb;
     plan->whole_tiles = h.whole_tiles;
-    if (!c.tuned) tu.wg_per_cu = auto_wg_per_cu(h.whole_tiles, h.n_tiles);
     plan->tuning = tu;
     if (request) {
         plan->request_bytes = request;

@@ -104,8 +104,7 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
                 // moves nothing; workgroups past the chosen count leave
                 const WsHeader *h = a.hdr;
                 nt = h->n_tiles;
-                const uint32_t per_cu = a.wg_per_cu ? a.wg_per_cu
-                                                    : auto_wg_per_cu(h->whole_tiles, nt);
+                const uint32_t per_cu = a.wg_per_cu ? a.wg_per_cu : kDefaultWgPerCu;
                 go = h->bad_key == kNone && h->win_state != kWinNoFit && nt <= a.max_tiles &&
                      blockIdx.x < (uint64_t)per_cu * a.num_cus;
             }
@@ -243,16 +242,14 @@ hipError_t launch_t(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStrea
     return hipGetLastError();
 }
 
-// The device-sized mover: a grid for the largest workgroup count the rule
-// can pick (the workgroups past the plan's choice leave at once), LDS for
-// the most blocks a tile can meet.
-constexpr uint32_t kMaxAutoWgPerCu = kWgPerCuWhole > kDefaultWgPerCu ? kWgPerCuWhole
-                                                                      : kDefaultWgPerCu;
+// The device-sized mover: the grid the plan's tuning asks for (the plan is
+// not read back first: the workgroups read its tile count from the device),
+// LDS for the most blocks a tile can meet.
 
 template <int VPT, int NT>
 hipError_t launch_device_sized_t(const MoveArgs &a, hipStream_t s) {
     const size_t lds = (size_t)a.max_blocks * 12u + 16u;
-    const uint64_t per_cu = a.wg_per_cu ? a.wg_per_cu : kMaxAutoWgPerCu;
+    const uint64_t per_cu = a.wg_per_cu ? a.wg_per_cu : kDefaultWgPerCu;
     uint64_t grid = per_cu * (uint64_t)a.num_cus;
     if (grid > kMaxMoveGrid) grid = kMaxMoveGrid;
     if (grid < 1) grid = 1;

@@ -262,7 +262,7 @@ def main() -> int:
     arena = torch.empty(S, dtype=torch.uint8, device=dev)
     tuning = None   # library defaults unless a knob is overridden
     if args.tile is not None or args.wg_per_cu is not None or args.nontemporal is not None:
-        tuning = ac.defrag_tuning(args.tile or 0, 2 if args.wg_per_cu is None else args.wg_per_cu,
+        tuning = ac.defrag_tuning(args.tile or 0, 1 if args.wg_per_cu is None else args.wg_per_cu,
                                   1 if args.nontemporal is None else args.nontemporal, 0)
     ws = ac.workspace(heap.n, S, args.tile or 0, device=dev, max_pinned=heap.n_pinned)
     new_off = torch.empty(heap.n, dtype=torch.int64, device=dev)

@@ -128,17 +128,16 @@ typedef struct defrag_stats_t {
 } defrag_stats_t;
 
 /* Optional knobs.  Passing NULL takes the defaults: 65536-byte tiles,
- * streaming loads and stores, and one mover workgroup per compute unit when
- * at least half the tiles are whole single-block windows, else two (the
- * plan decides, and records its choice in plan_host->tuning).  In a struct
- * passed explicitly, a zero tile size or spin limit takes its default and
- * the other fields are taken as given. */
+ * streaming loads and stores, and one 512-lane mover workgroup per compute
+ * unit (recorded in plan_host->tuning).  In a struct passed explicitly, a
+ * zero tile size or spin limit takes its default and the other fields are
+ * taken as given. */
 typedef struct defrag_tuning {
     uint32_t tile_bytes;      /* mover tile: power of two in [256, 131072].
                                  Fixed at plan time.  Compactions made mostly
-                                 of small shifts (under ~5 MiB, so a tile
+                                 of small shifts (up to ~6 MiB, so a tile
                                  often waits on one still being read) run
-                                 faster with 131072 and wg_per_cu 2.          */
+                                 faster with 131072.                          */
     uint32_t wg_per_cu;       /* mover workgroups per compute unit; 0 means as
                                  many as the kernel's resources allow         */
     uint32_t nontemporal;     /* streaming hints: 0 none, 1 loads and stores,
