@@ -157,6 +157,25 @@ int stats_pass(const defrag_table *table, uint64_t arena_bytes, uint64_t fit_nee
     return h->bad_key == kNone ? DEFRAG_OK : DEFRAG_EINVAL;
 }
 
+// The one-call path's post-check, queued on the side stream while the move
+// may still run: the statistics pass of the packed table, with its own
+// header (the move reads the plan's header as it starts) and otherwise only
+// the scratch region below the plan's data (the packed table has no more
+// entries than the planned one).
+int post_check_queue(const defrag_table *packed, uint64_t arena_bytes, void *ws_dev,
+                     size_t ws_bytes, hipStream_t stream) {
+    int rc = check_table(packed);
+    if (rc) return rc;
+    WsLayout L = ws_fixed(packed->n);
+    rc = check_ws(ws_dev, ws_bytes, L.tpart);
+    if (rc) return rc;
+    L.header = L.post;
+    return launch_scan(view_of(packed), arena_bytes, static_cast<uint8_t *>(ws_dev), L, nullptr,
+                       0, kDefaultTile, 0, kNone, stream) == hipSuccess
+               ? DEFRAG_OK
+               : DEFRAG_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -459,7 +478,7 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     const bool arena_ok = a->arena_dev && !(reinterpret_cast<uintptr_t>(a->arena_dev) & 15u);
     const bool post_ok = !after_host || (a->offset_out_dev && a->size_out_dev);
     const bool wg_ok = !a->tuning || a->tuning->wg_per_cu != 0;
-    bool remap_done = false;
+    bool remap_done = false, commit_done = false, post_done = false;
     int rc;
     if (arena_ok && post_ok && wg_ok) {
         PlanCtx c;
@@ -501,21 +520,41 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
         rc = plan_fill(a->table, a->arena_bytes, a->request_bytes, a->ws_dev, c, hp, plan);
         if (rc) return rc;
         plan->state = 2;
-        // The remap reads the plan and the handles, never the arena.  When
-        // the move is long beside it, it runs on the side stream while the
-        // move does, and the stream waits for it before the post-check.
+        // Remap, commit and the post-check read the plan, never the arena,
+        // so they run on the side stream while the move does, and the
+        // stream waits for them at the end.  The remap goes there only when
+        // the move is long beside it (its probes slow a short move more
+        // than they save); the post-check writes its own header.
         if ((a->n_handles || a->n_invalid_dev) &&
             plan->stats.moved_bytes / kRemapOverlapBytesPerHandle > a->n_handles) {
             rc = defrag_remap(plan, a->ws_dev, a->ws_bytes, a->h_in_dev, a->h_out_dev,
                               a->n_handles, a->n_invalid_dev, side);
             if (rc) return rc;
-            hipEvent_t remapped = nullptr;
-            if (hipEventCreateWithFlags(&remapped, hipEventDisableTiming) != hipSuccess)
-                return DEFRAG_EHIP;
-            const bool joined = hipEventRecord(remapped, side) == hipSuccess &&
-                                hipStreamWaitEvent(stream, remapped, 0) == hipSuccess;
-            if (hipEventDestroy(remapped) != hipSuccess || !joined) return DEFRAG_EHIP;
             remap_done = true;
+        }
+        if (a->offset_out_dev || a->size_out_dev || a->live_out_dev || a->pinned_out_dev) {
+            rc = defrag_commit(plan, a->ws_dev, a->ws_bytes, a->offset_out_dev,
+                               a->size_out_dev, a->live_out_dev, a->pinned_out_dev, side);
+            if (rc) return rc;
+            commit_done = true;
+        }
+        if (after_host) {
+            const defrag_table packed{a->offset_out_dev, a->size_out_dev, a->live_out_dev,
+                                      plan->live_blocks, a->pinned_out_dev};
+            rc = post_check_queue(&packed, a->arena_bytes, a->ws_dev, a->ws_bytes, side);
+            if (rc) {
+                arg_error(after_host);
+                return rc;
+            }
+            post_done = true;
+        }
+        if (remap_done || commit_done || post_done) {
+            hipEvent_t joined_ev = nullptr;
+            if (hipEventCreateWithFlags(&joined_ev, hipEventDisableTiming) != hipSuccess)
+                return DEFRAG_EHIP;
+            const bool joined = hipEventRecord(joined_ev, side) == hipSuccess &&
+                                hipStreamWaitEvent(stream, joined_ev, 0) == hipSuccess;
+            if (hipEventDestroy(joined_ev) != hipSuccess || !joined) return DEFRAG_EHIP;
         }
     } else {
         rc = a->request_bytes
@@ -537,15 +576,30 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
                           a->n_invalid_dev, stream);
         if (rc) return rc;
     }
-    if (a->offset_out_dev || a->size_out_dev || a->live_out_dev || a->pinned_out_dev) {
+    if (!commit_done &&
+        (a->offset_out_dev || a->size_out_dev || a->live_out_dev || a->pinned_out_dev)) {
         rc = defrag_commit(plan, a->ws_dev, a->ws_bytes, a->offset_out_dev, a->size_out_dev,
                            a->live_out_dev, a->pinned_out_dev, stream);
         if (rc) return rc;
     }
     // one synchronisation: the post-move statistics (if asked for) and the
-    // mover's status come back in the same header read
+    // mover's status come back in the same read
     WsHeader h;
-    if (after_host) {
+    if (post_done) {
+        // the plan's header and the post-check's, adjacent in the workspace
+        const WsLayout L = plan_layout(plan);
+        static_assert(sizeof(WsHeader) == 256, "two adjacent headers");
+        WsHeader both[2];
+        const uint8_t *ws = static_cast<const uint8_t *>(a->ws_dev);
+        if (L.post != L.header + sizeof(WsHeader) ||
+            hipMemcpyAsync(both, ws + L.header, sizeof(both), hipMemcpyDeviceToHost, stream) !=
+                hipSuccess ||
+            hipStreamSynchronize(stream) != hipSuccess)
+            return DEFRAG_EHIP;
+        h = both[0];
+        fill_stats(after_host, both[1], a->arena_bytes);
+        if (both[1].bad_key != kNone) return DEFRAG_EINVAL;
+    } else if (after_host) {
         const defrag_table packed{a->offset_out_dev, a->size_out_dev, a->live_out_dev,
                                   plan->live_blocks, a->pinned_out_dev};
         rc = stats_pass(&packed, a->arena_bytes, kNone, a->ws_dev, a->ws_bytes, stream,

@@ -200,7 +200,7 @@ constexpr size_t kPerTileBytes =
 
 struct WsLayout {
     // fixed part (depends on n only)
-    size_t header, part, prefix, spart, tpart, twhole, tprefix, live_dst, live_src, live_size,
+    size_t header, post, part, prefix, spart, tpart, twhole, tprefix, live_dst, live_src, live_size,
         live_pin, tile_base, live_z, live_pc, selpart, live_rec, live_key, ridx, fixed;
     // tile part (depends on the tile capacity)
     size_t tile_start, tile_first, tiles, flags, total;
@@ -215,6 +215,7 @@ inline WsLayout ws_fixed(uint64_t n) {
     const uint64_t nb = L.n_scan_blocks ? L.n_scan_blocks : 1;
     size_t at = 0;
     L.header = at;    at += align256(sizeof(WsHeader));
+    L.post = at;      at += align256(sizeof(WsHeader));  // the one-call post-check's
     L.part = at;      at += align256(nb * sizeof(ScanPart));
     L.prefix = at;    at += align256(nb * sizeof(ScanPart));
     L.spart = at;     at += align256(nb * sizeof(StatPart));
