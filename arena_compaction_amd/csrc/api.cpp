@@ -377,6 +377,7 @@ int defrag_move(void *arena_dev, uint64_t arena_bytes, defrag_plan_t *plan, void
     a.spin_limit = 1ull << plan->tuning.spin_limit_log2;
     a.tile_bytes = plan->tuning.tile_bytes;
     a.max_blocks = (uint32_t)plan->max_blocks_per_tile;
+    a.small_blocks = move_small_blocks(plan->arena_bytes, plan->n) ? 1u : 0u;
     if (launch_move(a, plan->tuning.wg_per_cu, plan->tuning.nontemporal, cus, stream) !=
         hipSuccess)
         return DEFRAG_EHIP;
@@ -503,6 +504,7 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
         m.spin_limit = 1ull << c.tu.spin_limit_log2;
         m.tile_bytes = c.tu.tile_bytes;
         m.max_blocks = c.tu.tile_bytes / 32 + 2;  // the most blocks a tile can meet
+        m.small_blocks = move_small_blocks(a->arena_bytes, a->table->n) ? 1u : 0u;
         m.device_sized = 1;
         m.wg_per_cu = c.tuned ? c.tu.wg_per_cu : 0;
         m.num_cus = (uint32_t)cus;

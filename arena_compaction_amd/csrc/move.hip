@@ -81,8 +81,8 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-template <int VPT, int NT>
-__global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
+template <int THREADS, int VPT, int NT>
+__global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
     extern __shared__ uint64_t lds_dyn[];
     uint64_t *s_shift = lds_dyn;                                           // [max_blocks]
     uint32_t *s_rel = reinterpret_cast<uint32_t *>(lds_dyn + a.max_blocks);  // [max_blocks]
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
         bool ok = nblk <= a.max_blocks;
 
         if (nblk > 1u && ok) {
-            for (uint32_t k = tid; k < nblk; k += kMoveThreads) {
+            for (uint32_t k = tid; k < nblk; k += THREADS) {
                 const uint64_t d = a.live_dst[first + k];
                 s_shift[k] = a.live_src[first + k] - d;
                 s_rel[k] = d <= tb ? 0u : (uint32_t)(d - tb);
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
         const uint8_t *first_src = a.arena + tb + rel0 + shift0;
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            const uint32_t r = ((uint32_t)j * kMoveThreads + tid) * 16u;
+            const uint32_t r = ((uint32_t)j * THREADS + tid) * 16u;
             uint64_t sh = shift0;
             if (nblk > 1u && ok) {
                 uint32_t lo = 0, n = nblk;  // largest k with s_rel[k] <= r
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
                 a.arena + tb, 0, (int)a.tile_bytes, kBufferRsrcWord3);
 #pragma unroll
             for (int j = 0; j < VPT; ++j) {
-                const uint32_t r = ((uint32_t)j * kMoveThreads + tid) * 16u;
+                const uint32_t r = ((uint32_t)j * THREADS + tid) * 16u;
                 const uint32_t off = (r >= rel0 && r < rel1) ? r : kOutOfWindow;
                 __builtin_amdgcn_raw_buffer_store_b128(v[j], win, (int)off, 0,
                                                        (NT & 2) ? kBufferNt : 0);
@@ -223,14 +223,14 @@ __global__ __launch_bounds__(kMoveThreads) void k_move(MoveArgs a) {
     }
 }
 
-template <int VPT, int NT>
+template <int THREADS, int VPT, int NT>
 hipError_t launch_t(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
     const size_t lds = (size_t)a.max_blocks * 12u + 16u;
     uint64_t per_cu = wg_per_cu;
     if (per_cu == 0) {  // as many as the kernel's resources allow (the query costs a few us)
         int occ = 0;
         const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &occ, k_move<VPT, NT>, kMoveThreads, lds);
+            &occ, k_move<THREADS, VPT, NT>, THREADS, lds);
         if (e != hipSuccess) return e;
         per_cu = occ < 1 ? 1u : (uint32_t)occ;
     }
@@ -238,49 +238,54 @@ hipError_t launch_t(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStrea
     if (grid > a.n_tiles) grid = a.n_tiles;
     if (grid > kMaxMoveGrid) grid = kMaxMoveGrid;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((k_move<VPT, NT>), dim3((uint32_t)grid), dim3(kMoveThreads), lds, s, a);
+    hipLaunchKernelGGL((k_move<THREADS, VPT, NT>), dim3((uint32_t)grid), dim3(THREADS), lds, s, a);
     return hipGetLastError();
 }
 
 // The device-sized mover: the grid the plan's tuning asks for (the plan is
 // not read back first: the workgroups read its tile count from the device),
 // LDS for the most blocks a tile can meet.
-
-template <int VPT, int NT>
+template <int THREADS, int VPT, int NT>
 hipError_t launch_device_sized_t(const MoveArgs &a, hipStream_t s) {
     const size_t lds = (size_t)a.max_blocks * 12u + 16u;
     const uint64_t per_cu = a.wg_per_cu ? a.wg_per_cu : kDefaultWgPerCu;
     uint64_t grid = per_cu * (uint64_t)a.num_cus;
     if (grid > kMaxMoveGrid) grid = kMaxMoveGrid;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((k_move<VPT, NT>), dim3((uint32_t)grid), dim3(kMoveThreads), lds, s, a);
+    hipLaunchKernelGGL((k_move<THREADS, VPT, NT>), dim3((uint32_t)grid), dim3(THREADS), lds, s, a);
     return hipGetLastError();
 }
 
-template <int NT>
-hipError_t launch_nt(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
-    switch (a.tile_bytes <= kMoveRowBytes ? 1u : a.tile_bytes / kMoveRowBytes) {
-        case 1: return launch_t<1, NT>(a, wg_per_cu, num_cus, s);
-        case 2: return launch_t<2, NT>(a, wg_per_cu, num_cus, s);
-        case 4: return launch_t<4, NT>(a, wg_per_cu, num_cus, s);
-        case 8: return launch_t<8, NT>(a, wg_per_cu, num_cus, s);
-        case 16: return launch_t<16, NT>(a, wg_per_cu, num_cus, s);
-        case 32: return launch_t<32, NT>(a, wg_per_cu, num_cus, s);
+template <int THREADS, int VPT, int NT, bool DEVICE_SIZED>
+hipError_t launch_one(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
+    if constexpr (VPT * THREADS * 16 > kMaxTile) {
+        return hipErrorInvalidValue;  // larger than any tile
+    } else if constexpr (DEVICE_SIZED) {
+        return launch_device_sized_t<THREADS, VPT, NT>(a, s);
+    } else {
+        return launch_t<THREADS, VPT, NT>(a, wg_per_cu, num_cus, s);
+    }
+}
+
+// Vectors per lane: the tile over the workgroup's row of 16-byte vectors.
+template <int THREADS, int NT, bool DEVICE_SIZED>
+hipError_t launch_threads(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
+    constexpr uint32_t row = THREADS * 16;
+    switch (a.tile_bytes <= row ? 1u : a.tile_bytes / row) {
+        case 1: return launch_one<THREADS, 1, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
+        case 2: return launch_one<THREADS, 2, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
+        case 4: return launch_one<THREADS, 4, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
+        case 8: return launch_one<THREADS, 8, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
+        case 16: return launch_one<THREADS, 16, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int NT>
-hipError_t launch_device_sized_nt(const MoveArgs &a, hipStream_t s) {
-    switch (a.tile_bytes <= kMoveRowBytes ? 1u : a.tile_bytes / kMoveRowBytes) {
-        case 1: return launch_device_sized_t<1, NT>(a, s);
-        case 2: return launch_device_sized_t<2, NT>(a, s);
-        case 4: return launch_device_sized_t<4, NT>(a, s);
-        case 8: return launch_device_sized_t<8, NT>(a, s);
-        case 16: return launch_device_sized_t<16, NT>(a, s);
-        case 32: return launch_device_sized_t<32, NT>(a, s);
-        default: return hipErrorInvalidValue;
-    }
+template <int NT, bool DEVICE_SIZED>
+hipError_t launch_nt(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
+    return a.small_blocks
+               ? launch_threads<kMoveThreadsSmallBlocks, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s)
+               : launch_threads<kMoveThreads, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
 }
 
 }  // namespace
@@ -289,20 +294,20 @@ hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, uint32_t nontempor
                        hipStream_t s) {
     if (a.n_tiles == 0) return hipSuccess;
     switch (nontemporal) {
-        case 0: return launch_nt<0>(a, wg_per_cu, num_cus, s);
-        case 1: return launch_nt<3>(a, wg_per_cu, num_cus, s);
-        case 2: return launch_nt<1>(a, wg_per_cu, num_cus, s);
-        case 3: return launch_nt<2>(a, wg_per_cu, num_cus, s);
+        case 0: return launch_nt<0, false>(a, wg_per_cu, num_cus, s);
+        case 1: return launch_nt<3, false>(a, wg_per_cu, num_cus, s);
+        case 2: return launch_nt<1, false>(a, wg_per_cu, num_cus, s);
+        case 3: return launch_nt<2, false>(a, wg_per_cu, num_cus, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_move_device_sized(const MoveArgs &a, uint32_t nontemporal, hipStream_t s) {
     switch (nontemporal) {
-        case 0: return launch_device_sized_nt<0>(a, s);
-        case 1: return launch_device_sized_nt<3>(a, s);
-        case 2: return launch_device_sized_nt<1>(a, s);
-        case 3: return launch_device_sized_nt<2>(a, s);
+        case 0: return launch_nt<0, true>(a, 0, 0, s);
+        case 1: return launch_nt<3, true>(a, 0, 0, s);
+        case 2: return launch_nt<1, true>(a, 0, 0, s);
+        case 3: return launch_nt<2, true>(a, 0, 0, s);
         default: return hipErrorInvalidValue;
     }
 }
