@@ -219,3 +219,36 @@ def test_plan_stays_usable_after_compact(ac):
         st = ac.defrag_stats(off, size, live, heap.arena_bytes, ws, pinned=pin)
         check_stats(st, oracle.stats(heap.offset, heap.size, heap.live, heap.arena_bytes,
                                      pinned=heap.pinned), "statistics pass")
+
+
+@pytest.mark.parametrize("k", ["training-80g", "small-blocks-4g"])
+def test_compact_commit_without_post_check(ac, k):
+    """The packed table asked for without the post-check (and, separately,
+    only its flag columns): commit then runs beside the move on its own,
+    and the table it writes is the oracle's."""
+    heap = W.workload(k, small=True)
+    log(f"case compact commit only {heap.describe()}")
+    host = pristine_host(heap)
+    off, size, live = device_table(heap, "cuda")
+    li = np.flatnonzero(heap.live)
+    m = li.shape[0]
+    want_new = oracle.new_offsets(heap.offset, heap.size, heap.live, heap.pinned)
+    for only_flags in (False, True):
+        arena = host.cuda()
+        ws = ac.workspace(heap.n, heap.arena_bytes)
+        c_off = None if only_flags else torch.empty(m, dtype=torch.int64, device="cuda")
+        c_size = None if only_flags else torch.empty(m, dtype=torch.int64, device="cuda")
+        c_live = torch.full((m,), 7, dtype=torch.uint8, device="cuda")
+        c_pin = torch.full((m,), 9, dtype=torch.uint8, device="cuda")
+        plan, post = ac.defrag_compact(off, size, live, heap.arena_bytes, arena, ws,
+                                       offset_out=c_off, size_out=c_size, live_out=c_live,
+                                       pinned_out=c_pin, after=False)
+        torch.cuda.synchronize()
+        assert post is None and plan.live_blocks == m
+        assert bool((c_live == 1).all()) and bool((c_pin == 0).all())
+        if not only_flags:
+            assert np.array_equal(t_to_u64(c_off), want_new[li])
+            assert np.array_equal(t_to_u64(c_size), heap.size[li])
+        ref = host.numpy().copy()
+        oracle.compact(ref, heap.offset, heap.size, heap.live, heap.pinned)
+        assert np.array_equal(arena.cpu().numpy(), ref)
