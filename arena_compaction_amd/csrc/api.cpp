@@ -526,18 +526,24 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
         // so they run on the side stream while the move does, and the
         // stream waits for them at the end.  The remap goes there only when
         // the move is long beside it (its probes slow a short move more
-        // than they save); the post-check writes its own header.
+        // than they save); the post-check writes its own header.  A failure
+        // after some of them are queued waits for those first, so no kernel
+        // of this call still writes the caller's buffers once it returns.
+        const auto fail = [&](int code) {
+            if (remap_done || commit_done || post_done) (void)hipStreamSynchronize(side);
+            return code;
+        };
         if ((a->n_handles || a->n_invalid_dev) &&
             plan->stats.moved_bytes / kRemapOverlapBytesPerHandle > a->n_handles) {
             rc = defrag_remap(plan, a->ws_dev, a->ws_bytes, a->h_in_dev, a->h_out_dev,
                               a->n_handles, a->n_invalid_dev, side);
-            if (rc) return rc;
+            if (rc) return fail(rc);
             remap_done = true;
         }
         if (a->offset_out_dev || a->size_out_dev || a->live_out_dev || a->pinned_out_dev) {
             rc = defrag_commit(plan, a->ws_dev, a->ws_bytes, a->offset_out_dev,
                                a->size_out_dev, a->live_out_dev, a->pinned_out_dev, side);
-            if (rc) return rc;
+            if (rc) return fail(rc);
             commit_done = true;
         }
         if (after_host) {
@@ -546,17 +552,17 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
             rc = post_check_queue(&packed, a->arena_bytes, a->ws_dev, a->ws_bytes, side);
             if (rc) {
                 arg_error(after_host);
-                return rc;
+                return fail(rc);
             }
             post_done = true;
         }
         if (remap_done || commit_done || post_done) {
             hipEvent_t joined_ev = nullptr;
             if (hipEventCreateWithFlags(&joined_ev, hipEventDisableTiming) != hipSuccess)
-                return DEFRAG_EHIP;
+                return fail(DEFRAG_EHIP);
             const bool joined = hipEventRecord(joined_ev, side) == hipSuccess &&
                                 hipStreamWaitEvent(stream, joined_ev, 0) == hipSuccess;
-            if (hipEventDestroy(joined_ev) != hipSuccess || !joined) return DEFRAG_EHIP;
+            if (hipEventDestroy(joined_ev) != hipSuccess || !joined) return fail(DEFRAG_EHIP);
         }
     } else {
         rc = a->request_bytes
