@@ -16,10 +16,6 @@ namespace {
 
 constexpr uint64_t kPlanMagic = 0x4e414c5047415244ull;  // "DRAGPLAN"
 
-// defrag_compact runs the remap beside the move when the move has more than
-// this many moved bytes per handle (the remap's probes slow a short move by
-// more than they save).
-constexpr uint64_t kRemapOverlapBytesPerHandle = 1024;
 
 std::atomic<uint64_t> g_epoch{0x9E3779B97F4A7C15ull};
 
@@ -524,17 +520,15 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
         plan->state = 2;
         // Remap, commit and the post-check read the plan, never the arena,
         // so they run on the side stream while the move does, and the
-        // stream waits for them at the end.  The remap goes there only when
-        // the move is long beside it (its probes slow a short move more
-        // than they save); the post-check writes its own header.  A failure
-        // after some of them are queued waits for those first, so no kernel
-        // of this call still writes the caller's buffers once it returns.
+        // stream waits for them at the end; the post-check writes its own
+        // header.  A failure after some of them are queued waits for those
+        // first, so no kernel of this call still writes the caller's
+        // buffers once it returns.
         const auto fail = [&](int code) {
             if (remap_done || commit_done || post_done) (void)hipStreamSynchronize(side);
             return code;
         };
-        if ((a->n_handles || a->n_invalid_dev) &&
-            plan->stats.moved_bytes / kRemapOverlapBytesPerHandle > a->n_handles) {
+        if (a->n_handles || a->n_invalid_dev) {
             rc = defrag_remap(plan, a->ws_dev, a->ws_bytes, a->h_in_dev, a->h_out_dev,
                               a->n_handles, a->n_invalid_dev, side);
             if (rc) return fail(rc);

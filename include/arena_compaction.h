@@ -311,12 +311,10 @@ int defrag_commit(const defrag_plan_t *plan_host, const void *ws_dev,
  * takes its tile count and workgroup count from the plan in the workspace,
  * and moves nothing if the plan failed; the plan is read back on a second
  * stream (one per device, created on first use and kept) while the move
- * runs.  Commit and the post-check, which never read the arena, then run on
- * that stream beside the move (the post-check with a header of its own in
- * the workspace), and so does the remap when the move has more than 1024
- * moved bytes per handle (else it follows the move); the stream waits for
- * them, and one read at the end brings the post-check and the mover's
- * status.  With a NULL or misaligned arena, a tuning of wg_per_cu 0, or
+ * runs.  Remap, commit and the post-check, which never read the arena,
+ * then run on that stream beside the move (the post-check with a header of
+ * its own in the workspace); the stream waits for them, and one read at the
+ * end brings the post-check and the mover's status.  With a NULL or misaligned arena, a tuning of wg_per_cu 0, or
  * after_host without offset_out_dev and size_out_dev, the steps run in the
  * plain order instead (plan, read back, argument checks, move).  Returns
  * the first failing step's code (nothing moves if the plan fails;
