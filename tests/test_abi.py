@@ -168,3 +168,37 @@ def test_oracle_is_not_linked_into_the_product():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f"{f} mentions the oracle"
+
+
+def test_build_is_quiet_and_device_code_has_no_packed_fp32():
+    """Every source compiles under -Wall -Wextra with nothing printed (the
+    build drops only the host pass's note that it does not know the
+    device-only feature), and the gfx950 code of each kernel file holds no
+    packed-FP32 arithmetic."""
+    import subprocess
+    import sys
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_acb", os.path.join(ROOT, "arena_compaction_amd", "build.py"))
+    acb = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(acb)
+    import tempfile
+    csrc = os.path.join(ROOT, "arena_compaction_amd", "csrc")
+    with tempfile.TemporaryDirectory() as tmp:   # the library's own build line
+        p = subprocess.run([acb.hipcc()] + acb.HIPCC_FLAGS +
+                           [os.path.join(csrc, s) for s in acb.SOURCES] +
+                           ["-o", os.path.join(tmp, "lib.so")],
+                           stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    shown = [ln for ln in p.stdout.splitlines() if ln.strip() != acb.HOST_FEATURE_NOTE]
+    assert p.returncode == 0 and not shown, shown
+    flags = [f for f in acb.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    for src in [s for s in acb.SOURCES if s.endswith(".hip")]:
+        p = subprocess.run([acb.hipcc()] + flags + ["--cuda-device-only", "-S", "-o", "-",
+                                                    os.path.join(csrc, src)],
+                           stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+        assert p.returncode == 0, p.stderr[-2000:]
+        asm = p.stdout
+        assert "gfx950" in asm and ".amdhsa_kernel" in asm, src
+        for op in ("v_pk_fma_f32", "v_pk_mul_f32", "v_pk_add_f32"):
+            assert op not in asm, f"{src}: {op} in the device code"
+    sys.stdout.flush()
