@@ -31,6 +31,8 @@ DEFRAG_ENOPLAN = -3
 DEFRAG_EHIP = -4
 DEFRAG_ETIMEOUT = -5
 DEFRAG_ENOFIT = -6
+DEFRAG_ECAPACITY = -7
+DEFRAG_ECORRUPT = -8
 REASONS = {0: "none", 1: "zero_size", 2: "misaligned", 3: "live_flag",
            4: "out_of_arena", 5: "overlap", 6: "argument", 7: "pinned_flag"}
 U64_MAX = (1 << 64) - 1
@@ -57,7 +59,15 @@ class defrag_stats_t(ctypes.Structure):
 
 class defrag_tuning(ctypes.Structure):
     _fields_ = [("tile_bytes", ctypes.c_uint32), ("wg_per_cu", ctypes.c_uint32),
-                ("nontemporal", ctypes.c_uint32), ("spin_limit_log2", ctypes.c_uint32)]
+                ("nontemporal", ctypes.c_uint32), ("spin_limit_log2", ctypes.c_uint32),
+                ("stall_every", ctypes.c_uint32), ("stall_sleeps", ctypes.c_uint32),
+                ("stall_seed", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+class defrag_move_report_t(ctypes.Structure):
+    _fields_ = [("status", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("tiles", ctypes.c_uint64), ("late_tiles", ctypes.c_uint64),
+                ("waited_tiles", ctypes.c_uint64), ("polls", ctypes.c_uint64)]
 
 
 class defrag_plan_t(ctypes.Structure):
@@ -100,7 +110,8 @@ class defrag_compact_args(ctypes.Structure):
                 ("h_in_dev", ctypes.c_void_p), ("h_out_dev", ctypes.c_void_p),
                 ("n_handles", ctypes.c_uint64), ("n_invalid_dev", ctypes.c_void_p),
                 ("offset_out_dev", ctypes.c_void_p), ("size_out_dev", ctypes.c_void_p),
-                ("live_out_dev", ctypes.c_void_p), ("pinned_out_dev", ctypes.c_void_p)]
+                ("live_out_dev", ctypes.c_void_p), ("pinned_out_dev", ctypes.c_void_p),
+                ("side_stream", ctypes.c_void_p)]
 
 
 # defrag_tile_t: one mover tile of a plan (defrag_plan_tiles)
@@ -144,6 +155,8 @@ def _load() -> ctypes.CDLL:
                                    ctypes.POINTER(defrag_stats_t)]
     L.defrag_move.argtypes = [P, U, ctypes.POINTER(defrag_plan_t), P, S, P]
     L.defrag_move_status.argtypes = [ctypes.POINTER(defrag_plan_t), P, P]
+    L.defrag_move_report.argtypes = [ctypes.POINTER(defrag_plan_t), P, P,
+                                     ctypes.POINTER(defrag_move_report_t)]
     L.defrag_plan_tiles.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, U, P]
     L.defrag_remap.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, U, P, P]
     L.defrag_commit.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, P, P, P]
@@ -155,7 +168,7 @@ def _load() -> ctypes.CDLL:
     L.defrag_strerror.restype = ctypes.c_char_p
     for f in ("defrag_stats", "defrag_first_fit", "defrag_plan", "defrag_plan_targeted",
               "defrag_move", "defrag_monitor", "defrag_compact",
-              "defrag_move_status", "defrag_plan_tiles",
+              "defrag_move_status", "defrag_move_report", "defrag_plan_tiles",
               "defrag_remap", "defrag_commit"):
         getattr(L, f).restype = ctypes.c_int
     return L
@@ -166,7 +179,8 @@ lib = _load()
 EXPORTS = ("defrag_workspace_bytes", "defrag_stats", "defrag_first_fit", "defrag_plan",
            "defrag_plan_targeted",
            "defrag_move",
-           "defrag_move_status", "defrag_plan_tiles", "defrag_remap", "defrag_commit",
+           "defrag_move_status", "defrag_move_report", "defrag_plan_tiles", "defrag_remap",
+           "defrag_commit",
            "defrag_compact", "defrag_monitor",
            "defrag_strerror")
 
@@ -300,6 +314,15 @@ def defrag_move_status(plan: defrag_plan_t, ws: torch.Tensor, stream=None) -> in
     return int(lib.defrag_move_status(ctypes.byref(plan), _ptr(ws), _stream(stream)))
 
 
+def defrag_move_report(plan: defrag_plan_t, ws: torch.Tensor, stream=None) -> defrag_move_report_t:
+    """The move's outcome (status) and the mover's wait counters."""
+    out = defrag_move_report_t()
+    rc = lib.defrag_move_report(ctypes.byref(plan), _ptr(ws), _stream(stream), ctypes.byref(out))
+    if rc != DEFRAG_OK:
+        raise DefragError(rc, "defrag_move_report")
+    return out
+
+
 def defrag_plan_tiles(plan: defrag_plan_t, ws: torch.Tensor, stream=None) -> np.ndarray:
     """The plan's mover tiles as a structured array of TILE_DTYPE."""
     n = int(plan.n_tiles)
@@ -347,13 +370,15 @@ def defrag_compact(offset, size, live, arena_bytes: int, arena: torch.Tensor, ws
                    handles: Optional[torch.Tensor] = None, h_out: Optional[torch.Tensor] = None,
                    n_invalid: Optional[torch.Tensor] = None, offset_out=None, size_out=None,
                    live_out=None, pinned_out=None, tuning: Optional[defrag_tuning] = None,
-                   stream=None, pinned=None, after: Optional[bool] = None):
+                   stream=None, pinned=None, after: Optional[bool] = None, side_stream=None):
     """Plan, move, remap, commit and the post-check in one C-ABI call.
     after (default: whenever offset_out and size_out are given) asks for the
     post-move statistics.  Returns (plan, post-move stats or None).
     offset_out, size_out, live_out and pinned_out need one element per live
     block, which is known only once the plan has run: neither this function
-    nor the library can check their length."""
+    nor the library can check their length.  side_stream: a torch stream
+    of the caller's for the work that overlaps the move (default: the
+    library's own)."""
     _need(arena, torch.uint8, 0, "arena")
     if after is None:
         after = offset_out is not None and size_out is not None
@@ -377,7 +402,8 @@ def defrag_compact(offset, size, live, arena_bytes: int, arena: torch.Tensor, ws
         _ptr(offset_out) if offset_out is not None and offset_out.numel() else None,
         _ptr(size_out) if size_out is not None and size_out.numel() else None,
         _ptr(live_out) if live_out is not None and live_out.numel() else None,
-        _ptr(pinned_out) if pinned_out is not None and pinned_out.numel() else None)
+        _ptr(pinned_out) if pinned_out is not None and pinned_out.numel() else None,
+        ctypes.c_void_p(side_stream.cuda_stream) if side_stream is not None else None)
     plan = defrag_plan_t()
     post = defrag_stats_t() if after else None
     rc = lib.defrag_compact(ctypes.byref(a), _stream(stream), ctypes.byref(plan),

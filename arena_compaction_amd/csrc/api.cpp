@@ -104,6 +104,22 @@ int current_device() {
     return d;
 }
 
+// The mover's outcome from its status bits; 0 when it finished.
+int move_outcome(const WsHeader &h, uint64_t epoch) {
+    if (h.epoch != epoch) return DEFRAG_ENOPLAN;
+    if (h.status & kStatusCorrupt) return DEFRAG_ECORRUPT;
+    if (h.status & kStatusCapacity) return DEFRAG_ECAPACITY;
+    if (h.status & kStatusTimeout) return DEFRAG_ETIMEOUT;
+    return DEFRAG_OK;
+}
+
+int check_tuning(const defrag_tuning &tu) {
+    if (!tile_ok(tu.tile_bytes) || tu.spin_limit_log2 > 40 || tu.nontemporal > 3 ||
+        tu.stall_sleeps > kMaxStallSleeps)
+        return DEFRAG_EINVAL;
+    return DEFRAG_OK;
+}
+
 int check_plan(const defrag_plan_t *p, const void *ws, size_t ws_bytes) {
     if (!p || p->magic != kPlanMagic || p->state < 1) return DEFRAG_ENOPLAN;
     if (ws != p->workspace) return DEFRAG_ENOPLAN;
@@ -137,13 +153,16 @@ int stats_pass(const defrag_table *table, uint64_t arena_bytes, uint64_t fit_nee
         arg_error(out_host);
         return rc;
     }
-    const WsLayout L = ws_fixed(table->n);
+    WsLayout L = ws_fixed(table->n);
     rc = check_ws(ws_dev, ws_bytes, L.tpart);  // the partial-result region only
     if (rc) {
         arg_error(out_host);
         return rc;
     }
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
+    // the statistics header (the second 256 bytes): a plan the workspace
+    // holds keeps its own header
+    L.header = L.post;
     if (launch_scan(view_of(table), arena_bytes, ws, L, nullptr, 0, kDefaultTile, 0, fit_need,
                     stream) != hipSuccess)
         return DEFRAG_EHIP;
@@ -153,11 +172,10 @@ int stats_pass(const defrag_table *table, uint64_t arena_bytes, uint64_t fit_nee
     return h->bad_key == kNone ? DEFRAG_OK : DEFRAG_EINVAL;
 }
 
-// The one-call path's post-check, queued on the side stream while the move
-// may still run: the statistics pass of the packed table, with its own
+// The one-call path's post-check, queued (on the side stream, while the move
+// may still run): the statistics pass of the packed table, with its own
 // header (the move reads the plan's header as it starts) and otherwise only
-// the scratch region below the plan's data (the packed table has no more
-// entries than the planned one).
+// the fixed statistics region in front of the plan's data.
 int post_check_queue(const defrag_table *packed, uint64_t arena_bytes, void *ws_dev,
                      size_t ws_bytes, hipStream_t stream) {
     int rc = check_table(packed);
@@ -165,9 +183,10 @@ int post_check_queue(const defrag_table *packed, uint64_t arena_bytes, void *ws_
     WsLayout L = ws_fixed(packed->n);
     rc = check_ws(ws_dev, ws_bytes, L.tpart);
     if (rc) return rc;
+    uint8_t *ws = static_cast<uint8_t *>(ws_dev);
     L.header = L.post;
-    return launch_scan(view_of(packed), arena_bytes, static_cast<uint8_t *>(ws_dev), L, nullptr,
-                       0, kDefaultTile, 0, kNone, stream) == hipSuccess
+    return launch_scan(view_of(packed), arena_bytes, ws, L, nullptr, 0, kDefaultTile, 0, kNone,
+                       stream) == hipSuccess
                ? DEFRAG_OK
                : DEFRAG_EHIP;
 }
@@ -220,11 +239,13 @@ int plan_queue(const defrag_table *table, uint64_t arena_bytes, uint64_t request
                uint64_t *new_offset_dev, defrag_plan_t *plan, PlanCtx *c) {
     if (!plan) return DEFRAG_EINVAL;
     std::memset(plan, 0, sizeof(*plan));
-    defrag_tuning tu{0, kDefaultWgPerCu, kDefaultNontemporal, 0};
+    defrag_tuning tu{};
+    tu.wg_per_cu = kDefaultWgPerCu;
+    tu.nontemporal = kDefaultNontemporal;
     if (tuning) tu = *tuning;
     if (!tu.tile_bytes) tu.tile_bytes = kDefaultTile;
     if (!tu.spin_limit_log2) tu.spin_limit_log2 = kDefaultSpinLog2;
-    if (!tile_ok(tu.tile_bytes) || tu.spin_limit_log2 > 40 || tu.nontemporal > 3) {
+    if (check_tuning(tu)) {
         arg_error(&plan->stats);
         return DEFRAG_EINVAL;
     }
@@ -322,7 +343,71 @@ hipStream_t side_stream_of(int dev) {
     return streams[dev];
 }
 
+// The end of a compaction: one read of the plan's header (the mover's
+// status) and, after a post-check, of the statistics header beside it.
+int compact_finish(const defrag_compact_args *a, hipStream_t stream, defrag_plan_t *plan,
+                   defrag_stats_t *after_host, bool post_done) {
+    const WsLayout L = plan_layout(plan);
+    const uint8_t *ws = static_cast<const uint8_t *>(a->ws_dev);
+    static_assert(sizeof(WsHeader) == 256, "two adjacent headers");
+    WsHeader both[2];
+    if (L.post != L.header + sizeof(WsHeader) ||
+        hipMemcpyAsync(both, ws + L.header, (post_done ? 2 : 1) * sizeof(WsHeader),
+                       hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return DEFRAG_EHIP;
+    if (post_done) {
+        fill_stats(after_host, both[1], a->arena_bytes);
+        if (both[1].bad_key != kNone) return DEFRAG_EINVAL;
+    }
+    return plan->n_tiles ? move_outcome(both[0], plan->epoch) : DEFRAG_OK;
+}
+
 }  // namespace
+
+namespace ac {
+
+// The whole compaction in the plain order, every step on `stream` and
+// nothing else created: plan (read back), the argument checks that need the
+// plan, move, remap, commit, post-check, one read at the end.
+int compact_serial(const defrag_compact_args *a, hipStream_t stream, defrag_plan_t *plan,
+                   defrag_stats_t *after_host) {
+    int rc = a->request_bytes
+                 ? defrag_plan_targeted(a->table, a->arena_bytes, a->request_bytes, a->tuning,
+                                        a->ws_dev, a->ws_bytes, stream, a->new_offset_dev, plan)
+                 : defrag_plan(a->table, a->arena_bytes, a->tuning, a->ws_dev, a->ws_bytes,
+                               stream, a->new_offset_dev, plan);
+    if (rc) return rc;
+    // the post-check reads the packed table (empty if nothing is live)
+    if (after_host && plan->live_blocks && (!a->offset_out_dev || !a->size_out_dev)) {
+        arg_error(after_host);
+        return DEFRAG_EINVAL;  // checked before anything moves
+    }
+    rc = defrag_move(a->arena_dev, a->arena_bytes, plan, a->ws_dev, a->ws_bytes, stream);
+    if (rc) return rc;
+    if (a->n_handles || a->n_invalid_dev) {
+        rc = defrag_remap(plan, a->ws_dev, a->ws_bytes, a->h_in_dev, a->h_out_dev, a->n_handles,
+                          a->n_invalid_dev, stream);
+        if (rc) return rc;
+    }
+    if (a->offset_out_dev || a->size_out_dev || a->live_out_dev || a->pinned_out_dev) {
+        rc = defrag_commit(plan, a->ws_dev, a->ws_bytes, a->offset_out_dev, a->size_out_dev,
+                           a->live_out_dev, a->pinned_out_dev, stream);
+        if (rc) return rc;
+    }
+    if (after_host) {
+        const defrag_table packed{a->offset_out_dev, a->size_out_dev, a->live_out_dev,
+                                  plan->live_blocks, a->pinned_out_dev};
+        rc = post_check_queue(&packed, a->arena_bytes, a->ws_dev, a->ws_bytes, stream);
+        if (rc) {
+            arg_error(after_host);
+            return rc;
+        }
+    }
+    return compact_finish(a, stream, plan, after_host, after_host != nullptr);
+}
+
+}  // namespace ac
 
 extern "C" {
 
@@ -352,7 +437,7 @@ int defrag_move(void *arena_dev, uint64_t arena_bytes, defrag_plan_t *plan, void
     if (rc) return rc;
     if (plan->state != 1) return DEFRAG_ENOPLAN;
     if (arena_bytes != plan->arena_bytes) return DEFRAG_EINVAL;
-    if (plan->tuning.nontemporal > 3) return DEFRAG_EINVAL;
+    if (check_tuning(plan->tuning)) return DEFRAG_EINVAL;
     if (plan->n_tiles && (!arena_dev || (reinterpret_cast<uintptr_t>(arena_dev) & 15u)))
         return DEFRAG_EINVAL;
     plan->state = 2;
@@ -374,6 +459,11 @@ int defrag_move(void *arena_dev, uint64_t arena_bytes, defrag_plan_t *plan, void
     a.tile_bytes = plan->tuning.tile_bytes;
     a.max_blocks = (uint32_t)plan->max_blocks_per_tile;
     a.small_blocks = move_small_blocks(plan->arena_bytes, plan->n) ? 1u : 0u;
+    a.arena_bytes = arena_bytes;
+    a.live_blocks = plan->live_blocks;
+    a.stall_every = plan->tuning.stall_every;
+    a.stall_sleeps = plan->tuning.stall_sleeps;
+    a.stall_seed = plan->tuning.stall_seed;
     if (launch_move(a, plan->tuning.wg_per_cu, plan->tuning.nontemporal, cus, stream) !=
         hipSuccess)
         return DEFRAG_EHIP;
@@ -391,8 +481,28 @@ int defrag_move_status(const defrag_plan_t *plan, const void *ws_dev, hipStream_
     WsHeader h;
     rc = read_header(&h, static_cast<const uint8_t *>(ws_dev), L, stream);
     if (rc) return rc;
-    if (h.epoch != plan->epoch) return DEFRAG_ENOPLAN;
-    if (h.status & kStatusTimeout) return DEFRAG_ETIMEOUT;
+    return move_outcome(h, plan->epoch);
+}
+
+int defrag_move_report(const defrag_plan_t *plan, const void *ws_dev, hipStream_t stream,
+                       defrag_move_report_t *out_host) {
+    if (!out_host) return DEFRAG_EINVAL;
+    std::memset(out_host, 0, sizeof(*out_host));
+    int rc = check_plan(plan, ws_dev, plan ? plan->workspace_bytes : 0);
+    if (rc) return rc;
+    if (plan->state != 2) return DEFRAG_ENOPLAN;
+    out_host->tiles = plan->n_tiles;
+    if (plan->n_tiles == 0) {
+        return hipStreamSynchronize(stream) == hipSuccess ? DEFRAG_OK : DEFRAG_EHIP;
+    }
+    WsHeader h;
+    rc = read_header(&h, static_cast<const uint8_t *>(ws_dev), plan_layout(plan), stream);
+    if (rc) return rc;
+    out_host->status = move_outcome(h, plan->epoch);
+    if (out_host->status == DEFRAG_ENOPLAN) return DEFRAG_ENOPLAN;
+    out_host->late_tiles = h.late_tiles;
+    out_host->waited_tiles = h.waited_tiles;
+    out_host->polls = h.polls;
     return DEFRAG_OK;
 }
 
@@ -475,145 +585,95 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     const bool arena_ok = a->arena_dev && !(reinterpret_cast<uintptr_t>(a->arena_dev) & 15u);
     const bool post_ok = !after_host || (a->offset_out_dev && a->size_out_dev);
     const bool wg_ok = !a->tuning || a->tuning->wg_per_cu != 0;
+    if (!(arena_ok && post_ok && wg_ok)) return compact_serial(a, stream, plan, after_host);
     bool remap_done = false, commit_done = false, post_done = false;
     int rc;
-    if (arena_ok && post_ok && wg_ok) {
-        PlanCtx c;
-        rc = plan_queue(a->table, a->arena_bytes, a->request_bytes, a->tuning, a->ws_dev,
-                        a->ws_bytes, stream, a->new_offset_dev, plan, &c);
-        if (rc) return rc;
-        const int cus = num_cus_of(c.dev);
-        hipStream_t side = side_stream_of(c.dev);
-        if (cus <= 0 || !side) return DEFRAG_EHIP;
-        hipEvent_t planned = nullptr;
-        if (hipEventCreateWithFlags(&planned, hipEventDisableTiming) != hipSuccess)
-            return DEFRAG_EHIP;
-        uint8_t *ws = static_cast<uint8_t *>(a->ws_dev);
-        MoveArgs m{};
-        m.arena = static_cast<uint8_t *>(a->arena_dev);
-        m.live_dst = reinterpret_cast<const uint64_t *>(ws + c.L.live_dst);
-        m.live_src = reinterpret_cast<const uint64_t *>(ws + c.L.live_src);
-        m.tiles = reinterpret_cast<const TileRec *>(ws + c.L.tiles);
-        m.flags = reinterpret_cast<uint32_t *>(ws + c.L.flags);
-        m.hdr = reinterpret_cast<WsHeader *>(ws + c.L.header);
-        m.epoch = c.epoch;
-        m.spin_limit = 1ull << c.tu.spin_limit_log2;
-        m.tile_bytes = c.tu.tile_bytes;
-        m.max_blocks = c.tu.tile_bytes / 32 + 2;  // the most blocks a tile can meet
-        m.small_blocks = move_small_blocks(a->arena_bytes, a->table->n) ? 1u : 0u;
-        m.device_sized = 1;
-        m.wg_per_cu = c.tuned ? c.tu.wg_per_cu : 0;
-        m.num_cus = (uint32_t)cus;
-        m.max_tiles = c.L.max_tiles;
-        WsHeader hp;
-        const bool queued =
-            hipEventRecord(planned, stream) == hipSuccess &&
-            launch_move_device_sized(m, c.tu.nontemporal, stream) == hipSuccess &&
-            hipStreamWaitEvent(side, planned, 0) == hipSuccess;
-        rc = queued ? read_header(&hp, ws, c.L, side) : DEFRAG_EHIP;
-        const hipError_t destroyed = hipEventDestroy(planned);
-        if (rc) return rc;
-        if (destroyed != hipSuccess) return DEFRAG_EHIP;
-        // a failed plan: the queued move saw it in the header and moved nothing
-        rc = plan_fill(a->table, a->arena_bytes, a->request_bytes, a->ws_dev, c, hp, plan);
-        if (rc) return rc;
-        plan->state = 2;
-        // Remap, commit and the post-check read the plan, never the arena,
-        // so they run on the side stream while the move does, and the
-        // stream waits for them at the end; the post-check writes its own
-        // header.  A failure after some of them are queued waits for those
-        // first, so no kernel of this call still writes the caller's
-        // buffers once it returns.
-        const auto fail = [&](int code) {
-            if (remap_done || commit_done || post_done) (void)hipStreamSynchronize(side);
-            return code;
-        };
-        if (a->n_handles || a->n_invalid_dev) {
-            rc = defrag_remap(plan, a->ws_dev, a->ws_bytes, a->h_in_dev, a->h_out_dev,
-                              a->n_handles, a->n_invalid_dev, side);
-            if (rc) return fail(rc);
-            remap_done = true;
-        }
-        if (a->offset_out_dev || a->size_out_dev || a->live_out_dev || a->pinned_out_dev) {
-            rc = defrag_commit(plan, a->ws_dev, a->ws_bytes, a->offset_out_dev,
-                               a->size_out_dev, a->live_out_dev, a->pinned_out_dev, side);
-            if (rc) return fail(rc);
-            commit_done = true;
-        }
-        if (after_host) {
-            const defrag_table packed{a->offset_out_dev, a->size_out_dev, a->live_out_dev,
-                                      plan->live_blocks, a->pinned_out_dev};
-            rc = post_check_queue(&packed, a->arena_bytes, a->ws_dev, a->ws_bytes, side);
-            if (rc) {
-                arg_error(after_host);
-                return fail(rc);
-            }
-            post_done = true;
-        }
-        if (remap_done || commit_done || post_done) {
-            hipEvent_t joined_ev = nullptr;
-            if (hipEventCreateWithFlags(&joined_ev, hipEventDisableTiming) != hipSuccess)
-                return fail(DEFRAG_EHIP);
-            const bool joined = hipEventRecord(joined_ev, side) == hipSuccess &&
-                                hipStreamWaitEvent(stream, joined_ev, 0) == hipSuccess;
-            if (hipEventDestroy(joined_ev) != hipSuccess || !joined) return fail(DEFRAG_EHIP);
-        }
-    } else {
-        rc = a->request_bytes
-                 ? defrag_plan_targeted(a->table, a->arena_bytes, a->request_bytes, a->tuning,
-                                        a->ws_dev, a->ws_bytes, stream, a->new_offset_dev, plan)
-                 : defrag_plan(a->table, a->arena_bytes, a->tuning, a->ws_dev, a->ws_bytes,
-                               stream, a->new_offset_dev, plan);
-        if (rc) return rc;
-        // the post-check reads the packed table (empty if nothing is live)
-        if (after_host && plan->live_blocks && (!a->offset_out_dev || !a->size_out_dev)) {
-            arg_error(after_host);
-            return DEFRAG_EINVAL;  // checked before anything moves
-        }
-        rc = defrag_move(a->arena_dev, a->arena_bytes, plan, a->ws_dev, a->ws_bytes, stream);
-        if (rc) return rc;
+    PlanCtx c;
+    rc = plan_queue(a->table, a->arena_bytes, a->request_bytes, a->tuning, a->ws_dev,
+                    a->ws_bytes, stream, a->new_offset_dev, plan, &c);
+    if (rc) return rc;
+    const int cus = num_cus_of(c.dev);
+    hipStream_t side = a->side_stream ? a->side_stream : side_stream_of(c.dev);
+    if (cus <= 0 || !side) return DEFRAG_EHIP;
+    hipEvent_t planned = nullptr;
+    if (hipEventCreateWithFlags(&planned, hipEventDisableTiming) != hipSuccess)
+        return DEFRAG_EHIP;
+    uint8_t *ws = static_cast<uint8_t *>(a->ws_dev);
+    MoveArgs m{};
+    m.arena = static_cast<uint8_t *>(a->arena_dev);
+    m.live_dst = reinterpret_cast<const uint64_t *>(ws + c.L.live_dst);
+    m.live_src = reinterpret_cast<const uint64_t *>(ws + c.L.live_src);
+    m.tiles = reinterpret_cast<const TileRec *>(ws + c.L.tiles);
+    m.flags = reinterpret_cast<uint32_t *>(ws + c.L.flags);
+    m.hdr = reinterpret_cast<WsHeader *>(ws + c.L.header);
+    m.epoch = c.epoch;
+    m.spin_limit = 1ull << c.tu.spin_limit_log2;
+    m.tile_bytes = c.tu.tile_bytes;
+    m.max_blocks = c.tu.tile_bytes / 32 + 2;  // the most blocks a tile can meet
+    m.small_blocks = move_small_blocks(a->arena_bytes, a->table->n) ? 1u : 0u;
+    m.device_sized = 1;
+    m.wg_per_cu = c.tuned ? c.tu.wg_per_cu : 0;
+    m.num_cus = (uint32_t)cus;
+    m.max_tiles = c.L.max_tiles;
+    m.arena_bytes = a->arena_bytes;
+    m.live_blocks = a->table->n;  // room of the packed arrays; the count comes from the header
+    m.stall_every = c.tu.stall_every;
+    m.stall_sleeps = c.tu.stall_sleeps;
+    m.stall_seed = c.tu.stall_seed;
+    WsHeader hp;
+    const bool queued =
+        hipEventRecord(planned, stream) == hipSuccess &&
+        launch_move_device_sized(m, c.tu.nontemporal, stream) == hipSuccess &&
+        hipStreamWaitEvent(side, planned, 0) == hipSuccess;
+    rc = queued ? read_header(&hp, ws, c.L, side) : DEFRAG_EHIP;
+    const hipError_t destroyed = hipEventDestroy(planned);
+    if (rc) return rc;
+    if (destroyed != hipSuccess) return DEFRAG_EHIP;
+    // a failed plan: the queued move saw it in the header and moved nothing
+    rc = plan_fill(a->table, a->arena_bytes, a->request_bytes, a->ws_dev, c, hp, plan);
+    if (rc) return rc;
+    plan->state = 2;
+    // Remap, commit and the post-check read the plan, never the arena,
+    // so they run on the side stream while the move does, and the
+    // stream waits for them at the end; the post-check writes its own
+    // header.  A failure after some of them are queued waits for those
+    // first, so no kernel of this call still writes the caller's
+    // buffers once it returns.
+    const auto fail = [&](int code) {
+        if (remap_done || commit_done || post_done) (void)hipStreamSynchronize(side);
+        return code;
+    };
+    if (a->n_handles || a->n_invalid_dev) {
+        rc = defrag_remap(plan, a->ws_dev, a->ws_bytes, a->h_in_dev, a->h_out_dev,
+                          a->n_handles, a->n_invalid_dev, side);
+        if (rc) return fail(rc);
+        remap_done = true;
     }
-    if (!remap_done && (a->n_handles || a->n_invalid_dev)) {
-        rc = defrag_remap(plan, a->ws_dev, a->ws_bytes, a->h_in_dev, a->h_out_dev, a->n_handles,
-                          a->n_invalid_dev, stream);
-        if (rc) return rc;
+    if (a->offset_out_dev || a->size_out_dev || a->live_out_dev || a->pinned_out_dev) {
+        rc = defrag_commit(plan, a->ws_dev, a->ws_bytes, a->offset_out_dev,
+                           a->size_out_dev, a->live_out_dev, a->pinned_out_dev, side);
+        if (rc) return fail(rc);
+        commit_done = true;
     }
-    if (!commit_done &&
-        (a->offset_out_dev || a->size_out_dev || a->live_out_dev || a->pinned_out_dev)) {
-        rc = defrag_commit(plan, a->ws_dev, a->ws_bytes, a->offset_out_dev, a->size_out_dev,
-                           a->live_out_dev, a->pinned_out_dev, stream);
-        if (rc) return rc;
-    }
-    // one synchronisation: the post-move statistics (if asked for) and the
-    // mover's status come back in the same read
-    WsHeader h;
-    if (post_done) {
-        // the plan's header and the post-check's, adjacent in the workspace
-        const WsLayout L = plan_layout(plan);
-        static_assert(sizeof(WsHeader) == 256, "two adjacent headers");
-        WsHeader both[2];
-        const uint8_t *ws = static_cast<const uint8_t *>(a->ws_dev);
-        if (L.post != L.header + sizeof(WsHeader) ||
-            hipMemcpyAsync(both, ws + L.header, sizeof(both), hipMemcpyDeviceToHost, stream) !=
-                hipSuccess ||
-            hipStreamSynchronize(stream) != hipSuccess)
-            return DEFRAG_EHIP;
-        h = both[0];
-        fill_stats(after_host, both[1], a->arena_bytes);
-        if (both[1].bad_key != kNone) return DEFRAG_EINVAL;
-    } else if (after_host) {
+    if (after_host) {
         const defrag_table packed{a->offset_out_dev, a->size_out_dev, a->live_out_dev,
                                   plan->live_blocks, a->pinned_out_dev};
-        rc = stats_pass(&packed, a->arena_bytes, kNone, a->ws_dev, a->ws_bytes, stream,
-                        after_host, &h);
-        if (rc) return rc;
-    } else {
-        rc = read_header(&h, static_cast<const uint8_t *>(a->ws_dev), plan_layout(plan), stream);
-        if (rc) return rc;
+        rc = post_check_queue(&packed, a->arena_bytes, a->ws_dev, a->ws_bytes, side);
+        if (rc) {
+            arg_error(after_host);
+            return fail(rc);
+        }
+        post_done = true;
     }
-    if (plan->n_tiles && h.epoch != plan->epoch) return DEFRAG_ENOPLAN;
-    if (plan->n_tiles && (h.status & kStatusTimeout)) return DEFRAG_ETIMEOUT;
-    return DEFRAG_OK;
+    if (remap_done || commit_done || post_done) {
+        hipEvent_t joined_ev = nullptr;
+        if (hipEventCreateWithFlags(&joined_ev, hipEventDisableTiming) != hipSuccess)
+            return fail(DEFRAG_EHIP);
+        const bool joined = hipEventRecord(joined_ev, side) == hipSuccess &&
+                            hipStreamWaitEvent(stream, joined_ev, 0) == hipSuccess;
+        if (hipEventDestroy(joined_ev) != hipSuccess || !joined) return fail(DEFRAG_EHIP);
+    }
+    return compact_finish(a, stream, plan, after_host, post_done);
 }
 
 const char *defrag_strerror(int code) {
@@ -625,6 +685,8 @@ const char *defrag_strerror(int code) {
         case DEFRAG_EHIP: return "HIP runtime error";
         case DEFRAG_ETIMEOUT: return "mover wait timed out";
         case DEFRAG_ENOFIT: return "no hole holds the request (and, for a targeted plan, no window can free it)";
+        case DEFRAG_ECAPACITY: return "a mover tile met more blocks than its launch holds";
+        case DEFRAG_ECORRUPT: return "the workspace no longer holds a consistent plan (tiles outside it were not moved)";
         default: return "unknown error";
     }
 }

@@ -11,7 +11,13 @@ namespace ac {
 
 constexpr uint32_t kScanThreads = 256;          // threads per scan workgroup
 constexpr uint32_t kScanItems = 4;              // table entries per thread (measured: 4 beats 2 and 8)
-constexpr uint32_t kScanTile = kScanThreads * kScanItems;  // entries per workgroup
+constexpr uint32_t kScanTile = kScanThreads * kScanItems;  // entries per workgroup step
+// The scans run on a fixed grid: at most this many workgroups, each taking a
+// contiguous chunk of whole steps.  Their per-workgroup results then fit in
+// regions of fixed size at the front of the workspace, which is all a
+// statistics pass writes besides its header: it can measure a table of any
+// size while the workspace holds a plan, whose arrays all lie behind them.
+constexpr uint32_t kMaxScanParts = 1024;
 constexpr uint32_t kSpineThreads = 256;         // single-workgroup passes (no spills)
 // Mover workgroup: 512 lanes, a 64 KiB tile being 8 vectors of 16 B per
 // lane (measured on the 80 GiB workload, one workgroup per CU: 512 lanes
@@ -67,11 +73,22 @@ struct alignas(256) WsHeader {
     uint64_t win_moved;      // live bytes inside it (the bytes that move)
     uint64_t fit_offset;     // first fit: lowest hole start holding the request
     uint64_t whole_tiles;    // tiles that are one whole window of one block
-    uint64_t pad[11];
+    // The mover's wait counters (zeroed by the plan): tiles whose dependency
+    // flags were not all seen set behind their loads, tiles that then read
+    // a flag unset at least once, and all such unset reads.
+    uint64_t late_tiles;
+    uint64_t waited_tiles;
+    uint64_t polls;
+    uint64_t pad[8];
 };
 static_assert(sizeof(WsHeader) == 256, "header size");
 
-constexpr uint32_t kStatusTimeout = 1u;  // a wait gave up, or a tile overflowed LDS
+constexpr uint32_t kStatusTimeout = 1u;   // a wait gave up (the watchdog)
+constexpr uint32_t kStatusCapacity = 2u;  // a tile met more blocks than its LDS holds
+constexpr uint32_t kStatusCorrupt = 4u;   // a tile's record or blocks lie outside the
+                                          // arena or the plan's arrays: not moved
+// Wait-path testing knob: at most this many sleeps per stalled tile.
+constexpr uint32_t kMaxStallSleeps = 4096;
 
 constexpr uint64_t kWinNone = 0;   // not a targeted plan
 constexpr uint64_t kWinFound = 1;
@@ -212,21 +229,31 @@ struct WsLayout {
         live_pin, tile_base, live_z, live_pc, selpart, live_rec, live_key, ridx, fixed;
     // tile part (depends on the tile capacity)
     size_t tile_start, tile_first, tiles, flags, total;
-    uint64_t n_scan_blocks, n_sel_blocks, max_tiles;
+    uint64_t n_scan_blocks, scan_chunk, n_sel_blocks, max_tiles;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Scan grid for n entries: nb workgroups of `chunk` entries each (a multiple
+// of kScanTile; the last one may be short), nb <= kMaxScanParts, none empty.
+inline void scan_geom(uint64_t n, uint64_t *nb, uint64_t *chunk) {
+    const uint64_t steps = (n + kScanTile - 1) / kScanTile;
+    const uint64_t per = (steps + kMaxScanParts - 1) / kMaxScanParts;  // steps per workgroup
+    *nb = per ? (steps + per - 1) / per : 0;
+    *chunk = (per ? per : 1) * kScanTile;
+}
+
 inline WsLayout ws_fixed(uint64_t n) {
     WsLayout L{};
-    L.n_scan_blocks = (n + kScanTile - 1) / kScanTile;
-    const uint64_t nb = L.n_scan_blocks ? L.n_scan_blocks : 1;
+    scan_geom(n, &L.n_scan_blocks, &L.scan_chunk);
+    constexpr uint64_t nb = kMaxScanParts;  // fixed: see kMaxScanParts
     size_t at = 0;
     L.header = at;    at += align256(sizeof(WsHeader));
-    L.post = at;      at += align256(sizeof(WsHeader));  // the one-call post-check's
+    L.post = at;      at += align256(sizeof(WsHeader));  // statistics passes' own header
     L.part = at;      at += align256(nb * sizeof(ScanPart));
     L.prefix = at;    at += align256(nb * sizeof(ScanPart));
     L.spart = at;     at += align256(nb * sizeof(StatPart));
+    // -- everything below here is a plan's: statistics passes stop above --
     L.tpart = at;     at += align256(nb * sizeof(uint64_t));
     L.twhole = at;    at += align256(nb * sizeof(uint64_t));
     L.tprefix = at;   at += align256(nb * sizeof(uint64_t));
@@ -348,12 +375,29 @@ struct MoveArgs {
     uint32_t wg_per_cu;   // device-sized: 0 = the default (kDefaultWgPerCu)
     uint32_t num_cus;
     uint64_t max_tiles;   // device-sized: the workspace's tile capacity
+    // Bounds every tile is checked against before it touches the arena: a
+    // record or block outside them (a workspace overwritten since its plan)
+    // moves nothing and reports kStatusCorrupt.
+    uint64_t arena_bytes;
+    uint64_t live_blocks; // entries of the packed live arrays (device-sized: from the header)
+    // Wait-path testing knob (0 = off): tile t holds its "sources read" flag
+    // back for stall_sleeps sleeps when mix(t, stall_seed) % stall_every == 0.
+    uint32_t stall_every;
+    uint32_t stall_sleeps;
+    uint32_t stall_seed;
+    uint32_t pad;
 };
 hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, uint32_t nontemporal,
                        int num_cus, hipStream_t s);
 // The device-sized mover: a grid for the largest workgroup count the rule
 // can pick, and LDS for the most blocks a tile can meet.
 hipError_t launch_move_device_sized(const MoveArgs &a, uint32_t nontemporal, hipStream_t s);
+
+// ---- api.cpp ----
+// The whole compaction in the plain order on one stream, creating nothing:
+// defrag_compact's fallback, and the static-scratch entry point's body.
+int compact_serial(const struct defrag_compact_args *a, hipStream_t stream,
+                   struct defrag_plan_t *plan, struct defrag_stats_t *after_host);
 
 // ---- remap.hip ----
 hipError_t launch_remap(const void *rec, const uint64_t *live_src, const uint32_t *key,

@@ -51,6 +51,20 @@
 // never straddles two blocks and both of its addresses are 16-byte aligned.
 // Per tile the kernel reads 16 B per live-block descriptor it needs (in LDS
 // only for tiles holding more than one block).
+//
+// The plan lives in caller memory, so before a tile touches the arena the
+// kernel checks what a plan guarantees: the tile's bytes lie in one window
+// inside the arena, its blocks inside the packed arrays, its dependencies
+// below it, and every source vector inside the arena.  A tile that fails
+// moves nothing and reports it (kStatusCorrupt); a tile meeting more blocks
+// than the launch gave it LDS for reports kStatusCapacity.  Neither happens
+// with a workspace left as its plan wrote it.
+//
+// Counters: a tile whose dependency flags were not all seen set behind its
+// loads counts as late, and as waited if it then read a flag unset (with
+// the number of such reads); all of it on the rare path.  A testing knob
+// holds chosen tiles' flags back for a bounded time, so that later tiles do
+// find them unset and the waits run at full size.
 #include "internal.h"
 
 namespace ac {
@@ -81,6 +95,14 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Wait-path testing knob: whether tile t holds its flag back (a 32-bit
+// multiplicative mix of the tile index and a seed; 0 = off).
+__device__ __forceinline__ bool stalls(uint32_t t, uint32_t every, uint32_t seed) {
+    uint32_t h = (t ^ seed) * 0x9E3779B1u;
+    h ^= h >> 15;
+    return every != 0u && h % every == 0u;
+}
+
 template <int THREADS, int VPT, int NT>
 __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
     extern __shared__ uint64_t lds_dyn[];
@@ -88,14 +110,16 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
     uint32_t *s_rel = reinterpret_cast<uint32_t *>(lds_dyn + a.max_blocks);  // [max_blocks]
     __shared__ uint32_t s_ticket;
     __shared__ uint32_t s_skip;
+    __shared__ uint32_t s_bad;     // a lane found a source outside the arena
     __shared__ uint64_t s_ntiles;
+    __shared__ uint64_t s_live;
     const uint32_t tid = threadIdx.x;
 
     if (tid == 0) {
         // a workspace re-planned since this plan: move nothing, write nothing
         // (the status query sees the epoch mismatch)
         uint32_t tk = 0xFFFFFFFFu;
-        uint64_t nt = a.n_tiles;
+        uint64_t nt = a.n_tiles, m = a.live_blocks;
         if (__hip_atomic_load(&a.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch) {
             bool go = true;
             if (a.device_sized) {
@@ -104,17 +128,23 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
                 // moves nothing; workgroups past the chosen count leave
                 const WsHeader *h = a.hdr;
                 nt = h->n_tiles;
+                m = h->live_blocks < m ? h->live_blocks : m;  // a.live_blocks: the arrays' room
                 const uint32_t per_cu = a.wg_per_cu ? a.wg_per_cu : kDefaultWgPerCu;
                 go = h->bad_key == kNone && h->win_state != kWinNoFit && nt <= a.max_tiles &&
                      blockIdx.x < (uint64_t)per_cu * a.num_cus;
             }
-            if (go) tk = atomicAdd(&a.hdr->ticket, 1u);
+            if (go && a.arena_bytes >= 32u) tk = atomicAdd(&a.hdr->ticket, 1u);
         }
         s_ticket = tk;
         s_ntiles = nt;
+        s_live = m;
+        s_bad = 0u;
     }
     __syncthreads();
     const uint64_t n_tiles = s_ntiles;
+    const uint64_t m_live = s_live;
+    const uint64_t S = a.arena_bytes;
+    const uint64_t T = a.tile_bytes;
     uint32_t t = s_ticket;
 
     while (t < n_tiles) {
@@ -130,11 +160,19 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
         const uint32_t last = __builtin_amdgcn_readfirstlane(rp.last_block);
         const uint32_t dep_lo = __builtin_amdgcn_readfirstlane(rp.dep_lo);
         const uint32_t dep_hi = __builtin_amdgcn_readfirstlane(rp.dep_hi);
-        const uint64_t tb = t0 & ~((uint64_t)a.tile_bytes - 1);  // the tile's window
-        const uint32_t rel0 = (uint32_t)(t0 - tb);
-        const uint32_t rel1 = (uint32_t)(t1 - tb);
+        const uint64_t tb = t0 & ~(T - 1);  // the tile's window
+        // What a plan guarantees, checked before the tile touches memory: its
+        // bytes lie in one window inside the arena, its first source too, its
+        // blocks in the live arrays, its dependencies below it.
+        const bool sane = t0 < t1 && t1 <= S && t1 - tb <= T && S - t0 >= 16u && first <= last &&
+                          last < m_live && shift0 <= S - 16u - t0 &&
+                          (dep_lo > dep_hi || dep_hi < t);
+        const uint32_t rel0 = sane ? (uint32_t)(t0 - tb) : 0u;
+        const uint32_t rel1 = sane ? (uint32_t)(t1 - tb) : 0u;
         const uint32_t nblk = last - first + 1u;
-        bool ok = nblk <= a.max_blocks;
+        const bool fits = nblk <= a.max_blocks;
+        const bool ok = sane && fits;
+        const uint64_t lim = sane ? S - 16u - tb : 0u;  // largest source offset from tb
 
         if (nblk > 1u && ok) {
             for (uint32_t k = tid; k < nblk; k += THREADS) {
@@ -145,10 +183,12 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
             __syncthreads();
         }
 
-        // no branch around a memory access: a lane outside [rel0, rel1)
-        // reloads the tile's first source vector and discards it
+        // no branch around a memory access: a lane outside [rel0, rel1), or
+        // whose source would leave the arena, reloads the tile's first
+        // source vector and discards it
         v4u v[VPT];
-        const uint8_t *first_src = a.arena + tb + rel0 + shift0;
+        const uint8_t *first_src = a.arena + (sane ? t0 + shift0 : 0u);
+        bool lane_bad = false;
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
             const uint32_t r = ((uint32_t)j * THREADS + tid) * 16u;
@@ -163,11 +203,14 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
                 sh = s_shift[lo];
             }
             const bool in = ok && r >= rel0 && r < rel1;
-            v[j] = load16<NT>(in ? a.arena + tb + r + sh : first_src);
+            const bool inside = sh <= lim && (uint64_t)r <= lim - sh;
+            lane_bad |= in && !inside;
+            v[j] = load16<NT>(in && inside ? a.arena + tb + r + sh : first_src);
         }
+        if (lane_bad) s_bad = 1u;
         // first look at the dependency flags, returned with the data loads
         uint32_t f_lo = 0u, f_hi = 0u;
-        if (tid == 0 && dep_lo <= dep_hi) {
+        if (tid == 0 && ok && dep_lo <= dep_hi) {
             f_lo = __hip_atomic_load(&a.flags[dep_lo], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             f_hi = __hip_atomic_load(&a.flags[dep_hi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -175,8 +218,18 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tid == 0) {
-            uint32_t skip = ok ? 0u : 1u;
-            if (!ok) atomicOr(&a.hdr->status, kStatusTimeout);
+            uint32_t skip = 0u;
+            if (!sane || s_bad) {
+                skip = 1u;
+                atomicOr(&a.hdr->status, kStatusCorrupt);
+            } else if (!fits) {
+                skip = 1u;
+                atomicOr(&a.hdr->status, kStatusCapacity);
+            }
+            s_bad = 0u;
+            if (__builtin_expect(stalls(t, a.stall_every, a.stall_seed), 0)) {
+                for (uint32_t k = 0; k < a.stall_sleeps; ++k) __builtin_amdgcn_s_sleep(127);
+            }
             __hip_atomic_store(&a.flags[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // the common case -- no dependency, or the one or two seen done
             // behind the data loads -- skips the polling loop, marked
@@ -184,17 +237,26 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
             // (measured: +0.6 points on the 80 GiB workload, +1.0 on the
             // self-overlapping one)
             const bool seen = dep_lo > dep_hi || (dep_hi - dep_lo <= 1u && f_lo && f_hi);
-            if (__builtin_expect(!seen, 0))
-            for (uint32_t u = dep_lo; u <= dep_hi && !skip; ++u) {
-                if ((u == dep_lo && f_lo) || (u == dep_hi && f_hi)) continue;  // seen done
+            if (__builtin_expect(!seen && !skip, 0)) {
                 uint64_t polls = 0;
-                while (__hip_atomic_load(&a.flags[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-                    if (++polls > a.spin_limit) {
-                        skip = 1u;
-                        atomicOr(&a.hdr->status, kStatusTimeout);
-                        break;
+                for (uint32_t u = dep_lo; u <= dep_hi && !skip; ++u) {
+                    if ((u == dep_lo && f_lo) || (u == dep_hi && f_hi)) continue;  // seen done
+                    uint64_t p = 0;
+                    while (__hip_atomic_load(&a.flags[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                        if (++p > a.spin_limit) {
+                            skip = 1u;
+                            atomicOr(&a.hdr->status, kStatusTimeout);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
                     }
-                    __builtin_amdgcn_s_sleep(1);
+                    polls += p;
+                }
+                atomicAdd(reinterpret_cast<unsigned long long *>(&a.hdr->late_tiles), 1ull);
+                if (polls) {
+                    atomicAdd(reinterpret_cast<unsigned long long *>(&a.hdr->waited_tiles), 1ull);
+                    atomicAdd(reinterpret_cast<unsigned long long *>(&a.hdr->polls),
+                              (unsigned long long)polls);
                 }
             }
             s_skip = skip;

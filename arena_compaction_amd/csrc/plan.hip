@@ -195,35 +195,42 @@ __device__ inline bool plan_dead(const WsHeader *hdr) {
     return hdr->bad_key != kNone || hdr->win_state == kWinNoFit;
 }
 
-// Pass 1: per-workgroup aggregate and first bad key.
+// Pass 1: per-workgroup aggregate and first bad key.  Workgroup g takes the
+// entries [g * chunk, (g + 1) * chunk), kScanTile at a time.
 __global__ __launch_bounds__(kScanThreads) void k_scan_partials(TableView t, uint64_t arena_bytes,
                                                                 const uint64_t *win,
-                                                                ScanPart *part) {
+                                                                uint64_t chunk, ScanPart *part) {
     __shared__ Agg sh[kScanThreads / 64];
     __shared__ uint64_t shr[kScanThreads / 64];
     const Window w = window_of(win);
-    const uint64_t i0 = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanItems;
-    Agg a = agg_zero();
+    const uint64_t base = (uint64_t)blockIdx.x * chunk;
+    const uint64_t end = umin64(base + chunk, t.n);
+    Agg acc = agg_zero();
     uint64_t bad = kNone;
-    uint64_t prev_end = 0;
-    if (i0 > 0 && i0 < t.n) prev_end = t.off[i0 - 1] + t.size[i0 - 1];
+    for (uint64_t s0 = base; s0 < end; s0 += kScanTile) {
+        const uint64_t i0 = s0 + (uint64_t)threadIdx.x * kScanItems;
+        Agg a = agg_zero();
+        uint64_t prev_end = 0;
+        if (i0 > 0 && i0 < t.n) prev_end = t.off[i0 - 1] + t.size[i0 - 1];
 #pragma unroll
-    for (uint32_t k = 0; k < kScanItems; ++k) {
-        const uint64_t i = i0 + k;
-        if (i < t.n) {
-            const uint64_t o = t.off[i], s = t.size[i];
-            const uint32_t l = live_of(t, i), p = pin_of(t, i);
-            const uint32_t r = entry_reason(i, o, s, l, p, arena_bytes, prev_end);
-            if (r) bad = umin64(bad, (i << 3) | r);
-            const uint32_t lb = l ? 1u : 0u, pb = p ? 1u : 0u;
-            a = combine(a, element(o, s, lb, pb, stays(o, lb, pb, w)));
-            prev_end = o + s;
+        for (uint32_t k = 0; k < kScanItems; ++k) {
+            const uint64_t i = i0 + k;
+            if (i < t.n) {
+                const uint64_t o = t.off[i], s = t.size[i];
+                const uint32_t l = live_of(t, i), p = pin_of(t, i);
+                const uint32_t r = entry_reason(i, o, s, l, p, arena_bytes, prev_end);
+                if (r) bad = umin64(bad, (i << 3) | r);
+                const uint32_t lb = l ? 1u : 0u, pb = p ? 1u : 0u;
+                a = combine(a, element(o, s, lb, pb, stays(o, lb, pb, w)));
+                prev_end = o + s;
+            }
         }
+        Agg total;
+        block_excl<kScanThreads>(a, total, sh);
+        acc = combine(acc, total);
     }
-    Agg total;
-    block_excl<kScanThreads>(a, total, sh);
     bad = block_reduce<kScanThreads>(bad, shr, OpMin());
-    if (threadIdx.x == 0) part[blockIdx.x] = ScanPart{total, bad};
+    if (threadIdx.x == 0) part[blockIdx.x] = ScanPart{acc, bad};
 }
 
 // Pass 2 (one workgroup): exclusive scan of the aggregates; table totals.
@@ -274,82 +281,89 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
                                                             const ScanPart *prefix,
                                                             const WsHeader *hdr, uint64_t *new_offset,
                                                             LiveOut lo, StatPart *spart,
-                                                            int outputs, uint64_t fit_need) {
+                                                            int outputs, uint64_t fit_need,
+                                                            uint64_t chunk) {
     __shared__ Agg sh[kScanThreads / 64];
     __shared__ uint64_t shr[kScanThreads / 64];
     if (plan_dead(hdr)) return;  // invalid table or nothing to plan: write nothing
     const Window w = window_of(win);
-    const uint64_t i0 = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanItems;
-    uint64_t o[kScanItems], s[kScanItems];
-    uint32_t l[kScanItems], p[kScanItems], f[kScanItems];
-    Agg a = agg_zero();
-#pragma unroll
-    for (uint32_t k = 0; k < kScanItems; ++k) {
-        const uint64_t i = i0 + k;
-        o[k] = 0;
-        s[k] = 0;
-        l[k] = 0;
-        p[k] = 0;
-        f[k] = 0;
-        if (i < t.n) {
-            o[k] = t.off[i];
-            s[k] = t.size[i];
-            l[k] = live_of(t, i) ? 1u : 0u;
-            p[k] = pin_of(t, i) ? 1u : 0u;
-            f[k] = stays(o[k], l[k], p[k], w);
-            a = combine(a, element(o[k], s[k], l[k], p[k], f[k]));
-        }
-    }
-    Agg total;
-    const Agg ex = block_excl<kScanThreads>(a, total, sh);
-    Agg run = combine(prefix[blockIdx.x].a, ex);
+    const uint64_t base = (uint64_t)blockIdx.x * chunk;
+    const uint64_t end = umin64(base + chunk, t.n);
+    Agg carry = prefix[blockIdx.x].a;  // everything before this workgroup's chunk
     uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, min_dst = kNone, min_size = kNone;
     uint64_t min_fit = kNone;
+    for (uint64_t s0 = base; s0 < end; s0 += kScanTile) {
+        const uint64_t i0 = s0 + (uint64_t)threadIdx.x * kScanItems;
+        uint64_t o[kScanItems], s[kScanItems];
+        uint32_t l[kScanItems], p[kScanItems], f[kScanItems];
+        Agg a = agg_zero();
 #pragma unroll
-    for (uint32_t k = 0; k < kScanItems; ++k) {
-        const uint64_t i = i0 + k;
-        if (i < t.n) {
-            const uint64_t nw = f[k] ? o[k] : run.v;
-            if ((outputs & kOutNew) && new_offset) new_offset[i] = nw;
-            if (l[k]) {
-                if (outputs & kOutNew) {
-                    lo.dst[run.cnt] = nw;
-                    lo.pin[run.cnt] = (uint8_t)p[k];
-                    if (lo.ent)
-                        lo.ent[run.cnt] = RemapEnt{(uint32_t)(o[k] & lo.key_mask),
-                                                   (uint32_t)((o[k] + s[k]) >> 5),
-                                                   (uint32_t)((o[k] - nw) >> 5), 0u};
-                    else if (lo.rec32)
-                        lo.rec32[run.cnt] = LiveRec32{(uint32_t)((o[k] + s[k]) >> 5),
-                                                      (uint32_t)((o[k] - nw) >> 5)};
-                    else
-                        lo.rec[run.cnt] = LiveRec{o[k] + s[k], o[k] - nw};
-                    if (lo.key) lo.key[run.cnt] = (uint32_t)(o[k] & lo.key_mask);
-                }
-                if (outputs & (kOutNew | kOutSelect)) {
-                    lo.src[run.cnt] = o[k];
-                    lo.size[run.cnt] = s[k];
-                }
-                if (outputs & kOutSelect) {
-                    lo.z[run.cnt] = run.lsum;
-                    lo.pc[run.cnt] = (uint32_t)run.pcnt;
-                }
-                const uint64_t gap = o[k] - run.mx;
-                if (gap) {
-                    gaps += 1;
-                    max_gap = umax64(max_gap, gap);
-                    if (gap >= fit_need) min_fit = umin64(min_fit, run.mx);
-                }
-                if (o[k] != nw) {
-                    moved += 1;
-                    moved_bytes += s[k];
-                    min_dst = umin64(min_dst, nw);
-                }
-                min_size = umin64(min_size, s[k]);
+        for (uint32_t k = 0; k < kScanItems; ++k) {
+            const uint64_t i = i0 + k;
+            o[k] = 0;
+            s[k] = 0;
+            l[k] = 0;
+            p[k] = 0;
+            f[k] = 0;
+            if (i < t.n) {
+                o[k] = t.off[i];
+                s[k] = t.size[i];
+                l[k] = live_of(t, i) ? 1u : 0u;
+                p[k] = pin_of(t, i) ? 1u : 0u;
+                f[k] = stays(o[k], l[k], p[k], w);
+                a = combine(a, element(o[k], s[k], l[k], p[k], f[k]));
             }
-            run = combine(run, element(o[k], s[k], l[k], p[k], f[k]));
         }
-    }
+        Agg total;
+        const Agg ex = block_excl<kScanThreads>(a, total, sh);
+        Agg run = combine(carry, ex);
+        carry = combine(carry, total);
+#pragma unroll
+        for (uint32_t k = 0; k < kScanItems; ++k) {
+            const uint64_t i = i0 + k;
+            if (i < t.n) {
+                const uint64_t nw = f[k] ? o[k] : run.v;
+                if ((outputs & kOutNew) && new_offset) new_offset[i] = nw;
+                if (l[k]) {
+                    if (outputs & kOutNew) {
+                        lo.dst[run.cnt] = nw;
+                        lo.pin[run.cnt] = (uint8_t)p[k];
+                        if (lo.ent)
+                            lo.ent[run.cnt] = RemapEnt{(uint32_t)(o[k] & lo.key_mask),
+                                                       (uint32_t)((o[k] + s[k]) >> 5),
+                                                       (uint32_t)((o[k] - nw) >> 5), 0u};
+                        else if (lo.rec32)
+                            lo.rec32[run.cnt] = LiveRec32{(uint32_t)((o[k] + s[k]) >> 5),
+                                                          (uint32_t)((o[k] - nw) >> 5)};
+                        else
+                            lo.rec[run.cnt] = LiveRec{o[k] + s[k], o[k] - nw};
+                        if (lo.key) lo.key[run.cnt] = (uint32_t)(o[k] & lo.key_mask);
+                    }
+                    if (outputs & (kOutNew | kOutSelect)) {
+                        lo.src[run.cnt] = o[k];
+                        lo.size[run.cnt] = s[k];
+                    }
+                    if (outputs & kOutSelect) {
+                        lo.z[run.cnt] = run.lsum;
+                        lo.pc[run.cnt] = (uint32_t)run.pcnt;
+                    }
+                    const uint64_t gap = o[k] - run.mx;
+                    if (gap) {
+                        gaps += 1;
+                        max_gap = umax64(max_gap, gap);
+                        if (gap >= fit_need) min_fit = umin64(min_fit, run.mx);
+                    }
+                    if (o[k] != nw) {
+                        moved += 1;
+                        moved_bytes += s[k];
+                        min_dst = umin64(min_dst, nw);
+                    }
+                    min_size = umin64(min_size, s[k]);
+                }
+                run = combine(run, element(o[k], s[k], l[k], p[k], f[k]));
+            }
+        }
+    }  // steps of the chunk
     max_gap = block_reduce<kScanThreads>(max_gap, shr, OpMax());
     gaps = block_reduce<kScanThreads>(gaps, shr, OpAdd());
     moved = block_reduce<kScanThreads>(moved, shr, OpAdd());
@@ -404,6 +418,9 @@ __device__ void scan_finish(const StatPart *spart, uint64_t nb, uint64_t arena_b
             hdr->epoch = epoch;
             hdr->ticket = 0;
             hdr->status = 0;
+            hdr->late_tiles = 0;
+            hdr->waited_tiles = 0;
+            hdr->polls = 0;
         }
     }
 }
@@ -442,19 +459,22 @@ __device__ inline uint64_t whole_in_block(const LiveView &lv, uint64_t k, uint64
 }
 
 // Pass 5: per-workgroup tile counts (and whole-window counts) over the live
-// blocks; workgroup blk covers live blocks [blk * kScanTile, ...).
+// blocks; workgroup blk covers live blocks [blk * chunk, (blk + 1) * chunk).
 __device__ void tcount_partial(LiveView lv, const WsHeader *hdr, uint64_t T, uint64_t *tpart,
-                               uint64_t *twhole, uint64_t blk) {
+                               uint64_t *twhole, uint64_t blk, uint64_t chunk) {
     __shared__ uint64_t sh[kScanThreads / 64];
     if (plan_dead(hdr)) return;
     const uint64_t m = hdr->live_blocks;
-    const uint64_t k0 = blk * kScanTile + (uint64_t)threadIdx.x * kScanItems;
+    const uint64_t end = umin64((blk + 1) * chunk, m);
     uint64_t c = 0, w = 0;
+    for (uint64_t k0 = blk * chunk + (uint64_t)threadIdx.x * kScanItems; k0 < end;
+         k0 += kScanTile) {
 #pragma unroll
-    for (uint32_t j = 0; j < kScanItems; ++j) {
-        if (k0 + j < m) {
-            c += tiles_in_block(lv, k0 + j, T);
-            w += whole_in_block(lv, k0 + j, T);
+        for (uint32_t j = 0; j < kScanItems; ++j) {
+            if (k0 + j < end) {
+                c += tiles_in_block(lv, k0 + j, T);
+                w += whole_in_block(lv, k0 + j, T);
+            }
         }
     }
     c = block_reduce<kScanThreads>(c, sh, OpAdd());
@@ -497,6 +517,7 @@ struct AfterScan {
     uint64_t tile_bytes;
     uint64_t *tpart, *twhole;
     uint64_t gnb;
+    uint64_t chunk;     // live blocks per counting workgroup
     uint32_t *ridx;
     uint32_t rw;        // remap bucket width (log2 bytes)
     uint64_t rnb;       // remap buckets
@@ -512,7 +533,7 @@ static_assert(kSpineThreads == kScanThreads, "the finish runs as one workgroup o
 __global__ __launch_bounds__(kScanThreads) void k_after_scan(AfterScan a, WsHeader *hdr) {
     const uint64_t blk = blockIdx.x;
     if (blk < a.gnb) {
-        tcount_partial(a.lv, hdr, a.tile_bytes, a.tpart, a.twhole, blk);
+        tcount_partial(a.lv, hdr, a.tile_bytes, a.tpart, a.twhole, blk, a.chunk);
     } else if (blk < a.gnb + a.rblocks) {
         remap_index_part(a.lv.src, hdr, a.rw, a.rnb, a.ridx, blk - a.gnb);
     } else {
@@ -549,24 +570,30 @@ __global__ __launch_bounds__(kSpineThreads) void k_tcount_spine(const uint64_t *
 // block whose first tile index is <= t).
 __global__ __launch_bounds__(kScanThreads) void k_tcount_down(LiveView lv, const WsHeader *hdr,
                                                               uint64_t T, const uint64_t *tprefix,
-                                                              uint32_t *tile_base) {
+                                                              uint32_t *tile_base, uint64_t chunk) {
     __shared__ uint64_t sh[kScanThreads / 64];
     if (plan_dead(hdr)) return;
     const uint64_t m = hdr->live_blocks;
-    const uint64_t k0 = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanItems;
-    uint64_t c[kScanItems];
-    uint64_t sum = 0;
+    const uint64_t base = (uint64_t)blockIdx.x * chunk;
+    const uint64_t end = umin64(base + chunk, m);
+    uint64_t carry = tprefix[blockIdx.x];
+    for (uint64_t s0 = base; s0 < end; s0 += kScanTile) {
+        const uint64_t k0 = s0 + (uint64_t)threadIdx.x * kScanItems;
+        uint64_t c[kScanItems];
+        uint64_t sum = 0;
 #pragma unroll
-    for (uint32_t j = 0; j < kScanItems; ++j) {
-        c[j] = (k0 + j < m) ? tiles_in_block(lv, k0 + j, T) : 0;
-        sum += c[j];
-    }
-    uint64_t total;
-    uint64_t run = tprefix[blockIdx.x] + block_excl_sum<kScanThreads>(sum, total, sh);
+        for (uint32_t j = 0; j < kScanItems; ++j) {
+            c[j] = (k0 + j < end) ? tiles_in_block(lv, k0 + j, T) : 0;
+            sum += c[j];
+        }
+        uint64_t total;
+        uint64_t run = carry + block_excl_sum<kScanThreads>(sum, total, sh);
+        carry += total;
 #pragma unroll
-    for (uint32_t j = 0; j < kScanItems; ++j) {
-        if (k0 + j < m) tile_base[k0 + j] = (uint32_t)run;
-        run += c[j];
+        for (uint32_t j = 0; j < kScanItems; ++j) {
+            if (k0 + j < end) tile_base[k0 + j] = (uint32_t)run;
+            run += c[j];
+        }
     }
 }
 
@@ -864,7 +891,7 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
     const uint64_t nb = L.n_scan_blocks;
     if (nb) {
         hipLaunchKernelGGL(k_scan_partials, dim3((uint32_t)nb), dim3(kScanThreads), 0, s, t,
-                           arena_bytes, win, part);
+                           arena_bytes, win, (uint64_t)L.scan_chunk, part);
         AC_TRY(hipGetLastError());
     }
     hipLaunchKernelGGL(k_scan_spine, dim3(1), dim3(kSpineThreads), 0, s, part, prefix, nb, hdr,
@@ -872,7 +899,8 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
     AC_TRY(hipGetLastError());
     if (nb) {
         hipLaunchKernelGGL(k_scan_down, dim3((uint32_t)nb), dim3(kScanThreads), 0, s, t, win,
-                           prefix, hdr, new_offset, lo, spart, outputs, fit_need);
+                           prefix, hdr, new_offset, lo, spart, outputs, fit_need,
+                           (uint64_t)L.scan_chunk);
         AC_TRY(hipGetLastError());
     }
     if (!(outputs & kOutNew)) {
@@ -896,6 +924,7 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
         as.tpart = tpart;
         as.twhole = twhole;
         as.gnb = gnb;
+        as.chunk = L.scan_chunk;
         as.ridx = ridx;
         as.rw = remap_shift(arena_bytes, t.n);
         as.rnb = remap_buckets(arena_bytes, t.n);
@@ -913,7 +942,7 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
                            hdr);
         AC_TRY(hipGetLastError());
         hipLaunchKernelGGL(k_tcount_down, dim3((uint32_t)gnb), dim3(kScanThreads), 0, s, lv, hdr,
-                           (uint64_t)tile_bytes, tprefix, tile_base);
+                           (uint64_t)tile_bytes, tprefix, tile_base, (uint64_t)L.scan_chunk);
         AC_TRY(hipGetLastError());
         // tile starts and records: a grid for the whole capacity, each lane
         // checks the device-side tile count (no host round trip)

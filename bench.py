@@ -85,58 +85,59 @@ def _host_description() -> str:
     return f"{model}; {os.cpu_count()} logical CPUs; {mem / 2**30:.0f} GiB RAM"
 
 
-def cpu_baseline(heap, budget_s: float = 12.0):
-    """The oracle, single-threaded, on a bounded slice of the same workload:
-    the entries of the training-80g table that lie in a 4 GiB window of its mixed
-    activation/small-block region, rebased to offset 0, with the handles that
-    fall inside it.  Times validate + new offsets + stats + ordered memmove +
-    remap, repeated (restoring the arena untimed) until the budget is spent."""
+def cpu_baseline(heap, reps: int = 3):
+    """The oracle as it stands, single-threaded, on the whole heap the GPU
+    compacts (every entry, every byte of the arena, every handle): validate +
+    new offsets + statistics, the ordered memmove, and the remap, each timed
+    on its own; median of ``reps`` runs, the arena restored to its pristine
+    payload before each run (untimed; the generator fills it on all cores).
+    Needs the arena's size in host memory."""
     import numpy as np
     import torch
     import oracle
     import workloads as W
 
-    lo_addr = 40 * W.GiB
-    hi_addr = 44 * W.GiB
-    off, size, live = heap.offset, heap.size, heap.live
-    i0 = int(np.searchsorted(off, lo_addr))
-    ends = off + size
-    i1 = int(np.searchsorted(ends, hi_addr, side="right"))
-    base = int(off[i0])
-    s_off = off[i0:i1] - np.uint64(base)
-    s_size = size[i0:i1].copy()
-    s_live = live[i0:i1].copy()
-    S = int(s_off[-1] + s_size[-1])
-    hs = heap.handles
-    hs = hs[(hs >= np.uint64(base)) & (hs < np.uint64(base + S))] - np.uint64(base)
-    pristine = torch.empty(S, dtype=torch.uint8)
-    W.fill_payload(pristine, base, heap.payload_mode, heap.payload_seed)
-    pristine = pristine.numpy()
-    arena = np.empty_like(pristine)
-    moved = oracle.stats(s_off, s_size, s_live, S).moved_bytes
-    reps, t_total = 0, 0.0
-    while t_total < budget_s and reps < 50:
-        np.copyto(arena, pristine)
+    S = heap.arena_bytes
+    off, size, live, hs = heap.offset, heap.size, heap.live, heap.handles
+    arena = np.empty(S, dtype=np.uint8)
+    at = torch.from_numpy(arena)
+    phases = {"plan_stats": [], "memmove": [], "remap": []}
+    moved = None
+    for r in range(reps):
+        W.fill_payload(at, 0, heap.payload_mode, heap.payload_seed)
         t0 = time.perf_counter()
-        rc = oracle.validate(s_off, s_size, s_live, S)[0]
-        oracle.new_offsets(s_off, s_size, s_live)
-        oracle.stats(s_off, s_size, s_live, S)
-        oracle.compact(arena, s_off, s_size, s_live)
-        oracle.remap(s_off, s_size, s_live, hs)
-        t_total += time.perf_counter() - t0
-        reps += 1
+        rc = oracle.validate(off, size, live, S, pinned=heap.pinned)[0]
+        oracle.new_offsets(off, size, live, heap.pinned)
+        st = oracle.stats(off, size, live, S, pinned=heap.pinned)
+        t1 = time.perf_counter()
+        oracle.compact(arena, off, size, live, heap.pinned)
+        t2 = time.perf_counter()
+        oracle.remap(off, size, live, hs, pinned=heap.pinned)
+        t3 = time.perf_counter()
         assert rc == oracle.OK
-    per = t_total / reps
+        moved = st.moved_bytes
+        phases["plan_stats"].append(t1 - t0)
+        phases["memmove"].append(t2 - t1)
+        phases["remap"].append(t3 - t2)
+        print(f"# cpu baseline run {r}: plan+stats {t1 - t0:.3f} s, memmove {t2 - t1:.3f} s, "
+              f"remap {t3 - t2:.3f} s", file=sys.stderr, flush=True)
+    del at, arena
+    med = {k: float(np.median(v)) for k, v in phases.items()}
+    total = sum(med.values())
     return {
-        "value": round(2 * moved / per / 1e9, 3),
+        "value": round(2 * moved / total / 1e9, 3),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
         "host": _host_description(),
-        "sample": (f"training-80g entries {i0}..{i1 - 1} (the 4 GiB window at 40 GiB, "
-                   f"{i1 - i0} entries, {S} B arena, {moved} B moved, {hs.shape[0]} handles); "
-                   f"validate+plan+stats+memmove+remap, {reps} reps, {per * 1e3:.1f} ms each"),
-        "handles_per_s": round(hs.shape[0] / per, 1),
+        "sample": (f"the whole {heap.name} heap ({S} B arena, {heap.n} entries, {moved} B "
+                   f"moved, {hs.shape[0]} handles): validate + new offsets + statistics, "
+                   f"ordered memmove, remap; median of {reps} runs, arena restored untimed "
+                   f"between runs"),
+        "seconds_per_compaction": round(total, 3),
+        "seconds": {k: round(v, 4) for k, v in med.items()},
+        "memmove_GBps": round(2 * moved / med["memmove"] / 1e9, 3),
+        "handles_per_s": round(hs.shape[0] / med["remap"], 1),
     }
 
 
@@ -220,10 +221,16 @@ def main() -> int:
                     help="refill the arena before each step by regenerating the payload with "
                          "torch ops instead of copying a pristine snapshot")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cpu-reps", type=int, default=3,
+                    help="runs of the CPU oracle on the whole heap (median reported)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="GIB",
                     help="only run a plain device-to-device copy of GIB GiB (twice): the "
                          "reference kernel that scales the HBM byte counters")
+    ap.add_argument("--calibrate-move", type=int, default=0, metavar="GIB",
+                    help="only run the mover (twice) on one GIB GiB block that moves down by "
+                         "GIB GiB: a plain copy of known size with the mover's own streaming "
+                         "loads and stores and no dependency, to scale the byte counters of "
+                         "its non-temporal accesses")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -248,6 +255,23 @@ def main() -> int:
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": nb, "copies": 2}), flush=True)
+        return 0
+    if args.calibrate_move:
+        nb = args.calibrate_move << 30
+        heap = W.table_from_lists(2 * nb, [(0, nb), (nb, nb)], [0, 1], [], name="calibrate")
+        o_, s_, l_ = (torch.from_numpy(heap.offset.view(np.int64)).to(dev),
+                      torch.from_numpy(heap.size.view(np.int64)).to(dev),
+                      torch.from_numpy(heap.live).to(dev))
+        a = torch.zeros(2 * nb, dtype=torch.uint8, device=dev)
+        ws = ac.workspace(heap.n, 2 * nb, device=dev)
+        for _ in range(2):
+            p = ac.defrag_plan(o_, s_, l_, 2 * nb, ws)
+            ac.defrag_move(a, p, ws)
+            assert ac.defrag_move_status(p, ws) == ac.DEFRAG_OK
+            rep = ac.defrag_move_report(p, ws)
+            assert rep.late_tiles == 0
+        print(json.dumps({"calibrate_move_bytes": nb, "moves": 2, "tiles": int(p.n_tiles)}),
+              flush=True)
         return 0
     t_gen = time.time()
     heap = W.workload(args.workload)
@@ -347,6 +371,7 @@ def main() -> int:
         torch.cuda.synchronize()
         st = ac.defrag_move_status(plan, ws)
         assert st == ac.DEFRAG_OK, st
+        rep = ac.defrag_move_report(plan, ws)
         if heap.pinned is None:   # one top hole afterwards
             assert post.hole_count == (1 if post.free_bytes else 0)
             assert post.frag_free_over_largest_minus_1 == 0.0
@@ -482,6 +507,8 @@ def main() -> int:
         "move_pct_hbm_peak": round(100 * move_gbps / HBM_PEAK_GBPS, 2),
         "handles_per_s": round(handles_per_s, 1),
         "ms": {k: round(v, 4) for k, v in mean.items()},
+        "mover_waits": {"tiles": int(rep.tiles), "late_tiles": int(rep.late_tiles),
+                        "waited_tiles": int(rep.waited_tiles), "polls": int(rep.polls)},
         "min_move_ms": round(float(np.min(times["move"])), 4),
         "median_move_ms": round(float(np.median(times["move"])), 4),
         "max_move_GBps": round(2 * moved / (float(np.min(times["move"])) * 1e-3) / 1e9, 2),
@@ -514,7 +541,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline and args.workload == "training-80g":
         print("# cpu baseline ...", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(heap, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(heap, args.cpu_reps)
     print(json.dumps(out), flush=True)
     return 0
 

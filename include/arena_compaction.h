@@ -40,21 +40,22 @@
  * Ownership: the caller owns every buffer (arena, table, outputs, handles and
  * the workspace).  The library allocates no device memory and never writes
  * the table.  Its only process-wide state is a counter for plan epochs, a
- * per-device cache of the compute-unit count, and one HIP stream per device
- * that defrag_compact creates on first use.
+ * per-device cache of the compute-unit count, and -- unless the caller
+ * passes its own (defrag_compact_args.side_stream) -- one HIP stream per
+ * device that defrag_compact creates on first use.
  *
  * Concurrency: between defrag_plan and the end of defrag_move nothing else
  * may read or write the arena, the table or the workspace (the 910C page runs
  * compaction while the affected tensors pause reads and writes -- a global
  * sync point).  defrag_remap and defrag_commit read the plan from the
  * workspace too, so until the last of them the workspace serves no other
- * call, except defrag_stats and defrag_first_fit of a table with no more
- * entries than the planned one: those write only the workspace's scratch
- * region and the statistics fields of its header, below and beside the
- * plan's data (defrag_compact's post-check is such a call).  A larger table
- * would overwrite the plan without any call noticing.  Ordering is the
- * stream's order; calls on distinct workspaces are independent.  Every pointer argument named "_dev" is device memory on
- * the stream's device; "_host" is host memory.
+ * call, except defrag_stats and defrag_first_fit (of any table): those
+ * write only a statistics region of fixed size and a header of their own,
+ * in front of the plan's data (defrag_compact's post-check is such a call).
+ * Ordering is the stream's order;
+ * calls on distinct workspaces are independent.  Every pointer argument
+ * named "_dev" is device memory on the stream's device; "_host" is host
+ * memory.
  *
  * Errors: negative return codes below.  Validation runs inside defrag_plan /
  * defrag_stats on the device before any output is written, so an invalid
@@ -79,6 +80,14 @@ extern "C" {
 #define DEFRAG_EHIP (-4)       /* a HIP runtime call failed                    */
 #define DEFRAG_ETIMEOUT (-5)   /* mover watchdog expired (a wait never ended)  */
 #define DEFRAG_ENOFIT (-6)     /* no hole holds / no window frees the request  */
+#define DEFRAG_ECAPACITY (-7)  /* a mover tile met more blocks than the launch
+                                  gave it room for (the plan and the launch
+                                  disagree; the arena is then undefined)       */
+#define DEFRAG_ECORRUPT (-8)   /* the workspace no longer holds a consistent
+                                  plan (overwritten since planning): tiles
+                                  whose bytes or blocks fall outside the arena
+                                  or the plan's arrays were not moved; the
+                                  arena is then undefined                     */
 
 /* Why a table was rejected: the first failing entry, and within it the first
  * failing check in the order zero size, misaligned, live flag, pinned flag,
@@ -144,6 +153,17 @@ typedef struct defrag_tuning {
                                  2 loads only, 3 stores only                 */
     uint32_t spin_limit_log2; /* mover watchdog: a wait gives up after
                                  2^x polls (default 22, a few seconds)       */
+    /* Testing knob for the mover's dependency waits (0 = off); the result
+     * does not change.  Tile t holds back its "sources read" flag -- the one
+     * later tiles overwriting its sources wait for -- for stall_sleeps sleeps
+     * of 127 x 64 clocks (about 3.4 us each at 2.4 GHz, at most 4096) when
+     * h(t ^ stall_seed) % stall_every == 0, with h the 32-bit mix
+     * x * 0x9E3779B1 then x ^ (x >> 15).  defrag_move_report counts the
+     * waits that follow. */
+    uint32_t stall_every;
+    uint32_t stall_sleeps;
+    uint32_t stall_seed;
+    uint32_t reserved;        /* 0 */
 } defrag_tuning;
 
 /* Filled by defrag_plan (host memory, caller-owned).  Treat as opaque except
@@ -255,9 +275,30 @@ int defrag_move(void *arena_dev, uint64_t arena_bytes, defrag_plan_t *plan_host,
 /* After defrag_move: synchronise the stream and report whether the move
  * finished (DEFRAG_OK), or a wait timed out (DEFRAG_ETIMEOUT; the arena is
  * then undefined) or the workspace no longer held this plan
- * (DEFRAG_ENOPLAN; nothing moved). */
+ * (DEFRAG_ENOPLAN; nothing moved), or held it damaged (DEFRAG_ECORRUPT) or
+ * the launch had too little room for a tile's blocks (DEFRAG_ECAPACITY). */
 int defrag_move_status(const defrag_plan_t *plan_host, const void *ws_dev,
                        hipStream_t stream);
+
+/* After defrag_move (or defrag_compact): synchronise the stream and report
+ * the move's outcome (status: what defrag_move_status returns) with the
+ * mover's wait counters.  A tile is late when the flags of the earlier tiles
+ * it must wait for were not all set when it first read them, right behind
+ * its own loads; a late tile that then read one of them unset waited, and
+ * polls counts those unset reads.  Returns DEFRAG_OK when the report is
+ * filled (whatever the move's status), else an error as defrag_move_status.
+ * Zeroed by the plan: valid until the workspace is planned again. */
+typedef struct defrag_move_report_t {
+    int32_t status;
+    int32_t reserved;
+    uint64_t tiles;
+    uint64_t late_tiles;
+    uint64_t waited_tiles;
+    uint64_t polls;
+} defrag_move_report_t;
+
+int defrag_move_report(const defrag_plan_t *plan_host, const void *ws_dev,
+                       hipStream_t stream, defrag_move_report_t *out_host);
 
 /* Inspection of a plan's mover schedule, for tests and tools (the mover
  * itself needs no call).  The moved destination bytes are cut into tiles --
@@ -286,7 +327,16 @@ int defrag_plan_tiles(const defrag_plan_t *plan_host, const void *ws_dev,
 /* Remap handles (910C: update every reference in one batch).  h_out_dev may
  * equal h_in_dev.  *n_invalid_dev (may be NULL) receives the number of
  * handles mapped to UINT64_MAX.  Needs a valid plan of the table the handles
- * refer to (before or after the move).  Asynchronous. */
+ * refer to (before or after the move).  Asynchronous.
+ *
+ * The remap is a function of the old table and its new offsets alone:
+ * h inside live entry i maps to new_offset[i] + (h - offset[i]).  The plan
+ * is where the library keeps that pair (the packed old offsets and shifts,
+ * plus a bucket index over them), so the call takes the plan, not the
+ * table: a caller holding only (old table, new_offset) plans that table
+ * again (defrag_plan writes the same new_offset) and remaps through it.
+ * The workspace must still hold the plan: remap every batch of handles
+ * before the workspace is planned again. */
 int defrag_remap(const defrag_plan_t *plan_host, const void *ws_dev,
                  size_t ws_bytes, const uint64_t *h_in_dev, uint64_t *h_out_dev,
                  uint64_t n_handles, uint64_t *n_invalid_dev, hipStream_t stream);
@@ -340,6 +390,11 @@ typedef struct defrag_compact_args {
     uint64_t *size_out_dev;        /* any may be NULL                         */
     uint8_t *live_out_dev;
     uint8_t *pinned_out_dev;
+    /* The second stream the move overlaps with (see above): NULL takes the
+     * library's own, one per device, created on first use and kept; pass a
+     * stream of your own (on the same device, not `stream`) and the call
+     * creates none, so the library holds no stream at all. */
+    hipStream_t side_stream;
 } defrag_compact_args;
 
 int defrag_compact(const defrag_compact_args *args, hipStream_t stream,

@@ -101,6 +101,73 @@ def run_gpu(heap: W.Heap, dev="cuda", tuning=None, arena: Optional[torch.Tensor]
                   arena, ws)
 
 
+def run_gpu_compact(heap: W.Heap, arena: torch.Tensor, request: int = 0, tuning=None,
+                    side_stream=None) -> GpuRun:
+    """The whole operator through one C-ABI call (defrag_compact): plan
+    (targeted when request > 0), move, remap, commit and post-check."""
+    import arena_compaction_amd as ac
+    off, size, live = device_table(heap, "cuda")
+    pin = device_pinned(heap, "cuda")
+    ws = ac.workspace(heap.n, heap.arena_bytes, tuning.tile_bytes if tuning else 0,
+                      max_pinned=heap.n_pinned)
+    new_off = torch.full((heap.n,), -7, dtype=torch.int64, device="cuda")
+    h = u64_to_t(heap.handles, "cuda")
+    n_bad = torch.full((1,), -3, dtype=torch.int64, device="cuda")
+    m = int(heap.live.sum())
+    c_off = torch.empty(m, dtype=torch.int64, device="cuda")
+    c_size = torch.empty(m, dtype=torch.int64, device="cuda")
+    c_pin = torch.full((m,), 9, dtype=torch.uint8, device="cuda")
+    plan, post = ac.defrag_compact(off, size, live, heap.arena_bytes, arena, ws, request,
+                                   new_off, h, h, n_bad, c_off, c_size, None, c_pin,
+                                   tuning=tuning, pinned=pin, side_stream=side_stream)
+    torch.cuda.synchronize()
+    want_pin = (np.zeros(m, np.uint8) if heap.pinned is None
+                else heap.pinned[np.flatnonzero(heap.live)])
+    assert np.array_equal(c_pin.cpu().numpy(), want_pin)
+    return GpuRun(plan, t_to_u64(new_off), t_to_u64(h), int(n_bad.item()), post, 0, arena, ws)
+
+
+def oracle_arena(heap: W.Heap, hold: Optional[np.ndarray] = None) -> np.ndarray:
+    """The whole compacted arena on the host: the generator's pristine
+    payload, then the oracle's ordered memmove over it.  Full-size heaps
+    need their arena's size in host memory (80 GiB for training-80g)."""
+    ref = np.empty(heap.arena_bytes, dtype=np.uint8)
+    W.fill_payload(torch.from_numpy(ref), 0, heap.payload_mode, heap.payload_seed)
+    oracle.compact(ref, heap.offset, heap.size, heap.live,
+                   heap.pinned if hold is None else hold)
+    return ref
+
+
+_libc = None
+
+
+def check_arena_every_byte(arena: torch.Tensor, ref: np.ndarray, what: str = "",
+                           chunk: int = 1 << 30) -> None:
+    """Every byte of the device arena against a host arena, chunk by chunk
+    through one pinned buffer; reports the first differing bytes."""
+    global _libc
+    if _libc is None:
+        import ctypes
+        _libc = ctypes.CDLL(None)
+        _libc.memcmp.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
+        _libc.memcmp.restype = ctypes.c_int
+    S = ref.shape[0]
+    assert arena.numel() == S and ref.flags["C_CONTIGUOUS"]
+    chunk = min(chunk, max(S, 1))
+    buf = torch.empty(chunk, dtype=torch.uint8, pin_memory=True)
+    bnp = buf.numpy()
+    base = ref.ctypes.data
+    for k, p in enumerate(range(0, S, chunk)):
+        ln = min(chunk, S - p)
+        buf[:ln].copy_(arena[p:p + ln])
+        if _libc.memcmp(bnp.ctypes.data, base + p, ln) != 0:
+            bad = np.flatnonzero(bnp[:ln] != ref[p:p + ln])
+            raise AssertionError(f"{what}: arena differs from the oracle at {bad.shape[0]} bytes "
+                                 f"of [{p}, {p + ln}), first {(bad[:8] + p).tolist()}")
+        if k % 16 == 15:
+            log(f"  {what}: {p + ln} of {S} bytes equal")
+
+
 def check_stats(got, want, what=""):
     for k in STAT_KEYS:
         g, w = getattr(got, k), getattr(want, k)

@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
     for f in ("defrag_stats", "defrag_first_fit", "defrag_plan", "defrag_plan_targeted",
               "defrag_compact", "defrag_move", "defrag_remap",
               "defrag_workspace_bytes", "defrag_strerror", "defrag_commit",
-              "defrag_move_status", "defrag_plan_tiles"):
+              "defrag_move_status", "defrag_move_report", "defrag_plan_tiles"):
         assert f in fns, f
 
 
@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 def test_strerror_and_codes():
     import arena_compaction_amd as ac
     assert ac.defrag_strerror(0) == "ok"
-    for c in (-1, -2, -3, -4, -5, -6):
+    for c in (-1, -2, -3, -4, -5, -6, -7, -8):
         assert ac.defrag_strerror(c) not in ("ok", "unknown error")
     assert ac.defrag_strerror(-99) == "unknown error"
 
@@ -75,6 +75,9 @@ def test_host_side_argument_errors_need_no_gpu():
     assert L.defrag_commit(ctypes.byref(plan), None, 0, None, None, None, None, None) == ac.DEFRAG_ENOPLAN
     assert L.defrag_move_status(ctypes.byref(plan), None, None) == ac.DEFRAG_ENOPLAN
     assert L.defrag_plan_tiles(ctypes.byref(plan), None, 0, None, 0, None) == ac.DEFRAG_ENOPLAN
+    rep = ac.defrag_move_report_t()
+    assert L.defrag_move_report(ctypes.byref(plan), None, None, ctypes.byref(rep)) == ac.DEFRAG_ENOPLAN
+    assert L.defrag_move_report(ctypes.byref(plan), None, None, None) == ac.DEFRAG_EINVAL
     # missing table / output pointers
     st = ac.defrag_stats_t()
     assert L.defrag_stats(None, 0, None, 0, None, ctypes.byref(st)) == ac.DEFRAG_EINVAL
@@ -117,10 +120,10 @@ def test_host_side_argument_errors_need_no_gpu():
     assert L.defrag_compact(ctypes.byref(args), None, ctypes.byref(plan),
                             ctypes.byref(st)) == ac.DEFRAG_EINVAL
     assert L.defrag_compact(ctypes.byref(args), None, None, None) == ac.DEFRAG_EINVAL
-    # bad tile size
-    tu = ac.defrag_tuning(100, 0, 0, 0)
-    assert L.defrag_plan(ctypes.byref(t), 4096, ctypes.byref(tu), ctypes.c_void_p(0x1000),
-                         1 << 20, None, None, ctypes.byref(plan)) == ac.DEFRAG_EINVAL
+    # bad tile size, too many sleeps for the wait-path knob
+    for tu in (ac.defrag_tuning(100, 0, 0, 0), ac.defrag_tuning(0, 1, 1, 0, 1, 4097, 0, 0)):
+        assert L.defrag_plan(ctypes.byref(t), 4096, ctypes.byref(tu), ctypes.c_void_p(0x1000),
+                             1 << 20, None, None, ctypes.byref(plan)) == ac.DEFRAG_EINVAL
 
 
 def test_binding_refuses_bad_buffers_before_any_call():
@@ -202,3 +205,37 @@ def test_build_is_quiet_and_device_code_has_no_packed_fp32():
         for op in ("v_pk_fma_f32", "v_pk_mul_f32", "v_pk_add_f32"):
             assert op not in asm, f"{src}: {op} in the device code"
     sys.stdout.flush()
+
+
+def test_binding_structs_match_the_header():
+    """sizeof and field offsets of every struct the binding mirrors, as the C
+    compiler lays them out from the header."""
+    import ctypes
+    import subprocess
+    import tempfile
+    import arena_compaction_amd as ac
+    structs = {"defrag_table": ac.defrag_table, "defrag_stats_t": ac.defrag_stats_t,
+               "defrag_tuning": ac.defrag_tuning, "defrag_plan_t": ac.defrag_plan_t,
+               "defrag_compact_args": ac.defrag_compact_args,
+               "defrag_move_report_t": ac.defrag_move_report_t,
+               "defrag_monitor_cfg": ac.defrag_monitor_cfg,
+               "defrag_monitor_report": ac.defrag_monitor_report}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "arena_compaction.h"',
+             'int main(void) {']
+    for name, cls in structs.items():
+        lines.append(f'printf("{name} %zu\\n", sizeof({name}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{name}.{f} %zu\\n", offsetof({name}, {f}));')
+    lines.append('return 0; }')
+    with tempfile.TemporaryDirectory() as tmp:
+        src = os.path.join(tmp, "layout.c")
+        exe = os.path.join(tmp, "layout")
+        open(src, "w").write("\n".join(lines))
+        subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                        "-I", "/opt/rocm/include", src, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    got = dict(line.rsplit(" ", 1) for line in out.splitlines())
+    for name, cls in structs.items():
+        assert int(got[name]) == ctypes.sizeof(cls), name
+        for f, _ in cls._fields_:
+            assert int(got[f"{name}.{f}"]) == getattr(cls, f).offset, f"{name}.{f}"

@@ -7,9 +7,8 @@ import torch
 
 import oracle
 import workloads as W
-from harness import (GpuRun, check_arena_full, check_arena_sampled, check_stats,
-                     check_tables_and_handles,
-                     device_pinned, device_table, log, pristine_host, sample_windows, t_to_u64,
+from harness import (check_arena_full, check_stats, check_tables_and_handles,
+                     device_pinned, device_table, log, pristine_host, run_gpu_compact, t_to_u64,
                      u64_to_t)
 
 pytestmark = pytest.mark.gpu
@@ -24,26 +23,7 @@ def ac():
 
 
 def compact_gpu(heap, arena, request=0, tuning=None):
-    import arena_compaction_amd as ac
-    off, size, live = device_table(heap, "cuda")
-    pin = device_pinned(heap, "cuda")
-    ws = ac.workspace(heap.n, heap.arena_bytes, tuning.tile_bytes if tuning else 0,
-                      max_pinned=heap.n_pinned)
-    new_off = torch.full((heap.n,), -7, dtype=torch.int64, device="cuda")
-    h = u64_to_t(heap.handles, "cuda")
-    n_bad = torch.full((1,), -3, dtype=torch.int64, device="cuda")
-    m = int(heap.live.sum())
-    c_off = torch.empty(m, dtype=torch.int64, device="cuda")
-    c_size = torch.empty(m, dtype=torch.int64, device="cuda")
-    c_pin = torch.full((m,), 9, dtype=torch.uint8, device="cuda")
-    plan, post = ac.defrag_compact(off, size, live, heap.arena_bytes, arena, ws, request,
-                                   new_off, h, h, n_bad, c_off, c_size, None, c_pin,
-                                   tuning=tuning, pinned=pin)
-    torch.cuda.synchronize()
-    want_pin = (np.zeros(m, np.uint8) if heap.pinned is None
-                else heap.pinned[np.flatnonzero(heap.live)])
-    assert np.array_equal(c_pin.cpu().numpy(), want_pin)
-    return GpuRun(plan, t_to_u64(new_off), t_to_u64(h), int(n_bad.item()), post, 0, arena, ws)
+    return run_gpu_compact(heap, arena, request, tuning)
 
 
 @pytest.mark.parametrize("k", W.NAMES)
@@ -75,21 +55,6 @@ def test_compact_tiny_heaps_and_tiles(ac):
         check_arena_full(heap, r, host)
 
 
-@pytest.mark.parametrize("k", ["overlap-64g", "training-80g-pinned"])
-def test_compact_full_size_sampled(ac, k):
-    """The one-call path at full size on the self-overlapping and the pinned
-    workload (the move sized on the device)."""
-    heap = W.workload(k)
-    log(f"case compact {heap.describe()} (sampled bytes)")
-    arena = torch.empty(heap.arena_bytes, dtype=torch.uint8, device="cuda")
-    W.fill_payload(arena, 0, heap.payload_mode, heap.payload_seed)
-    r = compact_gpu(heap, arena)
-    check_tables_and_handles(heap, r)
-    check_arena_sampled(heap, r, sample_windows(heap, np.random.default_rng(9), n_random=512))
-    del r, arena
-    torch.cuda.empty_cache()
-
-
 @pytest.mark.parametrize("k", ["training-80g", "training-80g-pinned"])
 def test_compact_targeted_small(ac, k):
     heap = W.workload(k, small=True)
@@ -106,19 +71,6 @@ def test_compact_targeted_small(ac, k):
         check_tables_and_handles(heap, r, hold=hold)
         check_arena_full(heap, r, host, hold=hold)
         assert r.post_stats.largest_hole >= R
-
-
-def test_compact_full_size_training_80g(ac):
-    heap = W.workload("training-80g")
-    log(f"case compact {heap.describe()} (sampled bytes)")
-    arena = torch.empty(heap.arena_bytes, dtype=torch.uint8, device="cuda")
-    W.fill_payload(arena, 0, heap.payload_mode, heap.payload_seed)
-    r = compact_gpu(heap, arena)
-    check_tables_and_handles(heap, r)
-    check_arena_sampled(heap, r, sample_windows(heap, np.random.default_rng(8), n_random=512))
-    assert r.post_stats.hole_count == 1 and r.post_stats.frag_free_over_largest_minus_1 == 0.0
-    del r, arena
-    torch.cuda.empty_cache()
 
 
 def test_compact_errors_leave_the_arena(ac):

@@ -318,28 +318,6 @@ def test_full_size_workloads_every_byte(ac, k):
     _full_check(heap)
 
 
-@pytest.mark.parametrize("k", ["training-80g", "training-80g-pinned", "overlap-64g"])
-def test_full_size_workloads_sampled(ac, k):
-    heap = W.workload(k)
-    log(f"case {heap.describe()} (sampled bytes)")
-    r = run_gpu(heap)
-    assert r.status == ac.DEFRAG_OK
-    check_tables_and_handles(heap, r)
-    seed = {"training-80g": 3, "training-80g-pinned": 5, "overlap-64g": 5}[k]
-    wins = sample_windows(heap, np.random.default_rng(seed), n_random=1024)
-    check_arena_sampled(heap, r, wins)
-    if k.startswith("training-80g"):
-        s = r.plan.stats
-        assert abs(s.frag_free_over_largest_minus_1 - 4.7) < 1e-3
-        if k == "training-80g":   # one top hole afterwards
-            assert r.post_stats.frag_free_over_largest_minus_1 == 0.0
-        else:        # the pinned blocks keep free space in separate holes
-            assert r.post_stats.hole_count > 1
-            assert 0.0 < r.post_stats.frag_free_over_largest_minus_1 < 4.7
-    del r
-    torch.cuda.empty_cache()
-
-
 def test_pinned_edge_cases_gpu(ac):
     """Pinned blocks at the arena ends, adjacent pinned blocks, everything
     pinned, and runs on both sides of a pinned block inside one tile window
@@ -510,3 +488,37 @@ def test_remap_at_bucket_boundaries(ac):
         r = _full_check(heap)
         want, bad = oracle.remap(heap.offset, heap.size, heap.live, heap.handles)
         assert np.array_equal(r.remapped, want) and r.n_invalid == bad
+
+
+def test_scan_workgroups_taking_several_steps(ac):
+    """Above 1,024 x 1,024 entries each scan workgroup takes several steps of
+    1,024 entries with a running carry: 3,000,000 entries of 32-96 bytes with
+    random gaps, live flags and a few pinned blocks, compacted bit-exactly at
+    two tile sizes, and a bad entry deep inside a later step of a chunk."""
+    rng = np.random.default_rng(31)
+    n = 3_000_000
+    size = (rng.integers(1, 4, n) * 32).astype(np.uint64)
+    gap = (rng.integers(0, 3, n) * 32).astype(np.uint64)
+    off = np.cumsum(size + gap) - size
+    live = (rng.random(n) < 0.55).astype(np.uint8)
+    pinned = ((rng.random(n) < 0.002) & (live == 1)).astype(np.uint8)
+    S = int(off[-1] + size[-1]) + 4096
+    heap = W.Heap("chunked scan 3M", S, off.astype(np.uint64), size, live, np.zeros(0, np.uint64),
+                  "hash", 31, 31)
+    heap.pinned = pinned
+    heap.handles = W.edge_handles(heap, rng, 20_000)
+    for tile in (4096, 65536):
+        _full_check(heap, _tuning(ac, tile))
+    # an overlap in the third step of a later workgroup's chunk (3,000,000
+    # entries: 2,930 steps over 977 workgroups of 3 steps, 3,072 entries)
+    bad_at = 490 * 3072 + 2 * 1024 + 77
+    o = heap.offset.copy()
+    o[bad_at] = o[bad_at - 1]
+    dev_o, dev_s, dev_l = u64_to_t(o, "cuda"), u64_to_t(size, "cuda"), torch.from_numpy(live).cuda()
+    want = oracle.validate(o, size, live, S)
+    assert want[0] == oracle.EINVAL
+    ws = ac.workspace(n, S)
+    with pytest.raises(ac.DefragError) as ei:
+        ac.defrag_stats(dev_o, dev_s, dev_l, S, ws)
+    assert (ei.value.code, ei.value.invalid_index, ei.value.invalid_reason) == \
+        (ac.DEFRAG_EINVAL, want[1], want[2])

@@ -13,8 +13,9 @@ import torch
 import oracle
 import workloads as W
 import test_oracle_targeted as TT
-from harness import (check_arena_full, check_arena_sampled, check_tables_and_handles,
-                     device_pinned, device_table, log, pristine_host, run_gpu, sample_windows)
+from harness import (check_arena_every_byte, check_arena_full, check_arena_sampled,
+                     check_tables_and_handles, device_pinned, device_table, log, oracle_arena,
+                     pristine_host, run_gpu, sample_windows)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,11 +52,15 @@ def _check(heap, request, tile=0, full=True, rng=None):
     if full:
         check_arena_full(heap, r, host, hold=hold)
     else:
-        wins = sample_windows(heap, rng, n_random=512, hold=hold)
+        # a full-size heap: windows at the targeted range's edges first, then
+        # every byte against the oracle's arena built on the host
+        wins = sample_windows(heap, rng, n_random=64, per_block_cap=256, hold=hold)
         top = w.end - w.hole
         for p in (w.begin, max(w.begin, top - 2048), top, max(top, w.end - 4096)):
             wins.append((p, min(4096, heap.arena_bytes - p)))
         check_arena_sampled(heap, r, wins, hold=hold)
+        check_arena_every_byte(r.arena, oracle_arena(heap, hold),
+                               f"{heap.name} request {request}")
     # the freed hole is there afterwards
     assert r.post_stats.largest_hole >= request
     return w
@@ -116,6 +121,7 @@ def test_small_workloads_targeted_gpu(ac, k):
             _check(heap, R)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("k", ["training-80g", "training-80g-pinned"])
 def test_page_request_full_size(ac, k):
     """The 910C page's 4.2 GB request (4.2/80 of the arena) on the 80 GiB
