@@ -33,6 +33,8 @@ DEFRAG_ETIMEOUT = -5
 DEFRAG_ENOFIT = -6
 DEFRAG_ECAPACITY = -7
 DEFRAG_ECORRUPT = -8
+DEFRAG_ETOOBIG = -9
+STATIC_SCRATCH_BYTES = 128 << 20   # DEFRAG_STATIC_SCRATCH_BYTES
 REASONS = {0: "none", 1: "zero_size", 2: "misaligned", 3: "live_flag",
            4: "out_of_arena", 5: "overlap", 6: "argument", 7: "pinned_flag"}
 U64_MAX = (1 << 64) - 1
@@ -162,12 +164,15 @@ def _load() -> ctypes.CDLL:
     L.defrag_commit.argtypes = [ctypes.POINTER(defrag_plan_t), P, S, P, P, P, P, P]
     L.defrag_compact.argtypes = [ctypes.POINTER(defrag_compact_args), P,
                                  ctypes.POINTER(defrag_plan_t), ctypes.POINTER(defrag_stats_t)]
+    L.defrag_compact_static.argtypes = [ctypes.POINTER(defrag_compact_args), P,
+                                        ctypes.POINTER(defrag_plan_t),
+                                        ctypes.POINTER(defrag_stats_t)]
     L.defrag_monitor.argtypes = [ctypes.POINTER(defrag_stats_t), ctypes.POINTER(defrag_monitor_cfg),
                                  ctypes.POINTER(defrag_monitor_report)]
     L.defrag_strerror.argtypes = [ctypes.c_int]
     L.defrag_strerror.restype = ctypes.c_char_p
     for f in ("defrag_stats", "defrag_first_fit", "defrag_plan", "defrag_plan_targeted",
-              "defrag_move", "defrag_monitor", "defrag_compact",
+              "defrag_move", "defrag_monitor", "defrag_compact", "defrag_compact_static",
               "defrag_move_status", "defrag_move_report", "defrag_plan_tiles",
               "defrag_remap", "defrag_commit"):
         getattr(L, f).restype = ctypes.c_int
@@ -181,7 +186,7 @@ EXPORTS = ("defrag_workspace_bytes", "defrag_stats", "defrag_first_fit", "defrag
            "defrag_move",
            "defrag_move_status", "defrag_move_report", "defrag_plan_tiles", "defrag_remap",
            "defrag_commit",
-           "defrag_compact", "defrag_monitor",
+           "defrag_compact", "defrag_compact_static", "defrag_monitor",
            "defrag_strerror")
 
 
@@ -365,23 +370,12 @@ def defrag_commit(plan: defrag_plan_t, ws: torch.Tensor, offset_out=None, size_o
         raise DefragError(rc, "defrag_commit")
 
 
-def defrag_compact(offset, size, live, arena_bytes: int, arena: torch.Tensor, ws: torch.Tensor,
-                   request_bytes: int = 0, new_offset: Optional[torch.Tensor] = None,
-                   handles: Optional[torch.Tensor] = None, h_out: Optional[torch.Tensor] = None,
-                   n_invalid: Optional[torch.Tensor] = None, offset_out=None, size_out=None,
-                   live_out=None, pinned_out=None, tuning: Optional[defrag_tuning] = None,
-                   stream=None, pinned=None, after: Optional[bool] = None, side_stream=None):
-    """Plan, move, remap, commit and the post-check in one C-ABI call.
-    after (default: whenever offset_out and size_out are given) asks for the
-    post-move statistics.  Returns (plan, post-move stats or None).
-    offset_out, size_out, live_out and pinned_out need one element per live
-    block, which is known only once the plan has run: neither this function
-    nor the library can check their length.  side_stream: a torch stream
-    of the caller's for the work that overlaps the move (default: the
-    library's own)."""
+def _compact_args(offset, size, live, arena_bytes, arena, ws, request_bytes, new_offset, handles,
+                  h_out, n_invalid, offset_out, size_out, live_out, pinned_out, tuning, pinned,
+                  side_stream):
+    """The defrag_compact_args of a call, its argument checks, and the
+    buffers it points at (kept alive with it)."""
     _need(arena, torch.uint8, 0, "arena")
-    if after is None:
-        after = offset_out is not None and size_out is not None
     _need(new_offset, torch.int64, offset.numel(), "new_offset")
     H = 0 if handles is None else handles.numel()
     if handles is not None:
@@ -396,7 +390,8 @@ def defrag_compact(offset, size, live, arena_bytes: int, arena: torch.Tensor, ws
     t = make_table(offset, size, live, pinned)
     a = defrag_compact_args(
         ctypes.pointer(t), arena_bytes, _ptr(arena) if arena.numel() else None, request_bytes,
-        ctypes.pointer(tuning) if tuning is not None else None, _ptr(ws), ws.numel(),
+        ctypes.pointer(tuning) if tuning is not None else None,
+        _ptr(ws) if ws is not None else None, ws.numel() if ws is not None else 0,
         _ptr(new_offset) if new_offset is not None and new_offset.numel() else None,
         _ptr(handles) if H else None, _ptr(h_out) if H else None, H, _ptr(n_invalid),
         _ptr(offset_out) if offset_out is not None and offset_out.numel() else None,
@@ -404,12 +399,61 @@ def defrag_compact(offset, size, live, arena_bytes: int, arena: torch.Tensor, ws
         _ptr(live_out) if live_out is not None and live_out.numel() else None,
         _ptr(pinned_out) if pinned_out is not None and pinned_out.numel() else None,
         ctypes.c_void_p(side_stream.cuda_stream) if side_stream is not None else None)
+    return a, (t, h_out)
+
+
+def defrag_compact(offset, size, live, arena_bytes: int, arena: torch.Tensor, ws: torch.Tensor,
+                   request_bytes: int = 0, new_offset: Optional[torch.Tensor] = None,
+                   handles: Optional[torch.Tensor] = None, h_out: Optional[torch.Tensor] = None,
+                   n_invalid: Optional[torch.Tensor] = None, offset_out=None, size_out=None,
+                   live_out=None, pinned_out=None, tuning: Optional[defrag_tuning] = None,
+                   stream=None, pinned=None, after: Optional[bool] = None, side_stream=None):
+    """Plan, move, remap, commit and the post-check in one C-ABI call.
+    after (default: whenever offset_out and size_out are given) asks for the
+    post-move statistics.  Returns (plan, post-move stats or None).
+    offset_out, size_out, live_out and pinned_out need one element per live
+    block, which is known only once the plan has run: neither this function
+    nor the library can check their length.  side_stream: a torch stream
+    of the caller's for the work that overlaps the move (default: the
+    library's own)."""
+    if after is None:
+        after = offset_out is not None and size_out is not None
+    a, keep = _compact_args(offset, size, live, arena_bytes, arena, ws, request_bytes, new_offset,
+                            handles, h_out, n_invalid, offset_out, size_out, live_out, pinned_out,
+                            tuning, pinned, side_stream)
     plan = defrag_plan_t()
     post = defrag_stats_t() if after else None
     rc = lib.defrag_compact(ctypes.byref(a), _stream(stream), ctypes.byref(plan),
                             ctypes.byref(post) if after else None)
     if rc != DEFRAG_OK:
         raise DefragError(rc, "defrag_compact", plan.stats if rc == DEFRAG_EINVAL else None)
+    return plan, post
+
+
+def defrag_compact_static(offset, size, live, arena_bytes: int, arena: torch.Tensor,
+                          request_bytes: int = 0, new_offset: Optional[torch.Tensor] = None,
+                          handles: Optional[torch.Tensor] = None,
+                          h_out: Optional[torch.Tensor] = None,
+                          n_invalid: Optional[torch.Tensor] = None, offset_out=None,
+                          size_out=None, live_out=None, pinned_out=None,
+                          tuning: Optional[defrag_tuning] = None, stream=None, pinned=None,
+                          after: Optional[bool] = None):
+    """defrag_compact with the library's static scratch as its workspace:
+    the library allocates nothing and creates no stream or event for it
+    (every step runs on `stream`).  Returns (plan, post-move stats or None);
+    DEFRAG_ETOOBIG when the table needs more than the scratch holds."""
+    if after is None:
+        after = offset_out is not None and size_out is not None
+    a, keep = _compact_args(offset, size, live, arena_bytes, arena, None, request_bytes,
+                            new_offset, handles, h_out, n_invalid, offset_out, size_out, live_out,
+                            pinned_out, tuning, pinned, None)
+    plan = defrag_plan_t()
+    post = defrag_stats_t() if after else None
+    rc = lib.defrag_compact_static(ctypes.byref(a), _stream(stream), ctypes.byref(plan),
+                                   ctypes.byref(post) if after else None)
+    if rc != DEFRAG_OK:
+        raise DefragError(rc, "defrag_compact_static",
+                          plan.stats if rc == DEFRAG_EINVAL else None)
     return plan, post
 
 

@@ -686,6 +686,7 @@ const char *defrag_strerror(int code) {
         case DEFRAG_ETIMEOUT: return "mover wait timed out";
         case DEFRAG_ENOFIT: return "no hole holds the request (and, for a targeted plan, no window can free it)";
         case DEFRAG_ECAPACITY: return "a mover tile met more blocks than its launch holds";
+        case DEFRAG_ETOOBIG: return "the table needs more workspace than the library's static scratch holds";
         case DEFRAG_ECORRUPT: return "the workspace no longer holds a consistent plan (tiles outside it were not moved)";
         default: return "unknown error";
     }

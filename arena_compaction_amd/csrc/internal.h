@@ -7,6 +7,9 @@
 
 #include <hip/hip_runtime.h>
 
+// Nothing declared here is part of the library's interface.
+#pragma GCC visibility push(hidden)
+
 namespace ac {
 
 constexpr uint32_t kScanThreads = 256;          // threads per scan workgroup
@@ -407,3 +410,5 @@ hipError_t launch_remap(const void *rec, const uint64_t *live_src, const uint32_
                         uint64_t *n_invalid, int num_cus, hipStream_t s);
 
 }  // namespace ac
+
+#pragma GCC visibility pop

@@ -88,6 +88,9 @@ extern "C" {
                                   whose bytes or blocks fall outside the arena
                                   or the plan's arrays were not moved; the
                                   arena is then undefined                     */
+#define DEFRAG_ETOOBIG (-9)    /* defrag_compact_static: the table needs more
+                                  workspace than the library's static scratch
+                                  (DEFRAG_STATIC_SCRATCH_BYTES) holds          */
 
 /* Why a table was rejected: the first failing entry, and within it the first
  * failing check in the order zero size, misaligned, live flag, pinned flag,
@@ -399,6 +402,26 @@ typedef struct defrag_compact_args {
 
 int defrag_compact(const defrag_compact_args *args, hipStream_t stream,
                    defrag_plan_t *plan_host, defrag_stats_t *after_host);
+
+/* defrag_compact for callers that cannot allocate device memory or create
+ * streams and events: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The workspace is a device array the
+ * library holds itself, DEFRAG_STATIC_SCRATCH_BYTES per GPU, from its load
+ * to the end of the process; args->ws_dev, ws_bytes and side_stream must be
+ * 0 (else DEFRAG_EINVAL).  The steps run in defrag_compact's plain order on
+ * `stream` alone (plan, read back, move, remap, commit, post-check, one
+ * read at the end); the call calls no allocating routine and creates
+ * nothing.  A table that needs more workspace than the scratch holds --
+ * when defrag_workspace_bytes for it exceeds DEFRAG_STATIC_SCRATCH_BYTES,
+ * it may -- returns DEFRAG_ETOOBIG before anything moves.  Every call on a
+ * GPU uses that GPU's one array: calls that overlap on a GPU (from two
+ * threads, or on two streams) race; serialise them.  The filled plan_host
+ * describes the compaction but cannot be passed to calls that take a
+ * workspace.  Otherwise as defrag_compact (same results, same errors). */
+#define DEFRAG_STATIC_SCRATCH_BYTES (128ull << 20)
+
+int defrag_compact_static(const defrag_compact_args *args, hipStream_t stream,
+                          defrag_plan_t *plan_host, defrag_stats_t *after_host);
 
 /* Layout monitor: host arithmetic on a defrag_stats result, no HIP call.
  * CANN page, section 5.3 (MemoryMonitor): usage = live / arena is rated OK,

@@ -23,7 +23,8 @@ def test_header_declares_the_boundary():
     for f in ("defrag_stats", "defrag_first_fit", "defrag_plan", "defrag_plan_targeted",
               "defrag_compact", "defrag_move", "defrag_remap",
               "defrag_workspace_bytes", "defrag_strerror", "defrag_commit",
-              "defrag_move_status", "defrag_move_report", "defrag_plan_tiles"):
+              "defrag_move_status", "defrag_move_report", "defrag_plan_tiles",
+              "defrag_compact_static"):
         assert f in fns, f
 
 
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 def test_strerror_and_codes():
     import arena_compaction_amd as ac
     assert ac.defrag_strerror(0) == "ok"
-    for c in (-1, -2, -3, -4, -5, -6, -7, -8):
+    for c in (-1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert ac.defrag_strerror(c) not in ("ok", "unknown error")
     assert ac.defrag_strerror(-99) == "unknown error"
 
@@ -201,7 +202,9 @@ def test_build_is_quiet_and_device_code_has_no_packed_fp32():
                            stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
         assert p.returncode == 0, p.stderr[-2000:]
         asm = p.stdout
-        assert "gfx950" in asm and ".amdhsa_kernel" in asm, src
+        assert "gfx950" in asm, src
+        if "__global__" in open(os.path.join(csrc, src)).read():
+            assert ".amdhsa_kernel" in asm, src
         for op in ("v_pk_fma_f32", "v_pk_mul_f32", "v_pk_add_f32"):
             assert op not in asm, f"{src}: {op} in the device code"
     sys.stdout.flush()
@@ -239,3 +242,34 @@ def test_binding_structs_match_the_header():
         assert int(got[name]) == ctypes.sizeof(cls), name
         for f, _ in cls._fields_:
             assert int(got[f"{name}.{f}"]) == getattr(cls, f).offset, f"{name}.{f}"
+
+
+def test_static_entry_point_refusals_need_no_gpu():
+    """defrag_compact_static refuses, before any HIP call, a workspace or
+    side stream (its scratch and the caller's stream stand in for them) and
+    a table whose plan arrays alone exceed the static scratch."""
+    import arena_compaction_amd as ac
+    L = ac.lib
+    plan = ac.defrag_plan_t()
+    t = ac.defrag_table(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), None, 16)
+    args = ac.defrag_compact_args()
+    args.table = ctypes.pointer(t)
+    args.arena_bytes = 4096
+    args.ws_dev = ctypes.c_void_p(0x3000)
+    args.ws_bytes = 1 << 20
+    assert L.defrag_compact_static(ctypes.byref(args), None, ctypes.byref(plan), None) == \
+        ac.DEFRAG_EINVAL
+    assert plan.stats.invalid_reason == 6
+    args.ws_dev, args.ws_bytes = None, 0
+    args.side_stream = ctypes.c_void_p(0x4000)
+    assert L.defrag_compact_static(ctypes.byref(args), None, ctypes.byref(plan), None) == \
+        ac.DEFRAG_EINVAL
+    args.side_stream = None
+    t.n = 50_000_000   # ~3 GB of plan arrays
+    assert L.defrag_compact_static(ctypes.byref(args), None, ctypes.byref(plan), None) == \
+        ac.DEFRAG_ETOOBIG
+    assert L.defrag_compact_static(ctypes.byref(args), None, None, None) == ac.DEFRAG_EINVAL
+    assert ac.defrag_strerror(ac.DEFRAG_ETOOBIG) not in ("ok", "unknown error")
+    # the limit the header states: every workload here fits at full size
+    assert ac.STATIC_SCRATCH_BYTES == 128 << 20
+    assert ac.defrag_workspace_bytes(2_000_000, 4 << 30) <= ac.STATIC_SCRATCH_BYTES
