@@ -114,7 +114,7 @@ int move_outcome(const WsHeader &h, uint64_t epoch) {
 }
 
 int check_tuning(const defrag_tuning &tu) {
-    if (!tile_ok(tu.tile_bytes) || tu.spin_limit_log2 > 40 || tu.nontemporal > 3 ||
+    if ((tu.tile_bytes && !tile_ok(tu.tile_bytes)) || tu.spin_limit_log2 > 40 || tu.nontemporal > 3 ||
         tu.stall_sleeps > kMaxStallSleeps)
         return DEFRAG_EINVAL;
     return DEFRAG_OK;
@@ -163,7 +163,7 @@ int stats_pass(const defrag_table *table, uint64_t arena_bytes, uint64_t fit_nee
     // the statistics header (the second 256 bytes): a plan the workspace
     // holds keeps its own header
     L.header = L.post;
-    if (launch_scan(view_of(table), arena_bytes, ws, L, nullptr, 0, kDefaultTile, 0, fit_need,
+    if (launch_scan(view_of(table), arena_bytes, ws, L, nullptr, 0, TileChoice{kDefaultTile, kDefaultTile}, 0, fit_need,
                     stream) != hipSuccess)
         return DEFRAG_EHIP;
     rc = read_header(h, ws, L, stream);
@@ -185,7 +185,8 @@ int post_check_queue(const defrag_table *packed, uint64_t arena_bytes, void *ws_
     if (rc) return rc;
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
     L.header = L.post;
-    return launch_scan(view_of(packed), arena_bytes, ws, L, nullptr, 0, kDefaultTile, 0, kNone,
+    return launch_scan(view_of(packed), arena_bytes, ws, L, nullptr, 0,
+                       TileChoice{kDefaultTile, kDefaultTile}, 0, kNone,
                        stream) == hipSuccess
                ? DEFRAG_OK
                : DEFRAG_EHIP;
@@ -226,7 +227,8 @@ namespace {
 // A plan in flight: what its queued passes were given, for reading it back.
 struct PlanCtx {
     WsLayout L;
-    defrag_tuning tu;
+    defrag_tuning tu;   // tile_bytes 0: chosen by the plan from `tiles`
+    TileChoice tiles;
     bool tuned;  // the caller gave a tuning (else the plan picks workgroups)
     uint64_t epoch;
     int dev;
@@ -243,7 +245,6 @@ int plan_queue(const defrag_table *table, uint64_t arena_bytes, uint64_t request
     tu.wg_per_cu = kDefaultWgPerCu;
     tu.nontemporal = kDefaultNontemporal;
     if (tuning) tu = *tuning;
-    if (!tu.tile_bytes) tu.tile_bytes = kDefaultTile;
     if (!tu.spin_limit_log2) tu.spin_limit_log2 = kDefaultSpinLog2;
     if (check_tuning(tu)) {
         arg_error(&plan->stats);
@@ -264,14 +265,16 @@ int plan_queue(const defrag_table *table, uint64_t arena_bytes, uint64_t request
     c->dev = current_device();
     if (c->dev < 0) return DEFRAG_EHIP;
     c->tu = tu;
+    c->tiles = tu.tile_bytes ? TileChoice{tu.tile_bytes, tu.tile_bytes}
+                             : TileChoice{kAutoTileSmall, kAutoTileLarge};
     c->tuned = tuning != nullptr;
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
     c->epoch = g_epoch.fetch_add(0x9E3779B97F4A7C15ull) ^ reinterpret_cast<uintptr_t>(ws);
     const hipError_t e =
         request ? launch_targeted(view_of(table), arena_bytes, request, ws, c->L, new_offset_dev,
-                                  tu.tile_bytes, c->epoch, stream)
+                                  c->tiles, c->epoch, stream)
                 : launch_scan(view_of(table), arena_bytes, ws, c->L, new_offset_dev, kOutNew,
-                              tu.tile_bytes, c->epoch, kNone, stream);
+                              c->tiles, c->epoch, kNone, stream);
     return e == hipSuccess ? DEFRAG_OK : DEFRAG_EHIP;
 }
 
@@ -283,7 +286,10 @@ int plan_fill(const defrag_table *table, uint64_t arena_bytes, uint64_t request,
     if (request && h.win_state != kWinFound) return DEFRAG_ENOFIT;  // nothing written
     if (h.n_tiles > c.L.max_tiles) return DEFRAG_EWORKSPACE;  // new offsets were written
 
+    // the tile size the plan chose (one of the candidates)
+    if (h.tile_bytes != c.tiles.a && h.tile_bytes != c.tiles.b) return DEFRAG_EHIP;
     defrag_tuning tu = c.tu;
+    tu.tile_bytes = (uint32_t)h.tile_bytes;
     const uint64_t T = tu.tile_bytes;
     plan->epoch = c.epoch;
     plan->workspace = ws_dev;
@@ -608,8 +614,8 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     m.hdr = reinterpret_cast<WsHeader *>(ws + c.L.header);
     m.epoch = c.epoch;
     m.spin_limit = 1ull << c.tu.spin_limit_log2;
-    m.tile_bytes = c.tu.tile_bytes;
-    m.max_blocks = c.tu.tile_bytes / 32 + 2;  // the most blocks a tile can meet
+    m.tile_bytes = c.tiles.a;
+    m.max_blocks = c.tiles.a / 32 + 2;  // the most blocks a tile can meet
     m.small_blocks = move_small_blocks(a->arena_bytes, a->table->n) ? 1u : 0u;
     m.device_sized = 1;
     m.wg_per_cu = c.tuned ? c.tu.wg_per_cu : 0;
@@ -620,10 +626,16 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     m.stall_every = c.tu.stall_every;
     m.stall_sleeps = c.tu.stall_sleeps;
     m.stall_seed = c.tu.stall_seed;
+    // with the tile size left to the plan, a mover for each candidate: the
+    // one whose size the plan did not choose leaves at once
+    MoveArgs mb = m;
+    mb.tile_bytes = c.tiles.b;
+    mb.max_blocks = c.tiles.b / 32 + 2;
     WsHeader hp;
     const bool queued =
         hipEventRecord(planned, stream) == hipSuccess &&
         launch_move_device_sized(m, c.tu.nontemporal, stream) == hipSuccess &&
+        (c.tiles.a == c.tiles.b || launch_move_device_sized(mb, c.tu.nontemporal, stream) == hipSuccess) &&
         hipStreamWaitEvent(side, planned, 0) == hipSuccess;
     rc = queued ? read_header(&hp, ws, c.L, side) : DEFRAG_EHIP;
     const hipError_t destroyed = hipEventDestroy(planned);

@@ -36,6 +36,23 @@ inline bool move_small_blocks(uint64_t arena_bytes, uint64_t n) {
     return n && arena_bytes / n < kSmallBlockBytes;
 }
 constexpr uint32_t kDefaultTile = 65536;
+// With no tile size given, the plan picks one on the device from the shifts
+// it finds: 64 KiB tiles, or 128 KiB when most moved bytes shift by less
+// than kAutoSmallShift and at least kAutoMinMoved bytes move.  A tile whose
+// sources the tile it depends on has not yet read waits about a fixed time,
+// and with shifts that short (within the window of tiles in flight at once,
+// ~16 MiB of 64 KiB tiles on 256 compute units) most do; larger tiles
+// amortise the wait (an 8 GiB block shifted by 4 KiB-4 MiB: 67% of the HBM
+// peak with 64 KiB tiles, 77% with 128 KiB; the two cross near 11 MiB).
+constexpr uint32_t kAutoTileSmall = 65536;
+constexpr uint32_t kAutoTileLarge = 131072;
+constexpr uint64_t kAutoSmallShift = 8ull << 20;
+constexpr uint64_t kAutoMinMoved = 64ull << 20;  // below it, more (smaller) tiles keep all CUs busy
+
+// The tile sizes a plan counts tiles for: a == b for a size the caller gave.
+struct TileChoice {
+    uint32_t a, b;
+};
 // Mover workgroups per compute unit when the caller gives no tuning: one,
 // which keeps one narrow window of tiles in flight (two 512-lane workgroups
 // per CU: 80.5% on the 80 GiB workload).
@@ -82,7 +99,9 @@ struct alignas(256) WsHeader {
     uint64_t late_tiles;
     uint64_t waited_tiles;
     uint64_t polls;
-    uint64_t pad[8];
+    uint64_t tile_bytes;     // the plan's tile size (chosen on the device when auto)
+    uint64_t small_moved;    // moved bytes whose shift is below kAutoSmallShift
+    uint64_t pad[6];
 };
 static_assert(sizeof(WsHeader) == 256, "header size");
 
@@ -142,7 +161,7 @@ struct StatPart {
     uint64_t min_moved_dst;
     uint64_t min_size;
     uint64_t min_fit;   // lowest start of a hole below a live block holding fit_need
-    uint64_t pad;
+    uint64_t small_moved;  // moved bytes whose shift is below kAutoSmallShift
 };
 
 // One mover tile: the destination bytes [t0, t1) -- a piece of one run of
@@ -257,8 +276,8 @@ inline WsLayout ws_fixed(uint64_t n) {
     L.prefix = at;    at += align256(nb * sizeof(ScanPart));
     L.spart = at;     at += align256(nb * sizeof(StatPart));
     // -- everything below here is a plan's: statistics passes stop above --
-    L.tpart = at;     at += align256(nb * sizeof(uint64_t));
-    L.twhole = at;    at += align256(nb * sizeof(uint64_t));
+    L.tpart = at;     at += align256(2 * nb * sizeof(uint64_t));   // per tile-size candidate
+    L.twhole = at;    at += align256(2 * nb * sizeof(uint64_t));
     L.tprefix = at;   at += align256(nb * sizeof(uint64_t));
     L.live_dst = at;  at += align256((n + 1) * sizeof(uint64_t));
     L.live_src = at;  at += align256((n + 1) * sizeof(uint64_t));
@@ -346,13 +365,13 @@ inline LiveView live_view(const uint8_t *ws, const WsLayout &L) {
 // fit_need: a hole size to first-fit (header fit_offset), kNone for none.
 hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws,
                        const WsLayout &L, uint64_t *new_offset, int outputs,
-                       uint32_t tile_bytes, uint64_t epoch, uint64_t fit_need, hipStream_t s);
+                       TileChoice tiles, uint64_t epoch, uint64_t fit_need, hipStream_t s);
 // Targeted plan: a selection scan, the window search (header win_*), then
 // the plan scan with every live block outside the window held in place.
 // Nothing is planned (and new_offset is not written) when no window fits.
 hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t request,
                            uint8_t *ws, const WsLayout &L, uint64_t *new_offset,
-                           uint32_t tile_bytes, uint64_t epoch, hipStream_t s);
+                           TileChoice tiles, uint64_t epoch, hipStream_t s);
 hipError_t launch_commit(const uint8_t *ws, const WsLayout &L, uint64_t live_blocks,
                          uint64_t *off_out, uint64_t *size_out, uint8_t *live_out,
                          uint8_t *pinned_out, hipStream_t s);

@@ -125,13 +125,14 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
             if (a.device_sized) {
                 // the plan's results, read here instead of on the host: a
                 // failed plan (invalid table, no window, too many tiles)
-                // moves nothing; workgroups past the chosen count leave
+                // moves nothing, nor does the mover of a tile size the plan
+                // did not choose; workgroups past the chosen count leave
                 const WsHeader *h = a.hdr;
                 nt = h->n_tiles;
                 m = h->live_blocks < m ? h->live_blocks : m;  // a.live_blocks: the arrays' room
                 const uint32_t per_cu = a.wg_per_cu ? a.wg_per_cu : kDefaultWgPerCu;
                 go = h->bad_key == kNone && h->win_state != kWinNoFit && nt <= a.max_tiles &&
-                     blockIdx.x < (uint64_t)per_cu * a.num_cus;
+                     h->tile_bytes == a.tile_bytes && blockIdx.x < (uint64_t)per_cu * a.num_cus;
             }
             if (go && a.arena_bytes >= 32u) tk = atomicAdd(&a.hdr->ticket, 1u);
         }

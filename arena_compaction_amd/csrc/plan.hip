@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
     const uint64_t end = umin64(base + chunk, t.n);
     Agg carry = prefix[blockIdx.x].a;  // everything before this workgroup's chunk
     uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, min_dst = kNone, min_size = kNone;
-    uint64_t min_fit = kNone;
+    uint64_t min_fit = kNone, small_moved = 0;
     for (uint64_t s0 = base; s0 < end; s0 += kScanTile) {
         const uint64_t i0 = s0 + (uint64_t)threadIdx.x * kScanItems;
         uint64_t o[kScanItems], s[kScanItems];
@@ -357,6 +357,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
                         moved += 1;
                         moved_bytes += s[k];
                         min_dst = umin64(min_dst, nw);
+                        if (o[k] - nw < kAutoSmallShift) small_moved += s[k];
                     }
                     min_size = umin64(min_size, s[k]);
                 }
@@ -371,9 +372,10 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
     min_dst = block_reduce<kScanThreads>(min_dst, shr, OpMin());
     min_size = block_reduce<kScanThreads>(min_size, shr, OpMin());
     min_fit = block_reduce<kScanThreads>(min_fit, shr, OpMin());
+    small_moved = block_reduce<kScanThreads>(small_moved, shr, OpAdd());
     if (threadIdx.x == 0)
         spart[blockIdx.x] =
-            StatPart{max_gap, gaps, moved, moved_bytes, min_dst, min_size, min_fit, 0};
+            StatPart{max_gap, gaps, moved, moved_bytes, min_dst, min_size, min_fit, small_moved};
 }
 
 // Pass 4 (one workgroup): reduce the statistics, add the tail hole.  A plan
@@ -384,9 +386,10 @@ __device__ void scan_finish(const StatPart *spart, uint64_t nb, uint64_t arena_b
     __shared__ uint64_t sh[kSpineThreads / 64];
     if (plan_dead(hdr)) return;
     uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, min_dst = kNone, min_size = kNone;
-    uint64_t min_fit = kNone;
+    uint64_t min_fit = kNone, small_moved = 0;
     for (uint64_t j = threadIdx.x; j < nb; j += kSpineThreads) {
         const StatPart q = spart[j];
+        small_moved += q.small_moved;
         min_fit = umin64(min_fit, q.min_fit);
         max_gap = umax64(max_gap, q.max_gap);
         gaps += q.gaps;
@@ -402,6 +405,7 @@ __device__ void scan_finish(const StatPart *spart, uint64_t nb, uint64_t arena_b
     min_dst = block_reduce<kSpineThreads>(min_dst, sh, OpMin());
     min_size = block_reduce<kSpineThreads>(min_size, sh, OpMin());
     min_fit = block_reduce<kSpineThreads>(min_fit, sh, OpMin());
+    small_moved = block_reduce<kSpineThreads>(small_moved, sh, OpAdd());
     if (threadIdx.x == 0) {
         const uint64_t tail = arena_bytes - hdr->max_live_end;
         // holes below live blocks come first in address order; the tail last
@@ -411,6 +415,7 @@ __device__ void scan_finish(const StatPart *spart, uint64_t nb, uint64_t arena_b
         hdr->hole_count = gaps + (tail ? 1 : 0);
         hdr->moved_blocks = moved;
         hdr->moved_bytes = moved_bytes;
+        hdr->small_moved = small_moved;
         hdr->min_live_size = min_size;
         hdr->move_begin = min_dst;
         // plan fields: a statistics-only pass leaves an existing plan intact
@@ -459,29 +464,36 @@ __device__ inline uint64_t whole_in_block(const LiveView &lv, uint64_t k, uint64
 }
 
 // Pass 5: per-workgroup tile counts (and whole-window counts) over the live
-// blocks; workgroup blk covers live blocks [blk * chunk, (blk + 1) * chunk).
-__device__ void tcount_partial(LiveView lv, const WsHeader *hdr, uint64_t T, uint64_t *tpart,
+// blocks, for both tile-size candidates (tpart[blk], tpart[kMaxScanParts +
+// blk]); workgroup blk covers live blocks [blk * chunk, (blk + 1) * chunk).
+__device__ void tcount_partial(LiveView lv, const WsHeader *hdr, TileChoice tc, uint64_t *tpart,
                                uint64_t *twhole, uint64_t blk, uint64_t chunk) {
     __shared__ uint64_t sh[kScanThreads / 64];
     if (plan_dead(hdr)) return;
     const uint64_t m = hdr->live_blocks;
     const uint64_t end = umin64((blk + 1) * chunk, m);
-    uint64_t c = 0, w = 0;
+    uint64_t ca = 0, wa = 0, cb = 0, wb = 0;
     for (uint64_t k0 = blk * chunk + (uint64_t)threadIdx.x * kScanItems; k0 < end;
          k0 += kScanTile) {
 #pragma unroll
         for (uint32_t j = 0; j < kScanItems; ++j) {
             if (k0 + j < end) {
-                c += tiles_in_block(lv, k0 + j, T);
-                w += whole_in_block(lv, k0 + j, T);
+                ca += tiles_in_block(lv, k0 + j, tc.a);
+                wa += whole_in_block(lv, k0 + j, tc.a);
+                cb += tiles_in_block(lv, k0 + j, tc.b);
+                wb += whole_in_block(lv, k0 + j, tc.b);
             }
         }
     }
-    c = block_reduce<kScanThreads>(c, sh, OpAdd());
-    w = block_reduce<kScanThreads>(w, sh, OpAdd());
+    ca = block_reduce<kScanThreads>(ca, sh, OpAdd());
+    wa = block_reduce<kScanThreads>(wa, sh, OpAdd());
+    cb = block_reduce<kScanThreads>(cb, sh, OpAdd());
+    wb = block_reduce<kScanThreads>(wb, sh, OpAdd());
     if (threadIdx.x == 0) {
-        tpart[blk] = c;
-        twhole[blk] = w;
+        tpart[blk] = ca;
+        twhole[blk] = wa;
+        tpart[kMaxScanParts + blk] = cb;
+        twhole[kMaxScanParts + blk] = wb;
     }
 }
 
@@ -514,7 +526,7 @@ __device__ void remap_index_part(const uint64_t *__restrict__ live_src, const Ws
 // remap index, and the last one reduces the statistics (pass 4).
 struct AfterScan {
     LiveView lv;
-    uint64_t tile_bytes;
+    TileChoice tiles;
     uint64_t *tpart, *twhole;
     uint64_t gnb;
     uint64_t chunk;     // live blocks per counting workgroup
@@ -533,7 +545,7 @@ static_assert(kSpineThreads == kScanThreads, "the finish runs as one workgroup o
 __global__ __launch_bounds__(kScanThreads) void k_after_scan(AfterScan a, WsHeader *hdr) {
     const uint64_t blk = blockIdx.x;
     if (blk < a.gnb) {
-        tcount_partial(a.lv, hdr, a.tile_bytes, a.tpart, a.twhole, blk, a.chunk);
+        tcount_partial(a.lv, hdr, a.tiles, a.tpart, a.twhole, blk, a.chunk);
     } else if (blk < a.gnb + a.rblocks) {
         remap_index_part(a.lv.src, hdr, a.rw, a.rnb, a.ridx, blk - a.gnb);
     } else {
@@ -541,19 +553,35 @@ __global__ __launch_bounds__(kScanThreads) void k_after_scan(AfterScan a, WsHead
     }
 }
 
-// Pass 6 (one workgroup): exclusive scan of the counts; n_tiles.
+// Pass 6 (one workgroup): the tile size, then the exclusive scan of its
+// counts; n_tiles.  With two candidates the larger is taken when most moved
+// bytes shift by less than kAutoSmallShift and enough bytes move -- or when
+// the smaller's tiles would not fit the workspace and the larger's do.
 __global__ __launch_bounds__(kSpineThreads) void k_tcount_spine(const uint64_t *tpart,
                                                                 const uint64_t *twhole,
                                                                 uint64_t *tprefix, uint64_t nb,
-                                                                WsHeader *hdr) {
+                                                                WsHeader *hdr, TileChoice tc,
+                                                                uint64_t max_tiles) {
     __shared__ uint64_t sh[kSpineThreads / 64];
     if (plan_dead(hdr)) return;
+    uint64_t na = 0, nbt = 0;
+    for (uint64_t j = threadIdx.x; j < nb; j += kSpineThreads) {
+        na += tpart[j];
+        nbt += tpart[kMaxScanParts + j];
+    }
+    na = block_reduce<kSpineThreads>(na, sh, OpAdd());
+    nbt = block_reduce<kSpineThreads>(nbt, sh, OpAdd());
+    const uint64_t moved = hdr->moved_bytes;
+    bool pick_b = tc.a != tc.b && hdr->small_moved * 2 > moved && moved >= kAutoMinMoved;
+    if (tc.a != tc.b && (pick_b ? nbt : na) > max_tiles && (pick_b ? na : nbt) <= max_tiles)
+        pick_b = !pick_b;
+    const uint64_t off = pick_b ? kMaxScanParts : 0;
     uint64_t carry = 0, whole = 0;
-    for (uint64_t j = threadIdx.x; j < nb; j += kSpineThreads) whole += twhole[j];
+    for (uint64_t j = threadIdx.x; j < nb; j += kSpineThreads) whole += twhole[off + j];
     whole = block_reduce<kSpineThreads>(whole, sh, OpAdd());
     for (uint64_t base = 0; base < nb; base += kSpineThreads) {
         const uint64_t j = base + threadIdx.x;
-        const uint64_t x = j < nb ? tpart[j] : 0;
+        const uint64_t x = j < nb ? tpart[off + j] : 0;
         uint64_t total;
         const uint64_t ex = block_excl_sum<kSpineThreads>(x, total, sh);
         if (j < nb) tprefix[j] = carry + ex;
@@ -562,6 +590,7 @@ __global__ __launch_bounds__(kSpineThreads) void k_tcount_spine(const uint64_t *
     if (threadIdx.x == 0) {
         hdr->n_tiles = carry;
         hdr->whole_tiles = whole;
+        hdr->tile_bytes = pick_b ? tc.b : tc.a;
     }
 }
 
@@ -569,11 +598,12 @@ __global__ __launch_bounds__(kSpineThreads) void k_tcount_spine(const uint64_t *
 // same index as the next block that has one, so tile t belongs to the last
 // block whose first tile index is <= t).
 __global__ __launch_bounds__(kScanThreads) void k_tcount_down(LiveView lv, const WsHeader *hdr,
-                                                              uint64_t T, const uint64_t *tprefix,
+                                                              const uint64_t *tprefix,
                                                               uint32_t *tile_base, uint64_t chunk) {
     __shared__ uint64_t sh[kScanThreads / 64];
     if (plan_dead(hdr)) return;
     const uint64_t m = hdr->live_blocks;
+    const uint64_t T = hdr->tile_bytes;
     const uint64_t base = (uint64_t)blockIdx.x * chunk;
     const uint64_t end = umin64(base + chunk, m);
     uint64_t carry = tprefix[blockIdx.x];
@@ -612,11 +642,10 @@ __device__ inline int64_t last_le(const T *a, int64_t lo, int64_t hi, uint64_t x
 // Pass 8: one lane per tile writes its start and its first block.
 __global__ __launch_bounds__(256) void k_tile_starts(LiveView lv, const uint32_t *tile_base,
                                                      const WsHeader *hdr, uint64_t max_tiles,
-                                                     uint64_t T, uint64_t *tile_start,
-                                                     uint32_t *tile_first) {
+                                                     uint64_t *tile_start, uint32_t *tile_first) {
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (plan_dead(hdr) || hdr->n_tiles > max_tiles) return;  // plan fails
-    const uint64_t n_tiles = hdr->n_tiles, m = hdr->live_blocks;
+    const uint64_t n_tiles = hdr->n_tiles, m = hdr->live_blocks, T = hdr->tile_bytes;
     if (t >= n_tiles) return;
     const int64_t k = last_le(tile_base, 0, (int64_t)m, t);
     const uint64_t j = t - tile_base[k];
@@ -652,12 +681,12 @@ __device__ inline uint64_t tile_of(const LiveView &lv, const uint32_t *tile_base
 __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile_start,
                                                const uint32_t *tile_first,
                                                const uint32_t *tile_base, const WsHeader *hdr,
-                                               uint64_t max_tiles, uint64_t T,
+                                               uint64_t max_tiles,
                                                const uint32_t *ridx, uint32_t w, TileRec *tiles,
                                                uint32_t *flags) {
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (plan_dead(hdr) || hdr->n_tiles > max_tiles) return;  // plan fails
-    const uint64_t n_tiles = hdr->n_tiles, m = hdr->live_blocks;
+    const uint64_t n_tiles = hdr->n_tiles, m = hdr->live_blocks, T = hdr->tile_bytes;
     if (t >= n_tiles) return;
     const uint64_t t0 = tile_start[t];
     uint64_t bound = (t0 & ~(T - 1)) + T;
@@ -863,7 +892,7 @@ namespace {
 // Scan passes, then (kOutNew) the tile passes.  win: the targeted plan's
 // window in the header, or null.
 hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsLayout &L,
-                uint64_t *new_offset, int outputs, const uint64_t *win, uint32_t tile_bytes,
+                uint64_t *new_offset, int outputs, const uint64_t *win, TileChoice tiles,
                 uint64_t epoch, uint64_t fit_need, hipStream_t s) {
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.header);
     ScanPart *part = reinterpret_cast<ScanPart *>(ws + L.part);
@@ -920,7 +949,7 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
         uint32_t *ridx = reinterpret_cast<uint32_t *>(ws + L.ridx);
         AfterScan as{};
         as.lv = lv;
-        as.tile_bytes = tile_bytes;
+        as.tiles = tiles;
         as.tpart = tpart;
         as.twhole = twhole;
         as.gnb = gnb;
@@ -938,26 +967,26 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
         hipLaunchKernelGGL(k_after_scan, dim3((uint32_t)(gnb + as.rblocks + 1)),
                            dim3(kScanThreads), 0, s, as, hdr);
         AC_TRY(hipGetLastError());
-        hipLaunchKernelGGL(k_tcount_spine, dim3(1), dim3(kSpineThreads), 0, s, tpart, twhole, tprefix, gnb,
-                           hdr);
+        hipLaunchKernelGGL(k_tcount_spine, dim3(1), dim3(kSpineThreads), 0, s, tpart, twhole,
+                           tprefix, gnb, hdr, tiles, (uint64_t)L.max_tiles);
         AC_TRY(hipGetLastError());
         hipLaunchKernelGGL(k_tcount_down, dim3((uint32_t)gnb), dim3(kScanThreads), 0, s, lv, hdr,
-                           (uint64_t)tile_bytes, tprefix, tile_base, (uint64_t)L.scan_chunk);
+                           tprefix, tile_base, (uint64_t)L.scan_chunk);
         AC_TRY(hipGetLastError());
         // tile starts and records: a grid for the whole capacity, each lane
         // checks the device-side tile count (no host round trip)
         uint64_t *tile_start = reinterpret_cast<uint64_t *>(ws + L.tile_start);
         uint32_t *tile_first = reinterpret_cast<uint32_t *>(ws + L.tile_first);
-        TileRec *tiles = reinterpret_cast<TileRec *>(ws + L.tiles);
+        TileRec *trec = reinterpret_cast<TileRec *>(ws + L.tiles);
         uint32_t *flags = reinterpret_cast<uint32_t *>(ws + L.flags);
         const uint64_t grid = (L.max_tiles + 255) / 256;
         if (grid) {
             hipLaunchKernelGGL(k_tile_starts, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_base,
-                               hdr, L.max_tiles, (uint64_t)tile_bytes, tile_start, tile_first);
+                               hdr, L.max_tiles, tile_start, tile_first);
             AC_TRY(hipGetLastError());
             hipLaunchKernelGGL(k_tiles, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_start,
-                               tile_first, tile_base, hdr, L.max_tiles, (uint64_t)tile_bytes,
-                               ridx, remap_shift(arena_bytes, t.n), tiles, flags);
+                               tile_first, tile_base, hdr, L.max_tiles,
+                               ridx, remap_shift(arena_bytes, t.n), trec, flags);
             AC_TRY(hipGetLastError());
         }
     }
@@ -967,22 +996,22 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
 }  // namespace
 
 hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsLayout &L,
-                       uint64_t *new_offset, int outputs, uint32_t tile_bytes, uint64_t epoch,
+                       uint64_t *new_offset, int outputs, TileChoice tiles, uint64_t epoch,
                        uint64_t fit_need, hipStream_t s) {
-    return queue_scan(t, arena_bytes, ws, L, new_offset, outputs, nullptr, tile_bytes, epoch,
+    return queue_scan(t, arena_bytes, ws, L, new_offset, outputs, nullptr, tiles, epoch,
                       fit_need, s);
 }
 
 hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t request,
                            uint8_t *ws, const WsLayout &L, uint64_t *new_offset,
-                           uint32_t tile_bytes, uint64_t epoch, hipStream_t s) {
+                           TileChoice tiles, uint64_t epoch, hipStream_t s) {
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.header);
     const uint64_t *src = reinterpret_cast<const uint64_t *>(ws + L.live_src);
     const uint64_t *size = reinterpret_cast<const uint64_t *>(ws + L.live_size);
     const uint64_t *z = reinterpret_cast<const uint64_t *>(ws + L.live_z);
     const uint32_t *pc = reinterpret_cast<const uint32_t *>(ws + L.live_pc);
     SelPart *sp = reinterpret_cast<SelPart *>(ws + L.selpart);
-    AC_TRY(queue_scan(t, arena_bytes, ws, L, nullptr, kOutSelect, nullptr, tile_bytes, epoch,
+    AC_TRY(queue_scan(t, arena_bytes, ws, L, nullptr, kOutSelect, nullptr, tiles, epoch,
                       kNone, s));
     // candidates: every last hole l in [0, m], m <= n
     hipLaunchKernelGGL(k_select, dim3((uint32_t)L.n_sel_blocks), dim3(kSelThreads), 0, s, src, z,
@@ -991,7 +1020,7 @@ hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t re
     hipLaunchKernelGGL(k_select_finish, dim3(1), dim3(kSpineThreads), 0, s, sp, L.n_sel_blocks,
                        src, size, z, arena_bytes, hdr);
     AC_TRY(hipGetLastError());
-    return queue_scan(t, arena_bytes, ws, L, new_offset, kOutNew, &hdr->win_begin, tile_bytes,
+    return queue_scan(t, arena_bytes, ws, L, new_offset, kOutNew, &hdr->win_begin, tiles,
                       epoch, kNone, s);
 }
 

@@ -139,17 +139,22 @@ typedef struct defrag_stats_t {
     int32_t reserved;
 } defrag_stats_t;
 
-/* Optional knobs.  Passing NULL takes the defaults: 65536-byte tiles,
- * streaming loads and stores, and one 512-lane mover workgroup per compute
- * unit (recorded in plan_host->tuning).  In a struct passed explicitly, a
- * zero tile size or spin limit takes its default and the other fields are
- * taken as given. */
+/* Optional knobs.  Passing NULL takes the defaults: the tile size chosen by
+ * the plan (below), streaming loads and stores, and one 512-lane mover
+ * workgroup per compute unit (recorded in plan_host->tuning).  In a struct
+ * passed explicitly, a zero tile size or spin limit takes its default and the
+ * other fields are taken as given. */
 typedef struct defrag_tuning {
-    uint32_t tile_bytes;      /* mover tile: power of two in [256, 131072].
-                                 Fixed at plan time.  Compactions made mostly
-                                 of small shifts (up to ~6 MiB, so a tile
-                                 often waits on one still being read) run
-                                 faster with 131072.                          */
+    uint32_t tile_bytes;      /* mover tile: power of two in [256, 131072],
+                                 or 0: the plan chooses on the device from the
+                                 shifts it finds -- 131072 when more than half
+                                 of the moved bytes shift by less than 8 MiB
+                                 and at least 64 MiB move (a tile then often
+                                 waits on one still being read, and larger
+                                 tiles amortise that wait), else 65536 -- and
+                                 the other one if the first's tiles do not fit
+                                 the workspace.  plan_host->tuning.tile_bytes
+                                 says which.                                 */
     uint32_t wg_per_cu;       /* mover workgroups per compute unit; 0 means as
                                  many as the kernel's resources allow         */
     uint32_t nontemporal;     /* streaming hints: 0 none, 1 loads and stores,
@@ -202,8 +207,8 @@ typedef struct defrag_plan_t {
 } defrag_plan_t;
 
 /* Workspace bytes for a table of n entries, at most max_pinned of them
- * pinned, over an arena of arena_bytes, with the given tile size (0 =
- * default).  Returns 0 for impossible arguments, including an arena that
+ * pinned, over an arena of arena_bytes, with the given tile size (0: room
+ * for the smaller size the plan may choose, 65536).  Returns 0 for impossible arguments, including an arena that
  * would need more than 0xFFFF0000 mover tiles (tile indices are 32-bit).  The workspace is device
  * memory, 256-byte aligned, owned by the caller; any content.  defrag_plan
  * uses whatever size it is given and returns DEFRAG_EWORKSPACE if the

@@ -312,7 +312,7 @@ def test_plan_protocol_errors(ac):
     assert ei.value.code == ac.DEFRAG_ENOPLAN
 
 
-@pytest.mark.parametrize("k", ["mixed-64m", "pairs-1g", "small-blocks-4g"])
+@pytest.mark.parametrize("k", ["mixed-64m", "pairs-1g", "small-blocks-4g", "small-shift-8g"])
 def test_full_size_workloads_every_byte(ac, k):
     heap = W.workload(k)
     _full_check(heap)

@@ -87,8 +87,23 @@ def expected_schedule(heap, hold, T):
     return np.column_stack([t0, t1, shift[moved[fi]], moved[fi], moved[la], dep_lo, dep_hi])
 
 
-def check_schedule(ac, heap, T=0, request=0):
-    T = T or 65536
+def auto_tile(heap, hold):
+    """The tile size a plan given none must choose, stated on the host: 128 KiB
+    when more than half of the moved bytes belong to blocks that shift by
+    less than 8 MiB and at least 64 MiB move, else 64 KiB (the workspaces
+    here hold either size's tiles)."""
+    li = np.flatnonzero(heap.live)
+    new = oracle.new_offsets(heap.offset, heap.size, heap.live, hold)[li].astype(np.int64)
+    shift = heap.offset[li].astype(np.int64) - new
+    sz = heap.size[li].astype(np.int64)
+    moved = int(sz[shift > 0].sum())
+    small = int(sz[(shift > 0) & (shift < (8 << 20))].sum())
+    return 131072 if (2 * small > moved and moved >= (64 << 20)) else 65536
+
+
+def check_schedule(ac, heap, T=65536, request=0):
+    """T None: no tile size given, the plan picks one (checked against the
+    rule stated in auto_tile)."""
     hold = heap.pinned
     if request:
         w = oracle.target_window(heap.offset, heap.size, heap.live, heap.arena_bytes, request,
@@ -98,13 +113,16 @@ def check_schedule(ac, heap, T=0, request=0):
     log(f"case schedule {heap.describe()} T={T} request={request}")
     off, size, live = device_table(heap, "cuda")
     pin = device_pinned(heap, "cuda")
-    ws = ac.workspace(heap.n, heap.arena_bytes, T, max_pinned=heap.n_pinned)
-    tu = ac.defrag_tuning(T, 0, 1, 0)
+    ws = ac.workspace(heap.n, heap.arena_bytes, T or 0, max_pinned=heap.n_pinned)
+    tu = ac.defrag_tuning(T, 0, 1, 0) if T else None   # None: the plan picks the size
     if request:
         plan = ac.defrag_plan_targeted(off, size, live, heap.arena_bytes, request, ws,
                                        tuning=tu, pinned=pin)
     else:
         plan = ac.defrag_plan(off, size, live, heap.arena_bytes, ws, tuning=tu, pinned=pin)
+    if not T:
+        T = auto_tile(heap, hold)
+        assert plan.tuning.tile_bytes == T, (plan.tuning.tile_bytes, T)
     got = ac.defrag_plan_tiles(plan, ws)
     want = expected_schedule(heap, hold, T)
     assert got.shape[0] == want.shape[0] == plan.n_tiles, (got.shape, want.shape, plan.n_tiles)
@@ -123,7 +141,7 @@ def check_schedule(ac, heap, T=0, request=0):
     return plan
 
 
-@pytest.mark.parametrize("T", [256, 4096, 65536])
+@pytest.mark.parametrize("T", [256, 4096, 65536, 131072, None])
 @pytest.mark.parametrize("k", W.NAMES)
 def test_schedule_small_workloads(ac, k, T):
     check_schedule(ac, W.workload(k, small=True), T)
@@ -145,9 +163,10 @@ def test_schedule_targeted(ac, k):
 
 @pytest.mark.parametrize("k", W.NAMES)
 def test_schedule_full_size(ac, k):
-    """The real launch configuration: full-size tables, 64 KiB tiles."""
+    """The real launch configuration: full-size tables, the tile size the
+    plan picks itself."""
     heap = W.workload(k)
-    plan = check_schedule(ac, heap)
+    plan = check_schedule(ac, heap, None)
     log(f"  {plan.n_tiles} tiles, {plan.whole_tiles} whole")
     torch.cuda.empty_cache()
 

@@ -123,7 +123,19 @@ def test_overlap_64g_shape():
     _handles_inside_live(h)
 
 
-@pytest.mark.parametrize("k", ["mixed-64m", "pairs-1g", "training-80g", "small-blocks-4g", "overlap-64g"])
+def test_small_shift_8g_shape():
+    h = W.workload("small-shift-8g")
+    _valid(h)
+    assert h.n == 16
+    assert np.all(h.size[1::2] == W.GiB) and np.all(h.live[1::2] == 1) and np.all(h.live[0::2] == 0)
+    holes = h.size[0::2]
+    assert holes.min() >= 4 * W.KiB and holes.max() <= W.MiB and np.all(holes % 32 == 0)
+    assert h.arena_bytes == 8 * W.GiB + int(holes.sum())
+    assert h.handles.shape[0] == 1_000_000
+    _handles_inside_live(h)
+
+
+@pytest.mark.parametrize("k", W.NAMES)
 def test_small_variants_valid_and_seeded(k):
     a = W.workload(k, small=True)
     b = W.workload(k, small=True)

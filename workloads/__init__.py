@@ -439,6 +439,27 @@ def self_overlap_64gib(seed: int = 5, n_live: int = 64, block_bytes: int = 1 * G
                 0x5EED0000 + seed, seed)
 
 
+def small_shift_8gib(seed: int = 6, n_live: int = 8, block_bytes: int = 1 * GiB,
+                     hole_lo: int = 4 * KiB, hole_hi: int = 1 * MiB,
+                     n_handles: int = 1_000_000) -> Heap:
+    """Small shifts: n_live live blocks of block_bytes, each above a freed hole
+    of log-uniform hole_lo..hole_hi bytes (ceil to 32 B), so every block moves
+    down by a few KiB to a few MiB -- far less than its size -- the regime
+    where a tile most often waits for the one reading the bytes it
+    overwrites.  Same layout as the self-overlap heap, with short holes."""
+    rng = np.random.default_rng(seed)
+    holes = _ceil_to(_loguniform(rng, hole_lo, hole_hi, n_live), 32)
+    size = np.empty(2 * n_live, dtype=np.uint64)
+    size[0::2] = holes
+    size[1::2] = np.uint64(block_bytes)
+    live = np.zeros(2 * n_live, dtype=np.uint8)
+    live[1::2] = 1
+    off = _packed_offsets(size)
+    S = int(off[-1] + size[-1])
+    h = draw_handles(off, size, live, n_handles, rng)
+    return Heap("small-shift-8g", S, off, size, live, h, "hash", 0xC0FFEE00 + seed, seed)
+
+
 # name -> (full size, reduced size with the same structure: small enough for
 # the oracle to finish in seconds, large enough for several mover tiles)
 _WORKLOADS = {
@@ -459,6 +480,9 @@ _WORKLOADS = {
     "overlap-64g": (self_overlap_64gib,
                     lambda: self_overlap_64gib(n_live=8, block_bytes=8 * MiB, hole_lo=4 * KiB,
                                                hole_hi=1 * MiB, n_handles=65536)),
+    "small-shift-8g": (small_shift_8gib,
+                       lambda: small_shift_8gib(block_bytes=8 * MiB, hole_hi=64 * KiB,
+                                                n_handles=65536)),
 }
 NAMES = tuple(_WORKLOADS)
 
@@ -477,6 +501,8 @@ SUMMARY = {
                        "(every live block moves); 8M handles",
     "overlap-64g": "64 GiB arena of 64 live 1 GiB blocks, each above a freed 4 KiB-64 MiB "
                    "hole (every move self-overlapping); 1M handles",
+    "small-shift-8g": "8 GiB arena of 8 live 1 GiB blocks, each above a freed 4 KiB-1 MiB "
+                      "hole (every block shifts by a few KiB to a few MiB); 1M handles",
 }
 
 
