@@ -108,7 +108,7 @@ static_assert(sizeof(WsHeader) == 256, "header size");
 constexpr uint32_t kStatusTimeout = 1u;   // a wait gave up (the watchdog)
 constexpr uint32_t kStatusCapacity = 2u;  // a tile met more blocks than its LDS holds
 constexpr uint32_t kStatusCorrupt = 4u;   // a tile's record or blocks lie outside the
-                                          // arena or the plan's arrays: not moved
+                                          // arena or the plan's arrays: nothing moved
 // Wait-path testing knob: at most this many sleeps per stalled tile.
 constexpr uint32_t kMaxStallSleeps = 4096;
 
@@ -397,11 +397,10 @@ struct MoveArgs {
     uint32_t wg_per_cu;   // device-sized: 0 = the default (kDefaultWgPerCu)
     uint32_t num_cus;
     uint64_t max_tiles;   // device-sized: the workspace's tile capacity
-    // Bounds every tile is checked against before it touches the arena: a
-    // record or block outside them (a workspace overwritten since its plan)
-    // moves nothing and reports kStatusCorrupt.
+    // What the check pass before a separate move holds each tile record to
+    // (a workspace overwritten since its plan moves nothing: kStatusCorrupt).
     uint64_t arena_bytes;
-    uint64_t live_blocks; // entries of the packed live arrays (device-sized: from the header)
+    uint64_t live_blocks; // entries of the packed live arrays
     // Wait-path testing knob (0 = off): tile t holds its "sources read" flag
     // back for stall_sleeps sleeps when mix(t, stall_seed) % stall_every == 0.
     uint32_t stall_every;

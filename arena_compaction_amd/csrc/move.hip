@@ -52,13 +52,19 @@
 // Per tile the kernel reads 16 B per live-block descriptor it needs (in LDS
 // only for tiles holding more than one block).
 //
-// The plan lives in caller memory, so before a tile touches the arena the
-// kernel checks what a plan guarantees: the tile's bytes lie in one window
-// inside the arena, its blocks inside the packed arrays, its dependencies
-// below it, and every source vector inside the arena.  A tile that fails
-// moves nothing and reports it (kStatusCorrupt); a tile meeting more blocks
-// than the launch gave it LDS for reports kStatusCapacity.  Neither happens
-// with a workspace left as its plan wrote it.
+// The plan lives in caller memory.  When it has been read back to the host
+// since it was written (defrag_move, a call of its own), a check pass runs
+// first: every tile's bytes in one window inside the arena, its first source
+// too, its blocks inside the packed arrays, its dependencies below it (else
+// kStatusCorrupt), its blocks within the LDS the launch gives (else
+// kStatusCapacity); on either the mover moves nothing.  A tile of several
+// blocks also checks each vector's source against the arena (a lane that
+// fails loads a safe vector instead and reports kStatusCorrupt).
+// Queued right behind its own plan (defrag_compact) the mover takes the
+// records as written.  The tile loop itself stays lean: each workgroup has
+// one tile in flight, so every instruction between claiming a tile and
+// issuing its loads, or between the loads' return and the stores, is paid
+// on every tile (per-tile checks there cost 0.7% on the 80 GiB workload).
 //
 // Counters: a tile whose dependency flags were not all seen set behind its
 // loads counts as late, and as waited if it then read a flag unset (with
@@ -103,6 +109,34 @@ __device__ __forceinline__ bool stalls(uint32_t t, uint32_t every, uint32_t seed
     return every != 0u && h % every == 0u;
 }
 
+// Before a move whose plan was read back to the host (and so could have been
+// overwritten in the workspace since): every tile record checked against
+// what a plan guarantees -- its bytes 16-byte aligned in one window inside
+// the arena, its first block's sources (for a tile of one block, all of its
+// sources) inside the arena, its blocks inside the packed arrays, its
+// dependencies below it, its blocks within the LDS the launch gives -- one
+// lane per tile.  A failure sets a status bit and the mover, queued behind,
+// moves nothing.  (A tile of several blocks checks each vector's source
+// itself: the block sizes it reads are not in its record.)
+__global__ __launch_bounds__(256) void k_verify_tiles(MoveArgs a) {
+    const uint64_t S = a.arena_bytes, T = a.tile_bytes, m = a.live_blocks;
+    uint32_t bad = 0u, over = 0u;
+    for (uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; t < a.n_tiles;
+         t += (uint64_t)gridDim.x * blockDim.x) {
+        const TileRec r = a.tiles[t];
+        const uint64_t tb = r.t0 & ~(T - 1);
+        const bool multi = r.first_block != r.last_block;
+        const bool ok = ((r.t0 | r.t1 | r.shift0) & 15u) == 0 && r.t0 < r.t1 &&
+                        r.t1 - tb <= T && r.shift0 < S && r.t1 <= S - r.shift0 &&
+                        (r.dep_lo > r.dep_hi || r.dep_hi < t) &&
+                        (!multi || (r.first_block < r.last_block && r.last_block < m));
+        if (!ok) bad = 1u;
+        else if (multi && r.last_block - r.first_block + 1u > a.max_blocks) over = 1u;
+    }
+    if (bad) atomicOr(&a.hdr->status, kStatusCorrupt);
+    if (over) atomicOr(&a.hdr->status, kStatusCapacity);
+}
+
 template <int THREADS, int VPT, int NT>
 __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
     extern __shared__ uint64_t lds_dyn[];
@@ -110,17 +144,17 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
     uint32_t *s_rel = reinterpret_cast<uint32_t *>(lds_dyn + a.max_blocks);  // [max_blocks]
     __shared__ uint32_t s_ticket;
     __shared__ uint32_t s_skip;
-    __shared__ uint32_t s_bad;     // a lane found a source outside the arena
     __shared__ uint64_t s_ntiles;
-    __shared__ uint64_t s_live;
     const uint32_t tid = threadIdx.x;
 
     if (tid == 0) {
         // a workspace re-planned since this plan: move nothing, write nothing
-        // (the status query sees the epoch mismatch)
+        // (the status query sees the epoch mismatch); nor when the records
+        // failed their check
         uint32_t tk = 0xFFFFFFFFu;
-        uint64_t nt = a.n_tiles, m = a.live_blocks;
-        if (__hip_atomic_load(&a.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch) {
+        uint64_t nt = a.n_tiles;
+        if (__hip_atomic_load(&a.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch &&
+            (a.hdr->status & (kStatusCorrupt | kStatusCapacity)) == 0u) {
             bool go = true;
             if (a.device_sized) {
                 // the plan's results, read here instead of on the host: a
@@ -129,23 +163,17 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
                 // did not choose; workgroups past the chosen count leave
                 const WsHeader *h = a.hdr;
                 nt = h->n_tiles;
-                m = h->live_blocks < m ? h->live_blocks : m;  // a.live_blocks: the arrays' room
                 const uint32_t per_cu = a.wg_per_cu ? a.wg_per_cu : kDefaultWgPerCu;
                 go = h->bad_key == kNone && h->win_state != kWinNoFit && nt <= a.max_tiles &&
                      h->tile_bytes == a.tile_bytes && blockIdx.x < (uint64_t)per_cu * a.num_cus;
             }
-            if (go && a.arena_bytes >= 32u) tk = atomicAdd(&a.hdr->ticket, 1u);
+            if (go) tk = atomicAdd(&a.hdr->ticket, 1u);
         }
         s_ticket = tk;
         s_ntiles = nt;
-        s_live = m;
-        s_bad = 0u;
     }
     __syncthreads();
     const uint64_t n_tiles = s_ntiles;
-    const uint64_t m_live = s_live;
-    const uint64_t S = a.arena_bytes;
-    const uint64_t T = a.tile_bytes;
     uint32_t t = s_ticket;
 
     while (t < n_tiles) {
@@ -161,19 +189,11 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
         const uint32_t last = __builtin_amdgcn_readfirstlane(rp.last_block);
         const uint32_t dep_lo = __builtin_amdgcn_readfirstlane(rp.dep_lo);
         const uint32_t dep_hi = __builtin_amdgcn_readfirstlane(rp.dep_hi);
-        const uint64_t tb = t0 & ~(T - 1);  // the tile's window
-        // What a plan guarantees, checked before the tile touches memory: its
-        // bytes lie in one window inside the arena, its first source too, its
-        // blocks in the live arrays, its dependencies below it.
-        const bool sane = t0 < t1 && t1 <= S && t1 - tb <= T && S - t0 >= 16u && first <= last &&
-                          last < m_live && shift0 <= S - 16u - t0 &&
-                          (dep_lo > dep_hi || dep_hi < t);
-        const uint32_t rel0 = sane ? (uint32_t)(t0 - tb) : 0u;
-        const uint32_t rel1 = sane ? (uint32_t)(t1 - tb) : 0u;
+        const uint64_t tb = t0 & ~((uint64_t)a.tile_bytes - 1);  // the tile's window
+        const uint32_t rel0 = (uint32_t)(t0 - tb);
+        const uint32_t rel1 = (uint32_t)(t1 - tb);
         const uint32_t nblk = last - first + 1u;
-        const bool fits = nblk <= a.max_blocks;
-        const bool ok = sane && fits;
-        const uint64_t lim = sane ? S - 16u - tb : 0u;  // largest source offset from tb
+        const bool ok = nblk <= a.max_blocks;  // LDS room (checked again; the plan sized it)
 
         if (nblk > 1u && ok) {
             for (uint32_t k = tid; k < nblk; k += THREADS) {
@@ -184,15 +204,19 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
             __syncthreads();
         }
 
-        // no branch around a memory access: a lane outside [rel0, rel1), or
-        // whose source would leave the arena, reloads the tile's first
-        // source vector and discards it
+        // no branch around a memory access: a lane outside [rel0, rel1)
+        // reloads the tile's first source vector and discards it; so does a
+        // lane of a tile of several blocks whose source would leave the arena
+        // (the blocks' shifts come from the packed arrays, which the check
+        // pass does not read) -- and reports it
         v4u v[VPT];
-        const uint8_t *first_src = a.arena + (sane ? t0 + shift0 : 0u);
+        const uint8_t *first_src = a.arena + tb + rel0 + shift0;
+        const uint64_t lim = a.arena_bytes - 16u - tb;  // largest source offset from tb
         bool lane_bad = false;
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
             const uint32_t r = ((uint32_t)j * THREADS + tid) * 16u;
+            bool in = ok && r >= rel0 && r < rel1;
             uint64_t sh = shift0;
             if (nblk > 1u && ok) {
                 uint32_t lo = 0, n = nblk;  // largest k with s_rel[k] <= r
@@ -202,16 +226,16 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
                     n -= half;
                 }
                 sh = s_shift[lo];
+                const bool inside = (sh & 15u) == 0 && sh <= lim && (uint64_t)r <= lim - sh;
+                lane_bad |= in && !inside;
+                in = in && inside;
             }
-            const bool in = ok && r >= rel0 && r < rel1;
-            const bool inside = sh <= lim && (uint64_t)r <= lim - sh;
-            lane_bad |= in && !inside;
-            v[j] = load16<NT>(in && inside ? a.arena + tb + r + sh : first_src);
+            v[j] = load16<NT>(in ? a.arena + tb + r + sh : first_src);
         }
-        if (lane_bad) s_bad = 1u;
+        if (__builtin_expect(lane_bad, 0)) atomicOr(&a.hdr->status, kStatusCorrupt);
         // first look at the dependency flags, returned with the data loads
         uint32_t f_lo = 0u, f_hi = 0u;
-        if (tid == 0 && ok && dep_lo <= dep_hi) {
+        if (tid == 0 && dep_lo <= dep_hi) {
             f_lo = __hip_atomic_load(&a.flags[dep_lo], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             f_hi = __hip_atomic_load(&a.flags[dep_hi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -219,16 +243,9 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tid == 0) {
-            uint32_t skip = 0u;
-            if (!sane || s_bad) {
-                skip = 1u;
-                atomicOr(&a.hdr->status, kStatusCorrupt);
-            } else if (!fits) {
-                skip = 1u;
-                atomicOr(&a.hdr->status, kStatusCapacity);
-            }
-            s_bad = 0u;
-            if (__builtin_expect(stalls(t, a.stall_every, a.stall_seed), 0)) {
+            uint32_t skip = ok ? 0u : 1u;
+            if (!ok) atomicOr(&a.hdr->status, kStatusCapacity);
+            if (__builtin_expect(a.stall_every != 0u, 0) && stalls(t, a.stall_every, a.stall_seed)) {
                 for (uint32_t k = 0; k < a.stall_sleeps; ++k) __builtin_amdgcn_s_sleep(127);
             }
             __hip_atomic_store(&a.flags[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -356,6 +373,10 @@ hipError_t launch_nt(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStre
 hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, uint32_t nontemporal, int num_cus,
                        hipStream_t s) {
     if (a.n_tiles == 0) return hipSuccess;
+    uint64_t vgrid = (a.n_tiles + 255) / 256;
+    if (vgrid > (uint64_t)num_cus * 4) vgrid = (uint64_t)num_cus * 4;
+    hipLaunchKernelGGL(k_verify_tiles, dim3((uint32_t)vgrid), dim3(256), 0, s, a);
+    AC_TRY(hipGetLastError());
     switch (nontemporal) {
         case 0: return launch_nt<0, false>(a, wg_per_cu, num_cus, s);
         case 1: return launch_nt<3, false>(a, wg_per_cu, num_cus, s);
