@@ -93,7 +93,7 @@ int read_header(WsHeader *out, const uint8_t *ws, const WsLayout &L, hipStream_t
 }
 
 TableView view_of(const defrag_table *t) {
-    return TableView{t->offset_dev, t->size_dev, t->live_dev, t->pinned_dev, t->n};
+    return TableView{t->offset_dev, t->size_dev, t->live_dev, t->pinned_dev, t->n, nullptr, 0};
 }
 
 WsLayout plan_layout(const defrag_plan_t *p) { return ws_with_tiles(p->n, p->max_tiles); }
@@ -175,9 +175,12 @@ int stats_pass(const defrag_table *table, uint64_t arena_bytes, uint64_t fit_nee
 // The one-call path's post-check, queued (on the side stream, while the move
 // may still run): the statistics pass of the packed table, with its own
 // header (the move reads the plan's header as it starts) and otherwise only
-// the fixed statistics region in front of the plan's data.
+// the fixed statistics region in front of the plan's data.  With a gate (the
+// plan's header, queued before the plan is read back) packed->n is an upper
+// bound: the passes take the plan's live count, and nothing if it failed.
 int post_check_queue(const defrag_table *packed, uint64_t arena_bytes, void *ws_dev,
-                     size_t ws_bytes, hipStream_t stream) {
+                     size_t ws_bytes, const WsHeader *gate, uint64_t max_tiles,
+                     hipStream_t stream) {
     int rc = check_table(packed);
     if (rc) return rc;
     WsLayout L = ws_fixed(packed->n);
@@ -185,7 +188,10 @@ int post_check_queue(const defrag_table *packed, uint64_t arena_bytes, void *ws_
     if (rc) return rc;
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
     L.header = L.post;
-    return launch_scan(view_of(packed), arena_bytes, ws, L, nullptr, 0,
+    TableView v = view_of(packed);
+    v.gate = gate;
+    v.gate_max_tiles = max_tiles;
+    return launch_scan(v, arena_bytes, ws, L, nullptr, 0,
                        TileChoice{kDefaultTile, kDefaultTile}, 0, kNone,
                        stream) == hipSuccess
                ? DEFRAG_OK
@@ -404,7 +410,8 @@ int compact_serial(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     if (after_host) {
         const defrag_table packed{a->offset_out_dev, a->size_out_dev, a->live_out_dev,
                                   plan->live_blocks, a->pinned_out_dev};
-        rc = post_check_queue(&packed, a->arena_bytes, a->ws_dev, a->ws_bytes, stream);
+        rc = post_check_queue(&packed, a->arena_bytes, a->ws_dev, a->ws_bytes, nullptr, 0,
+                              stream);
         if (rc) {
             arg_error(after_host);
             return rc;
@@ -555,8 +562,8 @@ int defrag_remap(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes,
                      reinterpret_cast<const uint64_t *>(ws + L.live_src),
                      reinterpret_cast<const uint32_t *>(ws + L.live_key),
                      reinterpret_cast<const uint32_t *>(ws + L.ridx), plan->arena_bytes, plan->n,
-                     plan->live_blocks, h_in_dev, h_out_dev, n_handles, n_invalid_dev, cus,
-                     stream) != hipSuccess)
+                     plan->live_blocks, h_in_dev, h_out_dev, n_handles, n_invalid_dev, nullptr,
+                     0, cus, stream) != hipSuccess)
         return DEFRAG_EHIP;
     return DEFRAG_OK;
 }
@@ -568,7 +575,8 @@ int defrag_commit(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes
     if (rc) return rc;
     const WsLayout L = plan_layout(plan);
     if (launch_commit(static_cast<const uint8_t *>(ws_dev), L, plan->live_blocks, offset_out_dev,
-                      size_out_dev, live_out_dev, pinned_out_dev, stream) != hipSuccess)
+                      size_out_dev, live_out_dev, pinned_out_dev, nullptr, 0, nullptr,
+                      stream) != hipSuccess)
         return DEFRAG_EHIP;
     return DEFRAG_OK;
 }
@@ -581,30 +589,31 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
         arg_error(&plan->stats);
         return DEFRAG_EINVAL;
     }
-    // The move is queued right behind the plan's passes, sized from the
-    // header on the device, and the plan is read back on a second stream
-    // while it runs: the host never stands between plan and move.  That
-    // needs the arena and the post-check's outputs known good before
-    // anything is queued, and a workgroup count the device can pick;
-    // otherwise the calls run in the plain order (plan, read back, check,
-    // move), which rejects a bad argument before any byte moves.
+    // Everything is queued at once and sized on the device: the move right
+    // behind the plan's passes, reading the tile count from the plan's
+    // header; remap, commit and the post-check on a second stream that
+    // waits for the plan and takes the live count from the same header (a
+    // failed plan moves and writes nothing).  They read the plan, never the
+    // arena, so they run while the move does.  One read of both headers at
+    // the end fills the host plan.  That needs the arena and the
+    // post-check's outputs known good before anything is queued, and a
+    // workgroup count the device can pick; otherwise the calls run in the
+    // plain order (plan, read back, check, move), which rejects a bad
+    // argument before any byte moves.
     const bool arena_ok = a->arena_dev && !(reinterpret_cast<uintptr_t>(a->arena_dev) & 15u);
     const bool post_ok = !after_host || (a->offset_out_dev && a->size_out_dev);
     const bool wg_ok = !a->tuning || a->tuning->wg_per_cu != 0;
     if (!(arena_ok && post_ok && wg_ok)) return compact_serial(a, stream, plan, after_host);
-    bool remap_done = false, commit_done = false, post_done = false;
-    int rc;
     PlanCtx c;
-    rc = plan_queue(a->table, a->arena_bytes, a->request_bytes, a->tuning, a->ws_dev,
-                    a->ws_bytes, stream, a->new_offset_dev, plan, &c);
+    int rc = plan_queue(a->table, a->arena_bytes, a->request_bytes, a->tuning, a->ws_dev,
+                        a->ws_bytes, stream, a->new_offset_dev, plan, &c);
     if (rc) return rc;
     const int cus = num_cus_of(c.dev);
     hipStream_t side = a->side_stream ? a->side_stream : side_stream_of(c.dev);
     if (cus <= 0 || !side) return DEFRAG_EHIP;
-    hipEvent_t planned = nullptr;
-    if (hipEventCreateWithFlags(&planned, hipEventDisableTiming) != hipSuccess)
-        return DEFRAG_EHIP;
     uint8_t *ws = static_cast<uint8_t *>(a->ws_dev);
+    const WsHeader *gate = reinterpret_cast<const WsHeader *>(ws + c.L.header);
+    const uint64_t n = a->table->n;  // the bound of every live count below
     MoveArgs m{};
     m.arena = static_cast<uint8_t *>(a->arena_dev);
     m.live_dst = reinterpret_cast<const uint64_t *>(ws + c.L.live_dst);
@@ -616,76 +625,93 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     m.spin_limit = 1ull << c.tu.spin_limit_log2;
     m.tile_bytes = c.tiles.a;
     m.max_blocks = c.tiles.a / 32 + 2;  // the most blocks a tile can meet
-    m.small_blocks = move_small_blocks(a->arena_bytes, a->table->n) ? 1u : 0u;
+    m.small_blocks = move_small_blocks(a->arena_bytes, n) ? 1u : 0u;
     m.device_sized = 1;
     m.wg_per_cu = c.tuned ? c.tu.wg_per_cu : 0;
     m.num_cus = (uint32_t)cus;
     m.max_tiles = c.L.max_tiles;
     m.arena_bytes = a->arena_bytes;
-    m.live_blocks = a->table->n;  // room of the packed arrays; the count comes from the header
+    m.live_blocks = n;  // room of the packed arrays; the count comes from the header
     m.stall_every = c.tu.stall_every;
     m.stall_sleeps = c.tu.stall_sleeps;
     m.stall_seed = c.tu.stall_seed;
     // with the tile size left to the plan, a mover for each candidate: the
-    // one whose size the plan did not choose leaves at once
+    // one whose size the plan did not choose leaves at once.  Below
+    // kAutoMinMoved arena bytes the plan keeps the smaller size unless its
+    // tiles overflow the workspace, which the bound rules out here.
     MoveArgs mb = m;
     mb.tile_bytes = c.tiles.b;
     mb.max_blocks = c.tiles.b / 32 + 2;
-    WsHeader hp;
-    const bool queued =
-        hipEventRecord(planned, stream) == hipSuccess &&
-        launch_move_device_sized(m, c.tu.nontemporal, stream) == hipSuccess &&
-        (c.tiles.a == c.tiles.b || launch_move_device_sized(mb, c.tu.nontemporal, stream) == hipSuccess) &&
-        hipStreamWaitEvent(side, planned, 0) == hipSuccess;
-    rc = queued ? read_header(&hp, ws, c.L, side) : DEFRAG_EHIP;
-    const hipError_t destroyed = hipEventDestroy(planned);
-    if (rc) return rc;
-    if (destroyed != hipSuccess) return DEFRAG_EHIP;
-    // a failed plan: the queued move saw it in the header and moved nothing
-    rc = plan_fill(a->table, a->arena_bytes, a->request_bytes, a->ws_dev, c, hp, plan);
+    const bool one_mover =
+        c.tiles.a == c.tiles.b || (a->arena_bytes < kAutoMinMoved &&
+                                   tiles_bound(a->arena_bytes, n, c.tiles.a) <= c.L.max_tiles);
+    const bool want_remap = a->n_handles || a->n_invalid_dev;
+    const bool want_commit =
+        a->offset_out_dev || a->size_out_dev || a->live_out_dev || a->pinned_out_dev;
+    const bool side_work = want_remap || want_commit || after_host;
+    hipEvent_t planned = nullptr, joined = nullptr;
+    if (side_work && (hipEventCreateWithFlags(&planned, hipEventDisableTiming) != hipSuccess ||
+                      hipEventCreateWithFlags(&joined, hipEventDisableTiming) != hipSuccess)) {
+        if (planned) (void)hipEventDestroy(planned);
+        return DEFRAG_EHIP;
+    }
+    bool ok = (!side_work || hipEventRecord(planned, stream) == hipSuccess) &&
+              launch_move_device_sized(m, c.tu.nontemporal, stream) == hipSuccess &&
+              (one_mover || launch_move_device_sized(mb, c.tu.nontemporal, stream) == hipSuccess);
+    bool side_queued = false;
+    if (ok && side_work) {
+        ok = hipStreamWaitEvent(side, planned, 0) == hipSuccess;
+        side_queued = ok;
+        // the commit (with the invalid-handle count's reset) first: the
+        // post-check reads the packed table
+        if (ok && (want_commit || a->n_invalid_dev))
+            ok = launch_commit(ws, c.L, n, a->offset_out_dev, a->size_out_dev, a->live_out_dev,
+                               a->pinned_out_dev, gate, c.L.max_tiles, a->n_invalid_dev,
+                               side) == hipSuccess;
+        if (ok && a->n_handles)
+            ok = launch_remap(ws + c.L.live_rec, reinterpret_cast<const uint64_t *>(ws + c.L.live_src),
+                              reinterpret_cast<const uint32_t *>(ws + c.L.live_key),
+                              reinterpret_cast<const uint32_t *>(ws + c.L.ridx), a->arena_bytes, n,
+                              n, a->h_in_dev, a->h_out_dev, a->n_handles, a->n_invalid_dev, gate,
+                              c.L.max_tiles, cus, side) == hipSuccess;
+        if (ok && after_host) {
+            const defrag_table packed{a->offset_out_dev, a->size_out_dev, a->live_out_dev, n,
+                                      a->pinned_out_dev};
+            rc = post_check_queue(&packed, a->arena_bytes, a->ws_dev, a->ws_bytes, gate,
+                                  c.L.max_tiles, side);
+            ok = rc == DEFRAG_OK;
+        }
+        if (ok)
+            ok = hipEventRecord(joined, side) == hipSuccess &&
+                 hipStreamWaitEvent(stream, joined, 0) == hipSuccess;
+    }
+    if (side_work) {
+        (void)hipEventDestroy(planned);
+        (void)hipEventDestroy(joined);
+    }
+    if (!ok) {
+        // no kernel of this call still writes the caller's buffers once it returns
+        if (side_queued) (void)hipStreamSynchronize(side);
+        (void)hipStreamSynchronize(stream);
+        if (after_host) arg_error(after_host);
+        return rc ? rc : DEFRAG_EHIP;
+    }
+    // the plan's header (and the mover's status in it) and the post-check's
+    static_assert(sizeof(WsHeader) == 256, "two adjacent headers");
+    WsHeader both[2];
+    if (c.L.post != c.L.header + sizeof(WsHeader) ||
+        hipMemcpyAsync(both, ws + c.L.header, sizeof(both), hipMemcpyDeviceToHost, stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return DEFRAG_EHIP;
+    rc = plan_fill(a->table, a->arena_bytes, a->request_bytes, a->ws_dev, c, both[0], plan);
     if (rc) return rc;
     plan->state = 2;
-    // Remap, commit and the post-check read the plan, never the arena,
-    // so they run on the side stream while the move does, and the
-    // stream waits for them at the end; the post-check writes its own
-    // header.  A failure after some of them are queued waits for those
-    // first, so no kernel of this call still writes the caller's
-    // buffers once it returns.
-    const auto fail = [&](int code) {
-        if (remap_done || commit_done || post_done) (void)hipStreamSynchronize(side);
-        return code;
-    };
-    if (a->n_handles || a->n_invalid_dev) {
-        rc = defrag_remap(plan, a->ws_dev, a->ws_bytes, a->h_in_dev, a->h_out_dev,
-                          a->n_handles, a->n_invalid_dev, side);
-        if (rc) return fail(rc);
-        remap_done = true;
-    }
-    if (a->offset_out_dev || a->size_out_dev || a->live_out_dev || a->pinned_out_dev) {
-        rc = defrag_commit(plan, a->ws_dev, a->ws_bytes, a->offset_out_dev,
-                           a->size_out_dev, a->live_out_dev, a->pinned_out_dev, side);
-        if (rc) return fail(rc);
-        commit_done = true;
-    }
     if (after_host) {
-        const defrag_table packed{a->offset_out_dev, a->size_out_dev, a->live_out_dev,
-                                  plan->live_blocks, a->pinned_out_dev};
-        rc = post_check_queue(&packed, a->arena_bytes, a->ws_dev, a->ws_bytes, side);
-        if (rc) {
-            arg_error(after_host);
-            return fail(rc);
-        }
-        post_done = true;
+        fill_stats(after_host, both[1], a->arena_bytes);
+        if (both[1].bad_key != kNone) return DEFRAG_EINVAL;
     }
-    if (remap_done || commit_done || post_done) {
-        hipEvent_t joined_ev = nullptr;
-        if (hipEventCreateWithFlags(&joined_ev, hipEventDisableTiming) != hipSuccess)
-            return fail(DEFRAG_EHIP);
-        const bool joined = hipEventRecord(joined_ev, side) == hipSuccess &&
-                            hipStreamWaitEvent(stream, joined_ev, 0) == hipSuccess;
-        if (hipEventDestroy(joined_ev) != hipSuccess || !joined) return fail(DEFRAG_EHIP);
-    }
-    return compact_finish(a, stream, plan, after_host, post_done);
+    return plan->n_tiles ? move_outcome(both[0], plan->epoch) : DEFRAG_OK;
 }
 
 const char *defrag_strerror(int code) {

@@ -242,15 +242,14 @@ inline bool remap_ent(uint64_t arena_bytes, uint64_t n) {
     return remap_rec32(arena_bytes) && remap_keys32(arena_bytes, n);
 }
 
-constexpr size_t kPerTileBytes =
-    sizeof(uint64_t) + sizeof(uint32_t) + sizeof(TileRec) + sizeof(uint32_t);
+constexpr size_t kPerTileBytes = sizeof(TileRec) + sizeof(uint32_t);
 
 struct WsLayout {
     // fixed part (depends on n only)
-    size_t header, post, part, prefix, spart, tpart, twhole, tprefix, live_dst, live_src, live_size,
+    size_t header, post, part, spart, tpart, twhole, lbase, live_dst, live_src, live_size,
         live_pin, tile_base, live_z, live_pc, selpart, live_rec, live_key, ridx, fixed;
     // tile part (depends on the tile capacity)
-    size_t tile_start, tile_first, tiles, flags, total;
+    size_t tiles, flags, total;
     uint64_t n_scan_blocks, scan_chunk, n_sel_blocks, max_tiles;
 };
 
@@ -273,12 +272,11 @@ inline WsLayout ws_fixed(uint64_t n) {
     L.header = at;    at += align256(sizeof(WsHeader));
     L.post = at;      at += align256(sizeof(WsHeader));  // statistics passes' own header
     L.part = at;      at += align256(nb * sizeof(ScanPart));
-    L.prefix = at;    at += align256(nb * sizeof(ScanPart));
     L.spart = at;     at += align256(nb * sizeof(StatPart));
     // -- everything below here is a plan's: statistics passes stop above --
     L.tpart = at;     at += align256(2 * nb * sizeof(uint64_t));   // per tile-size candidate
     L.twhole = at;    at += align256(2 * nb * sizeof(uint64_t));
-    L.tprefix = at;   at += align256(nb * sizeof(uint64_t));
+    L.lbase = at;     at += align256((nb + 1) * sizeof(uint64_t));
     L.live_dst = at;  at += align256((n + 1) * sizeof(uint64_t));
     L.live_src = at;  at += align256((n + 1) * sizeof(uint64_t));
     L.live_size = at; at += align256((n + 1) * sizeof(uint64_t));
@@ -299,8 +297,6 @@ inline WsLayout ws_with_tiles(uint64_t n, uint64_t max_tiles) {
     WsLayout L = ws_fixed(n);
     L.max_tiles = max_tiles;
     size_t at = L.fixed;
-    L.tile_start = at; at += align256(max_tiles * sizeof(uint64_t));
-    L.tile_first = at; at += align256(max_tiles * sizeof(uint32_t));
     L.tiles = at;      at += align256(max_tiles * sizeof(TileRec));
     L.flags = at;      at += align256(max_tiles * sizeof(uint32_t));
     L.total = at;
@@ -331,8 +327,29 @@ struct TableView {
     const uint64_t *size;
     const uint8_t *live;    // may be null: all live
     const uint8_t *pinned;  // may be null: none pinned
-    uint64_t n;
+    uint64_t n;             // entries (with a gate: the most there can be)
+    // A gate, for a table another queued pass writes (the packed table of a
+    // plan): the plan's header.  The table then has that plan's live-block
+    // count of entries, and a pass over it writes nothing if the plan failed.
+    const struct WsHeader *gate;
+    uint64_t gate_max_tiles;
 };
+
+// Whether the plan whose header this is failed: an invalid table, no window
+// for a targeted request, or more tiles than the workspace holds.
+__device__ inline bool plan_failed(const WsHeader *h, uint64_t max_tiles) {
+    return h->bad_key != kNone || h->win_state == kWinNoFit || h->n_tiles > max_tiles;
+}
+// Entries of a table, and whether a pass over it may run (gate above).
+__device__ inline bool table_entries(const TableView &t, uint64_t *n) {
+    if (!t.gate) {
+        *n = t.n;
+        return true;
+    }
+    if (plan_failed(t.gate, t.gate_max_tiles)) return false;
+    *n = t.gate->live_blocks < t.n ? t.gate->live_blocks : t.n;
+    return true;
+}
 
 // Packed live-block arrays (m + 1 entries each).
 struct LiveView {
@@ -372,9 +389,14 @@ hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws,
 hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t request,
                            uint8_t *ws, const WsLayout &L, uint64_t *new_offset,
                            TileChoice tiles, uint64_t epoch, hipStream_t s);
+// gate (the one-call path, queued before the plan is read back): the plan's
+// header gives the live-block count (live_blocks is then the most there can
+// be) and nothing is written if the plan failed; zero: a counter to clear
+// (the remap's invalid count) once the plan is known good.
 hipError_t launch_commit(const uint8_t *ws, const WsLayout &L, uint64_t live_blocks,
                          uint64_t *off_out, uint64_t *size_out, uint8_t *live_out,
-                         uint8_t *pinned_out, hipStream_t s);
+                         uint8_t *pinned_out, const WsHeader *gate, uint64_t max_tiles,
+                         uint64_t *zero, hipStream_t s);
 
 // ---- move.hip ----
 struct MoveArgs {
@@ -421,11 +443,14 @@ int compact_serial(const struct defrag_compact_args *a, hipStream_t stream,
                    struct defrag_plan_t *plan, struct defrag_stats_t *after_host);
 
 // ---- remap.hip ----
+// gate: as launch_commit (the count of invalid handles is then taken as
+// cleared already: see launch_commit's zero).
 hipError_t launch_remap(const void *rec, const uint64_t *live_src, const uint32_t *key,
                         const uint32_t *ridx,
                         uint64_t arena_bytes, uint64_t n, uint64_t live_blocks,
                         const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
-                        uint64_t *n_invalid, int num_cus, hipStream_t s);
+                        uint64_t *n_invalid, const WsHeader *gate, uint64_t max_tiles,
+                        int num_cus, hipStream_t s);
 
 }  // namespace ac
 

@@ -22,18 +22,24 @@
 // merges adjacent free blocks, section 2.2), so one pass over live entries in
 // order sees every hole once, plus the tail above the highest live block.
 //
-// Passes (n up to 2^32 entries): per-workgroup aggregates, a single-workgroup
-// spine scan, a downsweep that writes new offsets, the packed live-block
-// arrays (new and old offset, size, pinned flag) and per-workgroup
-// statistics, and a single-workgroup finish.  Then the mover's tiles: every
-// moved block counts the tiles that start inside it (a run of moved blocks
-// starts one, and so does every tile-size boundary inside a run), and the
-// remap's bucket index over old offsets is built (it also narrows the tiles'
-// source searches) -- in a plan the finish, these counts and the index share
-// one launch, as each reads only what the scan wrote; a scan of the counts
-// gives each block its first tile, and one lane per tile writes the tile's
-// start, its range, its blocks and its dependencies.  The whole sequence is
-// queued at once; the host reads the header back only at the end.
+// Passes (n up to 2^32 entries), each a wide launch -- the one-workgroup
+// spines are gone: every workgroup of a pass scans the (at most 1,024)
+// per-workgroup results of the pass before it for its own prefix.
+//   1. per-workgroup aggregates (and the first bad entry);
+//   2. each workgroup's prefix, then its entries: new offsets, the packed
+//      live-block arrays (new and old offset, size, pinned flag, the remap's
+//      records), hole and move statistics, and the tiles its moved blocks
+//      start, counted for both candidate tile sizes; workgroup 0 writes the
+//      table's totals (a statistics pass then ends with a one-workgroup
+//      finish);
+//   3. (plans) each workgroup picks the tile size from the totals, the same
+//      way, and gives each of its live blocks its first tile index;
+//      workgroup 0 finishes the header (statistics, tile count and size,
+//      the mover's fields); further workgroups build the remap's bucket
+//      index over old offsets (it also narrows the tiles' source searches);
+//   4. (plans) one lane per tile: its start, range, blocks and dependencies.
+// The whole sequence is queued at once; the host reads the header back only
+// at the end.
 #include "internal.h"
 
 namespace ac {
@@ -163,6 +169,53 @@ struct OpAdd { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { re
 struct OpMax { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return umax64(a, b); } };
 struct OpMin { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return umin64(a, b); } };
 
+// Workgroup reduction of the statistics and up to four extra sums in one
+// LDS round trip (one barrier pair for all fields, not one per field): each
+// wave reduces with shuffles, then every thread combines the waves' values.
+// sh: 12 * NT/64 slots.
+template <int NT>
+__device__ inline void block_reduce_stats(StatPart &q, uint64_t (&x)[4], uint64_t *sh) {
+    constexpr int NW = NT / 64;
+    constexpr int F = 12;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        q.max_gap = umax64(q.max_gap, (uint64_t)__shfl_xor(q.max_gap, d, 64));
+        q.gaps += (uint64_t)__shfl_xor(q.gaps, d, 64);
+        q.moved_blocks += (uint64_t)__shfl_xor(q.moved_blocks, d, 64);
+        q.moved_bytes += (uint64_t)__shfl_xor(q.moved_bytes, d, 64);
+        q.min_moved_dst = umin64(q.min_moved_dst, (uint64_t)__shfl_xor(q.min_moved_dst, d, 64));
+        q.min_size = umin64(q.min_size, (uint64_t)__shfl_xor(q.min_size, d, 64));
+        q.min_fit = umin64(q.min_fit, (uint64_t)__shfl_xor(q.min_fit, d, 64));
+        q.small_moved += (uint64_t)__shfl_xor(q.small_moved, d, 64);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] += (uint64_t)__shfl_xor(x[k], d, 64);
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        uint64_t *o = sh + F * w;
+        o[0] = q.max_gap; o[1] = q.gaps; o[2] = q.moved_blocks; o[3] = q.moved_bytes;
+        o[4] = q.min_moved_dst; o[5] = q.min_size; o[6] = q.min_fit; o[7] = q.small_moved;
+        o[8] = x[0]; o[9] = x[1]; o[10] = x[2]; o[11] = x[3];
+    }
+    __syncthreads();
+    q = StatPart{0, 0, 0, 0, kNone, kNone, kNone, 0};
+    x[0] = x[1] = x[2] = x[3] = 0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        const uint64_t *o = sh + F * k;
+        q.max_gap = umax64(q.max_gap, o[0]);
+        q.gaps += o[1];
+        q.moved_blocks += o[2];
+        q.moved_bytes += o[3];
+        q.min_moved_dst = umin64(q.min_moved_dst, o[4]);
+        q.min_size = umin64(q.min_size, o[5]);
+        q.min_fit = umin64(q.min_fit, o[6]);
+        q.small_moved += o[7];
+        x[0] += o[8]; x[1] += o[9]; x[2] += o[10]; x[3] += o[11];
+    }
+    __syncthreads();
+}
+
 // Reason code of entry i (0 when it passes); checks in the documented order.
 __device__ inline uint32_t entry_reason(uint64_t i, uint64_t o, uint64_t s, uint32_t l,
                                         uint32_t p, uint64_t arena_bytes, uint64_t prev_end) {
@@ -202,20 +255,22 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_partials(TableView t, uin
                                                                 uint64_t chunk, ScanPart *part) {
     __shared__ Agg sh[kScanThreads / 64];
     __shared__ uint64_t shr[kScanThreads / 64];
+    uint64_t n;
+    if (!table_entries(t, &n)) return;  // a gated table whose plan failed
     const Window w = window_of(win);
     const uint64_t base = (uint64_t)blockIdx.x * chunk;
-    const uint64_t end = umin64(base + chunk, t.n);
+    const uint64_t end = umin64(base + chunk, n);
     Agg acc = agg_zero();
     uint64_t bad = kNone;
     for (uint64_t s0 = base; s0 < end; s0 += kScanTile) {
         const uint64_t i0 = s0 + (uint64_t)threadIdx.x * kScanItems;
         Agg a = agg_zero();
         uint64_t prev_end = 0;
-        if (i0 > 0 && i0 < t.n) prev_end = t.off[i0 - 1] + t.size[i0 - 1];
+        if (i0 > 0 && i0 < n) prev_end = t.off[i0 - 1] + t.size[i0 - 1];
 #pragma unroll
         for (uint32_t k = 0; k < kScanItems; ++k) {
             const uint64_t i = i0 + k;
-            if (i < t.n) {
+            if (i < n) {
                 const uint64_t o = t.off[i], s = t.size[i];
                 const uint32_t l = live_of(t, i), p = pin_of(t, i);
                 const uint32_t r = entry_reason(i, o, s, l, p, arena_bytes, prev_end);
@@ -233,35 +288,51 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_partials(TableView t, uin
     if (threadIdx.x == 0) part[blockIdx.x] = ScanPart{acc, bad};
 }
 
-// Pass 2 (one workgroup): exclusive scan of the aggregates; table totals.
-__global__ __launch_bounds__(kSpineThreads) void k_scan_spine(const ScanPart *part, ScanPart *prefix,
-                                                              uint64_t nb, WsHeader *hdr,
-                                                              int reset_window) {
-    __shared__ Agg sh[kSpineThreads / 64];
-    __shared__ uint64_t shr[kSpineThreads / 64];
-    Agg carry = agg_zero();
-    uint64_t bad = kNone;
-    for (uint64_t base = 0; base < nb; base += kSpineThreads) {
-        const uint64_t j = base + threadIdx.x;
-        Agg x = agg_zero();
+// Every pass after the aggregates takes what it needs of them itself: each
+// workgroup scans the (at most kMaxScanParts) aggregates for its own prefix
+// and the table's totals -- a few microseconds of L2-resident work in every
+// workgroup, in place of a one-workgroup launch and the gap in front of it.
+// before: aggregates of the parts below g; total: of all; bad: the smallest
+// bad-entry key.  s_before: an LDS slot for the broadcast.
+__device__ void parts_prefix(const ScanPart *part, uint64_t nb, uint64_t g, Agg *sh,
+                             uint64_t *shr, Agg *s_before, Agg &before, Agg &total,
+                             uint64_t &bad) {
+    constexpr uint32_t kPer = kMaxScanParts / kScanThreads;
+    const uint64_t j0 = (uint64_t)threadIdx.x * kPer;
+    Agg loc = agg_zero(), upto = agg_zero();
+    uint64_t b = kNone;
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k) {
+        const uint64_t j = j0 + k;
+        if (j == g) upto = loc;
         if (j < nb) {
-            x = part[j].a;
-            bad = umin64(bad, part[j].bad_key);
+            loc = combine(loc, part[j].a);
+            b = umin64(b, part[j].bad_key);
         }
-        Agg total;
-        const Agg ex = block_excl<kSpineThreads>(x, total, sh);
-        if (j < nb) prefix[j] = ScanPart{combine(carry, ex), 0};
-        carry = combine(carry, total);
     }
-    bad = block_reduce<kSpineThreads>(bad, shr, OpMin());
-    if (threadIdx.x == 0) {
-        hdr->live_bytes = carry.lsum;
-        hdr->max_live_end = carry.mx;
-        hdr->live_blocks = carry.cnt;
-        hdr->pinned_blocks = carry.pcnt;
-        hdr->bad_key = bad;
-        if (reset_window) hdr->win_state = kWinNone;
+    const Agg ex = block_excl<kScanThreads>(loc, total, sh);
+    if (g >= j0 && g < j0 + kPer) *s_before = combine(ex, upto);
+    bad = block_reduce<kScanThreads>(b, shr, OpMin());  // (its barriers publish s_before)
+    before = *s_before;
+}
+
+// The same for sums of u64 (tile counts): the sum below g and the total.
+__device__ void sums_prefix(const uint64_t *x, uint64_t nb, uint64_t g, uint64_t *sh,
+                            uint64_t *s_before, uint64_t &before, uint64_t &total) {
+    constexpr uint32_t kPer = kMaxScanParts / kScanThreads;
+    const uint64_t j0 = (uint64_t)threadIdx.x * kPer;
+    uint64_t loc = 0, upto = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k) {
+        const uint64_t j = j0 + k;
+        if (j == g) upto = loc;
+        if (j < nb) loc += x[j];
     }
+    const uint64_t ex = block_excl_sum<kScanThreads>(loc, total, sh);
+    if (g >= j0 && g < j0 + kPer) *s_before = ex + upto;
+    __syncthreads();
+    before = *s_before;
+    __syncthreads();
 }
 
 struct LiveOut {
@@ -276,22 +347,83 @@ struct LiveOut {
     uint64_t key_mask;  // old offset -> offset inside its remap bucket
 };
 
-// Pass 3: new offsets, packed live arrays, per-workgroup hole/move stats.
-__global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const uint64_t *win,
-                                                            const ScanPart *prefix,
-                                                            const WsHeader *hdr, uint64_t *new_offset,
-                                                            LiveOut lo, StatPart *spart,
-                                                            int outputs, uint64_t fit_need,
-                                                            uint64_t chunk) {
+// Tiles a run of moved blocks starts in one live block: at the run's first
+// byte (if not on a window boundary) and at every multiple of T inside it.
+// a: new offset, s: size, start: the block opens a run.
+__device__ inline uint64_t tiles_of(uint64_t a, uint64_t s, bool start, uint64_t T) {
+    const uint64_t b = a + s;
+    const uint64_t mult = (b + T - 1) / T - (a + T - 1) / T;  // multiples of T in [a, b)
+    return mult + ((start && (a & (T - 1))) ? 1 : 0);
+}
+// Whole windows [cT, cT + T) inside a moved block: each is one tile of that
+// block alone.
+__device__ inline uint64_t whole_of(uint64_t a, uint64_t s, uint64_t T) {
+    const uint64_t lo = (a + T - 1) / T, hi = (a + s) / T;
+    return hi > lo ? hi - lo : 0;
+}
+
+struct DownArgs {
+    TableView t;
+    const uint64_t *win;      // a targeted plan's window (in its header), or null
+    const ScanPart *part;
+    uint64_t nb;       // aggregates (0 for an empty table)
+    uint64_t ngroups;  // workgroups of this pass: max(nb, 1)
+    uint64_t chunk;
+    WsHeader *hdr;
+    uint64_t *new_offset;
+    LiveOut lo;
+    StatPart *spart;
+    uint64_t *tpart, *twhole;  // tile counts per workgroup, both candidates (plans)
+    uint64_t *lbase;           // live blocks below each workgroup's entries (plans; ngroups + 1)
+    TileChoice tiles;
+    int outputs;
+    uint64_t fit_need;
+    uint64_t epoch;
+};
+
+// Pass 2: the workgroup's prefix (from the aggregates), then its entries in
+// order: new offsets, the packed live arrays, hole and move statistics, and
+// (plans) the tiles its moved blocks start, for both tile-size candidates.
+// Workgroup 0 writes the table's totals and validity to the header.  An
+// invalid table writes nothing else.  The block before a live entry moved
+// iff the packed position after it differs from its end (a block that stays,
+// pinned or held, resets the position to its own end).
+__global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
     __shared__ Agg sh[kScanThreads / 64];
     __shared__ uint64_t shr[kScanThreads / 64];
-    if (plan_dead(hdr)) return;  // invalid table or nothing to plan: write nothing
-    const Window w = window_of(win);
-    const uint64_t base = (uint64_t)blockIdx.x * chunk;
-    const uint64_t end = umin64(base + chunk, t.n);
-    Agg carry = prefix[blockIdx.x].a;  // everything before this workgroup's chunk
+    __shared__ uint64_t s_red[12 * (kScanThreads / 64)];
+    __shared__ Agg s_before;
+    const TableView &t = d.t;
+    const uint64_t g = blockIdx.x;
+    uint64_t n;
+    if (!table_entries(t, &n)) return;  // a gated table whose plan failed
+    Agg before, total;
+    uint64_t bad;
+    parts_prefix(d.part, d.nb, g, sh, shr, &s_before, before, total, bad);
+    const bool no_fit = d.win && d.hdr->win_state == kWinNoFit;  // set before this pass
+    if (g == 0 && threadIdx.x == 0) {
+        WsHeader *hdr = d.hdr;
+        hdr->live_bytes = total.lsum;
+        hdr->max_live_end = total.mx;
+        hdr->live_blocks = total.cnt;
+        hdr->pinned_blocks = total.pcnt;
+        hdr->bad_key = bad;
+        if (!d.win) hdr->win_state = kWinNone;
+        // a plan (or a selection) overwrites the packed arrays: an older plan
+        // in the workspace goes stale
+        if (d.outputs && bad == kNone && !no_fit) hdr->epoch = d.epoch;
+        if ((d.outputs & kOutNew) && bad == kNone && !no_fit) d.lbase[d.ngroups] = total.cnt;
+    }
+    if (bad != kNone || no_fit) return;  // invalid table or nothing to plan: write nothing
+    const Window w = window_of(d.win);
+    const uint64_t base = g * d.chunk;
+    const uint64_t end = umin64(base + d.chunk, n);
+    const bool tiles = (d.outputs & kOutNew) != 0;
+    if (tiles && threadIdx.x == 0) d.lbase[g] = before.cnt;
+    const uint64_t Ta = d.tiles.a, Tb = d.tiles.b;
+    Agg carry = before;
     uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, min_dst = kNone, min_size = kNone;
-    uint64_t min_fit = kNone, small_moved = 0;
+    uint64_t min_fit = kNone, small_moved = 0, ca = 0, wa = 0, cb = 0, wb = 0;
     for (uint64_t s0 = base; s0 < end; s0 += kScanTile) {
         const uint64_t i0 = s0 + (uint64_t)threadIdx.x * kScanItems;
         uint64_t o[kScanItems], s[kScanItems];
@@ -305,7 +437,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
             l[k] = 0;
             p[k] = 0;
             f[k] = 0;
-            if (i < t.n) {
+            if (i < n) {
                 o[k] = t.off[i];
                 s[k] = t.size[i];
                 l[k] = live_of(t, i) ? 1u : 0u;
@@ -314,18 +446,19 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
                 a = combine(a, element(o[k], s[k], l[k], p[k], f[k]));
             }
         }
-        Agg total;
-        const Agg ex = block_excl<kScanThreads>(a, total, sh);
+        Agg tot;
+        const Agg ex = block_excl<kScanThreads>(a, tot, sh);
         Agg run = combine(carry, ex);
-        carry = combine(carry, total);
+        carry = combine(carry, tot);
 #pragma unroll
         for (uint32_t k = 0; k < kScanItems; ++k) {
             const uint64_t i = i0 + k;
-            if (i < t.n) {
+            if (i < n) {
                 const uint64_t nw = f[k] ? o[k] : run.v;
-                if ((outputs & kOutNew) && new_offset) new_offset[i] = nw;
+                if ((d.outputs & kOutNew) && d.new_offset) d.new_offset[i] = nw;
                 if (l[k]) {
-                    if (outputs & kOutNew) {
+                    const LiveOut &lo = d.lo;
+                    if (d.outputs & kOutNew) {
                         lo.dst[run.cnt] = nw;
                         lo.pin[run.cnt] = (uint8_t)p[k];
                         if (lo.ent)
@@ -339,11 +472,11 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
                             lo.rec[run.cnt] = LiveRec{o[k] + s[k], o[k] - nw};
                         if (lo.key) lo.key[run.cnt] = (uint32_t)(o[k] & lo.key_mask);
                     }
-                    if (outputs & (kOutNew | kOutSelect)) {
+                    if (d.outputs & (kOutNew | kOutSelect)) {
                         lo.src[run.cnt] = o[k];
                         lo.size[run.cnt] = s[k];
                     }
-                    if (outputs & kOutSelect) {
+                    if (d.outputs & kOutSelect) {
                         lo.z[run.cnt] = run.lsum;
                         lo.pc[run.cnt] = (uint32_t)run.pcnt;
                     }
@@ -351,13 +484,21 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
                     if (gap) {
                         gaps += 1;
                         max_gap = umax64(max_gap, gap);
-                        if (gap >= fit_need) min_fit = umin64(min_fit, run.mx);
+                        if (gap >= d.fit_need) min_fit = umin64(min_fit, run.mx);
                     }
                     if (o[k] != nw) {
                         moved += 1;
                         moved_bytes += s[k];
                         min_dst = umin64(min_dst, nw);
                         if (o[k] - nw < kAutoSmallShift) small_moved += s[k];
+                        if (tiles) {
+                            // the live block before this one moved: the run goes on
+                            const bool start = !(run.cnt > 0 && run.v != run.mx);
+                            ca += tiles_of(nw, s[k], start, Ta);
+                            wa += whole_of(nw, s[k], Ta);
+                            cb += tiles_of(nw, s[k], start, Tb);
+                            wb += whole_of(nw, s[k], Tb);
+                        }
                     }
                     min_size = umin64(min_size, s[k]);
                 }
@@ -365,47 +506,47 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(TableView t, const u
             }
         }
     }  // steps of the chunk
-    max_gap = block_reduce<kScanThreads>(max_gap, shr, OpMax());
-    gaps = block_reduce<kScanThreads>(gaps, shr, OpAdd());
-    moved = block_reduce<kScanThreads>(moved, shr, OpAdd());
-    moved_bytes = block_reduce<kScanThreads>(moved_bytes, shr, OpAdd());
-    min_dst = block_reduce<kScanThreads>(min_dst, shr, OpMin());
-    min_size = block_reduce<kScanThreads>(min_size, shr, OpMin());
-    min_fit = block_reduce<kScanThreads>(min_fit, shr, OpMin());
-    small_moved = block_reduce<kScanThreads>(small_moved, shr, OpAdd());
-    if (threadIdx.x == 0)
-        spart[blockIdx.x] =
-            StatPart{max_gap, gaps, moved, moved_bytes, min_dst, min_size, min_fit, small_moved};
+    StatPart q{max_gap, gaps, moved, moved_bytes, min_dst, min_size, min_fit, small_moved};
+    uint64_t x[4] = {ca, wa, cb, wb};
+    block_reduce_stats<kScanThreads>(q, x, s_red);
+    if (threadIdx.x == 0) {
+        d.spart[g] = q;
+        if (tiles) {
+            d.tpart[g] = x[0];
+            d.twhole[g] = x[1];
+            d.tpart[kMaxScanParts + g] = x[2];
+            d.twhole[kMaxScanParts + g] = x[3];
+        }
+    }
 }
 
-// Pass 4 (one workgroup): reduce the statistics, add the tail hole.  A plan
-// runs it inside the launch after the scan (k_after_scan); a statistics pass
-// alone launches it by itself.
-__device__ void scan_finish(const StatPart *spart, uint64_t nb, uint64_t arena_bytes,
-                            WsHeader *hdr, int outputs, uint64_t epoch, uint64_t fit_need) {
-    __shared__ uint64_t sh[kSpineThreads / 64];
-    if (plan_dead(hdr)) return;
-    uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, min_dst = kNone, min_size = kNone;
-    uint64_t min_fit = kNone, small_moved = 0;
-    for (uint64_t j = threadIdx.x; j < nb; j += kSpineThreads) {
+// The statistics of all workgroups, reduced by one workgroup (the tail hole
+// added) into the header; with `plan`, the plan's mover fields are reset too.
+// x: up to four sums more (e.g. whole-tile counts), reduced alongside.
+__device__ void stats_finish(const StatPart *spart, uint64_t nb, uint64_t arena_bytes,
+                             WsHeader *hdr, bool plan, uint64_t fit_need,
+                             const uint64_t *xsrc = nullptr, uint64_t *xsum = nullptr) {
+    __shared__ uint64_t sh[12 * (kScanThreads / 64)];
+    StatPart a{0, 0, 0, 0, kNone, kNone, kNone, 0};
+    uint64_t x[4] = {0, 0, 0, 0};
+    for (uint64_t j = threadIdx.x; j < nb; j += kScanThreads) {
         const StatPart q = spart[j];
-        small_moved += q.small_moved;
-        min_fit = umin64(min_fit, q.min_fit);
-        max_gap = umax64(max_gap, q.max_gap);
-        gaps += q.gaps;
-        moved += q.moved_blocks;
-        moved_bytes += q.moved_bytes;
-        min_dst = umin64(min_dst, q.min_moved_dst);
-        min_size = umin64(min_size, q.min_size);
+        a.small_moved += q.small_moved;
+        a.min_fit = umin64(a.min_fit, q.min_fit);
+        a.max_gap = umax64(a.max_gap, q.max_gap);
+        a.gaps += q.gaps;
+        a.moved_blocks += q.moved_blocks;
+        a.moved_bytes += q.moved_bytes;
+        a.min_moved_dst = umin64(a.min_moved_dst, q.min_moved_dst);
+        a.min_size = umin64(a.min_size, q.min_size);
+        if (xsrc) x[0] += xsrc[j];
     }
-    max_gap = block_reduce<kSpineThreads>(max_gap, sh, OpMax());
-    gaps = block_reduce<kSpineThreads>(gaps, sh, OpAdd());
-    moved = block_reduce<kSpineThreads>(moved, sh, OpAdd());
-    moved_bytes = block_reduce<kSpineThreads>(moved_bytes, sh, OpAdd());
-    min_dst = block_reduce<kSpineThreads>(min_dst, sh, OpMin());
-    min_size = block_reduce<kSpineThreads>(min_size, sh, OpMin());
-    min_fit = block_reduce<kSpineThreads>(min_fit, sh, OpMin());
-    small_moved = block_reduce<kSpineThreads>(small_moved, sh, OpAdd());
+    block_reduce_stats<kScanThreads>(a, x, sh);
+    if (xsum) *xsum = x[0];
+    const uint64_t max_gap = a.max_gap, gaps = a.gaps, moved = a.moved_blocks,
+                   moved_bytes = a.moved_bytes, min_dst = a.min_moved_dst, min_size = a.min_size,
+                   small_moved = a.small_moved;
+    uint64_t min_fit = a.min_fit;
     if (threadIdx.x == 0) {
         const uint64_t tail = arena_bytes - hdr->max_live_end;
         // holes below live blocks come first in address order; the tail last
@@ -418,9 +559,7 @@ __device__ void scan_finish(const StatPart *spart, uint64_t nb, uint64_t arena_b
         hdr->small_moved = small_moved;
         hdr->min_live_size = min_size;
         hdr->move_begin = min_dst;
-        // plan fields: a statistics-only pass leaves an existing plan intact
-        if (outputs) {
-            hdr->epoch = epoch;
+        if (plan) {
             hdr->ticket = 0;
             hdr->status = 0;
             hdr->late_tiles = 0;
@@ -430,18 +569,21 @@ __device__ void scan_finish(const StatPart *spart, uint64_t nb, uint64_t arena_b
     }
 }
 
-__global__ __launch_bounds__(kSpineThreads) void k_scan_finish(const StatPart *spart, uint64_t nb,
-                                                               uint64_t arena_bytes, WsHeader *hdr,
-                                                               int outputs, uint64_t epoch,
-                                                               uint64_t fit_need) {
-    scan_finish(spart, nb, arena_bytes, hdr, outputs, epoch, fit_need);
+// Pass 3 of a statistics pass (one workgroup): its finish.
+__global__ __launch_bounds__(kScanThreads) void k_scan_finish(const StatPart *spart, uint64_t nb,
+                                                              uint64_t arena_bytes, WsHeader *hdr,
+                                                              uint64_t fit_need, TableView t) {
+    uint64_t n;
+    if (!table_entries(t, &n)) return;  // a gated table whose plan failed
+    if (plan_dead(hdr)) return;
+    stats_finish(spart, nb, arena_bytes, hdr, false, fit_need);
 }
 
 // ---------------------------------------------------------------------------
 // Tiles.  A run is a maximal sequence of moved live blocks; its destinations
 // are contiguous (packed inside one segment).  Its tiles are the pieces of it
 // inside each tile-size window: one starts at the run's first byte, and one at
-// every multiple of T inside the run.
+// every multiple of T inside it.
 
 __device__ inline bool moved_at(const LiveView &lv, uint64_t k) { return lv.src[k] != lv.dst[k]; }
 
@@ -449,63 +591,16 @@ __device__ inline bool moved_at(const LiveView &lv, uint64_t k) { return lv.src[
 __device__ inline uint64_t tiles_in_block(const LiveView &lv, uint64_t k, uint64_t T) {
     if (!moved_at(lv, k)) return 0;
     const bool start = (k == 0) || !moved_at(lv, k - 1);
-    const uint64_t a = lv.dst[k], b = a + lv.size[k];
-    const uint64_t mult = (b + T - 1) / T - (a + T - 1) / T;  // multiples of T in [a, b)
-    return mult + ((start && (a & (T - 1))) ? 1 : 0);
-}
-
-// Whole windows [cT, cT + T) inside moved block k: each is one tile holding
-// that block alone (the mover's straight-line case).
-__device__ inline uint64_t whole_in_block(const LiveView &lv, uint64_t k, uint64_t T) {
-    if (!moved_at(lv, k)) return 0;
-    const uint64_t a = lv.dst[k], b = a + lv.size[k];
-    const uint64_t lo = (a + T - 1) / T, hi = b / T;
-    return hi > lo ? hi - lo : 0;
-}
-
-// Pass 5: per-workgroup tile counts (and whole-window counts) over the live
-// blocks, for both tile-size candidates (tpart[blk], tpart[kMaxScanParts +
-// blk]); workgroup blk covers live blocks [blk * chunk, (blk + 1) * chunk).
-__device__ void tcount_partial(LiveView lv, const WsHeader *hdr, TileChoice tc, uint64_t *tpart,
-                               uint64_t *twhole, uint64_t blk, uint64_t chunk) {
-    __shared__ uint64_t sh[kScanThreads / 64];
-    if (plan_dead(hdr)) return;
-    const uint64_t m = hdr->live_blocks;
-    const uint64_t end = umin64((blk + 1) * chunk, m);
-    uint64_t ca = 0, wa = 0, cb = 0, wb = 0;
-    for (uint64_t k0 = blk * chunk + (uint64_t)threadIdx.x * kScanItems; k0 < end;
-         k0 += kScanTile) {
-#pragma unroll
-        for (uint32_t j = 0; j < kScanItems; ++j) {
-            if (k0 + j < end) {
-                ca += tiles_in_block(lv, k0 + j, tc.a);
-                wa += whole_in_block(lv, k0 + j, tc.a);
-                cb += tiles_in_block(lv, k0 + j, tc.b);
-                wb += whole_in_block(lv, k0 + j, tc.b);
-            }
-        }
-    }
-    ca = block_reduce<kScanThreads>(ca, sh, OpAdd());
-    wa = block_reduce<kScanThreads>(wa, sh, OpAdd());
-    cb = block_reduce<kScanThreads>(cb, sh, OpAdd());
-    wb = block_reduce<kScanThreads>(wb, sh, OpAdd());
-    if (threadIdx.x == 0) {
-        tpart[blk] = ca;
-        twhole[blk] = wa;
-        tpart[kMaxScanParts + blk] = cb;
-        twhole[kMaxScanParts + blk] = wb;
-    }
+    return tiles_of(lv.dst[k], lv.size[k], start, T);
 }
 
 // The remap's bucket index: ridx[b] = number of live blocks whose old offset
 // is below b << w, for b in [0, nb]; one lane per entry, a binary search over
-// the packed old offsets (workgroup blk covers entries [256 blk, ...)).  A
-// failed plan leaves it alone.
-__device__ void remap_index_part(const uint64_t *__restrict__ live_src, const WsHeader *hdr,
-                                 uint32_t w, uint64_t nb, uint32_t *ridx, uint64_t blk) {
+// the packed old offsets (workgroup blk covers entries [256 blk, ...)).
+__device__ void remap_index_part(const uint64_t *__restrict__ live_src, uint64_t m, uint32_t w,
+                                 uint64_t nb, uint32_t *ridx, uint64_t blk) {
     const uint64_t b = blk * kScanThreads + threadIdx.x;
-    if (b > nb || plan_dead(hdr)) return;
-    const uint64_t m = hdr->live_blocks;
+    if (b > nb) return;
     const uint64_t x = b << w;
     uint64_t lo = 0, len = m;  // first k with src[k] >= x
     while (len > 0) {
@@ -520,100 +615,83 @@ __device__ void remap_index_part(const uint64_t *__restrict__ live_src, const Ws
     ridx[b] = (uint32_t)lo;
 }
 
-// After a plan's scan, three jobs that read only what the scan wrote and
-// write disjoint outputs, in one launch (two dependent launches fewer):
-// workgroups [0, gnb) count tiles (pass 5), the next rblocks build the
-// remap index, and the last one reduces the statistics (pass 4).
-struct AfterScan {
+struct BaseArgs {
     LiveView lv;
+    const uint64_t *tpart, *twhole, *lbase;
+    const StatPart *spart;
+    uint64_t nb;
     TileChoice tiles;
-    uint64_t *tpart, *twhole;
-    uint64_t gnb;
-    uint64_t chunk;     // live blocks per counting workgroup
+    uint64_t max_tiles;
+    uint32_t *tile_base;
     uint32_t *ridx;
     uint32_t rw;        // remap bucket width (log2 bytes)
     uint64_t rnb;       // remap buckets
-    uint64_t rblocks;   // workgroups building the index
-    const StatPart *spart;
-    uint64_t nb;        // scan workgroups
     uint64_t arena_bytes;
-    int outputs;
-    uint64_t epoch;
-    uint64_t fit_need;
+    WsHeader *hdr;
 };
-static_assert(kSpineThreads == kScanThreads, "the finish runs as one workgroup of the fused launch");
-__global__ __launch_bounds__(kScanThreads) void k_after_scan(AfterScan a, WsHeader *hdr) {
-    const uint64_t blk = blockIdx.x;
-    if (blk < a.gnb) {
-        tcount_partial(a.lv, hdr, a.tiles, a.tpart, a.twhole, blk, a.chunk);
-    } else if (blk < a.gnb + a.rblocks) {
-        remap_index_part(a.lv.src, hdr, a.rw, a.rnb, a.ridx, blk - a.gnb);
-    } else {
-        scan_finish(a.spart, a.nb, a.arena_bytes, hdr, a.outputs, a.epoch, a.fit_need);
-    }
-}
 
-// Pass 6 (one workgroup): the tile size, then the exclusive scan of its
-// counts; n_tiles.  With two candidates the larger is taken when most moved
-// bytes shift by less than kAutoSmallShift and enough bytes move -- or when
-// the smaller's tiles would not fit the workspace and the larger's do.
-__global__ __launch_bounds__(kSpineThreads) void k_tcount_spine(const uint64_t *tpart,
-                                                                const uint64_t *twhole,
-                                                                uint64_t *tprefix, uint64_t nb,
-                                                                WsHeader *hdr, TileChoice tc,
-                                                                uint64_t max_tiles) {
-    __shared__ uint64_t sh[kSpineThreads / 64];
-    if (plan_dead(hdr)) return;
-    uint64_t na = 0, nbt = 0;
-    for (uint64_t j = threadIdx.x; j < nb; j += kSpineThreads) {
-        na += tpart[j];
-        nbt += tpart[kMaxScanParts + j];
-    }
-    na = block_reduce<kSpineThreads>(na, sh, OpAdd());
-    nbt = block_reduce<kSpineThreads>(nbt, sh, OpAdd());
-    const uint64_t moved = hdr->moved_bytes;
-    bool pick_b = tc.a != tc.b && hdr->small_moved * 2 > moved && moved >= kAutoMinMoved;
-    if (tc.a != tc.b && (pick_b ? nbt : na) > max_tiles && (pick_b ? na : nbt) <= max_tiles)
-        pick_b = !pick_b;
-    const uint64_t off = pick_b ? kMaxScanParts : 0;
-    uint64_t carry = 0, whole = 0;
-    for (uint64_t j = threadIdx.x; j < nb; j += kSpineThreads) whole += twhole[off + j];
-    whole = block_reduce<kSpineThreads>(whole, sh, OpAdd());
-    for (uint64_t base = 0; base < nb; base += kSpineThreads) {
-        const uint64_t j = base + threadIdx.x;
-        const uint64_t x = j < nb ? tpart[off + j] : 0;
-        uint64_t total;
-        const uint64_t ex = block_excl_sum<kSpineThreads>(x, total, sh);
-        if (j < nb) tprefix[j] = carry + ex;
-        carry += total;
-    }
-    if (threadIdx.x == 0) {
-        hdr->n_tiles = carry;
-        hdr->whole_tiles = whole;
-        hdr->tile_bytes = pick_b ? tc.b : tc.a;
-    }
-}
-
-// Pass 7: each live block's first tile index (a block with no tile gets the
-// same index as the next block that has one, so tile t belongs to the last
-// block whose first tile index is <= t).
-__global__ __launch_bounds__(kScanThreads) void k_tcount_down(LiveView lv, const WsHeader *hdr,
-                                                              const uint64_t *tprefix,
-                                                              uint32_t *tile_base, uint64_t chunk) {
+// Pass 3 of a plan.  Workgroups [0, nb): the tile size (every workgroup
+// decides it the same way, from the same totals: the larger candidate when
+// most moved bytes shift by less than kAutoSmallShift and enough bytes move,
+// or when the smaller's tiles would not fit the workspace and the larger's
+// do), then each of its live blocks' first tile index -- a block with no
+// tile gets the index of the next tile that starts, so tile t belongs to the
+// last block whose first index is <= t.  Workgroup 0 also finishes the
+// header: statistics, tile count and size, the mover's fields.  The
+// workgroups after them build the remap's bucket index.
+__global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
     __shared__ uint64_t sh[kScanThreads / 64];
+    __shared__ uint64_t s_red[12 * (kScanThreads / 64)];
+    __shared__ uint64_t s_before;
+    WsHeader *hdr = a.hdr;
     if (plan_dead(hdr)) return;
+    const uint64_t g = blockIdx.x;
     const uint64_t m = hdr->live_blocks;
-    const uint64_t T = hdr->tile_bytes;
-    const uint64_t base = (uint64_t)blockIdx.x * chunk;
-    const uint64_t end = umin64(base + chunk, m);
-    uint64_t carry = tprefix[blockIdx.x];
-    for (uint64_t s0 = base; s0 < end; s0 += kScanTile) {
+    if (g >= a.nb) {
+        remap_index_part(a.lv.src, m, a.rw, a.rnb, a.ridx, g - a.nb);
+        return;
+    }
+    uint64_t moved = 0, small = 0;
+    for (uint64_t j = threadIdx.x; j < a.nb; j += kScanThreads) {
+        moved += a.spart[j].moved_bytes;
+        small += a.spart[j].small_moved;
+    }
+    {
+        StatPart q{0, 0, 0, 0, kNone, kNone, kNone, 0};
+        uint64_t x[4] = {moved, small, 0, 0};
+        block_reduce_stats<kScanThreads>(q, x, s_red);
+        moved = x[0];
+        small = x[1];
+    }
+    uint64_t pa, na, pb, nbt;
+    sums_prefix(a.tpart, a.nb, g, sh, &s_before, pa, na);
+    sums_prefix(a.tpart + kMaxScanParts, a.nb, g, sh, &s_before, pb, nbt);
+    const TileChoice tc = a.tiles;
+    bool pick_b = tc.a != tc.b && small * 2 > moved && moved >= kAutoMinMoved;
+    if (tc.a != tc.b && (pick_b ? nbt : na) > a.max_tiles && (pick_b ? na : nbt) <= a.max_tiles)
+        pick_b = !pick_b;
+    const uint64_t T = pick_b ? tc.b : tc.a;
+    const uint64_t n_tiles = pick_b ? nbt : na;
+    if (g == 0) {
+        uint64_t whole = 0;
+        stats_finish(a.spart, a.nb, a.arena_bytes, hdr, true, kNone,
+                     a.twhole + (pick_b ? kMaxScanParts : 0), &whole);
+        if (threadIdx.x == 0) {
+            hdr->n_tiles = n_tiles;
+            hdr->whole_tiles = whole;
+            hdr->tile_bytes = T;
+        }
+    }
+    if (n_tiles > a.max_tiles) return;  // the plan fails (the header says so)
+    const uint64_t k_begin = a.lbase[g], k_end = a.lbase[g + 1];
+    uint64_t carry = pick_b ? pb : pa;
+    for (uint64_t s0 = k_begin; s0 < k_end; s0 += kScanTile) {
         const uint64_t k0 = s0 + (uint64_t)threadIdx.x * kScanItems;
         uint64_t c[kScanItems];
         uint64_t sum = 0;
 #pragma unroll
         for (uint32_t j = 0; j < kScanItems; ++j) {
-            c[j] = (k0 + j < end) ? tiles_in_block(lv, k0 + j, T) : 0;
+            c[j] = (k0 + j < k_end) ? tiles_in_block(a.lv, k0 + j, T) : 0;
             sum += c[j];
         }
         uint64_t total;
@@ -621,7 +699,7 @@ __global__ __launch_bounds__(kScanThreads) void k_tcount_down(LiveView lv, const
         carry += total;
 #pragma unroll
         for (uint32_t j = 0; j < kScanItems; ++j) {
-            if (k0 + j < end) tile_base[k0 + j] = (uint32_t)run;
+            if (k0 + j < k_end) a.tile_base[k0 + j] = (uint32_t)run;
             run += c[j];
         }
     }
@@ -639,22 +717,17 @@ __device__ inline int64_t last_le(const T *a, int64_t lo, int64_t hi, uint64_t x
     return l - 1;
 }
 
-// Pass 8: one lane per tile writes its start and its first block.
-__global__ __launch_bounds__(256) void k_tile_starts(LiveView lv, const uint32_t *tile_base,
-                                                     const WsHeader *hdr, uint64_t max_tiles,
-                                                     uint64_t *tile_start, uint32_t *tile_first) {
-    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (plan_dead(hdr) || hdr->n_tiles > max_tiles) return;  // plan fails
-    const uint64_t n_tiles = hdr->n_tiles, m = hdr->live_blocks, T = hdr->tile_bytes;
-    if (t >= n_tiles) return;
+// Where tile t starts, and its first block.
+__device__ inline uint64_t tile_start(const LiveView &lv, const uint32_t *tile_base, uint64_t m,
+                                      uint64_t t, uint64_t T, uint64_t *first) {
     const int64_t k = last_le(tile_base, 0, (int64_t)m, t);
     const uint64_t j = t - tile_base[k];
     const uint64_t a = lv.dst[k];
     const bool start = (k == 0) || !moved_at(lv, (uint64_t)k - 1);
     const uint64_t lead = (start && (a & (T - 1))) ? 1 : 0;
     const uint64_t first_mult = (a + T - 1) & ~(T - 1);
-    tile_start[t] = (j < lead) ? a : first_mult + (j - lead) * T;
-    tile_first[t] = (uint32_t)k;
+    *first = (uint64_t)k;
+    return (j < lead) ? a : first_mult + (j - lead) * T;
 }
 
 // The tile holding destination byte q of moved block b (tiles cut each run
@@ -671,27 +744,25 @@ __device__ inline uint64_t tile_of(const LiveView &lv, const uint32_t *tile_base
     return lead ? tile_base[b] : tile_base[b] - 1;
 }
 
-// Pass 9: one lane per tile.  [t0, t1) = the run's bytes from the tile start
+// Pass 4: one lane per tile.  [t0, t1) = the run's bytes from the tile start
 // up to the next tile start, the window end or the run end.  A tile may write
 // only once every tile whose sources overlap [t0, t1) has read them.  Sources
 // rise strictly with destinations (src = dst + shift, shifts never negative,
 // order kept), so the destinations whose sources lie in [t0, t1) are at most
 // t1 - t0 consecutive live bytes, all at or below [t0, t1): their tiles are a
 // short range ending at or before this one.
-__global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile_start,
-                                               const uint32_t *tile_first,
-                                               const uint32_t *tile_base, const WsHeader *hdr,
-                                               uint64_t max_tiles,
+__global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint32_t *tile_base,
+                                               const WsHeader *hdr, uint64_t max_tiles,
                                                const uint32_t *ridx, uint32_t w, TileRec *tiles,
                                                uint32_t *flags) {
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (plan_dead(hdr) || hdr->n_tiles > max_tiles) return;  // plan fails
     const uint64_t n_tiles = hdr->n_tiles, m = hdr->live_blocks, T = hdr->tile_bytes;
     if (t >= n_tiles) return;
-    const uint64_t t0 = tile_start[t];
+    uint64_t first, next_first;
+    const uint64_t t0 = tile_start(lv, tile_base, m, t, T, &first);
     uint64_t bound = (t0 & ~(T - 1)) + T;
-    if (t + 1 < n_tiles) bound = umin64(bound, tile_start[t + 1]);
-    const uint64_t first = tile_first[t];
+    if (t + 1 < n_tiles) bound = umin64(bound, tile_start(lv, tile_base, m, t + 1, T, &next_first));
     // last block of the run inside [t0, bound): blocks after first that start
     // below bound and moved form a prefix -- gallop, then bisect
     uint64_t last = first, stride = 1;
@@ -742,7 +813,13 @@ __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint64_t *tile
 }
 
 __global__ void k_commit(LiveView lv, uint64_t m, uint64_t *off_out, uint64_t *size_out,
-                         uint8_t *live_out, uint8_t *pinned_out) {
+                         uint8_t *live_out, uint8_t *pinned_out, const WsHeader *gate,
+                         uint64_t max_tiles, uint64_t *zero) {
+    if (zero && blockIdx.x == 0 && threadIdx.x == 0) *zero = 0;
+    if (gate) {  // queued before the plan was read back: its count, if it did not fail
+        if (plan_failed(gate, max_tiles)) return;
+        m = gate->live_blocks < m ? gate->live_blocks : m;
+    }
     for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < m;
          k += (uint64_t)gridDim.x * blockDim.x) {
         if (off_out) off_out[k] = lv.dst[k];
@@ -896,99 +973,91 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
                 uint64_t epoch, uint64_t fit_need, hipStream_t s) {
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.header);
     ScanPart *part = reinterpret_cast<ScanPart *>(ws + L.part);
-    ScanPart *prefix = reinterpret_cast<ScanPart *>(ws + L.prefix);
     StatPart *spart = reinterpret_cast<StatPart *>(ws + L.spart);
-    LiveOut lo{reinterpret_cast<uint64_t *>(ws + L.live_dst),
-               reinterpret_cast<uint64_t *>(ws + L.live_src),
-               reinterpret_cast<uint64_t *>(ws + L.live_size),
-               reinterpret_cast<uint8_t *>(ws + L.live_pin),
-               reinterpret_cast<uint64_t *>(ws + L.live_z),
-               reinterpret_cast<uint32_t *>(ws + L.live_pc),
-               nullptr, nullptr, nullptr, nullptr, 0};
+    DownArgs d{};
+    d.t = t;
+    d.win = win;
+    d.part = part;
+    d.nb = L.n_scan_blocks;
+    d.ngroups = d.nb ? d.nb : 1;
+    d.chunk = L.scan_chunk;
+    d.hdr = hdr;
+    d.new_offset = new_offset;
+    d.lo = LiveOut{reinterpret_cast<uint64_t *>(ws + L.live_dst),
+                   reinterpret_cast<uint64_t *>(ws + L.live_src),
+                   reinterpret_cast<uint64_t *>(ws + L.live_size),
+                   reinterpret_cast<uint8_t *>(ws + L.live_pin),
+                   reinterpret_cast<uint64_t *>(ws + L.live_z),
+                   reinterpret_cast<uint32_t *>(ws + L.live_pc),
+                   nullptr, nullptr, nullptr, nullptr, 0};
     if (remap_ent(arena_bytes, t.n)) {
-        lo.ent = reinterpret_cast<RemapEnt *>(ws + L.live_rec);
-        lo.key_mask = (1ull << remap_shift(arena_bytes, t.n)) - 1;
+        d.lo.ent = reinterpret_cast<RemapEnt *>(ws + L.live_rec);
+        d.lo.key_mask = (1ull << remap_shift(arena_bytes, t.n)) - 1;
     } else if (remap_rec32(arena_bytes)) {
-        lo.rec32 = reinterpret_cast<LiveRec32 *>(ws + L.live_rec);
+        d.lo.rec32 = reinterpret_cast<LiveRec32 *>(ws + L.live_rec);
     } else {
-        lo.rec = reinterpret_cast<LiveRec *>(ws + L.live_rec);
+        d.lo.rec = reinterpret_cast<LiveRec *>(ws + L.live_rec);
     }
-    if (!lo.ent && remap_keys32(arena_bytes, t.n)) {
-        lo.key = reinterpret_cast<uint32_t *>(ws + L.live_key);
-        lo.key_mask = (1ull << remap_shift(arena_bytes, t.n)) - 1;
+    if (!d.lo.ent && remap_keys32(arena_bytes, t.n)) {
+        d.lo.key = reinterpret_cast<uint32_t *>(ws + L.live_key);
+        d.lo.key_mask = (1ull << remap_shift(arena_bytes, t.n)) - 1;
     }
-    const uint64_t nb = L.n_scan_blocks;
-    if (nb) {
-        hipLaunchKernelGGL(k_scan_partials, dim3((uint32_t)nb), dim3(kScanThreads), 0, s, t,
+    d.spart = spart;
+    d.tpart = reinterpret_cast<uint64_t *>(ws + L.tpart);
+    d.twhole = reinterpret_cast<uint64_t *>(ws + L.twhole);
+    d.lbase = reinterpret_cast<uint64_t *>(ws + L.lbase);
+    d.tiles = tiles;
+    d.outputs = outputs;
+    d.fit_need = fit_need;
+    d.epoch = epoch;
+    // pass 1: aggregates
+    if (d.nb) {
+        hipLaunchKernelGGL(k_scan_partials, dim3((uint32_t)d.nb), dim3(kScanThreads), 0, s, t,
                            arena_bytes, win, (uint64_t)L.scan_chunk, part);
         AC_TRY(hipGetLastError());
     }
-    hipLaunchKernelGGL(k_scan_spine, dim3(1), dim3(kSpineThreads), 0, s, part, prefix, nb, hdr,
-                       win ? 0 : 1);
+    // pass 2: each workgroup's prefix, then its entries
+    hipLaunchKernelGGL(k_scan_down, dim3((uint32_t)d.ngroups), dim3(kScanThreads), 0, s, d);
     AC_TRY(hipGetLastError());
-    if (nb) {
-        hipLaunchKernelGGL(k_scan_down, dim3((uint32_t)nb), dim3(kScanThreads), 0, s, t, win,
-                           prefix, hdr, new_offset, lo, spart, outputs, fit_need,
-                           (uint64_t)L.scan_chunk);
-        AC_TRY(hipGetLastError());
+    if (outputs == 0) {  // a statistics pass: its finish
+        hipLaunchKernelGGL(k_scan_finish, dim3(1), dim3(kScanThreads), 0, s, spart, d.nb,
+                           arena_bytes, hdr, fit_need, t);
+        return hipGetLastError();
     }
-    if (!(outputs & kOutNew)) {
-        hipLaunchKernelGGL(k_scan_finish, dim3(1), dim3(kSpineThreads), 0, s, spart, nb,
-                           arena_bytes, hdr, outputs, epoch, fit_need);
+    if (!(outputs & kOutNew)) return hipSuccess;  // a selection scan: nothing more
+    // pass 3: tile size, the blocks' first tiles and the header's finish;
+    // the remap index beside them
+    const LiveView lv = live_view(ws, L);
+    uint32_t *ridx = reinterpret_cast<uint32_t *>(ws + L.ridx);
+    uint32_t *tile_base = reinterpret_cast<uint32_t *>(ws + L.tile_base);
+    BaseArgs b{};
+    b.lv = lv;
+    b.tpart = d.tpart;
+    b.twhole = d.twhole;
+    b.lbase = d.lbase;
+    b.spart = spart;
+    b.nb = d.ngroups;
+    b.tiles = tiles;
+    b.max_tiles = L.max_tiles;
+    b.tile_base = tile_base;
+    b.ridx = ridx;
+    b.rw = remap_shift(arena_bytes, t.n);
+    b.rnb = remap_buckets(arena_bytes, t.n);
+    b.arena_bytes = arena_bytes;
+    b.hdr = hdr;
+    const uint64_t rblocks = (b.rnb + 1 + kScanThreads - 1) / kScanThreads;
+    hipLaunchKernelGGL(k_plan_bases, dim3((uint32_t)(d.ngroups + rblocks)), dim3(kScanThreads), 0,
+                       s, b);
+    AC_TRY(hipGetLastError());
+    // pass 4: the tile records, a grid for the whole capacity (each lane
+    // checks the device-side tile count: no host round trip)
+    TileRec *trec = reinterpret_cast<TileRec *>(ws + L.tiles);
+    uint32_t *flags = reinterpret_cast<uint32_t *>(ws + L.flags);
+    const uint64_t grid = (L.max_tiles + 255) / 256;
+    if (grid) {
+        hipLaunchKernelGGL(k_tiles, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_base, hdr,
+                           L.max_tiles, ridx, b.rw, trec, flags);
         AC_TRY(hipGetLastError());
-    }
-    if (outputs & kOutNew) {
-        const LiveView lv = live_view(ws, L);
-        uint64_t *tpart = reinterpret_cast<uint64_t *>(ws + L.tpart);
-        uint64_t *tprefix = reinterpret_cast<uint64_t *>(ws + L.tprefix);
-        uint64_t *twhole = reinterpret_cast<uint64_t *>(ws + L.twhole);
-        uint32_t *tile_base = reinterpret_cast<uint32_t *>(ws + L.tile_base);
-        const uint64_t gnb = nb ? nb : 1;  // live blocks <= entries
-        // tile counts, the remap's bucket index (the tile records use it
-        // too) and the statistics finish, in one launch
-        uint32_t *ridx = reinterpret_cast<uint32_t *>(ws + L.ridx);
-        AfterScan as{};
-        as.lv = lv;
-        as.tiles = tiles;
-        as.tpart = tpart;
-        as.twhole = twhole;
-        as.gnb = gnb;
-        as.chunk = L.scan_chunk;
-        as.ridx = ridx;
-        as.rw = remap_shift(arena_bytes, t.n);
-        as.rnb = remap_buckets(arena_bytes, t.n);
-        as.rblocks = (as.rnb + 1 + kScanThreads - 1) / kScanThreads;
-        as.spart = spart;
-        as.nb = nb;
-        as.arena_bytes = arena_bytes;
-        as.outputs = outputs;
-        as.epoch = epoch;
-        as.fit_need = fit_need;
-        hipLaunchKernelGGL(k_after_scan, dim3((uint32_t)(gnb + as.rblocks + 1)),
-                           dim3(kScanThreads), 0, s, as, hdr);
-        AC_TRY(hipGetLastError());
-        hipLaunchKernelGGL(k_tcount_spine, dim3(1), dim3(kSpineThreads), 0, s, tpart, twhole,
-                           tprefix, gnb, hdr, tiles, (uint64_t)L.max_tiles);
-        AC_TRY(hipGetLastError());
-        hipLaunchKernelGGL(k_tcount_down, dim3((uint32_t)gnb), dim3(kScanThreads), 0, s, lv, hdr,
-                           tprefix, tile_base, (uint64_t)L.scan_chunk);
-        AC_TRY(hipGetLastError());
-        // tile starts and records: a grid for the whole capacity, each lane
-        // checks the device-side tile count (no host round trip)
-        uint64_t *tile_start = reinterpret_cast<uint64_t *>(ws + L.tile_start);
-        uint32_t *tile_first = reinterpret_cast<uint32_t *>(ws + L.tile_first);
-        TileRec *trec = reinterpret_cast<TileRec *>(ws + L.tiles);
-        uint32_t *flags = reinterpret_cast<uint32_t *>(ws + L.flags);
-        const uint64_t grid = (L.max_tiles + 255) / 256;
-        if (grid) {
-            hipLaunchKernelGGL(k_tile_starts, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_base,
-                               hdr, L.max_tiles, tile_start, tile_first);
-            AC_TRY(hipGetLastError());
-            hipLaunchKernelGGL(k_tiles, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_start,
-                               tile_first, tile_base, hdr, L.max_tiles,
-                               ridx, remap_shift(arena_bytes, t.n), trec, flags);
-            AC_TRY(hipGetLastError());
-        }
     }
     return hipSuccess;
 }
@@ -1026,12 +1095,15 @@ hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t re
 
 hipError_t launch_commit(const uint8_t *ws, const WsLayout &L, uint64_t live_blocks,
                          uint64_t *off_out, uint64_t *size_out, uint8_t *live_out,
-                         uint8_t *pinned_out, hipStream_t s) {
-    if (live_blocks == 0) return hipSuccess;
+                         uint8_t *pinned_out, const WsHeader *gate, uint64_t max_tiles,
+                         uint64_t *zero, hipStream_t s) {
+    if (live_blocks == 0 && !zero) return hipSuccess;
     uint64_t grid = (live_blocks + 255) / 256;
     if (grid > 4096) grid = 4096;
+    if (grid < 1) grid = 1;
     hipLaunchKernelGGL(k_commit, dim3((uint32_t)grid), dim3(256), 0, s, live_view(ws, L),
-                       live_blocks, off_out, size_out, live_out, pinned_out);
+                       live_blocks, off_out, size_out, live_out, pinned_out, gate, max_tiles,
+                       zero);
     return hipGetLastError();
 }
 

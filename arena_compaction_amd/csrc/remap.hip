@@ -43,7 +43,12 @@ __global__ __launch_bounds__(kRemapThreads) void k_remap(const void *__restrict_
                                                          const uint32_t *__restrict__ ridx,
                                                          uint32_t w, uint64_t nb, uint64_t m,
                                                          const uint64_t *h_in, uint64_t *h_out,
-                                                         uint64_t H, unsigned long long *n_invalid) {
+                                                         uint64_t H, unsigned long long *n_invalid,
+                                                         const WsHeader *gate, uint64_t max_tiles) {
+    if (gate) {  // queued before the plan was read back: its count, if it did not fail
+        if (plan_failed(gate, max_tiles)) return;
+        m = gate->live_blocks;
+    }
     uint64_t bad = 0;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < H; k += stride) {
@@ -104,7 +109,13 @@ __global__ __launch_bounds__(kRemapThreads) void k_remap_ent(const RemapEnt *__r
                                                              uint32_t w, uint64_t nb, uint64_t m,
                                                              const uint64_t *h_in, uint64_t *h_out,
                                                              uint64_t H,
-                                                             unsigned long long *n_invalid) {
+                                                             unsigned long long *n_invalid,
+                                                             const WsHeader *gate,
+                                                             uint64_t max_tiles) {
+    if (gate) {  // queued before the plan was read back: its count, if it did not fail
+        if (plan_failed(gate, max_tiles)) return;
+        m = gate->live_blocks;
+    }
     uint64_t bad = 0;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < H; k += stride) {
@@ -157,8 +168,9 @@ hipError_t launch_remap(const void *rec, const uint64_t *live_src, const uint32_
                         const uint32_t *ridx,
                         uint64_t arena_bytes, uint64_t n, uint64_t live_blocks,
                         const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
-                        uint64_t *n_invalid, int num_cus, hipStream_t s) {
-    if (n_invalid) {
+                        uint64_t *n_invalid, const WsHeader *gate, uint64_t max_tiles,
+                        int num_cus, hipStream_t s) {
+    if (n_invalid && !gate) {
         hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, n_invalid);
         AC_TRY(hipGetLastError());
     }
@@ -173,13 +185,15 @@ hipError_t launch_remap(const void *rec, const uint64_t *live_src, const uint32_
     if (remap_ent(arena_bytes, n))
         hipLaunchKernelGGL(k_remap_ent, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s,
                            static_cast<const RemapEnt *>(rec), ridx, w, nb, live_blocks, h_in,
-                           h_out, n_handles, bad);
+                           h_out, n_handles, bad, gate, max_tiles);
     else if (remap_rec32(arena_bytes))
         hipLaunchKernelGGL(k_remap<true>, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s, rec,
-                           live_src, k32, ridx, w, nb, live_blocks, h_in, h_out, n_handles, bad);
+                           live_src, k32, ridx, w, nb, live_blocks, h_in, h_out, n_handles, bad,
+                           gate, max_tiles);
     else
         hipLaunchKernelGGL(k_remap<false>, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s, rec,
-                           live_src, k32, ridx, w, nb, live_blocks, h_in, h_out, n_handles, bad);
+                           live_src, k32, ridx, w, nb, live_blocks, h_in, h_out, n_handles, bad,
+                           gate, max_tiles);
     return hipGetLastError();
 }
 
