@@ -163,7 +163,8 @@ int stats_pass(const defrag_table *table, uint64_t arena_bytes, uint64_t fit_nee
     // the statistics header (the second 256 bytes): a plan the workspace
     // holds keeps its own header
     L.header = L.post;
-    if (launch_scan(view_of(table), arena_bytes, ws, L, nullptr, 0, TileChoice{kDefaultTile, kDefaultTile}, 0, fit_need,
+    if (launch_scan(view_of(table), arena_bytes, ws, L, nullptr, 0,
+                    TileChoice{kDefaultTile, kDefaultTile}, 0, fit_need, nullptr,
                     stream) != hipSuccess)
         return DEFRAG_EHIP;
     rc = read_header(h, ws, L, stream);
@@ -192,7 +193,7 @@ int post_check_queue(const defrag_table *packed, uint64_t arena_bytes, void *ws_
     v.gate = gate;
     v.gate_max_tiles = max_tiles;
     return launch_scan(v, arena_bytes, ws, L, nullptr, 0,
-                       TileChoice{kDefaultTile, kDefaultTile}, 0, kNone,
+                       TileChoice{kDefaultTile, kDefaultTile}, 0, kNone, nullptr,
                        stream) == hipSuccess
                ? DEFRAG_OK
                : DEFRAG_EHIP;
@@ -242,9 +243,11 @@ struct PlanCtx {
 
 // Full plan (request == 0) or targeted plan (request > 0): check the
 // arguments and queue every pass.  Nothing is read back.
+// clear: a word the plan's last scan pass sets to zero, or null.
 int plan_queue(const defrag_table *table, uint64_t arena_bytes, uint64_t request,
                const defrag_tuning *tuning, void *ws_dev, size_t ws_bytes, hipStream_t stream,
-               uint64_t *new_offset_dev, defrag_plan_t *plan, PlanCtx *c) {
+               uint64_t *new_offset_dev, defrag_plan_t *plan, PlanCtx *c,
+               uint64_t *clear = nullptr) {
     if (!plan) return DEFRAG_EINVAL;
     std::memset(plan, 0, sizeof(*plan));
     defrag_tuning tu{};
@@ -278,9 +281,9 @@ int plan_queue(const defrag_table *table, uint64_t arena_bytes, uint64_t request
     c->epoch = g_epoch.fetch_add(0x9E3779B97F4A7C15ull) ^ reinterpret_cast<uintptr_t>(ws);
     const hipError_t e =
         request ? launch_targeted(view_of(table), arena_bytes, request, ws, c->L, new_offset_dev,
-                                  c->tiles, c->epoch, stream)
+                                  c->tiles, c->epoch, clear, stream)
                 : launch_scan(view_of(table), arena_bytes, ws, c->L, new_offset_dev, kOutNew,
-                              c->tiles, c->epoch, kNone, stream);
+                              c->tiles, c->epoch, kNone, clear, stream);
     return e == hipSuccess ? DEFRAG_OK : DEFRAG_EHIP;
 }
 
@@ -558,12 +561,8 @@ int defrag_remap(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes,
     if (cus <= 0) return DEFRAG_EHIP;
     const WsLayout L = plan_layout(plan);
     const uint8_t *ws = static_cast<const uint8_t *>(ws_dev);
-    if (launch_remap(ws + L.live_rec,
-                     reinterpret_cast<const uint64_t *>(ws + L.live_src),
-                     reinterpret_cast<const uint32_t *>(ws + L.live_key),
-                     reinterpret_cast<const uint32_t *>(ws + L.ridx), plan->arena_bytes, plan->n,
-                     plan->live_blocks, h_in_dev, h_out_dev, n_handles, n_invalid_dev, nullptr,
-                     0, cus, stream) != hipSuccess)
+    if (launch_remap(ws, L, plan->arena_bytes, plan->n, plan->live_blocks, h_in_dev, h_out_dev,
+                     n_handles, n_invalid_dev, nullptr, nullptr, 0, cus, stream) != hipSuccess)
         return DEFRAG_EHIP;
     return DEFRAG_OK;
 }
@@ -575,8 +574,7 @@ int defrag_commit(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes
     if (rc) return rc;
     const WsLayout L = plan_layout(plan);
     if (launch_commit(static_cast<const uint8_t *>(ws_dev), L, plan->live_blocks, offset_out_dev,
-                      size_out_dev, live_out_dev, pinned_out_dev, nullptr, 0, nullptr,
-                      stream) != hipSuccess)
+                      size_out_dev, live_out_dev, pinned_out_dev, stream) != hipSuccess)
         return DEFRAG_EHIP;
     return DEFRAG_OK;
 }
@@ -604,9 +602,11 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     const bool post_ok = !after_host || (a->offset_out_dev && a->size_out_dev);
     const bool wg_ok = !a->tuning || a->tuning->wg_per_cu != 0;
     if (!(arena_ok && post_ok && wg_ok)) return compact_serial(a, stream, plan, after_host);
+    // the plan clears the invalid-handle count: the remap's launch then
+    // only adds to it
     PlanCtx c;
     int rc = plan_queue(a->table, a->arena_bytes, a->request_bytes, a->tuning, a->ws_dev,
-                        a->ws_bytes, stream, a->new_offset_dev, plan, &c);
+                        a->ws_bytes, stream, a->new_offset_dev, plan, &c, a->n_invalid_dev);
     if (rc) return rc;
     const int cus = num_cus_of(c.dev);
     hipStream_t side = a->side_stream ? a->side_stream : side_stream_of(c.dev);
@@ -636,14 +636,15 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     m.stall_sleeps = c.tu.stall_sleeps;
     m.stall_seed = c.tu.stall_seed;
     // with the tile size left to the plan, a mover for each candidate: the
-    // one whose size the plan did not choose leaves at once.  Below
-    // kAutoMinMoved arena bytes the plan keeps the smaller size unless its
-    // tiles overflow the workspace, which the bound rules out here.
+    // one whose size the plan did not choose leaves at once.  In an arena
+    // of at most kAutoMinMoved bytes fewer bytes than that move (a moved
+    // block has a hole below it), so the plan keeps the smaller size unless
+    // its tiles overflow the workspace, which the bound rules out here.
     MoveArgs mb = m;
     mb.tile_bytes = c.tiles.b;
     mb.max_blocks = c.tiles.b / 32 + 2;
     const bool one_mover =
-        c.tiles.a == c.tiles.b || (a->arena_bytes < kAutoMinMoved &&
+        c.tiles.a == c.tiles.b || (a->arena_bytes <= kAutoMinMoved &&
                                    tiles_bound(a->arena_bytes, n, c.tiles.a) <= c.L.max_tiles);
     const bool want_remap = a->n_handles || a->n_invalid_dev;
     const bool want_commit =
@@ -662,17 +663,13 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     if (ok && side_work) {
         ok = hipStreamWaitEvent(side, planned, 0) == hipSuccess;
         side_queued = ok;
-        // the commit (with the invalid-handle count's reset) first: the
-        // post-check reads the packed table
-        if (ok && (want_commit || a->n_invalid_dev))
-            ok = launch_commit(ws, c.L, n, a->offset_out_dev, a->size_out_dev, a->live_out_dev,
-                               a->pinned_out_dev, gate, c.L.max_tiles, a->n_invalid_dev,
-                               side) == hipSuccess;
-        if (ok && a->n_handles)
-            ok = launch_remap(ws + c.L.live_rec, reinterpret_cast<const uint64_t *>(ws + c.L.live_src),
-                              reinterpret_cast<const uint32_t *>(ws + c.L.live_key),
-                              reinterpret_cast<const uint32_t *>(ws + c.L.ridx), a->arena_bytes, n,
-                              n, a->h_in_dev, a->h_out_dev, a->n_handles, a->n_invalid_dev, gate,
+        // remap and commit in one launch, before the post-check, which
+        // reads the packed table
+        const CommitOut out{a->offset_out_dev, a->size_out_dev, a->live_out_dev,
+                            a->pinned_out_dev};
+        if (ok && (want_commit || a->n_handles))
+            ok = launch_remap(ws, c.L, a->arena_bytes, n, n, a->h_in_dev, a->h_out_dev,
+                              a->n_handles, a->n_invalid_dev, want_commit ? &out : nullptr, gate,
                               c.L.max_tiles, cus, side) == hipSuccess;
         if (ok && after_host) {
             const defrag_table packed{a->offset_out_dev, a->size_out_dev, a->live_out_dev, n,

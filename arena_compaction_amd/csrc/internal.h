@@ -101,7 +101,10 @@ struct alignas(256) WsHeader {
     uint64_t polls;
     uint64_t tile_bytes;     // the plan's tile size (chosen on the device when auto)
     uint64_t small_moved;    // moved bytes whose shift is below kAutoSmallShift
-    uint64_t pad[6];
+    // statistics passes: down-sweep workgroups done (cleared by the
+    // aggregates pass); the last one to finish completes the header
+    uint64_t arrive;
+    uint64_t pad[5];
 };
 static_assert(sizeof(WsHeader) == 256, "header size");
 
@@ -337,8 +340,11 @@ struct TableView {
 
 // Whether the plan whose header this is failed: an invalid table, no window
 // for a targeted request, or more tiles than the workspace holds.
+// (Every field is loaded before any is tested: one memory round trip, not
+// one per field.)
 __device__ inline bool plan_failed(const WsHeader *h, uint64_t max_tiles) {
-    return h->bad_key != kNone || h->win_state == kWinNoFit || h->n_tiles > max_tiles;
+    const uint64_t bad = h->bad_key, win = h->win_state, nt = h->n_tiles;
+    return (bad != kNone) | (win == kWinNoFit) | (nt > max_tiles);
 }
 // Entries of a table, and whether a pass over it may run (gate above).
 __device__ inline bool table_entries(const TableView &t, uint64_t *n) {
@@ -346,8 +352,9 @@ __device__ inline bool table_entries(const TableView &t, uint64_t *n) {
         *n = t.n;
         return true;
     }
+    const uint64_t m = t.gate->live_blocks;
     if (plan_failed(t.gate, t.gate_max_tiles)) return false;
-    *n = t.gate->live_blocks < t.n ? t.gate->live_blocks : t.n;
+    *n = m < t.n ? m : t.n;
     return true;
 }
 
@@ -380,23 +387,22 @@ inline LiveView live_view(const uint8_t *ws, const WsLayout &L) {
 // L.max_tiles tiles).  All asynchronous; the header then holds totals,
 // statistics and n_tiles (tiles are built only if n_tiles <= L.max_tiles).
 // fit_need: a hole size to first-fit (header fit_offset), kNone for none.
+// clear: a word a plan's last scan pass sets to zero (the one-call path's
+// invalid-handle count, so that its remap needs no launch of its own for
+// it), or null.
 hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws,
                        const WsLayout &L, uint64_t *new_offset, int outputs,
-                       TileChoice tiles, uint64_t epoch, uint64_t fit_need, hipStream_t s);
+                       TileChoice tiles, uint64_t epoch, uint64_t fit_need, uint64_t *clear,
+                       hipStream_t s);
 // Targeted plan: a selection scan, the window search (header win_*), then
 // the plan scan with every live block outside the window held in place.
 // Nothing is planned (and new_offset is not written) when no window fits.
 hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t request,
                            uint8_t *ws, const WsLayout &L, uint64_t *new_offset,
-                           TileChoice tiles, uint64_t epoch, hipStream_t s);
-// gate (the one-call path, queued before the plan is read back): the plan's
-// header gives the live-block count (live_blocks is then the most there can
-// be) and nothing is written if the plan failed; zero: a counter to clear
-// (the remap's invalid count) once the plan is known good.
+                           TileChoice tiles, uint64_t epoch, uint64_t *clear, hipStream_t s);
 hipError_t launch_commit(const uint8_t *ws, const WsLayout &L, uint64_t live_blocks,
                          uint64_t *off_out, uint64_t *size_out, uint8_t *live_out,
-                         uint8_t *pinned_out, const WsHeader *gate, uint64_t max_tiles,
-                         uint64_t *zero, hipStream_t s);
+                         uint8_t *pinned_out, hipStream_t s);
 
 // ---- move.hip ----
 struct MoveArgs {
@@ -443,14 +449,23 @@ int compact_serial(const struct defrag_compact_args *a, hipStream_t stream,
                    struct defrag_plan_t *plan, struct defrag_stats_t *after_host);
 
 // ---- remap.hip ----
-// gate: as launch_commit (the count of invalid handles is then taken as
-// cleared already: see launch_commit's zero).
-hipError_t launch_remap(const void *rec, const uint64_t *live_src, const uint32_t *key,
-                        const uint32_t *ridx,
-                        uint64_t arena_bytes, uint64_t n, uint64_t live_blocks,
-                        const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
-                        uint64_t *n_invalid, const WsHeader *gate, uint64_t max_tiles,
-                        int num_cus, hipStream_t s);
+// The packed table's outputs (defrag_commit's); a null pointer is not written.
+struct CommitOut {
+    uint64_t *off;
+    uint64_t *size;
+    uint8_t *live;
+    uint8_t *pinned;
+};
+// Remap n_handles handles through the plan in the workspace (n: the planned
+// table's entries).  commit: also write the packed table, in the same
+// launch.  gate (the one-call path, queued before the plan is read back):
+// the plan's header gives the live-block count (live_blocks is then the
+// most there can be), nothing is written if the plan failed, and n_invalid
+// is taken as cleared already (the plan's last pass clears it).
+hipError_t launch_remap(const uint8_t *ws, const WsLayout &L, uint64_t arena_bytes, uint64_t n,
+                        uint64_t live_blocks, const uint64_t *h_in, uint64_t *h_out,
+                        uint64_t n_handles, uint64_t *n_invalid, const CommitOut *commit,
+                        const WsHeader *gate, uint64_t max_tiles, int num_cus, hipStream_t s);
 
 }  // namespace ac
 

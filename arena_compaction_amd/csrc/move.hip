@@ -152,23 +152,29 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
         // (the status query sees the epoch mismatch); nor when the records
         // failed their check
         uint32_t tk = 0xFFFFFFFFu;
-        uint64_t nt = a.n_tiles;
-        if (__hip_atomic_load(&a.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch &&
-            (a.hdr->status & (kStatusCorrupt | kStatusCapacity)) == 0u) {
-            bool go = true;
-            if (a.device_sized) {
-                // the plan's results, read here instead of on the host: a
-                // failed plan (invalid table, no window, too many tiles)
-                // moves nothing, nor does the mover of a tile size the plan
-                // did not choose; workgroups past the chosen count leave
-                const WsHeader *h = a.hdr;
-                nt = h->n_tiles;
-                const uint32_t per_cu = a.wg_per_cu ? a.wg_per_cu : kDefaultWgPerCu;
-                go = h->bad_key == kNone && h->win_state != kWinNoFit && nt <= a.max_tiles &&
-                     h->tile_bytes == a.tile_bytes && blockIdx.x < (uint64_t)per_cu * a.num_cus;
-            }
-            if (go) tk = atomicAdd(&a.hdr->ticket, 1u);
+        const WsHeader *h = a.hdr;
+        // every header field needed here is loaded before any is tested:
+        // one memory round trip in front of the first claim, not one per field
+        const uint64_t ep = __hip_atomic_load(&h->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t st = h->status;
+        uint64_t nt = a.n_tiles, bad = kNone, win = kWinNone, tb = a.tile_bytes;
+        if (a.device_sized) {
+            nt = h->n_tiles;
+            bad = h->bad_key;
+            win = h->win_state;
+            tb = h->tile_bytes;
         }
+        bool go = (ep == a.epoch) & ((st & (kStatusCorrupt | kStatusCapacity)) == 0u);
+        if (a.device_sized) {
+            // the plan's results, read here instead of on the host: a
+            // failed plan (invalid table, no window, too many tiles)
+            // moves nothing, nor does the mover of a tile size the plan
+            // did not choose; workgroups past the chosen count leave
+            const uint32_t per_cu = a.wg_per_cu ? a.wg_per_cu : kDefaultWgPerCu;
+            go = go & (bad == kNone) & (win != kWinNoFit) & (nt <= a.max_tiles) &
+                 (tb == a.tile_bytes) & (blockIdx.x < (uint64_t)per_cu * a.num_cus);
+        }
+        if (go) tk = atomicAdd(&a.hdr->ticket, 1u);
         s_ticket = tk;
         s_ntiles = nt;
     }

@@ -22,16 +22,17 @@
 // merges adjacent free blocks, section 2.2), so one pass over live entries in
 // order sees every hole once, plus the tail above the highest live block.
 //
-// Passes (n up to 2^32 entries), each a wide launch -- the one-workgroup
-// spines are gone: every workgroup of a pass scans the (at most 1,024)
-// per-workgroup results of the pass before it for its own prefix.
+// Passes (n up to 2^32 entries), each a wide launch with no one-workgroup
+// pass between them: every workgroup of a pass scans the (at most 1,024)
+// per-workgroup results of the pass before it for its own prefix, since
+// each dependent launch costs several microseconds of dispatch.
 //   1. per-workgroup aggregates (and the first bad entry);
 //   2. each workgroup's prefix, then its entries: new offsets, the packed
 //      live-block arrays (new and old offset, size, pinned flag, the remap's
 //      records), hole and move statistics, and the tiles its moved blocks
 //      start, counted for both candidate tile sizes; workgroup 0 writes the
-//      table's totals (a statistics pass then ends with a one-workgroup
-//      finish);
+//      table's totals; in a statistics pass the last workgroup to finish
+//      completes the header, which ends the pass;
 //   3. (plans) each workgroup picks the tile size from the totals, the same
 //      way, and gives each of its live blocks its first tile index;
 //      workgroup 0 finishes the header (statistics, tile count and size,
@@ -245,18 +246,22 @@ __device__ inline uint32_t stays(uint64_t o, uint32_t l, uint32_t p, const Windo
 
 // Nothing more to plan: the table is invalid, or no window fits the request.
 __device__ inline bool plan_dead(const WsHeader *hdr) {
-    return hdr->bad_key != kNone || hdr->win_state == kWinNoFit;
+    const uint64_t bad = hdr->bad_key, win = hdr->win_state;  // both loads, then the tests
+    return (bad != kNone) | (win == kWinNoFit);
 }
 
 // Pass 1: per-workgroup aggregate and first bad key.  Workgroup g takes the
 // entries [g * chunk, (g + 1) * chunk), kScanTile at a time.
 __global__ __launch_bounds__(kScanThreads) void k_scan_partials(TableView t, uint64_t arena_bytes,
                                                                 const uint64_t *win,
-                                                                uint64_t chunk, ScanPart *part) {
+                                                                uint64_t chunk, ScanPart *part,
+                                                                uint64_t *arrive) {
     __shared__ Agg sh[kScanThreads / 64];
     __shared__ uint64_t shr[kScanThreads / 64];
     uint64_t n;
     if (!table_entries(t, &n)) return;  // a gated table whose plan failed
+    // a statistics pass: the down-sweep counts its finished workgroups
+    if (arrive && blockIdx.x == 0 && threadIdx.x == 0) *arrive = 0;
     const Window w = window_of(win);
     const uint64_t base = (uint64_t)blockIdx.x * chunk;
     const uint64_t end = umin64(base + chunk, n);
@@ -317,16 +322,18 @@ __device__ void parts_prefix(const ScanPart *part, uint64_t nb, uint64_t g, Agg 
 }
 
 // The same for sums of u64 (tile counts): the sum below g and the total.
-__device__ void sums_prefix(const uint64_t *x, uint64_t nb, uint64_t g, uint64_t *sh,
+// v: this thread's values x[threadIdx.x * kPartsPer + k] (0 past the end),
+// loaded by the caller.
+constexpr uint32_t kPartsPer = kMaxScanParts / kScanThreads;
+__device__ void sums_prefix(const uint64_t (&v)[kPartsPer], uint64_t g, uint64_t *sh,
                             uint64_t *s_before, uint64_t &before, uint64_t &total) {
-    constexpr uint32_t kPer = kMaxScanParts / kScanThreads;
+    constexpr uint32_t kPer = kPartsPer;
     const uint64_t j0 = (uint64_t)threadIdx.x * kPer;
     uint64_t loc = 0, upto = 0;
 #pragma unroll
     for (uint32_t k = 0; k < kPer; ++k) {
-        const uint64_t j = j0 + k;
-        if (j == g) upto = loc;
-        if (j < nb) loc += x[j];
+        if (j0 + k == g) upto = loc;
+        loc += v[k];
     }
     const uint64_t ex = block_excl_sum<kScanThreads>(loc, total, sh);
     if (g >= j0 && g < j0 + kPer) *s_before = ex + upto;
@@ -350,16 +357,69 @@ struct LiveOut {
 // Tiles a run of moved blocks starts in one live block: at the run's first
 // byte (if not on a window boundary) and at every multiple of T inside it.
 // a: new offset, s: size, start: the block opens a run.
+// T is a power of two: x / T is a shift.
+__device__ inline uint64_t div_tile(uint64_t x, uint64_t T) { return x >> __builtin_ctzll(T); }
+
 __device__ inline uint64_t tiles_of(uint64_t a, uint64_t s, bool start, uint64_t T) {
     const uint64_t b = a + s;
-    const uint64_t mult = (b + T - 1) / T - (a + T - 1) / T;  // multiples of T in [a, b)
+    const uint64_t mult = div_tile(b + T - 1, T) - div_tile(a + T - 1, T);  // multiples of T in [a, b)
     return mult + ((start && (a & (T - 1))) ? 1 : 0);
 }
 // Whole windows [cT, cT + T) inside a moved block: each is one tile of that
 // block alone.
 __device__ inline uint64_t whole_of(uint64_t a, uint64_t s, uint64_t T) {
-    const uint64_t lo = (a + T - 1) / T, hi = (a + s) / T;
+    const uint64_t lo = div_tile(a + T - 1, T), hi = div_tile(a + s, T);
     return hi > lo ? hi - lo : 0;
+}
+
+// The statistics of all workgroups, reduced by one workgroup (the tail hole
+// added) into the header; with `plan`, the plan's mover fields are reset too.
+// x: up to four sums more (e.g. whole-tile counts), reduced alongside.
+// max_end: the highest live end (the header's max_live_end).
+__device__ void stats_finish(const StatPart *spart, uint64_t nb, uint64_t arena_bytes,
+                             uint64_t max_end, WsHeader *hdr, bool plan, uint64_t fit_need,
+                             const uint64_t *xsrc = nullptr, uint64_t *xsum = nullptr) {
+    __shared__ uint64_t sh[12 * (kScanThreads / 64)];
+    StatPart a{0, 0, 0, 0, kNone, kNone, kNone, 0};
+    uint64_t x[4] = {0, 0, 0, 0};
+    for (uint64_t j = threadIdx.x; j < nb; j += kScanThreads) {
+        const StatPart q = spart[j];
+        a.small_moved += q.small_moved;
+        a.min_fit = umin64(a.min_fit, q.min_fit);
+        a.max_gap = umax64(a.max_gap, q.max_gap);
+        a.gaps += q.gaps;
+        a.moved_blocks += q.moved_blocks;
+        a.moved_bytes += q.moved_bytes;
+        a.min_moved_dst = umin64(a.min_moved_dst, q.min_moved_dst);
+        a.min_size = umin64(a.min_size, q.min_size);
+        if (xsrc) x[0] += xsrc[j];
+    }
+    block_reduce_stats<kScanThreads>(a, x, sh);
+    if (xsum) *xsum = x[0];
+    const uint64_t max_gap = a.max_gap, gaps = a.gaps, moved = a.moved_blocks,
+                   moved_bytes = a.moved_bytes, min_dst = a.min_moved_dst, min_size = a.min_size,
+                   small_moved = a.small_moved;
+    uint64_t min_fit = a.min_fit;
+    if (threadIdx.x == 0) {
+        const uint64_t tail = arena_bytes - max_end;
+        // holes below live blocks come first in address order; the tail last
+        if (min_fit == kNone && tail && tail >= fit_need) min_fit = max_end;
+        hdr->fit_offset = min_fit;
+        hdr->largest_hole = umax64(max_gap, tail);
+        hdr->hole_count = gaps + (tail ? 1 : 0);
+        hdr->moved_blocks = moved;
+        hdr->moved_bytes = moved_bytes;
+        hdr->small_moved = small_moved;
+        hdr->min_live_size = min_size;
+        hdr->move_begin = min_dst;
+        if (plan) {
+            hdr->ticket = 0;
+            hdr->status = 0;
+            hdr->late_tiles = 0;
+            hdr->waited_tiles = 0;
+            hdr->polls = 0;
+        }
+    }
 }
 
 struct DownArgs {
@@ -376,18 +436,25 @@ struct DownArgs {
     uint64_t *tpart, *twhole;  // tile counts per workgroup, both candidates (plans)
     uint64_t *lbase;           // live blocks below each workgroup's entries (plans; ngroups + 1)
     TileChoice tiles;
-    int outputs;
     uint64_t fit_need;
     uint64_t epoch;
+    uint64_t arena_bytes;
 };
 
 // Pass 2: the workgroup's prefix (from the aggregates), then its entries in
 // order: new offsets, the packed live arrays, hole and move statistics, and
 // (plans) the tiles its moved blocks start, for both tile-size candidates.
 // Workgroup 0 writes the table's totals and validity to the header.  An
-// invalid table writes nothing else.  The block before a live entry moved
+// invalid table writes nothing else.  In a statistics pass the last
+// workgroup to finish reduces every workgroup's statistics into the header
+// (a count of finished workgroups, cleared by pass 1, tells it that it is
+// the last; its fence and atomic make the others' results visible to it).  The block before a live entry moved
 // iff the packed position after it differs from its end (a block that stays,
 // pinned or held, resets the position to its own end).
+// OUT: the pass's outputs (0: a statistics pass; kOutNew: a plan;
+// kOutSelect: a selection scan), fixed per instantiation so that each holds
+// only its own code.
+template <int OUT>
 __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
     __shared__ Agg sh[kScanThreads / 64];
     __shared__ uint64_t shr[kScanThreads / 64];
@@ -397,6 +464,30 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
     const uint64_t g = blockIdx.x;
     uint64_t n;
     if (!table_entries(t, &n)) return;  // a gated table whose plan failed
+    const uint64_t base = g * d.chunk;
+    const uint64_t end = umin64(base + d.chunk, n);
+    uint64_t o[kScanItems], s[kScanItems];
+    uint32_t l[kScanItems], p[kScanItems];
+    const auto load = [&](uint64_t s0) {
+        const uint64_t i0 = s0 + (uint64_t)threadIdx.x * kScanItems;
+#pragma unroll
+        for (uint32_t k = 0; k < kScanItems; ++k) {
+            const uint64_t i = i0 + k;
+            o[k] = 0;
+            s[k] = 0;
+            l[k] = 0;
+            p[k] = 0;
+            if (i < n) {
+                o[k] = t.off[i];
+                s[k] = t.size[i];
+                l[k] = live_of(t, i) ? 1u : 0u;
+                p[k] = pin_of(t, i) ? 1u : 0u;
+            }
+        }
+    };
+    // the first step's entries are requested before the prefix's aggregates,
+    // so that the two loads overlap
+    if (base < end) load(base);
     Agg before, total;
     uint64_t bad;
     parts_prefix(d.part, d.nb, g, sh, shr, &s_before, before, total, bad);
@@ -411,37 +502,27 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
         if (!d.win) hdr->win_state = kWinNone;
         // a plan (or a selection) overwrites the packed arrays: an older plan
         // in the workspace goes stale
-        if (d.outputs && bad == kNone && !no_fit) hdr->epoch = d.epoch;
-        if ((d.outputs & kOutNew) && bad == kNone && !no_fit) d.lbase[d.ngroups] = total.cnt;
+        if (OUT && bad == kNone && !no_fit) hdr->epoch = d.epoch;
+        if ((OUT & kOutNew) && bad == kNone && !no_fit) d.lbase[d.ngroups] = total.cnt;
     }
     if (bad != kNone || no_fit) return;  // invalid table or nothing to plan: write nothing
     const Window w = window_of(d.win);
-    const uint64_t base = g * d.chunk;
-    const uint64_t end = umin64(base + d.chunk, n);
-    const bool tiles = (d.outputs & kOutNew) != 0;
+    constexpr bool tiles = (OUT & kOutNew) != 0;
     if (tiles && threadIdx.x == 0) d.lbase[g] = before.cnt;
     const uint64_t Ta = d.tiles.a, Tb = d.tiles.b;
     Agg carry = before;
     uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, min_dst = kNone, min_size = kNone;
     uint64_t min_fit = kNone, small_moved = 0, ca = 0, wa = 0, cb = 0, wb = 0;
     for (uint64_t s0 = base; s0 < end; s0 += kScanTile) {
+        if (s0 != base) load(s0);
         const uint64_t i0 = s0 + (uint64_t)threadIdx.x * kScanItems;
-        uint64_t o[kScanItems], s[kScanItems];
-        uint32_t l[kScanItems], p[kScanItems], f[kScanItems];
+        uint32_t f[kScanItems];
         Agg a = agg_zero();
 #pragma unroll
         for (uint32_t k = 0; k < kScanItems; ++k) {
             const uint64_t i = i0 + k;
-            o[k] = 0;
-            s[k] = 0;
-            l[k] = 0;
-            p[k] = 0;
             f[k] = 0;
             if (i < n) {
-                o[k] = t.off[i];
-                s[k] = t.size[i];
-                l[k] = live_of(t, i) ? 1u : 0u;
-                p[k] = pin_of(t, i) ? 1u : 0u;
                 f[k] = stays(o[k], l[k], p[k], w);
                 a = combine(a, element(o[k], s[k], l[k], p[k], f[k]));
             }
@@ -455,10 +536,10 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
             const uint64_t i = i0 + k;
             if (i < n) {
                 const uint64_t nw = f[k] ? o[k] : run.v;
-                if ((d.outputs & kOutNew) && d.new_offset) d.new_offset[i] = nw;
+                if ((OUT & kOutNew) && d.new_offset) d.new_offset[i] = nw;
                 if (l[k]) {
                     const LiveOut &lo = d.lo;
-                    if (d.outputs & kOutNew) {
+                    if constexpr ((OUT & kOutNew) != 0) {
                         lo.dst[run.cnt] = nw;
                         lo.pin[run.cnt] = (uint8_t)p[k];
                         if (lo.ent)
@@ -472,11 +553,11 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
                             lo.rec[run.cnt] = LiveRec{o[k] + s[k], o[k] - nw};
                         if (lo.key) lo.key[run.cnt] = (uint32_t)(o[k] & lo.key_mask);
                     }
-                    if (d.outputs & (kOutNew | kOutSelect)) {
+                    if constexpr ((OUT & (kOutNew | kOutSelect)) != 0) {
                         lo.src[run.cnt] = o[k];
                         lo.size[run.cnt] = s[k];
                     }
-                    if (d.outputs & kOutSelect) {
+                    if constexpr ((OUT & kOutSelect) != 0) {
                         lo.z[run.cnt] = run.lsum;
                         lo.pc[run.cnt] = (uint32_t)run.pcnt;
                     }
@@ -518,66 +599,25 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
             d.twhole[kMaxScanParts + g] = x[3];
         }
     }
-}
-
-// The statistics of all workgroups, reduced by one workgroup (the tail hole
-// added) into the header; with `plan`, the plan's mover fields are reset too.
-// x: up to four sums more (e.g. whole-tile counts), reduced alongside.
-__device__ void stats_finish(const StatPart *spart, uint64_t nb, uint64_t arena_bytes,
-                             WsHeader *hdr, bool plan, uint64_t fit_need,
-                             const uint64_t *xsrc = nullptr, uint64_t *xsum = nullptr) {
-    __shared__ uint64_t sh[12 * (kScanThreads / 64)];
-    StatPart a{0, 0, 0, 0, kNone, kNone, kNone, 0};
-    uint64_t x[4] = {0, 0, 0, 0};
-    for (uint64_t j = threadIdx.x; j < nb; j += kScanThreads) {
-        const StatPart q = spart[j];
-        a.small_moved += q.small_moved;
-        a.min_fit = umin64(a.min_fit, q.min_fit);
-        a.max_gap = umax64(a.max_gap, q.max_gap);
-        a.gaps += q.gaps;
-        a.moved_blocks += q.moved_blocks;
-        a.moved_bytes += q.moved_bytes;
-        a.min_moved_dst = umin64(a.min_moved_dst, q.min_moved_dst);
-        a.min_size = umin64(a.min_size, q.min_size);
-        if (xsrc) x[0] += xsrc[j];
-    }
-    block_reduce_stats<kScanThreads>(a, x, sh);
-    if (xsum) *xsum = x[0];
-    const uint64_t max_gap = a.max_gap, gaps = a.gaps, moved = a.moved_blocks,
-                   moved_bytes = a.moved_bytes, min_dst = a.min_moved_dst, min_size = a.min_size,
-                   small_moved = a.small_moved;
-    uint64_t min_fit = a.min_fit;
-    if (threadIdx.x == 0) {
-        const uint64_t tail = arena_bytes - hdr->max_live_end;
-        // holes below live blocks come first in address order; the tail last
-        if (min_fit == kNone && tail && tail >= fit_need) min_fit = hdr->max_live_end;
-        hdr->fit_offset = min_fit;
-        hdr->largest_hole = umax64(max_gap, tail);
-        hdr->hole_count = gaps + (tail ? 1 : 0);
-        hdr->moved_blocks = moved;
-        hdr->moved_bytes = moved_bytes;
-        hdr->small_moved = small_moved;
-        hdr->min_live_size = min_size;
-        hdr->move_begin = min_dst;
-        if (plan) {
-            hdr->ticket = 0;
-            hdr->status = 0;
-            hdr->late_tiles = 0;
-            hdr->waited_tiles = 0;
-            hdr->polls = 0;
+    if constexpr (OUT == 0) {  // a statistics pass
+        __shared__ uint32_t s_last;
+        if (threadIdx.x == 0) {
+            uint32_t last = 1;
+            if (d.ngroups > 1) {
+                __threadfence();  // this workgroup's statistics before its arrival
+                const uint64_t done = __hip_atomic_fetch_add(&d.hdr->arrive, 1ull, __ATOMIC_ACQ_REL,
+                                                             __HIP_MEMORY_SCOPE_AGENT);
+                last = done + 1 == d.ngroups;
+                __threadfence();
+            }
+            s_last = last;
         }
+        __syncthreads();
+        if (s_last)
+            stats_finish(d.spart, d.nb, d.arena_bytes, total.mx, d.hdr, false, d.fit_need);
     }
 }
 
-// Pass 3 of a statistics pass (one workgroup): its finish.
-__global__ __launch_bounds__(kScanThreads) void k_scan_finish(const StatPart *spart, uint64_t nb,
-                                                              uint64_t arena_bytes, WsHeader *hdr,
-                                                              uint64_t fit_need, TableView t) {
-    uint64_t n;
-    if (!table_entries(t, &n)) return;  // a gated table whose plan failed
-    if (plan_dead(hdr)) return;
-    stats_finish(spart, nb, arena_bytes, hdr, false, fit_need);
-}
 
 // ---------------------------------------------------------------------------
 // Tiles.  A run is a maximal sequence of moved live blocks; its destinations
@@ -596,23 +636,54 @@ __device__ inline uint64_t tiles_in_block(const LiveView &lv, uint64_t k, uint64
 
 // The remap's bucket index: ridx[b] = number of live blocks whose old offset
 // is below b << w, for b in [0, nb]; one lane per entry, a binary search over
-// the packed old offsets (workgroup blk covers entries [256 blk, ...)).
-__device__ void remap_index_part(const uint64_t *__restrict__ live_src, uint64_t m, uint32_t w,
-                                 uint64_t nb, uint32_t *ridx, uint64_t blk) {
-    const uint64_t b = blk * kScanThreads + threadIdx.x;
-    if (b > nb) return;
-    const uint64_t x = b << w;
-    uint64_t lo = 0, len = m;  // first k with src[k] >= x
+// the packed old offsets (workgroup blk covers entries [256 blk, ...)).  The
+// workgroup's answers lie between those of its first and last bucket; when
+// that stretch of old offsets is short (always, in a table of at most
+// kIndexStage live blocks) it is staged in LDS with one coalesced load and
+// searched there.
+constexpr uint32_t kIndexStage = 2048;
+
+// First k in [lo, hi) with a[k] >= x (hi if none).
+__device__ inline uint64_t first_ge(const uint64_t *a, uint64_t lo, uint64_t hi, uint64_t x) {
+    uint64_t len = hi - lo;
     while (len > 0) {
         const uint64_t half = len >> 1;
-        if (live_src[lo + half] < x) {
+        if (a[lo + half] < x) {
             lo += half + 1;
             len -= half + 1;
         } else {
             len = half;
         }
     }
-    ridx[b] = (uint32_t)lo;
+    return lo;
+}
+
+__device__ void remap_index_part(const uint64_t *__restrict__ live_src, uint64_t m, uint32_t w,
+                                 uint64_t nb, uint32_t *ridx, uint64_t blk) {
+    __shared__ uint64_t s_src[kIndexStage];
+    __shared__ uint64_t s_r[2];
+    const uint64_t b0 = blk * kScanThreads;
+    if (b0 > nb) return;  // (the whole workgroup)
+    const uint64_t b1 = umin64(b0 + kScanThreads - 1, nb);
+    if (m <= kIndexStage) {
+        if (threadIdx.x == 0) {
+            s_r[0] = 0;
+            s_r[1] = m;
+        }
+    } else if (threadIdx.x < 2) {
+        s_r[threadIdx.x] = first_ge(live_src, 0, m, (threadIdx.x ? b1 : b0) << w);
+    }
+    __syncthreads();
+    const uint64_t r0 = s_r[0], r1 = s_r[1];
+    const bool staged = r1 - r0 <= kIndexStage;
+    if (staged)
+        for (uint64_t i = threadIdx.x; i < r1 - r0; i += kScanThreads) s_src[i] = live_src[r0 + i];
+    __syncthreads();
+    const uint64_t b = b0 + threadIdx.x;
+    if (b > b1) return;
+    const uint64_t k = staged ? r0 + first_ge(s_src, 0, r1 - r0, b << w)
+                              : first_ge(live_src, r0, r1, b << w);
+    ridx[b] = (uint32_t)k;
 }
 
 struct BaseArgs {
@@ -628,6 +699,7 @@ struct BaseArgs {
     uint64_t rnb;       // remap buckets
     uint64_t arena_bytes;
     WsHeader *hdr;
+    uint64_t *clear;  // set to zero (or null)
 };
 
 // Pass 3 of a plan.  Workgroups [0, nb): the tile size (every workgroup
@@ -644,18 +716,33 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
     __shared__ uint64_t s_red[12 * (kScanThreads / 64)];
     __shared__ uint64_t s_before;
     WsHeader *hdr = a.hdr;
-    if (plan_dead(hdr)) return;
+    if (a.clear && blockIdx.x == 0 && threadIdx.x == 0) *a.clear = 0;
     const uint64_t g = blockIdx.x;
-    const uint64_t m = hdr->live_blocks;
     if (g >= a.nb) {
+        const uint64_t m = hdr->live_blocks;
+        if (plan_dead(hdr)) return;
         remap_index_part(a.lv.src, m, a.rw, a.rnb, a.ridx, g - a.nb);
         return;
+    }
+    // every load that does not depend on another is issued before the
+    // first is used (the header's verdict included): one memory round trip
+    // where there were four
+    const uint64_t j0 = (uint64_t)threadIdx.x * kPartsPer;
+    uint64_t ta[kPartsPer], tb[kPartsPer];
+#pragma unroll
+    for (uint32_t k = 0; k < kPartsPer; ++k) {
+        const bool in = j0 + k < a.nb;
+        ta[k] = in ? a.tpart[j0 + k] : 0;
+        tb[k] = in ? a.tpart[kMaxScanParts + j0 + k] : 0;
     }
     uint64_t moved = 0, small = 0;
     for (uint64_t j = threadIdx.x; j < a.nb; j += kScanThreads) {
         moved += a.spart[j].moved_bytes;
         small += a.spart[j].small_moved;
     }
+    const uint64_t k_begin = a.lbase[g], k_end = a.lbase[g + 1];
+    const uint64_t max_end = hdr->max_live_end;
+    if (plan_dead(hdr)) return;
     {
         StatPart q{0, 0, 0, 0, kNone, kNone, kNone, 0};
         uint64_t x[4] = {moved, small, 0, 0};
@@ -664,8 +751,8 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
         small = x[1];
     }
     uint64_t pa, na, pb, nbt;
-    sums_prefix(a.tpart, a.nb, g, sh, &s_before, pa, na);
-    sums_prefix(a.tpart + kMaxScanParts, a.nb, g, sh, &s_before, pb, nbt);
+    sums_prefix(ta, g, sh, &s_before, pa, na);
+    sums_prefix(tb, g, sh, &s_before, pb, nbt);
     const TileChoice tc = a.tiles;
     bool pick_b = tc.a != tc.b && small * 2 > moved && moved >= kAutoMinMoved;
     if (tc.a != tc.b && (pick_b ? nbt : na) > a.max_tiles && (pick_b ? na : nbt) <= a.max_tiles)
@@ -674,7 +761,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
     const uint64_t n_tiles = pick_b ? nbt : na;
     if (g == 0) {
         uint64_t whole = 0;
-        stats_finish(a.spart, a.nb, a.arena_bytes, hdr, true, kNone,
+        stats_finish(a.spart, a.nb, a.arena_bytes, max_end, hdr, true, kNone,
                      a.twhole + (pick_b ? kMaxScanParts : 0), &whole);
         if (threadIdx.x == 0) {
             hdr->n_tiles = n_tiles;
@@ -683,7 +770,6 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
         }
     }
     if (n_tiles > a.max_tiles) return;  // the plan fails (the header says so)
-    const uint64_t k_begin = a.lbase[g], k_end = a.lbase[g + 1];
     uint64_t carry = pick_b ? pb : pa;
     for (uint64_t s0 = k_begin; s0 < k_end; s0 += kScanTile) {
         const uint64_t k0 = s0 + (uint64_t)threadIdx.x * kScanItems;
@@ -717,16 +803,15 @@ __device__ inline int64_t last_le(const T *a, int64_t lo, int64_t hi, uint64_t x
     return l - 1;
 }
 
-// Where tile t starts, and its first block.
-__device__ inline uint64_t tile_start(const LiveView &lv, const uint32_t *tile_base, uint64_t m,
-                                      uint64_t t, uint64_t T, uint64_t *first) {
-    const int64_t k = last_le(tile_base, 0, (int64_t)m, t);
-    const uint64_t j = t - tile_base[k];
+// Where tile t starts, given its first block k (the last block whose first
+// tile index tb_k is <= t).
+__device__ inline uint64_t tile_start_at(const LiveView &lv, uint64_t k, uint64_t tb_k,
+                                         uint64_t t, uint64_t T) {
+    const uint64_t j = t - tb_k;
     const uint64_t a = lv.dst[k];
     const bool start = (k == 0) || !moved_at(lv, (uint64_t)k - 1);
     const uint64_t lead = (start && (a & (T - 1))) ? 1 : 0;
     const uint64_t first_mult = (a + T - 1) & ~(T - 1);
-    *first = (uint64_t)k;
     return (j < lead) ? a : first_mult + (j - lead) * T;
 }
 
@@ -738,7 +823,7 @@ __device__ inline uint64_t tile_of(const LiveView &lv, const uint32_t *tile_base
     const uint64_t A = (a + T - 1) & ~(T - 1);
     const bool start = (b == 0) || !moved_at(lv, b - 1);
     const uint64_t lead = (start && (a & (T - 1))) ? 1 : 0;
-    if (q >= A) return tile_base[b] + lead + (q - A) / T;
+    if (q >= A) return tile_base[b] + lead + div_tile(q - A, T);
     // q lies in the window block b starts in: block b's own first tile if it
     // starts a run there, else the tile that began earlier in the run
     return lead ? tile_base[b] : tile_base[b] - 1;
@@ -751,18 +836,70 @@ __device__ inline uint64_t tile_of(const LiveView &lv, const uint32_t *tile_base
 // order kept), so the destinations whose sources lie in [t0, t1) are at most
 // t1 - t0 consecutive live bytes, all at or below [t0, t1): their tiles are a
 // short range ending at or before this one.
+//
+// Each tile's first block is the last block whose first tile index is <= t
+// (a search over tile_base).  The workgroup's tiles [tb, tb + 256) -- and the
+// tile after them, whose start bounds the last one -- have their first blocks
+// in one stretch of tile_base; when it is short it is staged in LDS with one
+// coalesced load and every lane searches there (a small plan stages all of
+// tile_base and searches global memory not at all).  Each lane also leaves
+// its tile's start in LDS for the lane before it.
+constexpr uint32_t kTileStage = 2048;  // tile_base entries staged per workgroup
+
 __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint32_t *tile_base,
                                                const WsHeader *hdr, uint64_t max_tiles,
                                                const uint32_t *ridx, uint32_t w, TileRec *tiles,
                                                uint32_t *flags) {
-    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (plan_dead(hdr) || hdr->n_tiles > max_tiles) return;  // plan fails
+    __shared__ uint32_t s_tb[kTileStage];
+    __shared__ uint64_t s_t0[257];
+    __shared__ int64_t s_k[2];
     const uint64_t n_tiles = hdr->n_tiles, m = hdr->live_blocks, T = hdr->tile_bytes;
+    if (plan_dead(hdr) | (n_tiles > max_tiles)) return;  // plan fails
+    const uint64_t tb = (uint64_t)blockIdx.x * 256;
+    if (tb >= n_tiles) return;  // (the whole workgroup)
+    const uint64_t t = tb + threadIdx.x;
+    const uint64_t te = umin64(tb + 256, n_tiles);
+    const uint64_t tq = te < n_tiles ? te : te - 1;  // the last tile whose start is needed
+    // the stretch of tile_base holding the first blocks of tiles [tb, tq]
+    if (m <= kTileStage) {
+        if (threadIdx.x == 0) {
+            s_k[0] = 0;
+            s_k[1] = (int64_t)m - 1;
+        }
+    } else if (threadIdx.x < 2) {
+        s_k[threadIdx.x] = last_le(tile_base, 0, (int64_t)m, threadIdx.x ? tq : tb);
+    }
+    __syncthreads();
+    const int64_t k_lo = s_k[0], k_hi = s_k[1];
+    const bool staged = k_hi - k_lo < (int64_t)kTileStage;
+    if (staged)
+        for (int64_t i = threadIdx.x; i <= k_hi - k_lo; i += 256) s_tb[i] = tile_base[k_lo + i];
+    __syncthreads();
+    // first block of tile u (tb <= u <= tq), and its first tile index
+    const auto first_of = [&](uint64_t u, uint64_t *tb_k) -> uint64_t {
+        if (staged) {
+            const int64_t r = last_le(s_tb, 0, k_hi - k_lo + 1, u);
+            *tb_k = s_tb[r];
+            return (uint64_t)(k_lo + r);
+        }
+        const int64_t k = last_le(tile_base, k_lo, k_hi + 1, u);
+        *tb_k = tile_base[k];
+        return (uint64_t)k;
+    };
+    uint64_t first = 0, t0 = 0, tb_k;
+    if (t < te) {
+        first = first_of(t, &tb_k);
+        t0 = tile_start_at(lv, first, tb_k, t, T);
+        s_t0[threadIdx.x] = t0;
+    }
+    if (threadIdx.x == 255 && te < n_tiles) {  // the tile after the workgroup's
+        const uint64_t k = first_of(te, &tb_k);
+        s_t0[256] = tile_start_at(lv, k, tb_k, te, T);
+    }
+    __syncthreads();
     if (t >= n_tiles) return;
-    uint64_t first, next_first;
-    const uint64_t t0 = tile_start(lv, tile_base, m, t, T, &first);
     uint64_t bound = (t0 & ~(T - 1)) + T;
-    if (t + 1 < n_tiles) bound = umin64(bound, tile_start(lv, tile_base, m, t + 1, T, &next_first));
+    if (t + 1 < n_tiles) bound = umin64(bound, s_t0[threadIdx.x + 1]);
     // last block of the run inside [t0, bound): blocks after first that start
     // below bound and moved form a prefix -- gallop, then bisect
     uint64_t last = first, stride = 1;
@@ -813,13 +950,7 @@ __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint32_t *tile
 }
 
 __global__ void k_commit(LiveView lv, uint64_t m, uint64_t *off_out, uint64_t *size_out,
-                         uint8_t *live_out, uint8_t *pinned_out, const WsHeader *gate,
-                         uint64_t max_tiles, uint64_t *zero) {
-    if (zero && blockIdx.x == 0 && threadIdx.x == 0) *zero = 0;
-    if (gate) {  // queued before the plan was read back: its count, if it did not fail
-        if (plan_failed(gate, max_tiles)) return;
-        m = gate->live_blocks < m ? gate->live_blocks : m;
-    }
+                         uint8_t *live_out, uint8_t *pinned_out) {
     for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < m;
          k += (uint64_t)gridDim.x * blockDim.x) {
         if (off_out) off_out[k] = lv.dst[k];
@@ -970,7 +1101,7 @@ namespace {
 // window in the header, or null.
 hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsLayout &L,
                 uint64_t *new_offset, int outputs, const uint64_t *win, TileChoice tiles,
-                uint64_t epoch, uint64_t fit_need, hipStream_t s) {
+                uint64_t epoch, uint64_t fit_need, uint64_t *clear, hipStream_t s) {
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.header);
     ScanPart *part = reinterpret_cast<ScanPart *>(ws + L.part);
     StatPart *spart = reinterpret_cast<StatPart *>(ws + L.spart);
@@ -1007,24 +1138,29 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
     d.twhole = reinterpret_cast<uint64_t *>(ws + L.twhole);
     d.lbase = reinterpret_cast<uint64_t *>(ws + L.lbase);
     d.tiles = tiles;
-    d.outputs = outputs;
     d.fit_need = fit_need;
     d.epoch = epoch;
+    d.arena_bytes = arena_bytes;
     // pass 1: aggregates
     if (d.nb) {
         hipLaunchKernelGGL(k_scan_partials, dim3((uint32_t)d.nb), dim3(kScanThreads), 0, s, t,
-                           arena_bytes, win, (uint64_t)L.scan_chunk, part);
+                           arena_bytes, win, (uint64_t)L.scan_chunk, part,
+                           outputs == 0 ? &hdr->arrive : nullptr);
         AC_TRY(hipGetLastError());
     }
     // pass 2: each workgroup's prefix, then its entries
-    hipLaunchKernelGGL(k_scan_down, dim3((uint32_t)d.ngroups), dim3(kScanThreads), 0, s, d);
+    if (outputs == 0)
+        hipLaunchKernelGGL(k_scan_down<0>, dim3((uint32_t)d.ngroups), dim3(kScanThreads), 0, s, d);
+    else if (outputs == kOutNew)
+        hipLaunchKernelGGL(k_scan_down<kOutNew>, dim3((uint32_t)d.ngroups), dim3(kScanThreads), 0,
+                           s, d);
+    else
+        hipLaunchKernelGGL(k_scan_down<kOutSelect>, dim3((uint32_t)d.ngroups), dim3(kScanThreads),
+                           0, s, d);
     AC_TRY(hipGetLastError());
-    if (outputs == 0) {  // a statistics pass: its finish
-        hipLaunchKernelGGL(k_scan_finish, dim3(1), dim3(kScanThreads), 0, s, spart, d.nb,
-                           arena_bytes, hdr, fit_need, t);
-        return hipGetLastError();
-    }
-    if (!(outputs & kOutNew)) return hipSuccess;  // a selection scan: nothing more
+    // a statistics pass ends there (its last workgroup finishes it), and so
+    // does a selection scan
+    if (!(outputs & kOutNew)) return hipSuccess;
     // pass 3: tile size, the blocks' first tiles and the header's finish;
     // the remap index beside them
     const LiveView lv = live_view(ws, L);
@@ -1045,6 +1181,7 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
     b.rnb = remap_buckets(arena_bytes, t.n);
     b.arena_bytes = arena_bytes;
     b.hdr = hdr;
+    b.clear = clear;
     const uint64_t rblocks = (b.rnb + 1 + kScanThreads - 1) / kScanThreads;
     hipLaunchKernelGGL(k_plan_bases, dim3((uint32_t)(d.ngroups + rblocks)), dim3(kScanThreads), 0,
                        s, b);
@@ -1066,14 +1203,14 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
 
 hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, const WsLayout &L,
                        uint64_t *new_offset, int outputs, TileChoice tiles, uint64_t epoch,
-                       uint64_t fit_need, hipStream_t s) {
+                       uint64_t fit_need, uint64_t *clear, hipStream_t s) {
     return queue_scan(t, arena_bytes, ws, L, new_offset, outputs, nullptr, tiles, epoch,
-                      fit_need, s);
+                      fit_need, clear, s);
 }
 
 hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t request,
                            uint8_t *ws, const WsLayout &L, uint64_t *new_offset,
-                           TileChoice tiles, uint64_t epoch, hipStream_t s) {
+                           TileChoice tiles, uint64_t epoch, uint64_t *clear, hipStream_t s) {
     WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.header);
     const uint64_t *src = reinterpret_cast<const uint64_t *>(ws + L.live_src);
     const uint64_t *size = reinterpret_cast<const uint64_t *>(ws + L.live_size);
@@ -1081,7 +1218,7 @@ hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t re
     const uint32_t *pc = reinterpret_cast<const uint32_t *>(ws + L.live_pc);
     SelPart *sp = reinterpret_cast<SelPart *>(ws + L.selpart);
     AC_TRY(queue_scan(t, arena_bytes, ws, L, nullptr, kOutSelect, nullptr, tiles, epoch,
-                      kNone, s));
+                      kNone, nullptr, s));
     // candidates: every last hole l in [0, m], m <= n
     hipLaunchKernelGGL(k_select, dim3((uint32_t)L.n_sel_blocks), dim3(kSelThreads), 0, s, src, z,
                        pc, hdr, arena_bytes, request, sp);
@@ -1090,20 +1227,17 @@ hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t re
                        src, size, z, arena_bytes, hdr);
     AC_TRY(hipGetLastError());
     return queue_scan(t, arena_bytes, ws, L, new_offset, kOutNew, &hdr->win_begin, tiles,
-                      epoch, kNone, s);
+                      epoch, kNone, clear, s);
 }
 
 hipError_t launch_commit(const uint8_t *ws, const WsLayout &L, uint64_t live_blocks,
                          uint64_t *off_out, uint64_t *size_out, uint8_t *live_out,
-                         uint8_t *pinned_out, const WsHeader *gate, uint64_t max_tiles,
-                         uint64_t *zero, hipStream_t s) {
-    if (live_blocks == 0 && !zero) return hipSuccess;
+                         uint8_t *pinned_out, hipStream_t s) {
+    if (live_blocks == 0) return hipSuccess;
     uint64_t grid = (live_blocks + 255) / 256;
     if (grid > 4096) grid = 4096;
-    if (grid < 1) grid = 1;
     hipLaunchKernelGGL(k_commit, dim3((uint32_t)grid), dim3(256), 0, s, live_view(ws, L),
-                       live_blocks, off_out, size_out, live_out, pinned_out, gate, max_tiles,
-                       zero);
+                       live_blocks, off_out, size_out, live_out, pinned_out);
     return hipGetLastError();
 }
 

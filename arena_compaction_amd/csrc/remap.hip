@@ -29,6 +29,24 @@ namespace {
 
 constexpr uint32_t kRemapThreads = 256;
 
+// The one-call path's commit, done by the remap's launch: the packed live
+// arrays and where the packed table goes.
+struct CommitArgs {
+    LiveView lv;
+    CommitOut out;
+};
+
+// Lanes k < m write packed entry k (grid-stride).
+__device__ inline void commit_part(const CommitArgs &c, uint64_t m) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < m; k += stride) {
+        if (c.out.off) c.out.off[k] = c.lv.dst[k];
+        if (c.out.size) c.out.size[k] = c.lv.size[k];
+        if (c.out.live) c.out.live[k] = 1;
+        if (c.out.pinned) c.out.pinned[k] = c.lv.pin[k];
+    }
+}
+
 // One lane per handle, grid-stride.  The bucket of h gives the live blocks
 // starting in it, [ridx[b], ridx[b+1]); the block holding h, if any, is the
 // last one starting at or below h, so it is found by a short search inside
@@ -36,7 +54,8 @@ constexpr uint32_t kRemapThreads = 256;
 // 16-byte read.  A random handle costs about three dependent cache-line requests:
 // the index pair, a probe or two over the bucket's keys, the record.
 // REC32: the records are LiveRec32 (arenas below 2^37 bytes), else LiveRec.
-template <bool REC32>
+// COMMIT: the launch also writes the packed table (c).
+template <bool REC32, bool COMMIT>
 __global__ __launch_bounds__(kRemapThreads) void k_remap(const void *__restrict__ rec,
                                                          const uint64_t *__restrict__ live_src,
                                                          const uint32_t *__restrict__ key,
@@ -44,11 +63,14 @@ __global__ __launch_bounds__(kRemapThreads) void k_remap(const void *__restrict_
                                                          uint32_t w, uint64_t nb, uint64_t m,
                                                          const uint64_t *h_in, uint64_t *h_out,
                                                          uint64_t H, unsigned long long *n_invalid,
-                                                         const WsHeader *gate, uint64_t max_tiles) {
+                                                         const WsHeader *gate, uint64_t max_tiles,
+                                                         CommitArgs c) {
     if (gate) {  // queued before the plan was read back: its count, if it did not fail
+        const uint64_t gm = gate->live_blocks;
         if (plan_failed(gate, max_tiles)) return;
-        m = gate->live_blocks;
+        m = gm < m ? gm : m;
     }
+    if constexpr (COMMIT) commit_part(c, m);
     uint64_t bad = 0;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < H; k += stride) {
@@ -104,6 +126,7 @@ __global__ __launch_bounds__(kRemapThreads) void k_remap(const void *__restrict_
 // the last such probe leaves the answer in registers; only a handle below
 // the bucket's first block start reads a record afterwards, that of the
 // block before the bucket.
+template <bool COMMIT>
 __global__ __launch_bounds__(kRemapThreads) void k_remap_ent(const RemapEnt *__restrict__ ent,
                                                              const uint32_t *__restrict__ ridx,
                                                              uint32_t w, uint64_t nb, uint64_t m,
@@ -111,11 +134,13 @@ __global__ __launch_bounds__(kRemapThreads) void k_remap_ent(const RemapEnt *__r
                                                              uint64_t H,
                                                              unsigned long long *n_invalid,
                                                              const WsHeader *gate,
-                                                             uint64_t max_tiles) {
+                                                             uint64_t max_tiles, CommitArgs c) {
     if (gate) {  // queued before the plan was read back: its count, if it did not fail
+        const uint64_t gm = gate->live_blocks;
         if (plan_failed(gate, max_tiles)) return;
-        m = gate->live_blocks;
+        m = gm < m ? gm : m;
     }
+    if constexpr (COMMIT) commit_part(c, m);
     uint64_t bad = 0;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t k = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; k < H; k += stride) {
@@ -162,38 +187,55 @@ __global__ void k_zero_u64(uint64_t *p) {
     if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0;
 }
 
+template <bool COMMIT>
+void remap_launch(const uint8_t *ws, const WsLayout &L, uint64_t arena_bytes, uint64_t n,
+                  uint64_t live_blocks, const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
+                  unsigned long long *bad, const CommitArgs &c, const WsHeader *gate,
+                  uint64_t max_tiles, uint64_t grid, hipStream_t s) {
+    const void *rec = ws + L.live_rec;
+    const uint64_t *live_src = reinterpret_cast<const uint64_t *>(ws + L.live_src);
+    const uint32_t *key = reinterpret_cast<const uint32_t *>(ws + L.live_key);
+    const uint32_t *ridx = reinterpret_cast<const uint32_t *>(ws + L.ridx);
+    const uint32_t *k32 = remap_keys32(arena_bytes, n) ? key : nullptr;
+    const uint32_t w = remap_shift(arena_bytes, n);
+    const uint64_t nb = remap_buckets(arena_bytes, n);
+    if (remap_ent(arena_bytes, n))
+        hipLaunchKernelGGL(k_remap_ent<COMMIT>, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s,
+                           static_cast<const RemapEnt *>(rec), ridx, w, nb, live_blocks, h_in,
+                           h_out, n_handles, bad, gate, max_tiles, c);
+    else if (remap_rec32(arena_bytes))
+        hipLaunchKernelGGL((k_remap<true, COMMIT>), dim3((uint32_t)grid), dim3(kRemapThreads), 0,
+                           s, rec, live_src, k32, ridx, w, nb, live_blocks, h_in, h_out,
+                           n_handles, bad, gate, max_tiles, c);
+    else
+        hipLaunchKernelGGL((k_remap<false, COMMIT>), dim3((uint32_t)grid), dim3(kRemapThreads), 0,
+                           s, rec, live_src, k32, ridx, w, nb, live_blocks, h_in, h_out,
+                           n_handles, bad, gate, max_tiles, c);
+}
+
 }  // namespace
 
-hipError_t launch_remap(const void *rec, const uint64_t *live_src, const uint32_t *key,
-                        const uint32_t *ridx,
-                        uint64_t arena_bytes, uint64_t n, uint64_t live_blocks,
-                        const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
-                        uint64_t *n_invalid, const WsHeader *gate, uint64_t max_tiles,
-                        int num_cus, hipStream_t s) {
+hipError_t launch_remap(const uint8_t *ws, const WsLayout &L, uint64_t arena_bytes, uint64_t n,
+                        uint64_t live_blocks, const uint64_t *h_in, uint64_t *h_out,
+                        uint64_t n_handles, uint64_t *n_invalid, const CommitOut *commit,
+                        const WsHeader *gate, uint64_t max_tiles, int num_cus, hipStream_t s) {
     if (n_invalid && !gate) {
         hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, n_invalid);
         AC_TRY(hipGetLastError());
     }
-    if (n_handles == 0) return hipSuccess;
-    uint64_t grid = (n_handles + kRemapThreads - 1) / kRemapThreads;
+    const uint64_t work = (commit && live_blocks > n_handles) ? live_blocks : n_handles;
+    if (work == 0) return hipSuccess;
+    uint64_t grid = (work + kRemapThreads - 1) / kRemapThreads;
     const uint64_t cap = (uint64_t)num_cus * 2;  // measured best of 1, 2, 3, 4, 8, 16 per CU
     if (grid > cap) grid = cap;
-    const uint32_t *k32 = remap_keys32(arena_bytes, n) ? key : nullptr;
-    const uint32_t w = remap_shift(arena_bytes, n);
-    const uint64_t nb = remap_buckets(arena_bytes, n);
     unsigned long long *bad = reinterpret_cast<unsigned long long *>(n_invalid);
-    if (remap_ent(arena_bytes, n))
-        hipLaunchKernelGGL(k_remap_ent, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s,
-                           static_cast<const RemapEnt *>(rec), ridx, w, nb, live_blocks, h_in,
-                           h_out, n_handles, bad, gate, max_tiles);
-    else if (remap_rec32(arena_bytes))
-        hipLaunchKernelGGL(k_remap<true>, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s, rec,
-                           live_src, k32, ridx, w, nb, live_blocks, h_in, h_out, n_handles, bad,
-                           gate, max_tiles);
+    CommitArgs c{live_view(ws, L), commit ? *commit : CommitOut{nullptr, nullptr, nullptr, nullptr}};
+    if (commit)
+        remap_launch<true>(ws, L, arena_bytes, n, live_blocks, h_in, h_out, n_handles, bad, c, gate,
+                           max_tiles, grid, s);
     else
-        hipLaunchKernelGGL(k_remap<false>, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s, rec,
-                           live_src, k32, ridx, w, nb, live_blocks, h_in, h_out, n_handles, bad,
-                           gate, max_tiles);
+        remap_launch<false>(ws, L, arena_bytes, n, live_blocks, h_in, h_out, n_handles, bad, c,
+                            gate, max_tiles, grid, s);
     return hipGetLastError();
 }
 
