@@ -363,6 +363,7 @@ hipError_t launch_threads(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hi
         case 4: return launch_one<THREADS, 4, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
         case 8: return launch_one<THREADS, 8, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
         case 16: return launch_one<THREADS, 16, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
+        case 32: return launch_one<THREADS, 32, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -372,18 +372,40 @@ __device__ inline uint64_t whole_of(uint64_t a, uint64_t s, uint64_t T) {
     return hi > lo ? hi - lo : 0;
 }
 
+// A workgroup's statistics stored and loaded at the agent's coherence point
+// (relaxed agent-scope atomics), for a reader in the same launch on another
+// XCD: no cache writeback or invalidate is needed, only that the stores have
+// completed before the writer announces them.
+static_assert(sizeof(StatPart) == 8 * sizeof(uint64_t), "StatPart is eight words");
+__device__ inline void part_store(StatPart *p, const StatPart &q) {
+    uint64_t *w = reinterpret_cast<uint64_t *>(p);
+    const uint64_t v[8] = {q.max_gap, q.gaps, q.moved_blocks, q.moved_bytes,
+                           q.min_moved_dst, q.min_size, q.min_fit, q.small_moved};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) __hip_atomic_store(w + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline StatPart part_load(const StatPart *p) {
+    uint64_t *w = const_cast<uint64_t *>(reinterpret_cast<const uint64_t *>(p));
+    uint64_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __hip_atomic_load(w + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return StatPart{v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+}
+
 // The statistics of all workgroups, reduced by one workgroup (the tail hole
 // added) into the header; with `plan`, the plan's mover fields are reset too.
 // x: up to four sums more (e.g. whole-tile counts), reduced alongside.
-// max_end: the highest live end (the header's max_live_end).
+// max_end: the highest live end (the header's max_live_end).  coherent:
+// the parts were written in this launch (read them with part_load).
 __device__ void stats_finish(const StatPart *spart, uint64_t nb, uint64_t arena_bytes,
                              uint64_t max_end, WsHeader *hdr, bool plan, uint64_t fit_need,
-                             const uint64_t *xsrc = nullptr, uint64_t *xsum = nullptr) {
+                             const uint64_t *xsrc = nullptr, uint64_t *xsum = nullptr,
+                             bool coherent = false) {
     __shared__ uint64_t sh[12 * (kScanThreads / 64)];
     StatPart a{0, 0, 0, 0, kNone, kNone, kNone, 0};
     uint64_t x[4] = {0, 0, 0, 0};
     for (uint64_t j = threadIdx.x; j < nb; j += kScanThreads) {
-        const StatPart q = spart[j];
+        const StatPart q = coherent ? part_load(spart + j) : spart[j];
         a.small_moved += q.small_moved;
         a.min_fit = umin64(a.min_fit, q.min_fit);
         a.max_gap = umax64(a.max_gap, q.max_gap);
@@ -448,7 +470,7 @@ struct DownArgs {
 // invalid table writes nothing else.  In a statistics pass the last
 // workgroup to finish reduces every workgroup's statistics into the header
 // (a count of finished workgroups, cleared by pass 1, tells it that it is
-// the last; its fence and atomic make the others' results visible to it).  The block before a live entry moved
+// the last; the statistics themselves go through the coherence point).  The block before a live entry moved
 // iff the packed position after it differs from its end (a block that stays,
 // pinned or held, resets the position to its own end).
 // OUT: the pass's outputs (0: a statistics pass; kOutNew: a plan;
@@ -591,7 +613,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
     uint64_t x[4] = {ca, wa, cb, wb};
     block_reduce_stats<kScanThreads>(q, x, s_red);
     if (threadIdx.x == 0) {
-        d.spart[g] = q;
+        if constexpr (OUT == 0) part_store(d.spart + g, q);  // read in this launch
+        else d.spart[g] = q;
         if (tiles) {
             d.tpart[g] = x[0];
             d.twhole[g] = x[1];
@@ -604,17 +627,18 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
         if (threadIdx.x == 0) {
             uint32_t last = 1;
             if (d.ngroups > 1) {
-                __threadfence();  // this workgroup's statistics before its arrival
-                const uint64_t done = __hip_atomic_fetch_add(&d.hdr->arrive, 1ull, __ATOMIC_ACQ_REL,
+                // the statistics' stores complete before the arrival is counted
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                const uint64_t done = __hip_atomic_fetch_add(&d.hdr->arrive, 1ull, __ATOMIC_RELAXED,
                                                              __HIP_MEMORY_SCOPE_AGENT);
                 last = done + 1 == d.ngroups;
-                __threadfence();
             }
             s_last = last;
         }
         __syncthreads();
         if (s_last)
-            stats_finish(d.spart, d.nb, d.arena_bytes, total.mx, d.hdr, false, d.fit_need);
+            stats_finish(d.spart, d.nb, d.arena_bytes, total.mx, d.hdr, false, d.fit_need,
+                         nullptr, nullptr, true);
     }
 }
 

@@ -145,9 +145,9 @@ typedef struct defrag_stats_t {
  * passed explicitly, a zero tile size or spin limit takes its default and the
  * other fields are taken as given. */
 typedef struct defrag_tuning {
-    uint32_t tile_bytes;      /* mover tile: power of two in [256, 131072],
+    uint32_t tile_bytes;      /* mover tile: power of two in [256, 262144],
                                  or 0: the plan chooses on the device from the
-                                 shifts it finds -- 131072 when more than half
+                                 shifts it finds -- 262144 when more than half
                                  of the moved bytes shift by less than 8 MiB
                                  and at least 64 MiB move (a tile then often
                                  waits on one still being read, and larger

@@ -59,7 +59,7 @@ def test_workspace_bytes():
     pinned = ac.defrag_workspace_bytes(200_247, 80 << 30, 0, 40)
     assert big < pinned < big + 40 * 2 * 64
     assert ac.defrag_workspace_bytes(10, 4096, 0, 11) == 0   # more pinned than entries
-    for bad_tile in (100, 128, 3000, 262144):
+    for bad_tile in (100, 128, 3000, 524288):
         assert ac.defrag_workspace_bytes(16, 4096, bad_tile) == 0
     # more mover tiles than 32-bit tile indices (with room for the grid) allow
     assert ac.defrag_workspace_bytes(16, 1 << 44, 256) == 0

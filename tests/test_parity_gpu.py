@@ -18,7 +18,7 @@ from harness import (check_arena_full, check_arena_sampled, check_stats,
 
 pytestmark = pytest.mark.gpu
 
-TILES = (256, 4096, 65536, 131072)
+TILES = (256, 4096, 65536, 131072, 262144)
 
 
 @pytest.fixture(scope="module")
@@ -103,7 +103,8 @@ def test_random_medium_heaps_default_tuning(ac):
 
 
 @pytest.mark.parametrize("k", W.NAMES)
-@pytest.mark.parametrize("tile,nt", [(256, 0), (4096, 1), (65536, 0), (65536, 1), (131072, 0)])
+@pytest.mark.parametrize("tile,nt", [(256, 0), (4096, 1), (65536, 0), (65536, 1), (131072, 0),
+                                     (262144, 1)])
 def test_small_workloads_gpu(ac, k, tile, nt):
     _full_check(W.workload(k, small=True), _tuning(ac, tile, 0, nt))
 

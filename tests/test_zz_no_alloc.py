@@ -84,14 +84,23 @@ def test_static_scratch_matches_the_workspace_entry_point(ac):
     assert sizes[1][0] < sizes[0][0] and sizes[1][1] < sizes[0][1]
 
 
+# the largest mover tile the library takes (a power of two; twice it is
+# refused: see test_abi)
+MAX_TILE = 262144
+TILE_RECORD_BYTES = 52  # a tile's record and flag in the workspace
+
+
 def test_static_scratch_limits(ac):
     """More tiles than fit beside the plan arrays: refused by the plan on the
-    device, before anything moves (a 2^40-byte arena whose one 2^39-byte
-    block moves; only the table is read, the arena is never touched).  A
+    device, before anything moves (a 2^44-byte arena whose one 2^43-byte
+    block moves; only the table is read, the arena is never touched).  The
+    move needs more tile records than the scratch holds at every tile size
+    the plan may pick, so the refusal cannot depend on which it picks.  A
     workspace argument is refused on the host."""
-    S = 1 << 40
-    heap = W.table_from_lists(S, [(0, 1 << 39), (1 << 39, 1 << 39)], [0, 1], [(1 << 39) + 5],
-                              name="2^40 arena")
+    S = 1 << 44
+    assert (S // 2) // MAX_TILE * TILE_RECORD_BYTES > 8 * ac.STATIC_SCRATCH_BYTES
+    heap = W.table_from_lists(S, [(0, 1 << 43), (1 << 43, 1 << 43)], [0, 1], [(1 << 43) + 5],
+                              name="2^44 arena")
     off, size, live = device_table(heap, "cuda")
     dummy = torch.zeros(64, dtype=torch.uint8, device="cuda")
     with pytest.raises(ac.DefragError) as e:
