@@ -196,6 +196,66 @@ def ablation_waves(args, heap, arena, off, size, live, pinned, ws, tuning) -> in
     return 0 if equal else 1
 
 
+def latency(args, heap, arena, off, size, live, pinned, ws, tuning, h_in, h_out, n_bad, new_off,
+            c_off, c_size, c_live, c_pin) -> int:
+    """Wall time per call, in microseconds, of the one-call path and its
+    pieces: the C function called directly with its argument struct built
+    once (the binding's marshalling timed apart), each call ending in its
+    own read-back, so back-to-back calls do not overlap."""
+    import ctypes
+    import torch
+    import arena_compaction_amd as ac
+    S = heap.arena_bytes
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    reps = max(args.steps, 1) * 20
+    out = {}
+
+    def timeit(name, fn):
+        for _ in range(max(args.warmup, 1) * 3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        out[name] = round((time.perf_counter() - t0) / reps * 1e6, 1)
+
+    full = dict(handles=h_in, h_out=h_out, n_invalid=n_bad, offset_out=c_off, size_out=c_size,
+                live_out=c_live, pinned_out=c_pin)
+    variants = {
+        "one_call": (full, True),
+        "one_call_no_post_check": (full, False),
+        "plan_move_commit": (dict(offset_out=c_off, size_out=c_size, live_out=c_live,
+                                  pinned_out=c_pin), False),
+        "plan_move": ({}, False),
+    }
+    for name, (kw, after) in variants.items():
+        a, keep = ac._compact_args(off, size, live, S, arena, ws, 0, new_off, kw.get("handles"),
+                                   kw.get("h_out"), kw.get("n_invalid"), kw.get("offset_out"),
+                                   kw.get("size_out"), kw.get("live_out"), kw.get("pinned_out"),
+                                   tuning, pinned, None)
+        plan, post = ac.defrag_plan_t(), ac.defrag_stats_t()
+
+        def call(a=a, plan=plan, post=post, after=after):
+            rc = ac.lib.defrag_compact(ctypes.byref(a), sp, ctypes.byref(plan),
+                                       ctypes.byref(post) if after else None)
+            if rc != ac.DEFRAG_OK:
+                raise ac.DefragError(rc, "defrag_compact")
+        timeit(name, call)
+    timeit("binding_marshalling", lambda: ac._compact_args(
+        off, size, live, S, arena, ws, 0, new_off, h_in, h_out, n_bad, c_off, c_size, c_live,
+        c_pin, tuning, pinned, None))
+    timeit("plan_via_binding", lambda: ac.defrag_plan(off, size, live, S, ws, new_off,
+                                                      tuning=tuning, stream=stream, pinned=pinned))
+    timeit("stats_via_binding", lambda: ac.defrag_stats(off, size, live, S, ws, stream=stream,
+                                                        pinned=pinned))
+    print(json.dumps({"workload": heap.name, "entries": heap.n, "live_blocks": int(heap.live.sum()),
+                      "handles": int(heap.handles.size), "calls_per_figure": reps,
+                      "us_per_call": out}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,6 +291,12 @@ def main() -> int:
                          "GIB GiB: a plain copy of known size with the mover's own streaming "
                          "loads and stores and no dependency, to scale the byte counters of "
                          "its non-temporal accesses")
+    ap.add_argument("--latency", action="store_true",
+                    help="instead of the benchmark: the wall time of one defrag_compact call "
+                         "through the C-ABI (arguments built once, the call's own final "
+                         "read-back included), with and without each piece of the step, and of "
+                         "defrag_plan and defrag_stats alone; the arena is not refilled "
+                         "between calls (a repeated compaction moves the same bytes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -301,6 +367,9 @@ def main() -> int:
           flush=True)
     if args.ablation_waves:
         return ablation_waves(args, heap, arena, off, size, live, pinned, ws, tuning)
+    if args.latency:
+        return latency(args, heap, arena, off, size, live, pinned, ws, tuning, h_in, h_out, n_bad,
+                       new_off, c_off, c_size, c_live, c_pin)
     stream = torch.cuda.current_stream()
     refill_from = 0
     snap = {"from": None, "bytes": None}   # pristine bytes [from, S), when they fit
