@@ -163,9 +163,8 @@ int stats_pass(const defrag_table *table, uint64_t arena_bytes, uint64_t fit_nee
     // the statistics header (the second 256 bytes): a plan the workspace
     // holds keeps its own header
     L.header = L.post;
-    if (launch_scan(view_of(table), arena_bytes, ws, L, nullptr, 0,
-                    TileChoice{kDefaultTile, kDefaultTile}, 0, fit_need, nullptr,
-                    stream) != hipSuccess)
+    if (launch_stats_one(view_of(table), arena_bytes, ws, L, fit_need, false, stream) !=
+        hipSuccess)
         return DEFRAG_EHIP;
     rc = read_header(h, ws, L, stream);
     if (rc) return rc;
@@ -192,9 +191,7 @@ int post_check_queue(const defrag_table *packed, uint64_t arena_bytes, void *ws_
     TableView v = view_of(packed);
     v.gate = gate;
     v.gate_max_tiles = max_tiles;
-    return launch_scan(v, arena_bytes, ws, L, nullptr, 0,
-                       TileChoice{kDefaultTile, kDefaultTile}, 0, kNone, nullptr,
-                       stream) == hipSuccess
+    return launch_stats_one(v, arena_bytes, ws, L, kNone, true, stream) == hipSuccess
                ? DEFRAG_OK
                : DEFRAG_EHIP;
 }

@@ -103,8 +103,9 @@ struct alignas(256) WsHeader {
     uint64_t polls;
     uint64_t tile_bytes;     // the plan's tile size (chosen on the device when auto)
     uint64_t small_moved;    // moved bytes whose shift is below kAutoSmallShift
-    // statistics passes: down-sweep workgroups done (cleared by the
-    // aggregates pass); the last one to finish completes the header
+    // statistics passes: workgroups done (cleared by the aggregates pass,
+    // or for the one-launch pass by the plan before it, and by the last
+    // workgroup once it has completed the header)
     uint64_t arrive;
     uint64_t pad[5];
 };
@@ -251,7 +252,7 @@ constexpr size_t kPerTileBytes = sizeof(TileRec) + sizeof(uint32_t);
 
 struct WsLayout {
     // fixed part (depends on n only)
-    size_t header, post, part, spart, tpart, twhole, lbase, live_dst, live_src, live_size,
+    size_t header, post, part, spart, csum, tpart, twhole, lbase, live_dst, live_src, live_size,
         live_pin, tile_base, live_z, live_pc, selpart, live_rec, live_key, ridx, fixed;
     // tile part (depends on the tile capacity)
     size_t tiles, flags, total;
@@ -278,6 +279,7 @@ inline WsLayout ws_fixed(uint64_t n) {
     L.post = at;      at += align256(sizeof(WsHeader));  // statistics passes' own header
     L.part = at;      at += align256(nb * sizeof(ScanPart));
     L.spart = at;     at += align256(nb * sizeof(StatPart));
+    L.csum = at;      at += align256(nb * 16 * sizeof(uint64_t));  // one-launch statistics
     // -- everything below here is a plan's: statistics passes stop above --
     L.tpart = at;     at += align256(2 * nb * sizeof(uint64_t));   // per tile-size candidate
     L.twhole = at;    at += align256(2 * nb * sizeof(uint64_t));
@@ -385,13 +387,14 @@ inline LiveView live_view(const uint8_t *ws, const WsLayout &L) {
     } while (0)
 
 // ---- plan.hip ----
-// Scan passes and, with kOutNew, the mover's tiles (for at most
+// Plan and selection scans and, with kOutNew, the mover's tiles (for at most
 // L.max_tiles tiles).  All asynchronous; the header then holds totals,
 // statistics and n_tiles (tiles are built only if n_tiles <= L.max_tiles).
 // fit_need: a hole size to first-fit (header fit_offset), kNone for none.
 // clear: a word a plan's last scan pass sets to zero (the one-call path's
 // invalid-handle count, so that its remap needs no launch of its own for
-// it), or null.
+// it), or null.  A plan also clears the statistics header's count of
+// finished workgroups, which launch_stats_one needs cleared.
 hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws,
                        const WsLayout &L, uint64_t *new_offset, int outputs,
                        TileChoice tiles, uint64_t epoch, uint64_t fit_need, uint64_t *clear,
@@ -402,6 +405,14 @@ hipError_t launch_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws,
 hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t request,
                            uint8_t *ws, const WsLayout &L, uint64_t *new_offset,
                            TileChoice tiles, uint64_t epoch, uint64_t *clear, hipStream_t s);
+// A statistics pass (and, if fit_need != kNone, the first fit) in one
+// launch, into the header at L.header.  Its last workgroup finds itself by
+// a count in that header: after_plan -- a plan ran on this workspace
+// before, in stream order, and cleared it (each pass leaves it cleared) --
+// or else a one-thread launch clears it first.
+hipError_t launch_stats_one(const TableView &t, uint64_t arena_bytes, uint8_t *ws,
+                            const WsLayout &L, uint64_t fit_need, bool after_plan,
+                            hipStream_t s);
 hipError_t launch_commit(const uint8_t *ws, const WsLayout &L, uint64_t live_blocks,
                          uint64_t *off_out, uint64_t *size_out, uint8_t *live_out,
                          uint8_t *pinned_out, hipStream_t s);

@@ -22,25 +22,26 @@
 // merges adjacent free blocks, section 2.2), so one pass over live entries in
 // order sees every hole once, plus the tail above the highest live block.
 //
-// Passes (n up to 2^32 entries), each a wide launch with no one-workgroup
-// pass between them: every workgroup of a pass scans the (at most 1,024)
-// per-workgroup results of the pass before it for its own prefix, since
-// each dependent launch costs several microseconds of dispatch.
+// A plan's passes (n up to 2^32 entries), each a wide launch with no
+// one-workgroup pass between them: every workgroup of a pass scans the (at
+// most 1,024) per-workgroup results of the pass before it for its own
+// prefix, since each dependent launch costs several microseconds of
+// dispatch.
 //   1. per-workgroup aggregates (and the first bad entry);
 //   2. each workgroup's prefix, then its entries: new offsets, the packed
 //      live-block arrays (new and old offset, size, pinned flag, the remap's
 //      records), hole and move statistics, and the tiles its moved blocks
 //      start, counted for both candidate tile sizes; workgroup 0 writes the
-//      table's totals; in a statistics pass the last workgroup to finish
-//      completes the header, which ends the pass;
-//   3. (plans) each workgroup picks the tile size from the totals, the same
-//      way, and gives each of its live blocks its first tile index;
-//      workgroup 0 finishes the header (statistics, tile count and size,
-//      the mover's fields); further workgroups build the remap's bucket
-//      index over old offsets (it also narrows the tiles' source searches);
-//   4. (plans) one lane per tile: its start, range, blocks and dependencies.
+//      table's totals;
+//   3. each workgroup picks the tile size from the totals, the same way, and
+//      gives each of its live blocks its first tile index; workgroup 0
+//      finishes the header (statistics, tile count and size, the mover's
+//      fields); further workgroups build the remap's bucket index over old
+//      offsets (it also narrows the tiles' source searches);
+//   4. one lane per tile: its start, range, blocks and dependencies.
 // The whole sequence is queued at once; the host reads the header back only
-// at the end.
+// at the end.  A statistics pass alone is one launch of its own
+// (k_stats_one), which needs no prefix.
 #include "internal.h"
 
 namespace ac {
@@ -254,14 +255,11 @@ __device__ inline bool plan_dead(const WsHeader *hdr) {
 // entries [g * chunk, (g + 1) * chunk), kScanTile at a time.
 __global__ __launch_bounds__(kScanThreads) void k_scan_partials(TableView t, uint64_t arena_bytes,
                                                                 const uint64_t *win,
-                                                                uint64_t chunk, ScanPart *part,
-                                                                uint64_t *arrive) {
+                                                                uint64_t chunk, ScanPart *part) {
     __shared__ Agg sh[kScanThreads / 64];
     __shared__ uint64_t shr[kScanThreads / 64];
     uint64_t n;
     if (!table_entries(t, &n)) return;  // a gated table whose plan failed
-    // a statistics pass: the down-sweep counts its finished workgroups
-    if (arrive && blockIdx.x == 0 && threadIdx.x == 0) *arrive = 0;
     const Window w = window_of(win);
     const uint64_t base = (uint64_t)blockIdx.x * chunk;
     const uint64_t end = umin64(base + chunk, n);
@@ -372,40 +370,18 @@ __device__ inline uint64_t whole_of(uint64_t a, uint64_t s, uint64_t T) {
     return hi > lo ? hi - lo : 0;
 }
 
-// A workgroup's statistics stored and loaded at the agent's coherence point
-// (relaxed agent-scope atomics), for a reader in the same launch on another
-// XCD: no cache writeback or invalidate is needed, only that the stores have
-// completed before the writer announces them.
-static_assert(sizeof(StatPart) == 8 * sizeof(uint64_t), "StatPart is eight words");
-__device__ inline void part_store(StatPart *p, const StatPart &q) {
-    uint64_t *w = reinterpret_cast<uint64_t *>(p);
-    const uint64_t v[8] = {q.max_gap, q.gaps, q.moved_blocks, q.moved_bytes,
-                           q.min_moved_dst, q.min_size, q.min_fit, q.small_moved};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) __hip_atomic_store(w + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline StatPart part_load(const StatPart *p) {
-    uint64_t *w = const_cast<uint64_t *>(reinterpret_cast<const uint64_t *>(p));
-    uint64_t v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = __hip_atomic_load(w + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return StatPart{v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
-}
-
 // The statistics of all workgroups, reduced by one workgroup (the tail hole
 // added) into the header; with `plan`, the plan's mover fields are reset too.
 // x: up to four sums more (e.g. whole-tile counts), reduced alongside.
-// max_end: the highest live end (the header's max_live_end).  coherent:
-// the parts were written in this launch (read them with part_load).
+// max_end: the highest live end (the header's max_live_end).
 __device__ void stats_finish(const StatPart *spart, uint64_t nb, uint64_t arena_bytes,
                              uint64_t max_end, WsHeader *hdr, bool plan, uint64_t fit_need,
-                             const uint64_t *xsrc = nullptr, uint64_t *xsum = nullptr,
-                             bool coherent = false) {
+                             const uint64_t *xsrc = nullptr, uint64_t *xsum = nullptr) {
     __shared__ uint64_t sh[12 * (kScanThreads / 64)];
     StatPart a{0, 0, 0, 0, kNone, kNone, kNone, 0};
     uint64_t x[4] = {0, 0, 0, 0};
     for (uint64_t j = threadIdx.x; j < nb; j += kScanThreads) {
-        const StatPart q = coherent ? part_load(spart + j) : spart[j];
+        const StatPart q = spart[j];
         a.small_moved += q.small_moved;
         a.min_fit = umin64(a.min_fit, q.min_fit);
         a.max_gap = umax64(a.max_gap, q.max_gap);
@@ -467,15 +443,11 @@ struct DownArgs {
 // order: new offsets, the packed live arrays, hole and move statistics, and
 // (plans) the tiles its moved blocks start, for both tile-size candidates.
 // Workgroup 0 writes the table's totals and validity to the header.  An
-// invalid table writes nothing else.  In a statistics pass the last
-// workgroup to finish reduces every workgroup's statistics into the header
-// (a count of finished workgroups, cleared by pass 1, tells it that it is
-// the last; the statistics themselves go through the coherence point).  The block before a live entry moved
+// invalid table writes nothing else.  The block before a live entry moved
 // iff the packed position after it differs from its end (a block that stays,
 // pinned or held, resets the position to its own end).
-// OUT: the pass's outputs (0: a statistics pass; kOutNew: a plan;
-// kOutSelect: a selection scan), fixed per instantiation so that each holds
-// only its own code.
+// OUT: the pass's outputs (kOutNew: a plan; kOutSelect: a selection scan),
+// fixed per instantiation so that each holds only its own code.
 template <int OUT>
 __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
     __shared__ Agg sh[kScanThreads / 64];
@@ -613,8 +585,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
     uint64_t x[4] = {ca, wa, cb, wb};
     block_reduce_stats<kScanThreads>(q, x, s_red);
     if (threadIdx.x == 0) {
-        if constexpr (OUT == 0) part_store(d.spart + g, q);  // read in this launch
-        else d.spart[g] = q;
+        d.spart[g] = q;
         if (tiles) {
             d.tpart[g] = x[0];
             d.twhole[g] = x[1];
@@ -622,26 +593,323 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
             d.twhole[kMaxScanParts + g] = x[3];
         }
     }
-    if constexpr (OUT == 0) {  // a statistics pass
-        __shared__ uint32_t s_last;
-        if (threadIdx.x == 0) {
-            uint32_t last = 1;
-            if (d.ngroups > 1) {
-                // the statistics' stores complete before the arrival is counted
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                const uint64_t done = __hip_atomic_fetch_add(&d.hdr->arrive, 1ull, __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_AGENT);
-                last = done + 1 == d.ngroups;
-            }
-            s_last = last;
-        }
-        __syncthreads();
-        if (s_last)
-            stats_finish(d.spart, d.nb, d.arena_bytes, total.mx, d.hdr, false, d.fit_need,
-                         nullptr, nullptr, true);
-    }
 }
 
+
+// ---------------------------------------------------------------------------
+// A statistics pass in one launch (the post-check of a compaction).  Each
+// workgroup summarises its chunk of entries on its own, with no prefix; the
+// few quantities that depend on the entries before the chunk are kept
+// apart:
+//   * the hole below the chunk's first live block, which starts at the
+//     highest live end before the chunk (a max over the chunks before);
+//   * which of the chunk's blocks move.  A movable live block moves iff a
+//     hole lies between the start of its segment's packed run and it.  A
+//     block after a hole inside the chunk, or in a segment that starts
+//     inside it (after a pinned block), is decided locally (`a`); the
+//     blocks packed tight from the chunk's first live block, before any
+//     pinned one (`b`), move iff the segment is *pending* there -- a hole
+//     lies between the segment's start and that block, the hole just below
+//     it included.  Pending passes from chunk to chunk: a chunk holding a
+//     pinned block sets it to whether a hole follows its last pinned block;
+//     any other chunk with live blocks ORs in its boundary hole and its
+//     inner ones; an empty chunk passes it on.
+// The last workgroup to finish (counted in the header; a plan run before
+// clears the count) reads every summary, takes the max and the pending
+// state across the (at most 1,024) chunks with two workgroup scans, and
+// completes the header, which holds the same figures as the two-launch
+// pass's.
+struct ChunkSum {
+    uint64_t cnt, lsum, mx, pcnt;  // live blocks, live bytes, highest live end (0: none), pinned
+    uint64_t bad;                  // smallest bad-entry key
+    uint64_t first;                // offset of the first live entry (kNone: none)
+    uint64_t reset;                // a pinned entry is inside
+    uint64_t pend;                 // reset: a hole follows the last pinned block; else a hole
+                                   // follows the first live block
+    uint64_t a_blocks, a_bytes;    // blocks that move whatever lies before the chunk
+    uint64_t b_blocks, b_bytes;    // blocks that move iff pending at the first live block
+    uint64_t max_gap, gaps;        // holes between live blocks inside the chunk
+    uint64_t min_fit, min_size;
+};
+static_assert(sizeof(ChunkSum) == 16 * sizeof(uint64_t), "one 128-byte summary per chunk");
+
+__global__ void k_clear_u64(uint64_t *p) {
+    if (threadIdx.x == 0) *p = 0;
+}
+
+__device__ inline void csum_store(ChunkSum *p, const ChunkSum &c) {
+    uint64_t *w = reinterpret_cast<uint64_t *>(p);
+    const uint64_t *v = reinterpret_cast<const uint64_t *>(&c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) __hip_atomic_store(w + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline ChunkSum csum_load(const ChunkSum *p) {
+    uint64_t *w = const_cast<uint64_t *>(reinterpret_cast<const uint64_t *>(p));
+    ChunkSum c;
+    uint64_t *v = reinterpret_cast<uint64_t *>(&c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = __hip_atomic_load(w + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return c;
+}
+
+// Exclusive workgroup scan of a u64 under max; also returns the total.
+template <int NT>
+__device__ inline uint64_t block_excl_max(uint64_t x, uint64_t &total, uint64_t *sh) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    uint64_t inc = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint64_t y = __shfl_up(inc, d, 64);
+        if (lane >= d) inc = umax64(inc, y);
+    }
+    if (lane == 63) sh[w] = inc;
+    __syncthreads();
+    uint64_t pre = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+        if (k < w) pre = umax64(pre, sh[k]);
+        tot = umax64(tot, sh[k]);
+    }
+    uint64_t ex = __shfl_up(inc, 1, 64);
+    if (lane == 0) ex = 0;
+    __syncthreads();
+    total = tot;
+    return umax64(pre, ex);
+}
+
+// The pending state as a function of the state before a chunk: constant
+// (a pinned block inside sets it) or "or v" (bit 1: constant, bit 0: v).
+// first then second:
+__device__ inline uint32_t pend_then(uint32_t f, uint32_t g) {
+    if (g & 2u) return g;
+    return (f & 2u) | ((f | g) & 1u);
+}
+
+// Exclusive workgroup scan of pending functions (the identity is "or 0").
+template <int NT>
+__device__ inline uint32_t block_excl_pend(uint32_t x, uint32_t *sh) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    uint32_t inc = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(inc, d, 64);
+        if (lane >= d) inc = pend_then(y, inc);
+    }
+    if (lane == 63) sh[w] = inc;
+    __syncthreads();
+    uint32_t pre = 0u;
+#pragma unroll
+    for (int k = 0; k < NW; ++k)
+        if (k < w) pre = pend_then(pre, sh[k]);
+    uint32_t ex = __shfl_up(inc, 1, 64);
+    if (lane == 0) ex = 0u;
+    __syncthreads();
+    return pend_then(pre, ex);
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_stats_one(TableView t, uint64_t arena_bytes,
+                                                            uint64_t chunk, uint64_t ngroups,
+                                                            ChunkSum *cs, WsHeader *hdr,
+                                                            uint64_t fit_need) {
+    __shared__ Agg sh[kScanThreads / 64];
+    __shared__ uint64_t shr[kScanThreads / 64];
+    __shared__ uint64_t s_red[12 * (kScanThreads / 64)];
+    __shared__ uint32_t shp[kScanThreads / 64];
+    __shared__ uint32_t s_last;
+    uint64_t n;
+    if (!table_entries(t, &n)) return;  // a gated table whose plan failed
+    const uint64_t g = blockIdx.x;
+    const uint64_t base = g * chunk;
+    const uint64_t end = umin64(base + chunk, n);
+    const Window win = window_of(nullptr);
+    Agg carry = agg_zero();  // this chunk's own, from zero
+    uint64_t first = kNone;  // (workgroup-uniform)
+    uint64_t bad = kNone, max_gap = 0, gaps = 0, min_fit = kNone, min_size = kNone;
+    uint64_t a_blocks = 0, a_bytes = 0, b_blocks = 0, b_bytes = 0;
+    for (uint64_t s0 = base; s0 < end; s0 += kScanTile) {
+        const uint64_t i0 = s0 + (uint64_t)threadIdx.x * kScanItems;
+        uint64_t o[kScanItems], s[kScanItems];
+        uint32_t l[kScanItems], p[kScanItems], f[kScanItems];
+        uint64_t prev_end = 0, my_first = kNone;
+        if (i0 > 0 && i0 < n) prev_end = t.off[i0 - 1] + t.size[i0 - 1];
+        Agg a = agg_zero();
+#pragma unroll
+        for (uint32_t k = 0; k < kScanItems; ++k) {
+            const uint64_t i = i0 + k;
+            o[k] = s[k] = 0;
+            l[k] = p[k] = f[k] = 0;
+            if (i < n) {
+                o[k] = t.off[i];
+                s[k] = t.size[i];
+                const uint32_t lr = live_of(t, i), pr = pin_of(t, i);  // as given: checked below
+                l[k] = lr ? 1u : 0u;
+                p[k] = pr ? 1u : 0u;
+                f[k] = stays(o[k], l[k], p[k], win);
+                const uint32_t r = entry_reason(i, o[k], s[k], lr, pr, arena_bytes, prev_end);
+                if (r) bad = umin64(bad, (i << 3) | r);
+                prev_end = o[k] + s[k];
+                if (l[k] && my_first == kNone) my_first = o[k];
+                a = combine(a, element(o[k], s[k], l[k], p[k], f[k]));
+            }
+        }
+        // offsets ascend, so the chunk's first live entry has the least
+        // offset among its live ones
+        if (first == kNone) first = block_reduce<kScanThreads>(my_first, shr, OpMin());
+        Agg tot;
+        const Agg ex = block_excl<kScanThreads>(a, tot, sh);
+        Agg run = combine(carry, ex);
+        carry = combine(carry, tot);
+#pragma unroll
+        for (uint32_t k = 0; k < kScanItems; ++k) {
+            if (i0 + k >= n) continue;
+            if (l[k]) {
+                if (run.cnt) {  // the hole below this block lies inside the chunk
+                    const uint64_t gap = o[k] - run.mx;
+                    if (gap) {
+                        gaps += 1;
+                        max_gap = umax64(max_gap, gap);
+                        if (gap >= fit_need) min_fit = umin64(min_fit, run.mx);
+                    }
+                }
+                min_size = umin64(min_size, s[k]);
+                if (!f[k]) {
+                    if (run.r) {  // its segment starts inside the chunk: packed at run.v
+                        if (o[k] != run.v) {
+                            a_blocks += 1;
+                            a_bytes += s[k];
+                        }
+                    } else if (o[k] - run.v != first) {  // a hole since the first live block
+                        a_blocks += 1;
+                        a_bytes += s[k];
+                    } else {  // packed tight from the first live block
+                        b_blocks += 1;
+                        b_bytes += s[k];
+                    }
+                }
+            }
+            run = combine(run, element(o[k], s[k], l[k], p[k], f[k]));
+        }
+    }
+    StatPart q{max_gap, gaps, a_blocks, a_bytes, bad, min_size, min_fit, 0};
+    uint64_t x[4] = {b_blocks, b_bytes, 0, 0};
+    block_reduce_stats<kScanThreads>(q, x, s_red);
+    if (threadIdx.x == 0) {
+        ChunkSum c;
+        c.cnt = carry.cnt;
+        c.lsum = carry.lsum;
+        c.mx = carry.mx;
+        c.pcnt = carry.pcnt;
+        c.bad = q.min_moved_dst;  // (the bad key rode in that min slot)
+        c.first = first;
+        c.reset = carry.r ? 1u : 0u;
+        c.pend = carry.r ? (carry.v < carry.mx ? 1u : 0u)
+                         : (first != kNone && first + carry.v < carry.mx ? 1u : 0u);
+        c.a_blocks = q.moved_blocks;
+        c.a_bytes = q.moved_bytes;
+        c.b_blocks = x[0];
+        c.b_bytes = x[1];
+        c.max_gap = q.max_gap;
+        c.gaps = q.gaps;
+        c.min_fit = q.min_fit;
+        c.min_size = q.min_size;
+        csum_store(cs + g, c);
+        uint32_t last = 1;
+        if (ngroups > 1) {
+            // the summary's stores complete before the arrival is counted
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            const uint64_t done = __hip_atomic_fetch_add(&hdr->arrive, 1ull, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            last = done + 1 == ngroups;
+        }
+        s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+
+    // the last workgroup: chunks [threadIdx.x * kPer, + kPer)
+    constexpr uint32_t kPer = kMaxScanParts / kScanThreads;
+    const uint64_t j0 = (uint64_t)threadIdx.x * kPer;
+    ChunkSum c[kPer];
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k) {
+        if (j0 + k < ngroups) {
+            c[k] = csum_load(cs + j0 + k);
+        } else {
+            c[k] = ChunkSum{0, 0, 0, 0, kNone, kNone, 0, 0, 0, 0, 0, 0, 0, 0, kNone, kNone};
+        }
+    }
+    // the highest live end before each chunk
+    uint64_t mx_in[kPer];
+    uint64_t loc = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k) {
+        mx_in[k] = loc;
+        loc = umax64(loc, c[k].mx);
+    }
+    uint64_t max_end;
+    const uint64_t mx_ex = block_excl_max<kScanThreads>(loc, max_end, shr);
+    // the hole below each chunk's first live block, and its pending function
+    uint32_t fn[kPer], hole[kPer];
+    uint32_t mine = 0u;  // this thread's chunks, composed
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k) {
+        mx_in[k] = umax64(mx_in[k], mx_ex);
+        hole[k] = (c[k].first != kNone && mx_in[k] < c[k].first) ? 1u : 0u;
+        fn[k] = c[k].first == kNone ? 0u
+                : c[k].reset       ? (2u | (uint32_t)c[k].pend)
+                                   : ((hole[k] | (uint32_t)c[k].pend) & 1u);
+        mine = pend_then(mine, fn[k]);
+    }
+    uint32_t pend = block_excl_pend<kScanThreads>(mine, shp) & 1u;  // state before chunk j0
+    StatPart r{0, 0, 0, 0, kNone, kNone, kNone, 0};
+    uint64_t tx[4] = {0, 0, 0, 0};  // live blocks, live bytes, pinned blocks
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k) {
+        const uint64_t pend_first = pend | hole[k];  // pending at the chunk's first live block
+        r.moved_blocks += c[k].a_blocks + (pend_first ? c[k].b_blocks : 0);
+        r.moved_bytes += c[k].a_bytes + (pend_first ? c[k].b_bytes : 0);
+        r.gaps += c[k].gaps + hole[k];
+        r.max_gap = umax64(r.max_gap, c[k].max_gap);
+        r.min_fit = umin64(r.min_fit, c[k].min_fit);
+        if (hole[k]) {
+            const uint64_t gap = c[k].first - mx_in[k];
+            r.max_gap = umax64(r.max_gap, gap);
+            if (gap >= fit_need) r.min_fit = umin64(r.min_fit, mx_in[k]);
+        }
+        r.min_moved_dst = umin64(r.min_moved_dst, c[k].bad);
+        r.min_size = umin64(r.min_size, c[k].min_size);
+        tx[0] += c[k].cnt;
+        tx[1] += c[k].lsum;
+        tx[2] += c[k].pcnt;
+        pend = pend_then(pend, fn[k]) & 1u;
+    }
+    block_reduce_stats<kScanThreads>(r, tx, s_red);
+    if (threadIdx.x == 0) {
+        hdr->live_bytes = tx[1];
+        hdr->max_live_end = max_end;
+        hdr->live_blocks = tx[0];
+        hdr->pinned_blocks = tx[2];
+        hdr->bad_key = r.min_moved_dst;
+        hdr->win_state = kWinNone;
+        const uint64_t tail = arena_bytes - max_end;
+        uint64_t fit = r.min_fit;
+        // holes below live blocks come first in address order; the tail last
+        if (fit == kNone && tail && tail >= fit_need) fit = max_end;
+        hdr->fit_offset = fit;
+        hdr->largest_hole = umax64(r.max_gap, tail);
+        hdr->hole_count = r.gaps + (tail ? 1 : 0);
+        hdr->moved_blocks = r.moved_blocks;
+        hdr->moved_bytes = r.moved_bytes;
+        hdr->small_moved = 0;
+        hdr->min_live_size = r.min_size;
+        hdr->move_begin = kNone;
+        hdr->arrive = 0;  // every pass leaves it cleared
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Tiles.  A run is a maximal sequence of moved live blocks; its destinations
@@ -724,6 +992,7 @@ struct BaseArgs {
     uint64_t arena_bytes;
     WsHeader *hdr;
     uint64_t *clear;  // set to zero (or null)
+    uint64_t *arrive_post;  // the statistics header's count of finished workgroups
 };
 
 // Pass 3 of a plan.  Workgroups [0, nb): the tile size (every workgroup
@@ -740,7 +1009,10 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
     __shared__ uint64_t s_red[12 * (kScanThreads / 64)];
     __shared__ uint64_t s_before;
     WsHeader *hdr = a.hdr;
-    if (a.clear && blockIdx.x == 0 && threadIdx.x == 0) *a.clear = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (a.clear) *a.clear = 0;
+        *a.arrive_post = 0;  // for a one-launch statistics pass after this plan
+    }
     const uint64_t g = blockIdx.x;
     if (g >= a.nb) {
         const uint64_t m = hdr->live_blocks;
@@ -1168,23 +1440,18 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
     // pass 1: aggregates
     if (d.nb) {
         hipLaunchKernelGGL(k_scan_partials, dim3((uint32_t)d.nb), dim3(kScanThreads), 0, s, t,
-                           arena_bytes, win, (uint64_t)L.scan_chunk, part,
-                           outputs == 0 ? &hdr->arrive : nullptr);
+                           arena_bytes, win, (uint64_t)L.scan_chunk, part);
         AC_TRY(hipGetLastError());
     }
     // pass 2: each workgroup's prefix, then its entries
-    if (outputs == 0)
-        hipLaunchKernelGGL(k_scan_down<0>, dim3((uint32_t)d.ngroups), dim3(kScanThreads), 0, s, d);
-    else if (outputs == kOutNew)
+    if (outputs == kOutNew)
         hipLaunchKernelGGL(k_scan_down<kOutNew>, dim3((uint32_t)d.ngroups), dim3(kScanThreads), 0,
                            s, d);
     else
         hipLaunchKernelGGL(k_scan_down<kOutSelect>, dim3((uint32_t)d.ngroups), dim3(kScanThreads),
                            0, s, d);
     AC_TRY(hipGetLastError());
-    // a statistics pass ends there (its last workgroup finishes it), and so
-    // does a selection scan
-    if (!(outputs & kOutNew)) return hipSuccess;
+    if (!(outputs & kOutNew)) return hipSuccess;  // a selection scan ends there
     // pass 3: tile size, the blocks' first tiles and the header's finish;
     // the remap index beside them
     const LiveView lv = live_view(ws, L);
@@ -1206,6 +1473,7 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
     b.arena_bytes = arena_bytes;
     b.hdr = hdr;
     b.clear = clear;
+    b.arrive_post = &reinterpret_cast<WsHeader *>(ws + L.post)->arrive;
     const uint64_t rblocks = (b.rnb + 1 + kScanThreads - 1) / kScanThreads;
     hipLaunchKernelGGL(k_plan_bases, dim3((uint32_t)(d.ngroups + rblocks)), dim3(kScanThreads), 0,
                        s, b);
@@ -1252,6 +1520,21 @@ hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t re
     AC_TRY(hipGetLastError());
     return queue_scan(t, arena_bytes, ws, L, new_offset, kOutNew, &hdr->win_begin, tiles,
                       epoch, kNone, clear, s);
+}
+
+hipError_t launch_stats_one(const TableView &t, uint64_t arena_bytes, uint8_t *ws,
+                            const WsLayout &L, uint64_t fit_need, bool after_plan,
+                            hipStream_t s) {
+    const uint64_t ngroups = L.n_scan_blocks ? L.n_scan_blocks : 1;
+    WsHeader *hdr = reinterpret_cast<WsHeader *>(ws + L.header);
+    if (!after_plan && ngroups > 1) {
+        hipLaunchKernelGGL(k_clear_u64, dim3(1), dim3(64), 0, s, &hdr->arrive);
+        AC_TRY(hipGetLastError());
+    }
+    hipLaunchKernelGGL(k_stats_one, dim3((uint32_t)ngroups), dim3(kScanThreads), 0, s, t,
+                       arena_bytes, (uint64_t)L.scan_chunk, ngroups,
+                       reinterpret_cast<ChunkSum *>(ws + L.csum), hdr, fit_need);
+    return hipGetLastError();
 }
 
 hipError_t launch_commit(const uint8_t *ws, const WsLayout &L, uint64_t live_blocks,
