@@ -420,6 +420,70 @@ __device__ void stats_finish(const StatPart *spart, uint64_t nb, uint64_t arena_
     }
 }
 
+// What a workgroup's entries add up to in the down-sweep: hole and move
+// statistics, and the tiles its moved blocks start (and the whole windows
+// they fill) for both candidate tile sizes.
+struct DownAcc {
+    uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, min_dst = kNone,
+             min_size = kNone, min_fit = kNone, small_moved = 0, ca = 0, wa = 0, cb = 0, wb = 0;
+};
+
+// One entry of the down-sweep: entry i (offset o, size s, live l, pinned p,
+// stays f) after the scan state `run` of the entries before it.  Writes its
+// new offset and, if live, its packed-array entries (at index run.cnt);
+// adds to `acc`; leaves `run` past it.  OUT: the pass's outputs.
+template <int OUT>
+__device__ inline void down_item(uint64_t i, uint64_t o, uint64_t s, uint32_t l, uint32_t p,
+                                 uint32_t f, Agg &run, uint64_t *new_offset, const LiveOut &lo,
+                                 uint64_t fit_need, TileChoice tc, DownAcc &acc) {
+    const uint64_t nw = f ? o : run.v;
+    if ((OUT & kOutNew) && new_offset) new_offset[i] = nw;
+    if (l) {
+        if constexpr ((OUT & kOutNew) != 0) {
+            lo.dst[run.cnt] = nw;
+            lo.pin[run.cnt] = (uint8_t)p;
+            if (lo.ent)
+                lo.ent[run.cnt] = RemapEnt{(uint32_t)(o & lo.key_mask), (uint32_t)((o + s) >> 5),
+                                           (uint32_t)((o - nw) >> 5), 0u};
+            else if (lo.rec32)
+                lo.rec32[run.cnt] = LiveRec32{(uint32_t)((o + s) >> 5), (uint32_t)((o - nw) >> 5)};
+            else
+                lo.rec[run.cnt] = LiveRec{o + s, o - nw};
+            if (lo.key) lo.key[run.cnt] = (uint32_t)(o & lo.key_mask);
+        }
+        if constexpr ((OUT & (kOutNew | kOutSelect)) != 0) {
+            lo.src[run.cnt] = o;
+            lo.size[run.cnt] = s;
+        }
+        if constexpr ((OUT & kOutSelect) != 0) {
+            lo.z[run.cnt] = run.lsum;
+            lo.pc[run.cnt] = (uint32_t)run.pcnt;
+        }
+        const uint64_t gap = o - run.mx;
+        if (gap) {
+            acc.gaps += 1;
+            acc.max_gap = umax64(acc.max_gap, gap);
+            if (gap >= fit_need) acc.min_fit = umin64(acc.min_fit, run.mx);
+        }
+        if (o != nw) {
+            acc.moved += 1;
+            acc.moved_bytes += s;
+            acc.min_dst = umin64(acc.min_dst, nw);
+            if (o - nw < kAutoSmallShift) acc.small_moved += s;
+            if constexpr ((OUT & kOutNew) != 0) {
+                // the live block before this one moved: the run goes on
+                const bool start = !(run.cnt > 0 && run.v != run.mx);
+                acc.ca += tiles_of(nw, s, start, tc.a);
+                acc.wa += whole_of(nw, s, tc.a);
+                acc.cb += tiles_of(nw, s, start, tc.b);
+                acc.wb += whole_of(nw, s, tc.b);
+            }
+        }
+        acc.min_size = umin64(acc.min_size, s);
+    }
+    run = combine(run, element(o, s, l, p, f));
+}
+
 struct DownArgs {
     TableView t;
     const uint64_t *win;      // a targeted plan's window (in its header), or null
@@ -503,10 +567,8 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
     const Window w = window_of(d.win);
     constexpr bool tiles = (OUT & kOutNew) != 0;
     if (tiles && threadIdx.x == 0) d.lbase[g] = before.cnt;
-    const uint64_t Ta = d.tiles.a, Tb = d.tiles.b;
     Agg carry = before;
-    uint64_t max_gap = 0, gaps = 0, moved = 0, moved_bytes = 0, min_dst = kNone, min_size = kNone;
-    uint64_t min_fit = kNone, small_moved = 0, ca = 0, wa = 0, cb = 0, wb = 0;
+    DownAcc acc;
     for (uint64_t s0 = base; s0 < end; s0 += kScanTile) {
         if (s0 != base) load(s0);
         const uint64_t i0 = s0 + (uint64_t)threadIdx.x * kScanItems;
@@ -528,61 +590,14 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
 #pragma unroll
         for (uint32_t k = 0; k < kScanItems; ++k) {
             const uint64_t i = i0 + k;
-            if (i < n) {
-                const uint64_t nw = f[k] ? o[k] : run.v;
-                if ((OUT & kOutNew) && d.new_offset) d.new_offset[i] = nw;
-                if (l[k]) {
-                    const LiveOut &lo = d.lo;
-                    if constexpr ((OUT & kOutNew) != 0) {
-                        lo.dst[run.cnt] = nw;
-                        lo.pin[run.cnt] = (uint8_t)p[k];
-                        if (lo.ent)
-                            lo.ent[run.cnt] = RemapEnt{(uint32_t)(o[k] & lo.key_mask),
-                                                       (uint32_t)((o[k] + s[k]) >> 5),
-                                                       (uint32_t)((o[k] - nw) >> 5), 0u};
-                        else if (lo.rec32)
-                            lo.rec32[run.cnt] = LiveRec32{(uint32_t)((o[k] + s[k]) >> 5),
-                                                          (uint32_t)((o[k] - nw) >> 5)};
-                        else
-                            lo.rec[run.cnt] = LiveRec{o[k] + s[k], o[k] - nw};
-                        if (lo.key) lo.key[run.cnt] = (uint32_t)(o[k] & lo.key_mask);
-                    }
-                    if constexpr ((OUT & (kOutNew | kOutSelect)) != 0) {
-                        lo.src[run.cnt] = o[k];
-                        lo.size[run.cnt] = s[k];
-                    }
-                    if constexpr ((OUT & kOutSelect) != 0) {
-                        lo.z[run.cnt] = run.lsum;
-                        lo.pc[run.cnt] = (uint32_t)run.pcnt;
-                    }
-                    const uint64_t gap = o[k] - run.mx;
-                    if (gap) {
-                        gaps += 1;
-                        max_gap = umax64(max_gap, gap);
-                        if (gap >= d.fit_need) min_fit = umin64(min_fit, run.mx);
-                    }
-                    if (o[k] != nw) {
-                        moved += 1;
-                        moved_bytes += s[k];
-                        min_dst = umin64(min_dst, nw);
-                        if (o[k] - nw < kAutoSmallShift) small_moved += s[k];
-                        if (tiles) {
-                            // the live block before this one moved: the run goes on
-                            const bool start = !(run.cnt > 0 && run.v != run.mx);
-                            ca += tiles_of(nw, s[k], start, Ta);
-                            wa += whole_of(nw, s[k], Ta);
-                            cb += tiles_of(nw, s[k], start, Tb);
-                            wb += whole_of(nw, s[k], Tb);
-                        }
-                    }
-                    min_size = umin64(min_size, s[k]);
-                }
-                run = combine(run, element(o[k], s[k], l[k], p[k], f[k]));
-            }
+            if (i < n)
+                down_item<OUT>(i, o[k], s[k], l[k], p[k], f[k], run, d.new_offset, d.lo,
+                               d.fit_need, d.tiles, acc);
         }
     }  // steps of the chunk
-    StatPart q{max_gap, gaps, moved, moved_bytes, min_dst, min_size, min_fit, small_moved};
-    uint64_t x[4] = {ca, wa, cb, wb};
+    StatPart q{acc.max_gap, acc.gaps, acc.moved, acc.moved_bytes, acc.min_dst, acc.min_size,
+               acc.min_fit, acc.small_moved};
+    uint64_t x[4] = {acc.ca, acc.wa, acc.cb, acc.wb};
     block_reduce_stats<kScanThreads>(q, x, s_red);
     if (threadIdx.x == 0) {
         d.spart[g] = q;
@@ -1125,13 +1140,72 @@ __device__ inline uint64_t tile_of(const LiveView &lv, const uint32_t *tile_base
     return lead ? tile_base[b] : tile_base[b] - 1;
 }
 
-// Pass 4: one lane per tile.  [t0, t1) = the run's bytes from the tile start
-// up to the next tile start, the window end or the run end.  A tile may write
-// only once every tile whose sources overlap [t0, t1) has read them.  Sources
-// rise strictly with destinations (src = dst + shift, shifts never negative,
+// Tile t's record, given its start t0, its first block and its end bound
+// (the next tile's start or the window's end).  [t0, t1) = the run's bytes
+// from t0 up to the bound or the run's end.  A tile may write only once
+// every tile whose sources overlap [t0, t1) has read them.  Sources rise
+// strictly with destinations (src = dst + shift, shifts never negative,
 // order kept), so the destinations whose sources lie in [t0, t1) are at most
-// t1 - t0 consecutive live bytes, all at or below [t0, t1): their tiles are a
-// short range ending at or before this one.
+// t1 - t0 consecutive live bytes, all at or below [t0, t1): their tiles are
+// a short range ending at or before this one.  ridx: the remap's bucket
+// index (bucket width 2^w), which narrows the search for the first such
+// block, or null to search all m blocks.
+__device__ inline TileRec tile_record(const LiveView &lv, const uint32_t *tile_base, uint64_t m,
+                                      uint64_t t, uint64_t t0, uint64_t first, uint64_t bound,
+                                      uint64_t T, const uint32_t *ridx, uint32_t w) {
+    // last block of the run inside [t0, bound): blocks after first that start
+    // below bound and moved form a prefix -- gallop, then bisect
+    uint64_t last = first, stride = 1;
+    while (last + stride < m && lv.dst[last + stride] < bound && moved_at(lv, last + stride)) {
+        last += stride;
+        stride <<= 1;
+    }
+    for (; stride > 0; stride >>= 1)
+        if (last + stride < m && lv.dst[last + stride] < bound && moved_at(lv, last + stride))
+            last += stride;
+    const uint64_t t1 = umin64(bound, lv.dst[last] + lv.size[last]);
+    // sources overlapping [t0, t1): first block whose source ends above t0.
+    // The remap index narrows it to the blocks starting in t0's bucket and
+    // the one before them: an earlier block ends before the bucket starts,
+    // and the first block of the next bucket already ends above t0.
+    int64_t lo = 0, hi = (int64_t)m;
+    if (ridx) {
+        const uint64_t bk = t0 >> w;
+        lo = ridx[bk] ? (int64_t)ridx[bk] - 1 : 0;
+        hi = (int64_t)ridx[bk + 1];
+    }
+    while (lo < hi) {
+        const int64_t mid = lo + ((hi - lo) >> 1);
+        if (lv.src[mid] + lv.size[mid] <= t0) lo = mid + 1;
+        else hi = mid;
+    }
+    uint32_t dep_lo = 1, dep_hi = 0;  // empty
+    if (lo < (int64_t)m && lv.src[lo] < t1 && t > 0) {
+        const uint64_t j = (uint64_t)lo;
+        const uint64_t q_lo = lv.dst[j] + (t0 > lv.src[j] ? t0 - lv.src[j] : 0);
+        // ... and the last block whose source starts below t1 (gallop from j)
+        uint64_t c = j;
+        stride = 1;
+        while (c + stride < m && lv.src[c + stride] < t1) {
+            c += stride;
+            stride <<= 1;
+        }
+        for (; stride > 0; stride >>= 1)
+            if (c + stride < m && lv.src[c + stride] < t1) c += stride;
+        const uint64_t q_hi = lv.dst[c] + umin64(lv.size[c], t1 - lv.src[c]) - 1;
+        const uint64_t u_lo = tile_of(lv, tile_base, j, q_lo, T);
+        uint64_t u_hi = tile_of(lv, tile_base, c, q_hi, T);
+        if (u_hi > t - 1) u_hi = t - 1;
+        if (u_lo <= u_hi) {
+            dep_lo = (uint32_t)u_lo;
+            dep_hi = (uint32_t)u_hi;
+        }
+    }
+    return TileRec{t0, t1, lv.src[first] - lv.dst[first], (uint32_t)first, (uint32_t)last,
+                   dep_lo, dep_hi, 0};
+}
+
+// Pass 4: one lane per tile, each writing its record (tile_record).
 //
 // Each tile's first block is the last block whose first tile index is <= t
 // (a search over tile_base).  The workgroup's tiles [tb, tb + 256) -- and the
@@ -1196,52 +1270,7 @@ __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint32_t *tile
     if (t >= n_tiles) return;
     uint64_t bound = (t0 & ~(T - 1)) + T;
     if (t + 1 < n_tiles) bound = umin64(bound, s_t0[threadIdx.x + 1]);
-    // last block of the run inside [t0, bound): blocks after first that start
-    // below bound and moved form a prefix -- gallop, then bisect
-    uint64_t last = first, stride = 1;
-    while (last + stride < m && lv.dst[last + stride] < bound && moved_at(lv, last + stride)) {
-        last += stride;
-        stride <<= 1;
-    }
-    for (; stride > 0; stride >>= 1)
-        if (last + stride < m && lv.dst[last + stride] < bound && moved_at(lv, last + stride))
-            last += stride;
-    const uint64_t t1 = umin64(bound, lv.dst[last] + lv.size[last]);
-    // sources overlapping [t0, t1): first block whose source ends above t0.
-    // The remap index narrows it to the blocks starting in t0's bucket and
-    // the one before them: an earlier block ends before the bucket starts,
-    // and the first block of the next bucket already ends above t0.
-    const uint64_t bk = t0 >> w;
-    int64_t lo = ridx[bk] ? (int64_t)ridx[bk] - 1 : 0, hi = (int64_t)ridx[bk + 1];
-    while (lo < hi) {
-        const int64_t mid = lo + ((hi - lo) >> 1);
-        if (lv.src[mid] + lv.size[mid] <= t0) lo = mid + 1;
-        else hi = mid;
-    }
-    uint32_t dep_lo = 1, dep_hi = 0;  // empty
-    if (lo < (int64_t)m && lv.src[lo] < t1 && t > 0) {
-        const uint64_t j = (uint64_t)lo;
-        const uint64_t q_lo = lv.dst[j] + (t0 > lv.src[j] ? t0 - lv.src[j] : 0);
-        // ... and the last block whose source starts below t1 (gallop from j)
-        uint64_t c = j;
-        stride = 1;
-        while (c + stride < m && lv.src[c + stride] < t1) {
-            c += stride;
-            stride <<= 1;
-        }
-        for (; stride > 0; stride >>= 1)
-            if (c + stride < m && lv.src[c + stride] < t1) c += stride;
-        const uint64_t q_hi = lv.dst[c] + umin64(lv.size[c], t1 - lv.src[c]) - 1;
-        const uint64_t u_lo = tile_of(lv, tile_base, j, q_lo, T);
-        uint64_t u_hi = tile_of(lv, tile_base, c, q_hi, T);
-        if (u_hi > t - 1) u_hi = t - 1;
-        if (u_lo <= u_hi) {
-            dep_lo = (uint32_t)u_lo;
-            dep_hi = (uint32_t)u_hi;
-        }
-    }
-    tiles[t] = TileRec{t0, t1, lv.src[first] - lv.dst[first], (uint32_t)first, (uint32_t)last,
-                       dep_lo, dep_hi, 0};
+    tiles[t] = tile_record(lv, tile_base, m, t, t0, first, bound, T, ridx, w);
     flags[t] = 0u;
 }
 
@@ -1437,6 +1466,7 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
     d.fit_need = fit_need;
     d.epoch = epoch;
     d.arena_bytes = arena_bytes;
+
     // pass 1: aggregates
     if (d.nb) {
         hipLaunchKernelGGL(k_scan_partials, dim3((uint32_t)d.nb), dim3(kScanThreads), 0, s, t,
