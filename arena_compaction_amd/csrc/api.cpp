@@ -172,15 +172,12 @@ int stats_pass(const defrag_table *table, uint64_t arena_bytes, uint64_t fit_nee
     return h->bad_key == kNone ? DEFRAG_OK : DEFRAG_EINVAL;
 }
 
-// The one-call path's post-check, queued (on the side stream, while the move
-// may still run): the statistics pass of the packed table, with its own
-// header (the move reads the plan's header as it starts) and otherwise only
-// the fixed statistics region in front of the plan's data.  With a gate (the
-// plan's header, queued before the plan is read back) packed->n is an upper
-// bound: the passes take the plan's live count, and nothing if it failed.
+// The post-check of the plain order (compact_serial), queued: the
+// statistics pass of the packed table, with its own header (a plan's header
+// is never written by it) and otherwise only the fixed statistics region in
+// front of the plan's data; one launch, after the plan on this workspace.
 int post_check_queue(const defrag_table *packed, uint64_t arena_bytes, void *ws_dev,
-                     size_t ws_bytes, const WsHeader *gate, uint64_t max_tiles,
-                     hipStream_t stream) {
+                     size_t ws_bytes, hipStream_t stream) {
     int rc = check_table(packed);
     if (rc) return rc;
     WsLayout L = ws_fixed(packed->n);
@@ -188,10 +185,8 @@ int post_check_queue(const defrag_table *packed, uint64_t arena_bytes, void *ws_
     if (rc) return rc;
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
     L.header = L.post;
-    TableView v = view_of(packed);
-    v.gate = gate;
-    v.gate_max_tiles = max_tiles;
-    return launch_stats_one(v, arena_bytes, ws, L, kNone, true, stream) == hipSuccess
+    return launch_stats_one(view_of(packed), arena_bytes, ws, L, kNone, true, stream) ==
+                   hipSuccess
                ? DEFRAG_OK
                : DEFRAG_EHIP;
 }
@@ -410,8 +405,7 @@ int compact_serial(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     if (after_host) {
         const defrag_table packed{a->offset_out_dev, a->size_out_dev, a->live_out_dev,
                                   plan->live_blocks, a->pinned_out_dev};
-        rc = post_check_queue(&packed, a->arena_bytes, a->ws_dev, a->ws_bytes, nullptr, 0,
-                              stream);
+        rc = post_check_queue(&packed, a->arena_bytes, a->ws_dev, a->ws_bytes, stream);
         if (rc) {
             arg_error(after_host);
             return rc;
@@ -559,7 +553,8 @@ int defrag_remap(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes,
     const WsLayout L = plan_layout(plan);
     const uint8_t *ws = static_cast<const uint8_t *>(ws_dev);
     if (launch_remap(ws, L, plan->arena_bytes, plan->n, plan->live_blocks, h_in_dev, h_out_dev,
-                     n_handles, n_invalid_dev, nullptr, nullptr, 0, cus, stream) != hipSuccess)
+                     n_handles, n_invalid_dev, nullptr, false, nullptr, 0, cus,
+                     stream) != hipSuccess)
         return DEFRAG_EHIP;
     return DEFRAG_OK;
 }
@@ -660,21 +655,16 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     if (ok && side_work) {
         ok = hipStreamWaitEvent(side, planned, 0) == hipSuccess;
         side_queued = ok;
-        // remap and commit in one launch, before the post-check, which
-        // reads the packed table
+        // remap, commit and the post-check in one launch (the post-check
+        // takes the packed table from the plan's packed arrays, the values
+        // the commit writes)
         const CommitOut out{a->offset_out_dev, a->size_out_dev, a->live_out_dev,
                             a->pinned_out_dev};
-        if (ok && (want_commit || a->n_handles))
+        if (ok && (want_commit || a->n_handles || after_host))
             ok = launch_remap(ws, c.L, a->arena_bytes, n, n, a->h_in_dev, a->h_out_dev,
-                              a->n_handles, a->n_invalid_dev, want_commit ? &out : nullptr, gate,
-                              c.L.max_tiles, cus, side) == hipSuccess;
-        if (ok && after_host) {
-            const defrag_table packed{a->offset_out_dev, a->size_out_dev, a->live_out_dev, n,
-                                      a->pinned_out_dev};
-            rc = post_check_queue(&packed, a->arena_bytes, a->ws_dev, a->ws_bytes, gate,
-                                  c.L.max_tiles, side);
-            ok = rc == DEFRAG_OK;
-        }
+                              a->n_handles, a->n_invalid_dev, want_commit ? &out : nullptr,
+                              after_host != nullptr, gate, c.L.max_tiles, cus,
+                              side) == hipSuccess;
         if (ok)
             ok = hipEventRecord(joined, side) == hipSuccess &&
                  hipStreamWaitEvent(stream, joined, 0) == hipSuccess;

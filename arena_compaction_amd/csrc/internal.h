@@ -471,14 +471,18 @@ struct CommitOut {
 };
 // Remap n_handles handles through the plan in the workspace (n: the planned
 // table's entries).  commit: also write the packed table, in the same
-// launch.  gate (the one-call path, queued before the plan is read back):
-// the plan's header gives the live-block count (live_blocks is then the
-// most there can be), nothing is written if the plan failed, and n_invalid
-// is taken as cleared already (the plan's last pass clears it).
+// launch.  post: also the post-check, the statistics of that packed table
+// (read from the plan's packed arrays) into the statistics header, in the
+// same launch (its count of finished workgroups cleared by the plan).  gate
+// (the one-call path, queued before the plan is read back): the plan's
+// header gives the live-block count (live_blocks is then the most there can
+// be), nothing is written if the plan failed, and n_invalid is taken as
+// cleared already (the plan's last pass clears it).
 hipError_t launch_remap(const uint8_t *ws, const WsLayout &L, uint64_t arena_bytes, uint64_t n,
                         uint64_t live_blocks, const uint64_t *h_in, uint64_t *h_out,
                         uint64_t n_handles, uint64_t *n_invalid, const CommitOut *commit,
-                        const WsHeader *gate, uint64_t max_tiles, int num_cus, hipStream_t s);
+                        bool post, const WsHeader *gate, uint64_t max_tiles, int num_cus,
+                        hipStream_t s);
 
 }  // namespace ac
 

@@ -42,208 +42,10 @@
 // The whole sequence is queued at once; the host reads the header back only
 // at the end.  A statistics pass alone is one launch of its own
 // (k_stats_one), which needs no prefix.
-#include "internal.h"
+#include "stats_one.h"
 
 namespace ac {
 namespace {
-
-__device__ inline uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-__device__ inline uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
-
-__device__ inline Agg agg_zero() { return Agg{0, 0, 0, 0, 0, 0, 0}; }
-
-// Associative, not commutative: a before b.
-__device__ inline Agg combine(const Agg &a, const Agg &b) {
-    Agg c;
-    c.r = a.r | b.r;
-    c.v = b.r ? b.v : a.v + b.v;
-    c.mx = umax64(a.mx, b.mx);
-    c.cnt = a.cnt + b.cnt;
-    c.lsum = a.lsum + b.lsum;
-    c.pcnt = a.pcnt + b.pcnt;
-    c.pad = 0;
-    return c;
-}
-
-// p: the entry is pinned; f: it stays in place (pinned, or a live block
-// outside a targeted plan's window).  A block that stays starts a segment.
-__device__ inline Agg element(uint64_t o, uint64_t s, uint32_t l, uint32_t p, uint32_t f) {
-    Agg e = agg_zero();
-    if (f) {
-        e.r = 1;
-        e.v = o + s;
-    } else if (l) {
-        e.v = s;
-    }
-    if (l) {
-        e.mx = o + s;
-        e.cnt = 1;
-        e.lsum = s;
-    }
-    e.pcnt = p;
-    return e;
-}
-
-__device__ inline Agg shfl_up_agg(const Agg &a, int d) {
-    Agg b;
-    b.v = __shfl_up(a.v, d, 64);
-    b.mx = __shfl_up(a.mx, d, 64);
-    b.cnt = __shfl_up(a.cnt, d, 64);
-    b.lsum = __shfl_up(a.lsum, d, 64);
-    b.pcnt = __shfl_up(a.pcnt, d, 64);
-    b.r = __shfl_up(a.r, d, 64);
-    b.pad = 0;
-    return b;
-}
-
-// Exclusive workgroup scan in thread order; also returns the total.
-// sh needs NT/64 entries.
-template <int NT>
-__device__ inline Agg block_excl(const Agg &x, Agg &total, Agg *sh) {
-    constexpr int NW = NT / 64;
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    Agg inc = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const Agg y = shfl_up_agg(inc, d);
-        if (lane >= d) inc = combine(y, inc);
-    }
-    if (lane == 63) sh[w] = inc;
-    __syncthreads();
-    Agg pre = agg_zero(), tot = agg_zero();
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-        const Agg z = sh[k];
-        if (k < w) pre = combine(pre, z);
-        tot = combine(tot, z);
-    }
-    Agg ex = shfl_up_agg(inc, 1);
-    if (lane == 0) ex = agg_zero();
-    __syncthreads();
-    total = tot;
-    return combine(pre, ex);
-}
-
-// Exclusive workgroup sum of u64; also returns the total.  sh: NT/64 slots.
-template <int NT>
-__device__ inline uint64_t block_excl_sum(uint64_t x, uint64_t &total, uint64_t *sh) {
-    constexpr int NW = NT / 64;
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    uint64_t inc = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint64_t y = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += y;
-    }
-    if (lane == 63) sh[w] = inc;
-    __syncthreads();
-    uint64_t pre = 0, tot = 0;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-        if (k < w) pre += sh[k];
-        tot += sh[k];
-    }
-    uint64_t ex = __shfl_up(inc, 1, 64);
-    if (lane == 0) ex = 0;
-    __syncthreads();
-    total = tot;
-    return pre + ex;
-}
-
-// Workgroup reductions through LDS (NT threads, sh has NT/64 slots).
-template <int NT, typename Op>
-__device__ inline uint64_t block_reduce(uint64_t v, uint64_t *sh, Op op) {
-    constexpr int NW = NT / 64;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v = op(v, (uint64_t)__shfl_xor(v, d, 64));
-    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-    __syncthreads();
-    uint64_t r = sh[0];
-#pragma unroll
-    for (int k = 1; k < NW; ++k) r = op(r, sh[k]);
-    __syncthreads();
-    return r;
-}
-
-struct OpAdd { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return a + b; } };
-struct OpMax { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return umax64(a, b); } };
-struct OpMin { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return umin64(a, b); } };
-
-// Workgroup reduction of the statistics and up to four extra sums in one
-// LDS round trip (one barrier pair for all fields, not one per field): each
-// wave reduces with shuffles, then every thread combines the waves' values.
-// sh: 12 * NT/64 slots.
-template <int NT>
-__device__ inline void block_reduce_stats(StatPart &q, uint64_t (&x)[4], uint64_t *sh) {
-    constexpr int NW = NT / 64;
-    constexpr int F = 12;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        q.max_gap = umax64(q.max_gap, (uint64_t)__shfl_xor(q.max_gap, d, 64));
-        q.gaps += (uint64_t)__shfl_xor(q.gaps, d, 64);
-        q.moved_blocks += (uint64_t)__shfl_xor(q.moved_blocks, d, 64);
-        q.moved_bytes += (uint64_t)__shfl_xor(q.moved_bytes, d, 64);
-        q.min_moved_dst = umin64(q.min_moved_dst, (uint64_t)__shfl_xor(q.min_moved_dst, d, 64));
-        q.min_size = umin64(q.min_size, (uint64_t)__shfl_xor(q.min_size, d, 64));
-        q.min_fit = umin64(q.min_fit, (uint64_t)__shfl_xor(q.min_fit, d, 64));
-        q.small_moved += (uint64_t)__shfl_xor(q.small_moved, d, 64);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) x[k] += (uint64_t)__shfl_xor(x[k], d, 64);
-    }
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) {
-        uint64_t *o = sh + F * w;
-        o[0] = q.max_gap; o[1] = q.gaps; o[2] = q.moved_blocks; o[3] = q.moved_bytes;
-        o[4] = q.min_moved_dst; o[5] = q.min_size; o[6] = q.min_fit; o[7] = q.small_moved;
-        o[8] = x[0]; o[9] = x[1]; o[10] = x[2]; o[11] = x[3];
-    }
-    __syncthreads();
-    q = StatPart{0, 0, 0, 0, kNone, kNone, kNone, 0};
-    x[0] = x[1] = x[2] = x[3] = 0;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-        const uint64_t *o = sh + F * k;
-        q.max_gap = umax64(q.max_gap, o[0]);
-        q.gaps += o[1];
-        q.moved_blocks += o[2];
-        q.moved_bytes += o[3];
-        q.min_moved_dst = umin64(q.min_moved_dst, o[4]);
-        q.min_size = umin64(q.min_size, o[5]);
-        q.min_fit = umin64(q.min_fit, o[6]);
-        q.small_moved += o[7];
-        x[0] += o[8]; x[1] += o[9]; x[2] += o[10]; x[3] += o[11];
-    }
-    __syncthreads();
-}
-
-// Reason code of entry i (0 when it passes); checks in the documented order.
-__device__ inline uint32_t entry_reason(uint64_t i, uint64_t o, uint64_t s, uint32_t l,
-                                        uint32_t p, uint64_t arena_bytes, uint64_t prev_end) {
-    if (s == 0) return 1;
-    if ((o | s) & 31u) return 2;
-    if (l > 1u) return 3;
-    if (p > 1u || (p == 1u && l == 0u)) return 7;
-    if (o > arena_bytes || s > arena_bytes - o) return 4;
-    if (i > 0 && prev_end > o) return 5;
-    return 0;
-}
-
-__device__ inline uint32_t live_of(const TableView &t, uint64_t i) { return t.live ? t.live[i] : 1u; }
-__device__ inline uint32_t pin_of(const TableView &t, uint64_t i) { return t.pinned ? t.pinned[i] : 0u; }
-
-// A targeted plan moves only the live blocks inside its window [begin, end);
-// win is null for a full plan.
-struct Window {
-    uint64_t begin, end;
-};
-__device__ inline Window window_of(const uint64_t *win) {
-    return win ? Window{win[0], win[1]} : Window{0, kNone};
-}
-__device__ inline uint32_t stays(uint64_t o, uint32_t l, uint32_t p, const Window &w) {
-    return (p || (l && (o < w.begin || o >= w.end))) ? 1u : 0u;
-}
 
 // Nothing more to plan: the table is invalid, or no window fits the request.
 __device__ inline bool plan_dead(const WsHeader *hdr) {
@@ -611,319 +413,17 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
 }
 
 
-// ---------------------------------------------------------------------------
-// A statistics pass in one launch (the post-check of a compaction).  Each
-// workgroup summarises its chunk of entries on its own, with no prefix; the
-// few quantities that depend on the entries before the chunk are kept
-// apart:
-//   * the hole below the chunk's first live block, which starts at the
-//     highest live end before the chunk (a max over the chunks before);
-//   * which of the chunk's blocks move.  A movable live block moves iff a
-//     hole lies between the start of its segment's packed run and it.  A
-//     block after a hole inside the chunk, or in a segment that starts
-//     inside it (after a pinned block), is decided locally (`a`); the
-//     blocks packed tight from the chunk's first live block, before any
-//     pinned one (`b`), move iff the segment is *pending* there -- a hole
-//     lies between the segment's start and that block, the hole just below
-//     it included.  Pending passes from chunk to chunk: a chunk holding a
-//     pinned block sets it to whether a hole follows its last pinned block;
-//     any other chunk with live blocks ORs in its boundary hole and its
-//     inner ones; an empty chunk passes it on.
-// The last workgroup to finish (counted in the header; a plan run before
-// clears the count) reads every summary, takes the max and the pending
-// state across the (at most 1,024) chunks with two workgroup scans, and
-// completes the header, which holds the same figures as the two-launch
-// pass's.
-struct ChunkSum {
-    uint64_t cnt, lsum, mx, pcnt;  // live blocks, live bytes, highest live end (0: none), pinned
-    uint64_t bad;                  // smallest bad-entry key
-    uint64_t first;                // offset of the first live entry (kNone: none)
-    uint64_t reset;                // a pinned entry is inside
-    uint64_t pend;                 // reset: a hole follows the last pinned block; else a hole
-                                   // follows the first live block
-    uint64_t a_blocks, a_bytes;    // blocks that move whatever lies before the chunk
-    uint64_t b_blocks, b_bytes;    // blocks that move iff pending at the first live block
-    uint64_t max_gap, gaps;        // holes between live blocks inside the chunk
-    uint64_t min_fit, min_size;
-};
-static_assert(sizeof(ChunkSum) == 16 * sizeof(uint64_t), "one 128-byte summary per chunk");
-
 __global__ void k_clear_u64(uint64_t *p) {
     if (threadIdx.x == 0) *p = 0;
-}
-
-__device__ inline void csum_store(ChunkSum *p, const ChunkSum &c) {
-    uint64_t *w = reinterpret_cast<uint64_t *>(p);
-    const uint64_t *v = reinterpret_cast<const uint64_t *>(&c);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) __hip_atomic_store(w + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline ChunkSum csum_load(const ChunkSum *p) {
-    uint64_t *w = const_cast<uint64_t *>(reinterpret_cast<const uint64_t *>(p));
-    ChunkSum c;
-    uint64_t *v = reinterpret_cast<uint64_t *>(&c);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = __hip_atomic_load(w + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return c;
-}
-
-// Exclusive workgroup scan of a u64 under max; also returns the total.
-template <int NT>
-__device__ inline uint64_t block_excl_max(uint64_t x, uint64_t &total, uint64_t *sh) {
-    constexpr int NW = NT / 64;
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    uint64_t inc = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint64_t y = __shfl_up(inc, d, 64);
-        if (lane >= d) inc = umax64(inc, y);
-    }
-    if (lane == 63) sh[w] = inc;
-    __syncthreads();
-    uint64_t pre = 0, tot = 0;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-        if (k < w) pre = umax64(pre, sh[k]);
-        tot = umax64(tot, sh[k]);
-    }
-    uint64_t ex = __shfl_up(inc, 1, 64);
-    if (lane == 0) ex = 0;
-    __syncthreads();
-    total = tot;
-    return umax64(pre, ex);
-}
-
-// The pending state as a function of the state before a chunk: constant
-// (a pinned block inside sets it) or "or v" (bit 1: constant, bit 0: v).
-// first then second:
-__device__ inline uint32_t pend_then(uint32_t f, uint32_t g) {
-    if (g & 2u) return g;
-    return (f & 2u) | ((f | g) & 1u);
-}
-
-// Exclusive workgroup scan of pending functions (the identity is "or 0").
-template <int NT>
-__device__ inline uint32_t block_excl_pend(uint32_t x, uint32_t *sh) {
-    constexpr int NW = NT / 64;
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    uint32_t inc = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(inc, d, 64);
-        if (lane >= d) inc = pend_then(y, inc);
-    }
-    if (lane == 63) sh[w] = inc;
-    __syncthreads();
-    uint32_t pre = 0u;
-#pragma unroll
-    for (int k = 0; k < NW; ++k)
-        if (k < w) pre = pend_then(pre, sh[k]);
-    uint32_t ex = __shfl_up(inc, 1, 64);
-    if (lane == 0) ex = 0u;
-    __syncthreads();
-    return pend_then(pre, ex);
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_stats_one(TableView t, uint64_t arena_bytes,
                                                             uint64_t chunk, uint64_t ngroups,
                                                             ChunkSum *cs, WsHeader *hdr,
                                                             uint64_t fit_need) {
-    __shared__ Agg sh[kScanThreads / 64];
-    __shared__ uint64_t shr[kScanThreads / 64];
-    __shared__ uint64_t s_red[12 * (kScanThreads / 64)];
-    __shared__ uint32_t shp[kScanThreads / 64];
-    __shared__ uint32_t s_last;
     uint64_t n;
     if (!table_entries(t, &n)) return;  // a gated table whose plan failed
-    const uint64_t g = blockIdx.x;
-    const uint64_t base = g * chunk;
-    const uint64_t end = umin64(base + chunk, n);
-    const Window win = window_of(nullptr);
-    Agg carry = agg_zero();  // this chunk's own, from zero
-    uint64_t first = kNone;  // (workgroup-uniform)
-    uint64_t bad = kNone, max_gap = 0, gaps = 0, min_fit = kNone, min_size = kNone;
-    uint64_t a_blocks = 0, a_bytes = 0, b_blocks = 0, b_bytes = 0;
-    for (uint64_t s0 = base; s0 < end; s0 += kScanTile) {
-        const uint64_t i0 = s0 + (uint64_t)threadIdx.x * kScanItems;
-        uint64_t o[kScanItems], s[kScanItems];
-        uint32_t l[kScanItems], p[kScanItems], f[kScanItems];
-        uint64_t prev_end = 0, my_first = kNone;
-        if (i0 > 0 && i0 < n) prev_end = t.off[i0 - 1] + t.size[i0 - 1];
-        Agg a = agg_zero();
-#pragma unroll
-        for (uint32_t k = 0; k < kScanItems; ++k) {
-            const uint64_t i = i0 + k;
-            o[k] = s[k] = 0;
-            l[k] = p[k] = f[k] = 0;
-            if (i < n) {
-                o[k] = t.off[i];
-                s[k] = t.size[i];
-                const uint32_t lr = live_of(t, i), pr = pin_of(t, i);  // as given: checked below
-                l[k] = lr ? 1u : 0u;
-                p[k] = pr ? 1u : 0u;
-                f[k] = stays(o[k], l[k], p[k], win);
-                const uint32_t r = entry_reason(i, o[k], s[k], lr, pr, arena_bytes, prev_end);
-                if (r) bad = umin64(bad, (i << 3) | r);
-                prev_end = o[k] + s[k];
-                if (l[k] && my_first == kNone) my_first = o[k];
-                a = combine(a, element(o[k], s[k], l[k], p[k], f[k]));
-            }
-        }
-        // offsets ascend, so the chunk's first live entry has the least
-        // offset among its live ones
-        if (first == kNone) first = block_reduce<kScanThreads>(my_first, shr, OpMin());
-        Agg tot;
-        const Agg ex = block_excl<kScanThreads>(a, tot, sh);
-        Agg run = combine(carry, ex);
-        carry = combine(carry, tot);
-#pragma unroll
-        for (uint32_t k = 0; k < kScanItems; ++k) {
-            if (i0 + k >= n) continue;
-            if (l[k]) {
-                if (run.cnt) {  // the hole below this block lies inside the chunk
-                    const uint64_t gap = o[k] - run.mx;
-                    if (gap) {
-                        gaps += 1;
-                        max_gap = umax64(max_gap, gap);
-                        if (gap >= fit_need) min_fit = umin64(min_fit, run.mx);
-                    }
-                }
-                min_size = umin64(min_size, s[k]);
-                if (!f[k]) {
-                    if (run.r) {  // its segment starts inside the chunk: packed at run.v
-                        if (o[k] != run.v) {
-                            a_blocks += 1;
-                            a_bytes += s[k];
-                        }
-                    } else if (o[k] - run.v != first) {  // a hole since the first live block
-                        a_blocks += 1;
-                        a_bytes += s[k];
-                    } else {  // packed tight from the first live block
-                        b_blocks += 1;
-                        b_bytes += s[k];
-                    }
-                }
-            }
-            run = combine(run, element(o[k], s[k], l[k], p[k], f[k]));
-        }
-    }
-    StatPart q{max_gap, gaps, a_blocks, a_bytes, bad, min_size, min_fit, 0};
-    uint64_t x[4] = {b_blocks, b_bytes, 0, 0};
-    block_reduce_stats<kScanThreads>(q, x, s_red);
-    if (threadIdx.x == 0) {
-        ChunkSum c;
-        c.cnt = carry.cnt;
-        c.lsum = carry.lsum;
-        c.mx = carry.mx;
-        c.pcnt = carry.pcnt;
-        c.bad = q.min_moved_dst;  // (the bad key rode in that min slot)
-        c.first = first;
-        c.reset = carry.r ? 1u : 0u;
-        c.pend = carry.r ? (carry.v < carry.mx ? 1u : 0u)
-                         : (first != kNone && first + carry.v < carry.mx ? 1u : 0u);
-        c.a_blocks = q.moved_blocks;
-        c.a_bytes = q.moved_bytes;
-        c.b_blocks = x[0];
-        c.b_bytes = x[1];
-        c.max_gap = q.max_gap;
-        c.gaps = q.gaps;
-        c.min_fit = q.min_fit;
-        c.min_size = q.min_size;
-        csum_store(cs + g, c);
-        uint32_t last = 1;
-        if (ngroups > 1) {
-            // the summary's stores complete before the arrival is counted
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            const uint64_t done = __hip_atomic_fetch_add(&hdr->arrive, 1ull, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-            last = done + 1 == ngroups;
-        }
-        s_last = last;
-    }
-    __syncthreads();
-    if (!s_last) return;
-
-    // the last workgroup: chunks [threadIdx.x * kPer, + kPer)
-    constexpr uint32_t kPer = kMaxScanParts / kScanThreads;
-    const uint64_t j0 = (uint64_t)threadIdx.x * kPer;
-    ChunkSum c[kPer];
-#pragma unroll
-    for (uint32_t k = 0; k < kPer; ++k) {
-        if (j0 + k < ngroups) {
-            c[k] = csum_load(cs + j0 + k);
-        } else {
-            c[k] = ChunkSum{0, 0, 0, 0, kNone, kNone, 0, 0, 0, 0, 0, 0, 0, 0, kNone, kNone};
-        }
-    }
-    // the highest live end before each chunk
-    uint64_t mx_in[kPer];
-    uint64_t loc = 0;
-#pragma unroll
-    for (uint32_t k = 0; k < kPer; ++k) {
-        mx_in[k] = loc;
-        loc = umax64(loc, c[k].mx);
-    }
-    uint64_t max_end;
-    const uint64_t mx_ex = block_excl_max<kScanThreads>(loc, max_end, shr);
-    // the hole below each chunk's first live block, and its pending function
-    uint32_t fn[kPer], hole[kPer];
-    uint32_t mine = 0u;  // this thread's chunks, composed
-#pragma unroll
-    for (uint32_t k = 0; k < kPer; ++k) {
-        mx_in[k] = umax64(mx_in[k], mx_ex);
-        hole[k] = (c[k].first != kNone && mx_in[k] < c[k].first) ? 1u : 0u;
-        fn[k] = c[k].first == kNone ? 0u
-                : c[k].reset       ? (2u | (uint32_t)c[k].pend)
-                                   : ((hole[k] | (uint32_t)c[k].pend) & 1u);
-        mine = pend_then(mine, fn[k]);
-    }
-    uint32_t pend = block_excl_pend<kScanThreads>(mine, shp) & 1u;  // state before chunk j0
-    StatPart r{0, 0, 0, 0, kNone, kNone, kNone, 0};
-    uint64_t tx[4] = {0, 0, 0, 0};  // live blocks, live bytes, pinned blocks
-#pragma unroll
-    for (uint32_t k = 0; k < kPer; ++k) {
-        const uint64_t pend_first = pend | hole[k];  // pending at the chunk's first live block
-        r.moved_blocks += c[k].a_blocks + (pend_first ? c[k].b_blocks : 0);
-        r.moved_bytes += c[k].a_bytes + (pend_first ? c[k].b_bytes : 0);
-        r.gaps += c[k].gaps + hole[k];
-        r.max_gap = umax64(r.max_gap, c[k].max_gap);
-        r.min_fit = umin64(r.min_fit, c[k].min_fit);
-        if (hole[k]) {
-            const uint64_t gap = c[k].first - mx_in[k];
-            r.max_gap = umax64(r.max_gap, gap);
-            if (gap >= fit_need) r.min_fit = umin64(r.min_fit, mx_in[k]);
-        }
-        r.min_moved_dst = umin64(r.min_moved_dst, c[k].bad);
-        r.min_size = umin64(r.min_size, c[k].min_size);
-        tx[0] += c[k].cnt;
-        tx[1] += c[k].lsum;
-        tx[2] += c[k].pcnt;
-        pend = pend_then(pend, fn[k]) & 1u;
-    }
-    block_reduce_stats<kScanThreads>(r, tx, s_red);
-    if (threadIdx.x == 0) {
-        hdr->live_bytes = tx[1];
-        hdr->max_live_end = max_end;
-        hdr->live_blocks = tx[0];
-        hdr->pinned_blocks = tx[2];
-        hdr->bad_key = r.min_moved_dst;
-        hdr->win_state = kWinNone;
-        const uint64_t tail = arena_bytes - max_end;
-        uint64_t fit = r.min_fit;
-        // holes below live blocks come first in address order; the tail last
-        if (fit == kNone && tail && tail >= fit_need) fit = max_end;
-        hdr->fit_offset = fit;
-        hdr->largest_hole = umax64(r.max_gap, tail);
-        hdr->hole_count = r.gaps + (tail ? 1 : 0);
-        hdr->moved_blocks = r.moved_blocks;
-        hdr->moved_bytes = r.moved_bytes;
-        hdr->small_moved = 0;
-        hdr->min_live_size = r.min_size;
-        hdr->move_begin = kNone;
-        hdr->arrive = 0;  // every pass leaves it cleared
-    }
+    stats_one_part(t, n, arena_bytes, chunk, ngroups, cs, hdr, fit_need);
 }
 
 // ---------------------------------------------------------------------------

@@ -22,18 +22,27 @@
 // keys and records are separate arrays, the keys 32- or 64-bit and the
 // records 8 or 16 bytes (k_remap).  HBM traffic is 16 B per handle; the
 // index and the entries stay in L2 / the last-level cache.
-#include "internal.h"
+#include "stats_one.h"
 
 namespace ac {
 namespace {
 
 constexpr uint32_t kRemapThreads = 256;
+static_assert(kRemapThreads == kScanThreads, "the post-check runs as a scan workgroup");
 
 // The one-call path's commit, done by the remap's launch: the packed live
 // arrays and where the packed table goes.
 struct CommitArgs {
     LiveView lv;
     CommitOut out;
+};
+
+// The post-check in the same launch: the statistics of the packed table,
+// read from the plan's packed arrays (the values the commit writes).
+struct PostArgs {
+    uint64_t arena_bytes, chunk, ngroups;
+    ChunkSum *cs;
+    WsHeader *hdr;  // the statistics header
 };
 
 // Lanes k < m write packed entry k (grid-stride).
@@ -47,6 +56,11 @@ __device__ inline void commit_part(const CommitArgs &c, uint64_t m) {
     }
 }
 
+__device__ inline void post_part(const CommitArgs &c, const PostArgs &post, uint64_t m) {
+    const TableView pt{c.lv.dst, c.lv.size, nullptr, c.lv.pin, m, nullptr, 0};  // all live
+    stats_one_part(pt, m, post.arena_bytes, post.chunk, post.ngroups, post.cs, post.hdr, kNone);
+}
+
 // One lane per handle, grid-stride.  The bucket of h gives the live blocks
 // starting in it, [ridx[b], ridx[b+1]); the block holding h, if any, is the
 // last one starting at or below h, so it is found by a short search inside
@@ -54,8 +68,9 @@ __device__ inline void commit_part(const CommitArgs &c, uint64_t m) {
 // 16-byte read.  A random handle costs about three dependent cache-line requests:
 // the index pair, a probe or two over the bucket's keys, the record.
 // REC32: the records are LiveRec32 (arenas below 2^37 bytes), else LiveRec.
-// COMMIT: the launch also writes the packed table (c).
-template <bool REC32, bool COMMIT>
+// COMMIT: the launch also writes the packed table (c); POST: and its
+// statistics (workgroups below post.ngroups, before their handles).
+template <bool REC32, bool COMMIT, bool POST>
 __global__ __launch_bounds__(kRemapThreads) void k_remap(const void *__restrict__ rec,
                                                          const uint64_t *__restrict__ live_src,
                                                          const uint32_t *__restrict__ key,
@@ -64,12 +79,13 @@ __global__ __launch_bounds__(kRemapThreads) void k_remap(const void *__restrict_
                                                          const uint64_t *h_in, uint64_t *h_out,
                                                          uint64_t H, unsigned long long *n_invalid,
                                                          const WsHeader *gate, uint64_t max_tiles,
-                                                         CommitArgs c) {
+                                                         CommitArgs c, PostArgs post) {
     if (gate) {  // queued before the plan was read back: its count, if it did not fail
         const uint64_t gm = gate->live_blocks;
         if (plan_failed(gate, max_tiles)) return;
         m = gm < m ? gm : m;
     }
+    if constexpr (POST) post_part(c, post, m);
     if constexpr (COMMIT) commit_part(c, m);
     uint64_t bad = 0;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
@@ -126,7 +142,7 @@ __global__ __launch_bounds__(kRemapThreads) void k_remap(const void *__restrict_
 // the last such probe leaves the answer in registers; only a handle below
 // the bucket's first block start reads a record afterwards, that of the
 // block before the bucket.
-template <bool COMMIT>
+template <bool COMMIT, bool POST>
 __global__ __launch_bounds__(kRemapThreads) void k_remap_ent(const RemapEnt *__restrict__ ent,
                                                              const uint32_t *__restrict__ ridx,
                                                              uint32_t w, uint64_t nb, uint64_t m,
@@ -134,12 +150,14 @@ __global__ __launch_bounds__(kRemapThreads) void k_remap_ent(const RemapEnt *__r
                                                              uint64_t H,
                                                              unsigned long long *n_invalid,
                                                              const WsHeader *gate,
-                                                             uint64_t max_tiles, CommitArgs c) {
+                                                             uint64_t max_tiles, CommitArgs c,
+                                                             PostArgs post) {
     if (gate) {  // queued before the plan was read back: its count, if it did not fail
         const uint64_t gm = gate->live_blocks;
         if (plan_failed(gate, max_tiles)) return;
         m = gm < m ? gm : m;
     }
+    if constexpr (POST) post_part(c, post, m);
     if constexpr (COMMIT) commit_part(c, m);
     uint64_t bad = 0;
     const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
@@ -187,11 +205,11 @@ __global__ void k_zero_u64(uint64_t *p) {
     if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0;
 }
 
-template <bool COMMIT>
+template <bool COMMIT, bool POST>
 void remap_launch(const uint8_t *ws, const WsLayout &L, uint64_t arena_bytes, uint64_t n,
                   uint64_t live_blocks, const uint64_t *h_in, uint64_t *h_out, uint64_t n_handles,
-                  unsigned long long *bad, const CommitArgs &c, const WsHeader *gate,
-                  uint64_t max_tiles, uint64_t grid, hipStream_t s) {
+                  unsigned long long *bad, const CommitArgs &c, const PostArgs &post,
+                  const WsHeader *gate, uint64_t max_tiles, uint64_t grid, hipStream_t s) {
     const void *rec = ws + L.live_rec;
     const uint64_t *live_src = reinterpret_cast<const uint64_t *>(ws + L.live_src);
     const uint32_t *key = reinterpret_cast<const uint32_t *>(ws + L.live_key);
@@ -200,17 +218,17 @@ void remap_launch(const uint8_t *ws, const WsLayout &L, uint64_t arena_bytes, ui
     const uint32_t w = remap_shift(arena_bytes, n);
     const uint64_t nb = remap_buckets(arena_bytes, n);
     if (remap_ent(arena_bytes, n))
-        hipLaunchKernelGGL(k_remap_ent<COMMIT>, dim3((uint32_t)grid), dim3(kRemapThreads), 0, s,
-                           static_cast<const RemapEnt *>(rec), ridx, w, nb, live_blocks, h_in,
-                           h_out, n_handles, bad, gate, max_tiles, c);
+        hipLaunchKernelGGL((k_remap_ent<COMMIT, POST>), dim3((uint32_t)grid), dim3(kRemapThreads),
+                           0, s, static_cast<const RemapEnt *>(rec), ridx, w, nb, live_blocks,
+                           h_in, h_out, n_handles, bad, gate, max_tiles, c, post);
     else if (remap_rec32(arena_bytes))
-        hipLaunchKernelGGL((k_remap<true, COMMIT>), dim3((uint32_t)grid), dim3(kRemapThreads), 0,
-                           s, rec, live_src, k32, ridx, w, nb, live_blocks, h_in, h_out,
-                           n_handles, bad, gate, max_tiles, c);
+        hipLaunchKernelGGL((k_remap<true, COMMIT, POST>), dim3((uint32_t)grid),
+                           dim3(kRemapThreads), 0, s, rec, live_src, k32, ridx, w, nb,
+                           live_blocks, h_in, h_out, n_handles, bad, gate, max_tiles, c, post);
     else
-        hipLaunchKernelGGL((k_remap<false, COMMIT>), dim3((uint32_t)grid), dim3(kRemapThreads), 0,
-                           s, rec, live_src, k32, ridx, w, nb, live_blocks, h_in, h_out,
-                           n_handles, bad, gate, max_tiles, c);
+        hipLaunchKernelGGL((k_remap<false, COMMIT, POST>), dim3((uint32_t)grid),
+                           dim3(kRemapThreads), 0, s, rec, live_src, k32, ridx, w, nb,
+                           live_blocks, h_in, h_out, n_handles, bad, gate, max_tiles, c, post);
 }
 
 }  // namespace
@@ -218,24 +236,40 @@ void remap_launch(const uint8_t *ws, const WsLayout &L, uint64_t arena_bytes, ui
 hipError_t launch_remap(const uint8_t *ws, const WsLayout &L, uint64_t arena_bytes, uint64_t n,
                         uint64_t live_blocks, const uint64_t *h_in, uint64_t *h_out,
                         uint64_t n_handles, uint64_t *n_invalid, const CommitOut *commit,
-                        const WsHeader *gate, uint64_t max_tiles, int num_cus, hipStream_t s) {
+                        bool post, const WsHeader *gate, uint64_t max_tiles, int num_cus,
+                        hipStream_t s) {
     if (n_invalid && !gate) {
         hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(64), 0, s, n_invalid);
         AC_TRY(hipGetLastError());
     }
     const uint64_t work = (commit && live_blocks > n_handles) ? live_blocks : n_handles;
-    if (work == 0) return hipSuccess;
+    PostArgs pa{arena_bytes, 0, 0, nullptr, nullptr};
+    if (post) {  // the packed table has at most live_blocks entries
+        const WsLayout F = ws_fixed(live_blocks);
+        pa.chunk = F.scan_chunk;
+        pa.ngroups = F.n_scan_blocks ? F.n_scan_blocks : 1;
+        pa.cs = reinterpret_cast<ChunkSum *>(const_cast<uint8_t *>(ws) + L.csum);
+        pa.hdr = reinterpret_cast<WsHeader *>(const_cast<uint8_t *>(ws) + L.post);
+    }
+    if (work == 0 && !post) return hipSuccess;
     uint64_t grid = (work + kRemapThreads - 1) / kRemapThreads;
     const uint64_t cap = (uint64_t)num_cus * 2;  // measured best of 1, 2, 3, 4, 8, 16 per CU
     if (grid > cap) grid = cap;
+    if (grid < pa.ngroups) grid = pa.ngroups;
     unsigned long long *bad = reinterpret_cast<unsigned long long *>(n_invalid);
     CommitArgs c{live_view(ws, L), commit ? *commit : CommitOut{nullptr, nullptr, nullptr, nullptr}};
-    if (commit)
-        remap_launch<true>(ws, L, arena_bytes, n, live_blocks, h_in, h_out, n_handles, bad, c, gate,
-                           max_tiles, grid, s);
+    if (commit && post)
+        remap_launch<true, true>(ws, L, arena_bytes, n, live_blocks, h_in, h_out, n_handles, bad, c,
+                                 pa, gate, max_tiles, grid, s);
+    else if (commit)
+        remap_launch<true, false>(ws, L, arena_bytes, n, live_blocks, h_in, h_out, n_handles, bad,
+                                  c, pa, gate, max_tiles, grid, s);
+    else if (post)
+        remap_launch<false, true>(ws, L, arena_bytes, n, live_blocks, h_in, h_out, n_handles, bad,
+                                  c, pa, gate, max_tiles, grid, s);
     else
-        remap_launch<false>(ws, L, arena_bytes, n, live_blocks, h_in, h_out, n_handles, bad, c,
-                            gate, max_tiles, grid, s);
+        remap_launch<false, false>(ws, L, arena_bytes, n, live_blocks, h_in, h_out, n_handles, bad,
+                                   c, pa, gate, max_tiles, grid, s);
     return hipGetLastError();
 }
 
