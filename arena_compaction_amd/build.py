@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libarena_compaction.so")
-SOURCES = ["api.cpp", "monitor.cpp", "plan.hip", "move.hip", "remap.hip", "static.hip"]
+SOURCES = ["api.cpp", "monitor.cpp", "readback.cpp", "plan.hip", "move.hip", "remap.hip",
+           "publish.hip", "static.hip"]
 ARCH = "gfx950"  # MI355X (CDNA4) only
 
 # No packed-FP32 instructions anywhere in the device code.  hipcc hands the

@@ -85,11 +85,7 @@ void fill_stats(defrag_stats_t *o, const WsHeader &h, uint64_t arena_bytes) {
 }
 
 int read_header(WsHeader *out, const uint8_t *ws, const WsLayout &L, hipStream_t s) {
-    if (hipMemcpyAsync(out, ws + L.header, sizeof(WsHeader), hipMemcpyDeviceToHost, s) !=
-        hipSuccess)
-        return DEFRAG_EHIP;
-    if (hipStreamSynchronize(s) != hipSuccess) return DEFRAG_EHIP;
-    return DEFRAG_OK;
+    return read_back(out, ws + L.header, sizeof(WsHeader), s);
 }
 
 TableView view_of(const defrag_table *t) {
@@ -358,11 +354,9 @@ int compact_finish(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     const uint8_t *ws = static_cast<const uint8_t *>(a->ws_dev);
     static_assert(sizeof(WsHeader) == 256, "two adjacent headers");
     WsHeader both[2];
-    if (L.post != L.header + sizeof(WsHeader) ||
-        hipMemcpyAsync(both, ws + L.header, (post_done ? 2 : 1) * sizeof(WsHeader),
-                       hipMemcpyDeviceToHost, stream) != hipSuccess ||
-        hipStreamSynchronize(stream) != hipSuccess)
-        return DEFRAG_EHIP;
+    if (L.post != L.header + sizeof(WsHeader)) return DEFRAG_EHIP;
+    const int rc = read_back(both, ws + L.header, (post_done ? 2 : 1) * sizeof(WsHeader), stream);
+    if (rc) return rc;
     if (post_done) {
         fill_stats(after_host, both[1], a->arena_bytes);
         if (both[1].bad_key != kNone) return DEFRAG_EINVAL;
@@ -683,11 +677,9 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     // the plan's header (and the mover's status in it) and the post-check's
     static_assert(sizeof(WsHeader) == 256, "two adjacent headers");
     WsHeader both[2];
-    if (c.L.post != c.L.header + sizeof(WsHeader) ||
-        hipMemcpyAsync(both, ws + c.L.header, sizeof(both), hipMemcpyDeviceToHost, stream) !=
-            hipSuccess ||
-        hipStreamSynchronize(stream) != hipSuccess)
-        return DEFRAG_EHIP;
+    if (c.L.post != c.L.header + sizeof(WsHeader)) return DEFRAG_EHIP;
+    rc = read_back(both, ws + c.L.header, sizeof(both), stream);
+    if (rc) return rc;
     rc = plan_fill(a->table, a->arena_bytes, a->request_bytes, a->ws_dev, c, both[0], plan);
     if (rc) return rc;
     plan->state = 2;

@@ -413,6 +413,26 @@ hipError_t launch_targeted(const TableView &t, uint64_t arena_bytes, uint64_t re
 hipError_t launch_stats_one(const TableView &t, uint64_t arena_bytes, uint8_t *ws,
                             const WsLayout &L, uint64_t fit_need, bool after_plan,
                             hipStream_t s);
+// A read-back's device half: words 8-byte words from src (device) into
+// dst_host (pinned, device-mapped host memory), then seq into *seq_host.
+hipError_t launch_publish(const uint64_t *src, uint64_t *dst_host, uint32_t words,
+                          uint64_t *seq_host, uint64_t seq, hipStream_t s);
+
+// Copy `bytes` (a positive multiple of 8, at most 1 KiB) of device memory
+// into host memory, queued on s behind everything queued before, and wait
+// for it: DEFRAG_OK, DEFRAG_EHIP (a HIP call or a queued kernel failed) or
+// DEFRAG_EINVAL (a size outside those bounds).
+int read_back(void *out_host, const void *src_dev, uint32_t bytes, hipStream_t s);
+
+// While one lives, the calling thread's read-backs allocate nothing: they
+// copy into the caller's pageable memory.
+struct NoAllocScope {
+    NoAllocScope();
+    ~NoAllocScope();
+    NoAllocScope(const NoAllocScope &) = delete;
+    NoAllocScope &operator=(const NoAllocScope &) = delete;
+};
+
 hipError_t launch_commit(const uint8_t *ws, const WsLayout &L, uint64_t live_blocks,
                          uint64_t *off_out, uint64_t *size_out, uint8_t *live_out,
                          uint8_t *pinned_out, hipStream_t s);

@@ -75,6 +75,7 @@ extern "C" int defrag_compact_static(const defrag_compact_args *a, hipStream_t s
     defrag_compact_args b = *a;
     b.ws_dev = ws;
     b.ws_bytes = kScratchBytes;
+    const ac::NoAllocScope no_alloc;  // its read-backs copy into pageable memory
     const int rc = ac::compact_serial(&b, stream, plan_host, after_host);
     return rc == DEFRAG_EWORKSPACE ? DEFRAG_ETOOBIG : rc;
 }
