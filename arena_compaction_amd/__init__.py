@@ -112,8 +112,7 @@ class defrag_compact_args(ctypes.Structure):
                 ("h_in_dev", ctypes.c_void_p), ("h_out_dev", ctypes.c_void_p),
                 ("n_handles", ctypes.c_uint64), ("n_invalid_dev", ctypes.c_void_p),
                 ("offset_out_dev", ctypes.c_void_p), ("size_out_dev", ctypes.c_void_p),
-                ("live_out_dev", ctypes.c_void_p), ("pinned_out_dev", ctypes.c_void_p),
-                ("side_stream", ctypes.c_void_p)]
+                ("live_out_dev", ctypes.c_void_p), ("pinned_out_dev", ctypes.c_void_p)]
 
 
 # defrag_tile_t: one mover tile of a plan (defrag_plan_tiles)
@@ -371,8 +370,7 @@ def defrag_commit(plan: defrag_plan_t, ws: torch.Tensor, offset_out=None, size_o
 
 
 def _compact_args(offset, size, live, arena_bytes, arena, ws, request_bytes, new_offset, handles,
-                  h_out, n_invalid, offset_out, size_out, live_out, pinned_out, tuning, pinned,
-                  side_stream):
+                  h_out, n_invalid, offset_out, size_out, live_out, pinned_out, tuning, pinned):
     """The defrag_compact_args of a call, its argument checks, and the
     buffers it points at (kept alive with it)."""
     _need(arena, torch.uint8, 0, "arena")
@@ -397,8 +395,7 @@ def _compact_args(offset, size, live, arena_bytes, arena, ws, request_bytes, new
         _ptr(offset_out) if offset_out is not None and offset_out.numel() else None,
         _ptr(size_out) if size_out is not None and size_out.numel() else None,
         _ptr(live_out) if live_out is not None and live_out.numel() else None,
-        _ptr(pinned_out) if pinned_out is not None and pinned_out.numel() else None,
-        ctypes.c_void_p(side_stream.cuda_stream) if side_stream is not None else None)
+        _ptr(pinned_out) if pinned_out is not None and pinned_out.numel() else None)
     return a, (t, h_out)
 
 
@@ -407,20 +404,18 @@ def defrag_compact(offset, size, live, arena_bytes: int, arena: torch.Tensor, ws
                    handles: Optional[torch.Tensor] = None, h_out: Optional[torch.Tensor] = None,
                    n_invalid: Optional[torch.Tensor] = None, offset_out=None, size_out=None,
                    live_out=None, pinned_out=None, tuning: Optional[defrag_tuning] = None,
-                   stream=None, pinned=None, after: Optional[bool] = None, side_stream=None):
+                   stream=None, pinned=None, after: Optional[bool] = None):
     """Plan, move, remap, commit and the post-check in one C-ABI call.
     after (default: whenever offset_out and size_out are given) asks for the
     post-move statistics.  Returns (plan, post-move stats or None).
     offset_out, size_out, live_out and pinned_out need one element per live
     block, which is known only once the plan has run: neither this function
-    nor the library can check their length.  side_stream: a torch stream
-    of the caller's for the work that overlaps the move (default: the
-    library's own)."""
+    nor the library can check their length."""
     if after is None:
         after = offset_out is not None and size_out is not None
     a, keep = _compact_args(offset, size, live, arena_bytes, arena, ws, request_bytes, new_offset,
                             handles, h_out, n_invalid, offset_out, size_out, live_out, pinned_out,
-                            tuning, pinned, side_stream)
+                            tuning, pinned)
     plan = defrag_plan_t()
     post = defrag_stats_t() if after else None
     rc = lib.defrag_compact(ctypes.byref(a), _stream(stream), ctypes.byref(plan),
@@ -446,7 +441,7 @@ def defrag_compact_static(offset, size, live, arena_bytes: int, arena: torch.Ten
         after = offset_out is not None and size_out is not None
     a, keep = _compact_args(offset, size, live, arena_bytes, arena, None, request_bytes,
                             new_offset, handles, h_out, n_invalid, offset_out, size_out, live_out,
-                            pinned_out, tuning, pinned, None)
+                            pinned_out, tuning, pinned)
     plan = defrag_plan_t()
     post = defrag_stats_t() if after else None
     rc = lib.defrag_compact_static(ctypes.byref(a), _stream(stream), ctypes.byref(plan),

@@ -89,7 +89,7 @@ int read_header(WsHeader *out, const uint8_t *ws, const WsLayout &L, hipStream_t
 }
 
 TableView view_of(const defrag_table *t) {
-    return TableView{t->offset_dev, t->size_dev, t->live_dev, t->pinned_dev, t->n, nullptr, 0};
+    return TableView{t->offset_dev, t->size_dev, t->live_dev, t->pinned_dev, t->n};
 }
 
 WsLayout plan_layout(const defrag_plan_t *p) { return ws_with_tiles(p->n, p->max_tiles); }
@@ -331,21 +331,6 @@ int plan_common(const defrag_table *table, uint64_t arena_bytes, uint64_t reques
     return plan_fill(table, arena_bytes, request, ws_dev, c, h, plan);
 }
 
-// One stream per device, created on first use, on which the one-call path
-// reads a plan back while its move runs.
-hipStream_t side_stream_of(int dev) {
-    static std::mutex mu;
-    static hipStream_t streams[64] = {};
-    if (dev < 0 || dev >= 64) return nullptr;
-    std::lock_guard<std::mutex> lk(mu);
-    if (!streams[dev]) {
-        hipStream_t s = nullptr;
-        if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return nullptr;
-        streams[dev] = s;
-    }
-    return streams[dev];
-}
-
 // The end of a compaction: one read of the plan's header (the mover's
 // status) and, after a post-check, of the statistics header beside it.
 int compact_finish(const defrag_compact_args *a, hipStream_t stream, defrag_plan_t *plan,
@@ -547,8 +532,7 @@ int defrag_remap(const defrag_plan_t *plan, const void *ws_dev, size_t ws_bytes,
     const WsLayout L = plan_layout(plan);
     const uint8_t *ws = static_cast<const uint8_t *>(ws_dev);
     if (launch_remap(ws, L, plan->arena_bytes, plan->n, plan->live_blocks, h_in_dev, h_out_dev,
-                     n_handles, n_invalid_dev, nullptr, false, nullptr, 0, cus,
-                     stream) != hipSuccess)
+                     n_handles, n_invalid_dev, cus, stream) != hipSuccess)
         return DEFRAG_EHIP;
     return DEFRAG_OK;
 }
@@ -588,15 +572,14 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     const bool post_ok = !after_host || (a->offset_out_dev && a->size_out_dev);
     const bool wg_ok = !a->tuning || a->tuning->wg_per_cu != 0;
     if (!(arena_ok && post_ok && wg_ok)) return compact_serial(a, stream, plan, after_host);
-    // the plan clears the invalid-handle count: the remap's launch then
-    // only adds to it
+    // the plan clears the invalid-handle count: the side job then only adds
+    // to it
     PlanCtx c;
     int rc = plan_queue(a->table, a->arena_bytes, a->request_bytes, a->tuning, a->ws_dev,
                         a->ws_bytes, stream, a->new_offset_dev, plan, &c, a->n_invalid_dev);
     if (rc) return rc;
     const int cus = num_cus_of(c.dev);
-    hipStream_t side = a->side_stream ? a->side_stream : side_stream_of(c.dev);
-    if (cus <= 0 || !side) return DEFRAG_EHIP;
+    if (cus <= 0) return DEFRAG_EHIP;
     uint8_t *ws = static_cast<uint8_t *>(a->ws_dev);
     const WsHeader *gate = reinterpret_cast<const WsHeader *>(ws + c.L.header);
     const uint64_t n = a->table->n;  // the bound of every live count below
@@ -629,50 +612,33 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     MoveArgs mb = m;
     mb.tile_bytes = c.tiles.b;
     mb.max_blocks = c.tiles.b / 32 + 2;
+    const uint64_t max_pinned = a->table->pinned_dev ? n : 0;
     const bool one_mover =
-        c.tiles.a == c.tiles.b || (a->arena_bytes <= kAutoMinMoved &&
-                                   tiles_bound(a->arena_bytes, n, c.tiles.a) <= c.L.max_tiles);
-    const bool want_remap = a->n_handles || a->n_invalid_dev;
+        c.tiles.a == c.tiles.b ||
+        (a->arena_bytes <= kAutoMinMoved &&
+         tiles_bound(a->arena_bytes, max_pinned, c.tiles.a) <= c.L.max_tiles);
+    // Remap, commit and the post-check read the plan, never the arena: the
+    // first workgroups of each mover's launch run them beside the move, in
+    // the launch whose tile size the plan chose (the post-check takes the
+    // packed table from the plan's packed arrays, the values the commit
+    // writes).
     const bool want_commit =
         a->offset_out_dev || a->size_out_dev || a->live_out_dev || a->pinned_out_dev;
-    const bool side_work = want_remap || want_commit || after_host;
-    hipEvent_t planned = nullptr, joined = nullptr;
-    if (side_work && (hipEventCreateWithFlags(&planned, hipEventDisableTiming) != hipSuccess ||
-                      hipEventCreateWithFlags(&joined, hipEventDisableTiming) != hipSuccess)) {
-        if (planned) (void)hipEventDestroy(planned);
-        return DEFRAG_EHIP;
-    }
-    bool ok = (!side_work || hipEventRecord(planned, stream) == hipSuccess) &&
-              launch_move_device_sized(m, c.tu.nontemporal, stream) == hipSuccess &&
-              (one_mover || launch_move_device_sized(mb, c.tu.nontemporal, stream) == hipSuccess);
-    bool side_queued = false;
-    if (ok && side_work) {
-        ok = hipStreamWaitEvent(side, planned, 0) == hipSuccess;
-        side_queued = ok;
-        // remap, commit and the post-check in one launch (the post-check
-        // takes the packed table from the plan's packed arrays, the values
-        // the commit writes)
-        const CommitOut out{a->offset_out_dev, a->size_out_dev, a->live_out_dev,
-                            a->pinned_out_dev};
-        if (ok && (want_commit || a->n_handles || after_host))
-            ok = launch_remap(ws, c.L, a->arena_bytes, n, n, a->h_in_dev, a->h_out_dev,
-                              a->n_handles, a->n_invalid_dev, want_commit ? &out : nullptr,
-                              after_host != nullptr, gate, c.L.max_tiles, cus,
-                              side) == hipSuccess;
-        if (ok)
-            ok = hipEventRecord(joined, side) == hipSuccess &&
-                 hipStreamWaitEvent(stream, joined, 0) == hipSuccess;
-    }
-    if (side_work) {
-        (void)hipEventDestroy(planned);
-        (void)hipEventDestroy(joined);
-    }
+    const bool side_work = a->n_handles || a->n_invalid_dev || want_commit || after_host;
+    const CommitOut out{a->offset_out_dev, a->size_out_dev, a->live_out_dev, a->pinned_out_dev};
+    SideArgs sj = side_args(ws, c.L, a->arena_bytes, n, n, a->h_in_dev, a->h_out_dev,
+                            a->n_handles, a->n_invalid_dev, want_commit ? &out : nullptr,
+                            after_host != nullptr, gate, c.L.max_tiles);
+    sj.any_tile = one_mover ? 1u : 0u;  // the one launch runs it
+    const SideArgs *side = side_work ? &sj : nullptr;
+    const bool ok =
+        launch_move_device_sized(m, c.tu.nontemporal, side, stream) == hipSuccess &&
+        (one_mover || launch_move_device_sized(mb, c.tu.nontemporal, side, stream) == hipSuccess);
     if (!ok) {
         // no kernel of this call still writes the caller's buffers once it returns
-        if (side_queued) (void)hipStreamSynchronize(side);
         (void)hipStreamSynchronize(stream);
         if (after_host) arg_error(after_host);
-        return rc ? rc : DEFRAG_EHIP;
+        return DEFRAG_EHIP;
     }
     // the plan's header (and the mover's status in it) and the post-check's
     static_assert(sizeof(WsHeader) == 256, "two adjacent headers");

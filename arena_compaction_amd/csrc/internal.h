@@ -334,12 +334,7 @@ struct TableView {
     const uint64_t *size;
     const uint8_t *live;    // may be null: all live
     const uint8_t *pinned;  // may be null: none pinned
-    uint64_t n;             // entries (with a gate: the most there can be)
-    // A gate, for a table another queued pass writes (the packed table of a
-    // plan): the plan's header.  The table then has that plan's live-block
-    // count of entries, and a pass over it writes nothing if the plan failed.
-    const struct WsHeader *gate;
-    uint64_t gate_max_tiles;
+    uint64_t n;             // entries
 };
 
 // Whether the plan whose header this is failed: an invalid table, no window
@@ -349,17 +344,6 @@ struct TableView {
 __device__ inline bool plan_failed(const WsHeader *h, uint64_t max_tiles) {
     const uint64_t bad = h->bad_key, win = h->win_state, nt = h->n_tiles;
     return (bad != kNone) | (win == kWinNoFit) | (nt > max_tiles);
-}
-// Entries of a table, and whether a pass over it may run (gate above).
-__device__ inline bool table_entries(const TableView &t, uint64_t *n) {
-    if (!t.gate) {
-        *n = t.n;
-        return true;
-    }
-    const uint64_t m = t.gate->live_blocks;
-    if (plan_failed(t.gate, t.gate_max_tiles)) return false;
-    *n = m < t.n ? m : t.n;
-    return true;
 }
 
 // Packed live-block arrays (m + 1 entries each).
@@ -472,8 +456,13 @@ struct MoveArgs {
 hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, uint32_t nontemporal,
                        int num_cus, hipStream_t s);
 // The device-sized mover: a grid for the largest workgroup count the rule
-// can pick, and LDS for the most blocks a tile can meet.
-hipError_t launch_move_device_sized(const MoveArgs &a, uint32_t nontemporal, hipStream_t s);
+// can pick, and LDS for the most blocks a tile can meet.  side (or null):
+// a side job (remap.hip, with a gate) that the launch's first workgroups
+// run beside the move if the plan chose this mover's tile size or
+// side->any_tile is set (of two movers, the chosen one's launch runs it).
+struct SideArgs;
+hipError_t launch_move_device_sized(const MoveArgs &a, uint32_t nontemporal,
+                                    const SideArgs *side, hipStream_t s);
 
 // ---- api.cpp ----
 // The whole compaction in the plain order on one stream, creating nothing:
@@ -489,20 +478,58 @@ struct CommitOut {
     uint8_t *live;
     uint8_t *pinned;
 };
-// Remap n_handles handles through the plan in the workspace (n: the planned
-// table's entries).  commit: also write the packed table, in the same
-// launch.  post: also the post-check, the statistics of that packed table
-// (read from the plan's packed arrays) into the statistics header, in the
-// same launch (its count of finished workgroups cleared by the plan).  gate
-// (the one-call path, queued before the plan is read back): the plan's
-// header gives the live-block count (live_blocks is then the most there can
-// be), nothing is written if the plan failed, and n_invalid is taken as
-// cleared already (the plan's last pass clears it).
+// The part of a compaction that reads the plan and never the arena, as one
+// job for a range of workgroups (side.h): the handle remap (h_in -> h_out,
+// H handles, those in no live block counted into n_invalid), the packed
+// table (commit != 0: the plan's packed live arrays into out) and the
+// post-check (post != 0: the statistics of that packed table into
+// post_hdr, its chunk summaries in csum).  m: the live-block count, or with
+// a gate (the plan's header, for a job queued before the plan is read
+// back) the most there can be: the job then takes the header's count, and
+// does nothing if the plan failed.
+enum : uint32_t { kSideEnt = 0, kSideRec32 = 1, kSideRec64 = 2 };
+struct SideArgs {
+    const void *rec;           // RemapEnt, LiveRec32 or LiveRec records
+    const uint64_t *live_src;  // old offsets (searched when key is null)
+    const uint32_t *key;       // 32-bit keys, or null
+    const uint32_t *ridx;      // bucket index
+    uint64_t nb;               // buckets
+    uint32_t w;                // log2 of the bucket width
+    uint32_t kind;             // kSideEnt, kSideRec32 or kSideRec64
+    const uint64_t *h_in;
+    uint64_t *h_out;
+    uint64_t H;
+    unsigned long long *n_invalid;
+    uint64_t m;
+    const WsHeader *gate;
+    uint64_t max_tiles;
+    LiveView lv;
+    CommitOut out;
+    uint32_t commit;
+    uint32_t post;
+    uint64_t arena_bytes, chunk, ngroups;  // post-check: chunks of the packed table (size_side)
+    void *csum;
+    WsHeader *post_hdr;
+    uint64_t work;      // the most entries or handles one lane pass covers
+    uint32_t groups;    // workgroups running the job (set by the launch)
+    uint32_t any_tile;  // in a mover's launch: run whatever tile size the plan chose
+};
+// A side job on the plan in the workspace (n: the planned table's entries;
+// live_blocks: its live count, or the most there can be with a gate).
+SideArgs side_args(const uint8_t *ws, const WsLayout &L, uint64_t arena_bytes, uint64_t n,
+                   uint64_t live_blocks, const uint64_t *h_in, uint64_t *h_out,
+                   uint64_t n_handles, uint64_t *n_invalid, const CommitOut *commit, bool post,
+                   const WsHeader *gate, uint64_t max_tiles);
+// Size a side job for workgroups of `lanes` lanes: enough workgroups for
+// its work, at most 512 lanes per compute unit and kMaxScanParts (groups),
+// and the post-check's chunks of the packed table, one per workgroup at
+// most (chunk, ngroups).
+void size_side(SideArgs &sj, uint32_t lanes, int num_cus);
+// defrag_remap: the handle remap alone, in a launch of its own (n_invalid
+// cleared first).
 hipError_t launch_remap(const uint8_t *ws, const WsLayout &L, uint64_t arena_bytes, uint64_t n,
                         uint64_t live_blocks, const uint64_t *h_in, uint64_t *h_out,
-                        uint64_t n_handles, uint64_t *n_invalid, const CommitOut *commit,
-                        bool post, const WsHeader *gate, uint64_t max_tiles, int num_cus,
-                        hipStream_t s);
+                        uint64_t n_handles, uint64_t *n_invalid, int num_cus, hipStream_t s);
 
 }  // namespace ac
 

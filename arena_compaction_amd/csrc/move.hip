@@ -71,7 +71,7 @@
 // the number of such reads); all of it on the rare path.  A testing knob
 // holds chosen tiles' flags back for a bounded time, so that later tiles do
 // find them unset and the waits run at full size.
-#include "internal.h"
+#include "side.h"
 
 namespace ac {
 namespace {
@@ -137,8 +137,9 @@ __global__ __launch_bounds__(256) void k_verify_tiles(MoveArgs a) {
     if (over) atomicOr(&a.hdr->status, kStatusCapacity);
 }
 
+// The tiles as moved by mover workgroup wg of a launch.
 template <int THREADS, int VPT, int NT>
-__global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
+__device__ __forceinline__ void move_tiles(const MoveArgs &a, uint32_t wg) {
     extern __shared__ uint64_t lds_dyn[];
     uint64_t *s_shift = lds_dyn;                                           // [max_blocks]
     uint32_t *s_rel = reinterpret_cast<uint32_t *>(lds_dyn + a.max_blocks);  // [max_blocks]
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
             // did not choose; workgroups past the chosen count leave
             const uint32_t per_cu = a.wg_per_cu ? a.wg_per_cu : kDefaultWgPerCu;
             go = go & (bad == kNone) & (win != kWinNoFit) & (nt <= a.max_tiles) &
-                 (tb == a.tile_bytes) & (blockIdx.x < (uint64_t)per_cu * a.num_cus);
+                 (tb == a.tile_bytes) & (wg < (uint64_t)per_cu * a.num_cus);
         }
         if (go) tk = atomicAdd(&a.hdr->ticket, 1u);
         s_ticket = tk;
@@ -310,6 +311,34 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
 }
 
 template <int THREADS, int VPT, int NT>
+__global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
+    move_tiles<THREADS, VPT, NT>(a, blockIdx.x);
+}
+
+// The one-call path's mover: its first side.groups workgroups run the side
+// job (remap, commit, post-check) instead, if the plan chose this mover's
+// tile size (or side.any_tile), and the movers are the workgroups after
+// them.  Registers are capped so that a side workgroup and a mover fit on
+// one CU together (a SIMD's 512 VGPRs over two workgroups' waves: 128 a lane
+// at 512 lanes, 64 at 1024), unless the mover's tile data alone would not
+// fit in that (those run on CUs of their own).
+template <int THREADS, int VPT>
+constexpr int side_waves_per_eu() {
+    return VPT * 4 + 32 < 65536 / THREADS ? THREADS / 128 : 1;
+}
+template <int THREADS, int VPT, int NT>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(side_waves_per_eu<THREADS, VPT>()))) void k_move_side(
+    MoveArgs a, SideArgs side) {
+    if (blockIdx.x < side.groups) {
+        const uint64_t tb = side.gate->tile_bytes;
+        if (__builtin_amdgcn_readfirstlane((uint32_t)(side.any_tile | (tb == a.tile_bytes))))
+            side_part<THREADS>(side, blockIdx.x);
+        return;
+    }
+    move_tiles<THREADS, VPT, NT>(a, blockIdx.x - side.groups);
+}
+
+template <int THREADS, int VPT, int NT>
 hipError_t launch_t(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
     const size_t lds = (size_t)a.max_blocks * 12u + 16u;
     uint64_t per_cu = wg_per_cu;
@@ -332,22 +361,32 @@ hipError_t launch_t(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStrea
 // not read back first: the workgroups read its tile count from the device),
 // LDS for the most blocks a tile can meet.
 template <int THREADS, int VPT, int NT>
-hipError_t launch_device_sized_t(const MoveArgs &a, hipStream_t s) {
+hipError_t launch_device_sized_t(const MoveArgs &a, const SideArgs *side, hipStream_t s) {
     const size_t lds = (size_t)a.max_blocks * 12u + 16u;
     const uint64_t per_cu = a.wg_per_cu ? a.wg_per_cu : kDefaultWgPerCu;
     uint64_t grid = per_cu * (uint64_t)a.num_cus;
     if (grid > kMaxMoveGrid) grid = kMaxMoveGrid;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((k_move<THREADS, VPT, NT>), dim3((uint32_t)grid), dim3(THREADS), lds, s, a);
+    if (side) {
+        if (!side->gate) return hipErrorInvalidValue;  // the job reads the plan's header
+        SideArgs sj = *side;
+        size_side(sj, THREADS, (int)a.num_cus);
+        hipLaunchKernelGGL((k_move_side<THREADS, VPT, NT>), dim3((uint32_t)(grid + sj.groups)),
+                           dim3(THREADS), lds, s, a, sj);
+    } else {
+        hipLaunchKernelGGL((k_move<THREADS, VPT, NT>), dim3((uint32_t)grid), dim3(THREADS), lds,
+                           s, a);
+    }
     return hipGetLastError();
 }
 
 template <int THREADS, int VPT, int NT, bool DEVICE_SIZED>
-hipError_t launch_one(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
+hipError_t launch_one(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, const SideArgs *side,
+                      hipStream_t s) {
     if constexpr (VPT * THREADS * 16 > kMaxTile) {
         return hipErrorInvalidValue;  // larger than any tile
     } else if constexpr (DEVICE_SIZED) {
-        return launch_device_sized_t<THREADS, VPT, NT>(a, s);
+        return launch_device_sized_t<THREADS, VPT, NT>(a, side, s);
     } else {
         return launch_t<THREADS, VPT, NT>(a, wg_per_cu, num_cus, s);
     }
@@ -355,24 +394,27 @@ hipError_t launch_one(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStr
 
 // Vectors per lane: the tile over the workgroup's row of 16-byte vectors.
 template <int THREADS, int NT, bool DEVICE_SIZED>
-hipError_t launch_threads(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
+hipError_t launch_threads(const MoveArgs &a, uint32_t wg_per_cu, int num_cus,
+                          const SideArgs *side, hipStream_t s) {
     constexpr uint32_t row = THREADS * 16;
     switch (a.tile_bytes <= row ? 1u : a.tile_bytes / row) {
-        case 1: return launch_one<THREADS, 1, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
-        case 2: return launch_one<THREADS, 2, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
-        case 4: return launch_one<THREADS, 4, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
-        case 8: return launch_one<THREADS, 8, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
-        case 16: return launch_one<THREADS, 16, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
-        case 32: return launch_one<THREADS, 32, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
+        case 1: return launch_one<THREADS, 1, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, side, s);
+        case 2: return launch_one<THREADS, 2, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, side, s);
+        case 4: return launch_one<THREADS, 4, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, side, s);
+        case 8: return launch_one<THREADS, 8, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, side, s);
+        case 16: return launch_one<THREADS, 16, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, side, s);
+        case 32: return launch_one<THREADS, 32, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, side, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int NT, bool DEVICE_SIZED>
-hipError_t launch_nt(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, hipStream_t s) {
-    return a.small_blocks
-               ? launch_threads<kMoveThreadsSmallBlocks, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s)
-               : launch_threads<kMoveThreads, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus, s);
+hipError_t launch_nt(const MoveArgs &a, uint32_t wg_per_cu, int num_cus, const SideArgs *side,
+                     hipStream_t s) {
+    return a.small_blocks ? launch_threads<kMoveThreadsSmallBlocks, NT, DEVICE_SIZED>(
+                                a, wg_per_cu, num_cus, side, s)
+                          : launch_threads<kMoveThreads, NT, DEVICE_SIZED>(a, wg_per_cu, num_cus,
+                                                                          side, s);
 }
 
 }  // namespace
@@ -385,20 +427,21 @@ hipError_t launch_move(const MoveArgs &a, uint32_t wg_per_cu, uint32_t nontempor
     hipLaunchKernelGGL(k_verify_tiles, dim3((uint32_t)vgrid), dim3(256), 0, s, a);
     AC_TRY(hipGetLastError());
     switch (nontemporal) {
-        case 0: return launch_nt<0, false>(a, wg_per_cu, num_cus, s);
-        case 1: return launch_nt<3, false>(a, wg_per_cu, num_cus, s);
-        case 2: return launch_nt<1, false>(a, wg_per_cu, num_cus, s);
-        case 3: return launch_nt<2, false>(a, wg_per_cu, num_cus, s);
+        case 0: return launch_nt<0, false>(a, wg_per_cu, num_cus, nullptr, s);
+        case 1: return launch_nt<3, false>(a, wg_per_cu, num_cus, nullptr, s);
+        case 2: return launch_nt<1, false>(a, wg_per_cu, num_cus, nullptr, s);
+        case 3: return launch_nt<2, false>(a, wg_per_cu, num_cus, nullptr, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_move_device_sized(const MoveArgs &a, uint32_t nontemporal, hipStream_t s) {
+hipError_t launch_move_device_sized(const MoveArgs &a, uint32_t nontemporal,
+                                    const SideArgs *side, hipStream_t s) {
     switch (nontemporal) {
-        case 0: return launch_nt<0, true>(a, 0, 0, s);
-        case 1: return launch_nt<3, true>(a, 0, 0, s);
-        case 2: return launch_nt<1, true>(a, 0, 0, s);
-        case 3: return launch_nt<2, true>(a, 0, 0, s);
+        case 0: return launch_nt<0, true>(a, 0, 0, side, s);
+        case 1: return launch_nt<3, true>(a, 0, 0, side, s);
+        case 2: return launch_nt<1, true>(a, 0, 0, side, s);
+        case 3: return launch_nt<2, true>(a, 0, 0, side, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -58,10 +58,9 @@ __device__ inline bool plan_dead(const WsHeader *hdr) {
 __global__ __launch_bounds__(kScanThreads) void k_scan_partials(TableView t, uint64_t arena_bytes,
                                                                 const uint64_t *win,
                                                                 uint64_t chunk, ScanPart *part) {
-    __shared__ Agg sh[kScanThreads / 64];
+    __shared__ Agg sh[kExclSlots<kScanThreads>];
     __shared__ uint64_t shr[kScanThreads / 64];
-    uint64_t n;
-    if (!table_entries(t, &n)) return;  // a gated table whose plan failed
+    const uint64_t n = t.n;
     const Window w = window_of(win);
     const uint64_t base = (uint64_t)blockIdx.x * chunk;
     const uint64_t end = umin64(base + chunk, n);
@@ -179,7 +178,7 @@ __device__ inline uint64_t whole_of(uint64_t a, uint64_t s, uint64_t T) {
 __device__ void stats_finish(const StatPart *spart, uint64_t nb, uint64_t arena_bytes,
                              uint64_t max_end, WsHeader *hdr, bool plan, uint64_t fit_need,
                              const uint64_t *xsrc = nullptr, uint64_t *xsum = nullptr) {
-    __shared__ uint64_t sh[12 * (kScanThreads / 64)];
+    __shared__ uint64_t sh[kStatSlots<kScanThreads>];
     StatPart a{0, 0, 0, 0, kNone, kNone, kNone, 0};
     uint64_t x[4] = {0, 0, 0, 0};
     for (uint64_t j = threadIdx.x; j < nb; j += kScanThreads) {
@@ -316,14 +315,13 @@ struct DownArgs {
 // fixed per instantiation so that each holds only its own code.
 template <int OUT>
 __global__ __launch_bounds__(kScanThreads) void k_scan_down(DownArgs d) {
-    __shared__ Agg sh[kScanThreads / 64];
+    __shared__ Agg sh[kExclSlots<kScanThreads>];
     __shared__ uint64_t shr[kScanThreads / 64];
-    __shared__ uint64_t s_red[12 * (kScanThreads / 64)];
+    __shared__ uint64_t s_red[kStatSlots<kScanThreads>];
     __shared__ Agg s_before;
     const TableView &t = d.t;
     const uint64_t g = blockIdx.x;
-    uint64_t n;
-    if (!table_entries(t, &n)) return;  // a gated table whose plan failed
+    const uint64_t n = t.n;
     const uint64_t base = g * d.chunk;
     const uint64_t end = umin64(base + d.chunk, n);
     uint64_t o[kScanItems], s[kScanItems];
@@ -421,9 +419,8 @@ __global__ __launch_bounds__(kScanThreads) void k_stats_one(TableView t, uint64_
                                                             uint64_t chunk, uint64_t ngroups,
                                                             ChunkSum *cs, WsHeader *hdr,
                                                             uint64_t fit_need) {
-    uint64_t n;
-    if (!table_entries(t, &n)) return;  // a gated table whose plan failed
-    stats_one_part(t, n, arena_bytes, chunk, ngroups, cs, hdr, fit_need);
+    stats_one_part<kScanThreads>(t, t.n, arena_bytes, chunk, ngroups, cs, hdr, fit_need,
+                                 blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -521,7 +518,7 @@ struct BaseArgs {
 // workgroups after them build the remap's bucket index.
 __global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
     __shared__ uint64_t sh[kScanThreads / 64];
-    __shared__ uint64_t s_red[12 * (kScanThreads / 64)];
+    __shared__ uint64_t s_red[kStatSlots<kScanThreads>];
     __shared__ uint64_t s_before;
     WsHeader *hdr = a.hdr;
     if (blockIdx.x == 0 && threadIdx.x == 0) {

@@ -68,11 +68,20 @@ __device__ inline Agg shfl_up_agg(const Agg &a, int d) {
     return b;
 }
 
+// LDS slots the two cross-wave helpers below need for NT lanes.
+template <int NT>
+constexpr int kExclSlots = 2 * (NT / 64) + 1;  // Agg slots of block_excl
+template <int NT>
+constexpr int kStatSlots = 12 * (NT / 64 + 1);  // u64 slots of block_reduce_stats
+
 // Exclusive workgroup scan in thread order; also returns the total.
-// sh needs NT/64 entries.
+// sh: kExclSlots<NT> entries.  Each wave scans itself with shuffles; the
+// first wave then scans the waves' totals (one per lane) and hands every
+// wave its prefix through LDS, so no lane holds more than a few aggregates.
 template <int NT>
 __device__ inline Agg block_excl(const Agg &x, Agg &total, Agg *sh) {
     constexpr int NW = NT / 64;
+    static_assert(NW >= 1 && NW <= 64 && (NW & (NW - 1)) == 0, "whole waves, a power of two");
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     Agg inc = x;
@@ -81,19 +90,26 @@ __device__ inline Agg block_excl(const Agg &x, Agg &total, Agg *sh) {
         const Agg y = shfl_up_agg(inc, d);
         if (lane >= d) inc = combine(y, inc);
     }
-    if (lane == 63) sh[w] = inc;
-    __syncthreads();
-    Agg pre = agg_zero(), tot = agg_zero();
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-        const Agg z = sh[k];
-        if (k < w) pre = combine(pre, z);
-        tot = combine(tot, z);
-    }
     Agg ex = shfl_up_agg(inc, 1);
     if (lane == 0) ex = agg_zero();
+    if (lane == 63) sh[w] = inc;
     __syncthreads();
-    total = tot;
+    if (w == 0) {
+        Agg t = lane < NW ? sh[lane] : agg_zero();
+#pragma unroll
+        for (int d = 1; d < NW; d <<= 1) {
+            const Agg y = shfl_up_agg(t, d);
+            if (lane >= d) t = combine(y, t);
+        }
+        Agg te = shfl_up_agg(t, 1);
+        if (lane == 0) te = agg_zero();
+        if (lane < NW) sh[NW + lane] = te;
+        if (lane == NW - 1) sh[2 * NW] = t;
+    }
+    __syncthreads();
+    const Agg pre = sh[NW + w];
+    total = sh[2 * NW];
+    __syncthreads();
     return combine(pre, ex);
 }
 
@@ -143,50 +159,55 @@ struct OpAdd { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { re
 struct OpMax { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return umax64(a, b); } };
 struct OpMin { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return umin64(a, b); } };
 
-// Workgroup reduction of the statistics and up to four extra sums in one
-// LDS round trip (one barrier pair for all fields, not one per field): each
-// wave reduces with shuffles, then every thread combines the waves' values.
-// sh: 12 * NT/64 slots.
+// Workgroup reduction of the statistics and up to four extra sums: each
+// wave reduces with shuffles and writes one row to LDS; the first wave's
+// lanes take one row each and reduce them with shuffles; every lane reads
+// the result.  sh: kStatSlots<NT> slots.
+__device__ inline void stat_shfl_reduce(StatPart &q, uint64_t (&x)[4], int d) {
+    q.max_gap = umax64(q.max_gap, (uint64_t)__shfl_xor(q.max_gap, d, 64));
+    q.gaps += (uint64_t)__shfl_xor(q.gaps, d, 64);
+    q.moved_blocks += (uint64_t)__shfl_xor(q.moved_blocks, d, 64);
+    q.moved_bytes += (uint64_t)__shfl_xor(q.moved_bytes, d, 64);
+    q.min_moved_dst = umin64(q.min_moved_dst, (uint64_t)__shfl_xor(q.min_moved_dst, d, 64));
+    q.min_size = umin64(q.min_size, (uint64_t)__shfl_xor(q.min_size, d, 64));
+    q.min_fit = umin64(q.min_fit, (uint64_t)__shfl_xor(q.min_fit, d, 64));
+    q.small_moved += (uint64_t)__shfl_xor(q.small_moved, d, 64);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] += (uint64_t)__shfl_xor(x[k], d, 64);
+}
+__device__ inline void stat_store(uint64_t *o, const StatPart &q, const uint64_t (&x)[4]) {
+    o[0] = q.max_gap; o[1] = q.gaps; o[2] = q.moved_blocks; o[3] = q.moved_bytes;
+    o[4] = q.min_moved_dst; o[5] = q.min_size; o[6] = q.min_fit; o[7] = q.small_moved;
+    o[8] = x[0]; o[9] = x[1]; o[10] = x[2]; o[11] = x[3];
+}
+__device__ inline void stat_load(const uint64_t *o, StatPart &q, uint64_t (&x)[4]) {
+    q = StatPart{o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
+    x[0] = o[8]; x[1] = o[9]; x[2] = o[10]; x[3] = o[11];
+}
 template <int NT>
 __device__ inline void block_reduce_stats(StatPart &q, uint64_t (&x)[4], uint64_t *sh) {
     constexpr int NW = NT / 64;
+    static_assert(NW >= 1 && NW <= 64 && (NW & (NW - 1)) == 0, "whole waves, a power of two");
     constexpr int F = 12;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        q.max_gap = umax64(q.max_gap, (uint64_t)__shfl_xor(q.max_gap, d, 64));
-        q.gaps += (uint64_t)__shfl_xor(q.gaps, d, 64);
-        q.moved_blocks += (uint64_t)__shfl_xor(q.moved_blocks, d, 64);
-        q.moved_bytes += (uint64_t)__shfl_xor(q.moved_bytes, d, 64);
-        q.min_moved_dst = umin64(q.min_moved_dst, (uint64_t)__shfl_xor(q.min_moved_dst, d, 64));
-        q.min_size = umin64(q.min_size, (uint64_t)__shfl_xor(q.min_size, d, 64));
-        q.min_fit = umin64(q.min_fit, (uint64_t)__shfl_xor(q.min_fit, d, 64));
-        q.small_moved += (uint64_t)__shfl_xor(q.small_moved, d, 64);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) x[k] += (uint64_t)__shfl_xor(x[k], d, 64);
-    }
+    for (int d = 32; d >= 1; d >>= 1) stat_shfl_reduce(q, x, d);
+    const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) {
-        uint64_t *o = sh + F * w;
-        o[0] = q.max_gap; o[1] = q.gaps; o[2] = q.moved_blocks; o[3] = q.moved_bytes;
-        o[4] = q.min_moved_dst; o[5] = q.min_size; o[6] = q.min_fit; o[7] = q.small_moved;
-        o[8] = x[0]; o[9] = x[1]; o[10] = x[2]; o[11] = x[3];
+    if (lane == 0) stat_store(sh + F * w, q, x);
+    __syncthreads();
+    if (w == 0) {
+        if (lane < NW) {
+            stat_load(sh + F * lane, q, x);
+        } else {  // the identity
+            q = StatPart{0, 0, 0, 0, kNone, kNone, kNone, 0};
+            x[0] = x[1] = x[2] = x[3] = 0;
+        }
+#pragma unroll
+        for (int d = NW / 2; d >= 1; d >>= 1) stat_shfl_reduce(q, x, d);
+        if (lane == 0) stat_store(sh + F * NW, q, x);
     }
     __syncthreads();
-    q = StatPart{0, 0, 0, 0, kNone, kNone, kNone, 0};
-    x[0] = x[1] = x[2] = x[3] = 0;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-        const uint64_t *o = sh + F * k;
-        q.max_gap = umax64(q.max_gap, o[0]);
-        q.gaps += o[1];
-        q.moved_blocks += o[2];
-        q.moved_bytes += o[3];
-        q.min_moved_dst = umin64(q.min_moved_dst, o[4]);
-        q.min_size = umin64(q.min_size, o[5]);
-        q.min_fit = umin64(q.min_fit, o[6]);
-        q.small_moved += o[7];
-        x[0] += o[8]; x[1] += o[9]; x[2] += o[10]; x[3] += o[11];
-    }
+    stat_load(sh + F * NW, q, x);
     __syncthreads();
 }
 

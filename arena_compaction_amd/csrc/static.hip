@@ -55,8 +55,8 @@ void refuse(defrag_plan_t *plan) {
 extern "C" int defrag_compact_static(const defrag_compact_args *a, hipStream_t stream,
                                      defrag_plan_t *plan_host, defrag_stats_t *after_host) {
     if (!plan_host) return DEFRAG_EINVAL;
-    // the scratch stands in for the workspace and the call uses one stream
-    if (!a || a->ws_dev || a->ws_bytes || a->side_stream ||
+    // the scratch stands in for the workspace
+    if (!a || a->ws_dev || a->ws_bytes ||
         (a->n_handles && (!a->h_in_dev || !a->h_out_dev))) {
         refuse(plan_host);
         return DEFRAG_EINVAL;

@@ -57,13 +57,8 @@ __device__ inline void csum_store(ChunkSum *p, const ChunkSum &c) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) __hip_atomic_store(w + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline ChunkSum csum_load(const ChunkSum *p) {
-    uint64_t *w = const_cast<uint64_t *>(reinterpret_cast<const uint64_t *>(p));
-    ChunkSum c;
-    uint64_t *v = reinterpret_cast<uint64_t *>(&c);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = __hip_atomic_load(w + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return c;
+__device__ inline uint64_t csum_field(const uint64_t *f) {
+    return __hip_atomic_load(const_cast<uint64_t *>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Exclusive workgroup scan of a u64 under max; also returns the total.
@@ -125,19 +120,21 @@ __device__ inline uint32_t block_excl_pend(uint32_t x, uint32_t *sh) {
     return pend_then(pre, ex);
 }
 
-// The pass as run by workgroup blockIdx.x of a launch of kScanThreads lanes
-// and at least `ngroups` workgroups (those past it do nothing here): table
-// t of n entries (n as gated), chunks of `chunk` entries, the summaries in
-// cs, the header hdr.  Workgroup-uniform; barriers inside.
+// The pass as run by workgroup g (of NT lanes, ITEMS entries a lane per
+// step) of at least `ngroups` workgroups taking part (those at or past it
+// do nothing here): table t of n entries, chunks of `chunk` entries, the
+// summaries in cs, the header hdr.  Workgroup-uniform; barriers inside.
+template <int NT, int ITEMS = kScanItems>
 __device__ void stats_one_part(const TableView &t, uint64_t n, uint64_t arena_bytes,
                                uint64_t chunk, uint64_t ngroups, ChunkSum *cs, WsHeader *hdr,
-                               uint64_t fit_need) {
-    __shared__ Agg sh[kScanThreads / 64];
-    __shared__ uint64_t shr[kScanThreads / 64];
-    __shared__ uint64_t s_red[12 * (kScanThreads / 64)];
-    __shared__ uint32_t shp[kScanThreads / 64];
+                               uint64_t fit_need, uint64_t g) {
+    static_assert(NT % 64 == 0 && kMaxScanParts % NT == 0, "whole waves; whole chunks a lane");
+    constexpr uint32_t kStep = NT * ITEMS;  // entries per workgroup step
+    __shared__ Agg sh[kExclSlots<NT>];
+    __shared__ uint64_t shr[NT / 64];
+    __shared__ uint64_t s_red[kStatSlots<NT>];
+    __shared__ uint32_t shp[NT / 64];
     __shared__ uint32_t s_last;
-    const uint64_t g = blockIdx.x;
     if (g >= ngroups) return;
     const uint64_t base = g * chunk;
     const uint64_t end = umin64(base + chunk, n);
@@ -146,15 +143,15 @@ __device__ void stats_one_part(const TableView &t, uint64_t n, uint64_t arena_by
     uint64_t first = kNone;  // (workgroup-uniform)
     uint64_t bad = kNone, max_gap = 0, gaps = 0, min_fit = kNone, min_size = kNone;
     uint64_t a_blocks = 0, a_bytes = 0, b_blocks = 0, b_bytes = 0;
-    for (uint64_t s0 = base; s0 < end; s0 += kScanTile) {
-        const uint64_t i0 = s0 + (uint64_t)threadIdx.x * kScanItems;
-        uint64_t o[kScanItems], s[kScanItems];
-        uint32_t l[kScanItems], p[kScanItems], f[kScanItems];
+    for (uint64_t s0 = base; s0 < end; s0 += kStep) {
+        const uint64_t i0 = s0 + (uint64_t)threadIdx.x * ITEMS;
+        uint64_t o[ITEMS], s[ITEMS];
+        uint32_t l[ITEMS], p[ITEMS], f[ITEMS];
         uint64_t prev_end = 0, my_first = kNone;
         if (i0 > 0 && i0 < n) prev_end = t.off[i0 - 1] + t.size[i0 - 1];
         Agg a = agg_zero();
 #pragma unroll
-        for (uint32_t k = 0; k < kScanItems; ++k) {
+        for (uint32_t k = 0; k < (uint32_t)ITEMS; ++k) {
             const uint64_t i = i0 + k;
             o[k] = s[k] = 0;
             l[k] = p[k] = f[k] = 0;
@@ -174,13 +171,13 @@ __device__ void stats_one_part(const TableView &t, uint64_t n, uint64_t arena_by
         }
         // offsets ascend, so the chunk's first live entry has the least
         // offset among its live ones
-        if (first == kNone) first = block_reduce<kScanThreads>(my_first, shr, OpMin());
+        if (first == kNone) first = block_reduce<NT>(my_first, shr, OpMin());
         Agg tot;
-        const Agg ex = block_excl<kScanThreads>(a, tot, sh);
+        const Agg ex = block_excl<NT>(a, tot, sh);
         Agg run = combine(carry, ex);
         carry = combine(carry, tot);
 #pragma unroll
-        for (uint32_t k = 0; k < kScanItems; ++k) {
+        for (uint32_t k = 0; k < (uint32_t)ITEMS; ++k) {
             if (i0 + k >= n) continue;
             if (l[k]) {
                 if (run.cnt) {  // the hole below this block lies inside the chunk
@@ -212,7 +209,7 @@ __device__ void stats_one_part(const TableView &t, uint64_t n, uint64_t arena_by
     }
     StatPart q{max_gap, gaps, a_blocks, a_bytes, bad, min_size, min_fit, 0};
     uint64_t x[4] = {b_blocks, b_bytes, 0, 0};
-    block_reduce_stats<kScanThreads>(q, x, s_red);
+    block_reduce_stats<NT>(q, x, s_red);
     if (threadIdx.x == 0) {
         ChunkSum c;
         c.cnt = carry.cnt;
@@ -246,64 +243,67 @@ __device__ void stats_one_part(const TableView &t, uint64_t n, uint64_t arena_by
     __syncthreads();
     if (!s_last) return;
 
-    // the last workgroup: chunks [threadIdx.x * kPer, + kPer)
-    constexpr uint32_t kPer = kMaxScanParts / kScanThreads;
+    // the last workgroup: chunks [threadIdx.x * kPer, + kPer).  A summary is
+    // read in two parts -- the four fields the two scans need, then the rest
+    // one chunk at a time while summing -- so no lane holds whole summaries.
+    constexpr uint32_t kPer = kMaxScanParts / NT;
     const uint64_t j0 = (uint64_t)threadIdx.x * kPer;
-    ChunkSum c[kPer];
+    uint64_t mx_in[kPer], first_of[kPer];
+    uint32_t rp[kPer];  // bit 1: a pinned entry inside; bit 0: its pend field
+    uint64_t loc = 0;  // the highest live end before each chunk
 #pragma unroll
     for (uint32_t k = 0; k < kPer; ++k) {
+        uint64_t mx = 0, fi = kNone, re = 0, pe = 0;
         if (j0 + k < ngroups) {
-            c[k] = csum_load(cs + j0 + k);
-        } else {
-            c[k] = ChunkSum{0, 0, 0, 0, kNone, kNone, 0, 0, 0, 0, 0, 0, 0, 0, kNone, kNone};
+            const ChunkSum *p = cs + j0 + k;
+            mx = csum_field(&p->mx);
+            fi = csum_field(&p->first);
+            re = csum_field(&p->reset);
+            pe = csum_field(&p->pend);
         }
-    }
-    // the highest live end before each chunk
-    uint64_t mx_in[kPer];
-    uint64_t loc = 0;
-#pragma unroll
-    for (uint32_t k = 0; k < kPer; ++k) {
         mx_in[k] = loc;
-        loc = umax64(loc, c[k].mx);
+        loc = umax64(loc, mx);
+        first_of[k] = fi;
+        rp[k] = (re ? 2u : 0u) | (uint32_t)(pe & 1u);
     }
     uint64_t max_end;
-    const uint64_t mx_ex = block_excl_max<kScanThreads>(loc, max_end, shr);
+    const uint64_t mx_ex = block_excl_max<NT>(loc, max_end, shr);
     // the hole below each chunk's first live block, and its pending function
     uint32_t fn[kPer], hole[kPer];
     uint32_t mine = 0u;  // this thread's chunks, composed
 #pragma unroll
     for (uint32_t k = 0; k < kPer; ++k) {
         mx_in[k] = umax64(mx_in[k], mx_ex);
-        hole[k] = (c[k].first != kNone && mx_in[k] < c[k].first) ? 1u : 0u;
-        fn[k] = c[k].first == kNone ? 0u
-                : c[k].reset       ? (2u | (uint32_t)c[k].pend)
-                                   : ((hole[k] | (uint32_t)c[k].pend) & 1u);
+        hole[k] = (first_of[k] != kNone && mx_in[k] < first_of[k]) ? 1u : 0u;
+        fn[k] = first_of[k] == kNone ? 0u : (rp[k] & 2u) ? rp[k] : ((hole[k] | rp[k]) & 1u);
         mine = pend_then(mine, fn[k]);
     }
-    uint32_t pend = block_excl_pend<kScanThreads>(mine, shp) & 1u;  // state before chunk j0
+    uint32_t pend = block_excl_pend<NT>(mine, shp) & 1u;  // state before chunk j0
     StatPart r{0, 0, 0, 0, kNone, kNone, kNone, 0};
     uint64_t tx[4] = {0, 0, 0, 0};  // live blocks, live bytes, pinned blocks
 #pragma unroll
     for (uint32_t k = 0; k < kPer; ++k) {
+        if (j0 + k >= ngroups) break;
+        const ChunkSum *p = cs + j0 + k;
         const uint64_t pend_first = pend | hole[k];  // pending at the chunk's first live block
-        r.moved_blocks += c[k].a_blocks + (pend_first ? c[k].b_blocks : 0);
-        r.moved_bytes += c[k].a_bytes + (pend_first ? c[k].b_bytes : 0);
-        r.gaps += c[k].gaps + hole[k];
-        r.max_gap = umax64(r.max_gap, c[k].max_gap);
-        r.min_fit = umin64(r.min_fit, c[k].min_fit);
+        r.moved_blocks += csum_field(&p->a_blocks) + (pend_first ? csum_field(&p->b_blocks) : 0);
+        r.moved_bytes += csum_field(&p->a_bytes) + (pend_first ? csum_field(&p->b_bytes) : 0);
+        r.gaps += csum_field(&p->gaps) + hole[k];
+        r.max_gap = umax64(r.max_gap, csum_field(&p->max_gap));
+        r.min_fit = umin64(r.min_fit, csum_field(&p->min_fit));
         if (hole[k]) {
-            const uint64_t gap = c[k].first - mx_in[k];
+            const uint64_t gap = first_of[k] - mx_in[k];
             r.max_gap = umax64(r.max_gap, gap);
             if (gap >= fit_need) r.min_fit = umin64(r.min_fit, mx_in[k]);
         }
-        r.min_moved_dst = umin64(r.min_moved_dst, c[k].bad);
-        r.min_size = umin64(r.min_size, c[k].min_size);
-        tx[0] += c[k].cnt;
-        tx[1] += c[k].lsum;
-        tx[2] += c[k].pcnt;
+        r.min_moved_dst = umin64(r.min_moved_dst, csum_field(&p->bad));
+        r.min_size = umin64(r.min_size, csum_field(&p->min_size));
+        tx[0] += csum_field(&p->cnt);
+        tx[1] += csum_field(&p->lsum);
+        tx[2] += csum_field(&p->pcnt);
         pend = pend_then(pend, fn[k]) & 1u;
     }
-    block_reduce_stats<kScanThreads>(r, tx, s_red);
+    block_reduce_stats<NT>(r, tx, s_red);
     if (threadIdx.x == 0) {
         hdr->live_bytes = tx[1];
         hdr->max_live_end = max_end;

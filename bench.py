@@ -234,7 +234,7 @@ def latency(args, heap, arena, off, size, live, pinned, ws, tuning, h_in, h_out,
         a, keep = ac._compact_args(off, size, live, S, arena, ws, 0, new_off, kw.get("handles"),
                                    kw.get("h_out"), kw.get("n_invalid"), kw.get("offset_out"),
                                    kw.get("size_out"), kw.get("live_out"), kw.get("pinned_out"),
-                                   tuning, pinned, None)
+                                   tuning, pinned)
         plan, post = ac.defrag_plan_t(), ac.defrag_stats_t()
 
         def call(a=a, plan=plan, post=post, after=after):
@@ -245,7 +245,7 @@ def latency(args, heap, arena, off, size, live, pinned, ws, tuning, h_in, h_out,
         timeit(name, call)
     timeit("binding_marshalling", lambda: ac._compact_args(
         off, size, live, S, arena, ws, 0, new_off, h_in, h_out, n_bad, c_off, c_size, c_live,
-        c_pin, tuning, pinned, None))
+        c_pin, tuning, pinned))
     timeit("plan_via_binding", lambda: ac.defrag_plan(off, size, live, S, ws, new_off,
                                                       tuning=tuning, stream=stream, pinned=pinned))
     timeit("stats_via_binding", lambda: ac.defrag_stats(off, size, live, S, ws, stream=stream,

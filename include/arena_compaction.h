@@ -38,11 +38,13 @@
  * table without planning.
  *
  * Ownership: the caller owns every buffer (arena, table, outputs, handles and
- * the workspace).  The library allocates no device memory and never writes
- * the table.  Its only process-wide state is a counter for plan epochs, a
- * per-device cache of the compute-unit count, and -- unless the caller
- * passes its own (defrag_compact_args.side_stream) -- one HIP stream per
- * device that defrag_compact creates on first use.
+ * the workspace).  The library allocates no device memory, creates no stream
+ * or event, and never writes the table.  Its only process-wide state is a
+ * counter for plan epochs, a per-device cache of the compute-unit count, and
+ * a pool of small pinned host buffers (about 1 KiB each, one per call in
+ * flight at a time, allocated on first need and kept until the process
+ * ends) into which the calls that return figures read their results back;
+ * defrag_compact_static uses none of them.
  *
  * Concurrency: between defrag_plan and the end of defrag_move nothing else
  * may read or write the arena, the table or the workspace (the 910C page runs
@@ -364,15 +366,15 @@ int defrag_commit(const defrag_plan_t *plan_host, const void *ws_dev,
  * defrag_plan (or defrag_plan_targeted when request_bytes > 0),
  * defrag_move, defrag_remap (when n_handles or n_invalid_dev is given),
  * defrag_commit (when any packed-table output is given) and, when
- * after_host is given, defrag_stats of the packed table.  The move is
- * queued right behind the plan's passes, before the plan is read back: it
- * takes its tile count and workgroup count from the plan in the workspace,
- * and moves nothing if the plan failed; the plan is read back on a second
- * stream (one per device, created on first use and kept) while the move
- * runs.  Remap, commit and the post-check, which never read the arena,
- * then run on that stream beside the move (the post-check with a header of
- * its own in the workspace); the stream waits for them, and one read at the
- * end brings the post-check and the mover's status.  With a NULL or misaligned arena, a tuning of wg_per_cu 0, or
+ * after_host is given, defrag_stats of the packed table.  Everything runs
+ * on `stream`.  The move is queued right behind the plan's passes, before
+ * the plan is read back: it takes its tile count and workgroup count from
+ * the plan in the workspace, and moves nothing if the plan failed.  Remap,
+ * commit and the post-check, which read the plan and never the arena, run
+ * in the first workgroups of the move's own launch, beside the movers (the
+ * post-check with a header of its own in the workspace); one read at the
+ * end brings the plan, the mover's status and the post-check.  With a NULL
+ * or misaligned arena, a tuning of wg_per_cu 0, or
  * after_host without offset_out_dev and size_out_dev, the steps run in the
  * plain order instead (plan, read back, argument checks, move).  Returns
  * the first failing step's code (nothing moves if the plan fails;
@@ -398,11 +400,6 @@ typedef struct defrag_compact_args {
     uint64_t *size_out_dev;        /* any may be NULL                         */
     uint8_t *live_out_dev;
     uint8_t *pinned_out_dev;
-    /* The second stream the move overlaps with (see above): NULL takes the
-     * library's own, one per device, created on first use and kept; pass a
-     * stream of your own (on the same device, not `stream`) and the call
-     * creates none, so the library holds no stream at all. */
-    hipStream_t side_stream;
 } defrag_compact_args;
 
 int defrag_compact(const defrag_compact_args *args, hipStream_t stream,
@@ -412,8 +409,8 @@ int defrag_compact(const defrag_compact_args *args, hipStream_t stream,
  * streams and events: code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation.  The workspace is a device array the
  * library holds itself, DEFRAG_STATIC_SCRATCH_BYTES per GPU, from its load
- * to the end of the process; args->ws_dev, ws_bytes and side_stream must be
- * 0 (else DEFRAG_EINVAL).  The steps run in defrag_compact's plain order on
+ * to the end of the process; args->ws_dev and ws_bytes must be 0 (else
+ * DEFRAG_EINVAL).  The steps run in defrag_compact's plain order on
  * `stream` alone (plan, read back, move, remap, commit, post-check, one
  * read at the end); the call calls no allocating routine and creates
  * nothing.  A table that needs more workspace than the scratch holds --

@@ -101,8 +101,8 @@ def run_gpu(heap: W.Heap, dev="cuda", tuning=None, arena: Optional[torch.Tensor]
                   arena, ws)
 
 
-def run_gpu_compact(heap: W.Heap, arena: torch.Tensor, request: int = 0, tuning=None,
-                    side_stream=None) -> GpuRun:
+def run_gpu_compact(heap: W.Heap, arena: torch.Tensor, request: int = 0,
+                    tuning=None) -> GpuRun:
     """The whole operator through one C-ABI call (defrag_compact): plan
     (targeted when request > 0), move, remap, commit and post-check."""
     import arena_compaction_amd as ac
@@ -119,7 +119,7 @@ def run_gpu_compact(heap: W.Heap, arena: torch.Tensor, request: int = 0, tuning=
     c_pin = torch.full((m,), 9, dtype=torch.uint8, device="cuda")
     plan, post = ac.defrag_compact(off, size, live, heap.arena_bytes, arena, ws, request,
                                    new_off, h, h, n_bad, c_off, c_size, None, c_pin,
-                                   tuning=tuning, pinned=pin, side_stream=side_stream)
+                                   tuning=tuning, pinned=pin)
     torch.cuda.synchronize()
     want_pin = (np.zeros(m, np.uint8) if heap.pinned is None
                 else heap.pinned[np.flatnonzero(heap.live)])

@@ -245,9 +245,9 @@ def test_binding_structs_match_the_header():
 
 
 def test_static_entry_point_refusals_need_no_gpu():
-    """defrag_compact_static refuses, before any HIP call, a workspace or
-    side stream (its scratch and the caller's stream stand in for them) and
-    a table whose plan arrays alone exceed the static scratch."""
+    """defrag_compact_static refuses, before any HIP call, a workspace (its
+    scratch stands in for it) and a table whose plan arrays alone exceed the
+    static scratch."""
     import arena_compaction_amd as ac
     L = ac.lib
     plan = ac.defrag_plan_t()
@@ -261,10 +261,6 @@ def test_static_entry_point_refusals_need_no_gpu():
         ac.DEFRAG_EINVAL
     assert plan.stats.invalid_reason == 6
     args.ws_dev, args.ws_bytes = None, 0
-    args.side_stream = ctypes.c_void_p(0x4000)
-    assert L.defrag_compact_static(ctypes.byref(args), None, ctypes.byref(plan), None) == \
-        ac.DEFRAG_EINVAL
-    args.side_stream = None
     t.n = 50_000_000   # ~3 GB of plan arrays
     assert L.defrag_compact_static(ctypes.byref(args), None, ctypes.byref(plan), None) == \
         ac.DEFRAG_ETOOBIG

@@ -3,7 +3,7 @@ dependency waits forced with the testing knob (and counted), a tile with
 more blocks than the launch holds (DEFRAG_ECAPACITY, not a watchdog), a
 workspace overwritten after its plan (DEFRAG_ECORRUPT: no tile outside the
 arena moves), statistics of a far larger table beside a plan, and the
-one-call path on a side stream the caller owns.  Every
+one-call path when its plan picks the second tile-size candidate.  Every
 condition is forced from the host; every kernel runs to its normal end."""
 import numpy as np
 import pytest
@@ -181,12 +181,36 @@ def test_statistics_beside_a_plan_of_fewer_entries(ac):
                           want_new[np.flatnonzero(small.live)])
 
 
-def test_compact_on_a_side_stream_of_the_callers(ac):
-    for k in ("training-80g", "small-blocks-4g", "mixed-64m"):
-        heap = W.workload(k, small=True)
-        log(f"case compact with a caller side stream {heap.describe()}")
-        host = pristine_host(heap)
-        side = torch.cuda.Stream()
-        r = run_gpu_compact(heap, host.cuda(), side_stream=side)
-        check_tables_and_handles(heap, r)
-        check_arena_full(heap, r, host)
+def _small_shift_heap():
+    """Three 96 MiB blocks above holes of 4 KiB, 64 KiB and 1 MiB and one
+    freed 32 MiB block: 288 MiB move, all by less than 8 MiB, so a plan
+    given no tile size picks the larger candidate (256 KiB)."""
+    KiB = 1 << 10
+    blocks, live, at = [], [], 0
+    for hole, sz in ((4 * KiB, 96 * MiB), (64 * KiB, 96 * MiB), (1 * MiB, 96 * MiB)):
+        blocks.append((at, hole))
+        live.append(0)
+        blocks.append((at + hole, sz))
+        live.append(1)
+        at += hole + sz
+    blocks.append((at, 32 * MiB))
+    live.append(0)
+    S = at + 32 * MiB
+    rng = np.random.default_rng(11)
+    handles = np.concatenate([rng.integers(0, S, 4000, dtype=np.uint64),
+                              np.array([0, 4 * KiB, 4 * KiB + 96 * MiB - 1, S - 1], np.uint64)])
+    return W.table_from_lists(S, blocks, live, handles, name="small shifts 288 MiB")
+
+
+def test_compact_when_the_plan_picks_the_larger_tile(ac):
+    """defrag_compact launches a mover for each tile-size candidate, and the
+    remap, commit and post-check run in the first workgroups of the chosen
+    one's launch: here the second launch (256 KiB tiles), the first moving
+    nothing and running none of them."""
+    heap = _small_shift_heap()
+    log(f"case compact, plan picks 256 KiB tiles: {heap.describe()}")
+    host = pristine_host(heap)
+    r = run_gpu_compact(heap, host.cuda())
+    assert r.plan.tuning.tile_bytes == 262144
+    check_tables_and_handles(heap, r)
+    check_arena_full(heap, r, host)
