@@ -18,6 +18,7 @@
 // memory instead.
 #include <atomic>
 #include <chrono>
+#include <cstddef>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -33,8 +34,9 @@ constexpr auto kPollFor = std::chrono::microseconds(200);
 
 struct HostSlot {
     uint64_t data[kSlotBytes / 8];
-    uint64_t seq;     // written by the device: the last read-back completed
-    uint64_t issued;  // host only: the last sequence number queued
+    uint64_t seq;        // written by the device: the last read-back completed
+    uint64_t issued;     // host only: the last sequence number queued
+    HostSlot *dev_addr;  // this slot as the device addresses it
 };
 
 std::mutex g_mu;
@@ -50,14 +52,20 @@ HostSlot *take_slot() {
             return s;
         }
     }
-    void *p = nullptr;
+    void *p = nullptr, *d = nullptr;
     if (hipHostMalloc(&p, sizeof(HostSlot),
                       hipHostMallocPortable | hipHostMallocMapped | hipHostMallocCoherent) !=
             hipSuccess ||
         !p)
         return nullptr;
+    if (hipHostGetDevicePointer(&d, p, 0) != hipSuccess || !d) {
+        (void)hipHostFree(p);
+        return nullptr;
+    }
     std::memset(p, 0, sizeof(HostSlot));
-    return static_cast<HostSlot *>(p);
+    HostSlot *s = static_cast<HostSlot *>(p);
+    s->dev_addr = static_cast<HostSlot *>(d);
+    return s;
 }
 
 void give_slot(HostSlot *s) {
@@ -83,8 +91,12 @@ int read_back(void *out, const void *src_dev, uint32_t bytes, hipStream_t s) {
     HostSlot *slot = take_slot();
     if (!slot) return copy_pageable(out, src_dev, bytes, s);
     const uint64_t seq = ++slot->issued;
-    if (launch_publish(static_cast<const uint64_t *>(src_dev), slot->data, bytes / 8, &slot->seq,
-                       seq, s) != hipSuccess) {
+    // the slot's fields at the device's address of it (address arithmetic only)
+    char *dev = reinterpret_cast<char *>(slot->dev_addr);
+    uint64_t *dev_data = reinterpret_cast<uint64_t *>(dev + offsetof(HostSlot, data));
+    uint64_t *dev_seq = reinterpret_cast<uint64_t *>(dev + offsetof(HostSlot, seq));
+    if (launch_publish(static_cast<const uint64_t *>(src_dev), dev_data, bytes / 8, dev_seq, seq,
+                       s) != hipSuccess) {
         give_slot(slot);  // nothing was queued
         return DEFRAG_EHIP;
     }
