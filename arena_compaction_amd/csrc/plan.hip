@@ -650,56 +650,127 @@ __device__ inline uint64_t tile_of(const LiveView &lv, const uint32_t *tile_base
 __device__ inline TileRec tile_record(const LiveView &lv, const uint32_t *tile_base, uint64_t m,
                                       uint64_t t, uint64_t t0, uint64_t first, uint64_t bound,
                                       uint64_t T, const uint32_t *ridx, uint32_t w) {
-    // last block of the run inside [t0, bound): blocks after first that start
-    // below bound and moved form a prefix -- gallop, then bisect
-    uint64_t last = first, stride = 1;
-    while (last + stride < m && lv.dst[last + stride] < bound && moved_at(lv, last + stride)) {
-        last += stride;
-        stride <<= 1;
-    }
-    for (; stride > 0; stride >>= 1)
-        if (last + stride < m && lv.dst[last + stride] < bound && moved_at(lv, last + stride))
-            last += stride;
-    const uint64_t t1 = umin64(bound, lv.dst[last] + lv.size[last]);
-    // sources overlapping [t0, t1): first block whose source ends above t0.
-    // The remap index narrows it to the blocks starting in t0's bucket and
-    // the one before them: an earlier block ends before the bucket starts,
-    // and the first block of the next bucket already ends above t0.
+    // Two searches that do not depend on each other run in one loop, the
+    // loads of a step issued together (each step is a memory round trip):
+    //  * the last block of the run inside [t0, bound): the blocks after
+    //    first that start below bound and moved form a prefix -- gallop
+    //    (doubling), then bisect; the end of the last one found so far is
+    //    kept, so t1 needs no further load;
+    //  * the first block whose source ends above t0 (the first whose source
+    //    can overlap [t0, t1)).  The remap index narrows it to the blocks
+    //    starting in t0's bucket and the one before them: an earlier block
+    //    ends before the bucket starts, and the first block of the next
+    //    bucket already ends above t0.
     int64_t lo = 0, hi = (int64_t)m;
     if (ridx) {
         const uint64_t bk = t0 >> w;
-        lo = ridx[bk] ? (int64_t)ridx[bk] - 1 : 0;
-        hi = (int64_t)ridx[bk + 1];
+        const uint32_t r0 = ridx[bk], r1 = ridx[bk + 1];
+        lo = r0 ? (int64_t)r0 - 1 : 0;
+        hi = (int64_t)r1;
     }
-    while (lo < hi) {
+    uint64_t last = first, stride = 1;
+    uint64_t last_end = lv.dst[first] + lv.size[first];
+    bool doubling = true;
+    for (;;) {
+        const bool g_on = stride > 0;
+        const bool s_on = lo < hi;
+        if (!g_on && !s_on) break;
+        const uint64_t gi = last + stride;
         const int64_t mid = lo + ((hi - lo) >> 1);
-        if (lv.src[mid] + lv.size[mid] <= t0) lo = mid + 1;
-        else hi = mid;
-    }
-    uint32_t dep_lo = 1, dep_hi = 0;  // empty
-    if (lo < (int64_t)m && lv.src[lo] < t1 && t > 0) {
-        const uint64_t j = (uint64_t)lo;
-        const uint64_t q_lo = lv.dst[j] + (t0 > lv.src[j] ? t0 - lv.src[j] : 0);
-        // ... and the last block whose source starts below t1 (gallop from j)
-        uint64_t c = j;
-        stride = 1;
-        while (c + stride < m && lv.src[c + stride] < t1) {
-            c += stride;
-            stride <<= 1;
+        bool g_ok = false;
+        uint64_t g_end = 0;
+        if (g_on && gi < m) {
+            const uint64_t d = lv.dst[gi], sz = lv.size[gi], sr = lv.src[gi];
+            g_ok = (d < bound) & (sr != d);  // starts below bound, moved
+            g_end = d + sz;
         }
-        for (; stride > 0; stride >>= 1)
-            if (c + stride < m && lv.src[c + stride] < t1) c += stride;
-        const uint64_t q_hi = lv.dst[c] + umin64(lv.size[c], t1 - lv.src[c]) - 1;
-        const uint64_t u_lo = tile_of(lv, tile_base, j, q_lo, T);
-        uint64_t u_hi = tile_of(lv, tile_base, c, q_hi, T);
-        if (u_hi > t - 1) u_hi = t - 1;
-        if (u_lo <= u_hi) {
-            dep_lo = (uint32_t)u_lo;
-            dep_hi = (uint32_t)u_hi;
+        bool s_right = false;
+        if (s_on) s_right = lv.src[mid] + lv.size[mid] <= t0;
+        if (g_on) {
+            if (g_ok) {
+                last = gi;
+                last_end = g_end;
+            }
+            if (doubling && g_ok) {
+                stride <<= 1;
+            } else {
+                doubling = false;
+                stride >>= 1;
+            }
+        }
+        if (s_on) {
+            if (s_right) lo = mid + 1;
+            else hi = mid;
+        }
+    }
+    const uint64_t t1 = umin64(bound, last_end);
+    uint32_t dep_lo = 1, dep_hi = 0;  // empty
+    if (lo < (int64_t)m && t > 0) {
+        const uint64_t j = (uint64_t)lo;
+        const uint64_t sj = lv.src[j];
+        if (sj < t1) {
+            const uint64_t q_lo = lv.dst[j] + (t0 > sj ? t0 - sj : 0);
+            const uint64_t u_lo = tile_of(lv, tile_base, j, q_lo, T);
+            // ... and the last block whose source starts below t1 (gallop from j)
+            uint64_t c = j;
+            stride = 1;
+            while (c + stride < m && lv.src[c + stride] < t1) {
+                c += stride;
+                stride <<= 1;
+            }
+            for (; stride > 0; stride >>= 1)
+                if (c + stride < m && lv.src[c + stride] < t1) c += stride;
+            const uint64_t q_hi = lv.dst[c] + umin64(lv.size[c], t1 - lv.src[c]) - 1;
+            uint64_t u_hi = tile_of(lv, tile_base, c, q_hi, T);
+            if (u_hi > t - 1) u_hi = t - 1;
+            if (u_lo <= u_hi) {
+                dep_lo = (uint32_t)u_lo;
+                dep_hi = (uint32_t)u_hi;
+            }
         }
     }
     return TileRec{t0, t1, lv.src[first] - lv.dst[first], (uint32_t)first, (uint32_t)last,
                    dep_lo, dep_hi, 0};
+}
+
+// The last index k with a[k] <= x in a[0, m), or -1, for x = x0 (into
+// out[0]) and x = x1 (into out[1]), a ascending: two searches side by
+// side, 128 lanes each, every round testing 128 evenly spaced entries of
+// the bracket at once (one memory round trip a round: three for a million
+// entries, where one lane's bisection takes twenty).  Workgroup-uniform; 256
+// lanes; barriers inside.
+__device__ inline void find_stretch(const uint32_t *a, int64_t m, uint64_t x0, uint64_t x1,
+                                    int64_t *out) {
+    __shared__ uint32_t s_cnt[4];
+    __shared__ int64_t s_br[2][2];
+    const uint32_t half = threadIdx.x >> 7, lane = threadIdx.x & 127, wave = threadIdx.x >> 6;
+    const uint64_t x = half ? x1 : x0;
+    if (lane == 0) {  // the bracket (lo, hi): a[lo] <= x < a[hi], a[-1] and a[m] beyond
+        s_br[half][0] = -1;
+        s_br[half][1] = m;
+    }
+    __syncthreads();
+    for (;;) {
+        const int64_t lo = s_br[half][0], hi = s_br[half][1];
+        const int64_t lo_o = s_br[half ^ 1][0], hi_o = s_br[half ^ 1][1];
+        if (hi - lo <= 1 && hi_o - lo_o <= 1) break;  // both done (uniform)
+        const int64_t span = hi - lo - 1;  // candidates lo + 1 .. hi - 1
+        const int64_t step = span > 0 ? (span + 127) / 128 : 1;
+        const int64_t idx = lo + 1 + (int64_t)lane * step;
+        const bool p = span > 0 && idx < hi && (uint64_t)a[idx] <= x;
+        const uint64_t bal = __ballot(p);
+        if ((threadIdx.x & 63) == 0) s_cnt[wave] = (uint32_t)__popcll(bal);
+        __syncthreads();
+        if (lane == 0 && span > 0) {  // the entries at or below x form a prefix
+            const int64_t c = (int64_t)(s_cnt[2 * half] + s_cnt[2 * half + 1]);
+            const int64_t nlo = c ? lo + 1 + (c - 1) * step : lo;
+            const int64_t nhi = lo + 1 + c * step;
+            s_br[half][0] = nlo;
+            s_br[half][1] = nhi < hi ? nhi : hi;
+        }
+        __syncthreads();
+    }
+    if (lane == 0) out[half] = s_br[half][0];
 }
 
 // Pass 4: one lane per tile, each writing its record (tile_record).
@@ -733,8 +804,8 @@ __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint32_t *tile
             s_k[0] = 0;
             s_k[1] = (int64_t)m - 1;
         }
-    } else if (threadIdx.x < 2) {
-        s_k[threadIdx.x] = last_le(tile_base, 0, (int64_t)m, threadIdx.x ? tq : tb);
+    } else {
+        find_stretch(tile_base, (int64_t)m, tb, tq, s_k);
     }
     __syncthreads();
     const int64_t k_lo = s_k[0], k_hi = s_k[1];
