@@ -37,17 +37,20 @@ inline bool move_small_blocks(uint64_t arena_bytes, uint64_t n) {
 }
 constexpr uint32_t kDefaultTile = 65536;
 // With no tile size given, the plan picks one on the device from the shifts
-// it finds: 64 KiB tiles, or 256 KiB when most moved bytes shift by less
+// it finds: 64 KiB tiles, or 128 KiB when most moved bytes shift by less
 // than kAutoSmallShift and at least kAutoMinMoved bytes move.  A tile whose
 // sources the tile it depends on has not yet read waits about a fixed time,
 // and with shifts that short (within the window of tiles in flight at once,
-// ~16 MiB of 64 KiB tiles on 256 compute units) most do; larger tiles
-// amortise the wait.  Measured (mover only, share of the 8 TB/s peak): eight
-// 1 GiB blocks each above a 4 KiB-1 MiB hole, 62% with 64 KiB tiles, 74%
-// with 128 KiB, 77% with 256 KiB; sixty-four 1 GiB blocks above 4 KiB-64 MiB
-// holes (most bytes shifting far), 85%, 82% and 77%.
+// ~16 MiB of 64 KiB tiles on 256 compute units) most do.  128 KiB tiles are
+// moved two per workgroup in flight, so a tile looks at its dependencies
+// only after the next tile's loads have gone out, and by then they have
+// nearly always published.  Measured (mover only, share of the 8 TB/s
+// peak): eight 1 GiB blocks each above a 4 KiB-1 MiB hole, 62% with 64 KiB
+// tiles, 77% with 256 KiB tiles one at a time, 83% with 128 KiB two at a
+// time; sixty-four 1 GiB blocks above 4 KiB-64 MiB holes (most bytes
+// shifting far), 85% with 64 KiB tiles and 83% with 128 KiB two at a time.
 constexpr uint32_t kAutoTileSmall = 65536;
-constexpr uint32_t kAutoTileLarge = 262144;
+constexpr uint32_t kAutoTileLarge = 131072;
 constexpr uint64_t kAutoSmallShift = 8ull << 20;
 constexpr uint64_t kAutoMinMoved = 64ull << 20;  // below it, more (smaller) tiles keep all CUs busy
 

@@ -137,7 +137,186 @@ __global__ __launch_bounds__(256) void k_verify_tiles(MoveArgs a) {
     if (over) atomicOr(&a.hdr->status, kStatusCapacity);
 }
 
-// The tiles as moved by mover workgroup wg of a launch.
+// A tile as its record gives it to the workgroup: its window, the bytes of
+// the window it writes, the earlier tiles it waits for, and whether its
+// blocks fit the launch's LDS.
+struct TileView {
+    uint64_t tb;
+    uint32_t rel0, rel1, dep_lo, dep_hi;
+    bool ok;
+};
+
+// Mover workgroup wg's first ticket (0xFFFFFFFF when it takes part in
+// nothing) into *s_ticket and the tile count into *s_ntiles; thread 0.
+__device__ __forceinline__ void first_claim(const MoveArgs &a, uint32_t wg, uint32_t *s_ticket,
+                                            uint64_t *s_ntiles) {
+    // a workspace re-planned since this plan: move nothing, write nothing
+    // (the status query sees the epoch mismatch); nor when the records
+    // failed their check
+    uint32_t tk = 0xFFFFFFFFu;
+    const WsHeader *h = a.hdr;
+    // every header field needed here is loaded before any is tested: one
+    // memory round trip in front of the first claim, not one per field
+    const uint64_t ep = __hip_atomic_load(&h->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t st = h->status;
+    uint64_t nt = a.n_tiles, bad = kNone, win = kWinNone, tb = a.tile_bytes;
+    if (a.device_sized) {
+        nt = h->n_tiles;
+        bad = h->bad_key;
+        win = h->win_state;
+        tb = h->tile_bytes;
+    }
+    bool go = (ep == a.epoch) & ((st & (kStatusCorrupt | kStatusCapacity)) == 0u);
+    if (a.device_sized) {
+        // the plan's results, read here instead of on the host: a failed
+        // plan (invalid table, no window, too many tiles) moves nothing, nor
+        // does the mover of a tile size the plan did not choose; workgroups
+        // past the chosen count leave
+        const uint32_t per_cu = a.wg_per_cu ? a.wg_per_cu : kDefaultWgPerCu;
+        go = go & (bad == kNone) & (win != kWinNoFit) & (nt <= a.max_tiles) &
+             (tb == a.tile_bytes) & (wg < (uint64_t)per_cu * a.num_cus);
+    }
+    if (go) tk = atomicAdd(&a.hdr->ticket, 1u);
+    *s_ticket = tk;
+    *s_ntiles = nt;
+}
+
+// Start tile t: read its record, stage the shifts and starts of a tile of
+// several blocks in LDS, and issue every 16-byte source load into v (still
+// in flight on return).
+template <int THREADS, int VPT, int NT>
+__device__ __forceinline__ TileView load_tile(const MoveArgs &a, uint32_t t, v4u (&v)[VPT],
+                                              uint64_t *s_shift, uint32_t *s_rel) {
+    const uint32_t tid = threadIdx.x;
+    // The record is the same for every lane: make each field wave-uniform
+    // (one wait for the record, scalar registers after) -- otherwise the
+    // compiler waits for the record again before every data load below.
+    const TileRec &rp = a.tiles[t];
+    const uint64_t t0 = uniform64(rp.t0);
+    const uint64_t t1 = uniform64(rp.t1);
+    const uint64_t shift0 = uniform64(rp.shift0);
+    const uint32_t first = __builtin_amdgcn_readfirstlane(rp.first_block);
+    const uint32_t last = __builtin_amdgcn_readfirstlane(rp.last_block);
+    TileView d;
+    d.dep_lo = __builtin_amdgcn_readfirstlane(rp.dep_lo);
+    d.dep_hi = __builtin_amdgcn_readfirstlane(rp.dep_hi);
+    d.tb = t0 & ~((uint64_t)a.tile_bytes - 1);  // the tile's window
+    d.rel0 = (uint32_t)(t0 - d.tb);
+    d.rel1 = (uint32_t)(t1 - d.tb);
+    const uint32_t nblk = last - first + 1u;
+    d.ok = nblk <= a.max_blocks;  // LDS room (checked again; the plan sized it)
+
+    if (nblk > 1u && d.ok) {
+        for (uint32_t k = tid; k < nblk; k += THREADS) {
+            const uint64_t dst = a.live_dst[first + k];
+            s_shift[k] = a.live_src[first + k] - dst;
+            s_rel[k] = dst <= d.tb ? 0u : (uint32_t)(dst - d.tb);
+        }
+        __syncthreads();
+    }
+
+    // no branch around a memory access: a lane outside [rel0, rel1) reloads
+    // the tile's first source vector and discards it; so does a lane of a
+    // tile of several blocks whose source would leave the arena (the blocks'
+    // shifts come from the packed arrays, which the check pass does not
+    // read) -- and reports it
+    const uint8_t *first_src = a.arena + d.tb + d.rel0 + shift0;
+    const uint64_t lim = a.arena_bytes - 16u - d.tb;  // largest source offset from tb
+    bool lane_bad = false;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const uint32_t r = ((uint32_t)j * THREADS + tid) * 16u;
+        bool in = d.ok && r >= d.rel0 && r < d.rel1;
+        uint64_t sh = shift0;
+        if (nblk > 1u && d.ok) {
+            uint32_t lo = 0, n = nblk;  // largest k with s_rel[k] <= r
+            while (n > 1u) {
+                const uint32_t half = n >> 1;
+                lo = (s_rel[lo + half] <= r) ? lo + half : lo;
+                n -= half;
+            }
+            sh = s_shift[lo];
+            const bool inside = (sh & 15u) == 0 && sh <= lim && (uint64_t)r <= lim - sh;
+            lane_bad |= in && !inside;
+            in = in && inside;
+        }
+        v[j] = load16<NT>(in ? a.arena + d.tb + r + sh : first_src);
+    }
+    if (__builtin_expect(lane_bad, 0)) atomicOr(&a.hdr->status, kStatusCorrupt);
+    return d;
+}
+
+// Thread 0, once every source load of tile t has returned: publish its
+// "sources read" flag (the testing knob may hold it back first).
+__device__ __forceinline__ void publish_tile(const MoveArgs &a, uint32_t t, bool ok) {
+    if (!ok) atomicOr(&a.hdr->status, kStatusCapacity);
+    if (__builtin_expect(a.stall_every != 0u, 0) && stalls(t, a.stall_every, a.stall_seed)) {
+        for (uint32_t k = 0; k < a.stall_sleeps; ++k) __builtin_amdgcn_s_sleep(127);
+    }
+    __hip_atomic_store(&a.flags[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0: wait until every tile in [dep_lo, dep_hi] has published (one
+// seen set already -- f_lo for dep_lo, f_hi for dep_hi -- is not looked at
+// again; look_first: take that first look here).  Returns 1 when the tile
+// must not store: a wait gave up (status timeout) or its blocks do not fit
+// the LDS.  A tile whose dependencies were not all seen done at the first
+// look counts as late, and as waited if it polled.
+__device__ __forceinline__ uint32_t wait_deps(const MoveArgs &a, uint32_t dep_lo, uint32_t dep_hi,
+                                              uint32_t f_lo, uint32_t f_hi, bool ok,
+                                              bool look_first) {
+    if (look_first && dep_lo <= dep_hi) {
+        f_lo = __hip_atomic_load(&a.flags[dep_lo], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        f_hi = __hip_atomic_load(&a.flags[dep_hi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    uint32_t skip = ok ? 0u : 1u;
+    // the common case -- no dependency, or the one or two seen done behind
+    // the data loads -- skips the polling loop, marked unlikely so the
+    // compiler keeps the tile's path straight (measured: +0.6 points on the
+    // 80 GiB workload, +1.0 on the self-overlapping one)
+    const bool seen = dep_lo > dep_hi || (dep_hi - dep_lo <= 1u && f_lo && f_hi);
+    if (__builtin_expect(!seen && !skip, 0)) {
+        uint64_t polls = 0;
+        for (uint32_t u = dep_lo; u <= dep_hi && !skip; ++u) {
+            if ((u == dep_lo && f_lo) || (u == dep_hi && f_hi)) continue;  // seen done
+            uint64_t p = 0;
+            while (__hip_atomic_load(&a.flags[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                if (++p > a.spin_limit) {
+                    skip = 1u;
+                    atomicOr(&a.hdr->status, kStatusTimeout);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            polls += p;
+        }
+        atomicAdd(reinterpret_cast<unsigned long long *>(&a.hdr->late_tiles), 1ull);
+        if (polls) {
+            atomicAdd(reinterpret_cast<unsigned long long *>(&a.hdr->waited_tiles), 1ull);
+            atomicAdd(reinterpret_cast<unsigned long long *>(&a.hdr->polls),
+                      (unsigned long long)polls);
+        }
+    }
+    return skip;
+}
+
+// Buffer stores over the tile's window: a lane outside [rel0, rel1) gets an
+// offset past the window's end, which the hardware drops -- no branch around
+// any store.
+template <int THREADS, int VPT, int NT>
+__device__ __forceinline__ void store_tile(const MoveArgs &a, const TileView &d,
+                                           const v4u (&v)[VPT]) {
+    const __amdgpu_buffer_rsrc_t win =
+        __builtin_amdgcn_make_buffer_rsrc(a.arena + d.tb, 0, (int)a.tile_bytes, kBufferRsrcWord3);
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const uint32_t r = ((uint32_t)j * THREADS + threadIdx.x) * 16u;
+        const uint32_t off = (r >= d.rel0 && r < d.rel1) ? r : kOutOfWindow;
+        __builtin_amdgcn_raw_buffer_store_b128(v[j], win, (int)off, 0, (NT & 2) ? kBufferNt : 0);
+    }
+}
+
+// The tiles as moved by mover workgroup wg of a launch: one tile at a time.
 template <int THREADS, int VPT, int NT>
 __device__ __forceinline__ void move_tiles(const MoveArgs &a, uint32_t wg) {
     extern __shared__ uint64_t lds_dyn[];
@@ -147,160 +326,29 @@ __device__ __forceinline__ void move_tiles(const MoveArgs &a, uint32_t wg) {
     __shared__ uint32_t s_skip;
     __shared__ uint64_t s_ntiles;
     const uint32_t tid = threadIdx.x;
-
-    if (tid == 0) {
-        // a workspace re-planned since this plan: move nothing, write nothing
-        // (the status query sees the epoch mismatch); nor when the records
-        // failed their check
-        uint32_t tk = 0xFFFFFFFFu;
-        const WsHeader *h = a.hdr;
-        // every header field needed here is loaded before any is tested:
-        // one memory round trip in front of the first claim, not one per field
-        const uint64_t ep = __hip_atomic_load(&h->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t st = h->status;
-        uint64_t nt = a.n_tiles, bad = kNone, win = kWinNone, tb = a.tile_bytes;
-        if (a.device_sized) {
-            nt = h->n_tiles;
-            bad = h->bad_key;
-            win = h->win_state;
-            tb = h->tile_bytes;
-        }
-        bool go = (ep == a.epoch) & ((st & (kStatusCorrupt | kStatusCapacity)) == 0u);
-        if (a.device_sized) {
-            // the plan's results, read here instead of on the host: a
-            // failed plan (invalid table, no window, too many tiles)
-            // moves nothing, nor does the mover of a tile size the plan
-            // did not choose; workgroups past the chosen count leave
-            const uint32_t per_cu = a.wg_per_cu ? a.wg_per_cu : kDefaultWgPerCu;
-            go = go & (bad == kNone) & (win != kWinNoFit) & (nt <= a.max_tiles) &
-                 (tb == a.tile_bytes) & (wg < (uint64_t)per_cu * a.num_cus);
-        }
-        if (go) tk = atomicAdd(&a.hdr->ticket, 1u);
-        s_ticket = tk;
-        s_ntiles = nt;
-    }
+    if (tid == 0) first_claim(a, wg, &s_ticket, &s_ntiles);
     __syncthreads();
     const uint64_t n_tiles = s_ntiles;
     uint32_t t = s_ticket;
 
     while (t < n_tiles) {
-
-        // The record is the same for every lane: make each field wave-uniform
-        // (one wait for the record, scalar registers after) -- otherwise the
-        // compiler waits for the record again before every data load below.
-        const TileRec &rp = a.tiles[t];
-        const uint64_t t0 = uniform64(rp.t0);
-        const uint64_t t1 = uniform64(rp.t1);
-        const uint64_t shift0 = uniform64(rp.shift0);
-        const uint32_t first = __builtin_amdgcn_readfirstlane(rp.first_block);
-        const uint32_t last = __builtin_amdgcn_readfirstlane(rp.last_block);
-        const uint32_t dep_lo = __builtin_amdgcn_readfirstlane(rp.dep_lo);
-        const uint32_t dep_hi = __builtin_amdgcn_readfirstlane(rp.dep_hi);
-        const uint64_t tb = t0 & ~((uint64_t)a.tile_bytes - 1);  // the tile's window
-        const uint32_t rel0 = (uint32_t)(t0 - tb);
-        const uint32_t rel1 = (uint32_t)(t1 - tb);
-        const uint32_t nblk = last - first + 1u;
-        const bool ok = nblk <= a.max_blocks;  // LDS room (checked again; the plan sized it)
-
-        if (nblk > 1u && ok) {
-            for (uint32_t k = tid; k < nblk; k += THREADS) {
-                const uint64_t d = a.live_dst[first + k];
-                s_shift[k] = a.live_src[first + k] - d;
-                s_rel[k] = d <= tb ? 0u : (uint32_t)(d - tb);
-            }
-            __syncthreads();
-        }
-
-        // no branch around a memory access: a lane outside [rel0, rel1)
-        // reloads the tile's first source vector and discards it; so does a
-        // lane of a tile of several blocks whose source would leave the arena
-        // (the blocks' shifts come from the packed arrays, which the check
-        // pass does not read) -- and reports it
         v4u v[VPT];
-        const uint8_t *first_src = a.arena + tb + rel0 + shift0;
-        const uint64_t lim = a.arena_bytes - 16u - tb;  // largest source offset from tb
-        bool lane_bad = false;
-#pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const uint32_t r = ((uint32_t)j * THREADS + tid) * 16u;
-            bool in = ok && r >= rel0 && r < rel1;
-            uint64_t sh = shift0;
-            if (nblk > 1u && ok) {
-                uint32_t lo = 0, n = nblk;  // largest k with s_rel[k] <= r
-                while (n > 1u) {
-                    const uint32_t half = n >> 1;
-                    lo = (s_rel[lo + half] <= r) ? lo + half : lo;
-                    n -= half;
-                }
-                sh = s_shift[lo];
-                const bool inside = (sh & 15u) == 0 && sh <= lim && (uint64_t)r <= lim - sh;
-                lane_bad |= in && !inside;
-                in = in && inside;
-            }
-            v[j] = load16<NT>(in ? a.arena + tb + r + sh : first_src);
-        }
-        if (__builtin_expect(lane_bad, 0)) atomicOr(&a.hdr->status, kStatusCorrupt);
+        const TileView d = load_tile<THREADS, VPT, NT>(a, t, v, s_shift, s_rel);
         // first look at the dependency flags, returned with the data loads
         uint32_t f_lo = 0u, f_hi = 0u;
-        if (tid == 0 && dep_lo <= dep_hi) {
-            f_lo = __hip_atomic_load(&a.flags[dep_lo], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            f_hi = __hip_atomic_load(&a.flags[dep_hi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0 && d.dep_lo <= d.dep_hi) {
+            f_lo = __hip_atomic_load(&a.flags[d.dep_lo], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            f_hi = __hip_atomic_load(&a.flags[d.dep_hi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         // every load of this tile has returned before its flag is published
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tid == 0) {
-            uint32_t skip = ok ? 0u : 1u;
-            if (!ok) atomicOr(&a.hdr->status, kStatusCapacity);
-            if (__builtin_expect(a.stall_every != 0u, 0) && stalls(t, a.stall_every, a.stall_seed)) {
-                for (uint32_t k = 0; k < a.stall_sleeps; ++k) __builtin_amdgcn_s_sleep(127);
-            }
-            __hip_atomic_store(&a.flags[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            // the common case -- no dependency, or the one or two seen done
-            // behind the data loads -- skips the polling loop, marked
-            // unlikely so the compiler keeps the tile's path straight
-            // (measured: +0.6 points on the 80 GiB workload, +1.0 on the
-            // self-overlapping one)
-            const bool seen = dep_lo > dep_hi || (dep_hi - dep_lo <= 1u && f_lo && f_hi);
-            if (__builtin_expect(!seen && !skip, 0)) {
-                uint64_t polls = 0;
-                for (uint32_t u = dep_lo; u <= dep_hi && !skip; ++u) {
-                    if ((u == dep_lo && f_lo) || (u == dep_hi && f_hi)) continue;  // seen done
-                    uint64_t p = 0;
-                    while (__hip_atomic_load(&a.flags[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-                        if (++p > a.spin_limit) {
-                            skip = 1u;
-                            atomicOr(&a.hdr->status, kStatusTimeout);
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                    }
-                    polls += p;
-                }
-                atomicAdd(reinterpret_cast<unsigned long long *>(&a.hdr->late_tiles), 1ull);
-                if (polls) {
-                    atomicAdd(reinterpret_cast<unsigned long long *>(&a.hdr->waited_tiles), 1ull);
-                    atomicAdd(reinterpret_cast<unsigned long long *>(&a.hdr->polls),
-                              (unsigned long long)polls);
-                }
-            }
-            s_skip = skip;
+            publish_tile(a, t, d.ok);
+            s_skip = wait_deps(a, d.dep_lo, d.dep_hi, f_lo, f_hi, d.ok, false);
         }
         __syncthreads();
-        if (!s_skip) {
-            // buffer stores over the tile's window: a lane outside [rel0,
-            // rel1) gets an offset past the window's end, which the hardware
-            // drops -- no branch around any store
-            const __amdgpu_buffer_rsrc_t win = __builtin_amdgcn_make_buffer_rsrc(
-                a.arena + tb, 0, (int)a.tile_bytes, kBufferRsrcWord3);
-#pragma unroll
-            for (int j = 0; j < VPT; ++j) {
-                const uint32_t r = ((uint32_t)j * THREADS + tid) * 16u;
-                const uint32_t off = (r >= rel0 && r < rel1) ? r : kOutOfWindow;
-                __builtin_amdgcn_raw_buffer_store_b128(v[j], win, (int)off, 0,
-                                                       (NT & 2) ? kBufferNt : 0);
-            }
-        }
+        if (!s_skip) store_tile<THREADS, VPT, NT>(a, d, v);
         // Claim the next tile only now: each workgroup holds one ticket at a
         // time, which keeps the tiles in flight in one narrow window of the
         // arena (measured: about 2% more bandwidth than claiming early).
@@ -310,9 +358,74 @@ __device__ __forceinline__ void move_tiles(const MoveArgs &a, uint32_t wg) {
     }
 }
 
+// The same with two tiles per workgroup in flight: the next tile (B) is
+// claimed and its loads issued before the current one (A) waits for the
+// tiles it depends on and stores, so by the time A looks at its
+// dependencies they have nearly always published (a neighbour a short shift
+// away published while B's loads ran).  Every wait still targets lower
+// tickets only: A's dependencies lie below A < B, and the lowest ticket not
+// yet published is some workgroup's B, whose A waits on published tickets
+// alone, so the schedule cannot deadlock.  Used for 128 KiB tiles of
+// 512 lanes, where two tiles fit one lane's registers: there it beats one
+// tile at a time at every shift measured (short shifts 74 -> 83% of the HBM
+// peak, long ones 82 -> 84%); with 64 KiB tiles the doubled window of
+// tickets in flight costs more than it saves.
+template <int THREADS, int VPT, int NT>
+__device__ __forceinline__ void move_tiles_two(const MoveArgs &a, uint32_t wg) {
+    extern __shared__ uint64_t lds_dyn[];
+    uint64_t *s_shift = lds_dyn;                                           // [max_blocks]
+    uint32_t *s_rel = reinterpret_cast<uint32_t *>(lds_dyn + a.max_blocks);  // [max_blocks]
+    __shared__ uint32_t s_ticket;
+    __shared__ uint32_t s_skip;
+    __shared__ uint64_t s_ntiles;
+    const uint32_t tid = threadIdx.x;
+    if (tid == 0) first_claim(a, wg, &s_ticket, &s_ntiles);
+    __syncthreads();
+    const uint64_t n_tiles = s_ntiles;
+    uint32_t tA = s_ticket;
+    if (tA >= n_tiles) return;  // (the whole workgroup)
+    v4u vA[VPT];
+    TileView dA = load_tile<THREADS, VPT, NT>(a, tA, vA, s_shift, s_rel);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) publish_tile(a, tA, dA.ok);
+    for (;;) {
+        if (tid == 0) s_ticket = atomicAdd(&a.hdr->ticket, 1u);
+        __syncthreads();
+        const uint32_t tB = s_ticket;
+        const bool haveB = tB < n_tiles;
+        v4u vB[VPT];
+        TileView dB{};
+        // (the LDS table is A's no longer: its loads have returned)
+        if (haveB) dB = load_tile<THREADS, VPT, NT>(a, tB, vB, s_shift, s_rel);
+        if (tid == 0) s_skip = wait_deps(a, dA.dep_lo, dA.dep_hi, 0u, 0u, dA.ok, true);
+        __syncthreads();
+        if (!s_skip) store_tile<THREADS, VPT, NT>(a, dA, vA);
+        if (!haveB) break;
+        // every load of B has returned before its flag is published
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) publish_tile(a, tB, dB.ok);
+        tA = tB;
+        dA = dB;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) vA[j] = vB[j];
+    }
+}
+
+// Which loop moves a launch's tiles (see move_tiles_two).
+template <int THREADS, int VPT>
+constexpr bool kTwoInFlight = THREADS == 512 && VPT == 16;
+
+template <int THREADS, int VPT, int NT>
+__device__ __forceinline__ void move_launch_tiles(const MoveArgs &a, uint32_t wg) {
+    if constexpr (kTwoInFlight<THREADS, VPT>) move_tiles_two<THREADS, VPT, NT>(a, wg);
+    else move_tiles<THREADS, VPT, NT>(a, wg);
+}
+
 template <int THREADS, int VPT, int NT>
 __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
-    move_tiles<THREADS, VPT, NT>(a, blockIdx.x);
+    move_launch_tiles<THREADS, VPT, NT>(a, blockIdx.x);
 }
 
 // The one-call path's mover: its first side.groups workgroups run the side
@@ -324,7 +437,8 @@ __global__ __launch_bounds__(THREADS) void k_move(MoveArgs a) {
 // fit in that (those run on CUs of their own).
 template <int THREADS, int VPT>
 constexpr int side_waves_per_eu() {
-    return VPT * 4 + 32 < 65536 / THREADS ? THREADS / 128 : 1;
+    constexpr int data = (kTwoInFlight<THREADS, VPT> ? 2 : 1) * VPT * 4;  // VGPRs of tile data
+    return data + 32 < 65536 / THREADS ? THREADS / 128 : 1;
 }
 template <int THREADS, int VPT, int NT>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(side_waves_per_eu<THREADS, VPT>()))) void k_move_side(
@@ -335,7 +449,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(side_wa
             side_part<THREADS>(side, blockIdx.x);
         return;
     }
-    move_tiles<THREADS, VPT, NT>(a, blockIdx.x - side.groups);
+    move_launch_tiles<THREADS, VPT, NT>(a, blockIdx.x - side.groups);
 }
 
 template <int THREADS, int VPT, int NT>

@@ -88,7 +88,7 @@ def expected_schedule(heap, hold, T):
 
 
 def auto_tile(heap, hold):
-    """The tile size a plan given none must choose, stated on the host: 256 KiB
+    """The tile size a plan given none must choose, stated on the host: 128 KiB
     when more than half of the moved bytes belong to blocks that shift by
     less than 8 MiB and at least 64 MiB move, else 64 KiB (the workspaces
     here hold either size's tiles)."""
@@ -98,7 +98,7 @@ def auto_tile(heap, hold):
     sz = heap.size[li].astype(np.int64)
     moved = int(sz[shift > 0].sum())
     small = int(sz[(shift > 0) & (shift < (8 << 20))].sum())
-    return 262144 if (2 * small > moved and moved >= (64 << 20)) else 65536
+    return 131072 if (2 * small > moved and moved >= (64 << 20)) else 65536
 
 
 def check_schedule(ac, heap, T=65536, request=0):
