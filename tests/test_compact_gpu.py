@@ -204,3 +204,58 @@ def test_compact_commit_without_post_check(ac, k):
         ref = host.numpy().copy()
         oracle.compact(ref, heap.offset, heap.size, heap.live, heap.pinned)
         assert np.array_equal(arena.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("k", ["mixed-64m", "training-80g"])
+def test_compact_side_job_parts(ac, k):
+    """Remap, commit and the post-check run in the first workgroups of the
+    mover's launch, each only when asked for: handles alone (no packed
+    table, no post-check), the invalid-handle count alone (no handles), and
+    the packed table with its post-check but no handles -- each against
+    the oracle; and after a failed plan none of the caller's outputs is
+    written."""
+    heap = W.workload(k, small=True)
+    log(f"case side job parts {heap.describe()}")
+    host = pristine_host(heap)
+    off, size, live = device_table(heap, "cuda")
+    ws = ac.workspace(heap.n, heap.arena_bytes)
+    m = int(heap.live.sum())
+    want_h, want_bad = oracle.remap(heap.offset, heap.size, heap.live, heap.handles)
+    want_new = oracle.new_offsets(heap.offset, heap.size, heap.live)
+    want_post = oracle.stats(want_new[np.flatnonzero(heap.live)], heap.size[np.flatnonzero(heap.live)],
+                             np.ones(m, np.uint8), heap.arena_bytes)
+    # handles alone
+    h = u64_to_t(heap.handles, "cuda")
+    h_out = torch.full_like(h, -5)
+    nb = torch.full((1,), -3, dtype=torch.int64, device="cuda")
+    plan, post = ac.defrag_compact(off, size, live, heap.arena_bytes, host.cuda(), ws,
+                                   handles=h, h_out=h_out, n_invalid=nb)
+    assert post is None and plan.live_blocks == m
+    assert np.array_equal(t_to_u64(h_out), want_h) and int(nb.item()) == want_bad
+    # the count alone: no handles, so nothing is invalid
+    nb.fill_(-3)
+    ac.defrag_compact(off, size, live, heap.arena_bytes, host.cuda(), ws, n_invalid=nb)
+    assert int(nb.item()) == 0
+    # the packed table and its post-check, no handles
+    c_off = torch.full((m,), -7, dtype=torch.int64, device="cuda")
+    c_size = torch.full((m,), -7, dtype=torch.int64, device="cuda")
+    c_live = torch.full((m,), 7, dtype=torch.uint8, device="cuda")
+    plan, post = ac.defrag_compact(off, size, live, heap.arena_bytes, host.cuda(), ws,
+                                   offset_out=c_off, size_out=c_size, live_out=c_live)
+    assert np.array_equal(t_to_u64(c_off), want_new[np.flatnonzero(heap.live)])
+    assert np.array_equal(t_to_u64(c_size), heap.size[np.flatnonzero(heap.live)])
+    assert bool(torch.all(c_live == 1))
+    check_stats(post, want_post, "post-check without handles")
+    # a failed plan (an invalid entry): no output written
+    bad = size.clone()
+    bad[1] = 48
+    h_out.fill_(-5)
+    c_off.fill_(-7)
+    c_size.fill_(-7)
+    with pytest.raises(ac.DefragError) as e:
+        ac.defrag_compact(off, bad, live, heap.arena_bytes, host.cuda(), ws, handles=h,
+                          h_out=h_out, offset_out=c_off, size_out=c_size)
+    assert e.value.code == ac.DEFRAG_EINVAL and e.value.invalid_index == 1
+    torch.cuda.synchronize()
+    assert bool(torch.all(h_out == -5)) and bool(torch.all(c_off == -7))
+    assert bool(torch.all(c_size == -7))
