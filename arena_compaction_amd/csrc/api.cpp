@@ -557,13 +557,13 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
         arg_error(&plan->stats);
         return DEFRAG_EINVAL;
     }
-    // Everything is queued at once and sized on the device: the move right
-    // behind the plan's passes, reading the tile count from the plan's
-    // header; remap, commit and the post-check on a second stream that
-    // waits for the plan and takes the live count from the same header (a
-    // failed plan moves and writes nothing).  They read the plan, never the
-    // arena, so they run while the move does.  One read of both headers at
-    // the end fills the host plan.  That needs the arena and the
+    // Everything is queued at once on `stream` and sized on the device: the
+    // move right behind the plan's passes, reading the tile count from the
+    // plan's header; remap, commit and the post-check in the first
+    // workgroups of the mover's launch, taking the live count from the same
+    // header (a failed plan moves and writes nothing).  They read the plan,
+    // never the arena, so they run while the move does.  One read of both
+    // headers at the end fills the host plan.  That needs the arena and the
     // post-check's outputs known good before anything is queued, and a
     // workgroup count the device can pick; otherwise the calls run in the
     // plain order (plan, read back, check, move), which rejects a bad

@@ -149,11 +149,12 @@ typedef struct defrag_stats_t {
 typedef struct defrag_tuning {
     uint32_t tile_bytes;      /* mover tile: power of two in [256, 262144],
                                  or 0: the plan chooses on the device from the
-                                 shifts it finds -- 262144 when more than half
+                                 shifts it finds -- 131072 when more than half
                                  of the moved bytes shift by less than 8 MiB
                                  and at least 64 MiB move (a tile then often
-                                 waits on one still being read, and larger
-                                 tiles amortise that wait), else 65536 -- and
+                                 depends on one still being read; 128 KiB
+                                 tiles are moved two per workgroup in flight,
+                                 which hides that wait), else 65536 -- and
                                  the other one if the first's tiles do not fit
                                  the workspace.  plan_host->tuning.tile_bytes
                                  says which.                                 */
