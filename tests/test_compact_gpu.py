@@ -259,3 +259,58 @@ def test_compact_side_job_parts(ac, k):
     torch.cuda.synchronize()
     assert bool(torch.all(h_out == -5)) and bool(torch.all(c_off == -7))
     assert bool(torch.all(c_size == -7))
+
+
+@pytest.mark.parametrize("tile", [0, 256])
+def test_compact_edge_cases(ac, tile):
+    """The one call on degenerate tables -- no entries, nothing live, all
+    live with no hole, one tiny block far up -- with every output asked
+    for (buffers of at least one entry, so the call takes its one-stream
+    path even when nothing is live): new offsets, handles (edges included),
+    the packed table, its post-check and every arena byte against the
+    oracle."""
+    cases = [
+        W.table_from_lists(4096, [], [], [0, 5, 4096]),                    # n = 0
+        W.table_from_lists(4096, [(0, 1024), (2048, 512)], [0, 0], [0, 2048]),  # all free
+        W.table_from_lists(2048, [(0, 1024), (1024, 1024)], [1, 1], [0, 2047]),  # all live, full
+        W.table_from_lists(4096, [(0, 1024), (1024, 1024)], [1, 1], [0, 2047, 2048]),
+        W.table_from_lists(8192, [(4096, 32)], [1], [4096, 4127]),         # one tiny block
+    ]
+    tu = ac.defrag_tuning(tile, 1, 1, 0) if tile else None
+    for heap in cases:
+        log(f"case one-call edge {heap.describe()} tile {tile}")
+        host = pristine_host(heap)
+        arena = host.cuda()
+        off, size, live = device_table(heap, "cuda")
+        ws = ac.workspace(max(heap.n, 1), heap.arena_bytes, tile)
+        li = np.flatnonzero(heap.live)
+        m, k = li.shape[0], max(li.shape[0], 1)
+        hs = np.concatenate([heap.handles, W.edge_handles(heap, np.random.default_rng(1), 8)])
+        h = u64_to_t(hs, "cuda")
+        h_out = torch.full_like(h, -5)
+        nb = torch.full((1,), -3, dtype=torch.int64, device="cuda")
+        new_off = torch.full((max(heap.n, 1),), -7, dtype=torch.int64, device="cuda")
+        c_off = torch.full((k,), -7, dtype=torch.int64, device="cuda")
+        c_size = torch.full((k,), -7, dtype=torch.int64, device="cuda")
+        c_live = torch.full((k,), 7, dtype=torch.uint8, device="cuda")
+        plan, post = ac.defrag_compact(off, size, live, heap.arena_bytes, arena, ws,
+                                       new_offset=new_off[:heap.n], handles=h, h_out=h_out,
+                                       n_invalid=nb, offset_out=c_off, size_out=c_size,
+                                       live_out=c_live, tuning=tu, after=True)
+        torch.cuda.synchronize()
+        want_new = oracle.new_offsets(heap.offset, heap.size, heap.live)
+        assert np.array_equal(t_to_u64(new_off)[:heap.n], want_new)
+        want_h, want_bad = oracle.remap(heap.offset, heap.size, heap.live, hs)
+        assert np.array_equal(t_to_u64(h_out), want_h) and int(nb.item()) == want_bad
+        assert plan.live_blocks == m
+        assert np.array_equal(t_to_u64(c_off)[:m], want_new[li])
+        assert np.array_equal(t_to_u64(c_size)[:m], heap.size[li])
+        assert bool(torch.all(c_live[:m] == 1))
+        if m < k:  # nothing live: the packed outputs are not written
+            assert int(c_off[0]) == -7 and int(c_size[0]) == -7 and int(c_live[0]) == 7
+        want_post = oracle.stats(want_new[li], heap.size[li], np.ones(m, np.uint8),
+                                 heap.arena_bytes)
+        check_stats(post, want_post, "one-call edge post-check")
+        ref = host.numpy().copy()
+        oracle.compact(ref, heap.offset, heap.size, heap.live)
+        assert np.array_equal(arena.cpu().numpy(), ref)
