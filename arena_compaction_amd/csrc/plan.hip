@@ -533,7 +533,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
         return;
     }
     // every load that does not depend on another is issued before the
-    // first is used (the header's verdict included): one memory round trip
+    // first is used (the header's outcome included): one memory round trip
     // where there were four
     const uint64_t j0 = (uint64_t)threadIdx.x * kPartsPer;
     uint64_t ta[kPartsPer], tb[kPartsPer];
