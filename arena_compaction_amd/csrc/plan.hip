@@ -877,20 +877,21 @@ __device__ inline bool sel_better(uint64_t c1, uint64_t k1, uint64_t c2, uint64_
     return c1 < c2 || (c1 == c2 && k1 < k2);
 }
 
+struct SelCand {
+    uint64_t c, k, l;
+};
+__device__ inline SelCand sel_op(const SelCand &a, const SelCand &b) {
+    return sel_better(b.c, b.k, a.c, a.k) ? b : a;
+}
+
 // Workgroup arg-min of (cost, k) carrying l, through LDS (NT threads).
 template <int NT>
 __device__ inline void sel_reduce(uint64_t &c, uint64_t &k, uint64_t &l, uint64_t *sh) {
     constexpr int NW = NT / 64;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        const uint64_t c2 = __shfl_xor(c, d, 64), k2 = __shfl_xor(k, d, 64),
-                       l2 = __shfl_xor(l, d, 64);
-        if (sel_better(c2, k2, c, k)) {
-            c = c2;
-            k = k2;
-            l = l2;
-        }
-    }
+    const SelCand best = wave_reduce(SelCand{c, k, l}, sel_op);
+    c = best.c;
+    k = best.k;
+    l = best.l;
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
         sh[3 * w] = c;

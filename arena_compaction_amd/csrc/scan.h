@@ -15,6 +15,7 @@
 #ifndef ARENA_COMPACTION_SCAN_H
 #define ARENA_COMPACTION_SCAN_H
 #include "internal.h"
+#include "wave.h"
 
 namespace ac {
 namespace {
@@ -56,17 +57,7 @@ __device__ inline Agg element(uint64_t o, uint64_t s, uint32_t l, uint32_t p, ui
     return e;
 }
 
-__device__ inline Agg shfl_up_agg(const Agg &a, int d) {
-    Agg b;
-    b.v = __shfl_up(a.v, d, 64);
-    b.mx = __shfl_up(a.mx, d, 64);
-    b.cnt = __shfl_up(a.cnt, d, 64);
-    b.lsum = __shfl_up(a.lsum, d, 64);
-    b.pcnt = __shfl_up(a.pcnt, d, 64);
-    b.r = __shfl_up(a.r, d, 64);
-    b.pad = 0;
-    return b;
-}
+__device__ inline Agg combine_op(const Agg &a, const Agg &b) { return combine(a, b); }
 
 // LDS slots the two cross-wave helpers below need for NT lanes.
 template <int NT>
@@ -75,34 +66,22 @@ template <int NT>
 constexpr int kStatSlots = 12 * (NT / 64 + 1);  // u64 slots of block_reduce_stats
 
 // Exclusive workgroup scan in thread order; also returns the total.
-// sh: kExclSlots<NT> entries.  Each wave scans itself with shuffles; the
+// sh: kExclSlots<NT> entries.  Each wave scans itself across its lanes; the
 // first wave then scans the waves' totals (one per lane) and hands every
 // wave its prefix through LDS, so no lane holds more than a few aggregates.
 template <int NT>
 __device__ inline Agg block_excl(const Agg &x, Agg &total, Agg *sh) {
     constexpr int NW = NT / 64;
-    static_assert(NW >= 1 && NW <= 64 && (NW & (NW - 1)) == 0, "whole waves, a power of two");
+    static_assert(NW >= 1 && NW <= 16 && (NW & (NW - 1)) == 0, "whole waves, a power of two");
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    Agg inc = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const Agg y = shfl_up_agg(inc, d);
-        if (lane >= d) inc = combine(y, inc);
-    }
-    Agg ex = shfl_up_agg(inc, 1);
-    if (lane == 0) ex = agg_zero();
+    const Agg inc = wave_incl_scan(x, combine_op);
+    const Agg ex = wave_shift_up(inc);
     if (lane == 63) sh[w] = inc;
     __syncthreads();
     if (w == 0) {
-        Agg t = lane < NW ? sh[lane] : agg_zero();
-#pragma unroll
-        for (int d = 1; d < NW; d <<= 1) {
-            const Agg y = shfl_up_agg(t, d);
-            if (lane >= d) t = combine(y, t);
-        }
-        Agg te = shfl_up_agg(t, 1);
-        if (lane == 0) te = agg_zero();
+        const Agg t = wave_incl_scan<NW>(lane < NW ? sh[lane] : agg_zero(), combine_op);
+        const Agg te = wave_shift_up(t);
         if (lane < NW) sh[NW + lane] = te;
         if (lane == NW - 1) sh[2 * NW] = t;
     }
@@ -113,18 +92,15 @@ __device__ inline Agg block_excl(const Agg &x, Agg &total, Agg *sh) {
     return combine(pre, ex);
 }
 
+__device__ inline uint64_t add_op(uint64_t a, uint64_t b) { return a + b; }
+
 // Exclusive workgroup sum of u64; also returns the total.  sh: NT/64 slots.
 template <int NT>
 __device__ inline uint64_t block_excl_sum(uint64_t x, uint64_t &total, uint64_t *sh) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    uint64_t inc = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint64_t y = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += y;
-    }
+    const uint64_t inc = wave_incl_scan(x, add_op);
     if (lane == 63) sh[w] = inc;
     __syncthreads();
     uint64_t pre = 0, tot = 0;
@@ -133,8 +109,7 @@ __device__ inline uint64_t block_excl_sum(uint64_t x, uint64_t &total, uint64_t 
         if (k < w) pre += sh[k];
         tot += sh[k];
     }
-    uint64_t ex = __shfl_up(inc, 1, 64);
-    if (lane == 0) ex = 0;
+    const uint64_t ex = wave_shift_up(inc);
     __syncthreads();
     total = tot;
     return pre + ex;
@@ -144,8 +119,7 @@ __device__ inline uint64_t block_excl_sum(uint64_t x, uint64_t &total, uint64_t 
 template <int NT, typename Op>
 __device__ inline uint64_t block_reduce(uint64_t v, uint64_t *sh, Op op) {
     constexpr int NW = NT / 64;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v = op(v, (uint64_t)__shfl_xor(v, d, 64));
+    v = wave_reduce(v, op);
     if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
     __syncthreads();
     uint64_t r = sh[0];
@@ -159,55 +133,58 @@ struct OpAdd { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { re
 struct OpMax { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return umax64(a, b); } };
 struct OpMin { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return umin64(a, b); } };
 
-// Workgroup reduction of the statistics and up to four extra sums: each
-// wave reduces with shuffles and writes one row to LDS; the first wave's
-// lanes take one row each and reduce them with shuffles; every lane reads
-// the result.  sh: kStatSlots<NT> slots.
-__device__ inline void stat_shfl_reduce(StatPart &q, uint64_t (&x)[4], int d) {
-    q.max_gap = umax64(q.max_gap, (uint64_t)__shfl_xor(q.max_gap, d, 64));
-    q.gaps += (uint64_t)__shfl_xor(q.gaps, d, 64);
-    q.moved_blocks += (uint64_t)__shfl_xor(q.moved_blocks, d, 64);
-    q.moved_bytes += (uint64_t)__shfl_xor(q.moved_bytes, d, 64);
-    q.min_moved_dst = umin64(q.min_moved_dst, (uint64_t)__shfl_xor(q.min_moved_dst, d, 64));
-    q.min_size = umin64(q.min_size, (uint64_t)__shfl_xor(q.min_size, d, 64));
-    q.min_fit = umin64(q.min_fit, (uint64_t)__shfl_xor(q.min_fit, d, 64));
-    q.small_moved += (uint64_t)__shfl_xor(q.small_moved, d, 64);
+// The statistics and up to four extra sums, as one value to reduce.
+struct StatRow {
+    StatPart q;
+    uint64_t x[4];
+};
+__device__ inline StatRow stat_op(const StatRow &a, const StatRow &b) {
+    StatRow c;
+    c.q.max_gap = umax64(a.q.max_gap, b.q.max_gap);
+    c.q.gaps = a.q.gaps + b.q.gaps;
+    c.q.moved_blocks = a.q.moved_blocks + b.q.moved_blocks;
+    c.q.moved_bytes = a.q.moved_bytes + b.q.moved_bytes;
+    c.q.min_moved_dst = umin64(a.q.min_moved_dst, b.q.min_moved_dst);
+    c.q.min_size = umin64(a.q.min_size, b.q.min_size);
+    c.q.min_fit = umin64(a.q.min_fit, b.q.min_fit);
+    c.q.small_moved = a.q.small_moved + b.q.small_moved;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) x[k] += (uint64_t)__shfl_xor(x[k], d, 64);
+    for (int k = 0; k < 4; ++k) c.x[k] = a.x[k] + b.x[k];
+    return c;
 }
-__device__ inline void stat_store(uint64_t *o, const StatPart &q, const uint64_t (&x)[4]) {
-    o[0] = q.max_gap; o[1] = q.gaps; o[2] = q.moved_blocks; o[3] = q.moved_bytes;
-    o[4] = q.min_moved_dst; o[5] = q.min_size; o[6] = q.min_fit; o[7] = q.small_moved;
-    o[8] = x[0]; o[9] = x[1]; o[10] = x[2]; o[11] = x[3];
+__device__ inline void stat_store(uint64_t *o, const StatRow &r) {
+    o[0] = r.q.max_gap; o[1] = r.q.gaps; o[2] = r.q.moved_blocks; o[3] = r.q.moved_bytes;
+    o[4] = r.q.min_moved_dst; o[5] = r.q.min_size; o[6] = r.q.min_fit; o[7] = r.q.small_moved;
+    o[8] = r.x[0]; o[9] = r.x[1]; o[10] = r.x[2]; o[11] = r.x[3];
 }
-__device__ inline void stat_load(const uint64_t *o, StatPart &q, uint64_t (&x)[4]) {
-    q = StatPart{o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
-    x[0] = o[8]; x[1] = o[9]; x[2] = o[10]; x[3] = o[11];
+__device__ inline StatRow stat_load(const uint64_t *o) {
+    return StatRow{StatPart{o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]},
+                   {o[8], o[9], o[10], o[11]}};
 }
+
+// Workgroup reduction of the statistics and up to four extra sums: each
+// wave reduces across its lanes and writes one row to LDS; the first wave's
+// lanes take one row each and reduce them the same way; every lane reads
+// the result.  sh: kStatSlots<NT> slots.
 template <int NT>
 __device__ inline void block_reduce_stats(StatPart &q, uint64_t (&x)[4], uint64_t *sh) {
     constexpr int NW = NT / 64;
-    static_assert(NW >= 1 && NW <= 64 && (NW & (NW - 1)) == 0, "whole waves, a power of two");
+    static_assert(NW >= 1 && NW <= 16 && (NW & (NW - 1)) == 0, "whole waves, a power of two");
     constexpr int F = 12;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) stat_shfl_reduce(q, x, d);
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    if (lane == 0) stat_store(sh + F * w, q, x);
+    const StatRow r = wave_reduce(StatRow{q, {x[0], x[1], x[2], x[3]}}, stat_op);
+    if (lane == 0) stat_store(sh + F * w, r);
     __syncthreads();
     if (w == 0) {
-        if (lane < NW) {
-            stat_load(sh + F * lane, q, x);
-        } else {  // the identity
-            q = StatPart{0, 0, 0, 0, kNone, kNone, kNone, 0};
-            x[0] = x[1] = x[2] = x[3] = 0;
-        }
-#pragma unroll
-        for (int d = NW / 2; d >= 1; d >>= 1) stat_shfl_reduce(q, x, d);
-        if (lane == 0) stat_store(sh + F * NW, q, x);
+        const StatRow t = wave_reduce<NW>(stat_load(sh + F * (lane < NW ? lane : 0)), stat_op);
+        if (lane == 0) stat_store(sh + F * NW, t);
     }
     __syncthreads();
-    stat_load(sh + F * NW, q, x);
+    const StatRow t = stat_load(sh + F * NW);
+    q = t.q;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = t.x[k];
     __syncthreads();
 }
 

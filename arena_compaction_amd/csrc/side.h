@@ -167,8 +167,7 @@ __device__ void side_part(const SideArgs &s, uint32_t g) {
     else
         bad = remap_range<kSideRec64>(s, m, k0, stride);
     if (s.n_invalid) {
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) bad += __shfl_xor(bad, d, 64);
+        bad = wave_reduce(bad, add_op);
         if ((threadIdx.x & 63) == 0 && bad) atomicAdd(s.n_invalid, (unsigned long long)bad);
     }
 }

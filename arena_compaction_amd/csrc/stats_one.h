@@ -61,18 +61,15 @@ __device__ inline uint64_t csum_field(const uint64_t *f) {
     return __hip_atomic_load(const_cast<uint64_t *>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ inline uint64_t max_op(uint64_t a, uint64_t b) { return umax64(a, b); }
+
 // Exclusive workgroup scan of a u64 under max; also returns the total.
 template <int NT>
 __device__ inline uint64_t block_excl_max(uint64_t x, uint64_t &total, uint64_t *sh) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    uint64_t inc = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint64_t y = __shfl_up(inc, d, 64);
-        if (lane >= d) inc = umax64(inc, y);
-    }
+    const uint64_t inc = wave_incl_scan(x, max_op);
     if (lane == 63) sh[w] = inc;
     __syncthreads();
     uint64_t pre = 0, tot = 0;
@@ -81,8 +78,7 @@ __device__ inline uint64_t block_excl_max(uint64_t x, uint64_t &total, uint64_t 
         if (k < w) pre = umax64(pre, sh[k]);
         tot = umax64(tot, sh[k]);
     }
-    uint64_t ex = __shfl_up(inc, 1, 64);
-    if (lane == 0) ex = 0;
+    const uint64_t ex = wave_shift_up(inc);
     __syncthreads();
     total = tot;
     return umax64(pre, ex);
@@ -102,20 +98,14 @@ __device__ inline uint32_t block_excl_pend(uint32_t x, uint32_t *sh) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    uint32_t inc = x;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(inc, d, 64);
-        if (lane >= d) inc = pend_then(y, inc);
-    }
+    const uint32_t inc = wave_incl_scan(x, pend_then);
     if (lane == 63) sh[w] = inc;
     __syncthreads();
     uint32_t pre = 0u;
 #pragma unroll
     for (int k = 0; k < NW; ++k)
         if (k < w) pre = pend_then(pre, sh[k]);
-    uint32_t ex = __shfl_up(inc, 1, 64);
-    if (lane == 0) ex = 0u;
+    const uint32_t ex = wave_shift_up(inc);
     __syncthreads();
     return pend_then(pre, ex);
 }
