@@ -611,13 +611,60 @@ __device__ inline int64_t last_le(const T *a, int64_t lo, int64_t hi, uint64_t x
     return l - 1;
 }
 
+// The packed live arrays and the tile bases as the tile records read them:
+// with STAGED, entries [lo, lo + cnt) from copies in LDS (the stretch of
+// blocks a workgroup's tiles start in, and one on each side), any other from
+// global memory; without, all from global memory.  The copies are addressed
+// as LDS so that a read of either kind stays its own instruction.
+typedef __attribute__((address_space(3))) const uint64_t lds_u64;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+template <bool STAGED>
+struct LiveAt {
+    LiveView lv;
+    const uint32_t *tile_base;
+    lds_u64 *s_dst, *s_src, *s_size;
+    lds_u32 *s_tb;
+    uint64_t lo, cnt;
+    __device__ bool staged(uint64_t k) const { return STAGED && k - lo < cnt; }  // (k < lo wraps)
+    __device__ uint64_t dst(uint64_t k) const { return staged(k) ? s_dst[k - lo] : lv.dst[k]; }
+    __device__ uint64_t src(uint64_t k) const { return staged(k) ? s_src[k - lo] : lv.src[k]; }
+    __device__ uint64_t size(uint64_t k) const { return staged(k) ? s_size[k - lo] : lv.size[k]; }
+    __device__ uint64_t tb(uint64_t k) const { return staged(k) ? s_tb[k - lo] : tile_base[k]; }
+    __device__ bool moved(uint64_t k) const { return src(k) != dst(k); }
+};
+
+// Every live block staged: all reads from LDS (entry k at k - lo), so the
+// reads of a search step are issued together.
+struct LiveLds {
+    lds_u64 *s_dst, *s_src, *s_size;
+    lds_u32 *s_tb;
+    uint32_t lo;
+    __device__ uint64_t dst(uint64_t k) const { return s_dst[(uint32_t)k - lo]; }
+    __device__ uint64_t src(uint64_t k) const { return s_src[(uint32_t)k - lo]; }
+    __device__ uint64_t size(uint64_t k) const { return s_size[(uint32_t)k - lo]; }
+    __device__ uint64_t tb(uint64_t k) const { return s_tb[(uint32_t)k - lo]; }
+    __device__ bool moved(uint64_t k) const { return src(k) != dst(k); }
+};
+
+// The same over a short array in LDS, in 32-bit arithmetic.
+__device__ inline int32_t last_le32(const uint32_t *a, int32_t lo, int32_t hi, uint32_t x) {
+    int32_t l = lo, h = hi;
+    while (l < h) {
+        const int32_t mid = l + ((h - l) >> 1);
+        if (a[mid] <= x) l = mid + 1;
+        else h = mid;
+    }
+    return l - 1;
+}
+
 // Where tile t starts, given its first block k (the last block whose first
 // tile index tb_k is <= t).
-__device__ inline uint64_t tile_start_at(const LiveView &lv, uint64_t k, uint64_t tb_k,
+template <typename LA>
+__device__ inline uint64_t tile_start_at(const LA &lv, uint64_t k, uint64_t tb_k,
                                          uint64_t t, uint64_t T) {
     const uint64_t j = t - tb_k;
-    const uint64_t a = lv.dst[k];
-    const bool start = (k == 0) || !moved_at(lv, (uint64_t)k - 1);
+    const uint64_t a = lv.dst(k);
+    const bool start = (k == 0) || !lv.moved(k - 1);
     const uint64_t lead = (start && (a & (T - 1))) ? 1 : 0;
     const uint64_t first_mult = (a + T - 1) & ~(T - 1);
     return (j < lead) ? a : first_mult + (j - lead) * T;
@@ -625,16 +672,17 @@ __device__ inline uint64_t tile_start_at(const LiveView &lv, uint64_t k, uint64_
 
 // The tile holding destination byte q of moved block b (tiles cut each run
 // at its start and at every multiple of T).
-__device__ inline uint64_t tile_of(const LiveView &lv, const uint32_t *tile_base, uint64_t b,
-                                   uint64_t q, uint64_t T) {
-    const uint64_t a = lv.dst[b];
+template <typename LA>
+__device__ inline uint64_t tile_of(const LA &lv, uint64_t b, uint64_t q, uint64_t T) {
+    const uint64_t a = lv.dst(b);
     const uint64_t A = (a + T - 1) & ~(T - 1);
-    const bool start = (b == 0) || !moved_at(lv, b - 1);
+    const bool start = (b == 0) || !lv.moved(b - 1);
     const uint64_t lead = (start && (a & (T - 1))) ? 1 : 0;
-    if (q >= A) return tile_base[b] + lead + div_tile(q - A, T);
+    const uint64_t tb = lv.tb(b);
+    if (q >= A) return tb + lead + div_tile(q - A, T);
     // q lies in the window block b starts in: block b's own first tile if it
     // starts a run there, else the tile that began earlier in the run
-    return lead ? tile_base[b] : tile_base[b] - 1;
+    return lead ? tb : tb - 1;
 }
 
 // Tile t's record, given its start t0, its first block and its end bound
@@ -647,11 +695,13 @@ __device__ inline uint64_t tile_of(const LiveView &lv, const uint32_t *tile_base
 // a short range ending at or before this one.  ridx: the remap's bucket
 // index (bucket width 2^w), which narrows the search for the first such
 // block, or null to search all m blocks.
-__device__ inline TileRec tile_record(const LiveView &lv, const uint32_t *tile_base, uint64_t m,
-                                      uint64_t t, uint64_t t0, uint64_t first, uint64_t bound,
-                                      uint64_t T, const uint32_t *ridx, uint32_t w) {
+template <typename LA>
+__device__ inline TileRec tile_record(const LA &lv, uint64_t m, uint64_t t, uint64_t t0,
+                                      uint64_t first, uint64_t bound, uint64_t T,
+                                      const uint32_t *ridx, uint32_t w) {
     // Two searches that do not depend on each other run in one loop, the
-    // loads of a step issued together (each step is a memory round trip):
+    // loads of a step issued together (each step is a memory round trip
+    // unless the blocks are staged):
     //  * the last block of the run inside [t0, bound): the blocks after
     //    first that start below bound and moved form a prefix -- gallop
     //    (doubling), then bisect; the end of the last one found so far is
@@ -669,7 +719,7 @@ __device__ inline TileRec tile_record(const LiveView &lv, const uint32_t *tile_b
         hi = (int64_t)r1;
     }
     uint64_t last = first, stride = 1;
-    uint64_t last_end = lv.dst[first] + lv.size[first];
+    uint64_t last_end = lv.dst(first) + lv.size(first);
     bool doubling = true;
     for (;;) {
         const bool g_on = stride > 0;
@@ -680,12 +730,12 @@ __device__ inline TileRec tile_record(const LiveView &lv, const uint32_t *tile_b
         bool g_ok = false;
         uint64_t g_end = 0;
         if (g_on && gi < m) {
-            const uint64_t d = lv.dst[gi], sz = lv.size[gi], sr = lv.src[gi];
+            const uint64_t d = lv.dst(gi), sz = lv.size(gi), sr = lv.src(gi);
             g_ok = (d < bound) & (sr != d);  // starts below bound, moved
             g_end = d + sz;
         }
         bool s_right = false;
-        if (s_on) s_right = lv.src[mid] + lv.size[mid] <= t0;
+        if (s_on) s_right = lv.src(mid) + lv.size(mid) <= t0;
         if (g_on) {
             if (g_ok) {
                 last = gi;
@@ -707,21 +757,22 @@ __device__ inline TileRec tile_record(const LiveView &lv, const uint32_t *tile_b
     uint32_t dep_lo = 1, dep_hi = 0;  // empty
     if (lo < (int64_t)m && t > 0) {
         const uint64_t j = (uint64_t)lo;
-        const uint64_t sj = lv.src[j];
+        const uint64_t sj = lv.src(j);
         if (sj < t1) {
-            const uint64_t q_lo = lv.dst[j] + (t0 > sj ? t0 - sj : 0);
-            const uint64_t u_lo = tile_of(lv, tile_base, j, q_lo, T);
+            const uint64_t q_lo = lv.dst(j) + (t0 > sj ? t0 - sj : 0);
+            const uint64_t u_lo = tile_of(lv, j, q_lo, T);
             // ... and the last block whose source starts below t1 (gallop from j)
             uint64_t c = j;
             stride = 1;
-            while (c + stride < m && lv.src[c + stride] < t1) {
+            while (c + stride < m && lv.src(c + stride) < t1) {
                 c += stride;
                 stride <<= 1;
             }
             for (; stride > 0; stride >>= 1)
-                if (c + stride < m && lv.src[c + stride] < t1) c += stride;
-            const uint64_t q_hi = lv.dst[c] + umin64(lv.size[c], t1 - lv.src[c]) - 1;
-            uint64_t u_hi = tile_of(lv, tile_base, c, q_hi, T);
+                if (c + stride < m && lv.src(c + stride) < t1) c += stride;
+            const uint64_t sc = lv.src(c);
+            const uint64_t q_hi = lv.dst(c) + umin64(lv.size(c), t1 - sc) - 1;
+            uint64_t u_hi = tile_of(lv, c, q_hi, T);
             if (u_hi > t - 1) u_hi = t - 1;
             if (u_lo <= u_hi) {
                 dep_lo = (uint32_t)u_lo;
@@ -729,7 +780,7 @@ __device__ inline TileRec tile_record(const LiveView &lv, const uint32_t *tile_b
             }
         }
     }
-    return TileRec{t0, t1, lv.src[first] - lv.dst[first], (uint32_t)first, (uint32_t)last,
+    return TileRec{t0, t1, lv.src(first) - lv.dst(first), (uint32_t)first, (uint32_t)last,
                    dep_lo, dep_hi, 0};
 }
 
@@ -778,17 +829,29 @@ __device__ inline void find_stretch(const uint32_t *a, int64_t m, uint64_t x0, u
 // Each tile's first block is the last block whose first tile index is <= t
 // (a search over tile_base).  The workgroup's tiles [tb, tb + 256) -- and the
 // tile after them, whose start bounds the last one -- have their first blocks
-// in one stretch of tile_base; when it is short it is staged in LDS with one
-// coalesced load and every lane searches there (a small plan stages all of
-// tile_base and searches global memory not at all).  Each lane also leaves
-// its tile's start in LDS for the lane before it.
-constexpr uint32_t kTileStage = 2048;  // tile_base entries staged per workgroup
+// in one stretch of tile_base.  When it is short, that stretch of tile_base
+// and of the packed live arrays (with one block on each side) is staged in
+// LDS with one memory round trip, and the searches for each tile's first
+// block, its start and its run read there; a small plan stages every live
+// block and reads global memory only to stage.  Each lane also leaves its
+// tile's start in LDS for the lane before it.
+constexpr uint32_t kTileStage = 2048;  // blocks of the stretch staged per workgroup
+// Plans of at most this many tiles stage the live arrays: 512 workgroups,
+// two on each compute unit of a 256-CU device.
+constexpr uint64_t kStageTileLimit = 512ull * 256;
 
+// STAGE: the live arrays are staged too (58 KiB of LDS, two workgroups per
+// compute unit); without, tile_base alone (8 KiB).  Staging pays when the
+// plan's tiles take few workgroups, which then all run at once.
+template <bool STAGE>
 __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint32_t *tile_base,
                                                const WsHeader *hdr, uint64_t max_tiles,
                                                const uint32_t *ridx, uint32_t w, TileRec *tiles,
                                                uint32_t *flags) {
-    __shared__ uint32_t s_tb[kTileStage];
+    constexpr uint32_t kCap = kTileStage + 2;
+    constexpr uint32_t kLiveCap = STAGE ? kCap : 1;
+    __shared__ uint32_t s_tb[kCap];
+    __shared__ uint64_t s_dst[kLiveCap], s_src[kLiveCap], s_size[kLiveCap];
     __shared__ uint64_t s_t0[257];
     __shared__ int64_t s_k[2];
     const uint64_t n_tiles = hdr->n_tiles, m = hdr->live_blocks, T = hdr->tile_bytes;
@@ -810,35 +873,80 @@ __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint32_t *tile
     __syncthreads();
     const int64_t k_lo = s_k[0], k_hi = s_k[1];
     const bool staged = k_hi - k_lo < (int64_t)kTileStage;
-    if (staged)
-        for (int64_t i = threadIdx.x; i <= k_hi - k_lo; i += 256) s_tb[i] = tile_base[k_lo + i];
-    __syncthreads();
-    // first block of tile u (tb <= u <= tq), and its first tile index
-    const auto first_of = [&](uint64_t u, uint64_t *tb_k) -> uint64_t {
-        if (staged) {
-            const int64_t r = last_le(s_tb, 0, k_hi - k_lo + 1, u);
-            *tb_k = s_tb[r];
-            return (uint64_t)(k_lo + r);
+    // staged: blocks [s_lo, s_lo + s_cnt) -- the stretch, the block before it
+    // (a tile's start reads the block before its first) and the one after
+    // it (a run's last block may follow the stretch)
+    const uint64_t s_lo = (staged && k_lo > 0) ? (uint64_t)k_lo - 1 : 0;
+    const uint64_t s_cnt = staged ? umin64((uint64_t)k_hi + 2, m) - s_lo : 0;
+    if (staged) {
+        // every load issued before the first is stored: one round trip
+        constexpr uint32_t kPer = (kCap + 255) / 256;
+        uint64_t vd[kPer] = {}, vs[kPer] = {}, vz[kPer] = {};
+        uint32_t vt[kPer] = {};
+#pragma unroll
+        for (uint32_t k = 0; k < kPer; ++k) {
+            const uint64_t i = threadIdx.x + k * 256;
+            if (i < s_cnt) {
+                vt[k] = tile_base[s_lo + i];
+                if constexpr (STAGE) {
+                    vd[k] = lv.dst[s_lo + i];
+                    vs[k] = lv.src[s_lo + i];
+                    vz[k] = lv.size[s_lo + i];
+                }
+            }
         }
-        const int64_t k = last_le(tile_base, k_lo, k_hi + 1, u);
+#pragma unroll
+        for (uint32_t k = 0; k < kPer; ++k) {
+            const uint64_t i = threadIdx.x + k * 256;
+            if (i < s_cnt) {
+                s_tb[i] = vt[k];
+                if constexpr (STAGE) {
+                    s_dst[i] = vd[k];
+                    s_src[i] = vs[k];
+                    s_size[i] = vz[k];
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const LiveAt<STAGE> la{lv, tile_base, (lds_u64 *)s_dst, (lds_u64 *)s_src, (lds_u64 *)s_size,
+                           (lds_u32 *)s_tb, s_lo, s_cnt};
+    const LiveLds ll{(lds_u64 *)s_dst, (lds_u64 *)s_src, (lds_u64 *)s_size, (lds_u32 *)s_tb,
+                     (uint32_t)s_lo};
+    const bool all = STAGE && s_lo == 0 && s_cnt == m;  // every live block staged
+    // first block of tile u among blocks [k0, k_hi] (k_lo <= k0), and its
+    // first tile index
+    const auto first_of = [&](uint64_t u, int64_t k0, uint64_t *tb_k) -> uint64_t {
+        if (staged) {
+            const int32_t r = last_le32(s_tb, (int32_t)(k0 - (int64_t)s_lo),
+                                        (int32_t)(k_hi - (int64_t)s_lo + 1), (uint32_t)u);
+            *tb_k = s_tb[r];
+            return s_lo + (uint64_t)r;
+        }
+        const int64_t k = last_le(tile_base, k0, k_hi + 1, u);
         *tb_k = tile_base[k];
         return (uint64_t)k;
     };
+    const auto start_of = [&](uint64_t k, uint64_t tb_k, uint64_t u) -> uint64_t {
+        return all ? tile_start_at(ll, k, tb_k, u, T) : tile_start_at(la, k, tb_k, u, T);
+    };
     uint64_t first = 0, t0 = 0, tb_k;
     if (t < te) {
-        first = first_of(t, &tb_k);
-        t0 = tile_start_at(lv, first, tb_k, t, T);
+        first = first_of(t, k_lo, &tb_k);
+        t0 = start_of(first, tb_k, t);
         s_t0[threadIdx.x] = t0;
     }
-    if (threadIdx.x == 255 && te < n_tiles) {  // the tile after the workgroup's
-        const uint64_t k = first_of(te, &tb_k);
-        s_t0[256] = tile_start_at(lv, k, tb_k, te, T);
+    if (threadIdx.x == 255 && te < n_tiles) {  // the tile after the workgroup's: its
+        // first block is at or after this lane's
+        const uint64_t k = first_of(te, (int64_t)first, &tb_k);
+        s_t0[256] = start_of(k, tb_k, te);
     }
     __syncthreads();
     if (t >= n_tiles) return;
     uint64_t bound = (t0 & ~(T - 1)) + T;
     if (t + 1 < n_tiles) bound = umin64(bound, s_t0[threadIdx.x + 1]);
-    tiles[t] = tile_record(lv, tile_base, m, t, t0, first, bound, T, ridx, w);
+    tiles[t] = all ? tile_record(ll, m, t, t0, first, bound, T, ridx, w)
+                   : tile_record(la, m, t, t0, first, bound, T, ridx, w);
     flags[t] = 0u;
 }
 
@@ -1083,8 +1191,15 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
     uint32_t *flags = reinterpret_cast<uint32_t *>(ws + L.flags);
     const uint64_t grid = (L.max_tiles + 255) / 256;
     if (grid) {
-        hipLaunchKernelGGL(k_tiles, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_base, hdr,
-                           L.max_tiles, ridx, b.rw, trec, flags);
+        // at most arena / T tiles cut at multiples of T, and one more per run
+        const uint32_t t_min = tiles.a < tiles.b ? tiles.a : tiles.b;
+        const uint64_t bound = arena_bytes / t_min + t.n;
+        if (bound <= kStageTileLimit)
+            hipLaunchKernelGGL(k_tiles<true>, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_base,
+                               hdr, L.max_tiles, ridx, b.rw, trec, flags);
+        else
+            hipLaunchKernelGGL(k_tiles<false>, dim3((uint32_t)grid), dim3(256), 0, s, lv,
+                               tile_base, hdr, L.max_tiles, ridx, b.rw, trec, flags);
         AC_TRY(hipGetLastError());
     }
     return hipSuccess;
