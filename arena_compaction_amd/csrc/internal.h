@@ -213,10 +213,13 @@ inline bool remap_rec32(uint64_t arena_bytes) { return arena_bytes < (1ull << 37
 
 // Remap index: the arena is cut into buckets of 2^w bytes, at most
 // remap_bucket_cap(n) of them, and ridx[b] counts the live blocks starting
-// below bucket b (entries 0 .. buckets).
+// below bucket b (entries 0 .. buckets).  At most 2^20 buckets (4 MiB of
+// index): on the 4 GiB heap of a million live blocks the remap took 254 us
+// with 2^18, 208 us with 2^20 and 242 us with 2^22 (whose index no longer
+// stays in cache and takes twice as long to build).
 inline uint64_t remap_bucket_cap(uint64_t n) {
     uint64_t c = 16;
-    while (c < 2 * n + 2 && c < (1ull << 18)) c <<= 1;
+    while (c < 2 * n + 2 && c < (1ull << 20)) c <<= 1;
     return c;
 }
 inline uint32_t remap_shift(uint64_t arena_bytes, uint64_t n) {

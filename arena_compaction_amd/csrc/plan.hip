@@ -438,13 +438,54 @@ __device__ inline uint64_t tiles_in_block(const LiveView &lv, uint64_t k, uint64
     return tiles_of(lv.dst[k], lv.size[k], start, T);
 }
 
+// The last index k with a[k] <= x in a[0, m), or -1, for x = x0 (into
+// out[0]) and x = x1 (into out[1]), a ascending: two searches side by
+// side, 128 lanes each, every round testing 128 evenly spaced entries of
+// the bracket at once (one memory round trip a round: three for a million
+// entries, where one lane's bisection takes twenty).  Workgroup-uniform; 256
+// lanes; barriers inside.
+template <typename T>
+__device__ inline void find_stretch(const T *a, int64_t m, uint64_t x0, uint64_t x1,
+                                    int64_t *out) {
+    __shared__ uint32_t s_cnt[4];
+    __shared__ int64_t s_br[2][2];
+    const uint32_t half = threadIdx.x >> 7, lane = threadIdx.x & 127, wave = threadIdx.x >> 6;
+    const uint64_t x = half ? x1 : x0;
+    if (lane == 0) {  // the bracket (lo, hi): a[lo] <= x < a[hi], a[-1] and a[m] beyond
+        s_br[half][0] = -1;
+        s_br[half][1] = m;
+    }
+    __syncthreads();
+    for (;;) {
+        const int64_t lo = s_br[half][0], hi = s_br[half][1];
+        const int64_t lo_o = s_br[half ^ 1][0], hi_o = s_br[half ^ 1][1];
+        if (hi - lo <= 1 && hi_o - lo_o <= 1) break;  // both done (uniform)
+        const int64_t span = hi - lo - 1;  // candidates lo + 1 .. hi - 1
+        const int64_t step = span > 0 ? (span + 127) / 128 : 1;
+        const int64_t idx = lo + 1 + (int64_t)lane * step;
+        const bool p = span > 0 && idx < hi && (uint64_t)a[idx] <= x;
+        const uint64_t bal = __ballot(p);
+        if ((threadIdx.x & 63) == 0) s_cnt[wave] = (uint32_t)__popcll(bal);
+        __syncthreads();
+        if (lane == 0 && span > 0) {  // the entries at or below x form a prefix
+            const int64_t c = (int64_t)(s_cnt[2 * half] + s_cnt[2 * half + 1]);
+            const int64_t nlo = c ? lo + 1 + (c - 1) * step : lo;
+            const int64_t nhi = lo + 1 + c * step;
+            s_br[half][0] = nlo;
+            s_br[half][1] = nhi < hi ? nhi : hi;
+        }
+        __syncthreads();
+    }
+    if (lane == 0) out[half] = s_br[half][0];
+}
+
 // The remap's bucket index: ridx[b] = number of live blocks whose old offset
 // is below b << w, for b in [0, nb]; one lane per entry, a binary search over
 // the packed old offsets (workgroup blk covers entries [256 blk, ...)).  The
-// workgroup's answers lie between those of its first and last bucket; when
-// that stretch of old offsets is short (always, in a table of at most
-// kIndexStage live blocks) it is staged in LDS with one coalesced load and
-// searched there.
+// workgroup's answers lie between those of its first and last bucket, found
+// by find_stretch; when that stretch of old offsets is short (always, in a
+// table of at most kIndexStage live blocks) it is staged in LDS with one
+// memory round trip and searched there.
 constexpr uint32_t kIndexStage = 2048;
 
 // First k in [lo, hi) with a[k] >= x (hi if none).
@@ -465,23 +506,42 @@ __device__ inline uint64_t first_ge(const uint64_t *a, uint64_t lo, uint64_t hi,
 __device__ void remap_index_part(const uint64_t *__restrict__ live_src, uint64_t m, uint32_t w,
                                  uint64_t nb, uint32_t *ridx, uint64_t blk) {
     __shared__ uint64_t s_src[kIndexStage];
-    __shared__ uint64_t s_r[2];
+    __shared__ int64_t s_r[2];
     const uint64_t b0 = blk * kScanThreads;
     if (b0 > nb) return;  // (the whole workgroup)
-    const uint64_t b1 = umin64(b0 + kScanThreads - 1, nb);
+    const uint64_t b1 = umin64(b0 + kScanThreads - 1, nb);  // >= 1: nb >= 1
     if (m <= kIndexStage) {
         if (threadIdx.x == 0) {
             s_r[0] = 0;
-            s_r[1] = m;
+            s_r[1] = (int64_t)m;
         }
-    } else if (threadIdx.x < 2) {
-        s_r[threadIdx.x] = first_ge(live_src, 0, m, (threadIdx.x ? b1 : b0) << w);
+    } else {
+        // blocks below x = (the last one at or below x - 1) + 1
+        find_stretch(live_src, (int64_t)m, b0 ? (b0 << w) - 1 : 0, (b1 << w) - 1, s_r);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            s_r[0] = b0 ? s_r[0] + 1 : 0;
+            s_r[1] = s_r[1] + 1;
+        }
     }
     __syncthreads();
-    const uint64_t r0 = s_r[0], r1 = s_r[1];
+    const uint64_t r0 = (uint64_t)s_r[0], r1 = (uint64_t)s_r[1];
     const bool staged = r1 - r0 <= kIndexStage;
-    if (staged)
-        for (uint64_t i = threadIdx.x; i < r1 - r0; i += kScanThreads) s_src[i] = live_src[r0 + i];
+    if (staged) {
+        // every load issued before the first is stored: one round trip
+        constexpr uint32_t kPer = kIndexStage / kScanThreads;
+        uint64_t v[kPer] = {};
+#pragma unroll
+        for (uint32_t k = 0; k < kPer; ++k) {
+            const uint64_t i = threadIdx.x + k * kScanThreads;
+            if (i < r1 - r0) v[k] = live_src[r0 + i];
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < kPer; ++k) {
+            const uint64_t i = threadIdx.x + k * kScanThreads;
+            if (i < r1 - r0) s_src[i] = v[k];
+        }
+    }
     __syncthreads();
     const uint64_t b = b0 + threadIdx.x;
     if (b > b1) return;
@@ -782,46 +842,6 @@ __device__ inline TileRec tile_record(const LA &lv, uint64_t m, uint64_t t, uint
     }
     return TileRec{t0, t1, lv.src(first) - lv.dst(first), (uint32_t)first, (uint32_t)last,
                    dep_lo, dep_hi, 0};
-}
-
-// The last index k with a[k] <= x in a[0, m), or -1, for x = x0 (into
-// out[0]) and x = x1 (into out[1]), a ascending: two searches side by
-// side, 128 lanes each, every round testing 128 evenly spaced entries of
-// the bracket at once (one memory round trip a round: three for a million
-// entries, where one lane's bisection takes twenty).  Workgroup-uniform; 256
-// lanes; barriers inside.
-__device__ inline void find_stretch(const uint32_t *a, int64_t m, uint64_t x0, uint64_t x1,
-                                    int64_t *out) {
-    __shared__ uint32_t s_cnt[4];
-    __shared__ int64_t s_br[2][2];
-    const uint32_t half = threadIdx.x >> 7, lane = threadIdx.x & 127, wave = threadIdx.x >> 6;
-    const uint64_t x = half ? x1 : x0;
-    if (lane == 0) {  // the bracket (lo, hi): a[lo] <= x < a[hi], a[-1] and a[m] beyond
-        s_br[half][0] = -1;
-        s_br[half][1] = m;
-    }
-    __syncthreads();
-    for (;;) {
-        const int64_t lo = s_br[half][0], hi = s_br[half][1];
-        const int64_t lo_o = s_br[half ^ 1][0], hi_o = s_br[half ^ 1][1];
-        if (hi - lo <= 1 && hi_o - lo_o <= 1) break;  // both done (uniform)
-        const int64_t span = hi - lo - 1;  // candidates lo + 1 .. hi - 1
-        const int64_t step = span > 0 ? (span + 127) / 128 : 1;
-        const int64_t idx = lo + 1 + (int64_t)lane * step;
-        const bool p = span > 0 && idx < hi && (uint64_t)a[idx] <= x;
-        const uint64_t bal = __ballot(p);
-        if ((threadIdx.x & 63) == 0) s_cnt[wave] = (uint32_t)__popcll(bal);
-        __syncthreads();
-        if (lane == 0 && span > 0) {  // the entries at or below x form a prefix
-            const int64_t c = (int64_t)(s_cnt[2 * half] + s_cnt[2 * half + 1]);
-            const int64_t nlo = c ? lo + 1 + (c - 1) * step : lo;
-            const int64_t nhi = lo + 1 + c * step;
-            s_br[half][0] = nlo;
-            s_br[half][1] = nhi < hi ? nhi : hi;
-        }
-        __syncthreads();
-    }
-    if (lane == 0) out[half] = s_br[half][0];
 }
 
 // Pass 4: one lane per tile, each writing its record (tile_record).

@@ -18,7 +18,7 @@
 // ascending), so free entries never cost a probe; a pinned block maps to
 // itself.  Random handles make the search bound by L2 requests (each probe
 // of each lane is its own cache line), so the plan builds an index -- the
-// arena cut into at most 2^18 power-of-two buckets, each pointing at the
+// arena cut into at most 2^20 power-of-two buckets, each pointing at the
 // first live block starting in it -- and each live block also has a search
 // key (its old offset inside its bucket) and a record (old end, shift).  In
 // arenas below 2^37 bytes with buckets of at most 2^32 bytes (the usual
