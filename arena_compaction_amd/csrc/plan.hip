@@ -34,10 +34,10 @@
 //      start, counted for both candidate tile sizes; workgroup 0 writes the
 //      table's totals;
 //   3. each workgroup picks the tile size from the totals, the same way, and
-//      gives each of its live blocks its first tile index; workgroup 0
-//      finishes the header (statistics, tile count and size, the mover's
-//      fields); further workgroups build the remap's bucket index over old
-//      offsets (it also narrows the tiles' source searches);
+//      gives each of its live blocks its first tile index; one more
+//      workgroup finishes the header (statistics, tile count and size, the
+//      mover's fields); further workgroups build the remap's bucket index
+//      over old offsets (it also narrows the tiles' source searches);
 //   4. one lane per tile: its start, range, blocks and dependencies.
 // The whole sequence is queued at once; the host reads the header back only
 // at the end.  A statistics pass alone is one launch of its own
@@ -171,54 +171,28 @@ __device__ inline uint64_t whole_of(uint64_t a, uint64_t s, uint64_t T) {
     return hi > lo ? hi - lo : 0;
 }
 
-// The statistics of all workgroups, reduced by one workgroup (the tail hole
-// added) into the header; with `plan`, the plan's mover fields are reset too.
-// x: up to four sums more (e.g. whole-tile counts), reduced alongside.
-// max_end: the highest live end (the header's max_live_end).
-__device__ void stats_finish(const StatPart *spart, uint64_t nb, uint64_t arena_bytes,
-                             uint64_t max_end, WsHeader *hdr, bool plan, uint64_t fit_need,
-                             const uint64_t *xsrc = nullptr, uint64_t *xsum = nullptr) {
-    __shared__ uint64_t sh[kStatSlots<kScanThreads>];
-    StatPart a{0, 0, 0, 0, kNone, kNone, kNone, 0};
-    uint64_t x[4] = {0, 0, 0, 0};
-    for (uint64_t j = threadIdx.x; j < nb; j += kScanThreads) {
-        const StatPart q = spart[j];
-        a.small_moved += q.small_moved;
-        a.min_fit = umin64(a.min_fit, q.min_fit);
-        a.max_gap = umax64(a.max_gap, q.max_gap);
-        a.gaps += q.gaps;
-        a.moved_blocks += q.moved_blocks;
-        a.moved_bytes += q.moved_bytes;
-        a.min_moved_dst = umin64(a.min_moved_dst, q.min_moved_dst);
-        a.min_size = umin64(a.min_size, q.min_size);
-        if (xsrc) x[0] += xsrc[j];
-    }
-    block_reduce_stats<kScanThreads>(a, x, sh);
-    if (xsum) *xsum = x[0];
-    const uint64_t max_gap = a.max_gap, gaps = a.gaps, moved = a.moved_blocks,
-                   moved_bytes = a.moved_bytes, min_dst = a.min_moved_dst, min_size = a.min_size,
-                   small_moved = a.small_moved;
-    uint64_t min_fit = a.min_fit;
-    if (threadIdx.x == 0) {
-        const uint64_t tail = arena_bytes - max_end;
-        // holes below live blocks come first in address order; the tail last
-        if (min_fit == kNone && tail && tail >= fit_need) min_fit = max_end;
-        hdr->fit_offset = min_fit;
-        hdr->largest_hole = umax64(max_gap, tail);
-        hdr->hole_count = gaps + (tail ? 1 : 0);
-        hdr->moved_blocks = moved;
-        hdr->moved_bytes = moved_bytes;
-        hdr->small_moved = small_moved;
-        hdr->min_live_size = min_size;
-        hdr->move_begin = min_dst;
-        if (plan) {
-            hdr->ticket = 0;
-            hdr->status = 0;
-            hdr->late_tiles = 0;
-            hdr->waited_tiles = 0;
-            hdr->polls = 0;
-        }
-    }
+// The header's statistics from the reduced per-workgroup statistics q (the
+// tail hole added), and the plan's mover fields reset.  max_end: the highest
+// live end (the header's max_live_end).  One lane.
+__device__ void stats_header(const StatPart &q, uint64_t arena_bytes, uint64_t max_end,
+                             uint64_t fit_need, WsHeader *hdr) {
+    const uint64_t tail = arena_bytes - max_end;
+    uint64_t min_fit = q.min_fit;
+    // holes below live blocks come first in address order; the tail last
+    if (min_fit == kNone && tail && tail >= fit_need) min_fit = max_end;
+    hdr->fit_offset = min_fit;
+    hdr->largest_hole = umax64(q.max_gap, tail);
+    hdr->hole_count = q.gaps + (tail ? 1 : 0);
+    hdr->moved_blocks = q.moved_blocks;
+    hdr->moved_bytes = q.moved_bytes;
+    hdr->small_moved = q.small_moved;
+    hdr->min_live_size = q.min_size;
+    hdr->move_begin = q.min_moved_dst;
+    hdr->ticket = 0;
+    hdr->status = 0;
+    hdr->late_tiles = 0;
+    hdr->waited_tiles = 0;
+    hdr->polls = 0;
 }
 
 // What a workgroup's entries add up to in the down-sweep: hole and move
@@ -429,15 +403,6 @@ __global__ __launch_bounds__(kScanThreads) void k_stats_one(TableView t, uint64_
 // inside each tile-size window: one starts at the run's first byte, and one at
 // every multiple of T inside it.
 
-__device__ inline bool moved_at(const LiveView &lv, uint64_t k) { return lv.src[k] != lv.dst[k]; }
-
-// Tiles starting inside live block k (0 if k did not move).
-__device__ inline uint64_t tiles_in_block(const LiveView &lv, uint64_t k, uint64_t T) {
-    if (!moved_at(lv, k)) return 0;
-    const bool start = (k == 0) || !moved_at(lv, k - 1);
-    return tiles_of(lv.dst[k], lv.size[k], start, T);
-}
-
 // The last index k with a[k] <= x in a[0, m), or -1, for x = x0 (into
 // out[0]) and x = x1 (into out[1]), a ascending: two searches side by
 // side, 128 lanes each, every round testing 128 evenly spaced entries of
@@ -573,9 +538,21 @@ struct BaseArgs {
 // or when the smaller's tiles would not fit the workspace and the larger's
 // do), then each of its live blocks' first tile index -- a block with no
 // tile gets the index of the next tile that starts, so tile t belongs to the
-// last block whose first index is <= t.  Workgroup 0 also finishes the
-// header: statistics, tile count and size, the mover's fields.  The
-// workgroups after them build the remap's bucket index.
+// last block whose first index is <= t.  Workgroup nb takes the same
+// decision and finishes the header beside them: statistics, tile count and
+// size, the mover's fields.  The workgroups after it build the remap's
+// bucket index.
+// The tile size, decided the same way by every workgroup from the same
+// totals: moved bytes, those shifting by less than kAutoSmallShift, and the
+// tiles each candidate cuts.  True: the larger candidate.
+__device__ inline bool pick_larger(TileChoice tc, uint64_t moved, uint64_t small, uint64_t na,
+                                   uint64_t nb, uint64_t max_tiles) {
+    bool pick_b = tc.a != tc.b && small * 2 > moved && moved >= kAutoMinMoved;
+    if (tc.a != tc.b && (pick_b ? nb : na) > max_tiles && (pick_b ? na : nb) <= max_tiles)
+        pick_b = !pick_b;
+    return pick_b;
+}
+
 __global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
     __shared__ uint64_t sh[kScanThreads / 64];
     __shared__ uint64_t s_red[kStatSlots<kScanThreads>];
@@ -586,10 +563,45 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
         *a.arrive_post = 0;  // for a one-launch statistics pass after this plan
     }
     const uint64_t g = blockIdx.x;
-    if (g >= a.nb) {
+    if (g > a.nb) {
         const uint64_t m = hdr->live_blocks;
         if (plan_dead(hdr)) return;
-        remap_index_part(a.lv.src, m, a.rw, a.rnb, a.ridx, g - a.nb);
+        remap_index_part(a.lv.src, m, a.rw, a.rnb, a.ridx, g - a.nb - 1);
+        return;
+    }
+    if (g == a.nb) {
+        // workgroup nb finishes the header beside the others: every
+        // per-workgroup statistic and tile count reduced at once (one
+        // memory round trip, one reduction), the same tile decision, the
+        // header written
+        StatPart q{0, 0, 0, 0, kNone, kNone, kNone, 0};
+        uint64_t x[4] = {0, 0, 0, 0};  // tiles and whole tiles, both candidates
+        for (uint64_t j = threadIdx.x; j < a.nb; j += kScanThreads) {
+            const StatPart p = a.spart[j];
+            q.max_gap = umax64(q.max_gap, p.max_gap);
+            q.gaps += p.gaps;
+            q.moved_blocks += p.moved_blocks;
+            q.moved_bytes += p.moved_bytes;
+            q.min_moved_dst = umin64(q.min_moved_dst, p.min_moved_dst);
+            q.min_size = umin64(q.min_size, p.min_size);
+            q.min_fit = umin64(q.min_fit, p.min_fit);
+            q.small_moved += p.small_moved;
+            x[0] += a.tpart[j];
+            x[1] += a.tpart[kMaxScanParts + j];
+            x[2] += a.twhole[j];
+            x[3] += a.twhole[kMaxScanParts + j];
+        }
+        const uint64_t max_end = hdr->max_live_end;
+        if (plan_dead(hdr)) return;
+        block_reduce_stats<kScanThreads>(q, x, s_red);
+        const bool pick_b = pick_larger(a.tiles, q.moved_bytes, q.small_moved, x[0], x[1],
+                                        a.max_tiles);
+        if (threadIdx.x == 0) {
+            stats_header(q, a.arena_bytes, max_end, kNone, hdr);
+            hdr->n_tiles = pick_b ? x[1] : x[0];
+            hdr->whole_tiles = pick_b ? x[3] : x[2];
+            hdr->tile_bytes = pick_b ? a.tiles.b : a.tiles.a;
+        }
         return;
     }
     // every load that does not depend on another is issued before the
@@ -609,7 +621,6 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
         small += a.spart[j].small_moved;
     }
     const uint64_t k_begin = a.lbase[g], k_end = a.lbase[g + 1];
-    const uint64_t max_end = hdr->max_live_end;
     if (plan_dead(hdr)) return;
     {
         StatPart q{0, 0, 0, 0, kNone, kNone, kNone, 0};
@@ -621,31 +632,38 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
     uint64_t pa, na, pb, nbt;
     sums_prefix(ta, g, sh, &s_before, pa, na);
     sums_prefix(tb, g, sh, &s_before, pb, nbt);
-    const TileChoice tc = a.tiles;
-    bool pick_b = tc.a != tc.b && small * 2 > moved && moved >= kAutoMinMoved;
-    if (tc.a != tc.b && (pick_b ? nbt : na) > a.max_tiles && (pick_b ? na : nbt) <= a.max_tiles)
-        pick_b = !pick_b;
-    const uint64_t T = pick_b ? tc.b : tc.a;
+    const bool pick_b = pick_larger(a.tiles, moved, small, na, nbt, a.max_tiles);
+    const uint64_t T = pick_b ? a.tiles.b : a.tiles.a;
     const uint64_t n_tiles = pick_b ? nbt : na;
-    if (g == 0) {
-        uint64_t whole = 0;
-        stats_finish(a.spart, a.nb, a.arena_bytes, max_end, hdr, true, kNone,
-                     a.twhole + (pick_b ? kMaxScanParts : 0), &whole);
-        if (threadIdx.x == 0) {
-            hdr->n_tiles = n_tiles;
-            hdr->whole_tiles = whole;
-            hdr->tile_bytes = T;
-        }
-    }
     if (n_tiles > a.max_tiles) return;  // the plan fails (the header says so)
     uint64_t carry = pick_b ? pb : pa;
     for (uint64_t s0 = k_begin; s0 < k_end; s0 += kScanTile) {
         const uint64_t k0 = s0 + (uint64_t)threadIdx.x * kScanItems;
+        // the lane's blocks and the one before them (whether it moved says
+        // whether a run starts), every load issued before the first is used
+        uint64_t dd[kScanItems + 1], ss[kScanItems + 1], zz[kScanItems];
+#pragma unroll
+        for (uint32_t j = 0; j <= kScanItems; ++j) {
+            const uint64_t k = k0 + j - 1;  // j = 0: the block before (none before block 0)
+            dd[j] = 0;
+            ss[j] = 0;
+            if (k0 + j >= 1 && k < k_end) {
+                dd[j] = a.lv.dst[k];
+                ss[j] = a.lv.src[k];
+            }
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < kScanItems; ++j) zz[j] = (k0 + j < k_end) ? a.lv.size[k0 + j] : 0;
         uint64_t c[kScanItems];
         uint64_t sum = 0;
 #pragma unroll
         for (uint32_t j = 0; j < kScanItems; ++j) {
-            c[j] = (k0 + j < k_end) ? tiles_in_block(a.lv, k0 + j, T) : 0;
+            // tiles starting inside block k0 + j (0 if it did not move)
+            c[j] = 0;
+            if (k0 + j < k_end && ss[j + 1] != dd[j + 1]) {
+                const bool start = ss[j] == dd[j];  // the block before stayed (or is none)
+                c[j] = tiles_of(dd[j + 1], zz[j], start, T);
+            }
             sum += c[j];
         }
         uint64_t total;
@@ -1202,7 +1220,7 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
     b.clear = clear;
     b.arrive_post = &reinterpret_cast<WsHeader *>(ws + L.post)->arrive;
     const uint64_t rblocks = (b.rnb + 1 + kScanThreads - 1) / kScanThreads;
-    hipLaunchKernelGGL(k_plan_bases, dim3((uint32_t)(d.ngroups + rblocks)), dim3(kScanThreads), 0,
+    hipLaunchKernelGGL(k_plan_bases, dim3((uint32_t)(d.ngroups + 1 + rblocks)), dim3(kScanThreads), 0,
                        s, b);
     AC_TRY(hipGetLastError());
     // pass 4: the tile records, a grid for the whole capacity (each lane
