@@ -491,6 +491,28 @@ def test_remap_at_bucket_boundaries(ac):
         assert np.array_equal(r.remapped, want) and r.n_invalid == bad
 
 
+def test_remap_index_over_a_dense_cluster(ac):
+    """Ten thousand 32-byte live blocks (each above a 32-byte hole) packed
+    into the first MiB of a 1 GiB arena, and a few large blocks far above:
+    the workgroup that builds the index buckets over the cluster meets more
+    live blocks than it stages in LDS, so its lanes search global memory.
+    Every handle -- one inside each small block, the large blocks' edges,
+    the holes -- matches the oracle, and the arena comes out bit-exact."""
+    MiB = 1 << 20
+    n_small = 10_000
+    blocks = [(32 + 64 * i, 32) for i in range(n_small)]
+    blocks += [(256 * MiB, 64 * MiB), (512 * MiB, 128 * MiB), (768 * MiB, 32 * MiB)]
+    live = [1] * n_small + [1, 0, 1]
+    hs = [32 + 64 * i + 8 * (i % 4) for i in range(n_small)]
+    hs += [16 + 64 * i for i in range(0, n_small, 97)]  # holes
+    for o, sz in blocks[n_small:]:
+        hs += [o - 32, o, o + 32, o + sz - 32, o + sz - 1, o + sz]
+    heap = W.table_from_lists(1 << 30, blocks, live, hs, name="dense cluster in 1 GiB")
+    r = _full_check(heap)
+    want, bad = oracle.remap(heap.offset, heap.size, heap.live, heap.handles)
+    assert np.array_equal(r.remapped, want) and r.n_invalid == bad
+
+
 def test_scan_workgroups_taking_several_steps(ac):
     """Above 1,024 x 1,024 entries each scan workgroup takes several steps of
     1,024 entries with a running carry: 3,000,000 entries of 32-96 bytes with

@@ -155,6 +155,25 @@ def test_schedule_random_tiny_heaps(ac):
         check_schedule(ac, heap, int(rng.choice([256, 512, 1024, 4096])))
 
 
+@pytest.mark.parametrize("T", [4096, 65536])
+@pytest.mark.parametrize("m", [2047, 2048, 2049, 2050, 4100])
+def test_schedule_at_the_staging_edges(ac, m, T):
+    """About 2,048 live blocks, the most a tile-record workgroup stages in
+    LDS: every block staged (the searches read LDS alone), one or two more
+    (the stretch staged, the blocks past it read from global memory), and
+    twice as many.  Blocks of 1 KiB each above a 32-byte hole, so every
+    block moves and all form one run: with 4 KiB tiles the tile count falls
+    on a multiple of 256 (a workgroup's tiles) at 2,048 blocks and just past
+    one above it; with 64 KiB tiles one workgroup's tiles start in more
+    blocks than it stages from 2,049 on."""
+    s, h = 1024, 32
+    blocks = [(h + i * (s + h), s) for i in range(m)]
+    S = m * (s + h) + 4096
+    heap = W.table_from_lists(S, blocks, [1] * m, name=f"staging edge m={m}")
+    plan = check_schedule(ac, heap, T)
+    assert plan.n_tiles == -(-m * s // T)  # one run packed from 0, cut at every multiple of T
+
+
 @pytest.mark.parametrize("k", ["training-80g", "training-80g-pinned"])
 def test_schedule_targeted(ac, k):
     heap = W.workload(k, small=True)
