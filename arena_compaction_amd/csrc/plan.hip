@@ -117,7 +117,7 @@ __device__ void parts_prefix(const ScanPart *part, uint64_t nb, uint64_t g, Agg 
     const Agg ex = block_excl<kScanThreads>(loc, total, sh);
     if (g >= j0 && g < j0 + kPer) *s_before = combine(ex, upto);
     bad = block_reduce<kScanThreads>(b, shr, OpMin());  // (its barriers publish s_before)
-    before = *s_before;
+    before = wave_uniform(*s_before);
 }
 
 // The same for sums of u64 (tile counts): the sum below g and the total.
@@ -137,7 +137,7 @@ __device__ void sums_prefix(const uint64_t (&v)[kPartsPer], uint64_t g, uint64_t
     const uint64_t ex = block_excl_sum<kScanThreads>(loc, total, sh);
     if (g >= j0 && g < j0 + kPer) *s_before = ex + upto;
     __syncthreads();
-    before = *s_before;
+    before = wave_uniform(*s_before);
     __syncthreads();
 }
 

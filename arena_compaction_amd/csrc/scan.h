@@ -57,7 +57,51 @@ __device__ inline Agg element(uint64_t o, uint64_t s, uint32_t l, uint32_t p, ui
     return e;
 }
 
-__device__ inline Agg combine_op(const Agg &a, const Agg &b) { return combine(a, b); }
+// One step of a wave scan over Agg: combine() with the value the DPP
+// control brings from another lane before this lane's, a field at a time.
+// Each field of the combined state depends only on that field of both
+// sides (v also on this lane's r), so only one field's cross-lane
+// temporaries are live at once, which keeps the side job's 1,024-lane mover
+// under its register cap.  A lane with no source takes the identity (zero).
+template <int CTRL, int ROW_MASK>
+__device__ inline void agg_step(Agg &x) {
+    const uint32_t ar = dpp_move<CTRL, ROW_MASK>(x.r);
+    const uint64_t av = dpp_move<CTRL, ROW_MASK>(x.v);
+    x.v = x.r ? x.v : av + x.v;
+    x.r |= ar;
+    x.mx = umax64(dpp_move<CTRL, ROW_MASK>(x.mx), x.mx);
+    x.cnt += dpp_move<CTRL, ROW_MASK>(x.cnt);
+    x.lsum += dpp_move<CTRL, ROW_MASK>(x.lsum);
+    x.pcnt += dpp_move<CTRL, ROW_MASK>(x.pcnt);
+}
+
+// wave_incl_scan (wave.h) over Agg under combine(), by agg_step.
+template <int SPAN = 64>
+__device__ inline Agg agg_incl_scan(Agg x) {
+    static_assert(SPAN == 64 || (SPAN >= 1 && SPAN <= 16), "a whole wave or one row");
+    if constexpr (SPAN > 1) agg_step<kDppRowShr | 1, 0xf>(x);
+    if constexpr (SPAN > 2) agg_step<kDppRowShr | 2, 0xf>(x);
+    if constexpr (SPAN > 4) agg_step<kDppRowShr | 4, 0xf>(x);
+    if constexpr (SPAN > 8) agg_step<kDppRowShr | 8, 0xf>(x);
+    if constexpr (SPAN > 16) {
+        agg_step<kDppRowBcast15, 0xa>(x);  // rows 1, 3 after rows 0, 2
+        agg_step<kDppRowBcast31, 0xc>(x);  // rows 2, 3 after rows 0-1
+    }
+    return x;
+}
+
+// The lane before's value (the identity in lane 0), a field at a time.
+__device__ inline Agg agg_shift_up(const Agg &x) {
+    Agg y;
+    y.v = wave_shift_up(x.v);
+    y.mx = wave_shift_up(x.mx);
+    y.cnt = wave_shift_up(x.cnt);
+    y.lsum = wave_shift_up(x.lsum);
+    y.pcnt = wave_shift_up(x.pcnt);
+    y.r = wave_shift_up(x.r);
+    y.pad = 0;
+    return y;
+}
 
 // LDS slots the two cross-wave helpers below need for NT lanes.
 template <int NT>
@@ -75,19 +119,19 @@ __device__ inline Agg block_excl(const Agg &x, Agg &total, Agg *sh) {
     static_assert(NW >= 1 && NW <= 16 && (NW & (NW - 1)) == 0, "whole waves, a power of two");
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const Agg inc = wave_incl_scan(x, combine_op);
-    const Agg ex = wave_shift_up(inc);
+    const Agg inc = agg_incl_scan(x);
+    const Agg ex = agg_shift_up(inc);
     if (lane == 63) sh[w] = inc;
     __syncthreads();
     if (w == 0) {
-        const Agg t = wave_incl_scan<NW>(lane < NW ? sh[lane] : agg_zero(), combine_op);
-        const Agg te = wave_shift_up(t);
+        const Agg t = agg_incl_scan<NW>(lane < NW ? sh[lane] : agg_zero());
+        const Agg te = agg_shift_up(t);
         if (lane < NW) sh[NW + lane] = te;
         if (lane == NW - 1) sh[2 * NW] = t;
     }
     __syncthreads();
-    const Agg pre = sh[NW + w];
-    total = sh[2 * NW];
+    const Agg pre = wave_uniform(sh[NW + w]);  // the wave's prefix
+    total = wave_uniform(sh[2 * NW]);
     __syncthreads();
     return combine(pre, ex);
 }
@@ -126,7 +170,7 @@ __device__ inline uint64_t block_reduce(uint64_t v, uint64_t *sh, Op op) {
 #pragma unroll
     for (int k = 1; k < NW; ++k) r = op(r, sh[k]);
     __syncthreads();
-    return r;
+    return wave_uniform(r);
 }
 
 struct OpAdd { __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return a + b; } };
@@ -138,20 +182,6 @@ struct StatRow {
     StatPart q;
     uint64_t x[4];
 };
-__device__ inline StatRow stat_op(const StatRow &a, const StatRow &b) {
-    StatRow c;
-    c.q.max_gap = umax64(a.q.max_gap, b.q.max_gap);
-    c.q.gaps = a.q.gaps + b.q.gaps;
-    c.q.moved_blocks = a.q.moved_blocks + b.q.moved_blocks;
-    c.q.moved_bytes = a.q.moved_bytes + b.q.moved_bytes;
-    c.q.min_moved_dst = umin64(a.q.min_moved_dst, b.q.min_moved_dst);
-    c.q.min_size = umin64(a.q.min_size, b.q.min_size);
-    c.q.min_fit = umin64(a.q.min_fit, b.q.min_fit);
-    c.q.small_moved = a.q.small_moved + b.q.small_moved;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) c.x[k] = a.x[k] + b.x[k];
-    return c;
-}
 __device__ inline void stat_store(uint64_t *o, const StatRow &r) {
     o[0] = r.q.max_gap; o[1] = r.q.gaps; o[2] = r.q.moved_blocks; o[3] = r.q.moved_bytes;
     o[4] = r.q.min_moved_dst; o[5] = r.q.min_size; o[6] = r.q.min_fit; o[7] = r.q.small_moved;
@@ -160,6 +190,26 @@ __device__ inline void stat_store(uint64_t *o, const StatRow &r) {
 __device__ inline StatRow stat_load(const uint64_t *o) {
     return StatRow{StatPart{o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]},
                    {o[8], o[9], o[10], o[11]}};
+}
+
+// The row reduced over the first SPAN lanes of the wave (wave_reduce's
+// SPAN), one field at a time: a field's cross-lane temporaries are live
+// only while it is reduced, which keeps the side job's 1,024-lane mover
+// under its register cap.
+template <int SPAN = 64>
+__device__ inline StatRow wave_reduce_row(const StatRow &r) {
+    StatRow o;
+    o.q.max_gap = wave_reduce<SPAN>(r.q.max_gap, umax64);
+    o.q.gaps = wave_reduce<SPAN>(r.q.gaps, add_op);
+    o.q.moved_blocks = wave_reduce<SPAN>(r.q.moved_blocks, add_op);
+    o.q.moved_bytes = wave_reduce<SPAN>(r.q.moved_bytes, add_op);
+    o.q.min_moved_dst = wave_reduce<SPAN>(r.q.min_moved_dst, umin64);
+    o.q.min_size = wave_reduce<SPAN>(r.q.min_size, umin64);
+    o.q.min_fit = wave_reduce<SPAN>(r.q.min_fit, umin64);
+    o.q.small_moved = wave_reduce<SPAN>(r.q.small_moved, add_op);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o.x[k] = wave_reduce<SPAN>(r.x[k], add_op);
+    return o;
 }
 
 // Workgroup reduction of the statistics and up to four extra sums: each
@@ -173,15 +223,15 @@ __device__ inline void block_reduce_stats(StatPart &q, uint64_t (&x)[4], uint64_
     constexpr int F = 12;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const StatRow r = wave_reduce(StatRow{q, {x[0], x[1], x[2], x[3]}}, stat_op);
+    const StatRow r = wave_reduce_row(StatRow{q, {x[0], x[1], x[2], x[3]}});
     if (lane == 0) stat_store(sh + F * w, r);
     __syncthreads();
     if (w == 0) {
-        const StatRow t = wave_reduce<NW>(stat_load(sh + F * (lane < NW ? lane : 0)), stat_op);
+        const StatRow t = wave_reduce_row<NW>(stat_load(sh + F * (lane < NW ? lane : 0)));
         if (lane == 0) stat_store(sh + F * NW, t);
     }
     __syncthreads();
-    const StatRow t = stat_load(sh + F * NW);
+    const StatRow t = wave_uniform(stat_load(sh + F * NW));
     q = t.q;
 #pragma unroll
     for (int k = 0; k < 4; ++k) x[k] = t.x[k];

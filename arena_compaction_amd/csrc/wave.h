@@ -58,6 +58,22 @@ __device__ inline T read_lane(const T &x) {
     return y;
 }
 
+// x, the same in every active lane of the wave (a value read from LDS that
+// every lane read at one address, say), in scalar registers: the compiler
+// cannot see that it is uniform, and would keep one copy a lane.
+template <typename T>
+__device__ inline T wave_uniform(const T &x) {
+    static_assert(sizeof(T) % 4 == 0, "whole 32-bit words");
+    constexpr int W = sizeof(T) / 4;
+    int w[W];
+    __builtin_memcpy(w, &x, sizeof(T));
+#pragma unroll
+    for (int k = 0; k < W; ++k) w[k] = __builtin_amdgcn_readfirstlane(w[k]);
+    T y;
+    __builtin_memcpy(&y, w, sizeof(T));
+    return y;
+}
+
 // Inclusive scan in lane order: lane i gets op(x_0, ..., x_i).  op(a, b)
 // combines a before b, is associative, and has the all-zero value as its
 // identity.  SPAN: lanes that hold values (64, or at most 16; lanes past it
