@@ -194,11 +194,13 @@ def strerror(code: int) -> str:
 
 
 def _ptr(t: Optional[torch.Tensor]):
+    """The device address of t (an int: every pointer argument and field is
+    declared c_void_p, which takes one as it is)."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
         raise ValueError("device arguments must be contiguous GPU tensors")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
 def _need(t: Optional[torch.Tensor], dtype: torch.dtype, n: int, what: str) -> None:
