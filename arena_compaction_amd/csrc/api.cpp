@@ -262,8 +262,9 @@ int plan_queue(const defrag_table *table, uint64_t arena_bytes, uint64_t request
     c->dev = current_device();
     if (c->dev < 0) return DEFRAG_EHIP;
     c->tu = tu;
-    c->tiles = tu.tile_bytes ? TileChoice{tu.tile_bytes, tu.tile_bytes}
-                             : TileChoice{kAutoTileSmall, kAutoTileLarge};
+    c->tiles = tu.tile_bytes ? TileChoice{tu.tile_bytes, tu.tile_bytes, 0u}
+                             : TileChoice{kAutoTileSmall, kAutoTileLarge,
+                                          auto_larger_always(arena_bytes, table->n) ? 1u : 0u};
     c->tuned = tuning != nullptr;
     uint8_t *ws = static_cast<uint8_t *>(ws_dev);
     c->epoch = g_epoch.fetch_add(0x9E3779B97F4A7C15ull) ^ reinterpret_cast<uintptr_t>(ws);
@@ -607,8 +608,10 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     // with the tile size left to the plan, a mover for each candidate: the
     // one whose size the plan did not choose leaves at once.  In an arena
     // of at most kAutoMinMoved bytes fewer bytes than that move (a moved
-    // block has a hole below it), so the plan keeps the smaller size unless
-    // its tiles overflow the workspace, which the bound rules out here.
+    // block has a hole below it), so the plan takes the larger size if the
+    // arena's blocks are large (auto_larger_always) and else keeps the
+    // smaller, unless its tiles overflow the workspace, which the bound
+    // rules out here (the larger cuts fewer): one mover, of that size.
     MoveArgs mb = m;
     mb.tile_bytes = c.tiles.b;
     mb.max_blocks = c.tiles.b / 32 + 2;
@@ -631,9 +634,11 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
                             after_host != nullptr, gate, c.L.max_tiles);
     sj.any_tile = one_mover ? 1u : 0u;  // the one launch runs it
     const SideArgs *side = side_work ? &sj : nullptr;
+    const MoveArgs &only = c.tiles.small_arena ? mb : m;
     const bool ok =
-        launch_move_device_sized(m, c.tu.nontemporal, side, stream) == hipSuccess &&
-        (one_mover || launch_move_device_sized(mb, c.tu.nontemporal, side, stream) == hipSuccess);
+        one_mover ? launch_move_device_sized(only, c.tu.nontemporal, side, stream) == hipSuccess
+                  : launch_move_device_sized(m, c.tu.nontemporal, side, stream) == hipSuccess &&
+                        launch_move_device_sized(mb, c.tu.nontemporal, side, stream) == hipSuccess;
     if (!ok) {
         // no kernel of this call still writes the caller's buffers once it returns
         (void)hipStreamSynchronize(stream);

@@ -154,10 +154,13 @@ typedef struct defrag_tuning {
                                  and at least 64 MiB move (a tile then often
                                  depends on one still being read; 128 KiB
                                  tiles are moved two per workgroup in flight,
-                                 which hides that wait), else 65536 -- and
-                                 the other one if the first's tiles do not fit
-                                 the workspace.  plan_host->tuning.tile_bytes
-                                 says which.                                 */
+                                 which hides that wait), or whenever the
+                                 arena is at most 64 MiB and its entries
+                                 average at least 8 KiB of it (a step bound
+                                 by latency, where half as many tiles wait
+                                 less), else 65536 -- and the other one if
+                                 the first's tiles do not fit the workspace.
+                                 plan_host->tuning.tile_bytes says which.    */
     uint32_t wg_per_cu;       /* mover workgroups per compute unit; 0 means as
                                  many as the kernel's resources allow         */
     uint32_t nontemporal;     /* streaming hints: 0 none, 1 loads and stores,
