@@ -101,6 +101,32 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_partials(TableView t, uin
 __device__ void parts_prefix(const ScanPart *part, uint64_t nb, uint64_t g, Agg *sh,
                              uint64_t *shr, Agg *s_before, Agg &before, Agg &total,
                              uint64_t &bad) {
+    if (nb <= 64) {
+        // few aggregates: the first wave scans them, one a lane, and hands
+        // out the prefix, the total and the first bad key through LDS (two
+        // barriers where the general path below takes five)
+        if (threadIdx.x < 64) {
+            const uint32_t j = threadIdx.x;
+            Agg x = agg_zero();
+            uint64_t b = kNone;
+            if (j < nb) {
+                x = part[j].a;
+                b = part[j].bad_key;
+            }
+            const Agg inc = agg_incl_scan(x);
+            const Agg ex = agg_shift_up(inc);
+            b = wave_reduce(b, umin64);
+            if (j == g) *s_before = ex;
+            if (j == 63) sh[0] = inc;  // lanes past nb add the identity: the total
+            if (j == 0) shr[0] = b;
+        }
+        __syncthreads();
+        before = wave_uniform(*s_before);
+        total = wave_uniform(sh[0]);
+        bad = wave_uniform(shr[0]);
+        __syncthreads();  // sh and shr are the caller's next scan's
+        return;
+    }
     constexpr uint32_t kPer = kMaxScanParts / kScanThreads;
     const uint64_t j0 = (uint64_t)threadIdx.x * kPer;
     Agg loc = agg_zero(), upto = agg_zero();
@@ -605,34 +631,72 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
         }
         return;
     }
-    // every load that does not depend on another is issued before the
-    // first is used (the header's outcome included): one memory round trip
-    // where there were four
-    const uint64_t j0 = (uint64_t)threadIdx.x * kPartsPer;
-    uint64_t ta[kPartsPer], tb[kPartsPer];
+    uint64_t moved = 0, small = 0, pa, na, pb, nbt;
+    uint64_t k_begin, k_end;
+    if (a.nb <= 64) {
+        // few workgroups before: the first wave takes one's counts a lane --
+        // tiles for both candidates (their sums below g and totals), moved
+        // and short-shift bytes -- and hands them out through LDS
+        __shared__ uint64_t s_few[6];
+        if (threadIdx.x < 64) {
+            const uint32_t j = threadIdx.x;
+            const bool in = j < a.nb;
+            const uint64_t ta = in ? a.tpart[j] : 0, tb = in ? a.tpart[kMaxScanParts + j] : 0;
+            const uint64_t mv = in ? a.spart[j].moved_bytes : 0;
+            const uint64_t sm = in ? a.spart[j].small_moved : 0;
+            const uint64_t ia = wave_incl_scan(ta, add_op), ib = wave_incl_scan(tb, add_op);
+            const uint64_t ea = wave_shift_up(ia), eb = wave_shift_up(ib);
+            const uint64_t m_all = wave_reduce(mv, add_op), s_all = wave_reduce(sm, add_op);
+            if (j == g) {
+                s_few[0] = ea;
+                s_few[1] = eb;
+            }
+            if (j == 63) {  // lanes past nb add zero: the totals
+                s_few[2] = ia;
+                s_few[3] = ib;
+                s_few[4] = m_all;
+                s_few[5] = s_all;
+            }
+        }
+        k_begin = a.lbase[g];
+        k_end = a.lbase[g + 1];
+        if (plan_dead(hdr)) return;
+        __syncthreads();
+        pa = wave_uniform(s_few[0]);
+        pb = wave_uniform(s_few[1]);
+        na = wave_uniform(s_few[2]);
+        nbt = wave_uniform(s_few[3]);
+        moved = wave_uniform(s_few[4]);
+        small = wave_uniform(s_few[5]);
+    } else {
+        // every load that does not depend on another is issued before the
+        // first is used (the header's outcome included): one memory round
+        // trip where there were four
+        const uint64_t j0 = (uint64_t)threadIdx.x * kPartsPer;
+        uint64_t ta[kPartsPer], tb[kPartsPer];
 #pragma unroll
-    for (uint32_t k = 0; k < kPartsPer; ++k) {
-        const bool in = j0 + k < a.nb;
-        ta[k] = in ? a.tpart[j0 + k] : 0;
-        tb[k] = in ? a.tpart[kMaxScanParts + j0 + k] : 0;
+        for (uint32_t k = 0; k < kPartsPer; ++k) {
+            const bool in = j0 + k < a.nb;
+            ta[k] = in ? a.tpart[j0 + k] : 0;
+            tb[k] = in ? a.tpart[kMaxScanParts + j0 + k] : 0;
+        }
+        for (uint64_t j = threadIdx.x; j < a.nb; j += kScanThreads) {
+            moved += a.spart[j].moved_bytes;
+            small += a.spart[j].small_moved;
+        }
+        k_begin = a.lbase[g];
+        k_end = a.lbase[g + 1];
+        if (plan_dead(hdr)) return;
+        {
+            StatPart q{0, 0, 0, 0, kNone, kNone, kNone, 0};
+            uint64_t x[4] = {moved, small, 0, 0};
+            block_reduce_stats<kScanThreads>(q, x, s_red);
+            moved = x[0];
+            small = x[1];
+        }
+        sums_prefix(ta, g, sh, &s_before, pa, na);
+        sums_prefix(tb, g, sh, &s_before, pb, nbt);
     }
-    uint64_t moved = 0, small = 0;
-    for (uint64_t j = threadIdx.x; j < a.nb; j += kScanThreads) {
-        moved += a.spart[j].moved_bytes;
-        small += a.spart[j].small_moved;
-    }
-    const uint64_t k_begin = a.lbase[g], k_end = a.lbase[g + 1];
-    if (plan_dead(hdr)) return;
-    {
-        StatPart q{0, 0, 0, 0, kNone, kNone, kNone, 0};
-        uint64_t x[4] = {moved, small, 0, 0};
-        block_reduce_stats<kScanThreads>(q, x, s_red);
-        moved = x[0];
-        small = x[1];
-    }
-    uint64_t pa, na, pb, nbt;
-    sums_prefix(ta, g, sh, &s_before, pa, na);
-    sums_prefix(tb, g, sh, &s_before, pb, nbt);
     const bool pick_b = pick_larger(a.tiles, moved, small, na, nbt, a.max_tiles);
     const uint64_t T = pick_b ? a.tiles.b : a.tiles.a;
     const uint64_t n_tiles = pick_b ? nbt : na;
