@@ -606,20 +606,14 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
     m.stall_sleeps = c.tu.stall_sleeps;
     m.stall_seed = c.tu.stall_seed;
     // with the tile size left to the plan, a mover for each candidate: the
-    // one whose size the plan did not choose leaves at once.  In an arena
-    // of at most kAutoMinMoved bytes fewer bytes than that move (a moved
-    // block has a hole below it), so the plan takes the larger size if the
-    // arena's blocks are large (auto_larger_always) and else keeps the
-    // smaller, unless its tiles overflow the workspace, which the bound
-    // rules out here (the larger cuts fewer): one mover, of that size.
+    // one whose size the plan did not choose leaves at once -- unless the
+    // plan takes the larger whatever the shifts (auto_larger_always; it
+    // cuts fewer tiles, so it fits wherever the smaller would): then one
+    // mover, of that size.
     MoveArgs mb = m;
     mb.tile_bytes = c.tiles.b;
     mb.max_blocks = c.tiles.b / 32 + 2;
-    const uint64_t max_pinned = a->table->pinned_dev ? n : 0;
-    const bool one_mover =
-        c.tiles.a == c.tiles.b ||
-        (a->arena_bytes <= kAutoMinMoved &&
-         tiles_bound(a->arena_bytes, max_pinned, c.tiles.a) <= c.L.max_tiles);
+    const bool one_mover = c.tiles.a == c.tiles.b || c.tiles.always_b;
     // Remap, commit and the post-check read the plan, never the arena: the
     // first workgroups of each mover's launch run them beside the move, in
     // the launch whose tile size the plan chose (the post-check takes the
@@ -634,7 +628,7 @@ int defrag_compact(const defrag_compact_args *a, hipStream_t stream, defrag_plan
                             after_host != nullptr, gate, c.L.max_tiles);
     sj.any_tile = one_mover ? 1u : 0u;  // the one launch runs it
     const SideArgs *side = side_work ? &sj : nullptr;
-    const MoveArgs &only = c.tiles.small_arena ? mb : m;
+    const MoveArgs &only = c.tiles.always_b ? mb : m;
     const bool ok =
         one_mover ? launch_move_device_sized(only, c.tu.nontemporal, side, stream) == hipSuccess
                   : launch_move_device_sized(m, c.tu.nontemporal, side, stream) == hipSuccess &&

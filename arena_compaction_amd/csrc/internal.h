@@ -53,21 +53,23 @@ constexpr uint32_t kAutoTileSmall = 65536;
 constexpr uint32_t kAutoTileLarge = 131072;
 constexpr uint64_t kAutoSmallShift = 8ull << 20;
 constexpr uint64_t kAutoMinMoved = 64ull << 20;
-// In an arena of at most kAutoMinMoved bytes whose blocks take the 512-lane
-// mover the plan always picks 128 KiB: a step that small is bound by
-// latency, and half as many tiles, two per workgroup in flight, wait less
-// (the 64 MiB table of 4,096 blocks: one call 67.9-68.9 -> 64.8-65.8 us,
-// 381 tiles of which 153-159 late -> 191 of which 36-46).  Tables of small
-// blocks, moved by the 1,024-lane mover one tile at a time, keep the rule
-// above.
+// The plan picks 128 KiB whatever the shifts in two cases.  An arena of at
+// most kAutoMinMoved bytes: a step that small is bound by latency, and half
+// as many tiles, two per workgroup in flight, wait less (the 64 MiB table
+// of 4,096 blocks: one call 67.9-68.9 -> 64.8-65.8 us, 381 tiles of which
+// 153-159 late -> 191 of which 36-46).  A table of small blocks (the
+// 1,024-lane mover, one tile at a time): each tile's record and block table
+// are fetched once for twice the bytes (the 4 GiB table of 32 B-4 KiB
+// blocks: mover 77.9 -> 78.6% of peak, one call 1.001-1.006 -> 0.974-0.979
+// ms).  The one-call path then launches that mover alone.
 inline bool auto_larger_always(uint64_t arena_bytes, uint64_t n) {
-    return arena_bytes <= kAutoMinMoved && !move_small_blocks(arena_bytes, n);
+    return arena_bytes <= kAutoMinMoved || move_small_blocks(arena_bytes, n);
 }
 
 // The tile sizes a plan counts tiles for: a == b for a size the caller gave.
 struct TileChoice {
     uint32_t a, b;
-    uint32_t small_arena;  // a != b: b whatever the shifts (auto_larger_always)
+    uint32_t always_b;  // a != b: b whatever the shifts (auto_larger_always)
 };
 // Mover workgroups per compute unit when the caller gives no tuning: one,
 // which keeps one narrow window of tiles in flight (two 512-lane workgroups

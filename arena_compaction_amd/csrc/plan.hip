@@ -570,11 +570,11 @@ struct BaseArgs {
 // bucket index.
 // The tile size, decided the same way by every workgroup from the same
 // totals: moved bytes, those shifting by less than kAutoSmallShift, and the
-// tiles each candidate cuts (the larger always in a small arena of large
-// blocks, tc.small_arena).  True: the larger candidate.
+// tiles each candidate cuts (the larger always in a small arena or a table
+// of small blocks, tc.always_b).  True: the larger candidate.
 __device__ inline bool pick_larger(TileChoice tc, uint64_t moved, uint64_t small, uint64_t na,
                                    uint64_t nb, uint64_t max_tiles) {
-    bool pick_b = tc.a != tc.b && (tc.small_arena || (small * 2 > moved && moved >= kAutoMinMoved));
+    bool pick_b = tc.a != tc.b && (tc.always_b || (small * 2 > moved && moved >= kAutoMinMoved));
     if (tc.a != tc.b && (pick_b ? nb : na) > max_tiles && (pick_b ? na : nb) <= max_tiles)
         pick_b = !pick_b;
     return pick_b;

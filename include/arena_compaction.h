@@ -155,11 +155,13 @@ typedef struct defrag_tuning {
                                  depends on one still being read; 128 KiB
                                  tiles are moved two per workgroup in flight,
                                  which hides that wait), or whenever the
-                                 arena is at most 64 MiB and its entries
-                                 average at least 8 KiB of it (a step bound
-                                 by latency, where half as many tiles wait
-                                 less), else 65536 -- and the other one if
-                                 the first's tiles do not fit the workspace.
+                                 arena is at most 64 MiB (a step bound by
+                                 latency, where half as many tiles wait less)
+                                 or its entries average under 8 KiB of it
+                                 (small blocks: each tile's block table then
+                                 serves twice the bytes), else 65536 -- and
+                                 the other one if the first's tiles do not
+                                 fit the workspace.
                                  plan_host->tuning.tile_bytes says which.    */
     uint32_t wg_per_cu;       /* mover workgroups per compute unit; 0 means as
                                  many as the kernel's resources allow         */

@@ -89,11 +89,11 @@ def expected_schedule(heap, hold, T):
 
 def auto_tile(heap, hold):
     """The tile size a plan given none must choose, stated on the host: 128 KiB
-    in an arena of at most 64 MiB whose entries average at least 8 KiB of it
-    (no table of small blocks), or when more than half of the moved bytes
-    belong to blocks that shift by less than 8 MiB and at least 64 MiB move,
-    else 64 KiB (the workspaces here hold either size's tiles)."""
-    if heap.arena_bytes <= (64 << 20) and not (heap.n and heap.arena_bytes // heap.n < 8192):
+    in an arena of at most 64 MiB, in a table of small blocks (entries
+    averaging under 8 KiB of the arena), or when more than half of the moved
+    bytes belong to blocks that shift by less than 8 MiB and at least 64 MiB
+    move, else 64 KiB (the workspaces here hold either size's tiles)."""
+    if heap.arena_bytes <= (64 << 20) or (heap.n and heap.arena_bytes // heap.n < 8192):
         return 131072
     li = np.flatnonzero(heap.live)
     new = oracle.new_offsets(heap.offset, heap.size, heap.live, hold)[li].astype(np.int64)
