@@ -274,7 +274,9 @@ struct WsLayout {
     size_t header, post, part, spart, csum, tpart, twhole, lbase, live_dst, live_src, live_size,
         live_pin, tile_base, live_z, live_pc, selpart, live_rec, live_key, ridx, fixed;
     // tile part (depends on the tile capacity)
-    size_t tiles, flags, total;
+    // tgrp: the first block of every 256th tile, and of the last (the tile
+    // pass's workgroups' stretches of blocks, recorded by the bases pass)
+    size_t tiles, flags, tgrp, total;
     uint64_t n_scan_blocks, scan_chunk, n_sel_blocks, max_tiles;
 };
 
@@ -325,6 +327,7 @@ inline WsLayout ws_with_tiles(uint64_t n, uint64_t max_tiles) {
     size_t at = L.fixed;
     L.tiles = at;      at += align256(max_tiles * sizeof(TileRec));
     L.flags = at;      at += align256(max_tiles * sizeof(uint32_t));
+    L.tgrp = at;       at += align256((max_tiles / 256 + 2) * sizeof(uint32_t));
     L.total = at;
     return L;
 }
@@ -340,9 +343,10 @@ inline uint64_t tiles_bound(uint64_t arena_bytes, uint64_t max_pinned, uint32_t 
 inline uint64_t tiles_fitting(uint64_t n, size_t ws_bytes) {
     const WsLayout F = ws_fixed(n);
     if (ws_bytes <= F.fixed) return 0;
-    // upper estimate, then step down past the (at most 4 x 255 bytes of)
-    // alignment padding
-    uint64_t t = (ws_bytes - F.fixed) / kPerTileBytes;
+    // upper estimate (each tile's record and flag and a 256th of a group
+    // entry), then step down past the (at most 3 x 255 bytes of) alignment
+    // padding and the two spare group entries: a few steps
+    uint64_t t = (uint64_t)(ws_bytes - F.fixed) * 256 / (kPerTileBytes * 256 + sizeof(uint32_t));
     while (t > 0 && ws_with_tiles(n, t).total > ws_bytes) --t;
     return t;
 }

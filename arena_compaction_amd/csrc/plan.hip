@@ -549,6 +549,7 @@ struct BaseArgs {
     TileChoice tiles;
     uint64_t max_tiles;
     uint32_t *tile_base;
+    uint32_t *tgrp;     // first block of every 256th tile and of the last
     uint32_t *ridx;
     uint32_t rw;        // remap bucket width (log2 bytes)
     uint64_t rnb;       // remap buckets
@@ -578,6 +579,30 @@ __device__ inline bool pick_larger(TileChoice tc, uint64_t moved, uint64_t small
     if (tc.a != tc.b && (pick_b ? nb : na) > max_tiles && (pick_b ? na : nb) <= max_tiles)
         pick_b = !pick_b;
     return pick_b;
+}
+
+// The tile pass's stretches: block k, whose tiles are [run, run + c), is
+// the first block of tile 256 q for each q with 256 q in that range
+// (tgrp[q]) and, if it holds the last tile, of that one (tgrp[groups]).
+// A lane writes a few such entries itself; a block with many (one of GiBs
+// has hundreds) has them written by the whole wave, 64 at a time.  Every
+// lane of the wave calls it (in: k is one of the workgroup's blocks).
+__device__ inline void mark_groups(uint32_t *tgrp, bool in, uint64_t k, uint64_t run, uint64_t c,
+                                   uint64_t n_tiles) {
+    const uint64_t q0 = (run + 255) / 256;
+    const uint64_t q1 = (in && c) ? (run + c + 255) / 256 : q0;  // groups q0 <= q < q1
+    if (q1 - q0 <= 4) {
+        for (uint64_t q = q0; q < q1; ++q) tgrp[q] = (uint32_t)k;
+    }
+    uint64_t many = __ballot(q1 - q0 > 4);
+    const uint32_t lane = threadIdx.x & 63;
+    while (many) {
+        const int L = __ffsll((unsigned long long)many) - 1;
+        const uint64_t b0 = __shfl(q0, L, 64), b1 = __shfl(q1, L, 64), bk = __shfl(k, L, 64);
+        for (uint64_t q = b0 + lane; q < b1; q += 64) tgrp[q] = (uint32_t)bk;
+        many &= many - 1;
+    }
+    if (in && c && run + c == n_tiles) tgrp[(n_tiles + 255) / 256] = (uint32_t)k;
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
@@ -736,7 +761,9 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_bases(BaseArgs a) {
         carry += total;
 #pragma unroll
         for (uint32_t j = 0; j < kScanItems; ++j) {
-            if (k0 + j < k_end) a.tile_base[k0 + j] = (uint32_t)run;
+            const bool in = k0 + j < k_end;
+            if (in) a.tile_base[k0 + j] = (uint32_t)run;
+            mark_groups(a.tgrp, in, k0 + j, run, c[j], n_tiles);
             run += c[j];
         }
     }
@@ -948,33 +975,30 @@ constexpr uint64_t kStageTileLimit = 512ull * 256;
 // plan's tiles take few workgroups, which then all run at once.
 template <bool STAGE>
 __global__ __launch_bounds__(256) void k_tiles(LiveView lv, const uint32_t *tile_base,
-                                               const WsHeader *hdr, uint64_t max_tiles,
-                                               const uint32_t *ridx, uint32_t w, TileRec *tiles,
-                                               uint32_t *flags) {
+                                               const uint32_t *tgrp, const WsHeader *hdr,
+                                               uint64_t max_tiles, const uint32_t *ridx,
+                                               uint32_t w, TileRec *tiles, uint32_t *flags) {
     constexpr uint32_t kCap = kTileStage + 2;
     constexpr uint32_t kLiveCap = STAGE ? kCap : 1;
     __shared__ uint32_t s_tb[kCap];
     __shared__ uint64_t s_dst[kLiveCap], s_src[kLiveCap], s_size[kLiveCap];
     __shared__ uint64_t s_t0[257];
-    __shared__ int64_t s_k[2];
+    // the first blocks of the workgroup's first tile and of the last tile
+    // whose start it needs (the bases pass recorded them; loaded beside the
+    // header: the array holds an entry past the grid's last workgroup)
+    const uint32_t g_lo = tgrp[blockIdx.x], g_hi = tgrp[blockIdx.x + 1];
     const uint64_t n_tiles = hdr->n_tiles, m = hdr->live_blocks, T = hdr->tile_bytes;
     if (plan_dead(hdr) | (n_tiles > max_tiles)) return;  // plan fails
     const uint64_t tb = (uint64_t)blockIdx.x * 256;
     if (tb >= n_tiles) return;  // (the whole workgroup)
     const uint64_t t = tb + threadIdx.x;
     const uint64_t te = umin64(tb + 256, n_tiles);
-    const uint64_t tq = te < n_tiles ? te : te - 1;  // the last tile whose start is needed
-    // the stretch of tile_base holding the first blocks of tiles [tb, tq]
-    if (m <= kTileStage) {
-        if (threadIdx.x == 0) {
-            s_k[0] = 0;
-            s_k[1] = (int64_t)m - 1;
-        }
-    } else {
-        find_stretch(tile_base, (int64_t)m, tb, tq, s_k);
-    }
-    __syncthreads();
-    const int64_t k_lo = s_k[0], k_hi = s_k[1];
+    // the stretch of tile_base holding the first blocks of tiles [tb, tq],
+    // tq = te or the last tile: a small plan takes all of its blocks (and
+    // then reads them through the LDS-only accessor)
+    const bool whole = m <= kTileStage;
+    const int64_t k_lo = whole ? 0 : (int64_t)g_lo;
+    const int64_t k_hi = whole ? (int64_t)m - 1 : (int64_t)g_hi;
     const bool staged = k_hi - k_lo < (int64_t)kTileStage;
     // staged: blocks [s_lo, s_lo + s_cnt) -- the stretch, the block before it
     // (a tile's start reads the block before its first) and the one after
@@ -1277,6 +1301,7 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
     b.tiles = tiles;
     b.max_tiles = L.max_tiles;
     b.tile_base = tile_base;
+    b.tgrp = reinterpret_cast<uint32_t *>(ws + L.tgrp);
     b.ridx = ridx;
     b.rw = remap_shift(arena_bytes, t.n);
     b.rnb = remap_buckets(arena_bytes, t.n);
@@ -1299,10 +1324,10 @@ hipError_t queue_scan(const TableView &t, uint64_t arena_bytes, uint8_t *ws, con
         const uint64_t bound = arena_bytes / t_min + t.n;
         if (bound <= kStageTileLimit)
             hipLaunchKernelGGL(k_tiles<true>, dim3((uint32_t)grid), dim3(256), 0, s, lv, tile_base,
-                               hdr, L.max_tiles, ridx, b.rw, trec, flags);
+                               b.tgrp, hdr, L.max_tiles, ridx, b.rw, trec, flags);
         else
             hipLaunchKernelGGL(k_tiles<false>, dim3((uint32_t)grid), dim3(256), 0, s, lv,
-                               tile_base, hdr, L.max_tiles, ridx, b.rw, trec, flags);
+                               tile_base, b.tgrp, hdr, L.max_tiles, ridx, b.rw, trec, flags);
         AC_TRY(hipGetLastError());
     }
     return hipSuccess;
