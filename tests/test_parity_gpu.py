@@ -513,6 +513,35 @@ def test_remap_index_over_a_dense_cluster(ac):
     assert np.array_equal(r.remapped, want) and r.n_invalid == bad
 
 
+def test_remap_batch_tails(ac):
+    """Each lane of the remap looks up several handles at once, k, k +
+    stride, ...: handle counts that leave a lane's last batch part-filled
+    (1, 3, one past a workgroup, one short of and one past a whole pass of
+    the launch), the handles a random mix of the table's edges and holes,
+    in place and into a second buffer; every handle matches the oracle and
+    nothing past the last handle is written."""
+    heap = W.workload("pairs-1g", small=True)
+    off, size, live = device_table(heap, "cuda")
+    ws = ac.workspace(heap.n, heap.arena_bytes)
+    plan = ac.defrag_plan(off, size, live, heap.arena_bytes, ws)
+    rng = np.random.default_rng(41)
+    pool = np.concatenate([heap.handles, W.edge_handles(heap, rng, 4096)])
+    lanes = 512 * 256  # the most a standalone remap launch runs
+    sentinel = np.uint64(0x5A5A5A5A5A5A5A5A)
+    bad = torch.zeros(1, dtype=torch.int64, device="cuda")
+    for H in (1, 3, 257, lanes - 1, 4 * lanes - 1, 4 * lanes + 5):
+        hs = pool[rng.integers(0, pool.size, H)]
+        want, wb = oracle.remap(heap.offset, heap.size, heap.live, hs)
+        h = u64_to_t(hs, "cuda")
+        buf = u64_to_t(np.full(H + 64, sentinel, np.uint64), "cuda")
+        ac.defrag_remap(plan, ws, h, buf[:H], bad)
+        got = t_to_u64(buf)
+        assert np.array_equal(got[:H], want) and int(bad) == wb, H
+        assert np.all(got[H:] == sentinel), H
+        ac.defrag_remap(plan, ws, h, h, bad)  # in place
+        assert np.array_equal(t_to_u64(h), want) and int(bad) == wb, H
+
+
 def test_scan_workgroups_taking_several_steps(ac):
     """Above 1,024 x 1,024 entries each scan workgroup takes several steps of
     1,024 entries with a running carry: 3,000,000 entries of 32-96 bytes with
