@@ -513,11 +513,10 @@ def test_remap_index_over_a_dense_cluster(ac):
     assert np.array_equal(r.remapped, want) and r.n_invalid == bad
 
 
-def test_remap_batch_tails(ac):
-    """Each lane of the remap looks up several handles at once, k, k +
-    stride, ...: handle counts that leave a lane's last batch part-filled
-    (1, 3, one past a workgroup, one short of and one past a whole pass of
-    the launch), the handles a random mix of the table's edges and holes,
+def test_remap_pass_tails(ac):
+    """Each lane of the remap takes handles k, k + stride, ...: handle
+    counts that leave the launch's last pass part-filled (1, 3, one past a
+    workgroup, one short of a whole pass, one short of and one past four), the handles a random mix of the table's edges and holes,
     in place and into a second buffer; every handle matches the oracle and
     nothing past the last handle is written."""
     heap = W.workload("pairs-1g", small=True)
